@@ -1,0 +1,281 @@
+// C ABI of the library: argument validation and launch (see include/dbs.h).
+//
+// Every entry point validates its arguments on the host before launching
+// anything, records a message for dbs_last_error() on failure and returns a
+// status code; no exception leaves this file.
+#include "dbs.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <exception>
+#include <string>
+#include <vector>
+
+#include "dbs_internal.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dbs_status fail(dbs_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+dbs_status ok() {
+  g_last_error.clear();
+  return DBS_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+dbs_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(DBS_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define DBS_GUARD_BEGIN try {
+#define DBS_GUARD_END                                                     \
+  }                                                                       \
+  catch (const std::exception& ex) {                                      \
+    return fail(DBS_ERR_INVALID_ARG, "internal error: %s", ex.what());    \
+  }                                                                       \
+  catch (...) {                                                           \
+    return fail(DBS_ERR_INVALID_ARG, "internal error");                   \
+  }
+
+#define REQUIRE(cond, st, ...) \
+  do {                         \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+dbs_status check_grid(int T, int H, int W, int prefix, int32_t* out) {
+  REQUIRE(out != nullptr, DBS_ERR_INVALID_ARG, "perm_out is NULL");
+  REQUIRE(T >= 1 && H >= 1 && W >= 1, DBS_ERR_INVALID_ARG, "grid sides must be >= 1 (got %d x %d x %d)", T, H, W);
+  REQUIRE(prefix >= 0, DBS_ERR_INVALID_ARG, "prefix must be >= 0");
+  const int64_t n = (int64_t)prefix + (int64_t)T * H * W;
+  REQUIRE(n <= INT32_MAX, DBS_ERR_INVALID_ARG, "sequence length %lld exceeds int32", (long long)n);
+  return DBS_OK;
+}
+
+// Shared checks for the token-geometry arguments of the device calls.
+dbs_status check_geometry(int B, int Hh, int N, int Npad, int d, int b) {
+  REQUIRE(B >= 1 && Hh >= 1, DBS_ERR_INVALID_ARG, "B and Hh must be >= 1 (got %d, %d)", B, Hh);
+  REQUIRE(N >= 1, DBS_ERR_INVALID_ARG, "N must be >= 1 (got %d)", N);
+  REQUIRE(d == 64 || d == 128, DBS_ERR_UNSUPPORTED, "head dim d=%d unsupported (64 or 128)", d);
+  REQUIRE(b == 64 || b == 128, DBS_ERR_UNSUPPORTED, "block size b=%d unsupported (64 or 128)", b);
+  REQUIRE(Npad >= N && Npad % b == 0, DBS_ERR_INVALID_ARG, "Npad=%d must be >= N=%d and a multiple of b=%d", Npad, N, b);
+  REQUIRE(Npad - N < b, DBS_ERR_INVALID_ARG, "Npad=%d holds a whole empty block beyond N=%d", Npad, N);
+  REQUIRE((int64_t)B * Hh * Npad * d <= ((int64_t)1 << 40), DBS_ERR_INVALID_ARG, "tensor too large");
+  return DBS_OK;
+}
+
+dbs_status check_strides(int64_t sb, int64_t sn, int64_t sh, dbs_dtype dt) {
+  const int64_t q = dt == DBS_BF16 ? 8 : 4;   // elements per 16 bytes
+  REQUIRE(sb >= 0 && sn >= 0 && sh >= 0, DBS_ERR_INVALID_ARG, "strides must be >= 0");
+  REQUIRE(sb % q == 0 && sn % q == 0 && sh % q == 0, DBS_ERR_ALIGNMENT,
+          "strides (%lld, %lld, %lld) must keep rows 16-byte aligned", (long long)sb, (long long)sn,
+          (long long)sh);
+  return DBS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dbs_abi_version(void) { return DBS_ABI_VERSION; }
+
+const char* dbs_last_error(void) { return g_last_error.c_str(); }
+
+dbs_status dbs_perm_gilbert3d(int T, int H, int W, int prefix, int32_t* perm_out) {
+  DBS_GUARD_BEGIN
+  dbs_status st = check_grid(T, H, W, prefix, perm_out);
+  if (st != DBS_OK) return st;
+  dbs::gilbert3d(T, H, W, prefix, perm_out);
+  return ok();
+  DBS_GUARD_END
+}
+
+dbs_status dbs_perm_cuboid(int T, int H, int W, int ct, int ch, int cw, int prefix, int32_t* perm_out) {
+  DBS_GUARD_BEGIN
+  dbs_status st = check_grid(T, H, W, prefix, perm_out);
+  if (st != DBS_OK) return st;
+  REQUIRE(ct >= 1 && ch >= 1 && cw >= 1, DBS_ERR_INVALID_ARG, "cuboid sides must be >= 1");
+  dbs::cuboid_order(T, H, W, ct, ch, cw, prefix, perm_out);
+  return ok();
+  DBS_GUARD_END
+}
+
+dbs_status dbs_perm_invert(const int32_t* perm, int n, int32_t* inv_out) {
+  DBS_GUARD_BEGIN
+  REQUIRE(perm != nullptr && inv_out != nullptr, DBS_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(n >= 1, DBS_ERR_INVALID_ARG, "n must be >= 1");
+  for (int i = 0; i < n; ++i) inv_out[i] = -1;
+  for (int i = 0; i < n; ++i) {
+    const int32_t p = perm[i];
+    REQUIRE(p >= 0 && p < n && inv_out[p] == -1, DBS_ERR_INVALID_ARG,
+            "not a permutation: entry %d is %d", i, p);
+    inv_out[p] = i;
+  }
+  return ok();
+  DBS_GUARD_END
+}
+
+dbs_status dbs_reorder(const void* x, dbs_dtype x_dt, int64_t sb, int64_t sn, int64_t sh, void* y,
+                       dbs_dtype y_dt, dbs_layout y_layout, const int32_t* perm, int perm_per_head,
+                       int B, int Hh, int N, int Npad, int d, int b, hipStream_t stream) {
+  DBS_GUARD_BEGIN
+  REQUIRE(x && y && perm, DBS_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(aligned16(x) && aligned16(y) && ((uintptr_t)perm & 3u) == 0, DBS_ERR_ALIGNMENT, "misaligned pointer");
+  REQUIRE(x_dt == DBS_BF16 || x_dt == DBS_FP32, DBS_ERR_INVALID_ARG, "bad x dtype");
+  REQUIRE(y_dt == DBS_BF16 || y_dt == DBS_FP32, DBS_ERR_INVALID_ARG, "bad y dtype");
+  REQUIRE(!(x_dt == DBS_BF16 && y_dt == DBS_FP32), DBS_ERR_UNSUPPORTED, "bf16 -> fp32 reorder not offered");
+  REQUIRE(y_layout == DBS_ROWS || y_layout == DBS_TILES_T, DBS_ERR_INVALID_ARG, "bad layout");
+  REQUIRE(!(y_layout == DBS_TILES_T && y_dt != DBS_BF16), DBS_ERR_UNSUPPORTED, "tiles layout is bf16 only");
+  REQUIRE(perm_per_head == 0 || perm_per_head == 1, DBS_ERR_INVALID_ARG, "perm_per_head must be 0 or 1");
+  dbs_status st = check_geometry(B, Hh, N, Npad, d, b);
+  if (st != DBS_OK) return st;
+  st = check_strides(sb, sn, sh, x_dt);
+  if (st != DBS_OK) return st;
+  dbs::ReorderArgs a{};
+  a.x = x; a.y = y; a.sb = sb; a.sn = sn; a.sh = sh; a.perm = perm;
+  a.perm_h_stride = perm_per_head ? N : 0;
+  a.B = B; a.Hh = Hh; a.N = N; a.Npad = Npad; a.d = d; a.b = b;
+  a.x_f32 = x_dt == DBS_FP32; a.y_f32 = y_dt == DBS_FP32; a.tiles_t = y_layout == DBS_TILES_T;
+  a.stream = stream;
+  return from_hip(dbs::launch_reorder(a), "dbs_reorder launch");
+  DBS_GUARD_END
+}
+
+dbs_status dbs_inverse_reorder(const void* y, dbs_dtype y_dt, void* x, dbs_dtype x_dt, int64_t sb,
+                               int64_t sn, int64_t sh, const int32_t* perm, int perm_per_head, int B,
+                               int Hh, int N, int Npad, int d, hipStream_t stream) {
+  DBS_GUARD_BEGIN
+  REQUIRE(x && y && perm, DBS_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(aligned16(x) && aligned16(y) && ((uintptr_t)perm & 3u) == 0, DBS_ERR_ALIGNMENT, "misaligned pointer");
+  REQUIRE(y_dt == DBS_BF16, DBS_ERR_UNSUPPORTED, "inverse_reorder reads bf16 rows");
+  REQUIRE(x_dt == DBS_BF16 || x_dt == DBS_FP32, DBS_ERR_INVALID_ARG, "bad x dtype");
+  REQUIRE(perm_per_head == 0 || perm_per_head == 1, DBS_ERR_INVALID_ARG, "perm_per_head must be 0 or 1");
+  REQUIRE(B >= 1 && Hh >= 1 && N >= 1 && Npad >= N, DBS_ERR_INVALID_ARG, "bad sizes");
+  REQUIRE(d == 64 || d == 128, DBS_ERR_UNSUPPORTED, "head dim d=%d unsupported", d);
+  dbs_status st = check_strides(sb, sn, sh, x_dt);
+  if (st != DBS_OK) return st;
+  dbs::ReorderArgs a{};
+  a.y = const_cast<void*>(y); a.x_out = x; a.sb = sb; a.sn = sn; a.sh = sh; a.perm = perm;
+  a.perm_h_stride = perm_per_head ? N : 0;
+  a.B = B; a.Hh = Hh; a.N = N; a.Npad = Npad; a.d = d; a.b = 0;
+  a.x_f32 = x_dt == DBS_FP32;
+  a.stream = stream;
+  return from_hip(dbs::launch_inverse_reorder(a), "dbs_inverse_reorder launch");
+  DBS_GUARD_END
+}
+
+size_t dbs_estimate_workspace_bytes(int B, int Hh, int N, int b, int k) {
+  if (B < 1 || Hh < 1 || N < 1 || b < 1 || k < 1) return 0;
+  const int64_t nb = (N + b - 1) / b;
+  return (size_t)((int64_t)B * Hh * nb * k * 4);
+}
+
+dbs_status dbs_estimate_blocks(const void* q_r, const void* k_r, dbs_dtype dt, int B, int Hh, int N,
+                               int Npad, int d, int b, int k, float scale, float* p_imp,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  DBS_GUARD_BEGIN
+  REQUIRE(q_r && k_r && p_imp && workspace, DBS_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(aligned16(q_r) && aligned16(k_r) && aligned16(p_imp) && aligned16(workspace),
+          DBS_ERR_ALIGNMENT, "misaligned pointer");
+  REQUIRE(dt == DBS_BF16, DBS_ERR_UNSUPPORTED, "estimate_blocks computes on bf16 inputs");
+  dbs_status st = check_geometry(B, Hh, N, Npad, d, b);
+  if (st != DBS_OK) return st;
+  REQUIRE(k >= 1 && k <= b, DBS_ERR_INVALID_ARG, "k=%d must be in [1, b=%d]", k, b);
+  REQUIRE((k & (k - 1)) == 0, DBS_ERR_UNSUPPORTED, "k=%d must be a power of two", k);
+  REQUIRE(std::isfinite(scale) && scale > 0.f, DBS_ERR_INVALID_ARG, "scale must be finite and > 0");
+  const size_t need = dbs_estimate_workspace_bytes(B, Hh, N, b, k);
+  REQUIRE(workspace_bytes >= need, DBS_ERR_INVALID_ARG, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  const int nb = Npad / b;
+  REQUIRE((int64_t)nb * k <= INT32_MAX / 2, DBS_ERR_INVALID_ARG, "too many sampled tokens");
+  dbs::EstimateArgs a{};
+  a.q_r = q_r; a.k_r = k_r; a.p_imp = p_imp; a.lse2 = static_cast<float*>(workspace);
+  a.B = B; a.Hh = Hh; a.N = N; a.Npad = Npad; a.d = d; a.b = b; a.k = k; a.nb = nb;
+  a.scale = scale; a.stream = stream;
+  return from_hip(dbs::launch_estimate(a), "dbs_estimate_blocks launch");
+  DBS_GUARD_END
+}
+
+dbs_status dbs_build_mask(const float* p_imp, int B, int Hh, int nb, float tau, int32_t* kv_count,
+                          int32_t* kv_idx, uint8_t* mask, hipStream_t stream) {
+  DBS_GUARD_BEGIN
+  REQUIRE(p_imp && kv_count && kv_idx, DBS_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(((uintptr_t)p_imp & 3u) == 0 && ((uintptr_t)kv_count & 3u) == 0 && ((uintptr_t)kv_idx & 3u) == 0,
+          DBS_ERR_ALIGNMENT, "misaligned pointer");
+  REQUIRE(B >= 1 && Hh >= 1, DBS_ERR_INVALID_ARG, "B and Hh must be >= 1");
+  REQUIRE(nb >= 1 && nb <= 4096, DBS_ERR_UNSUPPORTED, "nb=%d must be in [1, 4096]", nb);
+  REQUIRE(tau > 0.f && tau <= 1.f, DBS_ERR_INVALID_ARG, "tau=%g must be in (0, 1]", (double)tau);
+  REQUIRE((int64_t)B * Hh * nb <= INT32_MAX, DBS_ERR_INVALID_ARG, "too many rows");
+  dbs::MaskArgs a{};
+  a.p_imp = p_imp; a.kv_count = kv_count; a.kv_idx = kv_idx; a.mask = mask;
+  a.rows = B * Hh * nb; a.nb = nb; a.tau = tau; a.stream = stream;
+  return from_hip(dbs::launch_build_mask(a), "dbs_build_mask launch");
+  DBS_GUARD_END
+}
+
+dbs_status dbs_meanpool_kv(const void* k_r, const void* v_r, dbs_dtype dt, int B, int Hh, int N, int Npad,
+                           int d, int b, int n, void* k_g, void* v_g, hipStream_t stream) {
+  DBS_GUARD_BEGIN
+  REQUIRE(k_r && v_r && k_g && v_g, DBS_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(aligned16(k_r) && aligned16(v_r) && aligned16(k_g) && aligned16(v_g), DBS_ERR_ALIGNMENT,
+          "misaligned pointer");
+  REQUIRE(dt == DBS_BF16, DBS_ERR_UNSUPPORTED, "meanpool_kv is bf16 only");
+  dbs_status st = check_geometry(B, Hh, N, Npad, d, b);
+  if (st != DBS_OK) return st;
+  REQUIRE(n >= 1 && n <= N, DBS_ERR_INVALID_ARG, "pool window n=%d must be in [1, N]", n);
+  dbs::MeanpoolArgs a{};
+  a.k_r = k_r; a.v_t = v_r; a.k_g = k_g; a.v_g = v_g;
+  a.B = B; a.Hh = Hh; a.N = N; a.Npad = Npad; a.d = d; a.b = b; a.n = n; a.Ng = (N + n - 1) / n;
+  a.stream = stream;
+  return from_hip(dbs::launch_meanpool(a), "dbs_meanpool_kv launch");
+  DBS_GUARD_END
+}
+
+dbs_status dbs_sparse_attn_fwd(const void* q_r, const void* k_r, const void* v_r, dbs_dtype dt, int B,
+                               int Hh, int N, int Npad, int d, int b, float scale,
+                               const int32_t* kv_count, const int32_t* kv_idx, const void* k_g,
+                               const void* v_g, int Ng, int n_pool, void* o_r, float* lse,
+                               hipStream_t stream) {
+  DBS_GUARD_BEGIN
+  REQUIRE(q_r && k_r && v_r && kv_count && kv_idx && o_r, DBS_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(aligned16(q_r) && aligned16(k_r) && aligned16(v_r) && aligned16(o_r), DBS_ERR_ALIGNMENT,
+          "misaligned pointer");
+  REQUIRE(((uintptr_t)kv_count & 3u) == 0 && ((uintptr_t)kv_idx & 3u) == 0 && ((uintptr_t)lse & 3u) == 0,
+          DBS_ERR_ALIGNMENT, "misaligned pointer");
+  REQUIRE(dt == DBS_BF16, DBS_ERR_UNSUPPORTED, "sparse_attn_fwd computes on bf16 inputs");
+  dbs_status st = check_geometry(B, Hh, N, Npad, d, b);
+  if (st != DBS_OK) return st;
+  REQUIRE(std::isfinite(scale), DBS_ERR_INVALID_ARG, "scale must be finite");
+  REQUIRE((k_g == nullptr) == (v_g == nullptr), DBS_ERR_INVALID_ARG, "k_g and v_g must both be set or both NULL");
+  if (k_g != nullptr) {
+    REQUIRE(aligned16(k_g) && aligned16(v_g), DBS_ERR_ALIGNMENT, "misaligned pointer");
+    REQUIRE(n_pool >= 1 && n_pool <= N, DBS_ERR_INVALID_ARG, "n_pool=%d must be in [1, N]", n_pool);
+    REQUIRE(Ng == (N + n_pool - 1) / n_pool, DBS_ERR_INVALID_ARG, "Ng=%d must equal ceil(N/n_pool)=%d", Ng,
+            (N + n_pool - 1) / n_pool);
+  }
+  dbs::AttnArgs a{};
+  a.q_r = q_r; a.k_r = k_r; a.v_t = v_r; a.kv_count = kv_count; a.kv_idx = kv_idx;
+  a.k_g = k_g; a.v_g = v_g; a.o_r = o_r; a.lse = lse;
+  a.B = B; a.Hh = Hh; a.N = N; a.Npad = Npad; a.d = d; a.b = b; a.nb = Npad / b;
+  a.Ng = k_g ? Ng : 0; a.n_pool = k_g ? n_pool : 1; a.scale = scale; a.stream = stream;
+  REQUIRE((int64_t)B * Hh * a.nb <= INT32_MAX, DBS_ERR_INVALID_ARG, "too many query blocks");
+  return from_hip(dbs::launch_attn_fwd(a), "dbs_sparse_attn_fwd launch");
+  DBS_GUARD_END
+}
+
+}  // extern "C"

@@ -1,0 +1,281 @@
+// Cumulative-threshold block mask (gfx950).
+//
+// Video-BLADE "Step 2.1": sort each P_imp row descending and keep the fewest
+// key blocks whose cumulative score reaches tau of the row's mass.
+//
+// Exactness: every float32 in [0, 1] is an integer multiple of 2^-149 below
+// 2^150, so a row of up to 4096 values sums exactly in a 192-bit integer
+// (six 32-bit limbs).  The row total, the target ceil(tau * total) and the
+// running prefix are all exact; "prefix >= tau * total" is then decided
+// without rounding and the result cannot depend on the summation order.
+//
+// One workgroup per row: the row is sorted in LDS by a bitonic network on
+// 64-bit keys (~value bits, block index), which orders by value descending
+// and index ascending; wavefront 0 scans the sorted values 64 at a time
+// until the prefix reaches the target; the kept blocks are then written in
+// ascending index order by a block-wide compaction.
+#include "common.h"
+#include "../launch.h"
+
+namespace dbs {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxNb = 4096;
+constexpr int kLimbs = 6;
+
+struct U192 {
+  uint32_t w[kLimbs];
+};
+
+__device__ __forceinline__ U192 u192_zero() {
+  U192 r;
+#pragma unroll
+  for (int i = 0; i < kLimbs; ++i) r.w[i] = 0;
+  return r;
+}
+
+__device__ __forceinline__ U192 u192_add(const U192& a, const U192& b) {
+  U192 r;
+  uint64_t c = 0;
+#pragma unroll
+  for (int i = 0; i < kLimbs; ++i) {
+    const uint64_t s = (uint64_t)a.w[i] + b.w[i] + c;
+    r.w[i] = (uint32_t)s;
+    c = s >> 32;
+  }
+  return r;
+}
+
+__device__ __forceinline__ bool u192_ge(const U192& a, const U192& b) {
+#pragma unroll
+  for (int i = kLimbs - 1; i >= 0; --i) {
+    if (a.w[i] != b.w[i]) return a.w[i] > b.w[i];
+  }
+  return true;
+}
+
+// Exact integer value (units of 2^-149) of a non-negative float32 <= 1.
+__device__ __forceinline__ U192 f32_to_u192(uint32_t bits) {
+  U192 r = u192_zero();
+  const uint32_t e = bits >> 23, mant = bits & 0x7fffffu;
+  uint64_t sig;
+  int sh;
+  if (e == 0) {
+    sig = mant;
+    sh = 0;
+  } else {
+    sig = mant | 0x800000u;
+    sh = (int)e - 1;
+  }
+  const int limb = sh >> 5, off = sh & 31;
+  const uint64_t v = sig << off;              // < 2^55
+#pragma unroll
+  for (int i = 0; i < kLimbs; ++i) {
+    if (i == limb) r.w[i] = (uint32_t)v;
+    if (i == limb + 1) r.w[i] = (uint32_t)(v >> 32);
+  }
+  return r;
+}
+
+__device__ __forceinline__ uint32_t shfl_xor_u32(uint32_t v, int mask) {
+  const int lane = threadIdx.x & 63;
+  return (uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, (int)v);
+}
+
+__device__ __forceinline__ uint32_t shfl_from_u32(uint32_t v, int src) {
+  return (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)v);
+}
+
+__device__ __forceinline__ U192 wave_sum(U192 x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    U192 o;
+#pragma unroll
+    for (int i = 0; i < kLimbs; ++i) o.w[i] = shfl_xor_u32(x.w[i], m);
+    x = u192_add(x, o);
+  }
+  return x;
+}
+
+__device__ __forceinline__ U192 wave_inclusive_scan(U192 x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int src = lane >= d ? lane - d : lane;
+    U192 o;
+#pragma unroll
+    for (int i = 0; i < kLimbs; ++i) o.w[i] = shfl_from_u32(x.w[i], src);
+    if (lane >= d) x = u192_add(x, o);
+  }
+  return x;
+}
+
+__global__ __launch_bounds__(kThreads) void build_mask_kernel(
+    const float* __restrict__ p_imp, int nb, uint32_t tau_bits, int32_t* __restrict__ kv_count,
+    int32_t* __restrict__ kv_idx, uint8_t* __restrict__ mask) {
+  __shared__ uint64_t keys[kMaxNb];
+  __shared__ uint8_t flag[kMaxNb];
+  __shared__ uint32_t red[kThreads / 64][kLimbs];
+  __shared__ int s_invalid, s_m;
+  __shared__ int s_wave_cnt[kThreads / 64];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const uint32_t* prow = reinterpret_cast<const uint32_t*>(p_imp) + row * nb;
+  int P2 = 1;
+  while (P2 < nb) P2 <<= 1;
+
+  if (tid == 0) s_invalid = 0;
+  __syncthreads();
+  bool bad = false;
+  for (int j = tid; j < P2; j += kThreads) {
+    uint64_t key = ~0ull;
+    if (j < nb) {
+      uint32_t bits = prow[j];
+      if ((bits & 0x7fffffffu) == 0) bits = 0;          // -0 is 0
+      if (bits > 0x3f800000u) bad = true;               // negative, > 1, inf, NaN
+      key = ((uint64_t)(~bits) << 32) | (uint32_t)j;
+    }
+    keys[j] = key;
+  }
+  if (bad) s_invalid = 1;
+  __syncthreads();
+  const bool keep_all = s_invalid != 0 || tau_bits >= 0x3f800000u;
+
+  int m = nb;
+  if (!keep_all) {
+    // ---- bitonic sort, ascending keys ----------------------------------------
+    for (int k = 2; k <= P2; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < (P2 >> 1); i += kThreads) {
+          const int lo = 2 * j * (i / j) + (i % j), hi = lo + j;
+          const uint64_t a = keys[lo], b = keys[hi];
+          const bool asc = (lo & k) == 0;
+          if ((a > b) == asc) {
+            keys[lo] = b;
+            keys[hi] = a;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    // ---- exact row total ---------------------------------------------------------
+    U192 part = u192_zero();
+    for (int j = tid; j < nb; j += kThreads) part = u192_add(part, f32_to_u192(~(uint32_t)(keys[j] >> 32)));
+    part = wave_sum(part);
+    if (lane == 0) {
+#pragma unroll
+      for (int i = 0; i < kLimbs; ++i) red[wave][i] = part.w[i];
+    }
+    __syncthreads();
+    if (wave == 0) {
+      U192 total = u192_zero();
+      for (int w = 0; w < kThreads / 64; ++w) {
+        U192 t;
+#pragma unroll
+        for (int i = 0; i < kLimbs; ++i) t.w[i] = red[w][i];
+        total = u192_add(total, t);
+      }
+      // target = ceil(tau * total), tau = tm * 2^-sh exactly
+      const uint32_t te = tau_bits >> 23;
+      const uint64_t tm = te ? ((tau_bits & 0x7fffffu) | 0x800000u) : (tau_bits & 0x7fffffu);
+      const int sh = te ? 150 - (int)te : 149;
+      uint32_t prod[kLimbs + 1];
+      uint64_t c = 0;
+#pragma unroll
+      for (int i = 0; i < kLimbs; ++i) {
+        const uint64_t s = (uint64_t)total.w[i] * tm + c;
+        prod[i] = (uint32_t)s;
+        c = s >> 32;
+      }
+      prod[kLimbs] = (uint32_t)c;
+      // shift right by sh with a sticky bit for the ceiling
+      U192 tgt = u192_zero();
+      bool sticky = false;
+      const int ls = sh >> 5, bs = sh & 31;
+      for (int i = 0; i < kLimbs + 1; ++i) {
+        const int src = i + ls;
+        uint32_t v = 0;
+        if (src <= kLimbs) {
+          v = prod[src] >> bs;
+          if (bs && src + 1 <= kLimbs) v |= prod[src + 1] << (32 - bs);
+        }
+        if (i < kLimbs) tgt.w[i] = v;
+      }
+      for (int i = 0; i < ls && i <= kLimbs; ++i) sticky |= prod[i] != 0;
+      if (ls <= kLimbs && bs) sticky |= (prod[ls] & ((1u << bs) - 1u)) != 0;
+      if (sticky) {
+        U192 one = u192_zero();
+        one.w[0] = 1;
+        tgt = u192_add(tgt, one);
+      }
+      // ---- minimal prefix over the sorted values -----------------------------------
+      U192 run = u192_zero();
+      int found = nb;
+      for (int base = 0; base < nb; base += 64) {
+        const int j = base + lane;
+        const U192 x = j < nb ? f32_to_u192(~(uint32_t)(keys[j] >> 32)) : u192_zero();
+        const U192 inc = wave_inclusive_scan(x, lane);
+        const U192 pref = u192_add(run, inc);
+        const bool hit = j < nb && u192_ge(pref, tgt);
+        const uint64_t ball = __ballot(hit);
+        if (ball) {
+          found = base + __ffsll((unsigned long long)ball);   // first hit index + 1
+          break;
+        }
+        U192 last;
+#pragma unroll
+        for (int i = 0; i < kLimbs; ++i) last.w[i] = shfl_from_u32(inc.w[i], 63);
+        run = u192_add(run, last);
+      }
+      if (lane == 0) s_m = found;
+    }
+    __syncthreads();
+    m = s_m;
+  }
+
+  // ---- kept flags, then ascending compaction --------------------------------------------
+  for (int j = tid; j < nb; j += kThreads) flag[j] = keep_all ? 1 : 0;
+  __syncthreads();
+  if (!keep_all) {
+    for (int i = tid; i < m; i += kThreads) flag[(uint32_t)keys[i]] = 1;
+    __syncthreads();
+  }
+  const int per = (nb + kThreads - 1) / kThreads;
+  const int j0 = tid * per, j1 = min(nb, j0 + per);
+  int cnt = 0;
+  for (int j = j0; j < j1; ++j) cnt += flag[j];
+  // exclusive scan of cnt over the workgroup
+  int inc = cnt;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int src = lane >= d ? lane - d : lane;
+    const int o = __builtin_amdgcn_ds_bpermute(src << 2, inc);
+    if (lane >= d) inc += o;
+  }
+  if (lane == 63) s_wave_cnt[wave] = inc;
+  __syncthreads();
+  int pos = inc - cnt;
+  for (int w = 0; w < wave; ++w) pos += s_wave_cnt[w];
+  int32_t* irow = kv_idx + row * nb;
+  for (int j = j0; j < j1; ++j) {
+    if (flag[j]) irow[pos++] = j;
+  }
+  if (mask != nullptr) {
+    uint8_t* mrow = mask + row * nb;
+    for (int j = tid; j < nb; j += kThreads) mrow[j] = flag[j];
+  }
+  if (tid == 0) kv_count[row] = m;
+}
+
+}  // namespace
+
+hipError_t launch_build_mask(const MaskArgs& a) {
+  uint32_t tau_bits;
+  __builtin_memcpy(&tau_bits, &a.tau, 4);
+  hipLaunchKernelGGL(build_mask_kernel, dim3(a.rows), dim3(kThreads), 0, a.stream, a.p_imp, a.nb,
+                     tau_bits, a.kv_count, a.kv_idx, a.mask);
+  return hipGetLastError();
+}
+
+}  // namespace dbs

@@ -1,0 +1,293 @@
+// Token reorder / inverse reorder / ASA_G mean-pool kernels (gfx950).
+//
+// Video-BLADE "Preprocessing": Q, K, V are gathered into curve (or cuboid)
+// order before they are cut into blocks; the attention output is scattered
+// back to token order afterwards.  Video-BLADE "Step 2.2 (2)": the global
+// tokens are means of n consecutive reordered tokens.
+//
+// All three are pure data movement and HBM-bound.  Each thread moves whole
+// 16-byte chunks; rows of one token are 2*d bytes contiguous on both sides,
+// so every wave touches a handful of contiguous 128-256 byte segments.
+#include "common.h"
+#include "../launch.h"
+
+namespace dbs {
+namespace {
+
+constexpr int kThreads = 256;
+
+// Permutation entries are clamped to [0, N) so that a malformed permutation
+// can never address outside the token buffers.
+__device__ __forceinline__ int clamp_tok(int p, int N) { return p < 0 ? 0 : (p >= N ? N - 1 : p); }
+
+template <typename T> struct Vec8;
+template <> struct Vec8<__bf16> {
+  uint4 v;
+  __device__ __forceinline__ void load(const __bf16* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void to_bf16(uint4& o) const { o = v; }
+};
+template <> struct Vec8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ __forceinline__ void to_bf16(uint4& o) const {
+    o.x = pack_bf16x2(a.x, a.y);
+    o.y = pack_bf16x2(a.z, a.w);
+    o.z = pack_bf16x2(b.x, b.y);
+    o.w = pack_bf16x2(b.z, b.w);
+  }
+};
+
+// y rows layout: y[b, h, i, :] = x[b, perm[i], h, :] (i < N), zero rows after N.
+// One workgroup covers 64 rows of one (b, h); D/8 threads per row.
+template <typename Tin, typename Tout, int D>
+__global__ __launch_bounds__(kThreads) void reorder_rows_kernel(
+    const Tin* __restrict__ x, int64_t sb, int64_t sn, int64_t sh, Tout* __restrict__ y,
+    const int32_t* __restrict__ perm, int perm_h_stride, int Hh, int N, int Npad) {
+  constexpr int kChunks = D / 8;
+  constexpr int kRowsPerPass = kThreads / kChunks;
+  constexpr int kRowsPerBlock = 64;
+  const int h = blockIdx.y, bi = blockIdx.z;
+  const int c = threadIdx.x % kChunks;
+  const int64_t ybase = ((int64_t)bi * Hh + h) * Npad;
+  const int32_t* ph = perm + (int64_t)h * perm_h_stride;
+#pragma unroll
+  for (int pass = 0; pass < kRowsPerBlock / kRowsPerPass; ++pass) {
+    const int i = blockIdx.x * kRowsPerBlock + pass * kRowsPerPass + threadIdx.x / kChunks;
+    if (i >= Npad) break;
+    Tout* dst = y + (ybase + i) * D + 8 * c;
+    if (i < N) {
+      const Tin* src = x + bi * sb + (int64_t)clamp_tok(ph[i], N) * sn + (int64_t)h * sh + 8 * c;
+      if constexpr (sizeof(Tin) == sizeof(Tout)) {
+        if constexpr (sizeof(Tin) == 2) {
+          *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+        } else {
+          reinterpret_cast<float4*>(dst)[0] = reinterpret_cast<const float4*>(src)[0];
+          reinterpret_cast<float4*>(dst)[1] = reinterpret_cast<const float4*>(src)[1];
+        }
+      } else {
+        Vec8<Tin> v;
+        v.load(src);
+        uint4 o;
+        v.to_bf16(o);
+        *reinterpret_cast<uint4*>(dst) = o;
+      }
+    } else {
+      if constexpr (sizeof(Tout) == 2) {
+        *reinterpret_cast<uint4*>(dst) = make_uint4(0, 0, 0, 0);
+      } else {
+        reinterpret_cast<float4*>(dst)[0] = make_float4(0, 0, 0, 0);
+        reinterpret_cast<float4*>(dst)[1] = make_float4(0, 0, 0, 0);
+      }
+    }
+  }
+}
+
+// y tiles-transposed layout: y[b, h, J, e, t] = x[b, perm[J*BLK + t], h, e].
+// One workgroup per (tile J, h, b); thread (c, tg) gathers an 8-token x
+// 8-channel block, transposes it in registers and writes 8 channel rows.
+template <typename Tin, int D, int BLK>
+__global__ __launch_bounds__((D / 8) * (BLK / 8)) void reorder_tiles_t_kernel(
+    const Tin* __restrict__ x, int64_t sb, int64_t sn, int64_t sh, __bf16* __restrict__ y,
+    const int32_t* __restrict__ perm, int perm_h_stride, int Hh, int N, int nb) {
+  const int J = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
+  const int c = threadIdx.x % (D / 8);   // channel chunk: channels 8c..8c+7
+  const int tg = threadIdx.x / (D / 8);  // token group: tokens 8tg..8tg+7 of the tile
+  const int32_t* ph = perm + (int64_t)h * perm_h_stride;
+  uint32_t w[8][4];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int i = J * BLK + 8 * tg + e;
+    uint4 o = make_uint4(0, 0, 0, 0);
+    if (i < N) {
+      Vec8<Tin> v;
+      v.load(x + bi * sb + (int64_t)clamp_tok(ph[i], N) * sn + (int64_t)h * sh + 8 * c);
+      v.to_bf16(o);
+    }
+    w[e][0] = o.x; w[e][1] = o.y; w[e][2] = o.z; w[e][3] = o.w;
+  }
+  __bf16* tile = y + (((int64_t)bi * Hh + h) * nb + J) * (int64_t)(D * BLK);
+#pragma unroll
+  for (int ch = 0; ch < 8; ++ch) {
+    // channel 8c+ch of tokens 8tg..8tg+7: half `ch & 1` of word ch/2 of each token
+    uint32_t o[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t lo = w[2 * p][ch >> 1], hi = w[2 * p + 1][ch >> 1];
+      o[p] = (ch & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+    }
+    *reinterpret_cast<uint4*>(tile + (int64_t)(8 * c + ch) * BLK + 8 * tg) =
+        make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// x[b, perm[i], h, :] = y[b, h, i, :] for i < N (y rows layout, bf16).
+template <typename Tout, int D>
+__global__ __launch_bounds__(kThreads) void inverse_rows_kernel(
+    const __bf16* __restrict__ y, Tout* __restrict__ x, int64_t sb, int64_t sn, int64_t sh,
+    const int32_t* __restrict__ perm, int perm_h_stride, int Hh, int N, int Npad) {
+  constexpr int kChunks = D / 8;
+  constexpr int kRowsPerPass = kThreads / kChunks;
+  constexpr int kRowsPerBlock = 64;
+  const int h = blockIdx.y, bi = blockIdx.z;
+  const int c = threadIdx.x % kChunks;
+  const int64_t ybase = ((int64_t)bi * Hh + h) * Npad;
+  const int32_t* ph = perm + (int64_t)h * perm_h_stride;
+#pragma unroll
+  for (int pass = 0; pass < kRowsPerBlock / kRowsPerPass; ++pass) {
+    const int i = blockIdx.x * kRowsPerBlock + pass * kRowsPerPass + threadIdx.x / kChunks;
+    if (i >= N) break;
+    const uint4 v = *reinterpret_cast<const uint4*>(y + (ybase + i) * D + 8 * c);
+    Tout* dst = x + bi * sb + (int64_t)clamp_tok(ph[i], N) * sn + (int64_t)h * sh + 8 * c;
+    if constexpr (sizeof(Tout) == 2) {
+      *reinterpret_cast<uint4*>(dst) = v;
+    } else {
+      reinterpret_cast<float4*>(dst)[0] = make_float4(bf16_bits_to_f32(v.x & 0xffffu), bf16_bits_to_f32(v.x >> 16),
+                                                      bf16_bits_to_f32(v.y & 0xffffu), bf16_bits_to_f32(v.y >> 16));
+      reinterpret_cast<float4*>(dst)[1] = make_float4(bf16_bits_to_f32(v.z & 0xffffu), bf16_bits_to_f32(v.z >> 16),
+                                                      bf16_bits_to_f32(v.w & 0xffffu), bf16_bits_to_f32(v.w >> 16));
+    }
+  }
+}
+
+// Global K tokens: k_g[b, h, g, :] = mean of rows g*n .. g*n+r-1 (rows layout).
+template <int D>
+__global__ __launch_bounds__(kThreads) void meanpool_k_kernel(
+    const __bf16* __restrict__ k_r, __bf16* __restrict__ k_g, int Hh, int N, int Npad, int n,
+    int Ng, int Ngpad) {
+  constexpr int kChunks = D / 8;
+  const int h = blockIdx.y, bi = blockIdx.z;
+  const int g = blockIdx.x * (kThreads / kChunks) + threadIdx.x / kChunks;
+  const int c = threadIdx.x % kChunks;
+  if (g >= Ngpad) return;
+  const int64_t bh = (int64_t)bi * Hh + h;
+  uint4 o = make_uint4(0, 0, 0, 0);
+  if (g < Ng) {
+    const int r = min(n, N - g * n);
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int e = 0; e < r; ++e) {
+      const uint4 v = *reinterpret_cast<const uint4*>(k_r + (bh * Npad + (int64_t)g * n + e) * D + 8 * c);
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += bf16_bits_to_f32(wv[q] & 0xffffu);
+        acc[2 * q + 1] += bf16_bits_to_f32(wv[q] >> 16);
+      }
+    }
+    const float fr = (float)r;
+    o.x = pack_bf16x2(acc[0] / fr, acc[1] / fr);
+    o.y = pack_bf16x2(acc[2] / fr, acc[3] / fr);
+    o.z = pack_bf16x2(acc[4] / fr, acc[5] / fr);
+    o.w = pack_bf16x2(acc[6] / fr, acc[7] / fr);
+  }
+  *reinterpret_cast<uint4*>(k_g + (bh * Ngpad + g) * D + 8 * c) = o;
+}
+
+// Global V tokens from the tiles-transposed V: thread per (g, channel e).
+template <int D, int BLK>
+__global__ __launch_bounds__(kThreads) void meanpool_v_kernel(
+    const __bf16* __restrict__ v_t, __bf16* __restrict__ v_g, int Hh, int N, int nb, int n,
+    int Ng, int Ngpad) {
+  const int h = blockIdx.y, bi = blockIdx.z;
+  const int idx = blockIdx.x * kThreads + threadIdx.x;   // over Ngpad * D, g fastest
+  if (idx >= Ngpad * D) return;
+  const int g = idx % Ngpad, e = idx / Ngpad;
+  const int64_t bh = (int64_t)bi * Hh + h;
+  float acc = 0.f;
+  if (g < Ng) {
+    const int r = min(n, N - g * n);
+    const uint16_t* base = reinterpret_cast<const uint16_t*>(v_t) + bh * (int64_t)nb * D * BLK;
+    for (int t = 0; t < r; ++t) {
+      const int i = g * n + t;
+      acc += bf16_bits_to_f32(base[(int64_t)(i / BLK) * D * BLK + (int64_t)e * BLK + (i % BLK)]);
+    }
+    acc = acc / (float)r;
+  }
+  const int ngt = Ngpad / BLK;
+  uint16_t* out = reinterpret_cast<uint16_t*>(v_g) + bh * (int64_t)ngt * D * BLK;
+  out[(int64_t)(g / BLK) * D * BLK + (int64_t)e * BLK + (g % BLK)] =
+      (uint16_t)(g < Ng ? f32_to_bf16_bits(acc) : 0u);
+}
+
+template <typename Tin, typename Tout, int D>
+hipError_t launch_rows(const ReorderArgs& a) {
+  dim3 grid((a.Npad + 63) / 64, a.Hh, a.B);
+  hipLaunchKernelGGL((reorder_rows_kernel<Tin, Tout, D>), grid, dim3(kThreads), 0, a.stream,
+                     (const Tin*)a.x, a.sb, a.sn, a.sh, (Tout*)a.y, a.perm, a.perm_h_stride, a.Hh,
+                     a.N, a.Npad);
+  return hipGetLastError();
+}
+
+template <typename Tin, int D, int BLK>
+hipError_t launch_tiles(const ReorderArgs& a) {
+  dim3 grid(a.Npad / BLK, a.Hh, a.B);
+  hipLaunchKernelGGL((reorder_tiles_t_kernel<Tin, D, BLK>), grid, dim3((D / 8) * (BLK / 8)), 0,
+                     a.stream, (const Tin*)a.x, a.sb, a.sn, a.sh, (__bf16*)a.y, a.perm,
+                     a.perm_h_stride, a.Hh, a.N, a.Npad / BLK);
+  return hipGetLastError();
+}
+
+template <typename Tin, int D>
+hipError_t dispatch_tiles_b(const ReorderArgs& a) {
+  return a.b == 64 ? launch_tiles<Tin, D, 64>(a) : launch_tiles<Tin, D, 128>(a);
+}
+
+template <int D>
+hipError_t dispatch_reorder_d(const ReorderArgs& a) {
+  const bool in_f32 = a.x_f32, out_f32 = a.y_f32;
+  if (a.tiles_t) return in_f32 ? dispatch_tiles_b<float, D>(a) : dispatch_tiles_b<__bf16, D>(a);
+  if (in_f32 && out_f32) return launch_rows<float, float, D>(a);
+  if (in_f32) return launch_rows<float, __bf16, D>(a);
+  return launch_rows<__bf16, __bf16, D>(a);
+}
+
+template <int D>
+hipError_t dispatch_inverse_d(const ReorderArgs& a) {
+  dim3 grid((a.Npad + 63) / 64, a.Hh, a.B);
+  if (a.x_f32) {
+    hipLaunchKernelGGL((inverse_rows_kernel<float, D>), grid, dim3(kThreads), 0, a.stream,
+                       (const __bf16*)a.y, (float*)a.x_out, a.sb, a.sn, a.sh, a.perm,
+                       a.perm_h_stride, a.Hh, a.N, a.Npad);
+  } else {
+    hipLaunchKernelGGL((inverse_rows_kernel<__bf16, D>), grid, dim3(kThreads), 0, a.stream,
+                       (const __bf16*)a.y, (__bf16*)a.x_out, a.sb, a.sn, a.sh, a.perm,
+                       a.perm_h_stride, a.Hh, a.N, a.Npad);
+  }
+  return hipGetLastError();
+}
+
+template <int D, int BLK>
+hipError_t launch_meanpool(const MeanpoolArgs& a) {
+  const int Ngpad = (a.Ng + BLK - 1) / BLK * BLK;
+  {
+    dim3 grid((Ngpad + (kThreads / (D / 8)) - 1) / (kThreads / (D / 8)), a.Hh, a.B);
+    hipLaunchKernelGGL((meanpool_k_kernel<D>), grid, dim3(kThreads), 0, a.stream,
+                       (const __bf16*)a.k_r, (__bf16*)a.k_g, a.Hh, a.N, a.Npad, a.n, a.Ng, Ngpad);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid((Ngpad * D + kThreads - 1) / kThreads, a.Hh, a.B);
+  hipLaunchKernelGGL((meanpool_v_kernel<D, BLK>), grid, dim3(kThreads), 0, a.stream,
+                     (const __bf16*)a.v_t, (__bf16*)a.v_g, a.Hh, a.N, a.Npad / BLK, a.n, a.Ng,
+                     Ngpad);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_reorder(const ReorderArgs& a) {
+  return a.d == 64 ? dispatch_reorder_d<64>(a) : dispatch_reorder_d<128>(a);
+}
+
+hipError_t launch_inverse_reorder(const ReorderArgs& a) {
+  return a.d == 64 ? dispatch_inverse_d<64>(a) : dispatch_inverse_d<128>(a);
+}
+
+hipError_t launch_meanpool(const MeanpoolArgs& a) {
+  if (a.d == 64) return a.b == 64 ? launch_meanpool<64, 64>(a) : launch_meanpool<64, 128>(a);
+  return a.b == 64 ? launch_meanpool<128, 64>(a) : launch_meanpool<128, 128>(a);
+}
+
+}  // namespace dbs

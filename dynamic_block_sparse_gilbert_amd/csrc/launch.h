@@ -1,0 +1,74 @@
+// Internal launch interface between the C ABI layer (api.cpp) and the kernel
+// translation units.  Arguments here are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dbs {
+
+struct ReorderArgs {
+  const void* x;        // reorder: source [B, N, Hh, d] strided
+  void* y;              // reorder: destination; inverse: source (rows)
+  void* x_out;          // inverse: destination [B, N, Hh, d] strided
+  int64_t sb, sn, sh;
+  const int32_t* perm;
+  int perm_h_stride;    // 0 (shared) or N (per head)
+  int B, Hh, N, Npad, d, b;
+  bool x_f32, y_f32, tiles_t;
+  hipStream_t stream;
+};
+
+struct MeanpoolArgs {
+  const void* k_r;
+  const void* v_t;
+  void* k_g;
+  void* v_g;
+  int B, Hh, N, Npad, d, b, n, Ng;
+  hipStream_t stream;
+};
+
+struct EstimateArgs {
+  const void* q_r;
+  const void* k_r;
+  float* p_imp;
+  float* lse2;          // workspace: one float per sampled query slot
+  int B, Hh, N, Npad, d, b, k, nb;
+  float scale;
+  hipStream_t stream;
+};
+
+struct MaskArgs {
+  const float* p_imp;
+  int32_t* kv_count;
+  int32_t* kv_idx;
+  uint8_t* mask;
+  int rows, nb;
+  float tau;
+  hipStream_t stream;
+};
+
+struct AttnArgs {
+  const void* q_r;
+  const void* k_r;
+  const void* v_t;
+  const int32_t* kv_count;
+  const int32_t* kv_idx;
+  const void* k_g;
+  const void* v_g;
+  void* o_r;
+  float* lse;
+  int B, Hh, N, Npad, d, b, nb, Ng, n_pool;
+  float scale;
+  hipStream_t stream;
+};
+
+hipError_t launch_reorder(const ReorderArgs& a);
+hipError_t launch_inverse_reorder(const ReorderArgs& a);
+hipError_t launch_meanpool(const MeanpoolArgs& a);
+hipError_t launch_estimate(const EstimateArgs& a);
+hipError_t launch_build_mask(const MaskArgs& a);
+hipError_t launch_attn_fwd(const AttnArgs& a);
+
+}  // namespace dbs

@@ -1,0 +1,118 @@
+"""One ASA / ASA_G attention layer on the GPU, composed from the C-ABI calls.
+
+Video-BLADE: "Preprocessing" (reorder), "Step 1" (estimate), "Step 2.1"
+(mask), "Step 2.2" (block-sparse attention, optional global tokens), then the
+output goes back to token order.  Buffers are allocated once per shape and
+reused; permutations are built on the host by the library and uploaded once.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Dict, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+from . import ops
+
+
+@dataclass
+class LayerSpec:
+    T: int
+    H: int
+    W: int
+    heads: int
+    d: int
+    b: int = 128
+    k: int = 16
+    tau: float = 0.9
+    prefix: int = 0                     # text tokens before the video tokens (identity order)
+    order: str = "gilbert"              # "gilbert", "cuboid", "cuboid_per_head", "identity"
+    cuboid: Optional[Tuple[int, int, int]] = None
+    cuboids: Optional[Sequence[Tuple[int, int, int]]] = None   # per head (cuboid_per_head)
+    n_pool: int = 0                     # ASA_G window; 0 = plain ASA
+    batch: int = 1
+
+    @property
+    def N(self) -> int:
+        return self.prefix + self.T * self.H * self.W
+
+    @property
+    def nb(self) -> int:
+        return -(-self.N // self.b)
+
+    @property
+    def Npad(self) -> int:
+        return self.nb * self.b
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+def build_perm(spec: LayerSpec) -> np.ndarray:
+    """Host permutation: int32 [N] or [heads, N]."""
+    if spec.order == "gilbert":
+        return ops.perm_gilbert3d(spec.T, spec.H, spec.W, spec.prefix)
+    if spec.order == "cuboid":
+        return ops.perm_cuboid(spec.T, spec.H, spec.W, *spec.cuboid, prefix=spec.prefix)
+    if spec.order == "cuboid_per_head":
+        return np.stack([ops.perm_cuboid(spec.T, spec.H, spec.W, *c, prefix=spec.prefix) for c in spec.cuboids])
+    if spec.order == "identity":
+        return np.arange(spec.N, dtype=np.int32)
+    raise ValueError(spec.order)
+
+
+class AsaLayer:
+    """Holds the device permutation and the intermediate buffers of one layer shape."""
+
+    def __init__(self, spec: LayerSpec, device="cuda"):
+        self.spec = spec
+        self.device = torch.device(device)
+        self.perm = torch.from_numpy(build_perm(spec)).to(self.device)
+        s = spec
+        B, Hh, Npad, d, nb = s.batch, s.heads, s.Npad, s.d, s.nb
+        bf = dict(dtype=torch.bfloat16, device=self.device)
+        self.q_r = torch.empty((B, Hh, Npad, d), **bf)
+        self.k_r = torch.empty((B, Hh, Npad, d), **bf)
+        self.v_t = torch.empty((B, Hh, nb, d, s.b), **bf)
+        self.o_r = torch.empty((B, Hh, Npad, d), **bf)
+        self.p_imp = torch.empty((B, Hh, nb, nb), dtype=torch.float32, device=self.device)
+        self.ws = torch.empty(max(16, ops.estimate_workspace_bytes(B, Hh, s.N, s.b, s.k)),
+                              dtype=torch.uint8, device=self.device)
+        self.kv_count = torch.empty((B, Hh, nb), dtype=torch.int32, device=self.device)
+        self.kv_idx = torch.empty((B, Hh, nb, nb), dtype=torch.int32, device=self.device)
+        self.k_g = self.v_g = None
+        self.Ng = 0
+        if s.n_pool:
+            self.Ng = -(-s.N // s.n_pool)
+            Ngpad = -(-self.Ng // s.b) * s.b
+            self.k_g = torch.empty((B, Hh, Ngpad, d), **bf)
+            self.v_g = torch.empty((B, Hh, Ngpad // s.b, d, s.b), **bf)
+
+    def prepare(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> None:
+        """Reorder (and pool) the inputs; q, k, v are [B, N, Hh, d]."""
+        s = self.spec
+        ops.reorder(q, self.perm, s.Npad, s.b, "rows", y=self.q_r)
+        ops.reorder(k, self.perm, s.Npad, s.b, "rows", y=self.k_r)
+        ops.reorder(v, self.perm, s.Npad, s.b, "tiles_t", y=self.v_t)
+        if s.n_pool:
+            ops.meanpool_kv(self.k_r, self.v_t, s.N, s.b, s.n_pool, k_g=self.k_g, v_g=self.v_g)
+
+    def mask(self, tau: Optional[float] = None) -> None:
+        s = self.spec
+        ops.estimate_blocks(self.q_r, self.k_r, s.N, s.b, s.k, s.scale, p_imp=self.p_imp, workspace=self.ws)
+        ops.build_mask(self.p_imp, s.tau if tau is None else tau, kv_count=self.kv_count, kv_idx=self.kv_idx)
+
+    def attend(self, out: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16) -> torch.Tensor:
+        s = self.spec
+        ops.sparse_attn_fwd(self.q_r, self.k_r, self.v_t, s.N, s.b, s.scale, self.kv_count, self.kv_idx,
+                            self.k_g, self.v_g, self.Ng, s.n_pool, o_r=self.o_r)
+        return ops.inverse_reorder(self.o_r, self.perm, s.N, out=out, out_dtype=out_dtype)
+
+    def forward(self, q, k, v, out: Optional[torch.Tensor] = None, tau: Optional[float] = None,
+                out_dtype=torch.bfloat16) -> torch.Tensor:
+        self.prepare(q, k, v)
+        self.mask(tau)
+        return self.attend(out, out_dtype)

@@ -1,0 +1,171 @@
+"""Python binding of the C ABI: one wrapper per entry point, same names.
+
+The wrappers only marshal arguments: they read data_ptr(), strides and the
+current HIP stream from torch tensors, allocate outputs with torch when the
+caller does not pass them, and call the library.  Every step of the
+computation runs in the library's kernels.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+from ._lib import DBS_BF16, DBS_FP32, DBS_ROWS, DBS_TILES_T, check, lib
+
+_DT = {torch.bfloat16: DBS_BF16, torch.float32: DBS_FP32}
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("device tensors required")
+
+
+def _stream() -> C.c_void_p:
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _p(t: Optional[torch.Tensor]) -> C.c_void_p:
+    return C.c_void_p(0 if t is None else t.data_ptr())
+
+
+# ---------------------------------------------------------------------------- host
+
+
+def perm_gilbert3d(T: int, H: int, W: int, prefix: int = 0) -> np.ndarray:
+    out = np.empty(prefix + T * H * W, dtype=np.int32)
+    check("dbs_perm_gilbert3d", lib().dbs_perm_gilbert3d(T, H, W, prefix, out.ctypes.data))
+    return out
+
+
+def perm_cuboid(T: int, H: int, W: int, ct: int, ch: int, cw: int, prefix: int = 0) -> np.ndarray:
+    out = np.empty(prefix + T * H * W, dtype=np.int32)
+    check("dbs_perm_cuboid", lib().dbs_perm_cuboid(T, H, W, ct, ch, cw, prefix, out.ctypes.data))
+    return out
+
+
+def perm_invert(perm: np.ndarray) -> np.ndarray:
+    p = np.ascontiguousarray(perm, dtype=np.int32)
+    out = np.empty_like(p)
+    check("dbs_perm_invert", lib().dbs_perm_invert(p.ctypes.data, p.size, out.ctypes.data))
+    return out
+
+
+# --------------------------------------------------------------------------- device
+
+
+def reorder(x: torch.Tensor, perm: torch.Tensor, Npad: int, b: int, layout: str = "rows",
+            out_dtype: torch.dtype = torch.bfloat16, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x [B, N, Hh, d] (any strides, d contiguous) -> y rows [B, Hh, Npad, d] or tiles [B, Hh, Npad/b, d, b]."""
+    _dev(x, perm)
+    B, N, Hh, d = x.shape
+    if x.stride(3) != 1:
+        raise ValueError("the d axis of x must be contiguous")
+    lay = {"rows": DBS_ROWS, "tiles_t": DBS_TILES_T}[layout]
+    if y is None:
+        shape = (B, Hh, Npad, d) if lay == DBS_ROWS else (B, Hh, Npad // b, d, b)
+        y = torch.empty(shape, dtype=out_dtype, device=x.device)
+    per_head = 1 if perm.dim() == 2 else 0
+    check("dbs_reorder", lib().dbs_reorder(
+        _p(x), _dt(x), x.stride(0), x.stride(1), x.stride(2), _p(y), _dt(y), lay, _p(perm), per_head,
+        B, Hh, N, Npad, d, b, _stream()))
+    return y
+
+
+def inverse_reorder(y: torch.Tensor, perm: torch.Tensor, N: int,
+                    out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """y rows [B, Hh, Npad, d] bf16 -> out [B, N, Hh, d] (out may be a strided view)."""
+    _dev(y, perm, out)
+    B, Hh, Npad, d = y.shape
+    if out is None:
+        out = torch.empty((B, N, Hh, d), dtype=out_dtype, device=y.device)
+    if out.stride(3) != 1:
+        raise ValueError("the d axis of out must be contiguous")
+    per_head = 1 if perm.dim() == 2 else 0
+    check("dbs_inverse_reorder", lib().dbs_inverse_reorder(
+        _p(y), _dt(y), _p(out), _dt(out), out.stride(0), out.stride(1), out.stride(2), _p(perm), per_head,
+        B, Hh, N, Npad, d, _stream()))
+    return out
+
+
+def estimate_workspace_bytes(B: int, Hh: int, N: int, b: int, k: int) -> int:
+    return int(lib().dbs_estimate_workspace_bytes(B, Hh, N, b, k))
+
+
+def estimate_blocks(q_r: torch.Tensor, k_r: torch.Tensor, N: int, b: int, k: int, scale: float,
+                    p_imp: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """q_r, k_r rows [B, Hh, Npad, d] -> p_imp float32 [B, Hh, nb, nb]."""
+    _dev(q_r, k_r, p_imp, workspace)
+    B, Hh, Npad, d = q_r.shape
+    nb = Npad // b
+    if p_imp is None:
+        p_imp = torch.empty((B, Hh, nb, nb), dtype=torch.float32, device=q_r.device)
+    need = estimate_workspace_bytes(B, Hh, N, b, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_r.device)
+    check("dbs_estimate_blocks", lib().dbs_estimate_blocks(
+        _p(q_r), _p(k_r), _dt(q_r), B, Hh, N, Npad, d, b, k, float(scale), _p(p_imp), _p(workspace),
+        workspace.numel() * workspace.element_size(), _stream()))
+    return p_imp
+
+
+def build_mask(p_imp: torch.Tensor, tau: float, kv_count: Optional[torch.Tensor] = None,
+               kv_idx: Optional[torch.Tensor] = None, want_mask: bool = False,
+               mask: Optional[torch.Tensor] = None):
+    """p_imp [B, Hh, nb, nb] float32 -> (kv_count [B, Hh, nb], kv_idx [B, Hh, nb, nb], mask or None)."""
+    _dev(p_imp, kv_count, kv_idx, mask)
+    B, Hh, nb, _ = p_imp.shape
+    if kv_count is None:
+        kv_count = torch.empty((B, Hh, nb), dtype=torch.int32, device=p_imp.device)
+    if kv_idx is None:
+        kv_idx = torch.empty((B, Hh, nb, nb), dtype=torch.int32, device=p_imp.device)
+    if want_mask and mask is None:
+        mask = torch.empty((B, Hh, nb, nb), dtype=torch.uint8, device=p_imp.device)
+    check("dbs_build_mask", lib().dbs_build_mask(
+        _p(p_imp), B, Hh, nb, float(tau), _p(kv_count), _p(kv_idx), _p(mask), _stream()))
+    return kv_count, kv_idx, mask
+
+
+def meanpool_kv(k_r: torch.Tensor, v_t: torch.Tensor, N: int, b: int, n: int,
+                k_g: Optional[torch.Tensor] = None, v_g: Optional[torch.Tensor] = None
+                ) -> Tuple[torch.Tensor, torch.Tensor, int]:
+    """k_r rows, v_t tiles -> (k_g rows [B,Hh,Ngpad,d], v_g tiles [B,Hh,Ngpad/b,d,b], Ng)."""
+    _dev(k_r, v_t, k_g, v_g)
+    B, Hh, Npad, d = k_r.shape
+    Ng = -(-N // n)
+    Ngpad = -(-Ng // b) * b
+    if k_g is None:
+        k_g = torch.empty((B, Hh, Ngpad, d), dtype=torch.bfloat16, device=k_r.device)
+    if v_g is None:
+        v_g = torch.empty((B, Hh, Ngpad // b, d, b), dtype=torch.bfloat16, device=k_r.device)
+    check("dbs_meanpool_kv", lib().dbs_meanpool_kv(
+        _p(k_r), _p(v_t), _dt(k_r), B, Hh, N, Npad, d, b, n, _p(k_g), _p(v_g), _stream()))
+    return k_g, v_g, Ng
+
+
+def sparse_attn_fwd(q_r: torch.Tensor, k_r: torch.Tensor, v_t: torch.Tensor, N: int, b: int, scale: float,
+                    kv_count: torch.Tensor, kv_idx: torch.Tensor,
+                    k_g: Optional[torch.Tensor] = None, v_g: Optional[torch.Tensor] = None,
+                    Ng: int = 0, n_pool: int = 0, o_r: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, want_lse: bool = False):
+    """Returns (o_r rows [B, Hh, Npad, d] bf16, lse float32 [B, Hh, Npad] or None)."""
+    _dev(q_r, k_r, v_t, kv_count, kv_idx, k_g, v_g, o_r, lse)
+    B, Hh, Npad, d = q_r.shape
+    if o_r is None:
+        o_r = torch.empty_like(q_r)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hh, Npad), dtype=torch.float32, device=q_r.device)
+    check("dbs_sparse_attn_fwd", lib().dbs_sparse_attn_fwd(
+        _p(q_r), _p(k_r), _p(v_t), _dt(q_r), B, Hh, N, Npad, d, b, float(scale), _p(kv_count), _p(kv_idx),
+        _p(k_g), _p(v_g), int(Ng), int(n_pool), _p(o_r), _p(lse), _stream()))
+    return o_r, lse

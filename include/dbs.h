@@ -1,0 +1,189 @@
+/*
+ * dbs.h -- content-adaptive block-sparse attention (ASA / ASA_G), forward pass,
+ *          for AMD Instinct MI355X (gfx950).  C ABI, version 1.
+ *
+ * The method: Video-BLADE ("Preprocessing", "Step 1", "Step 2.1", "Step 2.2")
+ * and the BLADE notes (key designs 1 and 2).  A layer runs, on one stream:
+ *
+ *   dbs_reorder(Q), dbs_reorder(K), dbs_reorder(V)     tokens -> curve order
+ *   [dbs_meanpool_kv]                                  ASA_G global tokens
+ *   dbs_estimate_blocks                                sampled block importance
+ *   dbs_build_mask                                     cumulative-threshold mask
+ *   dbs_sparse_attn_fwd                                attention over kept tiles
+ *   dbs_inverse_reorder(O)                             back to token order
+ *
+ * Conventions for every call:
+ * - Device pointers are allocated and owned by the caller and must be 16-byte
+ *   aligned.  The library allocates no device memory and keeps no device state.
+ * - Device calls are asynchronous on the given stream (NULL: the default
+ *   stream) and never synchronise.  Arguments are checked on the host before
+ *   any launch; a failed check launches nothing.
+ * - The status is returned directly; dbs_last_error() describes the last
+ *   failure of the calling thread.  No C++ exception crosses the ABI.
+ * - B batch, Hh heads, N true tokens, Npad = N rounded up to a multiple of
+ *   the block size b, d head dimension, nb = Npad / b blocks.
+ *
+ * Tensor layouts (all contiguous unless strides are given):
+ *   DBS_ROWS     [B, Hh, Npad, d]            one token per row
+ *   DBS_TILES_T  [B, Hh, Npad / b, d, b]     each b-token tile stored d-major
+ *                                            (token index fastest); used for V
+ *                                            so that the P*V product reads
+ *                                            consecutive keys of one channel.
+ */
+#ifndef DBS_H
+#define DBS_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DBS_ABI_VERSION 1
+
+typedef enum {
+  DBS_OK = 0,
+  DBS_ERR_INVALID_ARG = -1,  /* null pointer, bad size or range            */
+  DBS_ERR_UNSUPPORTED = -2,  /* valid but not implemented (d, b, k, dtype) */
+  DBS_ERR_ALIGNMENT = -3,    /* a device pointer is not 16-byte aligned    */
+  DBS_ERR_LAUNCH = -4,       /* the kernel launch failed                   */
+  DBS_ERR_HIP = -5           /* another HIP runtime call failed            */
+} dbs_status;
+
+typedef enum { DBS_BF16 = 0, DBS_FP32 = 1 } dbs_dtype;
+typedef enum { DBS_ROWS = 0, DBS_TILES_T = 1 } dbs_layout;
+
+/* ABI version of the loaded library (DBS_ABI_VERSION). */
+int dbs_abi_version(void);
+
+/* Message for the calling thread's last failed call; "" if none.  Valid until
+ * that thread's next call. */
+const char* dbs_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Host permutation helpers (shape only; no device work).
+ *
+ * perm[new] = old: position `new` of the reordered sequence holds raster
+ * token `old` = prefix + (t * H + h) * W + w.  Positions < prefix (text
+ * tokens) stay in place.  perm_out must hold prefix + T*H*W entries.
+ * ------------------------------------------------------------------------- */
+
+/* Gilbert (generalised Hilbert) curve over the T x H x W latent grid, the
+ * locality-preserving order of Video-BLADE "Preprocessing".  The pages name the
+ * curve without defining it; the recursion implemented is a corner-to-corner
+ * walk that splits the box along its long side, or into a three-piece "U"
+ * across the plane of its two longest sides; every step moves to a grid
+ * neighbour.  Errors: INVALID_ARG if a side < 1, prefix < 0, perm_out NULL, or
+ * the length exceeds INT32_MAX. */
+dbs_status dbs_perm_gilbert3d(int T, int H, int W, int prefix, int32_t* perm_out);
+
+/* Cuboid-major order (Bidirectional Sparse Attention notes, "overall
+ * framework"; VEDA key design 2 for per-head shapes): cuboids of
+ * ct x ch x cw in raster order, raster order inside each cuboid; border
+ * cuboids hold fewer tokens.  Errors as above. */
+dbs_status dbs_perm_cuboid(int T, int H, int W, int ct, int ch, int cw, int prefix,
+                           int32_t* perm_out);
+
+/* inv_out[perm[i]] = i.  INVALID_ARG if perm is not a permutation of 0..n-1. */
+dbs_status dbs_perm_invert(const int32_t* perm, int n, int32_t* inv_out);
+
+/* ---------------------------------------------------------------------------
+ * Device calls.
+ * ------------------------------------------------------------------------- */
+
+/* Reorder tokens into curve / cuboid order (Video-BLADE "Preprocessing").
+ *   y[b, h, i, :] = x[b, perm_h[i], h, :]  for i < N;  rows N..Npad-1 = 0.
+ * x: element type x_dt, element strides (sb, sn, sh) for (batch, token, head);
+ *    the d channels contiguous.
+ * y: element type y_dt (DBS_FP32 -> DBS_BF16 rounds to nearest even; the
+ *    reverse is not offered), layout y_layout (DBS_TILES_T tiles of b tokens).
+ * perm: device int32, [N] for all heads (perm_per_head = 0) or [Hh, N], a
+ *    permutation of 0..N-1 (entries outside [0, N) are clamped into it, which
+ *    keeps every access in bounds but is not a meaningful result).
+ * Supported: d in {64, 128}; b in {64, 128}; Npad % b == 0; N <= Npad. */
+dbs_status dbs_reorder(const void* x, dbs_dtype x_dt, int64_t sb, int64_t sn, int64_t sh,
+                       void* y, dbs_dtype y_dt, dbs_layout y_layout,
+                       const int32_t* perm, int perm_per_head,
+                       int B, int Hh, int N, int Npad, int d, int b, hipStream_t stream);
+
+/* Inverse of dbs_reorder for the attention output:
+ *   x[b, perm_h[i], h, :] = y[b, h, i, :]  for i < N.
+ * y: DBS_ROWS, element type y_dt; x: element type x_dt with strides
+ * (sb, sn, sh).  DBS_BF16 -> DBS_FP32 widens exactly.  perm as for
+ * dbs_reorder (entries clamped into [0, N)). */
+dbs_status dbs_inverse_reorder(const void* y, dbs_dtype y_dt, void* x, dbs_dtype x_dt,
+                               int64_t sb, int64_t sn, int64_t sh,
+                               const int32_t* perm, int perm_per_head,
+                               int B, int Hh, int N, int Npad, int d, hipStream_t stream);
+
+/* Bytes of device workspace dbs_estimate_blocks needs (one float per sampled
+ * query: B * Hh * nb * k * 4).  Returns 0 for invalid sizes. */
+size_t dbs_estimate_workspace_bytes(int B, int Hh, int N, int b, int k);
+
+/* Block-importance estimation (Video-BLADE "Step 1"; BLADE notes key design 1).
+ * From every b-token block J, k_J = min(k, L_J) tokens are sampled at offsets
+ * floor(t * L_J / k_J), t < k_J (L_J = valid tokens of block J), in Q and K
+ * alike.  P_approx = row-softmax(Q_s K_s^T * scale) over all sampled keys of
+ * the (batch, head); p_imp[b, h, I, J] = max of P_approx over (samples of I) x
+ * (samples of J), float32, [B, Hh, nb, nb].
+ * q_r, k_r: DBS_ROWS, type dt (DBS_BF16 only).  k: a power of two, 1..b.
+ * workspace: device, >= dbs_estimate_workspace_bytes(...) bytes; its contents
+ * on entry do not matter.  Errors: UNSUPPORTED for d, b, k or dt outside the
+ * supported set; INVALID_ARG for a small workspace. */
+dbs_status dbs_estimate_blocks(const void* q_r, const void* k_r, dbs_dtype dt,
+                               int B, int Hh, int N, int Npad, int d, int b, int k, float scale,
+                               float* p_imp, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* Cumulative-threshold mask (Video-BLADE "Step 2.1").  For every row
+ * (b, h, I): order the blocks by p_imp value descending, then index
+ * ascending, and keep the fewest m >= 1 whose exact sum reaches
+ * tau * (exact row sum); tau >= 1 keeps all nb.  The sums are exact (every
+ * float32 is an exact rational), so the result does not depend on summation
+ * order.  A row holding a value outside [0, 1] or NaN keeps every block.
+ * kv_count[b, h, I] = m; kv_idx[b, h, I, 0..m-1] = kept blocks ascending
+ * (entries m..nb-1 are left untouched); mask (nullable) [B, Hh, nb, nb]
+ * uint8 1 for kept, 0 otherwise.  tau must be in (0, 1].  nb <= 4096. */
+dbs_status dbs_build_mask(const float* p_imp, int B, int Hh, int nb, float tau,
+                          int32_t* kv_count, int32_t* kv_idx, uint8_t* mask,
+                          hipStream_t stream);
+
+/* ASA_G global tokens (Video-BLADE "Step 2.2 (2)"; BLADE notes key design 2):
+ * mean of each window of n consecutive reordered tokens,
+ *   k_g[b, h, g, :] = mean(k_r[b, h, g*n .. g*n + r_g - 1, :]),
+ *   r_g = min(n, N - g*n),  g < Ng = ceil(N / n),  likewise v_g,
+ * accumulated in float32 and rounded to bf16.
+ * k_r: DBS_ROWS; v_r: DBS_TILES_T (tiles of b).  k_g: DBS_ROWS
+ * [B, Hh, Ngpad, d]; v_g: DBS_TILES_T [B, Hh, Ngpad / b, d, b] with
+ * Ngpad = ceil(Ng / b) * b; rows Ng..Ngpad-1 are written as zeros. */
+dbs_status dbs_meanpool_kv(const void* k_r, const void* v_r, dbs_dtype dt,
+                           int B, int Hh, int N, int Npad, int d, int b, int n,
+                           void* k_g, void* v_g, hipStream_t stream);
+
+/* Block-sparse attention forward (Video-BLADE "Step 2.2").  For every query
+ * row q < N of query block I:
+ *   O_q = sum_c softmax_c(s_qc) V_c,  s_qc = scale * q . k_c
+ * over the tokens c < N of the kept blocks kv_idx[b, h, I, 0..m-1]
+ * (m = kv_count[b, h, I]), and, when k_g != NULL (ASA_G), over all Ng global
+ * tokens with s = scale * q . k_g + ln(r_g), r_g = min(n_pool, N - g*n_pool).
+ * Scores and the softmax are float32; the probabilities are rounded to bf16
+ * for the P*V product (float32 accumulation).  Rows with no key at all get
+ * O = 0 and lse = -inf.
+ * q_r, k_r: DBS_ROWS bf16; v_r: DBS_TILES_T bf16; k_g, v_g as written by
+ * dbs_meanpool_kv.  o_r: DBS_ROWS bf16, rows >= N untouched.  lse (nullable):
+ * float32 [B, Hh, Npad], natural-log normaliser of each row < N.
+ * kv_count is clamped to [0, nb] and kv_idx entries outside [0, nb) are
+ * skipped, so malformed lists cannot read outside the K/V buffers. */
+dbs_status dbs_sparse_attn_fwd(const void* q_r, const void* k_r, const void* v_r, dbs_dtype dt,
+                               int B, int Hh, int N, int Npad, int d, int b, float scale,
+                               const int32_t* kv_count, const int32_t* kv_idx,
+                               const void* k_g, const void* v_g, int Ng, int n_pool,
+                               void* o_r, float* lse, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DBS_H */

@@ -39,21 +39,32 @@ def sample_rows(N: int, b: int, k: int) -> list:
     return rows
 
 
-def p_imp(q_r: np.ndarray, k_r: np.ndarray, N: int, b: int, k: int, scale: float) -> np.ndarray:
-    """P_imp [nb, nb] for one (batch, head); q_r, k_r are [>=N, d] in curve order."""
+def p_imp(q_r: np.ndarray, k_r: np.ndarray, N: int, b: int, k: int, scale: float,
+          query_blocks=None) -> np.ndarray:
+    """P_imp [nb, nb] for one (batch, head); q_r, k_r are [>=N, d] in curve order.
+
+    With query_blocks given, only those rows are computed (the others are NaN);
+    each computed row is the same as in the full map, since every sampled
+    query's softmax runs over all sampled keys either way.
+    """
     rows = sample_rows(N, b, k)
+    nb = len(rows)
+    if query_blocks is None:
+        query_blocks = range(nb)
+    query_blocks = list(query_blocks)
     flat = np.concatenate(rows)
     owner = np.concatenate([np.full(len(r), J) for J, r in enumerate(rows)])
-    qs = np.asarray(q_r, dtype=np.float64)[flat]
+    qflat = np.concatenate([rows[I] for I in query_blocks])
+    qowner = np.concatenate([np.full(len(rows[I]), I) for I in query_blocks])
+    qs = np.asarray(q_r, dtype=np.float64)[qflat]
     ks = np.asarray(k_r, dtype=np.float64)[flat]
     s = (qs @ ks.T) * scale
     s -= s.max(axis=1, keepdims=True)
     p = np.exp(s)
     p /= p.sum(axis=1, keepdims=True)          # P_approx, one row per sampled query
-    nb = len(rows)
-    out = np.empty((nb, nb), dtype=np.float64)
-    for I in range(nb):
-        pi = p[owner == I]
+    out = np.full((nb, nb), np.nan, dtype=np.float64)
+    for I in query_blocks:
+        pi = p[qowner == I]
         for J in range(nb):
             out[I, J] = pi[:, owner == J].max()
     return out

@@ -1,0 +1,198 @@
+"""CPU tier for the C-ABI library: it loads, exports every declared symbol, its
+host permutation helpers match the oracle bit for bit, and every device entry
+point rejects bad arguments on the host (no launch happens, so no GPU is
+needed)."""
+import ctypes as C
+import itertools
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle.perm import perm_cuboid as o_cuboid
+from oracle.perm import perm_gilbert3d as o_gilbert
+from workloads.configs import CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def dbs():
+    from dynamic_block_sparse_gilbert_amd import _lib, ops
+    _lib.lib()
+    return ops, _lib
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "dbs.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\*]+\s+)+\*?(dbs_\w+)\s*\(", src, re.M)))
+
+
+def test_all_declared_symbols_exported(dbs):
+    _, L = dbs
+    names = _declared()
+    assert len(names) >= 12, names
+    h = C.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(h, n), n
+    assert set(names) == set(L.SIGNATURES), set(names) ^ set(L.SIGNATURES)
+    assert L.lib().dbs_abi_version() == 1
+
+
+@pytest.mark.parametrize("T,H,W", list(itertools.product(range(1, 7), repeat=3)))
+def test_gilbert_cpp_matches_oracle_small(dbs, T, H, W):
+    ops, _ = dbs
+    assert np.array_equal(ops.perm_gilbert3d(T, H, W), o_gilbert(T, H, W))
+
+
+@pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: c.name)
+def test_gilbert_cpp_matches_oracle_workloads(dbs, cfg):
+    ops, _ = dbs
+    assert np.array_equal(ops.perm_gilbert3d(cfg.T, cfg.H, cfg.W, cfg.text_prefix),
+                          o_gilbert(cfg.T, cfg.H, cfg.W, cfg.text_prefix))
+
+
+@pytest.mark.parametrize("grid", [(40, 48, 80), (31, 45, 80), (5, 9, 7)])
+@pytest.mark.parametrize("cub", [(4, 4, 8), (1, 8, 16), (2, 8, 8), (8, 4, 4), (3, 2, 5)])
+def test_cuboid_cpp_matches_oracle(dbs, grid, cub):
+    ops, _ = dbs
+    assert np.array_equal(ops.perm_cuboid(*grid, *cub, prefix=3), o_cuboid(*grid, *cub, prefix=3))
+
+
+def test_perm_invert(dbs):
+    ops, L = dbs
+    p = ops.perm_gilbert3d(3, 4, 5, prefix=2)
+    inv = ops.perm_invert(p)
+    assert np.array_equal(inv[p], np.arange(p.size))
+    with pytest.raises(L.DbsError, match="INVALID_ARG"):
+        ops.perm_invert(np.array([0, 2, 2], dtype=np.int32))
+
+
+def test_perm_errors(dbs):
+    ops, L = dbs
+    with pytest.raises(L.DbsError, match="INVALID_ARG"):
+        ops.perm_gilbert3d(0, 3, 3)
+    with pytest.raises(L.DbsError, match="INVALID_ARG"):
+        ops.perm_cuboid(2, 2, 2, 0, 1, 1)
+    out = np.empty(8, dtype=np.int32)
+    assert L.lib().dbs_perm_gilbert3d(2, 2, 2, -1, out.ctypes.data) == -1
+    assert b"prefix" in L.lib().dbs_last_error()
+    assert L.lib().dbs_perm_gilbert3d(1 << 16, 1 << 16, 2, 0, out.ctypes.data) == -1
+
+
+# ---- device entry points: argument validation only (nothing is launched) ----
+# These pass fake device addresses that validation must reject before any
+# launch; they run only where no GPU is present, so a regression in the checks
+# shows up as a failed launch on the CPU, never as an access on a real device.
+
+
+def _no_gpu():
+    import torch
+    return not torch.cuda.is_available()
+
+
+cpu_only = pytest.mark.skipif(not _no_gpu(), reason="fake-pointer validation runs without a GPU only")
+
+A = 1 << 20          # a fake, 16-byte aligned "device" address; never dereferenced
+MIS = A + 4          # misaligned
+
+
+def _reorder(L, **kw):
+    a = dict(x=A, x_dt=0, sb=0, sn=1024, sh=128, y=A, y_dt=0, lay=0, perm=A, ph=0,
+             B=1, Hh=8, N=100, Npad=128, d=128, b=128)
+    a.update(kw)
+    return L.lib().dbs_reorder(a["x"], a["x_dt"], a["sb"], a["sn"], a["sh"], a["y"], a["y_dt"], a["lay"],
+                               a["perm"], a["ph"], a["B"], a["Hh"], a["N"], a["Npad"], a["d"], a["b"], None)
+
+
+@cpu_only
+def test_reorder_validation(dbs):
+    _, L = dbs
+    assert _reorder(L, x=0) == -1
+    assert _reorder(L, y=MIS) == -3
+    assert _reorder(L, d=96) == -2
+    assert _reorder(L, b=32) == -2
+    assert _reorder(L, Npad=120) == -1
+    assert _reorder(L, Npad=256) == -1          # a whole empty block
+    assert _reorder(L, sn=1025) == -3
+    assert _reorder(L, x_dt=0, y_dt=1) == -2
+    assert _reorder(L, lay=1, y_dt=1, x_dt=1) == -2
+    assert _reorder(L, ph=2) == -1
+    assert _reorder(L, N=0) == -1
+
+
+@cpu_only
+def test_estimate_validation(dbs):
+    _, L = dbs
+    f = L.lib().dbs_estimate_blocks
+    ws = L.lib().dbs_estimate_workspace_bytes(1, 2, 100, 64, 8)
+    assert ws == 1 * 2 * 2 * 8 * 4
+    ok = (A, A, 0, 1, 2, 100, 128, 64, 64, 8, 0.125, A, A, ws, None)
+    def call(**kw):
+        a = list(ok)
+        names = ["q", "k", "dt", "B", "Hh", "N", "Npad", "d", "b", "k_", "scale", "p", "w", "wb", "s"]
+        for n, v in kw.items():
+            a[names.index(n)] = v
+        return f(*a)
+    assert call(q=0) == -1
+    assert call(dt=1) == -2
+    assert call(k_=6) == -2
+    assert call(k_=0) == -1
+    assert call(k_=128) == -1
+    assert call(wb=ws - 4) == -1
+    assert call(scale=float("nan")) == -1
+    assert call(p=MIS) == -3
+    assert L.lib().dbs_estimate_workspace_bytes(0, 1, 1, 1, 1) == 0
+
+
+@cpu_only
+def test_mask_validation(dbs):
+    _, L = dbs
+    f = L.lib().dbs_build_mask
+    assert f(A, 1, 1, 16, 0.0, A, A, None, None) == -1
+    assert f(A, 1, 1, 16, 1.5, A, A, None, None) == -1
+    assert f(A, 1, 1, 16, float("nan"), A, A, None, None) == -1
+    assert f(A, 1, 1, 5000, 0.9, A, A, None, None) == -2
+    assert f(0, 1, 1, 16, 0.9, A, A, None, None) == -1
+    assert f(A + 2, 1, 1, 16, 0.9, A, A, None, None) == -3
+
+
+@cpu_only
+def test_attn_and_pool_validation(dbs):
+    _, L = dbs
+    f = L.lib().dbs_sparse_attn_fwd
+    base = [A, A, A, 0, 1, 4, 1000, 1024, 128, 128, 0.088, A, A, None, None, 0, 0, A, None, None]
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+    assert call(0, 0) == -1
+    assert call(3, 1) == -2
+    assert call(8, 80) == -2
+    assert call(13, A) == -1              # k_g without v_g
+    a = list(base); a[13] = A; a[14] = A; a[15] = 126; a[16] = 8
+    assert f(*a) == -1                    # Ng must be ceil(N / n) = 125
+    assert call(10, float("inf")) == -1
+    assert call(18, A + 2) == -3
+    g = L.lib().dbs_meanpool_kv
+    assert g(A, A, 0, 1, 4, 1000, 1024, 128, 128, 0, A, A, None) == -1
+    assert g(A, A, 1, 1, 4, 1000, 1024, 128, 128, 8, A, A, None) == -2
+    assert g(A, MIS, 0, 1, 4, 1000, 1024, 128, 128, 8, A, A, None) == -3
+
+
+@cpu_only
+def test_inverse_validation(dbs):
+    _, L = dbs
+    f = L.lib().dbs_inverse_reorder
+    assert f(A, 1, A, 0, 0, 1024, 128, A, 0, 1, 8, 100, 128, 128, None) == -2
+    assert f(A, 0, A, 0, 0, 1024, 128, 0, 0, 1, 8, 100, 128, 128, None) == -1
+    assert f(A, 0, A, 0, 0, 1024, 128, A, 0, 1, 8, 100, 128, 96, None) == -2
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    from dynamic_block_sparse_gilbert_amd import _lib
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.lib()

@@ -1,0 +1,176 @@
+"""GPU parity: sparse_attn_fwd against the oracle's block-masked float64
+attention, max-abs 2e-2 (bf16 inputs, fp32 accumulation, P rounded to bf16),
+for explicit KV-block lists, partial blocks, empty rows, malformed indices and
+the ASA_G global tokens."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import dev, dev_bf16, host, say, smooth_qkv
+from oracle.attention import global_bias, masked_attention
+from oracle.reorder import reorder_fast as o_reorder
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def _ops():
+    from dynamic_block_sparse_gilbert_amd import ops
+    return ops
+
+
+def _lists(kind, rows, nb, rng):
+    out = []
+    for r in range(rows):
+        row = []
+        for I in range(nb):
+            if kind == "all":
+                row.append(list(range(nb)))
+            elif kind == "single":
+                row.append([(3 * I + r) % nb])
+            elif kind == "empty":
+                row.append([] if I % 3 == 0 else sorted(rng.choice(nb, size=min(nb, 2), replace=False).tolist()))
+            else:
+                m = int(rng.integers(1, nb + 1))
+                row.append(sorted(rng.choice(nb, size=m, replace=False).tolist()))
+        out.append(row)
+    return out
+
+
+def _upload(lists, B, Hh, nb, bad=False, rng=None):
+    cnt = np.zeros((B, Hh, nb), np.int32)
+    idx = np.full((B, Hh, nb, nb), -7, np.int32)
+    for r, row in enumerate(lists):
+        bi, h = divmod(r, Hh)
+        for I, js in enumerate(row):
+            cnt[bi, h, I] = len(js)
+            idx[bi, h, I, :len(js)] = js
+    if bad:   # malformed entries must be skipped, not read
+        for bi in range(B):
+            for h in range(Hh):
+                I = int(rng.integers(0, nb))
+                if cnt[bi, h, I] < nb:
+                    idx[bi, h, I, cnt[bi, h, I]] = 10 ** 6
+                    cnt[bi, h, I] += 1
+                cnt[bi, h, (I + 1) % nb] = -5 if nb > 1 else cnt[bi, h, 0]
+    return cnt, idx
+
+
+CASES = [  # N, d, b
+    (2048, 64, 64), (1000, 128, 128), (777, 128, 64), (700, 64, 128), (128, 128, 128), (337, 64, 64),
+]
+
+
+@pytest.mark.parametrize("N,d,b", CASES)
+@pytest.mark.parametrize("kind", ["random", "all", "single", "empty"])
+def test_attn_lists(N, d, b, kind):
+    say("attn", N, d, b, kind)
+    B, Hh = 2, 2
+    rng = np.random.default_rng(N + d + b + len(kind))
+    q, k, v = smooth_qkv(N + d, B, N, Hh, d)
+    nb = -(-N // b)
+    Npad = nb * b
+    lists = _lists(kind, B * Hh, nb, rng)
+    cnt, idx = _upload(lists, B, Hh, nb)
+    ops = _ops()
+    perm = dev(np.arange(N, dtype=np.int32))
+    q_r = ops.reorder(dev_bf16(q), perm, Npad, b, "rows")
+    k_r = ops.reorder(dev_bf16(k), perm, Npad, b, "rows")
+    v_t = ops.reorder(dev_bf16(v), perm, Npad, b, "tiles_t")
+    scale = 1.0 / math.sqrt(d)
+    o_r, lse = ops.sparse_attn_fwd(q_r, k_r, v_t, N, b, scale, dev(cnt), dev(idx), want_lse=True)
+    torch.cuda.synchronize()
+    o, l = host(o_r), host(lse)
+    for bi in range(B):
+        for h in range(Hh):
+            ref, rl = masked_attention(q[bi, :, h], k[bi, :, h], v[bi, :, h], N, b, lists[bi * Hh + h], scale)
+            got = o[bi, h, :N]
+            empty = np.repeat([len(js) == 0 for js in lists[bi * Hh + h]], b)[:N]
+            if (~empty).any():
+                assert np.abs(got[~empty] - ref[~empty]).max() <= TOL
+                assert np.abs(l[bi, h, :N][~empty] - rl[~empty]).max() <= 1e-3
+            assert (got[empty] == 0).all()
+            assert np.isneginf(l[bi, h, :N][empty]).all()
+
+
+def test_attn_malformed_lists_are_skipped():
+    say("attn malformed")
+    N, d, b, B, Hh = 600, 128, 128, 1, 3
+    rng = np.random.default_rng(2)
+    q, k, v = smooth_qkv(3, B, N, Hh, d)
+    nb = -(-N // b)
+    lists = _lists("random", B * Hh, nb, rng)
+    cnt, idx = _upload(lists, B, Hh, nb, bad=True, rng=rng)
+    ops = _ops()
+    perm = dev(np.arange(N, dtype=np.int32))
+    Npad = nb * b
+    q_r = ops.reorder(dev_bf16(q), perm, Npad, b, "rows")
+    k_r = ops.reorder(dev_bf16(k), perm, Npad, b, "rows")
+    v_t = ops.reorder(dev_bf16(v), perm, Npad, b, "tiles_t")
+    o_r, _ = ops.sparse_attn_fwd(q_r, k_r, v_t, N, b, 1 / math.sqrt(d), dev(cnt), dev(idx))
+    torch.cuda.synchronize()
+    o = host(o_r)
+    for h in range(Hh):
+        eff = []
+        for I in range(nb):
+            c = min(max(int(cnt[0, h, I]), 0), nb)
+            eff.append([j for j in idx[0, h, I, :c].tolist() if 0 <= j < nb])
+        ref, _ = masked_attention(q[0, :, h], k[0, :, h], v[0, :, h], N, b, eff, 1 / math.sqrt(d))
+        nz = np.repeat([len(e) > 0 for e in eff], b)[:N]
+        assert np.abs(o[0, h, :N][nz] - ref[nz]).max() <= TOL
+        assert (o[0, h, :N][~nz] == 0).all()
+
+
+@pytest.mark.parametrize("N,d,b,n,kind", [
+    (1000, 64, 128, 8, "random"), (1000, 128, 64, 7, "empty"), (600, 128, 128, 1, "all"),
+    (17776 // 8, 64, 128, 8, "single"), (513, 64, 64, 16, "random"),
+])
+def test_attn_global_tokens(N, d, b, n, kind):
+    say("attn asa_g", N, d, b, n, kind)
+    B, Hh = 1, 2
+    rng = np.random.default_rng(N * n)
+    q, k, v = smooth_qkv(N + n, B, N, Hh, d)
+    nb = -(-N // b)
+    Npad = nb * b
+    lists = _lists(kind, B * Hh, nb, rng)
+    cnt, idx = _upload(lists, B, Hh, nb)
+    ops = _ops()
+    perm = dev(np.arange(N, dtype=np.int32))
+    q_r = ops.reorder(dev_bf16(q), perm, Npad, b, "rows")
+    k_r = ops.reorder(dev_bf16(k), perm, Npad, b, "rows")
+    v_t = ops.reorder(dev_bf16(v), perm, Npad, b, "tiles_t")
+    k_g, v_g, Ng = ops.meanpool_kv(k_r, v_t, N, b, n)
+    scale = 1.0 / math.sqrt(d)
+    o_r, lse = ops.sparse_attn_fwd(q_r, k_r, v_t, N, b, scale, dev(cnt), dev(idx), k_g, v_g, Ng, n,
+                                   want_lse=True)
+    torch.cuda.synchronize()
+    o, l = host(o_r), host(lse)
+    kg = host(k_g)[:, :, :Ng]
+    vg_t = host(v_g)
+    vg = vg_t.transpose(0, 1, 2, 4, 3).reshape(B, Hh, -1, d)[:, :, :Ng]
+    gb = global_bias(N, n)
+    for h in range(Hh):
+        # the kernel is compared on the pooled tokens it was given (pooling has its own test)
+        ref, rl = masked_attention(q[0, :, h], k[0, :, h], v[0, :, h], N, b, lists[h], scale,
+                                   kg[0, h], vg[0, h], gb)
+        assert np.abs(o[0, h, :N] - ref).max() <= TOL
+        assert np.abs(l[0, h, :N] - rl).max() <= 1e-3
+
+
+def test_attn_deterministic():
+    N, d, b = 1000, 128, 128
+    q, k, v = smooth_qkv(11, 1, N, 2, d)
+    nb = 8
+    rng = np.random.default_rng(0)
+    cnt, idx = _upload(_lists("random", 2, nb, rng), 1, 2, nb)
+    ops = _ops()
+    perm = dev(np.arange(N, dtype=np.int32))
+    q_r = ops.reorder(dev_bf16(q), perm, 1024, b, "rows")
+    k_r = ops.reorder(dev_bf16(k), perm, 1024, b, "rows")
+    v_t = ops.reorder(dev_bf16(v), perm, 1024, b, "tiles_t")
+    a = host(ops.sparse_attn_fwd(q_r, k_r, v_t, N, b, 0.088, dev(cnt), dev(idx))[0])
+    c = host(ops.sparse_attn_fwd(q_r, k_r, v_t, N, b, 0.088, dev(cnt), dev(idx))[0])
+    assert np.array_equal(a, c)

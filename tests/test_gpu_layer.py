@@ -1,0 +1,131 @@
+"""GPU parity for the whole layer (reorder -> estimate -> mask -> attention ->
+inverse reorder) on the workload shapes, against the oracle run step by step on
+the same bf16 values:
+- P_imp within relative 1e-3;
+- kv_count / kv_idx bit-exact given the GPU's P_imp (the oracle builds the mask
+  from the same array);
+- output within max-abs 2e-2 of the oracle's float64 attention under that mask,
+  on every query block for the small workloads and on sampled blocks (first,
+  last, middle and seeded random ones) at full size."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import dev, dev_bf16, host, kept_lists, say
+from oracle.attention import global_bias, meanpool, masked_attention
+from oracle.estimator import p_imp as o_p_imp
+from oracle.mask import build_mask as o_build_mask
+from oracle.perm import perm_cuboid, perm_gilbert3d
+from oracle.reorder import inverse_reorder as o_inverse
+from oracle.reorder import reorder_fast as o_reorder
+from workloads import get_config, make_inputs
+from workloads.generator import bf16_round, head_cuboid
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def _layer(cfg, heads, tau):
+    from dynamic_block_sparse_gilbert_amd.layer import AsaLayer, LayerSpec
+    cub = [head_cuboid(cfg, h) for h in heads] if cfg.reorder == "cuboid_per_head" else None
+    spec = LayerSpec(T=cfg.T, H=cfg.H, W=cfg.W, heads=len(heads), d=cfg.d, b=cfg.b, k=cfg.k, tau=tau,
+                     prefix=cfg.text_prefix, order=cfg.reorder, cuboid=cfg.cuboid, cuboids=cub,
+                     n_pool=cfg.global_pool)
+    return AsaLayer(spec)
+
+
+def _oracle_perm(cfg, heads):
+    if cfg.reorder == "gilbert":
+        return perm_gilbert3d(cfg.T, cfg.H, cfg.W, cfg.text_prefix)
+    if cfg.reorder == "cuboid":
+        return perm_cuboid(cfg.T, cfg.H, cfg.W, *cfg.cuboid, prefix=cfg.text_prefix)
+    return np.stack([perm_cuboid(cfg.T, cfg.H, cfg.W, *head_cuboid(cfg, h), prefix=cfg.text_prefix)
+                     for h in heads])
+
+
+def _check_layer(cfg, heads, tau, sample_blocks=None, p_heads=None, seed=0):
+    say("layer", cfg.name, "heads", heads, "tau", tau)
+    q, k, v = make_inputs(cfg, heads=heads)
+    layer = _layer(cfg, heads, tau)
+    perm = _oracle_perm(cfg, heads)
+    assert np.array_equal(host(layer.perm), perm)
+    if cfg.dtype == "fp32":
+        # float32 storage: the reorder rounds to bf16, the compute type; the
+        # oracle gets those same rounded values
+        out = layer.forward(dev(q), dev(k), dev(v), out_dtype=torch.float32)
+        q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
+    else:
+        out = layer.forward(dev_bf16(q), dev_bf16(k), dev_bf16(v), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    P, cnt, idx, o_r, out = host(layer.p_imp), host(layer.kv_count), host(layer.kv_idx), host(layer.o_r), host(out)
+    qr, kr, vr = (o_reorder(x, perm, cfg.Npad) for x in (q, k, v))
+    nb, N, b = cfg.nb, cfg.N, cfg.b
+    rng = np.random.default_rng(seed)
+    blocks = None
+    if sample_blocks:
+        blocks = sorted(set([0, 1, nb // 2, nb - 1] + rng.choice(nb, size=sample_blocks, replace=False).tolist()))
+    # 1. estimator
+    for h in (p_heads if p_heads is not None else range(len(heads))):
+        ref = o_p_imp(qr[0, h], kr[0, h], N, b, cfg.k, cfg.scale, query_blocks=blocks)
+        rows = range(nb) if blocks is None else blocks
+        for I in rows:
+            np.testing.assert_allclose(P[0, h, I], ref[I], rtol=1e-3, atol=1e-7, err_msg=f"h{h} I{I}")
+    # 2. mask, bit-exact on the GPU's P_imp (every row up to nb = 300)
+    mrows = range(nb) if (blocks is None or nb <= 300) else blocks
+    rows = [(h, I) for h in range(len(heads)) for I in mrows]
+    rc, ri, _, ties = o_build_mask(np.stack([P[0, h, I] for h, I in rows]), tau)
+    for j, (h, I) in enumerate(rows):
+        assert cnt[0, h, I] == rc[j], (h, I)
+        assert np.array_equal(idx[0, h, I, :rc[j]], ri[j, :rc[j]]), (h, I)
+    # 3. attention under that mask, then back to token order
+    lists = kept_lists(cnt, idx)
+    for h in range(len(heads)):
+        kg = vg = gb = None
+        if cfg.global_pool:
+            kg = bf16_round(meanpool(kr[0, h], N, cfg.global_pool).astype(np.float32))
+            vg = bf16_round(meanpool(vr[0, h], N, cfg.global_pool).astype(np.float32))
+            gb = global_bias(N, cfg.global_pool)
+        ref, _ = masked_attention(qr[0, h], kr[0, h], vr[0, h], N, b, lists[h], cfg.scale, kg, vg, gb,
+                                  query_blocks=blocks)
+        rows_tok = np.concatenate([np.arange(I * b, min((I + 1) * b, N)) for I in (blocks or range(nb))])
+        err = np.abs(o_r[0, h, rows_tok] - ref[rows_tok]).max()
+        assert err <= TOL, (h, err)
+        if blocks is None:
+            ph = perm[h] if perm.ndim == 2 else perm
+            back = o_inverse(o_r[:, h:h + 1], ph, N)
+            assert np.array_equal(out[:, :, h:h + 1], back)
+    s = 1.0 - cnt.sum() / cnt.size / nb
+    say("block sparsity", round(float(s), 4), "ties", len(ties))
+    return s
+
+
+def test_layer_config1_tiny():
+    cfg = get_config(1)
+    s = _check_layer(cfg, [0], 0.90)
+    assert 0.5 < s < 1.0
+
+
+def test_layer_config3_cogvideox_asa_g():
+    cfg = get_config(3)
+    _check_layer(cfg, [0, 17, 47], 0.95, sample_blocks=12)
+
+
+def test_layer_config2_wan_full():
+    """All 12 heads at full length, the launch configuration of the bench; masks
+    of every row checked, outputs on sampled query blocks of every head."""
+    cfg = get_config(2)
+    s = _check_layer(cfg, list(range(12)), 0.90, sample_blocks=4, p_heads=[0, 11])
+    assert 0.85 < s < 0.99
+
+
+def test_layer_config4_cuboid_long():
+    cfg = get_config(4)
+    _check_layer(cfg, [3], 0.90, sample_blocks=4)
+
+
+def test_layer_config5_per_head_cuboids():
+    cfg = get_config(5)
+    _check_layer(cfg, [0, 1], 0.90, sample_blocks=3)

@@ -109,3 +109,15 @@ def test_padding_rows_never_sampled():
     P2 = p_imp(q2, k2, N, b, 4, 0.5)
     assert np.array_equal(P1, P2)
     assert block_lengths(N, b).tolist() == [8, 8, 5]
+
+
+def test_query_block_subset_equals_full_rows():
+    N, b, k = 90, 16, 4
+    q, k_ = _qk(N, 8, seed=11)
+    full = p_imp(q, k_, N, b, k, 0.3)
+    part = p_imp(q, k_, N, b, k, 0.3, query_blocks=[0, 3, 5])
+    for I in range(full.shape[0]):
+        if I in (0, 3, 5):
+            assert np.array_equal(part[I], full[I])
+        else:
+            assert np.isnan(part[I]).all()
