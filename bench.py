@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark: one ASA attention layer forward on one MI355X.
+
+Workload: the Wan2.1-1.3B-shaped self-attention layer -- batch 1, 12 heads,
+head dim 128, bf16, latent 21 x 30 x 52 = 32,760 tokens (padded to 32,768),
+smooth-field Q/K (sigma 4) + 0.3 noise, iid V; b = 128, k = 16, Gilbert-curve
+reorder, threshold tau = 0.90 (tau = 0.95 is measured as well and reported
+under "extra").  Synthetic inputs stand in for the model's activations.
+
+A step is one pass of the whole hot path over that batch, all on one stream:
+reorder Q, K, V -> estimate_blocks -> build_mask -> sparse_attn_fwd ->
+inverse_reorder.  Inputs are resident in HBM before timing starts; buffers and
+the permutation are set up once outside the timed region.
+
+value = dense-equivalent TFLOP/s = 4 * B * H * N^2 * d / (seconds per step).
+roofline = the attention kernel (the dominant one): executed FLOP (4 * d *
+sum over kept block pairs of |I| * |J|) / its mean launch time, measured with
+HIP events recorded on its launch stream inside the timed region, against the
+bf16 dense MFMA peak.  cpu_baseline = the CPU oracle on a bounded sample of the
+same layer, scaled to the whole layer.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+HBM_PEAK_GBS = 8000.0              # MI355X HBM3E peak
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_wan_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "dynamic_block_sparse_gilbert_amd", "csrc", "kernels", "attn.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--tau", type=float, default=0.90)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the tau=0.95 measurement")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run one device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def src_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def kept_pair_tokens(cnt, idx, N, b):
+    """sum over kept (I, J) of |I| * |J| with valid-token block sizes."""
+    import numpy as np
+    nb = cnt.shape[-1]
+    L = np.array([min(b, N - J * b) for J in range(nb)], dtype=np.float64)
+    c = cnt.reshape(-1, nb)
+    ix = idx.reshape(-1, nb, nb)
+    total = 0.0
+    for r in range(c.shape[0]):
+        for I in range(nb):
+            total += L[I] * L[ix[r, I, :c[r, I]]].sum()
+    return total
+
+
+def run_steps(layer, q, k, v, out, tau, steps, warmup, torch):
+    """Returns (host ms per step between synchronisations, event ms per step, per-stage mean ms)."""
+    names = ["reorder_qkv", "estimate", "mask", "attn", "inverse"]
+    for _ in range(warmup):
+        layer.prepare(q, k, v)
+        layer.mask(tau)
+        layer.attend(out=out)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        e = ev[s]
+        e[0].record()
+        layer.prepare(q, k, v)
+        e[1].record()
+        from dynamic_block_sparse_gilbert_amd import ops
+        sp = layer.spec
+        ops.estimate_blocks(layer.q_r, layer.k_r, sp.N, sp.b, sp.k, sp.scale, p_imp=layer.p_imp,
+                            workspace=layer.ws)
+        e[2].record()
+        ops.build_mask(layer.p_imp, tau, kv_count=layer.kv_count, kv_idx=layer.kv_idx)
+        e[3].record()
+        ops.sparse_attn_fwd(layer.q_r, layer.k_r, layer.v_t, sp.N, sp.b, sp.scale, layer.kv_count,
+                            layer.kv_idx, layer.k_g, layer.v_g, layer.Ng, sp.n_pool, o_r=layer.o_r)
+        e[4].record()
+        ops.inverse_reorder(layer.o_r, layer.perm, sp.N, out=out)
+        e[5].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    stage = {n: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps
+             for i, n in enumerate(names)}
+    step_ev = sum(ev[s][0].elapsed_time(ev[s][-1]) for s in range(steps)) / steps
+    return wall, step_ev, stage
+
+
+def cpu_baseline(cfg, q, k, v, perm, tau):
+    """Oracle on a bounded sample: one head's estimator and mask, attention on 16
+    query blocks of it; scaled to all heads and all query blocks."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle.attention import masked_attention
+    from oracle.estimator import p_imp
+    from oracle.mask import build_mask
+    from oracle.reorder import reorder_fast
+
+    h = 0
+    x = [reorder_fast(t[:, :, h:h + 1], perm, cfg.Npad)[0, 0] for t in (q, k, v)]
+    t0 = time.perf_counter()
+    P = p_imp(x[0], x[1], cfg.N, cfg.b, cfg.k, cfg.scale).astype(np.float32)
+    t_est = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    cnt, idx, _, _ = build_mask(P, tau)
+    t_mask = time.perf_counter() - t0
+    kept = [idx[I, :cnt[I]].tolist() for I in range(cfg.nb)]
+    blocks = list(range(0, cfg.nb, cfg.nb // 16))[:16]
+    t0 = time.perf_counter()
+    masked_attention(x[0], x[1], x[2], cfg.N, cfg.b, kept, cfg.scale, query_blocks=blocks)
+    t_attn = (time.perf_counter() - t0) / len(blocks) * cfg.nb
+    per_head = t_est + t_mask + t_attn
+    total = per_head * cfg.heads
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {
+        "value": cfg.dense_flop() / total / 1e12,
+        "unit": "dense-equiv TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"head 0 of {cfg.heads}: full estimator ({t_est:.2f} s) and mask ({t_mask:.2f} s), "
+                   f"attention on {len(blocks)} of {cfg.nb} query blocks; scaled x{cfg.nb / len(blocks):.0f} "
+                   f"blocks and x{cfg.heads} heads -> {total:.1f} s per layer"),
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): every step of the path is "
+              "independent per head, so several GPUs would each run a share of the heads; that "
+              "configuration is not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from dynamic_block_sparse_gilbert_amd.layer import AsaLayer, LayerSpec
+    from workloads import get_config, make_inputs
+
+    cfg = get_config(2)
+    t_gen = time.perf_counter()
+    q, k, v = make_inputs(cfg)                    # bf16-representable float32 [1, N, 12, 128]
+    t_gen = time.perf_counter() - t_gen
+    dev = torch.device("cuda:0")
+    to = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)
+    qd, kd, vd = to(q), to(k), to(v)
+    out = torch.empty_like(qd)
+    spec = LayerSpec(T=cfg.T, H=cfg.H, W=cfg.W, heads=cfg.heads, d=cfg.d, b=cfg.b, k=cfg.k, tau=args.tau)
+    layer = AsaLayer(spec, device=dev)
+    torch.cuda.synchronize()
+
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    ms, ms_ev, stage = run_steps(layer, qd, kd, vd, out, args.tau, args.steps, args.warmup, torch)
+    cnt, idx = layer.kv_count.cpu().numpy(), layer.kv_idx.cpu().numpy()
+    nb = cfg.nb
+    sparsity = 1.0 - cnt.sum() / (cnt.size * nb)
+    pairs = kept_pair_tokens(cnt, idx, cfg.N, cfg.b)
+    exec_flop = 4.0 * cfg.d * pairs
+    attn_tflops = exec_flop / (stage["attn"] * 1e-3) / 1e12
+    dense = cfg.dense_flop()
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            tj = json.load(open(TRAFFIC_FILE))
+            if tj.get("attn_src_sha256_16") == src_hash(ATTN_SRC) and abs(tj.get("tau", -1) - args.tau) < 1e-9:
+                traffic = tj.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    # mask-generation byte passes: reorder of Q, K, V (read + write) and P_imp read / kv lists write
+    e = 2
+    reorder_bytes = 2.0 * 3 * cfg.heads * cfg.N * cfg.d * e
+    inverse_bytes = 2.0 * cfg.heads * cfg.N * cfg.d * e
+    mask_bytes = 4.0 * cfg.heads * nb * nb + 4.0 * cfg.heads * (nb + cnt.sum())
+
+    extra = {}
+    if not args.no_extra:
+        ms95, _, stage95 = run_steps(layer, qd, kd, vd, out, 0.95, max(5, args.steps // 2), 2, torch)
+        c95, i95 = layer.kv_count.cpu().numpy(), layer.kv_idx.cpu().numpy()
+        ef95 = 4.0 * cfg.d * kept_pair_tokens(c95, i95, cfg.N, cfg.b)
+        extra["tau_0.95"] = {
+            "ms_per_step": round(ms95, 4),
+            "value": round(dense / (ms95 * 1e-3) / 1e12, 2),
+            "block_sparsity": round(float(1.0 - c95.sum() / (c95.size * nb)), 4),
+            "stages_ms": {kk: round(vv, 4) for kk, vv in stage95.items()},
+            "attn_executed_tflops": round(ef95 / (stage95["attn"] * 1e-3) / 1e12, 2),
+        }
+
+    line = {
+        "metric": "ms/layer + dense-equiv TFLOP/s, block-sparse attn at 90-95% sparsity, 1 GPU",
+        "value": round(dense / (ms * 1e-3) / 1e12, 3),
+        "unit": "dense-equiv TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded smooth-field Q/K, iid V; no model weights)",
+        "config": {
+            "workload": "wan2.1-1.3b-shaped ASA layer: B=1, 12 heads, d=128, 21x30x52 = 32,760 tokens, "
+                        "b=128, k=16, Gilbert reorder",
+            "tau": args.tau,
+            "block_sparsity": round(float(sparsity), 4),
+            "token_pairs_kept": pairs,
+            "executed_attn_flop": exec_flop,
+            "dense_equiv_flop": dense,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_fwd_kernel<128,128>",
+            "achieved": round(attn_tflops, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic,
+            "launch_ms": round(stage["attn"], 4),
+        },
+        "stages_ms": {kk: round(vv, 4) for kk, vv in stage.items()},
+        "byte_passes": {
+            "reorder_qkv_GBs": round(reorder_bytes / (stage["reorder_qkv"] * 1e-3) / 1e9, 1),
+            "inverse_GBs": round(inverse_bytes / (stage["inverse"] * 1e-3) / 1e9, 1),
+            "mask_GBs": round(mask_bytes / (stage["mask"] * 1e-3) / 1e9, 1),
+            "hbm_peak_GBs": HBM_PEAK_GBS,
+        },
+        "step_ms_events": round(ms_ev, 4),
+        "input_gen_s": round(t_gen, 2),
+    }
+    if extra:
+        line["extra"] = extra
+    if not args.no_cpu_baseline:
+        perm = layer.perm.cpu().numpy()
+        line["cpu_baseline"] = cpu_baseline(cfg, q, k, v, perm, args.tau)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

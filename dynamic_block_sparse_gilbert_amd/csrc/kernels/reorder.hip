@@ -20,6 +20,13 @@ constexpr int kThreads = 256;
 // can never address outside the token buffers.
 __device__ __forceinline__ int clamp_tok(int p, int N) { return p < 0 ? 0 : (p >= N ? N - 1 : p); }
 
+// Column of token offset t inside a tiles-transposed tile: bits 2 and 3 of t
+// exchanged, i.e. each group of 16 tokens is stored in the order 0-3, 8-11,
+// 4-7, 12-15 (an involution).  The attention kernel relies on this order.
+__device__ __forceinline__ int tile_col(int t) {
+  return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1);
+}
+
 template <typename T> struct Vec8;
 template <> struct Vec8<__bf16> {
   uint4 v;
@@ -85,9 +92,10 @@ __global__ __launch_bounds__(kThreads) void reorder_rows_kernel(
   }
 }
 
-// y tiles-transposed layout: y[b, h, J, e, t] = x[b, perm[J*BLK + t], h, e].
-// One workgroup per (tile J, h, b); thread (c, tg) gathers an 8-token x
-// 8-channel block, transposes it in registers and writes 8 channel rows.
+// y tiles-transposed layout: y[b, h, J, e, tile_col(t)] = x[b, perm[J*BLK + t], h, e].
+// One workgroup per (tile J, h, b); thread (c, tg) gathers the 8 tokens that
+// land in columns 8tg..8tg+7 for 8 channels, transposes the block in
+// registers and writes 8 channel rows of 16 bytes.
 template <typename Tin, int D, int BLK>
 __global__ __launch_bounds__((D / 8) * (BLK / 8)) void reorder_tiles_t_kernel(
     const Tin* __restrict__ x, int64_t sb, int64_t sn, int64_t sh, __bf16* __restrict__ y,
@@ -99,7 +107,7 @@ __global__ __launch_bounds__((D / 8) * (BLK / 8)) void reorder_tiles_t_kernel(
   uint32_t w[8][4];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int i = J * BLK + 8 * tg + e;
+    const int i = J * BLK + tile_col(8 * tg + e);
     uint4 o = make_uint4(0, 0, 0, 0);
     if (i < N) {
       Vec8<Tin> v;
@@ -201,13 +209,13 @@ __global__ __launch_bounds__(kThreads) void meanpool_v_kernel(
     const uint16_t* base = reinterpret_cast<const uint16_t*>(v_t) + bh * (int64_t)nb * D * BLK;
     for (int t = 0; t < r; ++t) {
       const int i = g * n + t;
-      acc += bf16_bits_to_f32(base[(int64_t)(i / BLK) * D * BLK + (int64_t)e * BLK + (i % BLK)]);
+      acc += bf16_bits_to_f32(base[(int64_t)(i / BLK) * D * BLK + (int64_t)e * BLK + tile_col(i % BLK)]);
     }
     acc = acc / (float)r;
   }
   const int ngt = Ngpad / BLK;
   uint16_t* out = reinterpret_cast<uint16_t*>(v_g) + bh * (int64_t)ngt * D * BLK;
-  out[(int64_t)(g / BLK) * D * BLK + (int64_t)e * BLK + (g % BLK)] =
+  out[(int64_t)(g / BLK) * D * BLK + (int64_t)e * BLK + tile_col(g % BLK)] =
       (uint16_t)(g < Ng ? f32_to_bf16_bits(acc) : 0u);
 }
 

@@ -27,8 +27,12 @@
  *   DBS_ROWS     [B, Hh, Npad, d]            one token per row
  *   DBS_TILES_T  [B, Hh, Npad / b, d, b]     each b-token tile stored d-major
  *                                            (token index fastest); used for V
- *                                            so that the P*V product reads
- *                                            consecutive keys of one channel.
+ *                                            so that the P*V product reads the
+ *                                            keys of one channel contiguously.
+ *                                            Token offset t of a tile sits in
+ *                                            column t with bits 2 and 3 swapped:
+ *                                            every 16 tokens are stored in the
+ *                                            order 0-3, 8-11, 4-7, 12-15.
  */
 #ifndef DBS_H
 #define DBS_H

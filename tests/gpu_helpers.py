@@ -49,3 +49,16 @@ def kept_lists(kv_count: np.ndarray, kv_idx: np.ndarray):
     c = kv_count.reshape(-1, nb)
     i = kv_idx.reshape(-1, nb, nb)
     return [[i[r, I, :c[r, I]].tolist() for I in range(nb)] for r in range(c.shape[0])]
+
+
+def tile_col(t):
+    """Column of token offset t in a tiles-transposed tile (bits 2 and 3 swapped)."""
+    t = np.asarray(t)
+    return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1)
+
+
+def tiles_to_rows(yt: np.ndarray) -> np.ndarray:
+    """[B, Hh, nt, d, b] tiles-transposed -> [B, Hh, nt * b, d] rows."""
+    B, Hh, nt, d, b = yt.shape
+    cols = tile_col(np.arange(b))
+    return yt[..., cols].transpose(0, 1, 2, 4, 3).reshape(B, Hh, nt * b, d)

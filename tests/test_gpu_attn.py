@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import dev, dev_bf16, host, say, smooth_qkv
+from gpu_helpers import dev, dev_bf16, host, say, smooth_qkv, tiles_to_rows
 from oracle.attention import global_bias, masked_attention
 from oracle.reorder import reorder_fast as o_reorder
 
@@ -149,8 +149,7 @@ def test_attn_global_tokens(N, d, b, n, kind):
     torch.cuda.synchronize()
     o, l = host(o_r), host(lse)
     kg = host(k_g)[:, :, :Ng]
-    vg_t = host(v_g)
-    vg = vg_t.transpose(0, 1, 2, 4, 3).reshape(B, Hh, -1, d)[:, :, :Ng]
+    vg = tiles_to_rows(host(v_g))[:, :, :Ng]
     gb = global_bias(N, n)
     for h in range(Hh):
         # the kernel is compared on the pooled tokens it was given (pooling has its own test)

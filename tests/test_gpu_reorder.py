@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import dev, dev_bf16, host, say
+from gpu_helpers import dev, dev_bf16, host, say, tiles_to_rows
 from oracle.attention import meanpool
 from oracle.perm import perm_gilbert3d
 from oracle.reorder import inverse_reorder as o_inverse
@@ -21,8 +21,7 @@ def _ops():
 
 
 def _tiles_to_rows(yt: np.ndarray) -> np.ndarray:
-    B, Hh, nt, d, b = yt.shape
-    return yt.transpose(0, 1, 2, 4, 3).reshape(B, Hh, nt * b, d)
+    return tiles_to_rows(yt)
 
 
 CASES = [  # B, N, Hh, d, b, per_head, in_dtype
