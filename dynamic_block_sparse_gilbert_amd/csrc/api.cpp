@@ -180,10 +180,10 @@ dbs_status dbs_inverse_reorder(const void* y, dbs_dtype y_dt, void* x, dbs_dtype
   DBS_GUARD_END
 }
 
-size_t dbs_estimate_workspace_bytes(int B, int Hh, int N, int b, int k) {
-  if (B < 1 || Hh < 1 || N < 1 || b < 1 || k < 1) return 0;
-  const int64_t nb = (N + b - 1) / b;
-  return (size_t)((int64_t)B * Hh * nb * k * 4);
+size_t dbs_estimate_workspace_bytes(int B, int Hh, int N, int d, int b, int k) {
+  if (B < 1 || Hh < 1 || N < 1 || b < 1 || k < 1 || (d != 64 && d != 128)) return 0;
+  const int nb = (N + b - 1) / b;
+  return dbs::estimate_workspace_bytes(B, Hh, nb, k, d);
 }
 
 dbs_status dbs_estimate_blocks(const void* q_r, const void* k_r, dbs_dtype dt, int B, int Hh, int N,
@@ -199,12 +199,12 @@ dbs_status dbs_estimate_blocks(const void* q_r, const void* k_r, dbs_dtype dt, i
   REQUIRE(k >= 1 && k <= b, DBS_ERR_INVALID_ARG, "k=%d must be in [1, b=%d]", k, b);
   REQUIRE((k & (k - 1)) == 0, DBS_ERR_UNSUPPORTED, "k=%d must be a power of two", k);
   REQUIRE(std::isfinite(scale) && scale > 0.f, DBS_ERR_INVALID_ARG, "scale must be finite and > 0");
-  const size_t need = dbs_estimate_workspace_bytes(B, Hh, N, b, k);
+  const size_t need = dbs_estimate_workspace_bytes(B, Hh, N, d, b, k);
   REQUIRE(workspace_bytes >= need, DBS_ERR_INVALID_ARG, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   const int nb = Npad / b;
   REQUIRE((int64_t)nb * k <= INT32_MAX / 2, DBS_ERR_INVALID_ARG, "too many sampled tokens");
   dbs::EstimateArgs a{};
-  a.q_r = q_r; a.k_r = k_r; a.p_imp = p_imp; a.lse2 = static_cast<float*>(workspace);
+  a.q_r = q_r; a.k_r = k_r; a.p_imp = p_imp; a.workspace = workspace;
   a.B = B; a.Hh = Hh; a.N = N; a.Npad = Npad; a.d = d; a.b = b; a.k = k; a.nb = nb;
   a.scale = scale; a.stream = stream;
   return from_hip(dbs::launch_estimate(a), "dbs_estimate_blocks launch");

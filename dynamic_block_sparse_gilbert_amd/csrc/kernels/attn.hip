@@ -89,8 +89,13 @@ void attn_fwd_kernel(
     __bf16* __restrict__ o_r, float* __restrict__ lse,
     int Hh, int N, int Npad, int nb, int Ng, float sl2, float log2n, float log2r_last, int total) {
   using C = AttnCfg<D, BLK>;
-  __shared__ __attribute__((aligned(16))) __bf16 Kb[2][C::kUnits * 8];
-  __shared__ __attribute__((aligned(16))) __bf16 Vb[2][C::kUnits * 8];
+  // Four distinct arrays whose roles are static in each half of the 2x-unrolled
+  // pipeline, so the compiler can prove LDS reads never alias a DMA in flight
+  // and does not make them wait for it.
+  __shared__ __attribute__((aligned(16))) __bf16 Kb0[C::kUnits * 8];
+  __shared__ __attribute__((aligned(16))) __bf16 Kb1[C::kUnits * 8];
+  __shared__ __attribute__((aligned(16))) __bf16 Vb0[C::kUnits * 8];
+  __shared__ __attribute__((aligned(16))) __bf16 Vb1[C::kUnits * 8];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -252,26 +257,29 @@ void attn_fwd_kernel(
   };
 
   // One pipeline iteration: stage u is consumed, stage u+1's scores issued.
-  auto iterate = [&](int u, f32x16_t (&Scur)[2], f32x16_t (&Snext)[2]) {
+  // kdst / vdst receive the DMAs of stages u+2 (K) and u+1 (V); ksrc holds
+  // K of stage u+1 and vsrc holds V of stage u.
+  auto iterate = [&](int u, f32x16_t (&Scur)[2], f32x16_t (&Snext)[2], __bf16* kdst, __bf16* vdst,
+                     const __bf16* ksrc, const __bf16* vsrc) {
     wait_dma();
     __syncthreads();
-    if (u + 2 < U) dma(stage(u + 2), Kb[u & 1], 0);
-    if (u + 1 < U) dma(stage(u + 1), Vb[(u + 1) & 1], 1);
-    if (u + 1 < U) scores(Kb[(u + 1) & 1], Snext);
-    consume(stage(u), Scur, Vb[u & 1]);
+    if (u + 2 < U) dma(stage(u + 2), kdst, 0);
+    if (u + 1 < U) dma(stage(u + 1), vdst, 1);
+    if (u + 1 < U) scores(ksrc, Snext);
+    consume(stage(u), Scur, vsrc);
   };
 
   if (U > 0) {
-    dma(stage(0), Kb[0], 0);
-    dma(stage(0), Vb[0], 1);
-    if (U > 1) dma(stage(1), Kb[1], 0);
+    dma(stage(0), Kb0, 0);
+    dma(stage(0), Vb0, 1);
+    if (U > 1) dma(stage(1), Kb1, 0);
     wait_dma();
     __syncthreads();
     f32x16_t SA[2], SB[2];
-    scores(Kb[0], SA);
+    scores(Kb0, SA);
     for (int u = 0; u < U; u += 2) {
-      iterate(u, SA, SB);
-      if (u + 1 < U) iterate(u + 1, SB, SA);
+      iterate(u, SA, SB, Kb0, Vb1, Kb1, Vb0);
+      if (u + 1 < U) iterate(u + 1, SB, SA, Kb1, Vb0, Kb0, Vb1);
     }
   }
 

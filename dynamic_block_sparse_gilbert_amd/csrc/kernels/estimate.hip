@@ -4,42 +4,87 @@
 // of K; P_approx = softmax(Q_s K_s^T * scale) over all sampled keys; P_imp is
 // its max-pool over each (samples of I) x (samples of J) tile.
 //
-// Sampled tokens are addressed through a compact index r = J*k + t (t < k):
-// slot t of block J is reordered row J*b + floor(t*L_J/k_J) when t < k_J =
-// min(k, L_J), and an empty slot otherwise (only the last block can have
-// empty slots).  Since softmax is monotone in the score,
+// Sampled tokens use a compact index r = J*k + t (t < k): slot t of block J is
+// reordered row J*b + floor(t*L_J/k_J) when t < k_J = min(k, L_J), and an
+// empty slot otherwise (only the last block can have empty slots).  Since
+// softmax is monotone in the score,
 //     P_imp[I, J] = exp2( max_{q in I, c in J} (x_qc - lse2_q) ),
-// with x = score * scale * log2(e) and lse2_q = log2 sum_c exp2(x_qc).  Two
-// passes over the sampled keys therefore suffice and nothing of size
-// (sampled queries) x nb is ever stored:
-//   pass 1 (stats):    online max / sum per sampled query -> lse2 (workspace);
-//   pass 2 (blockmax): recompute x, subtract lse2, max-reduce each k x k
-//                      group with lane butterflies, one exp2 per group.
-// Both passes run S^T = K_s Q_s^T on bf16 MFMA 16x16x32 with fp32
-// accumulation; a workgroup of 8 wavefronts owns 128 sampled queries (16 per
-// wavefront, kept in VGPRs) and streams the sampled keys through LDS in
-// chunks of 64, so every key chunk is read once per 128 queries.
+// with x = score * scale * log2(e) and lse2_q = log2 sum_c exp2(x_qc); so two
+// passes over the sampled keys suffice and nothing of size (sampled queries)
+// x nb is ever stored.  Three launches:
+//   gather:   copy the sampled rows of Q and K into compact row-major arrays
+//             (zero rows for empty slots) in the workspace;
+//   stats:    online max / sum per sampled query over a range of the sampled
+//             keys -> one partial (max, sum) per key split;
+//   blockmax: merge the partials into lse2, recompute x over its own key range,
+//             subtract lse2, reduce each k x k group, one exp2 per group.
+// The key range is split over enough workgroups (about 4096 in total) that
+// the DMA latency of each key chunk is hidden by other resident workgroups.
+// Both passes compute S^T = K_s Q_s^T on bf16 MFMA 16x16x32 with fp32
+// accumulation.  A workgroup of 4 wavefronts owns 64 sampled queries (16 per
+// wavefront, in VGPRs); the compact keys stream through double-buffered,
+// XOR-swizzled LDS in chunks of 64 by the global->LDS DMA path.  Lane
+// reductions use DPP row permutations and v_permlane16/32_swap (VALU, no LDS).
 #include "common.h"
 #include "../launch.h"
 
 namespace dbs {
 namespace {
 
-constexpr int kWaves = 8;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kQPerWg = kWaves * 16;
 constexpr int kChunk = 64;
+constexpr int kMaxChunksPerSplit = 64;   // bound on chunks per key split (LDS staging)
+
+__device__ __forceinline__ int swz(int u) { return (u & ~15) | ((u & 15) ^ ((u >> 4) & 15)); }
+
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Lane-exchange reductions (max).  The DPP controls are row-local (16 lanes):
+// quad_perm [1,0,3,2] = 0xb1, quad_perm [2,3,0,1] = 0x4e, row_half_mirror =
+// 0x141, row_mirror = 0x140.  Mirrors are enough for a reduction: after the
+// two quad steps every quad holds its maximum, the half-mirror pairs quad 0
+// with 1 (and 2 with 3), the mirror pairs the two halves of the row.
+__device__ __forceinline__ float dpp_max(float v, int ctrl) {
+  const int o = (ctrl == 0xb1) ? __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf, false)
+              : (ctrl == 0x4e) ? __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4e, 0xf, 0xf, false)
+              : (ctrl == 0x141) ? __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false)
+                                : __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false);
+  return fmaxf(v, __int_as_float(o));
+}
+// max over lanes l and l ^ 16 / l ^ 32
+__device__ __forceinline__ float max_x16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_x32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_x16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_x32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 struct SampleGeom {
-  int N, b, k, klog2, nb, nsp, kj_last;
+  int N, b, k, klog2, nb, nsp, nsp_pad, kj_last;
+  int splits, cps;   // key splits and 64-key chunks per split
   // Reordered row of compact slot r, or -1 for an empty slot / r >= nsp.
   __device__ __forceinline__ int row(int r) const {
     if (r >= nsp) return -1;
     const int J = r >> klog2, t = r & (k - 1);
-    const int L = min(b, N - J * b);
-    const int kJ = min(k, L);
-    if (t >= kJ) return -1;
-    return J * b + (t * L) / kJ;
+    if (J < nb - 1) return J * b + t * (b >> klog2);   // full block: L = b, k_J = k
+    const int L = N - J * b;
+    if (t >= kj_last) return -1;
+    return J * b + (t * L) / kj_last;
   }
   __device__ __forceinline__ bool valid(int r) const {
     if (r >= nsp) return false;
@@ -47,103 +92,163 @@ struct SampleGeom {
   }
 };
 
+// Workgroup -> (bh, key split, query panel).  Logical ids run panel-fastest,
+// then split, then (batch, head), and are spread so that each XCD gets a
+// contiguous range: one head's sampled keys then stay in one XCD's L2.
+__device__ __forceinline__ void wg_coords(const SampleGeom& sg, int& bh, int& split, int& panel) {
+  const int panels = (sg.nsp + kQPerWg - 1) / kQPerWg;
+  const int total = gridDim.x;
+  const int id = xcd_remap(blockIdx.x, total);
+  panel = id % panels;
+  split = (id / panels) % sg.splits;
+  bh = id / (panels * sg.splits);
+}
+
+// Compact copies of the sampled rows: qs/ks [BH][nsp_pad][D], zero rows for
+// empty slots and padding.  One thread per 16-byte chunk.
 template <int D>
-__device__ __forceinline__ void load_q(const __bf16* q_r, int64_t rowbase, const SampleGeom& sg,
-                                       int rq, int g4, bf16x8_t (&qreg)[D / 32]) {
-  const int src = sg.row(rq);
+__global__ __launch_bounds__(256) void est_gather_kernel(
+    const __bf16* __restrict__ q_r, const __bf16* __restrict__ k_r, __bf16* __restrict__ qs,
+    __bf16* __restrict__ ks, SampleGeom sg, int Npad) {
+  const int bh = blockIdx.y;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int r = idx / (D / 8), c = idx % (D / 8);
+  if (r >= sg.nsp_pad) return;
+  const int src = sg.row(r);
+  uint4 vq = make_uint4(0, 0, 0, 0), vk = vq;
+  if (src >= 0) {
+    const int64_t off = ((int64_t)bh * Npad + src) * D + 8 * c;
+    vq = *reinterpret_cast<const uint4*>(q_r + off);
+    vk = *reinterpret_cast<const uint4*>(k_r + off);
+  }
+  const int64_t dst = ((int64_t)bh * sg.nsp_pad + r) * D + 8 * c;
+  *reinterpret_cast<uint4*>(qs + dst) = vq;
+  *reinterpret_cast<uint4*>(ks + dst) = vk;
+}
+
+// Empty key slots of a chunk get a score of -inf (the rare chunks that hold
+// padding or the last block's empty slots; kept out of the common path).
+__device__ __forceinline__ void mask_chunk(const SampleGeom& sg, int ck0, int g4, f32x4_t (&s)[4]) {
 #pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk) {
-    if (src >= 0) {
-      qreg[kk] = *reinterpret_cast<const bf16x8_t*>(q_r + (rowbase + src) * D + 32 * kk + 8 * g4);
-    } else {
-      qreg[kk] = bf16x8_t{};
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (!sg.valid(ck0 + 16 * t + 4 * g4 + j)) s[t][j] = -INFINITY;
+}
+
+// Common streaming loop: for every chunk of 64 compact keys, S^T tiles of the
+// wave's 16 queries (s[t][j]: key ck0 + 16t + 4*g4 + j, query l16) are handed
+// to `body(ck0, s)`.
+template <int D, typename Body>
+__device__ __forceinline__ void stream_keys(const __bf16* ks_bh, int c0, int c1,
+                                            const bf16x8_t (&qreg)[D / 32], Body&& body) {
+  constexpr int kUnits = kChunk * D / 8;       // 16-byte units per chunk
+  constexpr int kPer = kUnits / 64 / kWaves;   // DMA instructions per wave per chunk
+  // Two distinct arrays with statically known roles in each half of the
+  // 2x-unrolled loop: the compiler can then prove that the LDS reads of one
+  // buffer do not alias the DMA in flight into the other, and does not insert
+  // a wait for that DMA before the reads.
+  __shared__ __attribute__((aligned(16))) __bf16 Kc0[kUnits * 8];
+  __shared__ __attribute__((aligned(16))) __bf16 Kc1[kUnits * 8];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  int off[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int u = swz(64 * (wave + i * kWaves) + lane);
+    off[i] = (u / (D / 8)) * D + (u % (D / 8)) * 8;
+  }
+  auto dma = [&](int chunk, __bf16* buf) {
+    const __bf16* base = ks_bh + (int64_t)chunk * kChunk * D;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int n = wave + i * kWaves;
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(base + off[i]), (lds_void_t*)(buf + 64 * n * 8), 16, 0, 0);
+    }
+  };
+  auto compute = [&](int ch, const __bf16* kb) {
+    f32x4_t s[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      s[t] = f32x4_t{};
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) {
+        const int u = (16 * t + l16) * (D / 8) + 4 * kk + g4;
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kb + swz(u) * 8);
+        s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[kk], s[t], 0, 0, 0);
+      }
+    }
+    body(ch * kChunk, s);
+  };
+  dma(c0, Kc0);
+  for (int ch = c0; ch < c1; ch += 2) {
+    wait_dma();
+    __syncthreads();
+    if (ch + 1 < c1) dma(ch + 1, Kc1);
+    compute(ch, Kc0);
+    if (ch + 1 < c1) {
+      wait_dma();
+      __syncthreads();
+      if (ch + 2 < c1) dma(ch + 2, Kc0);
+      compute(ch + 1, Kc1);
     }
   }
 }
 
-// Stage kChunk sampled key rows starting at compact index ck0 into LDS.
 template <int D>
-__device__ __forceinline__ void load_keys(const __bf16* k_r, int64_t rowbase, const SampleGeom& sg,
-                                          int ck0, __bf16* Kc) {
-  constexpr int kStride = D + 8;
+__device__ __forceinline__ void load_q(const __bf16* qs_bh, int rq, int g4, bf16x8_t (&qreg)[D / 32]) {
+  const __bf16* qp = qs_bh + (int64_t)rq * D + 8 * g4;
 #pragma unroll
-  for (int c = threadIdx.x; c < kChunk * D / 8; c += kThreads) {
-    const int rr = c / (D / 8), cc = c % (D / 8);
-    const int src = sg.row(ck0 + rr);
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (src >= 0) v = *reinterpret_cast<const uint4*>(k_r + (rowbase + src) * D + 8 * cc);
-    *reinterpret_cast<uint4*>(Kc + rr * kStride + 8 * cc) = v;
-  }
-}
-
-// Scores of the wave's 16 queries against the 64 staged keys:
-// s[t][j] = key ck0 + 16t + 4*g4 + j, query l16.
-template <int D>
-__device__ __forceinline__ void score_chunk(const __bf16* Kc, int l16, int g4,
-                                            const bf16x8_t (&qreg)[D / 32], f32x4_t (&s)[4]) {
-  constexpr int kStride = D + 8;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    s[t] = f32x4_t{};
-    const __bf16* kp = Kc + (16 * t + l16) * kStride + 8 * g4;
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kp + 32 * kk);
-      s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[kk], s[t], 0, 0, 0);
-    }
-  }
+  for (int kk = 0; kk < D / 32; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * kk);
 }
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void est_stats_kernel(
-    const __bf16* __restrict__ q_r, const __bf16* __restrict__ k_r, float* __restrict__ lse2,
-    SampleGeom sg, int Npad, float sl2) {
-  __shared__ __attribute__((aligned(16))) __bf16 Kc[kChunk * (D + 8)];
+    const __bf16* __restrict__ qs, const __bf16* __restrict__ ks, float2* __restrict__ part,
+    SampleGeom sg, float sl2) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int bh = blockIdx.y;
-  const int64_t rowbase = (int64_t)bh * Npad;
-  const int rq = blockIdx.x * kQPerWg + wave * 16 + l16;
+  int bh, split, panel;
+  wg_coords(sg, bh, split, panel);
+  const int rq = panel * kQPerWg + wave * 16 + l16;
   bf16x8_t qreg[D / 32];
-  load_q<D>(q_r, rowbase, sg, rq, g4, qreg);
-
+  load_q<D>(qs + (int64_t)bh * sg.nsp_pad * D, rq, g4, qreg);
   float m = -INFINITY, l = 0.f;
   const int tail = (sg.nb - 1) * sg.k;   // first slot of the last block
-  for (int ck0 = 0; ck0 < sg.nsp; ck0 += kChunk) {
-    __syncthreads();
-    load_keys<D>(k_r, rowbase, sg, ck0, Kc);
-    __syncthreads();
-    f32x4_t s[4];
-    score_chunk<D>(Kc, l16, g4, qreg, s);
-    const bool check = (ck0 + kChunk > sg.nsp) || (sg.kj_last < sg.k && ck0 + kChunk > tail);
+  const int c0 = split * sg.cps, c1 = min(sg.nsp_pad / kChunk, c0 + sg.cps);
+  stream_keys<D>(ks + (int64_t)bh * sg.nsp_pad * D, c0, c1, qreg, [&](int ck0, f32x4_t (&s)[4]) {
+    if ((ck0 + kChunk > sg.nsp) || (sg.kj_last < sg.k && ck0 + kChunk > tail)) mask_chunk(sg, ck0, g4, s);
     float mx = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float x = s[t][j] * sl2;
-        if (check && !sg.valid(ck0 + 16 * t + 4 * g4 + j)) x = -INFINITY;
-        s[t][j] = x;
-        mx = fmaxf(mx, x);
-      }
-    }
-    mx = fmaxf(mx, xor_shfl(mx, 16));
-    mx = fmaxf(mx, xor_shfl(mx, 32));
+      for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s[t][j]);
+    mx = max_x32(max_x16(mx)) * sl2;
     const float m_new = fmaxf(m, mx);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     l *= fast_exp2(m - m_use);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) l += fast_exp2(s[t][j] - m_use);
+      for (int j = 0; j < 4; ++j) l += fast_exp2(__builtin_fmaf(s[t][j], sl2, -m_use));
     }
     m = m_new;
+  });
+  l = sum_x32(sum_x16(l));
+  if (g4 == 0 && rq < sg.nsp) part[((int64_t)bh * sg.splits + split) * sg.nsp + rq] = make_float2(m, l);
+}
+
+// log2 of the softmax normaliser of sampled query rq from its per-split partials.
+__device__ __forceinline__ float merge_lse2(const float2* part_bh, const SampleGeom& sg, int rq) {
+  float M = -INFINITY;
+  for (int s = 0; s < sg.splits; ++s) M = fmaxf(M, part_bh[(int64_t)s * sg.nsp + rq].x);
+  if (M == -INFINITY) return INFINITY;
+  float L = 0.f;
+  for (int s = 0; s < sg.splits; ++s) {
+    const float2 p = part_bh[(int64_t)s * sg.nsp + rq];
+    L += p.y * fast_exp2(p.x - M);
   }
-  l += xor_shfl(l, 16);
-  l += xor_shfl(l, 32);
-  if (g4 == 0 && rq < sg.nsp) {
-    lse2[(int64_t)bh * sg.nsp + rq] = sg.valid(rq) ? m + __log2f(l) : INFINITY;
-  }
+  return M + __log2f(L);
 }
 
 __global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
@@ -151,84 +256,108 @@ __global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
   if (i < n) p[i] = 0.f;
 }
 
-template <int D>
+// K: the sample count k when k <= 16; 32 stands for every k > 16.  The group
+// side inside one 16 x 16 score tile is min(k, 16); k == 16 stages its one
+// value per tile in LDS, k < 16 stores each group directly, k > 16 combines
+// tiles of the same group with atomicMax (P_imp zeroed first).  A
+// compile-time constant, so the reductions below are straight-line code.
+template <int D, int K>
 __global__ __launch_bounds__(kThreads) void est_blockmax_kernel(
-    const __bf16* __restrict__ q_r, const __bf16* __restrict__ k_r, const float* __restrict__ lse2,
-    float* __restrict__ p_imp, SampleGeom sg, int Npad, float sl2) {
-  __shared__ __attribute__((aligned(16))) __bf16 Kc[kChunk * (D + 8)];
+    const __bf16* __restrict__ qs, const __bf16* __restrict__ ks, const float2* __restrict__ part,
+    float* __restrict__ p_imp, SampleGeom sg, float sl2) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int bh = blockIdx.y;
-  const int64_t rowbase = (int64_t)bh * Npad;
-  const int rq = blockIdx.x * kQPerWg + wave * 16 + l16;
+  int bh, split, panel;
+  wg_coords(sg, bh, split, panel);
+  const int rq = panel * kQPerWg + wave * 16 + l16;
   bf16x8_t qreg[D / 32];
-  load_q<D>(q_r, rowbase, sg, rq, g4, qreg);
-  // an empty query slot contributes -inf to its group
-  const float myl = (rq < sg.nsp) ? lse2[(int64_t)bh * sg.nsp + rq] : INFINITY;
-  const int k = sg.k;
-  const int kr = k < 16 ? k : 16;        // group side inside one 16 x 16 tile
+  load_q<D>(qs + (int64_t)bh * sg.nsp_pad * D, rq, g4, qreg);
+  // an empty query slot (lse2 = +inf) contributes -inf to its group
+  const float myl = (rq < sg.nsp && sg.valid(rq))
+                        ? merge_lse2(part + (int64_t)bh * sg.splits * sg.nsp, sg, rq) : INFINITY;
+  constexpr int kr = K < 16 ? K : 16;
   const int I = rq >> sg.klog2;
-  const bool qrep = (l16 & (kr - 1)) == 0;
+  const bool qrep = (l16 & (kr - 1)) == 0 && rq < sg.nsp;
   float* prow = p_imp + ((int64_t)bh * sg.nb + I) * sg.nb;
   const int tail = (sg.nb - 1) * sg.k;
-
-  for (int ck0 = 0; ck0 < sg.nsp; ck0 += kChunk) {
-    __syncthreads();
-    load_keys<D>(k_r, rowbase, sg, ck0, Kc);
-    __syncthreads();
-    f32x4_t s[4];
-    score_chunk<D>(Kc, l16, g4, qreg, s);
-    const bool check = (ck0 + kChunk > sg.nsp) || (sg.kj_last < sg.k && ck0 + kChunk > tail);
+  const int c0 = split * sg.cps, c1 = min(sg.nsp_pad / kChunk, c0 + sg.cps);
+  // k == 16: one P_imp value per (wave, key tile); results are staged here so
+  // that no global store sits between the key-chunk DMAs (vmcnt counts both).
+  __shared__ float outbuf[kWaves][kMaxChunksPerSplit * 4];
+  float* outw = outbuf[wave];
+  stream_keys<D>(ks + (int64_t)bh * sg.nsp_pad * D, c0, c1, qreg, [&](int ck0, f32x4_t (&s)[4]) {
+    if ((ck0 + kChunk > sg.nsp) || (sg.kj_last < sg.k && ck0 + kChunk > tail)) mask_chunk(sg, ck0, g4, s);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       float u[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u[j] = s[t][j] * sl2 - myl;
-        if (check && !sg.valid(ck0 + 16 * t + 4 * g4 + j)) u[j] = -INFINITY;
-      }
-      // keys: reduce within groups of kr consecutive keys
+      for (int j = 0; j < 4; ++j) u[j] = __builtin_fmaf(s[t][j], sl2, -myl);
+      // keys: reduce within groups of kr consecutive keys (4 per lane, 16 per lane row)
+      constexpr int nv = kr >= 4 ? 1 : 4 / kr;
       float v[4];
-      int nv;
-      if (kr >= 4) {
+      if constexpr (kr >= 4) {
         v[0] = fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3]));
-        if (kr >= 8) v[0] = fmaxf(v[0], xor_shfl(v[0], 16));
-        if (kr >= 16) v[0] = fmaxf(v[0], xor_shfl(v[0], 32));
-        nv = 1;
-      } else if (kr == 2) {
+        if constexpr (kr >= 8) v[0] = max_x16(v[0]);
+        if constexpr (kr >= 16) v[0] = max_x32(v[0]);
+      } else if constexpr (kr == 2) {
         v[0] = fmaxf(u[0], u[1]);
         v[1] = fmaxf(u[2], u[3]);
-        nv = 2;
       } else {
         v[0] = u[0]; v[1] = u[1]; v[2] = u[2]; v[3] = u[3];
-        nv = 4;
       }
-      // queries: reduce within groups of kr consecutive queries (lanes)
-      for (int sft = 1; sft < kr; sft <<= 1) {
+      // queries: reduce within groups of kr consecutive lanes of a row
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (e < nv) v[e] = fmaxf(v[e], xor_shfl(v[e], sft));
+      for (int e = 0; e < nv; ++e) {
+        if constexpr (kr >= 2) v[e] = dpp_max(v[e], 0xb1);
+        if constexpr (kr >= 4) v[e] = dpp_max(v[e], 0x4e);
+        if constexpr (kr >= 8) v[e] = dpp_max(v[e], 0x141);
+        if constexpr (kr >= 16) v[e] = dpp_max(v[e], 0x140);
+      }
+      if constexpr (K == 16) {
+        // one group per tile, held by lane 0: staged in LDS, stored after the loop
+        if (lane == 0) outw[(ck0 / kChunk - c0) * 4 + t] = v[0];
+        continue;
       }
       const bool krep = kr >= 4 ? ((g4 & ((kr >> 2) - 1)) == 0) : true;
-      if (qrep && krep && rq < sg.nsp) {
+      if (qrep && krep) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (e < nv) {
-            const int ck = ck0 + 16 * t + 4 * g4 + e * (4 / nv);
-            if (ck < sg.nsp) {
-              const int J = ck >> sg.klog2;
-              const float p = fast_exp2(v[e]);
-              if (k <= 16) {
-                prow[J] = p;
-              } else {
-                atomicMax(reinterpret_cast<int*>(prow + J), __float_as_int(p));
-              }
+        for (int e = 0; e < nv; ++e) {
+          const int ck = ck0 + 16 * t + 4 * g4 + e * (4 / nv);
+          if (ck < sg.nsp) {
+            const int J = ck >> sg.klog2;
+            const float p = fast_exp2(v[e]);
+            if constexpr (K < 16) {
+              prow[J] = p;
+            } else {
+              atomicMax(reinterpret_cast<int*>(prow + J), __float_as_int(p));
             }
           }
         }
       }
     }
+  });
+  if (K == 16 && rq - l16 < sg.nsp) {
+    // the wave's 16 queries are exactly query block I; J runs over the split's tiles
+    const int nout = (c1 - c0) * 4;
+    for (int i = lane; i < nout; i += 64) {
+      const int J = c0 * 4 + i;
+      if (J < sg.nb) prow[J] = fast_exp2(outw[i]);
+    }
   }
+}
+
+// Key splits: enough workgroups in total (about 4096) to hide the latency of
+// each chunk's DMA behind other resident workgroups.
+void split_plan(int BH, int nsp, int& splits, int& cps) {
+  const int nsp_pad = (nsp + kChunk - 1) / kChunk * kChunk;
+  const int nchunks = nsp_pad / kChunk;
+  const int panels = (nsp + kQPerWg - 1) / kQPerWg;
+  const int64_t wgs = (int64_t)panels * BH;
+  int want = (int)((4096 + wgs - 1) / wgs);
+  want = want < 1 ? 1 : (want > nchunks ? nchunks : want);
+  cps = (nchunks + want - 1) / want;
+  if (cps > kMaxChunksPerSplit) cps = kMaxChunksPerSplit;
+  splits = (nchunks + cps - 1) / cps;
 }
 
 template <int D>
@@ -238,28 +367,53 @@ hipError_t launch_d(const EstimateArgs& a) {
   sg.klog2 = 0;
   while ((1 << sg.klog2) < a.k) ++sg.klog2;
   sg.nsp = a.nb * a.k;
+  sg.nsp_pad = (sg.nsp + kChunk - 1) / kChunk * kChunk;
   const int Llast = a.N - (a.nb - 1) * a.b;
   sg.kj_last = a.k < Llast ? a.k : Llast;
   const float sl2 = a.scale * kLog2e;
-  dim3 grid((sg.nsp + kQPerWg - 1) / kQPerWg, a.B * a.Hh);
-  hipLaunchKernelGGL((est_stats_kernel<D>), grid, dim3(kThreads), 0, a.stream,
-                     (const __bf16*)a.q_r, (const __bf16*)a.k_r, a.lse2, sg, a.Npad, sl2);
+  const int BH = a.B * a.Hh;
+  split_plan(BH, sg.nsp, sg.splits, sg.cps);
+  __bf16* qs = reinterpret_cast<__bf16*>(a.workspace);
+  __bf16* ks = qs + (int64_t)BH * sg.nsp_pad * D;
+  float2* part = reinterpret_cast<float2*>(ks + (int64_t)BH * sg.nsp_pad * D);
+
+  hipLaunchKernelGGL((est_gather_kernel<D>), dim3((sg.nsp_pad * (D / 8) + 255) / 256, BH), dim3(256), 0,
+                     a.stream, (const __bf16*)a.q_r, (const __bf16*)a.k_r, qs, ks, sg, a.Npad);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  dim3 grid((unsigned)(((sg.nsp + kQPerWg - 1) / kQPerWg) * sg.splits * BH));
+  hipLaunchKernelGGL((est_stats_kernel<D>), grid, dim3(kThreads), 0, a.stream, qs, ks, part, sg, sl2);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   if (a.k > 16) {
-    const int64_t n = (int64_t)a.B * a.Hh * a.nb * a.nb;
+    const int64_t n = (int64_t)BH * a.nb * a.nb;
     hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, a.stream,
                        a.p_imp, n);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((est_blockmax_kernel<D>), grid, dim3(kThreads), 0, a.stream,
-                     (const __bf16*)a.q_r, (const __bf16*)a.k_r, (const float*)a.lse2, a.p_imp, sg,
-                     a.Npad, sl2);
+  const float2* pp = part;
+  switch (a.k) {
+    case 1: hipLaunchKernelGGL((est_blockmax_kernel<D, 1>), grid, dim3(kThreads), 0, a.stream, qs, ks, pp, a.p_imp, sg, sl2); break;
+    case 2: hipLaunchKernelGGL((est_blockmax_kernel<D, 2>), grid, dim3(kThreads), 0, a.stream, qs, ks, pp, a.p_imp, sg, sl2); break;
+    case 4: hipLaunchKernelGGL((est_blockmax_kernel<D, 4>), grid, dim3(kThreads), 0, a.stream, qs, ks, pp, a.p_imp, sg, sl2); break;
+    case 8: hipLaunchKernelGGL((est_blockmax_kernel<D, 8>), grid, dim3(kThreads), 0, a.stream, qs, ks, pp, a.p_imp, sg, sl2); break;
+    case 16: hipLaunchKernelGGL((est_blockmax_kernel<D, 16>), grid, dim3(kThreads), 0, a.stream, qs, ks, pp, a.p_imp, sg, sl2); break;
+    default: hipLaunchKernelGGL((est_blockmax_kernel<D, 32>), grid, dim3(kThreads), 0, a.stream, qs, ks, pp, a.p_imp, sg, sl2); break;
+  }
   return hipGetLastError();
 }
 
 }  // namespace
+
+size_t estimate_workspace_bytes(int B, int Hh, int nb, int k, int d) {
+  const int64_t nsp = (int64_t)nb * k;
+  const int64_t nsp_pad = (nsp + kChunk - 1) / kChunk * kChunk;
+  const int64_t BH = (int64_t)B * Hh;
+  int splits, cps;
+  split_plan((int)BH, (int)nsp, splits, cps);
+  return (size_t)(BH * nsp_pad * d * 2 * 2 + BH * splits * nsp * 8);
+}
 
 hipError_t launch_estimate(const EstimateArgs& a) {
   return a.d == 64 ? launch_d<64>(a) : launch_d<128>(a);

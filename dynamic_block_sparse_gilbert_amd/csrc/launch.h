@@ -33,7 +33,7 @@ struct EstimateArgs {
   const void* q_r;
   const void* k_r;
   float* p_imp;
-  float* lse2;          // workspace: one float per sampled query slot
+  void* workspace;      // compact Q_s, K_s (bf16) and lse2 (float); see estimate_workspace_bytes
   int B, Hh, N, Npad, d, b, k, nb;
   float scale;
   hipStream_t stream;
@@ -68,6 +68,7 @@ hipError_t launch_reorder(const ReorderArgs& a);
 hipError_t launch_inverse_reorder(const ReorderArgs& a);
 hipError_t launch_meanpool(const MeanpoolArgs& a);
 hipError_t launch_estimate(const EstimateArgs& a);
+size_t estimate_workspace_bytes(int B, int Hh, int nb, int k, int d);
 hipError_t launch_build_mask(const MaskArgs& a);
 hipError_t launch_attn_fwd(const AttnArgs& a);
 

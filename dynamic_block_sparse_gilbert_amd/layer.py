@@ -79,7 +79,7 @@ class AsaLayer:
         self.v_t = torch.empty((B, Hh, nb, d, s.b), **bf)
         self.o_r = torch.empty((B, Hh, Npad, d), **bf)
         self.p_imp = torch.empty((B, Hh, nb, nb), dtype=torch.float32, device=self.device)
-        self.ws = torch.empty(max(16, ops.estimate_workspace_bytes(B, Hh, s.N, s.b, s.k)),
+        self.ws = torch.empty(max(16, ops.estimate_workspace_bytes(B, Hh, s.N, d, s.b, s.k)),
                               dtype=torch.uint8, device=self.device)
         self.kv_count = torch.empty((B, Hh, nb), dtype=torch.int32, device=self.device)
         self.kv_idx = torch.empty((B, Hh, nb, nb), dtype=torch.int32, device=self.device)

@@ -97,8 +97,8 @@ def inverse_reorder(y: torch.Tensor, perm: torch.Tensor, N: int,
     return out
 
 
-def estimate_workspace_bytes(B: int, Hh: int, N: int, b: int, k: int) -> int:
-    return int(lib().dbs_estimate_workspace_bytes(B, Hh, N, b, k))
+def estimate_workspace_bytes(B: int, Hh: int, N: int, d: int, b: int, k: int) -> int:
+    return int(lib().dbs_estimate_workspace_bytes(B, Hh, N, d, b, k))
 
 
 def estimate_blocks(q_r: torch.Tensor, k_r: torch.Tensor, N: int, b: int, k: int, scale: float,
@@ -110,7 +110,7 @@ def estimate_blocks(q_r: torch.Tensor, k_r: torch.Tensor, N: int, b: int, k: int
     nb = Npad // b
     if p_imp is None:
         p_imp = torch.empty((B, Hh, nb, nb), dtype=torch.float32, device=q_r.device)
-    need = estimate_workspace_bytes(B, Hh, N, b, k)
+    need = estimate_workspace_bytes(B, Hh, N, d, b, k)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_r.device)
     check("dbs_estimate_blocks", lib().dbs_estimate_blocks(

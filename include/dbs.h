@@ -122,9 +122,12 @@ dbs_status dbs_inverse_reorder(const void* y, dbs_dtype y_dt, void* x, dbs_dtype
                                const int32_t* perm, int perm_per_head,
                                int B, int Hh, int N, int Npad, int d, hipStream_t stream);
 
-/* Bytes of device workspace dbs_estimate_blocks needs (one float per sampled
- * query: B * Hh * nb * k * 4).  Returns 0 for invalid sizes. */
-size_t dbs_estimate_workspace_bytes(int B, int Hh, int N, int b, int k);
+/* Bytes of device workspace dbs_estimate_blocks needs: compact copies of the
+ * sampled Q and K rows (B * Hh * ceil(nb*k / 64)*64 * d bf16 each) and one
+ * partial softmax (max, sum) float pair per sampled query and key split (the
+ * library splits the sampled keys over up to nb*k/64 workgroups per query
+ * panel).  Returns 0 for invalid sizes. */
+size_t dbs_estimate_workspace_bytes(int B, int Hh, int N, int d, int b, int k);
 
 /* Block-importance estimation (Video-BLADE "Step 1"; BLADE notes key design 1).
  * From every b-token block J, k_J = min(k, L_J) tokens are sampled at offsets

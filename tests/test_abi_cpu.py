@@ -126,9 +126,9 @@ def test_reorder_validation(dbs):
 def test_estimate_validation(dbs):
     _, L = dbs
     f = L.lib().dbs_estimate_blocks
-    ws = L.lib().dbs_estimate_workspace_bytes(1, 2, 100, 64, 8)
-    assert ws == 1 * 2 * 2 * 8 * 4
-    ok = (A, A, 0, 1, 2, 100, 128, 64, 64, 8, 0.125, A, A, ws, None)
+    ws = L.lib().dbs_estimate_workspace_bytes(1, 2, 100, 128, 64, 8)
+    assert ws == 1 * 2 * 64 * 128 * 2 * 2 + 1 * 2 * 1 * 16 * 8   # compact Q_s, K_s (padded to 64) + 1 split of (m, l)
+    ok = (A, A, 0, 1, 2, 100, 128, 128, 64, 8, 0.125, A, A, ws, None)
     def call(**kw):
         a = list(ok)
         names = ["q", "k", "dt", "B", "Hh", "N", "Npad", "d", "b", "k_", "scale", "p", "w", "wb", "s"]
@@ -143,7 +143,8 @@ def test_estimate_validation(dbs):
     assert call(wb=ws - 4) == -1
     assert call(scale=float("nan")) == -1
     assert call(p=MIS) == -3
-    assert L.lib().dbs_estimate_workspace_bytes(0, 1, 1, 1, 1) == 0
+    assert L.lib().dbs_estimate_workspace_bytes(0, 1, 1, 64, 1, 1) == 0
+    assert L.lib().dbs_estimate_workspace_bytes(1, 1, 1, 96, 1, 1) == 0
 
 
 @cpu_only
