@@ -6,39 +6,48 @@
 // tokens with a +ln(r) logit bias (BLADE notes, key design 2).
 //
 // Decomposition: one workgroup per (batch, head, query block of BLK rows);
-// each wavefront owns 32 query rows (one MFMA tile), which keeps the scores of
-// two stages, P, Q and O in about 180 VGPRs (two wavefronts per SIMD).  Keys
-// are consumed in stages of 64 (a kept block of 128 is two stages;
-// global-token tiles likewise).
+// each wavefront owns 32 query rows (one MFMA tile).  Keys are consumed in
+// stages of 64 (a kept block of 128 is two stages; global-token tiles
+// likewise).
 //   S^T = K Q^T      bf16 MFMA 32x32x16, Q^T resident in VGPRs.  The
 //                    accumulator layout gives each lane the scores of single
 //                    queries, so softmax statistics stay in the lane (one
 //                    exchange between the two wave halves per stage).
-//   P^T = exp2(S^T * scale*log2e - m)   fp32, packed to bf16 by v_cvt_pk.
+//   P^T = exp2(S^T * scale*log2e - m)   fp32 (row sums in fp32), packed to
+//                    bf16 by v_cvt_pk.
 //   O^T += V^T P^T   bf16 MFMA 32x32x16; P^T comes straight from the score
 //                    accumulators.  Inside each 16-key step the MFMA k index
 //                    maps to keys {4g..4g+3, 8+4g..8+4g+3} (g = wave half) for
 //                    both operands; V tiles store every 16 keys in the order
 //                    0-3, 8-11, 4-7, 12-15, so a lane's 8 keys of one channel
 //                    are one contiguous 16-byte LDS read.
-// Pipelining: K and V stages are copied global -> LDS by the DMA path
-// (global_load_lds_dwordx4, no VGPR staging) into double buffers, two stages
-// ahead for K and one for V.  Within an iteration the MFMAs of the next
-// stage's scores are issued before the softmax of the current stage, so the
-// matrix core and the VALU work concurrently.  LDS tiles are XOR-swizzled in
-// 16-byte units (unit ^= line & 15 within each 256-byte line); the swizzle is
-// applied by choosing each lane's DMA source address.
+//
+// Software pipeline per stage u (one basic block, two phases):
+//   phase A: score MFMAs of stage u+1   ||  exp / pack / row-sum of stage u
+//   phase B: PV MFMAs of stage u        ||  row maximum of stage u+1
+//   then, for partial / global-token stages only, the key mask and bias and a
+//   fresh maximum, and the (rarely taken) lazy rescale decided from stage
+//   u+1's maximum.  Two wavefronts per SIMD from different workgroups fill
+//   each other's gaps; forcing an instruction interleave measured slower.
+// K and V stages are copied global -> LDS by the DMA path
+// (global_load_lds_dwordx4, no VGPR staging) into double buffers one
+// iteration ahead of their use.  LDS rows are padded by one 16-byte unit, so
+// the 8 lanes that share a bank window read 8 different 16-byte bank groups
+// and every read address is one per-lane base register plus an immediate.
 // Online softmax with a lazy rescale: the running maximum is raised (and O, l
 // rescaled) only when a stage's maximum exceeds it by more than 8 (log2
 // units), so probabilities stay below 2^8 and most stages skip the rescale.
 #include "common.h"
 #include "../launch.h"
 
+#include <type_traits>
+
 namespace dbs {
 namespace {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
 template <int D, int BLK>
 struct AttnCfg {
@@ -47,27 +56,38 @@ struct AttnCfg {
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kKT = 64;                 // keys per stage
   static constexpr int kSubs = BLK / kKT;        // stages per block
-  static constexpr int kUnits = kKT * D / 8;     // 16-byte units per K (or V) stage
-  static constexpr int kDma = kUnits / 64;       // DMA instructions per stage
-  static constexpr int kKRow = D / 8;            // units per K row
-  static constexpr int kVRow = kKT / 8;          // units per V^T row
+  // K stage in LDS: 64 key rows of D bf16, each padded by one 16-byte unit.
+  static constexpr int kKRowU = D / 8 + 1;
+  static constexpr int kKStride = kKRowU * 16;   // bytes per padded K row
+  static constexpr int kKBytes = kKT * kKStride;
+  static constexpr int kKInstr = kKBytes / 1024; // DMA instructions (1 KiB each) per K stage
+  // V^T stage in LDS: D channel rows of 64 keys, each padded by one unit.
+  static constexpr int kVRowU = kKT / 8 + 1;
+  static constexpr int kVStride = kVRowU * 16;
+  static constexpr int kVBytes = D * kVStride;
+  static constexpr int kVInstr = kVBytes / 1024;
+  static constexpr int kKPer = (kKInstr + kWaves - 1) / kWaves;   // per wave
+  static constexpr int kVPer = (kVInstr + kWaves - 1) / kWaves;
+  static_assert(kKBytes % 1024 == 0 && kVBytes % 1024 == 0, "stage must be whole DMA instructions");
 };
 
 constexpr float kLazyThreshold = 8.0f;
 
-// Physical 16-byte unit of logical unit u (an involution).
-__device__ __forceinline__ int swz(int u) { return (u & ~15) | ((u & 15) ^ ((u >> 4) & 15)); }
-
-__device__ __forceinline__ bf16x8_t lds_read16(const __bf16* base, int unit) {
-  return *reinterpret_cast<const bf16x8_t*>(base + swz(unit) * 8);
-}
-
 __device__ __forceinline__ uint32_t cvt_pk(float a, float b) {
-  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
   bf16x2_t p;
   p[0] = (__bf16)a;
   p[1] = (__bf16)b;
   return __builtin_bit_cast(uint32_t, p);
+}
+
+__device__ __forceinline__ float max_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -87,17 +107,18 @@ void attn_fwd_kernel(
     const int32_t* __restrict__ kv_count, const int32_t* __restrict__ kv_idx,
     const __bf16* __restrict__ k_g, const __bf16* __restrict__ v_g,
     __bf16* __restrict__ o_r, float* __restrict__ lse,
-    int Hh, int N, int Npad, int nb, int Ng, float sl2, float log2n, float log2r_last, int total) {
+    int Hh, int N, int Npad, int nb, int Ng, float sl2, float bias_n, float bias_last, int total) {
   using C = AttnCfg<D, BLK>;
   // Four distinct arrays whose roles are static in each half of the 2x-unrolled
   // pipeline, so the compiler can prove LDS reads never alias a DMA in flight
   // and does not make them wait for it.
-  __shared__ __attribute__((aligned(16))) __bf16 Kb0[C::kUnits * 8];
-  __shared__ __attribute__((aligned(16))) __bf16 Kb1[C::kUnits * 8];
-  __shared__ __attribute__((aligned(16))) __bf16 Vb0[C::kUnits * 8];
-  __shared__ __attribute__((aligned(16))) __bf16 Vb1[C::kUnits * 8];
+  __shared__ __attribute__((aligned(1024))) char Vb0[C::kVBytes];
+  __shared__ __attribute__((aligned(1024))) char Vb1[C::kVBytes];
+  __shared__ __attribute__((aligned(1024))) char Kb0[C::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char Kb1[C::kKBytes];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int wid = xcd_remap(blockIdx.x, total);
   const int I = wid % nb;
@@ -135,26 +156,48 @@ void attn_fwd_kernel(
     return s;
   };
 
-  // Per-lane source offsets (elements) of the swizzled DMA: loop invariant.
-  constexpr int kPer = C::kDma / C::kWaves;   // DMA instructions per wave per stage
-  int koff[kPer], voff[kPer];
+  // Per-lane source offsets (elements) of the padded DMA: loop invariant.
+  // LDS byte 1024 n + 16 lane of a stage holds padded unit p = 64 n + lane,
+  // i.e. row p / rowU, unit p % rowU; the pad unit re-reads the row's last
+  // unit (same cache line, no extra traffic).
+  int koff[C::kKPer], voff[C::kVPer];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int n = wave + i * C::kWaves;
-    const int u = swz(64 * n + lane);          // logical unit held by this lane's slot
-    koff[i] = (u / C::kKRow) * D + (u % C::kKRow) * 8;
-    voff[i] = (u / C::kVRow) * BLK + (u % C::kVRow) * 8;
+  for (int i = 0; i < C::kKPer; ++i) {
+    const int p = 64 * (wave + i * C::kWaves) + lane;
+    const int row = p / C::kKRowU, c = min(p % C::kKRowU, C::kKRowU - 2);
+    koff[i] = row * D + c * 8;
   }
-
-  // DMA one stage of K (kv = 0) or V^T (kv = 1) into an LDS buffer.
-  auto dma = [&](const StageDesc& s, __bf16* buf, int kv) {
-    const __bf16* base = kv == 0 ? s.k : s.v;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
+  for (int i = 0; i < C::kVPer; ++i) {
+    const int p = 64 * (wave + i * C::kWaves) + lane;
+    const int row = p / C::kVRowU, c = min(p % C::kVRowU, C::kVRowU - 2);
+    voff[i] = row * BLK + c * 8;
+  }
+  auto dma_k = [&](const StageDesc& s, char* buf) {
+#pragma unroll
+    for (int i = 0; i < C::kKPer; ++i) {
       const int n = wave + i * C::kWaves;
-      const __bf16* src = base + (kv == 0 ? koff[i] : voff[i]);
-      __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)(buf + 64 * n * 8), 16, 0, 0);
+      if (C::kKInstr % C::kWaves == 0 || n < C::kKInstr)
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(s.k + koff[i]), (lds_void_t*)(buf + 1024 * n), 16, 0, 0);
     }
+  };
+  auto dma_v = [&](const StageDesc& s, char* buf) {
+#pragma unroll
+    for (int i = 0; i < C::kVPer; ++i) {
+      const int n = wave + i * C::kWaves;
+      if (C::kVInstr % C::kWaves == 0 || n < C::kVInstr)
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(s.v + voff[i]), (lds_void_t*)(buf + 1024 * n), 16, 0, 0);
+    }
+  };
+
+  // Per-lane LDS read bases (bytes): K row l32 at unit g; V^T row l32 at unit g.
+  const int kbase = l32 * C::kKStride + 16 * g;
+  const int vbase = l32 * C::kVStride + 16 * g;
+  auto read_k = [&](const char* kb, int kt, int kk) {
+    return *reinterpret_cast<const bf16x8_t*>(kb + kbase + kt * 32 * C::kKStride + kk * 32);
+  };
+  auto read_v = [&](const char* vb, int dt, int st) {
+    return *reinterpret_cast<const bf16x8_t*>(vb + vbase + dt * 32 * C::kVStride + st * 32);
   };
 
   // Q^T operand: lane (l32, g) holds Q[q0 + l32][16 kk + 8 g .. +7].
@@ -168,123 +211,166 @@ void attn_fwd_kernel(
   f32x16_t oacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16_t{};
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY, mneg = 0.f, l = 0.f;
 
-  // S^T[kt] for the stage held in K buffer kb: keys 32 kt + (v/4)*8 + 4g + v%4.
-  auto scores = [&](const __bf16* kb, f32x16_t (&S)[2]) {
+  // S^T tiles of one stage: S[kt][v] is key 32 kt + (v/4)*8 + 4g + v%4 of
+  // query l32.
+  auto scores = [&](const char* kb, f32x16_t (&S)[2]) {
     S[0] = f32x16_t{};
     S[1] = f32x16_t{};
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8_t a = lds_read16(kb, (32 * kt + l32) * C::kKRow + 2 * kk + g);
-        S[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], S[kt], 0, 0, 0);
+      for (int kt = 0; kt < 2; ++kt)
+        S[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_k(kb, kt, kk), qreg[kk], S[kt], 0, 0, 0);
+    }
+  };
+
+  // Partial, invalid and global-token stages: move the ASA_G bias into the raw
+  // score domain (ln r / scale) and mask keys past the stage's limit.
+  auto fixup = [&](const StageDesc& s, f32x16_t (&S)[2]) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = s.key0 + 32 * kt + (v >> 2) * 8 + 4 * g + (v & 3);
+        float t = S[kt][v];
+        if (s.kind == 2) t += (key < s.limit - 1) ? bias_n : bias_last;
+        S[kt][v] = key >= s.limit ? -INFINITY : t;
       }
     }
   };
 
-  // Softmax of a stage's scores, then O^T += V^T P^T from V buffer vb.
-  auto consume = [&](const StageDesc& s, f32x16_t (&S)[2], const __bf16* vb) {
-    float mx = -INFINITY;
-    if (s.kind == 0) {
+  auto row_max = [&](const f32x16_t (&S)[2]) {
+    float a = S[0][0], b = S[1][0];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[kt][v]);
-      mx *= sl2;
-    } else {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = s.key0 + 32 * kt + (v >> 2) * 8 + 4 * g + (v & 3);
-          float t = S[kt][v] * sl2;
-          if (s.kind == 2) t += (key < s.limit - 1) ? log2n : log2r_last;
-          if (key >= s.limit) t = -INFINITY;
-          S[kt][v] = t;
-          mx = fmaxf(mx, t);
-        }
-      }
+    for (int v = 1; v < 15; v += 2) {
+      a = fmaxf(a, fmaxf(S[0][v], S[0][v + 1]));
+      b = fmaxf(b, fmaxf(S[1][v], S[1][v + 1]));
     }
-    mx = fmaxf(mx, xor_shfl(mx, 32));
+    a = fmaxf(a, S[0][15]);
+    b = fmaxf(b, S[1][15]);
+    return fmaxf(a, b);
+  };
+
+  // Raise the running maximum (log2 units) when the stage maximum mx_raw (raw
+  // score units) exceeds it by more than the lazy threshold.
+  auto decide = [&](float mx_raw) {
+    const float mx = max_halves(mx_raw) * sl2;
     const bool need = mx > m + kLazyThreshold;
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
-      const float m_new = need ? mx : m;
-      const float alpha = need ? fast_exp2(m - m_new) : 1.f;
-      m = m_new;
+      const float alpha = need ? fast_exp2(m - mx) : 1.f;
+      m = need ? mx : m;
       l *= alpha;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
     }
-    const float m_use = (m == -INFINITY) ? 0.f : m;
-    float ls = 0.f;
-    if (s.kind == 0) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float p = fast_exp2(__builtin_fmaf(S[kt][v], sl2, -m_use));
-          ls += p;
-          S[kt][v] = p;
-        }
-    } else {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float p = fast_exp2(S[kt][v] - m_use);
-          ls += p;
-          S[kt][v] = p;
-        }
-    }
-    l += ls;
+    mneg = (m == -INFINITY) ? 0.f : -m;
+  };
+
+  // Phase A: probabilities of the current stage (and, with a next stage, the
+  // next stage's score MFMAs interleaved with them).
+  auto phase_a = [&](const f32x16_t (&Sc)[2], f32x16_t (&Sn)[2], const char* ksrc, uint32_t (&P)[16],
+                      auto has_next) {
+    constexpr bool kNext = decltype(has_next)::value;
+    if constexpr (kNext) scores(ksrc, Sn);
+    float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int kt = st >> 1, o = (st & 1) * 8;
-      uint4 w;
-      w.x = cvt_pk(S[kt][o + 0], S[kt][o + 1]);
-      w.y = cvt_pk(S[kt][o + 2], S[kt][o + 3]);
-      w.z = cvt_pk(S[kt][o + 4], S[kt][o + 5]);
-      w.w = cvt_pk(S[kt][o + 6], S[kt][o + 7]);
-      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, w);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const bf16x8_t a = lds_read16(vb, (32 * dt + l32) * C::kVRow + 2 * st + g);
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[dt], 0, 0, 0);
+      for (int e = 0; e < 4; ++e) {
+        const float pa = fast_exp2(__builtin_fmaf(Sc[kt][o + 2 * e], sl2, mneg));
+        const float pb = fast_exp2(__builtin_fmaf(Sc[kt][o + 2 * e + 1], sl2, mneg));
+        P[4 * st + e] = cvt_pk(pa, pb);
+        s0 += pa;
+        s1 += pb;
       }
     }
+    l += s0 + s1;
+    asm volatile("" ::"v"(l));   // keep the row sums in this phase
   };
 
-  // One pipeline iteration: stage u is consumed, stage u+1's scores issued.
-  // kdst / vdst receive the DMAs of stages u+2 (K) and u+1 (V); ksrc holds
-  // K of stage u+1 and vsrc holds V of stage u.
-  auto iterate = [&](int u, f32x16_t (&Scur)[2], f32x16_t (&Snext)[2], __bf16* kdst, __bf16* vdst,
-                     const __bf16* ksrc, const __bf16* vsrc) {
+  // Phase B: O^T += V^T P^T for the current stage (and the next stage's
+  // row maximum interleaved with it).
+  auto phase_b = [&](const char* vsrc, const uint32_t (&P)[16], const f32x16_t (&Sn)[2], auto has_next) {
+    constexpr bool kNext = decltype(has_next)::value;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      uint4 w;
+      w.x = P[4 * st + 0];
+      w.y = P[4 * st + 1];
+      w.z = P[4 * st + 2];
+      w.w = P[4 * st + 3];
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, w);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_v(vsrc, dt, st), pb, oacc[dt], 0, 0, 0);
+    }
+    float mx = -INFINITY;
+    if constexpr (kNext) mx = row_max(Sn);
+    return mx;
+  };
+
+  // One pipeline iteration for stage u with a next stage u+1.  kdst / vdst
+  // receive the DMAs of stages u+2 (K) and u+1 (V); ksrc holds K of stage u+1
+  // and vsrc holds V of stage u.
+  auto iterate = [&](int u, const f32x16_t (&Sc)[2], f32x16_t (&Sn)[2], char* kdst, char* vdst,
+                     const char* ksrc, const char* vsrc) {
     wait_dma();
     __syncthreads();
-    if (u + 2 < U) dma(stage(u + 2), kdst, 0);
-    if (u + 1 < U) dma(stage(u + 1), vdst, 1);
-    if (u + 1 < U) scores(ksrc, Snext);
-    consume(stage(u), Scur, vsrc);
+    if (u + 2 < U) dma_k(stage(u + 2), kdst);
+    const StageDesc sn = stage(u + 1);
+    dma_v(sn, vdst);
+    uint32_t P[16];
+    phase_a(Sc, Sn, ksrc, P, std::true_type{});
+    float mx = phase_b(vsrc, P, Sn, std::true_type{});
+    // Pin the maximum inside the phase (otherwise it is sunk past the branch
+    // below, away from the MFMAs it is meant to overlap).
+    asm volatile("" ::"v"(mx));
+    if (sn.kind != 0) {
+      fixup(sn, Sn);
+      mx = row_max(Sn);
+    }
+    decide(mx);
+  };
+
+  // The last stage: no next stage to score.
+  auto last = [&](const f32x16_t (&Sc)[2], const char* vsrc) {
+    wait_dma();
+    __syncthreads();
+    uint32_t P[16];
+    f32x16_t unused[2];
+    phase_a(Sc, unused, nullptr, P, std::false_type{});
+    phase_b(vsrc, P, unused, std::false_type{});
   };
 
   if (U > 0) {
-    dma(stage(0), Kb0, 0);
-    dma(stage(0), Vb0, 1);
-    if (U > 1) dma(stage(1), Kb1, 0);
+    const StageDesc s0 = stage(0);
+    dma_k(s0, Kb0);
+    dma_v(s0, Vb0);
+    if (U > 1) dma_k(stage(1), Kb1);
     wait_dma();
     __syncthreads();
     f32x16_t SA[2], SB[2];
     scores(Kb0, SA);
-    for (int u = 0; u < U; u += 2) {
+    if (s0.kind != 0) fixup(s0, SA);
+    decide(row_max(SA));
+    int u = 0;
+    for (; u + 2 < U; u += 2) {
       iterate(u, SA, SB, Kb0, Vb1, Kb1, Vb0);
-      if (u + 1 < U) iterate(u + 1, SB, SA, Kb1, Vb0, Kb0, Vb1);
+      iterate(u + 1, SB, SA, Kb1, Vb0, Kb0, Vb1);
+    }
+    if (u + 1 < U) {
+      iterate(u, SA, SB, Kb0, Vb1, Kb1, Vb0);
+      last(SB, Vb1);
+    } else {
+      last(SA, Vb0);
     }
   }
 
   // ---- epilogue -------------------------------------------------------------------
-  const float lt = l + xor_shfl(l, 32);
+  const float lt = sum_halves(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const int q = q0 + l32;
   if (q < N) {
@@ -309,15 +395,16 @@ template <int D, int BLK>
 hipError_t launch(const AttnArgs& a) {
   const int total = a.B * a.Hh * a.nb;
   const float sl2 = a.scale * kLog2e;
-  float log2n = 0.f, log2r_last = 0.f;
+  float bias_n = 0.f, bias_last = 0.f;
   if (a.k_g != nullptr) {
-    log2n = std::log2((float)a.n_pool);
-    log2r_last = std::log2((float)(a.N - (a.Ng - 1) * a.n_pool));
+    // ln r in raw score units: the kernel multiplies scores by scale * log2(e)
+    bias_n = (float)(std::log((double)a.n_pool) / a.scale);
+    bias_last = (float)(std::log((double)(a.N - (a.Ng - 1) * a.n_pool)) / a.scale);
   }
   hipLaunchKernelGGL((attn_fwd_kernel<D, BLK>), dim3(total), dim3(AttnCfg<D, BLK>::kThreads), 0,
                      a.stream, (const __bf16*)a.q_r, (const __bf16*)a.k_r, (const __bf16*)a.v_t,
                      a.kv_count, a.kv_idx, (const __bf16*)a.k_g, (const __bf16*)a.v_g,
-                     (__bf16*)a.o_r, a.lse, a.Hh, a.N, a.Npad, a.nb, a.Ng, sl2, log2n, log2r_last,
+                     (__bf16*)a.o_r, a.lse, a.Hh, a.N, a.Npad, a.nb, a.Ng, sl2, bias_n, bias_last,
                      total);
   return hipGetLastError();
 }
