@@ -90,10 +90,11 @@ def run_steps(layer, q, k, v, out, tau, steps, warmup, torch):
         ops.estimate_blocks(layer.q_r, layer.k_r, sp.N, sp.b, sp.k, sp.scale, p_imp=layer.p_imp,
                             workspace=layer.ws)
         e[2].record()
-        ops.build_mask(layer.p_imp, tau, kv_count=layer.kv_count, kv_idx=layer.kv_idx)
+        ops.build_mask(layer.p_imp, tau, kv_count=layer.kv_count, kv_idx=layer.kv_idx, order=layer.order)
         e[3].record()
         ops.sparse_attn_fwd(layer.q_r, layer.k_r, layer.v_t, sp.N, sp.b, sp.scale, layer.kv_count,
-                            layer.kv_idx, layer.k_g, layer.v_g, layer.Ng, sp.n_pool, o_r=layer.o_r)
+                            layer.kv_idx, layer.k_g, layer.v_g, layer.Ng, sp.n_pool, o_r=layer.o_r,
+                            order=layer.order)
         e[4].record()
         ops.inverse_reorder(layer.o_r, layer.perm, sp.N, out=out)
         e[5].record()

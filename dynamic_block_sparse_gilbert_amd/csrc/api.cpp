@@ -212,17 +212,18 @@ dbs_status dbs_estimate_blocks(const void* q_r, const void* k_r, dbs_dtype dt, i
 }
 
 dbs_status dbs_build_mask(const float* p_imp, int B, int Hh, int nb, float tau, int32_t* kv_count,
-                          int32_t* kv_idx, uint8_t* mask, hipStream_t stream) {
+                          int32_t* kv_idx, uint8_t* mask, int32_t* order, hipStream_t stream) {
   DBS_GUARD_BEGIN
   REQUIRE(p_imp && kv_count && kv_idx, DBS_ERR_INVALID_ARG, "NULL pointer");
-  REQUIRE(((uintptr_t)p_imp & 3u) == 0 && ((uintptr_t)kv_count & 3u) == 0 && ((uintptr_t)kv_idx & 3u) == 0,
+  REQUIRE(((uintptr_t)p_imp & 3u) == 0 && ((uintptr_t)kv_count & 3u) == 0 && ((uintptr_t)kv_idx & 3u) == 0 &&
+              ((uintptr_t)order & 3u) == 0,
           DBS_ERR_ALIGNMENT, "misaligned pointer");
   REQUIRE(B >= 1 && Hh >= 1, DBS_ERR_INVALID_ARG, "B and Hh must be >= 1");
   REQUIRE(nb >= 1 && nb <= 4096, DBS_ERR_UNSUPPORTED, "nb=%d must be in [1, 4096]", nb);
   REQUIRE(tau > 0.f && tau <= 1.f, DBS_ERR_INVALID_ARG, "tau=%g must be in (0, 1]", (double)tau);
   REQUIRE((int64_t)B * Hh * nb <= INT32_MAX, DBS_ERR_INVALID_ARG, "too many rows");
   dbs::MaskArgs a{};
-  a.p_imp = p_imp; a.kv_count = kv_count; a.kv_idx = kv_idx; a.mask = mask;
+  a.p_imp = p_imp; a.kv_count = kv_count; a.kv_idx = kv_idx; a.mask = mask; a.order = order;
   a.rows = B * Hh * nb; a.nb = nb; a.tau = tau; a.stream = stream;
   return from_hip(dbs::launch_build_mask(a), "dbs_build_mask launch");
   DBS_GUARD_END
@@ -248,14 +249,15 @@ dbs_status dbs_meanpool_kv(const void* k_r, const void* v_r, dbs_dtype dt, int B
 
 dbs_status dbs_sparse_attn_fwd(const void* q_r, const void* k_r, const void* v_r, dbs_dtype dt, int B,
                                int Hh, int N, int Npad, int d, int b, float scale,
-                               const int32_t* kv_count, const int32_t* kv_idx, const void* k_g,
-                               const void* v_g, int Ng, int n_pool, void* o_r, float* lse,
+                               const int32_t* kv_count, const int32_t* kv_idx, const int32_t* order,
+                               const void* k_g, const void* v_g, int Ng, int n_pool, void* o_r, float* lse,
                                hipStream_t stream) {
   DBS_GUARD_BEGIN
   REQUIRE(q_r && k_r && v_r && kv_count && kv_idx && o_r, DBS_ERR_INVALID_ARG, "NULL pointer");
   REQUIRE(aligned16(q_r) && aligned16(k_r) && aligned16(v_r) && aligned16(o_r), DBS_ERR_ALIGNMENT,
           "misaligned pointer");
-  REQUIRE(((uintptr_t)kv_count & 3u) == 0 && ((uintptr_t)kv_idx & 3u) == 0 && ((uintptr_t)lse & 3u) == 0,
+  REQUIRE(((uintptr_t)kv_count & 3u) == 0 && ((uintptr_t)kv_idx & 3u) == 0 && ((uintptr_t)lse & 3u) == 0 &&
+              ((uintptr_t)order & 3u) == 0,
           DBS_ERR_ALIGNMENT, "misaligned pointer");
   REQUIRE(dt == DBS_BF16, DBS_ERR_UNSUPPORTED, "sparse_attn_fwd computes on bf16 inputs");
   dbs_status st = check_geometry(B, Hh, N, Npad, d, b);
@@ -269,7 +271,7 @@ dbs_status dbs_sparse_attn_fwd(const void* q_r, const void* k_r, const void* v_r
             (N + n_pool - 1) / n_pool);
   }
   dbs::AttnArgs a{};
-  a.q_r = q_r; a.k_r = k_r; a.v_t = v_r; a.kv_count = kv_count; a.kv_idx = kv_idx;
+  a.q_r = q_r; a.k_r = k_r; a.v_t = v_r; a.kv_count = kv_count; a.kv_idx = kv_idx; a.order = order;
   a.k_g = k_g; a.v_g = v_g; a.o_r = o_r; a.lse = lse;
   a.B = B; a.Hh = Hh; a.N = N; a.Npad = Npad; a.d = d; a.b = b; a.nb = Npad / b;
   a.Ng = k_g ? Ng : 0; a.n_pool = k_g ? n_pool : 1; a.scale = scale; a.stream = stream;

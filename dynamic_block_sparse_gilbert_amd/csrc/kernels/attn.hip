@@ -31,7 +31,8 @@
 //   each other's gaps; forcing an instruction interleave measured slower.
 // K and V stages are copied global -> LDS by the DMA path
 // (global_load_lds_dwordx4, no VGPR staging) into double buffers one
-// iteration ahead of their use.  LDS rows are padded by one 16-byte unit, so
+// iteration ahead of their use; the copies are spread between the MFMAs (V
+// of stage u+1 in phase A, K of stage u+2 in phase B).  LDS rows are padded by one 16-byte unit, so
 // the 8 lanes that share a bank window read 8 different 16-byte bank groups
 // and every read address is one per-lane base register plus an immediate.
 // Online softmax with a lazy rescale: the running maximum is raised (and O, l
@@ -73,6 +74,10 @@ struct AttnCfg {
 
 constexpr float kLazyThreshold = 8.0f;
 
+// sched_group_barrier instruction classes
+constexpr int kSgMfma = 0x008;
+constexpr int kSgVmem = 0x020;   // vector-memory reads (the global -> LDS copies)
+
 __device__ __forceinline__ uint32_t cvt_pk(float a, float b) {
   bf16x2_t p;
   p[0] = (__bf16)a;
@@ -105,6 +110,7 @@ __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2
 void attn_fwd_kernel(
     const __bf16* __restrict__ q_r, const __bf16* __restrict__ k_r, const __bf16* __restrict__ v_t,
     const int32_t* __restrict__ kv_count, const int32_t* __restrict__ kv_idx,
+    const int32_t* __restrict__ order,
     const __bf16* __restrict__ k_g, const __bf16* __restrict__ v_g,
     __bf16* __restrict__ o_r, float* __restrict__ lse,
     int Hh, int N, int Npad, int nb, int Ng, float sl2, float bias_n, float bias_last, int total) {
@@ -120,7 +126,11 @@ void attn_fwd_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, g = lane >> 5;
-  const int wid = xcd_remap(blockIdx.x, total);
+  // Work item: this XCD's next entry of the schedule (longest query blocks
+  // first when build_mask wrote one), clamped so a bad schedule stays in bounds.
+  const int slot = xcd_remap(blockIdx.x, total);
+  const int wid = order == nullptr ? slot
+                                   : min(max(__builtin_amdgcn_readfirstlane(order[slot]), 0), total - 1);
   const int I = wid % nb;
   const int bh = wid / nb;
   const int q0 = I * BLK + wave * C::kQW;
@@ -133,60 +143,61 @@ void attn_fwd_kernel(
   const int ntg = (k_g != nullptr) ? Ngpad / BLK : 0;
   const int U = (cnt + ntg) * C::kSubs;
 
+  // Stage u: kept block j = u / kSubs of the list, or global-token tile j - cnt.
+  // Selects only (no branches), so the copies can be scheduled inside the
+  // MFMA phases.
   auto stage = [&](int u) -> StageDesc {
     StageDesc s;
     const int j = u / C::kSubs, h = u % C::kSubs;
-    if (j < cnt) {
-      int J = __builtin_amdgcn_readfirstlane(idx[j]);   // uniform: keep it scalar
-      const bool ok = J >= 0 && J < nb;
-      J = ok ? J : 0;
-      s.key0 = J * BLK + h * C::kKT;
-      s.k = k_r + (rowbase + s.key0) * D;
-      s.v = v_t + ((int64_t)bh * nb + J) * (int64_t)(D * BLK) + h * C::kKT;
-      s.limit = ok ? N : -1;
-      s.kind = (ok && s.key0 + C::kKT <= N) ? 0 : 1;
-    } else {
-      const int J = j - cnt;
-      s.key0 = J * BLK + h * C::kKT;
-      s.k = k_g + ((int64_t)bh * Ngpad + s.key0) * D;
-      s.v = v_g + ((int64_t)bh * (Ngpad / BLK) + J) * (int64_t)(D * BLK) + h * C::kKT;
-      s.limit = Ng;
-      s.kind = 2;
-    }
+    const bool kept = j < cnt;
+    const int jj = kept ? j : (cnt > 0 ? cnt - 1 : 0);        // always inside the list row
+    int J = __builtin_amdgcn_readfirstlane(idx[jj]);
+    const bool ok = J >= 0 && J < nb;
+    J = ok ? J : 0;
+    const int Jg = j - cnt;
+    const int key0k = J * BLK + h * C::kKT, key0g = Jg * BLK + h * C::kKT;
+    s.key0 = kept ? key0k : key0g;
+    s.k = kept ? k_r + (rowbase + key0k) * D : k_g + ((int64_t)bh * Ngpad + key0g) * D;
+    s.v = kept ? v_t + ((int64_t)bh * nb + J) * (int64_t)(D * BLK) + h * C::kKT
+               : v_g + ((int64_t)bh * (Ngpad / BLK) + Jg) * (int64_t)(D * BLK) + h * C::kKT;
+    s.limit = kept ? (ok ? N : -1) : Ng;
+    s.kind = kept ? ((ok && key0k + C::kKT <= N) ? 0 : 1) : 2;
     return s;
   };
 
   // Per-lane source offsets (elements) of the padded DMA: loop invariant.
   // LDS byte 1024 n + 16 lane of a stage holds padded unit p = 64 n + lane,
   // i.e. row p / rowU, unit p % rowU; the pad unit re-reads the row's last
-  // unit (same cache line, no extra traffic).
+  // unit (same cache line, no extra traffic).  Every wavefront issues kKPer
+  // (kVPer) copies per stage; where the stage has fewer, the surplus ones
+  // repeat the last copy, writing the same bytes (no branch in the issue).
   int koff[C::kKPer], voff[C::kVPer];
 #pragma unroll
   for (int i = 0; i < C::kKPer; ++i) {
-    const int p = 64 * (wave + i * C::kWaves) + lane;
+    const int n = min(wave + i * C::kWaves, C::kKInstr - 1);
+    const int p = 64 * n + lane;
     const int row = p / C::kKRowU, c = min(p % C::kKRowU, C::kKRowU - 2);
     koff[i] = row * D + c * 8;
   }
 #pragma unroll
   for (int i = 0; i < C::kVPer; ++i) {
-    const int p = 64 * (wave + i * C::kWaves) + lane;
+    const int n = min(wave + i * C::kWaves, C::kVInstr - 1);
+    const int p = 64 * n + lane;
     const int row = p / C::kVRowU, c = min(p % C::kVRowU, C::kVRowU - 2);
     voff[i] = row * BLK + c * 8;
   }
   auto dma_k = [&](const StageDesc& s, char* buf) {
 #pragma unroll
     for (int i = 0; i < C::kKPer; ++i) {
-      const int n = wave + i * C::kWaves;
-      if (C::kKInstr % C::kWaves == 0 || n < C::kKInstr)
-        __builtin_amdgcn_global_load_lds((glb_void_t*)(s.k + koff[i]), (lds_void_t*)(buf + 1024 * n), 16, 0, 0);
+      const int n = min(wave + i * C::kWaves, C::kKInstr - 1);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(s.k + koff[i]), (lds_void_t*)(buf + 1024 * n), 16, 0, 0);
     }
   };
   auto dma_v = [&](const StageDesc& s, char* buf) {
 #pragma unroll
     for (int i = 0; i < C::kVPer; ++i) {
-      const int n = wave + i * C::kWaves;
-      if (C::kVInstr % C::kWaves == 0 || n < C::kVInstr)
-        __builtin_amdgcn_global_load_lds((glb_void_t*)(s.v + voff[i]), (lds_void_t*)(buf + 1024 * n), 16, 0, 0);
+      const int n = min(wave + i * C::kWaves, C::kVInstr - 1);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(s.v + voff[i]), (lds_void_t*)(buf + 1024 * n), 16, 0, 0);
     }
   };
 
@@ -271,9 +282,21 @@ void attn_fwd_kernel(
   // Phase A: probabilities of the current stage (and, with a next stage, the
   // next stage's score MFMAs interleaved with them).
   auto phase_a = [&](const f32x16_t (&Sc)[2], f32x16_t (&Sn)[2], const char* ksrc, uint32_t (&P)[16],
-                      auto has_next) {
+                     const StageDesc* dv, char* vdst, auto has_next) {
     constexpr bool kNext = decltype(has_next)::value;
-    if constexpr (kNext) scores(ksrc, Sn);
+    if constexpr (kNext) {
+      scores(ksrc, Sn);
+      dma_v(*dv, vdst);
+      // Spread the copies between the score MFMAs: issued in one burst they
+      // stall every wavefront of the CU behind the address unit.
+      constexpr int kM = 2 * (D / 16), kStep = kM / C::kVPer;
+#pragma unroll
+      for (int i = 0; i < C::kVPer; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, kStep, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, kM - kStep * C::kVPer, 0);
+    }
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -293,7 +316,8 @@ void attn_fwd_kernel(
 
   // Phase B: O^T += V^T P^T for the current stage (and the next stage's
   // row maximum interleaved with it).
-  auto phase_b = [&](const char* vsrc, const uint32_t (&P)[16], const f32x16_t (&Sn)[2], auto has_next) {
+  auto phase_b = [&](const char* vsrc, const uint32_t (&P)[16], const f32x16_t (&Sn)[2],
+                     const StageDesc* dk, char* kdst, auto has_next) {
     constexpr bool kNext = decltype(has_next)::value;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -308,7 +332,17 @@ void attn_fwd_kernel(
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_v(vsrc, dt, st), pb, oacc[dt], 0, 0, 0);
     }
     float mx = -INFINITY;
-    if constexpr (kNext) mx = row_max(Sn);
+    if constexpr (kNext) {
+      mx = row_max(Sn);
+      dma_k(*dk, kdst);
+      constexpr int kM = 4 * (D / 32), kStep = kM / C::kKPer;
+#pragma unroll
+      for (int i = 0; i < C::kKPer; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, kStep, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, kM - kStep * C::kKPer, 0);
+    }
     return mx;
   };
 
@@ -319,12 +353,11 @@ void attn_fwd_kernel(
                      const char* ksrc, const char* vsrc) {
     wait_dma();
     __syncthreads();
-    if (u + 2 < U) dma_k(stage(u + 2), kdst);
+    const StageDesc sk = stage(min(u + 2, U - 1));   // past the end: a harmless repeat
     const StageDesc sn = stage(u + 1);
-    dma_v(sn, vdst);
     uint32_t P[16];
-    phase_a(Sc, Sn, ksrc, P, std::true_type{});
-    float mx = phase_b(vsrc, P, Sn, std::true_type{});
+    phase_a(Sc, Sn, ksrc, P, &sn, vdst, std::true_type{});
+    float mx = phase_b(vsrc, P, Sn, &sk, kdst, std::true_type{});
     // Pin the maximum inside the phase (otherwise it is sunk past the branch
     // below, away from the MFMAs it is meant to overlap).
     asm volatile("" ::"v"(mx));
@@ -341,15 +374,15 @@ void attn_fwd_kernel(
     __syncthreads();
     uint32_t P[16];
     f32x16_t unused[2];
-    phase_a(Sc, unused, nullptr, P, std::false_type{});
-    phase_b(vsrc, P, unused, std::false_type{});
+    phase_a(Sc, unused, nullptr, P, nullptr, nullptr, std::false_type{});
+    phase_b(vsrc, P, unused, nullptr, nullptr, std::false_type{});
   };
 
   if (U > 0) {
     const StageDesc s0 = stage(0);
     dma_k(s0, Kb0);
     dma_v(s0, Vb0);
-    if (U > 1) dma_k(stage(1), Kb1);
+    dma_k(stage(min(1, U - 1)), Kb1);
     wait_dma();
     __syncthreads();
     f32x16_t SA[2], SB[2];
@@ -403,7 +436,7 @@ hipError_t launch(const AttnArgs& a) {
   }
   hipLaunchKernelGGL((attn_fwd_kernel<D, BLK>), dim3(total), dim3(AttnCfg<D, BLK>::kThreads), 0,
                      a.stream, (const __bf16*)a.q_r, (const __bf16*)a.k_r, (const __bf16*)a.v_t,
-                     a.kv_count, a.kv_idx, (const __bf16*)a.k_g, (const __bf16*)a.v_g,
+                     a.kv_count, a.kv_idx, a.order, (const __bf16*)a.k_g, (const __bf16*)a.v_g,
                      (__bf16*)a.o_r, a.lse, a.Hh, a.N, a.Npad, a.nb, a.Ng, sl2, bias_n, bias_last,
                      total);
   return hipGetLastError();

@@ -36,13 +36,22 @@ __device__ __forceinline__ float xor_shfl(float v, int mask) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+constexpr int kXcdRanges = 8;   // XCDs of an MI355X; workgroups are dealt to them round-robin
+
+// Range x of the split of `total` logical ids into kXcdRanges contiguous
+// ranges (the first total % 8 ranges one longer).
+__device__ __forceinline__ void xcd_range(int x, int total, int& start, int& size) {
+  const int per = total / kXcdRanges, rem = total % kXcdRanges;
+  start = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+  size = per + (x < rem ? 1 : 0);
+}
+
 // Remap a linear workgroup id so that the hardware's round-robin placement
-// over the 8 XCDs gives every XCD a contiguous range of logical ids (work
+// over the XCDs gives every XCD one contiguous range of logical ids (work
 // items that share K/V then share that XCD's L2).
 __device__ __forceinline__ int xcd_remap(int wg, int total) {
-  constexpr int kXcd = 8;
-  const int per = total / kXcd, rem = total % kXcd;
-  const int xcd = wg % kXcd, slot = wg / kXcd;
+  const int per = total / kXcdRanges, rem = total % kXcdRanges;
+  const int xcd = wg % kXcdRanges, slot = wg / kXcdRanges;
   return (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
 }
 

@@ -13,7 +13,8 @@
 // 64-bit keys (~value bits, block index), which orders by value descending
 // and index ascending; wavefront 0 scans the sorted values 64 at a time
 // until the prefix reaches the target; the kept blocks are then written in
-// ascending index order by a block-wide compaction.
+// ascending index order by a block-wide compaction.  Optionally a second
+// launch turns the kept counts into the attention kernel's work order.
 #include "common.h"
 #include "../launch.h"
 
@@ -268,6 +269,59 @@ __global__ __launch_bounds__(kThreads) void build_mask_kernel(
   if (tid == 0) kv_count[row] = m;
 }
 
+// Work order for the attention kernel: rows (b, h, I) are split into the
+// eight contiguous ranges that the attention launch assigns to the eight
+// XCDs (see xcd_range in common.h), and each range is listed by kept count
+// descending, so every XCD starts its longest query blocks first (a
+// longest-processing-time-first schedule; kept counts are very uneven).
+// One workgroup per range: a counting sort over the counts 0..nb in LDS.
+// Rows with equal counts come out in an arbitrary order.
+constexpr int kOrderThreads = 1024;
+
+__global__ __launch_bounds__(kOrderThreads) void build_order_kernel(const int32_t* __restrict__ kv_count,
+                                                                    int nb, int total,
+                                                                    int32_t* __restrict__ order) {
+  __shared__ int cursor[kMaxNb + 1];
+  __shared__ int wsum[kOrderThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  int start, size;
+  xcd_range(blockIdx.x, total, start, size);
+  const int nbins = nb + 1;                       // bin nb - c holds count c
+  for (int i = tid; i < nbins; i += kOrderThreads) cursor[i] = 0;
+  __syncthreads();
+  for (int i = tid; i < size; i += kOrderThreads) {
+    const int c = min(max(kv_count[start + i], 0), nb);
+    atomicAdd(&cursor[nb - c], 1);
+  }
+  __syncthreads();
+  // Exclusive prefix over the bins: thread t owns a contiguous chunk.
+  const int chunk = (nbins + kOrderThreads - 1) / kOrderThreads;
+  const int b0 = min(tid * chunk, nbins), b1 = min(b0 + chunk, nbins);
+  int local = 0;
+  for (int b = b0; b < b1; ++b) local += cursor[b];
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += t;
+  }
+  if (lane == 63) wsum[tid >> 6] = incl;
+  __syncthreads();
+  int run = incl - local;
+  for (int w = 0; w < (tid >> 6); ++w) run += wsum[w];
+  for (int b = b0; b < b1; ++b) {
+    const int h = cursor[b];
+    cursor[b] = run;
+    run += h;
+  }
+  __syncthreads();
+  for (int i = tid; i < size; i += kOrderThreads) {
+    const int c = min(max(kv_count[start + i], 0), nb);
+    const int pos = atomicAdd(&cursor[nb - c], 1);
+    order[start + pos] = start + i;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_build_mask(const MaskArgs& a) {
@@ -275,6 +329,12 @@ hipError_t launch_build_mask(const MaskArgs& a) {
   __builtin_memcpy(&tau_bits, &a.tau, 4);
   hipLaunchKernelGGL(build_mask_kernel, dim3(a.rows), dim3(kThreads), 0, a.stream, a.p_imp, a.nb,
                      tau_bits, a.kv_count, a.kv_idx, a.mask);
+  if (a.order != nullptr) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(build_order_kernel, dim3(kXcdRanges), dim3(kOrderThreads), 0, a.stream, a.kv_count,
+                       a.nb, a.rows, a.order);
+  }
   return hipGetLastError();
 }
 

@@ -44,6 +44,7 @@ struct MaskArgs {
   int32_t* kv_count;
   int32_t* kv_idx;
   uint8_t* mask;
+  int32_t* order;       // nullable: attention work order
   int rows, nb;
   float tau;
   hipStream_t stream;
@@ -55,6 +56,7 @@ struct AttnArgs {
   const void* v_t;
   const int32_t* kv_count;
   const int32_t* kv_idx;
+  const int32_t* order;  // nullable: work order from build_mask
   const void* k_g;
   const void* v_g;
   void* o_r;

@@ -83,6 +83,7 @@ class AsaLayer:
                               dtype=torch.uint8, device=self.device)
         self.kv_count = torch.empty((B, Hh, nb), dtype=torch.int32, device=self.device)
         self.kv_idx = torch.empty((B, Hh, nb, nb), dtype=torch.int32, device=self.device)
+        self.order = torch.empty((B * Hh * nb,), dtype=torch.int32, device=self.device)
         self.k_g = self.v_g = None
         self.Ng = 0
         if s.n_pool:
@@ -103,12 +104,13 @@ class AsaLayer:
     def mask(self, tau: Optional[float] = None) -> None:
         s = self.spec
         ops.estimate_blocks(self.q_r, self.k_r, s.N, s.b, s.k, s.scale, p_imp=self.p_imp, workspace=self.ws)
-        ops.build_mask(self.p_imp, s.tau if tau is None else tau, kv_count=self.kv_count, kv_idx=self.kv_idx)
+        ops.build_mask(self.p_imp, s.tau if tau is None else tau, kv_count=self.kv_count, kv_idx=self.kv_idx,
+                       order=self.order)
 
     def attend(self, out: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16) -> torch.Tensor:
         s = self.spec
         ops.sparse_attn_fwd(self.q_r, self.k_r, self.v_t, s.N, s.b, s.scale, self.kv_count, self.kv_idx,
-                            self.k_g, self.v_g, self.Ng, s.n_pool, o_r=self.o_r)
+                            self.k_g, self.v_g, self.Ng, s.n_pool, o_r=self.o_r, order=self.order)
         return ops.inverse_reorder(self.o_r, self.perm, s.N, out=out, out_dtype=out_dtype)
 
     def forward(self, q, k, v, out: Optional[torch.Tensor] = None, tau: Optional[float] = None,

@@ -121,9 +121,12 @@ def estimate_blocks(q_r: torch.Tensor, k_r: torch.Tensor, N: int, b: int, k: int
 
 def build_mask(p_imp: torch.Tensor, tau: float, kv_count: Optional[torch.Tensor] = None,
                kv_idx: Optional[torch.Tensor] = None, want_mask: bool = False,
-               mask: Optional[torch.Tensor] = None):
-    """p_imp [B, Hh, nb, nb] float32 -> (kv_count [B, Hh, nb], kv_idx [B, Hh, nb, nb], mask or None)."""
-    _dev(p_imp, kv_count, kv_idx, mask)
+               mask: Optional[torch.Tensor] = None, order: Optional[torch.Tensor] = None,
+               want_order: bool = False):
+    """p_imp [B, Hh, nb, nb] float32 -> (kv_count [B, Hh, nb], kv_idx [B, Hh, nb, nb], mask or None);
+    with want_order (or an `order` buffer) also the attention work order int32 [B * Hh * nb] as a
+    fourth element."""
+    _dev(p_imp, kv_count, kv_idx, mask, order)
     B, Hh, nb, _ = p_imp.shape
     if kv_count is None:
         kv_count = torch.empty((B, Hh, nb), dtype=torch.int32, device=p_imp.device)
@@ -131,8 +134,12 @@ def build_mask(p_imp: torch.Tensor, tau: float, kv_count: Optional[torch.Tensor]
         kv_idx = torch.empty((B, Hh, nb, nb), dtype=torch.int32, device=p_imp.device)
     if want_mask and mask is None:
         mask = torch.empty((B, Hh, nb, nb), dtype=torch.uint8, device=p_imp.device)
+    if want_order and order is None:
+        order = torch.empty((B * Hh * nb,), dtype=torch.int32, device=p_imp.device)
     check("dbs_build_mask", lib().dbs_build_mask(
-        _p(p_imp), B, Hh, nb, float(tau), _p(kv_count), _p(kv_idx), _p(mask), _stream()))
+        _p(p_imp), B, Hh, nb, float(tau), _p(kv_count), _p(kv_idx), _p(mask), _p(order), _stream()))
+    if order is not None:
+        return kv_count, kv_idx, mask, order
     return kv_count, kv_idx, mask
 
 
@@ -157,9 +164,11 @@ def sparse_attn_fwd(q_r: torch.Tensor, k_r: torch.Tensor, v_t: torch.Tensor, N: 
                     kv_count: torch.Tensor, kv_idx: torch.Tensor,
                     k_g: Optional[torch.Tensor] = None, v_g: Optional[torch.Tensor] = None,
                     Ng: int = 0, n_pool: int = 0, o_r: Optional[torch.Tensor] = None,
-                    lse: Optional[torch.Tensor] = None, want_lse: bool = False):
-    """Returns (o_r rows [B, Hh, Npad, d] bf16, lse float32 [B, Hh, Npad] or None)."""
-    _dev(q_r, k_r, v_t, kv_count, kv_idx, k_g, v_g, o_r, lse)
+                    lse: Optional[torch.Tensor] = None, want_lse: bool = False,
+                    order: Optional[torch.Tensor] = None):
+    """Returns (o_r rows [B, Hh, Npad, d] bf16, lse float32 [B, Hh, Npad] or None).  `order` is the
+    work order from build_mask (None: index order)."""
+    _dev(q_r, k_r, v_t, kv_count, kv_idx, k_g, v_g, o_r, lse, order)
     B, Hh, Npad, d = q_r.shape
     if o_r is None:
         o_r = torch.empty_like(q_r)
@@ -167,5 +176,5 @@ def sparse_attn_fwd(q_r: torch.Tensor, k_r: torch.Tensor, v_t: torch.Tensor, N: 
         lse = torch.empty((B, Hh, Npad), dtype=torch.float32, device=q_r.device)
     check("dbs_sparse_attn_fwd", lib().dbs_sparse_attn_fwd(
         _p(q_r), _p(k_r), _p(v_t), _dt(q_r), B, Hh, N, Npad, d, b, float(scale), _p(kv_count), _p(kv_idx),
-        _p(k_g), _p(v_g), int(Ng), int(n_pool), _p(o_r), _p(lse), _stream()))
+        _p(order), _p(k_g), _p(v_g), int(Ng), int(n_pool), _p(o_r), _p(lse), _stream()))
     return o_r, lse

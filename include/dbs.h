@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DBS_ABI_VERSION 1
+#define DBS_ABI_VERSION 2
 
 typedef enum {
   DBS_OK = 0,
@@ -152,9 +152,18 @@ dbs_status dbs_estimate_blocks(const void* q_r, const void* k_r, dbs_dtype dt,
  * order.  A row holding a value outside [0, 1] or NaN keeps every block.
  * kv_count[b, h, I] = m; kv_idx[b, h, I, 0..m-1] = kept blocks ascending
  * (entries m..nb-1 are left untouched); mask (nullable) [B, Hh, nb, nb]
- * uint8 1 for kept, 0 otherwise.  tau must be in (0, 1].  nb <= 4096. */
+ * uint8 1 for kept, 0 otherwise.  tau must be in (0, 1].  nb <= 4096.
+ * order (nullable): int32 [B * Hh * nb], a work order for
+ * dbs_sparse_attn_fwd, a permutation of the row index (b * Hh + h) * nb + I.
+ * The rows are split into eight contiguous ranges (the first
+ * (B*Hh*nb) % 8 of them one row longer), one per XCD of the attention launch,
+ * and each range lists its rows by kept count descending (equal counts in
+ * any order): every XCD starts its longest query blocks first.  Any order
+ * gives the same attention result; this one balances the uneven work.
+ * Errors: INVALID_ARG for a NULL p_imp / kv_count / kv_idx or tau outside
+ * (0, 1]; UNSUPPORTED for nb > 4096; ALIGNMENT for a misaligned pointer. */
 dbs_status dbs_build_mask(const float* p_imp, int B, int Hh, int nb, float tau,
-                          int32_t* kv_count, int32_t* kv_idx, uint8_t* mask,
+                          int32_t* kv_count, int32_t* kv_idx, uint8_t* mask, int32_t* order,
                           hipStream_t stream);
 
 /* ASA_G global tokens (Video-BLADE "Step 2.2 (2)"; BLADE notes key design 2):
@@ -182,10 +191,15 @@ dbs_status dbs_meanpool_kv(const void* k_r, const void* v_r, dbs_dtype dt,
  * dbs_meanpool_kv.  o_r: DBS_ROWS bf16, rows >= N untouched.  lse (nullable):
  * float32 [B, Hh, Npad], natural-log normaliser of each row < N.
  * kv_count is clamped to [0, nb] and kv_idx entries outside [0, nb) are
- * skipped, so malformed lists cannot read outside the K/V buffers. */
+ * skipped, so malformed lists cannot read outside the K/V buffers.
+ * order (nullable): the work order written by dbs_build_mask for the same
+ * kv_count (NULL: rows in index order).  Entries are clamped to
+ * [0, B*Hh*nb); an order that is not a permutation computes some rows twice
+ * and leaves others untouched, but never reads or writes outside the
+ * buffers. */
 dbs_status dbs_sparse_attn_fwd(const void* q_r, const void* k_r, const void* v_r, dbs_dtype dt,
                                int B, int Hh, int N, int Npad, int d, int b, float scale,
-                               const int32_t* kv_count, const int32_t* kv_idx,
+                               const int32_t* kv_count, const int32_t* kv_idx, const int32_t* order,
                                const void* k_g, const void* v_g, int Ng, int n_pool,
                                void* o_r, float* lse, hipStream_t stream);
 

@@ -37,7 +37,7 @@ def test_all_declared_symbols_exported(dbs):
     for n in names:
         assert hasattr(h, n), n
     assert set(names) == set(L.SIGNATURES), set(names) ^ set(L.SIGNATURES)
-    assert L.lib().dbs_abi_version() == 1
+    assert L.lib().dbs_abi_version() == 2
 
 
 @pytest.mark.parametrize("T,H,W", list(itertools.product(range(1, 7), repeat=3)))
@@ -151,19 +151,20 @@ def test_estimate_validation(dbs):
 def test_mask_validation(dbs):
     _, L = dbs
     f = L.lib().dbs_build_mask
-    assert f(A, 1, 1, 16, 0.0, A, A, None, None) == -1
-    assert f(A, 1, 1, 16, 1.5, A, A, None, None) == -1
-    assert f(A, 1, 1, 16, float("nan"), A, A, None, None) == -1
-    assert f(A, 1, 1, 5000, 0.9, A, A, None, None) == -2
-    assert f(0, 1, 1, 16, 0.9, A, A, None, None) == -1
-    assert f(A + 2, 1, 1, 16, 0.9, A, A, None, None) == -3
+    assert f(A, 1, 1, 16, 0.0, A, A, None, None, None) == -1
+    assert f(A, 1, 1, 16, 1.5, A, A, None, None, None) == -1
+    assert f(A, 1, 1, 16, float("nan"), A, A, None, None, None) == -1
+    assert f(A, 1, 1, 5000, 0.9, A, A, None, None, None) == -2
+    assert f(0, 1, 1, 16, 0.9, A, A, None, None, None) == -1
+    assert f(A + 2, 1, 1, 16, 0.9, A, A, None, None, None) == -3
+    assert f(A, 1, 1, 16, 0.9, A, A, None, A + 2, None) == -3      # misaligned order
 
 
 @cpu_only
 def test_attn_and_pool_validation(dbs):
     _, L = dbs
     f = L.lib().dbs_sparse_attn_fwd
-    base = [A, A, A, 0, 1, 4, 1000, 1024, 128, 128, 0.088, A, A, None, None, 0, 0, A, None, None]
+    base = [A, A, A, 0, 1, 4, 1000, 1024, 128, 128, 0.088, A, A, None, None, None, 0, 0, A, None, None]
     def call(i, v):
         a = list(base)
         a[i] = v
@@ -171,11 +172,12 @@ def test_attn_and_pool_validation(dbs):
     assert call(0, 0) == -1
     assert call(3, 1) == -2
     assert call(8, 80) == -2
-    assert call(13, A) == -1              # k_g without v_g
-    a = list(base); a[13] = A; a[14] = A; a[15] = 126; a[16] = 8
+    assert call(14, A) == -1              # k_g without v_g
+    a = list(base); a[14] = A; a[15] = A; a[16] = 126; a[17] = 8
     assert f(*a) == -1                    # Ng must be ceil(N / n) = 125
     assert call(10, float("inf")) == -1
-    assert call(18, A + 2) == -3
+    assert call(19, A + 2) == -3
+    assert call(13, A + 2) == -3          # misaligned order
     g = L.lib().dbs_meanpool_kv
     assert g(A, A, 0, 1, 4, 1000, 1024, 128, 128, 0, A, A, None) == -1
     assert g(A, A, 1, 1, 4, 1000, 1024, 128, 128, 8, A, A, None) == -2

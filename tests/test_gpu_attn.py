@@ -173,3 +173,35 @@ def test_attn_deterministic():
     a = host(ops.sparse_attn_fwd(q_r, k_r, v_t, N, b, 0.088, dev(cnt), dev(idx))[0])
     c = host(ops.sparse_attn_fwd(q_r, k_r, v_t, N, b, 0.088, dev(cnt), dev(idx))[0])
     assert np.array_equal(a, c)
+
+
+@pytest.mark.parametrize("N,d,b", [(1000, 128, 128), (2048, 64, 64), (700, 64, 128)])
+def test_attn_work_order_does_not_change_results(N, d, b):
+    """Rows are independent: the schedule from build_mask, a random
+    permutation and index order give bit-identical outputs and lse."""
+    say("attn order", N, d, b)
+    B, Hh = 2, 3
+    rng = np.random.default_rng(N + 3 * d + b)
+    q, k, v = smooth_qkv(N + 11, B, N, Hh, d)
+    nb = -(-N // b)
+    Npad = nb * b
+    cnt, idx = _upload(_lists("random", B * Hh, nb, rng), B, Hh, nb)
+    ops = _ops()
+    perm = dev(np.arange(N, dtype=np.int32))
+    q_r = ops.reorder(dev_bf16(q), perm, Npad, b, "rows")
+    k_r = ops.reorder(dev_bf16(k), perm, Npad, b, "rows")
+    v_t = ops.reorder(dev_bf16(v), perm, Npad, b, "tiles_t")
+    scale = 1.0 / math.sqrt(d)
+    P = np.zeros((B, Hh, nb, nb), np.float32)
+    for bi in range(B):
+        for h in range(Hh):
+            for I in range(nb):
+                P[bi, h, I, idx[bi, h, I, :cnt[bi, h, I]]] = 1.0
+    _, _, _, order = ops.build_mask(dev(P), 1.0, want_order=True)
+    outs = []
+    for o in (None, order, dev(rng.permutation(B * Hh * nb).astype(np.int32))):
+        o_r, lse = ops.sparse_attn_fwd(q_r, k_r, v_t, N, b, scale, dev(cnt), dev(idx), want_lse=True, order=o)
+        torch.cuda.synchronize()
+        outs.append((host(o_r)[:, :, :N].view(np.uint16), host(lse)[:, :, :N]))
+    for o_, l_ in outs[1:]:
+        assert np.array_equal(o_, outs[0][0]) and np.array_equal(l_, outs[0][1])

@@ -113,3 +113,33 @@ def test_mask_deterministic():
     a = [host(t) for t in ops.build_mask(P, 0.9)[:2]]
     b = [host(t) for t in ops.build_mask(P, 0.9)[:2]]
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def _xcd_ranges(total: int):
+    """The eight contiguous row ranges of the work order (first total % 8 one longer)."""
+    per, rem = divmod(total, 8)
+    out, start = [], 0
+    for x in range(8):
+        size = per + (1 if x < rem else 0)
+        out.append((start, size))
+        start += size
+    return out
+
+
+@pytest.mark.parametrize("B,Hh,nb", [(1, 12, 256), (2, 3, 139), (1, 1, 5), (1, 2, 1200)])
+def test_mask_work_order(B, Hh, nb):
+    """The work order is a permutation of the rows that lists each XCD range
+    by kept count descending (the rule stated in include/dbs.h)."""
+    say("mask order", B, Hh, nb)
+    rng = np.random.default_rng(B * 1000 + Hh * 10 + nb)
+    P = _rows("softmaxish", B * Hh * nb, nb, rng).reshape(B, Hh, nb, nb)
+    ops = _ops()
+    cnt, _, _, order = ops.build_mask(dev(P), 0.9, want_order=True)
+    torch.cuda.synchronize()
+    c, o = host(cnt).reshape(-1), host(order)
+    total = B * Hh * nb
+    assert np.array_equal(np.sort(o), np.arange(total))
+    for start, size in _xcd_ranges(total):
+        seg = o[start:start + size]
+        assert ((seg >= start) & (seg < start + size)).all()
+        assert (np.diff(c[seg]) <= 0).all()
