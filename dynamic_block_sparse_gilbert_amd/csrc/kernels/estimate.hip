@@ -7,17 +7,19 @@
 // Sampled tokens use a compact index r = J*k + t (t < k): slot t of block J is
 // reordered row J*b + floor(t*L_J/k_J) when t < k_J = min(k, L_J), and an
 // empty slot otherwise (only the last block can have empty slots).  Since
-// softmax is monotone in the score,
-//     P_imp[I, J] = exp2( max_{q in I, c in J} (x_qc - lse2_q) ),
-// with x = score * scale * log2(e) and lse2_q = log2 sum_c exp2(x_qc); so two
-// passes over the sampled keys suffice and nothing of size (sampled queries)
-// x nb is ever stored.  Three launches:
-//   gather:   copy the sampled rows of Q and K into compact row-major arrays
-//             (zero rows for empty slots) in the workspace;
-//   stats:    online max / sum per sampled query over a range of the sampled
-//             keys -> one partial (max, sum) per key split;
-//   blockmax: merge the partials into lse2, recompute x over its own key range,
-//             subtract lse2, reduce each k x k group, one exp2 per group.
+// softmax is monotone in the score and scale * log2(e) > 0,
+//     P_imp[I, J] = exp2( max_{q in I} (sl2 * t_qJ - lse2_q) ),
+//     t_qJ = max_{c in J} score_qc,  lse2_q = log2 sum_c exp2(sl2 * score_qc),
+// so one pass over the sampled scores suffices if the k_J-wide maxima t_qJ
+// are kept (a (sampled queries) x nb float array in the workspace; for k > 64
+// a block's maximum is kept as k / 64 cell maxima, one per 64-key chunk).
+// Three launches:
+//   gather: copy the sampled rows of Q and K into compact row-major arrays
+//           (zero rows for empty slots) in the workspace;
+//   pass:   per sampled query, over a range of the sampled keys: the online
+//           max / sum (one partial per key split) and the block maxima t_qJ;
+//   final:  merge the partials into lse2 and form P_imp, one exp2 per
+//           (query block, key block).
 // The key range is split over enough workgroups (about 4096 in total) that
 // the DMA latency of each key chunk is hidden by other resident workgroups.
 // Both passes compute S^T = K_s Q_s^T on bf16 MFMA 16x16x32 with fp32
@@ -38,7 +40,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kQPerWg = kWaves * 16;
 constexpr int kChunk = 64;
-constexpr int kMaxChunksPerSplit = 64;   // bound on chunks per key split (LDS staging)
+constexpr int kMaxChunksPerSplit = 64;   // bound on chunks per key split
 
 __device__ __forceinline__ int swz(int u) { return (u & ~15) | ((u & 15) ^ ((u >> 4) & 15)); }
 
@@ -77,6 +79,8 @@ __device__ __forceinline__ float sum_x32(float v) {
 struct SampleGeom {
   int N, b, k, klog2, nb, nsp, nsp_pad, kj_last;
   int splits, cps;   // key splits and 64-key chunks per split
+  int cell_log2;     // block maxima are kept per cell of min(k, 64) compact keys
+  int ncell;         // cells per sampled query: nsp >> cell_log2
   // Reordered row of compact slot r, or -1 for an empty slot / r >= nsp.
   __device__ __forceinline__ int row(int r) const {
     if (r >= nsp) return -1;
@@ -202,10 +206,31 @@ __device__ __forceinline__ void load_q(const __bf16* qs_bh, int rq, int g4, bf16
   for (int kk = 0; kk < D / 32; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * kk);
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void est_stats_kernel(
+// Raw block maxima of one 16-key score tile (keys ck0 + 16t + 4*g4 + j, query
+// l16): groups of kr = min(K, 16) consecutive keys, nv values per lane.
+template <int K>
+__device__ __forceinline__ void group_max(const f32x4_t& s, float (&v)[4]) {
+  constexpr int kr = K < 16 ? K : 16;
+  if constexpr (kr >= 4) {
+    v[0] = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    if constexpr (kr >= 8) v[0] = max_x16(v[0]);
+    if constexpr (kr >= 16) v[0] = max_x32(v[0]);
+  } else if constexpr (kr == 2) {
+    v[0] = fmaxf(s[0], s[1]);
+    v[1] = fmaxf(s[2], s[3]);
+  } else {
+    v[0] = s[0]; v[1] = s[1]; v[2] = s[2]; v[3] = s[3];
+  }
+}
+
+// K: the sample count k when k <= 32 (a cell is one block: a group of K keys
+// inside one 16-key tile, or for K = 32 two tiles); 64 stands for every
+// k >= 64 (a cell is one 64-key chunk).  A compile-time constant, so the
+// reductions below are straight-line code.
+template <int D, int K>
+__global__ __launch_bounds__(kThreads) void est_pass_kernel(
     const __bf16* __restrict__ qs, const __bf16* __restrict__ ks, float2* __restrict__ part,
-    SampleGeom sg, float sl2) {
+    float* __restrict__ tmax, SampleGeom sg, float sl2) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
   int bh, split, panel;
@@ -214,10 +239,37 @@ __global__ __launch_bounds__(kThreads) void est_stats_kernel(
   bf16x8_t qreg[D / 32];
   load_q<D>(qs + (int64_t)bh * sg.nsp_pad * D, rq, g4, qreg);
   float m = -INFINITY, l = 0.f;
+  constexpr int kr = K < 16 ? K : 16;
+  constexpr int nv = kr >= 4 ? 1 : 4 / kr;
+  const bool krep = kr >= 4 ? ((g4 & ((kr >> 2) - 1)) == 0) : true;
+  float* trow = tmax + ((int64_t)bh * sg.nsp + rq) * sg.ncell;
+  const bool qok = rq < sg.nsp;
   const int tail = (sg.nb - 1) * sg.k;   // first slot of the last block
   const int c0 = split * sg.cps, c1 = min(sg.nsp_pad / kChunk, c0 + sg.cps);
   stream_keys<D>(ks + (int64_t)bh * sg.nsp_pad * D, c0, c1, qreg, [&](int ck0, f32x4_t (&s)[4]) {
     if ((ck0 + kChunk > sg.nsp) || (sg.kj_last < sg.k && ck0 + kChunk > tail)) mask_chunk(sg, ck0, g4, s);
+    // block (cell) maxima of the raw scores
+    float gv[4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) group_max<K>(s[t], gv[t]);
+    if constexpr (K == 32) {           // cells of two tiles: 0-1, 2-3
+      gv[0][0] = fmaxf(gv[0][0], gv[1][0]);
+      gv[2][0] = fmaxf(gv[2][0], gv[3][0]);
+    } else if constexpr (K == 64) {    // one cell: the whole chunk
+      gv[0][0] = fmaxf(fmaxf(gv[0][0], gv[1][0]), fmaxf(gv[2][0], gv[3][0]));
+    }
+    constexpr int tstep = K >= 64 ? 4 : (K == 32 ? 2 : 1);
+    if (qok && krep) {
+#pragma unroll
+      for (int t = 0; t < 4; t += tstep) {
+#pragma unroll
+        for (int e = 0; e < nv; ++e) {
+          const int ck = ck0 + 16 * t + 4 * g4 + e * kr;
+          if (ck < sg.nsp) trow[ck >> sg.cell_log2] = gv[t][e];
+        }
+      }
+    }
+    // online normaliser
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -235,7 +287,7 @@ __global__ __launch_bounds__(kThreads) void est_stats_kernel(
     m = m_new;
   });
   l = sum_x32(sum_x16(l));
-  if (g4 == 0 && rq < sg.nsp) part[((int64_t)bh * sg.splits + split) * sg.nsp + rq] = make_float2(m, l);
+  if (g4 == 0 && qok) part[((int64_t)bh * sg.splits + split) * sg.nsp + rq] = make_float2(m, l);
 }
 
 // log2 of the softmax normaliser of sampled query rq from its per-split partials.
@@ -251,98 +303,38 @@ __device__ __forceinline__ float merge_lse2(const float2* part_bh, const SampleG
   return M + __log2f(L);
 }
 
-__global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0.f;
-}
+// P_imp of one (batch, head, query block I) row: lse2 of the block's valid
+// sampled queries from the split partials (in LDS), then for every key block
+// J the maximum over those queries of sl2 * t_qJ - lse2_q, and one exp2.
+// An empty query slot contributes nothing; a block without valid query slots
+// (impossible: k_J >= 1) would get exp2(-inf) = 0.
+constexpr int kFinalThreads = 256;
+constexpr int kMaxK = 128;   // k <= b <= 128
 
-// K: the sample count k when k <= 16; 32 stands for every k > 16.  The group
-// side inside one 16 x 16 score tile is min(k, 16); k == 16 stages its one
-// value per tile in LDS, k < 16 stores each group directly, k > 16 combines
-// tiles of the same group with atomicMax (P_imp zeroed first).  A
-// compile-time constant, so the reductions below are straight-line code.
-template <int D, int K>
-__global__ __launch_bounds__(kThreads) void est_blockmax_kernel(
-    const __bf16* __restrict__ qs, const __bf16* __restrict__ ks, const float2* __restrict__ part,
-    float* __restrict__ p_imp, SampleGeom sg, float sl2) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l16 = lane & 15, g4 = lane >> 4;
-  int bh, split, panel;
-  wg_coords(sg, bh, split, panel);
-  const int rq = panel * kQPerWg + wave * 16 + l16;
-  bf16x8_t qreg[D / 32];
-  load_q<D>(qs + (int64_t)bh * sg.nsp_pad * D, rq, g4, qreg);
-  // an empty query slot (lse2 = +inf) contributes -inf to its group
-  const float myl = (rq < sg.nsp && sg.valid(rq))
-                        ? merge_lse2(part + (int64_t)bh * sg.splits * sg.nsp, sg, rq) : INFINITY;
-  constexpr int kr = K < 16 ? K : 16;
-  const int I = rq >> sg.klog2;
-  const bool qrep = (l16 & (kr - 1)) == 0 && rq < sg.nsp;
+__global__ __launch_bounds__(kFinalThreads) void est_final_kernel(const float2* __restrict__ part,
+                                                                  const float* __restrict__ tmax,
+                                                                  float* __restrict__ p_imp, SampleGeom sg,
+                                                                  float sl2) {
+  __shared__ float lse[kMaxK];
+  const int I = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int kI = I < sg.nb - 1 ? sg.k : sg.kj_last;
+  if (tid < sg.k) {
+    const int rq = I * sg.k + tid;
+    lse[tid] = tid < kI ? merge_lse2(part + (int64_t)bh * sg.splits * sg.nsp, sg, rq) : INFINITY;
+  }
+  __syncthreads();
+  const int cpb = sg.ncell / sg.nb;   // cells per block: 1, or k / 64
+  const float* t0 = tmax + ((int64_t)bh * sg.nsp + (int64_t)I * sg.k) * sg.ncell;
   float* prow = p_imp + ((int64_t)bh * sg.nb + I) * sg.nb;
-  const int tail = (sg.nb - 1) * sg.k;
-  const int c0 = split * sg.cps, c1 = min(sg.nsp_pad / kChunk, c0 + sg.cps);
-  // k == 16: one P_imp value per (wave, key tile); results are staged here so
-  // that no global store sits between the key-chunk DMAs (vmcnt counts both).
-  __shared__ float outbuf[kWaves][kMaxChunksPerSplit * 4];
-  float* outw = outbuf[wave];
-  stream_keys<D>(ks + (int64_t)bh * sg.nsp_pad * D, c0, c1, qreg, [&](int ck0, f32x4_t (&s)[4]) {
-    if ((ck0 + kChunk > sg.nsp) || (sg.kj_last < sg.k && ck0 + kChunk > tail)) mask_chunk(sg, ck0, g4, s);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      float u[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) u[j] = __builtin_fmaf(s[t][j], sl2, -myl);
-      // keys: reduce within groups of kr consecutive keys (4 per lane, 16 per lane row)
-      constexpr int nv = kr >= 4 ? 1 : 4 / kr;
-      float v[4];
-      if constexpr (kr >= 4) {
-        v[0] = fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3]));
-        if constexpr (kr >= 8) v[0] = max_x16(v[0]);
-        if constexpr (kr >= 16) v[0] = max_x32(v[0]);
-      } else if constexpr (kr == 2) {
-        v[0] = fmaxf(u[0], u[1]);
-        v[1] = fmaxf(u[2], u[3]);
-      } else {
-        v[0] = u[0]; v[1] = u[1]; v[2] = u[2]; v[3] = u[3];
-      }
-      // queries: reduce within groups of kr consecutive lanes of a row
-#pragma unroll
-      for (int e = 0; e < nv; ++e) {
-        if constexpr (kr >= 2) v[e] = dpp_max(v[e], 0xb1);
-        if constexpr (kr >= 4) v[e] = dpp_max(v[e], 0x4e);
-        if constexpr (kr >= 8) v[e] = dpp_max(v[e], 0x141);
-        if constexpr (kr >= 16) v[e] = dpp_max(v[e], 0x140);
-      }
-      if constexpr (K == 16) {
-        // one group per tile, held by lane 0: staged in LDS, stored after the loop
-        if (lane == 0) outw[(ck0 / kChunk - c0) * 4 + t] = v[0];
-        continue;
-      }
-      const bool krep = kr >= 4 ? ((g4 & ((kr >> 2) - 1)) == 0) : true;
-      if (qrep && krep) {
-#pragma unroll
-        for (int e = 0; e < nv; ++e) {
-          const int ck = ck0 + 16 * t + 4 * g4 + e * (4 / nv);
-          if (ck < sg.nsp) {
-            const int J = ck >> sg.klog2;
-            const float p = fast_exp2(v[e]);
-            if constexpr (K < 16) {
-              prow[J] = p;
-            } else {
-              atomicMax(reinterpret_cast<int*>(prow + J), __float_as_int(p));
-            }
-          }
-        }
-      }
+  for (int J = tid; J < sg.nb; J += kFinalThreads) {
+    float best = -INFINITY;
+    for (int t = 0; t < kI; ++t) {
+      const float* tr = t0 + (int64_t)t * sg.ncell + J * cpb;
+      float v = tr[0];
+      for (int c = 1; c < cpb; ++c) v = fmaxf(v, tr[c]);
+      best = fmaxf(best, __builtin_fmaf(v, sl2, -lse[t]));
     }
-  });
-  if (K == 16 && rq - l16 < sg.nsp) {
-    // the wave's 16 queries are exactly query block I; J runs over the split's tiles
-    const int nout = (c1 - c0) * 4;
-    for (int i = lane; i < nout; i += 64) {
-      const int J = c0 * 4 + i;
-      if (J < sg.nb) prow[J] = fast_exp2(outw[i]);
-    }
+    prow[J] = fast_exp2(best);
   }
 }
 
@@ -368,6 +360,8 @@ hipError_t launch_d(const EstimateArgs& a) {
   while ((1 << sg.klog2) < a.k) ++sg.klog2;
   sg.nsp = a.nb * a.k;
   sg.nsp_pad = (sg.nsp + kChunk - 1) / kChunk * kChunk;
+  sg.cell_log2 = sg.klog2 < 6 ? sg.klog2 : 6;
+  sg.ncell = sg.nsp >> sg.cell_log2;
   const int Llast = a.N - (a.nb - 1) * a.b;
   sg.kj_last = a.k < Llast ? a.k : Llast;
   const float sl2 = a.scale * kLog2e;
@@ -376,31 +370,26 @@ hipError_t launch_d(const EstimateArgs& a) {
   __bf16* qs = reinterpret_cast<__bf16*>(a.workspace);
   __bf16* ks = qs + (int64_t)BH * sg.nsp_pad * D;
   float2* part = reinterpret_cast<float2*>(ks + (int64_t)BH * sg.nsp_pad * D);
+  float* tmax = reinterpret_cast<float*>(part + (int64_t)BH * sg.splits * sg.nsp);
 
   hipLaunchKernelGGL((est_gather_kernel<D>), dim3((sg.nsp_pad * (D / 8) + 255) / 256, BH), dim3(256), 0,
                      a.stream, (const __bf16*)a.q_r, (const __bf16*)a.k_r, qs, ks, sg, a.Npad);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid((unsigned)(((sg.nsp + kQPerWg - 1) / kQPerWg) * sg.splits * BH));
-  hipLaunchKernelGGL((est_stats_kernel<D>), grid, dim3(kThreads), 0, a.stream, qs, ks, part, sg, sl2);
+  switch (a.k) {
+    case 1: hipLaunchKernelGGL((est_pass_kernel<D, 1>), grid, dim3(kThreads), 0, a.stream, qs, ks, part, tmax, sg, sl2); break;
+    case 2: hipLaunchKernelGGL((est_pass_kernel<D, 2>), grid, dim3(kThreads), 0, a.stream, qs, ks, part, tmax, sg, sl2); break;
+    case 4: hipLaunchKernelGGL((est_pass_kernel<D, 4>), grid, dim3(kThreads), 0, a.stream, qs, ks, part, tmax, sg, sl2); break;
+    case 8: hipLaunchKernelGGL((est_pass_kernel<D, 8>), grid, dim3(kThreads), 0, a.stream, qs, ks, part, tmax, sg, sl2); break;
+    case 16: hipLaunchKernelGGL((est_pass_kernel<D, 16>), grid, dim3(kThreads), 0, a.stream, qs, ks, part, tmax, sg, sl2); break;
+    case 32: hipLaunchKernelGGL((est_pass_kernel<D, 32>), grid, dim3(kThreads), 0, a.stream, qs, ks, part, tmax, sg, sl2); break;
+    default: hipLaunchKernelGGL((est_pass_kernel<D, 64>), grid, dim3(kThreads), 0, a.stream, qs, ks, part, tmax, sg, sl2); break;
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.k > 16) {
-    const int64_t n = (int64_t)BH * a.nb * a.nb;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, a.stream,
-                       a.p_imp, n);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  const float2* pp = part;
-  switch (a.k) {
-    case 1: hipLaunchKernelGGL((est_blockmax_kernel<D, 1>), grid, dim3(kThreads), 0, a.stream, qs, ks, pp, a.p_imp, sg, sl2); break;
-    case 2: hipLaunchKernelGGL((est_blockmax_kernel<D, 2>), grid, dim3(kThreads), 0, a.stream, qs, ks, pp, a.p_imp, sg, sl2); break;
-    case 4: hipLaunchKernelGGL((est_blockmax_kernel<D, 4>), grid, dim3(kThreads), 0, a.stream, qs, ks, pp, a.p_imp, sg, sl2); break;
-    case 8: hipLaunchKernelGGL((est_blockmax_kernel<D, 8>), grid, dim3(kThreads), 0, a.stream, qs, ks, pp, a.p_imp, sg, sl2); break;
-    case 16: hipLaunchKernelGGL((est_blockmax_kernel<D, 16>), grid, dim3(kThreads), 0, a.stream, qs, ks, pp, a.p_imp, sg, sl2); break;
-    default: hipLaunchKernelGGL((est_blockmax_kernel<D, 32>), grid, dim3(kThreads), 0, a.stream, qs, ks, pp, a.p_imp, sg, sl2); break;
-  }
+  hipLaunchKernelGGL(est_final_kernel, dim3((unsigned)a.nb, (unsigned)BH), dim3(kFinalThreads), 0, a.stream,
+                     (const float2*)part, (const float*)tmax, a.p_imp, sg, sl2);
   return hipGetLastError();
 }
 
@@ -412,7 +401,10 @@ size_t estimate_workspace_bytes(int B, int Hh, int nb, int k, int d) {
   const int64_t BH = (int64_t)B * Hh;
   int splits, cps;
   split_plan((int)BH, (int)nsp, splits, cps);
-  return (size_t)(BH * nsp_pad * d * 2 * 2 + BH * splits * nsp * 8);
+  int klog2 = 0;
+  while ((1 << klog2) < k) ++klog2;
+  const int64_t cells = nsp >> (klog2 < 6 ? klog2 : 6);
+  return (size_t)(BH * nsp_pad * d * 2 * 2 + BH * splits * nsp * 8 + BH * nsp * cells * 4);
 }
 
 hipError_t launch_estimate(const EstimateArgs& a) {

@@ -123,10 +123,12 @@ dbs_status dbs_inverse_reorder(const void* y, dbs_dtype y_dt, void* x, dbs_dtype
                                int B, int Hh, int N, int Npad, int d, hipStream_t stream);
 
 /* Bytes of device workspace dbs_estimate_blocks needs: compact copies of the
- * sampled Q and K rows (B * Hh * ceil(nb*k / 64)*64 * d bf16 each) and one
+ * sampled Q and K rows (B * Hh * ceil(nb*k / 64)*64 * d bf16 each), one
  * partial softmax (max, sum) float pair per sampled query and key split (the
  * library splits the sampled keys over up to nb*k/64 workgroups per query
- * panel).  Returns 0 for invalid sizes. */
+ * panel), and per sampled query the maximum raw score over each cell of
+ * min(k, 64) sampled keys (B * Hh * nb*k * nb*k/min(k,64) floats; about
+ * 50 MB for 12 heads, nb = 256, k = 16).  Returns 0 for invalid sizes. */
 size_t dbs_estimate_workspace_bytes(int B, int Hh, int N, int d, int b, int k);
 
 /* Block-importance estimation (Video-BLADE "Step 1"; BLADE notes key design 1).
