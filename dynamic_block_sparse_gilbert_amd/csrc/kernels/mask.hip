@@ -21,7 +21,6 @@
 namespace dbs {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kMaxNb = 4096;
 constexpr int kLimbs = 6;
 
@@ -111,11 +110,14 @@ __device__ __forceinline__ U192 wave_inclusive_scan(U192 x, int lane) {
   return x;
 }
 
+// kCap: largest nb of the size class (LDS is sized for it, so small rows keep
+// many workgroups resident); kThreads: workgroup size.
+template <int kCap, int kThreads>
 __global__ __launch_bounds__(kThreads) void build_mask_kernel(
     const float* __restrict__ p_imp, int nb, uint32_t tau_bits, int32_t* __restrict__ kv_count,
     int32_t* __restrict__ kv_idx, uint8_t* __restrict__ mask) {
-  __shared__ uint64_t keys[kMaxNb];
-  __shared__ uint8_t flag[kMaxNb];
+  __shared__ uint64_t keys[kCap];
+  __shared__ uint8_t flag[kCap];
   __shared__ uint32_t red[kThreads / 64][kLimbs];
   __shared__ int s_invalid, s_m;
   __shared__ int s_wave_cnt[kThreads / 64];
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(kThreads) void build_mask_kernel(
     for (int k = 2; k <= P2; k <<= 1) {
       for (int j = k >> 1; j > 0; j >>= 1) {
         for (int i = tid; i < (P2 >> 1); i += kThreads) {
-          const int lo = 2 * j * (i / j) + (i % j), hi = lo + j;
+          const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1)), hi = lo + j;   // j is a power of two
           const uint64_t a = keys[lo], b = keys[hi];
           const bool asc = (lo & k) == 0;
           if ((a > b) == asc) {
@@ -327,8 +329,19 @@ __global__ __launch_bounds__(kOrderThreads) void build_order_kernel(const int32_
 hipError_t launch_build_mask(const MaskArgs& a) {
   uint32_t tau_bits;
   __builtin_memcpy(&tau_bits, &a.tau, 4);
-  hipLaunchKernelGGL(build_mask_kernel, dim3(a.rows), dim3(kThreads), 0, a.stream, a.p_imp, a.nb,
-                     tau_bits, a.kv_count, a.kv_idx, a.mask);
+  if (a.nb <= 64) {
+    hipLaunchKernelGGL((build_mask_kernel<64, 64>), dim3(a.rows), dim3(64), 0, a.stream, a.p_imp, a.nb,
+                       tau_bits, a.kv_count, a.kv_idx, a.mask);
+  } else if (a.nb <= 256) {
+    hipLaunchKernelGGL((build_mask_kernel<256, 128>), dim3(a.rows), dim3(128), 0, a.stream, a.p_imp, a.nb,
+                       tau_bits, a.kv_count, a.kv_idx, a.mask);
+  } else if (a.nb <= 1024) {
+    hipLaunchKernelGGL((build_mask_kernel<1024, 256>), dim3(a.rows), dim3(256), 0, a.stream, a.p_imp, a.nb,
+                       tau_bits, a.kv_count, a.kv_idx, a.mask);
+  } else {
+    hipLaunchKernelGGL((build_mask_kernel<kMaxNb, 256>), dim3(a.rows), dim3(256), 0, a.stream, a.p_imp,
+                       a.nb, tau_bits, a.kv_count, a.kv_idx, a.mask);
+  }
   if (a.order != nullptr) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
