@@ -34,6 +34,13 @@ SOURCES = [
 # Packed fp32 VALU ops are disabled on purpose: only plain fp32 ops are emitted.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
+# Per-source extra flags.  The attention kernel is compiled without NaN
+# semantics: its maximum reductions then map onto v_max3_f32 with no
+# canonicalising v_max_f32 x, x in front of every operand.  Infinities keep
+# their meaning (masked keys are -inf); NaN inputs give an undefined result
+# (an exact softmax of them is NaN anyway).
+SOURCE_FLAGS = {"kernels/attn.hip": ["-fno-honor-nans"]}
+
 
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
@@ -45,7 +52,7 @@ def hipcc() -> str:
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, src.replace("/", "_") + ".o")
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-c",
-           "-I", os.path.join(ROOT, "include"), "-I", CSRC, *DEVICE_FLAGS,
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []),
            "-x", "hip", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)

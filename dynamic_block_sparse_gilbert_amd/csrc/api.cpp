@@ -275,6 +275,7 @@ dbs_status dbs_sparse_attn_fwd(const void* q_r, const void* k_r, const void* v_r
   a.k_g = k_g; a.v_g = v_g; a.o_r = o_r; a.lse = lse;
   a.B = B; a.Hh = Hh; a.N = N; a.Npad = Npad; a.d = d; a.b = b; a.nb = Npad / b;
   a.Ng = k_g ? Ng : 0; a.n_pool = k_g ? n_pool : 1; a.scale = scale; a.stream = stream;
+  REQUIRE(a.nb <= 4096, DBS_ERR_UNSUPPORTED, "nb=%d must be <= 4096", a.nb);
   REQUIRE((int64_t)B * Hh * a.nb <= INT32_MAX, DBS_ERR_INVALID_ARG, "too many query blocks");
   return from_hip(dbs::launch_attn_fwd(a), "dbs_sparse_attn_fwd launch");
   DBS_GUARD_END

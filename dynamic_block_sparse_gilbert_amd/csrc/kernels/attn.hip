@@ -29,12 +29,18 @@
 //   fresh maximum, and the (rarely taken) lazy rescale decided from stage
 //   u+1's maximum.  Two wavefronts per SIMD from different workgroups fill
 //   each other's gaps; forcing an instruction interleave measured slower.
-// K and V stages are copied global -> LDS by the DMA path
-// (global_load_lds_dwordx4, no VGPR staging) into double buffers one
-// iteration ahead of their use; the copies are spread between the MFMAs (V
-// of stage u+1 in phase A, K of stage u+2 in phase B).  LDS rows are padded by one 16-byte unit, so
-// the 8 lanes that share a bank window read 8 different 16-byte bank groups
-// and every read address is one per-lane base register plus an immediate.
+// K and V stages are copied global -> LDS by the buffer form of the DMA path
+// (buffer_load_dwordx4 ... lds, no VGPR staging) into double buffers during
+// the iteration before their use (K of stage u+2 and V of stage u+1 during
+// iteration u); the copies are spread between the MFMAs.  The buffer form counts on vmcnt only, so the LDS operand reads keep
+// partial lgkmcnt waits (the flat form of the same copy forces a full LDS
+// drain after each issue).  One sched_group_barrier order per stage keeps
+// every LDS operand read two MFMAs ahead of its use.  The kept-block list of
+// the query block is staged in LDS once, so the stage descriptors read it
+// there rather than with scalar loads.  LDS rows are padded by one 16-byte
+// unit, so the 8 lanes that share a bank window read 8 different 16-byte bank
+// groups and every read address is one per-lane base register plus an
+// immediate.
 // Online softmax with a lazy rescale: the running maximum is raised (and O, l
 // rescaled) only when a stage's maximum exceeds it by more than 8 (log2
 // units), so probabilities stay below 2^8 and most stages skip the rescale.
@@ -47,7 +53,6 @@ namespace dbs {
 namespace {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
 template <int D, int BLK>
@@ -77,6 +82,7 @@ constexpr float kLazyThreshold = 8.0f;
 // sched_group_barrier instruction classes
 constexpr int kSgMfma = 0x008;
 constexpr int kSgVmem = 0x020;   // vector-memory reads (the global -> LDS copies)
+constexpr int kSgDsRead = 0x100;
 
 __device__ __forceinline__ uint32_t cvt_pk(float a, float b) {
   bf16x2_t p;
@@ -97,9 +103,20 @@ __device__ __forceinline__ float sum_halves(float v) {
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Raw buffer descriptor over `bytes` bytes at `base` (gfx9 word 3: 32-bit data
+// format, raw addressing).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// 16 bytes per lane from buffer offset soff + voff into LDS at lds + 16 * lane.
+__device__ __forceinline__ void copy16_lds(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, 0);
+}
+
 struct StageDesc {
-  const __bf16* k;     // first K row of the stage (rows of D)
-  const __bf16* v;     // row 0 of the V^T tile, offset to the stage's first key column
+  uint32_t koffs;      // byte offset of the stage's first K row in its head
+  uint32_t voffs;      // byte offset of the stage's V^T columns in its head
+  bool glob;           // global-token tile (K_g / V_g) rather than a kept block
   int key0;            // index of the stage's first key (token, or global token)
   int kind;            // 0 full, 1 partial / invalid (mask by key index), 2 global tokens
   int limit;           // keys with index >= limit are masked (kind 1, 2)
@@ -122,6 +139,8 @@ void attn_fwd_kernel(
   __shared__ __attribute__((aligned(1024))) char Vb1[C::kVBytes];
   __shared__ __attribute__((aligned(1024))) char Kb0[C::kKBytes];
   __shared__ __attribute__((aligned(1024))) char Kb1[C::kKBytes];
+  // The kept-block list of this query block (invalid entries as 0xFFFF).
+  __shared__ uint16_t idx_s[4096];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -143,23 +162,32 @@ void attn_fwd_kernel(
   const int ntg = (k_g != nullptr) ? Ngpad / BLK : 0;
   const int U = (cnt + ntg) * C::kSubs;
 
+  // Buffer descriptors of this head's K rows, V^T tiles and global-token
+  // tiles (raw addressing, 32-bit data format: word 3 = 0x00020000 on gfx9).
+  // The copies address them with a per-stage scalar offset and per-lane
+  // offsets; buffer copies to LDS count on vmcnt only.
+  const auto rk = make_rsrc(k_r + rowbase * D, (uint32_t)Npad * (uint32_t)(D * 2));
+  const auto rv = make_rsrc(v_t + (int64_t)bh * nb * (D * BLK), (uint32_t)nb * (uint32_t)(D * BLK * 2));
+  const auto rkg = make_rsrc(ntg > 0 ? k_g + (int64_t)bh * Ngpad * D : k_r, (uint32_t)Ngpad * (uint32_t)(D * 2));
+  const auto rvg = make_rsrc(ntg > 0 ? v_g + (int64_t)bh * Ngpad * D : v_t, (uint32_t)Ngpad * (uint32_t)(D * 2));
+
   // Stage u: kept block j = u / kSubs of the list, or global-token tile j - cnt.
   // Selects only (no branches), so the copies can be scheduled inside the
   // MFMA phases.
   auto stage = [&](int u) -> StageDesc {
     StageDesc s;
-    const int j = u / C::kSubs, h = u % C::kSubs;
+    const int j = (int)((unsigned)u / C::kSubs), h = (int)((unsigned)u % C::kSubs);
     const bool kept = j < cnt;
     const int jj = kept ? j : (cnt > 0 ? cnt - 1 : 0);        // always inside the list row
-    int J = __builtin_amdgcn_readfirstlane(idx[jj]);
-    const bool ok = J >= 0 && J < nb;
-    J = ok ? J : 0;
+    const int Jr = __builtin_amdgcn_readfirstlane((int)idx_s[jj]);
+    const bool ok = Jr < nb;
+    const int J = ok ? Jr : 0;
     const int Jg = j - cnt;
     const int key0k = J * BLK + h * C::kKT, key0g = Jg * BLK + h * C::kKT;
     s.key0 = kept ? key0k : key0g;
-    s.k = kept ? k_r + (rowbase + key0k) * D : k_g + ((int64_t)bh * Ngpad + key0g) * D;
-    s.v = kept ? v_t + ((int64_t)bh * nb + J) * (int64_t)(D * BLK) + h * C::kKT
-               : v_g + ((int64_t)bh * (Ngpad / BLK) + Jg) * (int64_t)(D * BLK) + h * C::kKT;
+    s.koffs = (uint32_t)(kept ? key0k : key0g) * (uint32_t)(D * 2);
+    s.voffs = ((uint32_t)(kept ? J : Jg) * (uint32_t)(D * BLK) + (uint32_t)(h * C::kKT)) * 2u;
+    s.glob = !kept;
     s.limit = kept ? (ok ? N : -1) : Ng;
     s.kind = kept ? ((ok && key0k + C::kKT <= N) ? 0 : 1) : 2;
     return s;
@@ -190,14 +218,14 @@ void attn_fwd_kernel(
 #pragma unroll
     for (int i = 0; i < C::kKPer; ++i) {
       const int n = min(wave + i * C::kWaves, C::kKInstr - 1);
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(s.k + koff[i]), (lds_void_t*)(buf + 1024 * n), 16, 0, 0);
+      copy16_lds(s.glob ? rkg : rk, buf + 1024 * n, (uint32_t)koff[i] * 2u, s.koffs);
     }
   };
   auto dma_v = [&](const StageDesc& s, char* buf) {
 #pragma unroll
     for (int i = 0; i < C::kVPer; ++i) {
       const int n = min(wave + i * C::kWaves, C::kVInstr - 1);
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(s.v + voff[i]), (lds_void_t*)(buf + 1024 * n), 16, 0, 0);
+      copy16_lds(s.glob ? rvg : rv, buf + 1024 * n, (uint32_t)voff[i] * 2u, s.voffs);
     }
   };
 
@@ -252,16 +280,21 @@ void attn_fwd_kernel(
     }
   };
 
+  // Maximum of the 32 scores of one stage as a tree of 3-input maxima (16 ops).
   auto row_max = [&](const f32x16_t (&S)[2]) {
-    float a = S[0][0], b = S[1][0];
+    auto mx3 = [](float a, float b, float c) { return fmaxf(fmaxf(a, b), c); };
+    float x[32];
 #pragma unroll
-    for (int v = 1; v < 15; v += 2) {
-      a = fmaxf(a, fmaxf(S[0][v], S[0][v + 1]));
-      b = fmaxf(b, fmaxf(S[1][v], S[1][v + 1]));
+    for (int v = 0; v < 16; ++v) {
+      x[v] = S[0][v];
+      x[16 + v] = S[1][v];
     }
-    a = fmaxf(a, S[0][15]);
-    b = fmaxf(b, S[1][15]);
-    return fmaxf(a, b);
+    float a[10];
+#pragma unroll
+    for (int j = 0; j < 10; ++j) a[j] = mx3(x[3 * j], x[3 * j + 1], x[3 * j + 2]);
+    const float c = mx3(a[9], x[30], x[31]);
+    const float d = mx3(mx3(a[0], a[1], a[2]), mx3(a[3], a[4], a[5]), mx3(a[6], a[7], a[8]));
+    return fmaxf(d, c);
   };
 
   // Raise the running maximum (log2 units) when the stage maximum mx_raw (raw
@@ -287,17 +320,8 @@ void attn_fwd_kernel(
     if constexpr (kNext) {
       scores(ksrc, Sn);
       dma_v(*dv, vdst);
-      // Spread the copies between the score MFMAs: issued in one burst they
-      // stall every wavefront of the CU behind the address unit.
-      constexpr int kM = 2 * (D / 16), kStep = kM / C::kVPer;
-#pragma unroll
-      for (int i = 0; i < C::kVPer; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, kStep, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, kM - kStep * C::kVPer, 0);
     }
-    float s0 = 0.f, s1 = 0.f;
+    float s0, s1;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int kt = st >> 1, o = (st & 1) * 8;
@@ -306,8 +330,8 @@ void attn_fwd_kernel(
         const float pa = fast_exp2(__builtin_fmaf(Sc[kt][o + 2 * e], sl2, mneg));
         const float pb = fast_exp2(__builtin_fmaf(Sc[kt][o + 2 * e + 1], sl2, mneg));
         P[4 * st + e] = cvt_pk(pa, pb);
-        s0 += pa;
-        s1 += pb;
+        s0 = (st | e) == 0 ? pa : s0 + pa;
+        s1 = (st | e) == 0 ? pb : s1 + pb;
       }
     }
     l += s0 + s1;
@@ -335,13 +359,16 @@ void attn_fwd_kernel(
     if constexpr (kNext) {
       mx = row_max(Sn);
       dma_k(*dk, kdst);
-      constexpr int kM = 4 * (D / 32), kStep = kM / C::kKPer;
+      // One order for the whole stage: every LDS operand read runs 2 MFMAs
+      // ahead of its use, and the copies sit between the MFMAs.
+      constexpr int kL = 2, kMM = 2 * (D / 16) + 4 * (D / 32), kVm = C::kVPer + C::kKPer;
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, kL, 0);
 #pragma unroll
-      for (int i = 0; i < C::kKPer; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, kStep, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
+      for (int i = 0; i < kMM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        if (i + kL < kMM) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+        if (i % 3 == 1 && i / 3 < kVm) __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, kM - kStep * C::kKPer, 0);
     }
     return mx;
   };
@@ -378,6 +405,11 @@ void attn_fwd_kernel(
     phase_b(vsrc, P, unused, nullptr, nullptr, std::false_type{});
   };
 
+  for (int t = threadIdx.x; t < cnt; t += C::kThreads) {
+    const int J = idx[t];
+    idx_s[t] = (J >= 0 && J < nb) ? (uint16_t)J : (uint16_t)0xFFFF;
+  }
+  __syncthreads();
   if (U > 0) {
     const StageDesc s0 = stage(0);
     dma_k(s0, Kb0);

@@ -198,7 +198,10 @@ dbs_status dbs_meanpool_kv(const void* k_r, const void* v_r, dbs_dtype dt,
  * kv_count (NULL: rows in index order).  Entries are clamped to
  * [0, B*Hh*nb); an order that is not a permutation computes some rows twice
  * and leaves others untouched, but never reads or writes outside the
- * buffers. */
+ * buffers.  Q, K and V must be finite (a NaN input gives an undefined
+ * result).  Returns UNSUPPORTED for nb > 4096 (the kernel keeps a query
+ * block's list in LDS) or a head dimension / block size other than 64, 128;
+ * INVALID_ARG / ALIGNMENT for bad sizes or pointers. */
 dbs_status dbs_sparse_attn_fwd(const void* q_r, const void* k_r, const void* v_r, dbs_dtype dt,
                                int B, int Hh, int N, int Npad, int d, int b, float scale,
                                const int32_t* kv_count, const int32_t* kv_idx, const int32_t* order,

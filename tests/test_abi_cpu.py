@@ -180,6 +180,8 @@ def test_attn_and_pool_validation(dbs):
     assert call(10, float("inf")) == -1
     assert call(19, A + 2) == -3
     assert call(13, A + 2) == -3          # misaligned order
+    a = list(base); a[6] = 4097 * 64 - 10; a[7] = 4097 * 64; a[9] = 64
+    assert f(*a) == -2                    # nb = 4097 > 4096: the list no longer fits LDS
     g = L.lib().dbs_meanpool_kv
     assert g(A, A, 0, 1, 4, 1000, 1024, 128, 128, 0, A, A, None) == -1
     assert g(A, A, 1, 1, 4, 1000, 1024, 128, 128, 8, A, A, None) == -2
