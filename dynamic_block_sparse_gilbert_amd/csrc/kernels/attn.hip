@@ -37,7 +37,8 @@
 // drain after each issue).  One sched_group_barrier order per stage keeps
 // every LDS operand read two MFMAs ahead of its use.  The kept-block list of
 // the query block is staged in LDS once, so the stage descriptors read it
-// there rather than with scalar loads.  LDS rows are padded by one 16-byte
+// there rather than with scalar loads; each stage descriptor is computed
+// once, one iteration ahead of its score MFMAs.  LDS rows are padded by one 16-byte
 // unit, so the 8 lanes that share a bank window read 8 different 16-byte bank
 // groups and every read address is one per-lane base register plus an
 // immediate.
@@ -78,6 +79,12 @@ struct AttnCfg {
 };
 
 constexpr float kLazyThreshold = 8.0f;
+
+// Kept-block list words in LDS: bits 0-11 block index, bit 12 + h the stage
+// (half block) h is partial or invalid, bit 14 the entry is invalid.
+constexpr int kIndexMask = 0xFFF;
+constexpr int kPartial = 0x1000;
+constexpr int kInvalidBit = 0x4000;
 
 // sched_group_barrier instruction classes
 constexpr int kSgMfma = 0x008;
@@ -139,7 +146,8 @@ void attn_fwd_kernel(
   __shared__ __attribute__((aligned(1024))) char Vb1[C::kVBytes];
   __shared__ __attribute__((aligned(1024))) char Kb0[C::kKBytes];
   __shared__ __attribute__((aligned(1024))) char Kb1[C::kKBytes];
-  // The kept-block list of this query block (invalid entries as 0xFFFF).
+  // The kept-block list of this query block, one word per entry (index and
+  // masking flags, see kIndexMask).
   __shared__ uint16_t idx_s[4096];
 
   const int lane = threadIdx.x & 63;
@@ -173,23 +181,21 @@ void attn_fwd_kernel(
 
   // Stage u: kept block j = u / kSubs of the list, or global-token tile j - cnt.
   // Selects only (no branches), so the copies can be scheduled inside the
-  // MFMA phases.
+  // MFMA phases.  The list word carries the block index and the masking
+  // flags, so a full stage costs a handful of scalar operations.
+  const int cnt_m1 = cnt > 0 ? cnt - 1 : 0;
   auto stage = [&](int u) -> StageDesc {
     StageDesc s;
     const int j = (int)((unsigned)u / C::kSubs), h = (int)((unsigned)u % C::kSubs);
     const bool kept = j < cnt;
-    const int jj = kept ? j : (cnt > 0 ? cnt - 1 : 0);        // always inside the list row
-    const int Jr = __builtin_amdgcn_readfirstlane((int)idx_s[jj]);
-    const bool ok = Jr < nb;
-    const int J = ok ? Jr : 0;
-    const int Jg = j - cnt;
-    const int key0k = J * BLK + h * C::kKT, key0g = Jg * BLK + h * C::kKT;
-    s.key0 = kept ? key0k : key0g;
-    s.koffs = (uint32_t)(kept ? key0k : key0g) * (uint32_t)(D * 2);
-    s.voffs = ((uint32_t)(kept ? J : Jg) * (uint32_t)(D * BLK) + (uint32_t)(h * C::kKT)) * 2u;
+    const int w = __builtin_amdgcn_readfirstlane((int)idx_s[min(j, cnt_m1)]);
+    const int Jx = kept ? (w & kIndexMask) : j - cnt;
+    s.key0 = Jx * BLK + h * C::kKT;
+    s.koffs = (uint32_t)s.key0 * (uint32_t)(D * 2);
+    s.voffs = ((uint32_t)Jx * (uint32_t)(D * BLK) + (uint32_t)(h * C::kKT)) * 2u;
     s.glob = !kept;
-    s.limit = kept ? (ok ? N : -1) : Ng;
-    s.kind = kept ? ((ok && key0k + C::kKT <= N) ? 0 : 1) : 2;
+    s.kind = kept ? ((w >> h) & kPartial ? 1 : 0) : 2;
+    s.limit = kept ? ((w & kInvalidBit) ? -1 : N) : Ng;
     return s;
   };
 
@@ -377,11 +383,10 @@ void attn_fwd_kernel(
   // receive the DMAs of stages u+2 (K) and u+1 (V); ksrc holds K of stage u+1
   // and vsrc holds V of stage u.
   auto iterate = [&](int u, const f32x16_t (&Sc)[2], f32x16_t (&Sn)[2], char* kdst, char* vdst,
-                     const char* ksrc, const char* vsrc) {
+                     const char* ksrc, const char* vsrc, const StageDesc& sn) {
     wait_dma();
     __syncthreads();
     const StageDesc sk = stage(min(u + 2, U - 1));   // past the end: a harmless repeat
-    const StageDesc sn = stage(u + 1);
     uint32_t P[16];
     phase_a(Sc, Sn, ksrc, P, &sn, vdst, std::true_type{});
     float mx = phase_b(vsrc, P, Sn, &sk, kdst, std::true_type{});
@@ -393,6 +398,7 @@ void attn_fwd_kernel(
       mx = row_max(Sn);
     }
     decide(mx);
+    return sk;
   };
 
   // The last stage: no next stage to score.
@@ -407,14 +413,20 @@ void attn_fwd_kernel(
 
   for (int t = threadIdx.x; t < cnt; t += C::kThreads) {
     const int J = idx[t];
-    idx_s[t] = (J >= 0 && J < nb) ? (uint16_t)J : (uint16_t)0xFFFF;
+    const bool ok = J >= 0 && J < nb;
+    int w = ok ? J : kInvalidBit;
+#pragma unroll
+    for (int h = 0; h < C::kSubs; ++h)
+      if (!ok || J * BLK + (h + 1) * C::kKT > N) w |= kPartial << h;
+    idx_s[t] = (uint16_t)w;
   }
   __syncthreads();
   if (U > 0) {
     const StageDesc s0 = stage(0);
+    StageDesc sd = stage(min(1, U - 1));
     dma_k(s0, Kb0);
     dma_v(s0, Vb0);
-    dma_k(stage(min(1, U - 1)), Kb1);
+    dma_k(sd, Kb1);
     wait_dma();
     __syncthreads();
     f32x16_t SA[2], SB[2];
@@ -423,11 +435,11 @@ void attn_fwd_kernel(
     decide(row_max(SA));
     int u = 0;
     for (; u + 2 < U; u += 2) {
-      iterate(u, SA, SB, Kb0, Vb1, Kb1, Vb0);
-      iterate(u + 1, SB, SA, Kb1, Vb0, Kb0, Vb1);
+      sd = iterate(u, SA, SB, Kb0, Vb1, Kb1, Vb0, sd);
+      sd = iterate(u + 1, SB, SA, Kb1, Vb0, Kb0, Vb1, sd);
     }
     if (u + 1 < U) {
-      iterate(u, SA, SB, Kb0, Vb1, Kb1, Vb0);
+      iterate(u, SA, SB, Kb0, Vb1, Kb1, Vb0, sd);
       last(SB, Vb1);
     } else {
       last(SA, Vb0);
