@@ -34,12 +34,12 @@ SOURCES = [
 # Packed fp32 VALU ops are disabled on purpose: only plain fp32 ops are emitted.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
-# Per-source extra flags.  The attention kernel is compiled without NaN
-# semantics: its maximum reductions then map onto v_max3_f32 with no
-# canonicalising v_max_f32 x, x in front of every operand.  Infinities keep
-# their meaning (masked keys are -inf); NaN inputs give an undefined result
-# (an exact softmax of them is NaN anyway).
-SOURCE_FLAGS = {"kernels/attn.hip": ["-fno-honor-nans"]}
+# Per-source extra flags.  The attention and estimator kernels are compiled
+# without NaN semantics: their maximum reductions then map onto v_max3_f32
+# with no canonicalising v_max_f32 x, x in front of every operand.
+# Infinities keep their meaning (masked keys are -inf); NaN inputs give an
+# undefined result (an exact softmax of them is NaN anyway).
+SOURCE_FLAGS = {"kernels/attn.hip": ["-fno-honor-nans"], "kernels/estimate.hip": ["-fno-honor-nans"]}
 
 
 def hipcc() -> str:

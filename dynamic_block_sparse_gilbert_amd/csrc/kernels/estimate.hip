@@ -20,13 +20,13 @@
 //           max / sum (one partial per key split) and the block maxima t_qJ;
 //   final:  merge the partials into lse2 and form P_imp, one exp2 per
 //           (query block, key block).
-// The key range is split over enough workgroups (about 4096 in total) that
-// the DMA latency of each key chunk is hidden by other resident workgroups.
-// Both passes compute S^T = K_s Q_s^T on bf16 MFMA 16x16x32 with fp32
-// accumulation.  A workgroup of 4 wavefronts owns 64 sampled queries (16 per
-// wavefront, in VGPRs); the compact keys stream through double-buffered,
-// XOR-swizzled LDS in chunks of 64 by the global->LDS DMA path.  Lane
-// reductions use DPP row permutations and v_permlane16/32_swap (VALU, no LDS).
+// The key range is split over enough workgroups (about 1536 of 8
+// wavefronts) that every CU holds two of them through most of the launch.
+// The pass computes S^T = K_s Q_s^T on bf16 MFMA 32x32x16 with fp32
+// accumulation: a workgroup of 8 wavefronts owns 256 sampled queries (32 per
+// wavefront, in VGPRs), so each 64-key chunk copied to LDS feeds 256 queries;
+// the compact keys stream through double-buffered, row-padded LDS by the
+// buffer form of the global -> LDS copy.
 #include "common.h"
 #include "../launch.h"
 
@@ -34,47 +34,14 @@ namespace dbs {
 namespace {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kQPerWg = kWaves * 16;
+constexpr int kQPerWg = kWaves * 32;
 constexpr int kChunk = 64;
 constexpr int kMaxChunksPerSplit = 64;   // bound on chunks per key split
 
-__device__ __forceinline__ int swz(int u) { return (u & ~15) | ((u & 15) ^ ((u >> 4) & 15)); }
-
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Lane-exchange reductions (max).  The DPP controls are row-local (16 lanes):
-// quad_perm [1,0,3,2] = 0xb1, quad_perm [2,3,0,1] = 0x4e, row_half_mirror =
-// 0x141, row_mirror = 0x140.  Mirrors are enough for a reduction: after the
-// two quad steps every quad holds its maximum, the half-mirror pairs quad 0
-// with 1 (and 2 with 3), the mirror pairs the two halves of the row.
-__device__ __forceinline__ float dpp_max(float v, int ctrl) {
-  const int o = (ctrl == 0xb1) ? __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf, false)
-              : (ctrl == 0x4e) ? __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4e, 0xf, 0xf, false)
-              : (ctrl == 0x141) ? __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false)
-                                : __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false);
-  return fmaxf(v, __int_as_float(o));
-}
-// max over lanes l and l ^ 16 / l ^ 32
-__device__ __forceinline__ float max_x16(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float max_x32(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_x16(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float sum_x32(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 struct SampleGeom {
   int N, b, k, klog2, nb, nsp, nsp_pad, kj_last;
@@ -130,164 +97,230 @@ __global__ __launch_bounds__(256) void est_gather_kernel(
   *reinterpret_cast<uint4*>(ks + dst) = vk;
 }
 
-// Empty key slots of a chunk get a score of -inf (the rare chunks that hold
-// padding or the last block's empty slots; kept out of the common path).
-__device__ __forceinline__ void mask_chunk(const SampleGeom& sg, int ck0, int g4, f32x4_t (&s)[4]) {
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (!sg.valid(ck0 + 16 * t + 4 * g4 + j)) s[t][j] = -INFINITY;
+// Raw buffer descriptor over `bytes` bytes at `base` (gfx9 word 3: 32-bit data
+// format, raw addressing).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// 16 bytes per lane from buffer offset soff + voff into LDS at lds + 16 * lane
+// (the buffer form of the global -> LDS copy counts on vmcnt only).
+__device__ __forceinline__ void copy16_lds(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, 0);
 }
 
-// Common streaming loop: for every chunk of 64 compact keys, S^T tiles of the
-// wave's 16 queries (s[t][j]: key ck0 + 16t + 4*g4 + j, query l16) are handed
-// to `body(ck0, s)`.
-template <int D, typename Body>
-__device__ __forceinline__ void stream_keys(const __bf16* ks_bh, int c0, int c1,
-                                            const bf16x8_t (&qreg)[D / 32], Body&& body) {
-  constexpr int kUnits = kChunk * D / 8;       // 16-byte units per chunk
-  constexpr int kPer = kUnits / 64 / kWaves;   // DMA instructions per wave per chunk
-  // Two distinct arrays with statically known roles in each half of the
-  // 2x-unrolled loop: the compiler can then prove that the LDS reads of one
-  // buffer do not alias the DMA in flight into the other, and does not insert
-  // a wait for that DMA before the reads.
-  __shared__ __attribute__((aligned(16))) __bf16 Kc0[kUnits * 8];
-  __shared__ __attribute__((aligned(16))) __bf16 Kc1[kUnits * 8];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l16 = lane & 15, g4 = lane >> 4;
-  int off[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int u = swz(64 * (wave + i * kWaves) + lane);
-    off[i] = (u / (D / 8)) * D + (u % (D / 8)) * 8;
-  }
-  auto dma = [&](int chunk, __bf16* buf) {
-    const __bf16* base = ks_bh + (int64_t)chunk * kChunk * D;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int n = wave + i * kWaves;
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(base + off[i]), (lds_void_t*)(buf + 64 * n * 8), 16, 0, 0);
-    }
+template <int D>
+struct PassCfg {
+  static constexpr int kRowU = D / 8 + 1;            // 16-byte units per padded key row
+  static constexpr int kStride = kRowU * 16;         // bytes per padded key row in LDS
+  static constexpr int kBytes = kChunk * kStride;    // one chunk in LDS
+  static constexpr int kInstr = kBytes / 1024;       // copy instructions (1 KiB) per chunk
+  static constexpr int kPer = (kInstr + kWaves - 1) / kWaves;
+  static_assert(kBytes % 1024 == 0, "a chunk must be whole copy instructions");
+};
+
+// Cell maxima of one chunk (keys ck0 .. ck0 + 63) of the wave's 32 queries.
+// S[kt][v] holds key ck0 + 32 kt + (v / 4) * 8 + 4 g + v % 4 of query l32.
+// Returns the lane's maximum over its 32 scores; stores each cell maximum of
+// query rq (when `store`) at trow[cell] for the cells that start below nsp
+// (the padding keys of the last chunk have no cell).  K as in est_pass_kernel.
+template <int K>
+__device__ __forceinline__ float cell_maxima(const f32x16_t (&S)[2], int ck0, int g, int cell_log2, int nsp,
+                                             float* trow, bool store) {
+  auto mx3 = [](float a, float b, float c) { return fmaxf(fmaxf(a, b), c); };
+  auto max4 = [&](const f32x16_t& t, int v0) { return fmaxf(fmaxf(t[v0], t[v0 + 1]), fmaxf(t[v0 + 2], t[v0 + 3])); };
+  auto max8 = [&](const f32x16_t& t, int v0) {
+    return fmaxf(mx3(t[v0], t[v0 + 1], t[v0 + 2]), mx3(t[v0 + 3], mx3(t[v0 + 4], t[v0 + 5], t[v0 + 6]), t[v0 + 7]));
   };
-  auto compute = [&](int ch, const __bf16* kb) {
-    f32x4_t s[4];
+  // Pair exchange across the wave halves: lanes of half 0 get max(a0, a1),
+  // lanes of half 1 get max(b0, b1) (x0 from half 0, x1 from half 1).
+  auto swap_max = [](float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  };
+  if constexpr (K >= 64) {
+    const float x = fmaxf(fmaxf(max8(S[0], 0), max8(S[0], 8)), fmaxf(max8(S[1], 0), max8(S[1], 8)));
+    const float c = swap_max(x, x);
+    if (store && g == 0 && ck0 < nsp) trow[ck0 >> cell_log2] = c;
+    return x;
+  } else if constexpr (K == 32) {
+    const float x0 = fmaxf(max8(S[0], 0), max8(S[0], 8)), x1 = fmaxf(max8(S[1], 0), max8(S[1], 8));
+    const float c = swap_max(x0, x1);   // half 0: tile 0, half 1: tile 1
+    if (store && ck0 + 32 * g < nsp) trow[(ck0 + 32 * g) >> 5] = c;
+    return fmaxf(x0, x1);
+  } else if constexpr (K == 16) {
+    float x = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      s[t] = f32x4_t{};
+    for (int kt = 0; kt < 2; ++kt) {
+      const float lo = max8(S[kt], 0), hi = max8(S[kt], 8);
+      const float c = swap_max(lo, hi);   // half 0: keys 0-15 of the tile, half 1: keys 16-31
+      const int key = ck0 + 32 * kt + 16 * g;
+      if (store && key < nsp) trow[key >> 4] = c;
+      x = mx3(x, lo, hi);
+    }
+    return x;
+  } else if constexpr (K == 8) {
+    float x = -INFINITY;
 #pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) {
-        const int u = (16 * t + l16) * (D / 8) + 4 * kk + g4;
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kb + swz(u) * 8);
-        s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[kk], s[t], 0, 0, 0);
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const float a = max4(S[kt], 8 * p), b = max4(S[kt], 8 * p + 4);
+        const float c = swap_max(a, b);   // cells of keys 16p + 0-7 (half 0) and 16p + 8-15 (half 1)
+        const int key = ck0 + 32 * kt + 16 * p + 8 * g;
+        if (store && key < nsp) trow[key >> 3] = c;
+        x = mx3(x, a, b);
       }
     }
-    body(ch * kChunk, s);
+    return x;
+  } else {
+    // K = 1, 2, 4: every cell lies inside one lane's run of 4 keys.
+    float x = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int key = ck0 + 32 * kt + 8 * a4 + 4 * g;
+        const float t[4] = {S[kt][4 * a4], S[kt][4 * a4 + 1], S[kt][4 * a4 + 2], S[kt][4 * a4 + 3]};
+        if constexpr (K == 4) {
+          const float c = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
+          if (store && key < nsp) trow[key >> 2] = c;
+          x = fmaxf(x, c);
+        } else if constexpr (K == 2) {
+          const float c0 = fmaxf(t[0], t[1]), c1 = fmaxf(t[2], t[3]);
+          if (store && key < nsp) trow[key >> 1] = c0;
+          if (store && key + 2 < nsp) trow[(key >> 1) + 1] = c1;
+          x = mx3(x, c0, c1);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (store && key + e < nsp) trow[key + e] = t[e];
+          x = mx3(x, fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
+        }
+      }
+    }
+    return x;
+  }
+}
+
+// K: the sample count k when k <= 32 (a cell is one block of K keys); 64
+// stands for every k >= 64 (a cell is one 64-key chunk).  A compile-time
+// constant, so the reductions are straight-line code.
+//
+// A workgroup of 8 wavefronts owns 256 sampled queries (32 per wavefront, Q^T
+// in VGPRs) and one key split: S^T = K_s Q_s^T on 32x32x16 bf16 MFMAs, with
+// the compact keys streamed through double-buffered, row-padded LDS in chunks
+// of 64 by the buffer form of the global -> LDS copy.  Each lane holds whole
+// query columns, so the online (max, sum) runs per lane and the two wave
+// halves merge at the end.
+template <int D, int K>
+__global__ __launch_bounds__(kThreads) void est_pass_kernel(
+    const __bf16* __restrict__ qs, const __bf16* __restrict__ ks, float2* __restrict__ part,
+    float* __restrict__ tmax, SampleGeom sg, float sl2) {
+  using C = PassCfg<D>;
+  // Distinct arrays with static roles in each half of the 2x-unrolled loop,
+  // so the LDS reads of one are not made to wait for the copy into the other.
+  __shared__ __attribute__((aligned(1024))) char Kc0[C::kBytes];
+  __shared__ __attribute__((aligned(1024))) char Kc1[C::kBytes];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  int bh, split, panel;
+  wg_coords(sg, bh, split, panel);
+  const int rq = panel * kQPerWg + wave * 32 + l32;
+  const bool qok = rq < sg.nsp;
+
+  // Q^T operand: lane (l32, g) holds Q_s[rq][16 kk + 8 g .. +7].
+  bf16x8_t qreg[D / 16];
+  {
+    const int rl = min(rq, sg.nsp_pad - 1);
+    const __bf16* qp = qs + ((int64_t)bh * sg.nsp_pad + rl) * D + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * kk);
+  }
+
+  // Copies: LDS byte 1024 n + 16 lane of a chunk holds padded unit p = 64 n +
+  // lane, i.e. key row p / kRowU, unit p % kRowU (the pad unit repeats the
+  // row's last unit).  Surplus instructions repeat the chunk's last one.
+  const auto rk = make_rsrc(ks + (int64_t)bh * sg.nsp_pad * D, (uint32_t)sg.nsp_pad * (uint32_t)(D * 2));
+  uint32_t voff[C::kPer];
+#pragma unroll
+  for (int i = 0; i < C::kPer; ++i) {
+    const int n = min(wave + i * kWaves, C::kInstr - 1);
+    const int p = 64 * n + lane;
+    const int row = p / C::kRowU, c = min(p % C::kRowU, C::kRowU - 2);
+    voff[i] = (uint32_t)(row * D * 2 + c * 16);
+  }
+  auto dma = [&](int ch, char* buf) {
+#pragma unroll
+    for (int i = 0; i < C::kPer; ++i) {
+      const int n = min(wave + i * kWaves, C::kInstr - 1);
+      copy16_lds(rk, buf + 1024 * n, voff[i], (uint32_t)ch * (uint32_t)(kChunk * D * 2));
+    }
   };
+  const int kbase = l32 * C::kStride + 16 * g;
+  auto scores = [&](const char* kb, f32x16_t (&S)[2]) {
+    S[0] = f32x16_t{};
+    S[1] = f32x16_t{};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kb + kbase + kt * 32 * C::kStride + kk * 32);
+        S[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], S[kt], 0, 0, 0);
+      }
+    }
+  };
+
+  float m = -INFINITY, l = 0.f;
+  float* trow = tmax + ((int64_t)bh * sg.nsp + (qok ? rq : 0)) * sg.ncell;
+  const int tail = (sg.nb - 1) * sg.k;   // first slot of the last block
+  auto body = [&](int ch, f32x16_t (&S)[2]) {
+    const int ck0 = ch * kChunk;
+    if (ck0 + kChunk > sg.nsp || (sg.kj_last < sg.k && ck0 + kChunk > tail)) {
+      // rare: padding or the last block's empty slots score -inf
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (!sg.valid(ck0 + 32 * kt + (v >> 2) * 8 + 4 * g + (v & 3))) S[kt][v] = -INFINITY;
+    }
+    const float mx = cell_maxima<K>(S, ck0, g, sg.cell_log2, sg.nsp, trow, qok) * sl2;
+    const float m_new = fmaxf(m, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    float s0 = l * fast_exp2(m - m_use), s1 = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      s0 += fast_exp2(__builtin_fmaf(S[0][v], sl2, -m_use));
+      s1 += fast_exp2(__builtin_fmaf(S[1][v], sl2, -m_use));
+    }
+    l = s0 + s1;
+    m = m_new;
+  };
+
+  const int c0 = split * sg.cps, c1 = min(sg.nsp_pad / kChunk, c0 + sg.cps);
+  f32x16_t S[2];
   dma(c0, Kc0);
   for (int ch = c0; ch < c1; ch += 2) {
     wait_dma();
     __syncthreads();
     if (ch + 1 < c1) dma(ch + 1, Kc1);
-    compute(ch, Kc0);
+    scores(Kc0, S);
+    body(ch, S);
     if (ch + 1 < c1) {
       wait_dma();
       __syncthreads();
       if (ch + 2 < c1) dma(ch + 2, Kc0);
-      compute(ch + 1, Kc1);
+      scores(Kc1, S);
+      body(ch + 1, S);
     }
   }
-}
-
-template <int D>
-__device__ __forceinline__ void load_q(const __bf16* qs_bh, int rq, int g4, bf16x8_t (&qreg)[D / 32]) {
-  const __bf16* qp = qs_bh + (int64_t)rq * D + 8 * g4;
-#pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * kk);
-}
-
-// Raw block maxima of one 16-key score tile (keys ck0 + 16t + 4*g4 + j, query
-// l16): groups of kr = min(K, 16) consecutive keys, nv values per lane.
-template <int K>
-__device__ __forceinline__ void group_max(const f32x4_t& s, float (&v)[4]) {
-  constexpr int kr = K < 16 ? K : 16;
-  if constexpr (kr >= 4) {
-    v[0] = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    if constexpr (kr >= 8) v[0] = max_x16(v[0]);
-    if constexpr (kr >= 16) v[0] = max_x32(v[0]);
-  } else if constexpr (kr == 2) {
-    v[0] = fmaxf(s[0], s[1]);
-    v[1] = fmaxf(s[2], s[3]);
-  } else {
-    v[0] = s[0]; v[1] = s[1]; v[2] = s[2]; v[3] = s[3];
-  }
-}
-
-// K: the sample count k when k <= 32 (a cell is one block: a group of K keys
-// inside one 16-key tile, or for K = 32 two tiles); 64 stands for every
-// k >= 64 (a cell is one 64-key chunk).  A compile-time constant, so the
-// reductions below are straight-line code.
-template <int D, int K>
-__global__ __launch_bounds__(kThreads) void est_pass_kernel(
-    const __bf16* __restrict__ qs, const __bf16* __restrict__ ks, float2* __restrict__ part,
-    float* __restrict__ tmax, SampleGeom sg, float sl2) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l16 = lane & 15, g4 = lane >> 4;
-  int bh, split, panel;
-  wg_coords(sg, bh, split, panel);
-  const int rq = panel * kQPerWg + wave * 16 + l16;
-  bf16x8_t qreg[D / 32];
-  load_q<D>(qs + (int64_t)bh * sg.nsp_pad * D, rq, g4, qreg);
-  float m = -INFINITY, l = 0.f;
-  constexpr int kr = K < 16 ? K : 16;
-  constexpr int nv = kr >= 4 ? 1 : 4 / kr;
-  const bool krep = kr >= 4 ? ((g4 & ((kr >> 2) - 1)) == 0) : true;
-  float* trow = tmax + ((int64_t)bh * sg.nsp + rq) * sg.ncell;
-  const bool qok = rq < sg.nsp;
-  const int tail = (sg.nb - 1) * sg.k;   // first slot of the last block
-  const int c0 = split * sg.cps, c1 = min(sg.nsp_pad / kChunk, c0 + sg.cps);
-  stream_keys<D>(ks + (int64_t)bh * sg.nsp_pad * D, c0, c1, qreg, [&](int ck0, f32x4_t (&s)[4]) {
-    if ((ck0 + kChunk > sg.nsp) || (sg.kj_last < sg.k && ck0 + kChunk > tail)) mask_chunk(sg, ck0, g4, s);
-    // block (cell) maxima of the raw scores
-    float gv[4][4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) group_max<K>(s[t], gv[t]);
-    if constexpr (K == 32) {           // cells of two tiles: 0-1, 2-3
-      gv[0][0] = fmaxf(gv[0][0], gv[1][0]);
-      gv[2][0] = fmaxf(gv[2][0], gv[3][0]);
-    } else if constexpr (K == 64) {    // one cell: the whole chunk
-      gv[0][0] = fmaxf(fmaxf(gv[0][0], gv[1][0]), fmaxf(gv[2][0], gv[3][0]));
-    }
-    constexpr int tstep = K >= 64 ? 4 : (K == 32 ? 2 : 1);
-    if (qok && krep) {
-#pragma unroll
-      for (int t = 0; t < 4; t += tstep) {
-#pragma unroll
-        for (int e = 0; e < nv; ++e) {
-          const int ck = ck0 + 16 * t + 4 * g4 + e * kr;
-          if (ck < sg.nsp) trow[ck >> sg.cell_log2] = gv[t][e];
-        }
-      }
-    }
-    // online normaliser
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s[t][j]);
-    mx = max_x32(max_x16(mx)) * sl2;
-    const float m_new = fmaxf(m, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    l *= fast_exp2(m - m_use);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) l += fast_exp2(__builtin_fmaf(s[t][j], sl2, -m_use));
-    }
-    m = m_new;
-  });
-  l = sum_x32(sum_x16(l));
-  if (g4 == 0 && qok) part[((int64_t)bh * sg.splits + split) * sg.nsp + rq] = make_float2(m, l);
+  // merge the two wave halves (each saw half of every chunk's keys)
+  const auto rm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  const float M = fmaxf(__uint_as_float(rm[0]), __uint_as_float(rm[1]));
+  const float mine = (M == -INFINITY) ? 0.f : l * fast_exp2(m - M);
+  const auto rl = __builtin_amdgcn_permlane32_swap(__float_as_uint(mine), __float_as_uint(mine), false, false);
+  const float L = __uint_as_float(rl[0]) + __uint_as_float(rl[1]);
+  if (g == 0 && qok) part[((int64_t)bh * sg.splits + split) * sg.nsp + rq] = make_float2(M, L);
 }
 
 // log2 of the softmax normaliser of sampled query rq from its per-split partials.
@@ -338,14 +371,14 @@ __global__ __launch_bounds__(kFinalThreads) void est_final_kernel(const float2* 
   }
 }
 
-// Key splits: enough workgroups in total (about 4096) to hide the latency of
-// each chunk's DMA behind other resident workgroups.
+// Key splits: about 1536 workgroups in total (three waves of two 8-wavefront
+// workgroups per CU), each streaming a contiguous range of 64-key chunks.
 void split_plan(int BH, int nsp, int& splits, int& cps) {
   const int nsp_pad = (nsp + kChunk - 1) / kChunk * kChunk;
   const int nchunks = nsp_pad / kChunk;
   const int panels = (nsp + kQPerWg - 1) / kQPerWg;
   const int64_t wgs = (int64_t)panels * BH;
-  int want = (int)((4096 + wgs - 1) / wgs);
+  int want = (int)((1536 + wgs - 1) / wgs);
   want = want < 1 ? 1 : (want > nchunks ? nchunks : want);
   cps = (nchunks + want - 1) / want;
   if (cps > kMaxChunksPerSplit) cps = kMaxChunksPerSplit;

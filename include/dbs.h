@@ -125,8 +125,8 @@ dbs_status dbs_inverse_reorder(const void* y, dbs_dtype y_dt, void* x, dbs_dtype
 /* Bytes of device workspace dbs_estimate_blocks needs: compact copies of the
  * sampled Q and K rows (B * Hh * ceil(nb*k / 64)*64 * d bf16 each), one
  * partial softmax (max, sum) float pair per sampled query and key split (the
- * library splits the sampled keys over up to nb*k/64 workgroups per query
- * panel), and per sampled query the maximum raw score over each cell of
+ * library splits the sampled keys over up to nb*k/64 workgroups per panel of
+ * 256 sampled queries), and per sampled query the maximum raw score over each cell of
  * min(k, 64) sampled keys (B * Hh * nb*k * nb*k/min(k,64) floats; about
  * 50 MB for 12 heads, nb = 256, k = 16).  Returns 0 for invalid sizes. */
 size_t dbs_estimate_workspace_bytes(int B, int Hh, int N, int d, int b, int k);
@@ -139,7 +139,8 @@ size_t dbs_estimate_workspace_bytes(int B, int Hh, int N, int d, int b, int k);
  * (samples of J), float32, [B, Hh, nb, nb].
  * q_r, k_r: DBS_ROWS, type dt (DBS_BF16 only).  k: a power of two, 1..b.
  * workspace: device, >= dbs_estimate_workspace_bytes(...) bytes; its contents
- * on entry do not matter.  Errors: UNSUPPORTED for d, b, k or dt outside the
+ * on entry do not matter.  Q and K must be finite (a NaN input gives an
+ * undefined result).  Errors: UNSUPPORTED for d, b, k or dt outside the
  * supported set; INVALID_ARG for a small workspace. */
 dbs_status dbs_estimate_blocks(const void* q_r, const void* k_r, dbs_dtype dt,
                                int B, int Hh, int N, int Npad, int d, int b, int k, float scale,
