@@ -324,16 +324,23 @@ __global__ __launch_bounds__(kThreads) void est_pass_kernel(
 }
 
 // log2 of the softmax normaliser of sampled query rq from its per-split partials.
+// The splits are merged in one sweep with a running maximum (the partials of
+// up to 8 splits are loaded together).
 __device__ __forceinline__ float merge_lse2(const float2* part_bh, const SampleGeom& sg, int rq) {
-  float M = -INFINITY;
-  for (int s = 0; s < sg.splits; ++s) M = fmaxf(M, part_bh[(int64_t)s * sg.nsp + rq].x);
-  if (M == -INFINITY) return INFINITY;
-  float L = 0.f;
-  for (int s = 0; s < sg.splits; ++s) {
-    const float2 p = part_bh[(int64_t)s * sg.nsp + rq];
-    L += p.y * fast_exp2(p.x - M);
+  float M = -INFINITY, L = 0.f;
+  for (int s0 = 0; s0 < sg.splits; s0 += 8) {
+    float2 p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      p[e] = s0 + e < sg.splits ? part_bh[(int64_t)(s0 + e) * sg.nsp + rq] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float Mn = fmaxf(M, p[e].x);
+      if (Mn != -INFINITY) L = L * fast_exp2(M - Mn) + p[e].y * fast_exp2(p[e].x - Mn);
+      M = Mn;
+    }
   }
-  return M + __log2f(L);
+  return M == -INFINITY ? INFINITY : M + __log2f(L);
 }
 
 // P_imp of one (batch, head, query block I) row: lse2 of the block's valid
@@ -361,11 +368,21 @@ __global__ __launch_bounds__(kFinalThreads) void est_final_kernel(const float2* 
   float* prow = p_imp + ((int64_t)bh * sg.nb + I) * sg.nb;
   for (int J = tid; J < sg.nb; J += kFinalThreads) {
     float best = -INFINITY;
-    for (int t = 0; t < kI; ++t) {
-      const float* tr = t0 + (int64_t)t * sg.ncell + J * cpb;
-      float v = tr[0];
-      for (int c = 1; c < cpb; ++c) v = fmaxf(v, tr[c]);
-      best = fmaxf(best, __builtin_fmaf(v, sl2, -lse[t]));
+    // 8 sampled queries at a time, their loads issued together
+    for (int t0q = 0; t0q < kI; t0q += 8) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int t = min(t0q + e, kI - 1);
+        const float* tr = t0 + (int64_t)t * sg.ncell + J * cpb;
+        v[e] = tr[0];
+        for (int c = 1; c < cpb; ++c) v[e] = fmaxf(v[e], tr[c]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int t = min(t0q + e, kI - 1);
+        best = fmaxf(best, __builtin_fmaf(v[e], sl2, -lse[t]));
+      }
     }
     prow[J] = fast_exp2(best);
   }
