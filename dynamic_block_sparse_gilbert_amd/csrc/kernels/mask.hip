@@ -9,12 +9,15 @@
 // running prefix are all exact; "prefix >= tau * total" is then decided
 // without rounding and the result cannot depend on the summation order.
 //
-// One workgroup per row: the row is sorted in LDS by a bitonic network on
-// 64-bit keys (~value bits, block index), which orders by value descending
-// and index ascending; wavefront 0 scans the sorted values 64 at a time
-// until the prefix reaches the target; the kept blocks are then written in
-// ascending index order by a block-wide compaction.  Optionally a second
-// launch turns the kept counts into the attention kernel's work order.
+// Rows of up to 256 blocks take one wavefront each (four rows per workgroup,
+// no workgroup barrier): the 64-bit keys (~value bits, block index), which
+// order by value descending and index ascending, are sorted in registers by
+// a bitonic network with cross-lane exchanges; one wavefront scan of the
+// lanes' exact sums finds the first prefix that reaches the target.  Longer
+// rows take one workgroup each and sort in LDS, wavefront 0 scanning the
+// sorted values 64 at a time.  The kept blocks are written in ascending index
+// order by a compaction.  Optionally a second launch turns the kept counts
+// into the attention kernel's work order.
 #include "common.h"
 #include "../launch.h"
 
@@ -271,6 +274,184 @@ __global__ __launch_bounds__(kThreads) void build_mask_kernel(
   if (tid == 0) kv_count[row] = m;
 }
 
+// Rows of up to 256 blocks: one wavefront per row, four rows per workgroup,
+// no workgroup barrier.  Lane l holds the KPL = P2 / 64 keys of elements
+// l * KPL .. l * KPL + KPL - 1 in registers; the bitonic network compares
+// element e with e ^ j: for j < KPL inside the lane, otherwise with lane
+// l ^ (j / KPL) through a cross-lane exchange (ds_swizzle xor below 32,
+// v_permlane32_swap at 32).  The exact sums are the same 192-bit integers as
+// in build_mask_kernel, so the result is identical.
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v, int d) {
+  switch (d) {   // ds_swizzle bit mode: and_mask 0x1f, xor_mask d (within 32 lanes)
+    case 1: return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x041f);
+    case 2: return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x081f);
+    case 4: return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x101f);
+    case 8: return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x201f);
+    case 16: return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401f);
+    default: {
+      const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+      return (threadIdx.x & 32) ? r[0] : r[1];
+    }
+  }
+}
+
+template <int KPL>
+__global__ __launch_bounds__(256) void build_mask_wave_kernel(
+    const float* __restrict__ p_imp, int nb, int rows, uint32_t tau_bits, int32_t* __restrict__ kv_count,
+    int32_t* __restrict__ kv_idx, uint8_t* __restrict__ mask) {
+  constexpr int P2 = 64 * KPL;
+  __shared__ uint8_t flag_all[4][P2];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + w;
+  if (row >= rows) return;
+  uint8_t* flag = flag_all[w];
+  const uint32_t* prow = reinterpret_cast<const uint32_t*>(p_imp) + row * nb;
+
+  uint64_t key[KPL];
+  bool bad = false;
+#pragma unroll
+  for (int r = 0; r < KPL; ++r) {
+    const int e = lane * KPL + r;
+    key[r] = ~0ull;
+    if (e < nb) {
+      uint32_t bits = prow[e];
+      if ((bits & 0x7fffffffu) == 0) bits = 0;          // -0 is 0
+      if (bits > 0x3f800000u) bad = true;               // negative, > 1, inf, NaN
+      key[r] = ((uint64_t)(~bits) << 32) | (uint32_t)e;
+    }
+  }
+  const bool keep_all = __ballot(bad) != 0 || tau_bits >= 0x3f800000u;
+
+  int m = nb;
+  if (!keep_all) {
+    // ---- bitonic sort, ascending keys ------------------------------------------
+#pragma unroll
+    for (int k = 2; k <= P2; k <<= 1) {
+#pragma unroll
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        if (j >= KPL) {
+          const int d = j / KPL;
+#pragma unroll
+          for (int r = 0; r < KPL; ++r) {
+            const int e = lane * KPL + r;
+            const uint64_t o = ((uint64_t)lane_xor((uint32_t)(key[r] >> 32), d) << 32) |
+                               lane_xor((uint32_t)key[r], d);
+            const bool keep_min = ((e & j) == 0) == ((e & k) == 0);
+            key[r] = keep_min ? (o < key[r] ? o : key[r]) : (o > key[r] ? o : key[r]);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < KPL; ++r) {
+            if (r & j) continue;
+            const int e = lane * KPL + r;
+            const uint64_t a = key[r], b = key[r | j];
+            const bool asc = (e & k) == 0;
+            if ((a > b) == asc) {
+              key[r] = b;
+              key[r | j] = a;
+            }
+          }
+        }
+      }
+    }
+    // ---- exact row total and target ceil(tau * total) ----------------------------
+    U192 val[KPL];
+    U192 lsum = u192_zero();
+#pragma unroll
+    for (int r = 0; r < KPL; ++r) {
+      val[r] = lane * KPL + r < nb ? f32_to_u192(~(uint32_t)(key[r] >> 32)) : u192_zero();
+      lsum = u192_add(lsum, val[r]);
+    }
+    const U192 total = wave_sum(lsum);
+    const uint32_t te = tau_bits >> 23;
+    const uint64_t tm = te ? ((tau_bits & 0x7fffffu) | 0x800000u) : (tau_bits & 0x7fffffu);
+    const int sh = te ? 150 - (int)te : 149;
+    uint32_t prod[kLimbs + 1];
+    uint64_t c = 0;
+#pragma unroll
+    for (int i = 0; i < kLimbs; ++i) {
+      const uint64_t t = (uint64_t)total.w[i] * tm + c;
+      prod[i] = (uint32_t)t;
+      c = t >> 32;
+    }
+    prod[kLimbs] = (uint32_t)c;
+    U192 tgt = u192_zero();
+    bool sticky = false;
+    const int ls = sh >> 5, bs = sh & 31;
+    for (int i = 0; i < kLimbs; ++i) {
+      const int src = i + ls;
+      uint32_t v = 0;
+      if (src <= kLimbs) {
+        v = prod[src] >> bs;
+        if (bs && src + 1 <= kLimbs) v |= prod[src + 1] << (32 - bs);
+      }
+      tgt.w[i] = v;
+    }
+    for (int i = 0; i < ls && i <= kLimbs; ++i) sticky |= prod[i] != 0;
+    if (ls <= kLimbs && bs) sticky |= (prod[ls] & ((1u << bs) - 1u)) != 0;
+    if (sticky) {
+      U192 one = u192_zero();
+      one.w[0] = 1;
+      tgt = u192_add(tgt, one);
+    }
+    // ---- minimal prefix over the sorted values ------------------------------------
+    // prefix of element e = (sums of lanes below) + (the lane's values up to e)
+    const U192 incl = wave_inclusive_scan(lsum, lane);
+    U192 run;
+#pragma unroll
+    for (int i = 0; i < kLimbs; ++i) run.w[i] = shfl_from_u32(incl.w[i], lane > 0 ? lane - 1 : 0);
+    if (lane == 0) run = u192_zero();
+    int first = KPL;   // first element of this lane whose prefix reaches the target
+#pragma unroll
+    for (int r = 0; r < KPL; ++r) {
+      run = u192_add(run, val[r]);
+      if (first == KPL && lane * KPL + r < nb && u192_ge(run, tgt)) first = r;
+    }
+    const uint64_t ball = __ballot(first < KPL);
+    const int fl = ball ? __ffsll((unsigned long long)ball) - 1 : 63;
+    const int fr = __shfl(first, fl, 64);
+    m = ball ? fl * KPL + fr + 1 : nb;
+  }
+
+  // ---- kept flags, then ascending compaction ----------------------------------------
+#pragma unroll
+  for (int r = 0; r < KPL; ++r) flag[lane * KPL + r] = 0;
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int r = 0; r < KPL; ++r) {
+    const int e = lane * KPL + r;
+    if (e < m) flag[keep_all ? e : (uint32_t)key[r]] = 1;
+  }
+  __builtin_amdgcn_wave_barrier();
+  int cnt = 0;
+  uint8_t f[KPL];
+#pragma unroll
+  for (int r = 0; r < KPL; ++r) {
+    f[r] = lane * KPL + r < nb ? flag[lane * KPL + r] : 0;
+    cnt += f[r];
+  }
+  int inc = cnt;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int src = lane >= d ? lane - d : lane;
+    const int o = __builtin_amdgcn_ds_bpermute(src << 2, inc);
+    if (lane >= d) inc += o;
+  }
+  int pos = inc - cnt;
+  int32_t* irow = kv_idx + row * nb;
+#pragma unroll
+  for (int r = 0; r < KPL; ++r) {
+    if (f[r]) irow[pos++] = lane * KPL + r;
+  }
+  if (mask != nullptr) {
+    uint8_t* mrow = mask + row * nb;
+#pragma unroll
+    for (int r = 0; r < KPL; ++r)
+      if (lane * KPL + r < nb) mrow[lane * KPL + r] = f[r];
+  }
+  if (lane == 0) kv_count[row] = m;
+}
+
 // Work order for the attention kernel: rows (b, h, I) are split into the
 // eight contiguous ranges that the attention launch assigns to the eight
 // XCDs (see xcd_range in common.h), and each range is listed by kept count
@@ -329,11 +510,15 @@ __global__ __launch_bounds__(kOrderThreads) void build_order_kernel(const int32_
 hipError_t launch_build_mask(const MaskArgs& a) {
   uint32_t tau_bits;
   __builtin_memcpy(&tau_bits, &a.tau, 4);
+  const dim3 wgrid((unsigned)((a.rows + 3) / 4));
   if (a.nb <= 64) {
-    hipLaunchKernelGGL((build_mask_kernel<64, 64>), dim3(a.rows), dim3(64), 0, a.stream, a.p_imp, a.nb,
+    hipLaunchKernelGGL((build_mask_wave_kernel<1>), wgrid, dim3(256), 0, a.stream, a.p_imp, a.nb, a.rows,
+                       tau_bits, a.kv_count, a.kv_idx, a.mask);
+  } else if (a.nb <= 128) {
+    hipLaunchKernelGGL((build_mask_wave_kernel<2>), wgrid, dim3(256), 0, a.stream, a.p_imp, a.nb, a.rows,
                        tau_bits, a.kv_count, a.kv_idx, a.mask);
   } else if (a.nb <= 256) {
-    hipLaunchKernelGGL((build_mask_kernel<256, 128>), dim3(a.rows), dim3(128), 0, a.stream, a.p_imp, a.nb,
+    hipLaunchKernelGGL((build_mask_wave_kernel<4>), wgrid, dim3(256), 0, a.stream, a.p_imp, a.nb, a.rows,
                        tau_bits, a.kv_count, a.kv_idx, a.mask);
   } else if (a.nb <= 1024) {
     hipLaunchKernelGGL((build_mask_kernel<1024, 256>), dim3(a.rows), dim3(256), 0, a.stream, a.p_imp, a.nb,
