@@ -186,14 +186,25 @@ size_t dbs_estimate_workspace_bytes(int B, int Hh, int N, int d, int b, int k) {
   return dbs::estimate_workspace_bytes(B, Hh, nb, k, d);
 }
 
-dbs_status dbs_estimate_blocks(const void* q_r, const void* k_r, dbs_dtype dt, int B, int Hh, int N,
-                               int Npad, int d, int b, int k, float scale, float* p_imp,
-                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  DBS_GUARD_BEGIN
-  REQUIRE(q_r && k_r && p_imp && workspace, DBS_ERR_INVALID_ARG, "NULL pointer");
-  REQUIRE(aligned16(q_r) && aligned16(k_r) && aligned16(p_imp) && aligned16(workspace),
-          DBS_ERR_ALIGNMENT, "misaligned pointer");
-  REQUIRE(dt == DBS_BF16, DBS_ERR_UNSUPPORTED, "estimate_blocks computes on bf16 inputs");
+}  // extern "C"
+
+namespace {
+
+// Token-order Q operand: element (b, i, h, :) at b * sb + i * sn + h * sh.
+dbs_status check_tok(const void* x, dbs_dtype dt, int64_t sb, int64_t sn, int64_t sh, const int32_t* perm,
+                     int perm_per_head) {
+  REQUIRE(x && perm, DBS_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(aligned16(x) && ((uintptr_t)perm & 3u) == 0, DBS_ERR_ALIGNMENT, "misaligned pointer");
+  REQUIRE(dt == DBS_BF16 || dt == DBS_FP32, DBS_ERR_INVALID_ARG, "bad dtype");
+  REQUIRE(perm_per_head == 0 || perm_per_head == 1, DBS_ERR_INVALID_ARG, "perm_per_head must be 0 or 1");
+  return check_strides(sb, sn, sh, dt);
+}
+
+dbs_status estimate_impl(const void* q_r, const void* k_r, int B, int Hh, int N, int Npad, int d, int b, int k,
+                         float scale, float* p_imp, void* workspace, size_t workspace_bytes,
+                         const dbs::TokIO& tok, hipStream_t stream) {
+  REQUIRE(k_r && p_imp && workspace, DBS_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(aligned16(k_r) && aligned16(p_imp) && aligned16(workspace), DBS_ERR_ALIGNMENT, "misaligned pointer");
   dbs_status st = check_geometry(B, Hh, N, Npad, d, b);
   if (st != DBS_OK) return st;
   REQUIRE(k >= 1 && k <= b, DBS_ERR_INVALID_ARG, "k=%d must be in [1, b=%d]", k, b);
@@ -206,8 +217,38 @@ dbs_status dbs_estimate_blocks(const void* q_r, const void* k_r, dbs_dtype dt, i
   dbs::EstimateArgs a{};
   a.q_r = q_r; a.k_r = k_r; a.p_imp = p_imp; a.workspace = workspace;
   a.B = B; a.Hh = Hh; a.N = N; a.Npad = Npad; a.d = d; a.b = b; a.k = k; a.nb = nb;
-  a.scale = scale; a.stream = stream;
+  a.scale = scale; a.tok = tok; a.stream = stream;
   return from_hip(dbs::launch_estimate(a), "dbs_estimate_blocks launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+dbs_status dbs_estimate_blocks(const void* q_r, const void* k_r, dbs_dtype dt, int B, int Hh, int N,
+                               int Npad, int d, int b, int k, float scale, float* p_imp,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  DBS_GUARD_BEGIN
+  REQUIRE(q_r, DBS_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(aligned16(q_r), DBS_ERR_ALIGNMENT, "misaligned pointer");
+  REQUIRE(dt == DBS_BF16, DBS_ERR_UNSUPPORTED, "estimate_blocks computes on bf16 inputs");
+  return estimate_impl(q_r, k_r, B, Hh, N, Npad, d, b, k, scale, p_imp, workspace, workspace_bytes, dbs::TokIO{},
+                       stream);
+  DBS_GUARD_END
+}
+
+dbs_status dbs_estimate_blocks_tok(const void* q, dbs_dtype q_dt, int64_t sb, int64_t sn, int64_t sh,
+                                   const int32_t* perm, int perm_per_head, const void* k_r, int B, int Hh,
+                                   int N, int Npad, int d, int b, int k, float scale, float* p_imp,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  DBS_GUARD_BEGIN
+  dbs_status st = check_tok(q, q_dt, sb, sn, sh, perm, perm_per_head);
+  if (st != DBS_OK) return st;
+  dbs::TokIO tok{};
+  tok.q = q; tok.q_f32 = q_dt == DBS_FP32; tok.qsb = sb; tok.qsn = sn; tok.qsh = sh;
+  tok.perm = perm; tok.perm_h_stride = perm_per_head ? N : 0;
+  return estimate_impl(nullptr, k_r, B, Hh, N, Npad, d, b, k, scale, p_imp, workspace, workspace_bytes, tok,
+                       stream);
   DBS_GUARD_END
 }
 
@@ -247,19 +288,19 @@ dbs_status dbs_meanpool_kv(const void* k_r, const void* v_r, dbs_dtype dt, int B
   DBS_GUARD_END
 }
 
-dbs_status dbs_sparse_attn_fwd(const void* q_r, const void* k_r, const void* v_r, dbs_dtype dt, int B,
-                               int Hh, int N, int Npad, int d, int b, float scale,
-                               const int32_t* kv_count, const int32_t* kv_idx, const int32_t* order,
-                               const void* k_g, const void* v_g, int Ng, int n_pool, void* o_r, float* lse,
-                               hipStream_t stream) {
-  DBS_GUARD_BEGIN
-  REQUIRE(q_r && k_r && v_r && kv_count && kv_idx && o_r, DBS_ERR_INVALID_ARG, "NULL pointer");
-  REQUIRE(aligned16(q_r) && aligned16(k_r) && aligned16(v_r) && aligned16(o_r), DBS_ERR_ALIGNMENT,
-          "misaligned pointer");
+}  // extern "C"
+
+namespace {
+
+dbs_status attn_impl(const void* q_r, const void* k_r, const void* v_r, int B, int Hh, int N, int Npad, int d,
+                     int b, float scale, const int32_t* kv_count, const int32_t* kv_idx, const int32_t* order,
+                     const void* k_g, const void* v_g, int Ng, int n_pool, void* o_r, float* lse,
+                     const dbs::TokIO& tok, hipStream_t stream) {
+  REQUIRE(k_r && v_r && kv_count && kv_idx, DBS_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(aligned16(k_r) && aligned16(v_r), DBS_ERR_ALIGNMENT, "misaligned pointer");
   REQUIRE(((uintptr_t)kv_count & 3u) == 0 && ((uintptr_t)kv_idx & 3u) == 0 && ((uintptr_t)lse & 3u) == 0 &&
               ((uintptr_t)order & 3u) == 0,
           DBS_ERR_ALIGNMENT, "misaligned pointer");
-  REQUIRE(dt == DBS_BF16, DBS_ERR_UNSUPPORTED, "sparse_attn_fwd computes on bf16 inputs");
   dbs_status st = check_geometry(B, Hh, N, Npad, d, b);
   if (st != DBS_OK) return st;
   REQUIRE(std::isfinite(scale), DBS_ERR_INVALID_ARG, "scale must be finite");
@@ -274,10 +315,48 @@ dbs_status dbs_sparse_attn_fwd(const void* q_r, const void* k_r, const void* v_r
   a.q_r = q_r; a.k_r = k_r; a.v_t = v_r; a.kv_count = kv_count; a.kv_idx = kv_idx; a.order = order;
   a.k_g = k_g; a.v_g = v_g; a.o_r = o_r; a.lse = lse;
   a.B = B; a.Hh = Hh; a.N = N; a.Npad = Npad; a.d = d; a.b = b; a.nb = Npad / b;
-  a.Ng = k_g ? Ng : 0; a.n_pool = k_g ? n_pool : 1; a.scale = scale; a.stream = stream;
+  a.Ng = k_g ? Ng : 0; a.n_pool = k_g ? n_pool : 1; a.scale = scale; a.tok = tok; a.stream = stream;
   REQUIRE(a.nb <= 4096, DBS_ERR_UNSUPPORTED, "nb=%d must be <= 4096", a.nb);
   REQUIRE((int64_t)B * Hh * a.nb <= INT32_MAX, DBS_ERR_INVALID_ARG, "too many query blocks");
   return from_hip(dbs::launch_attn_fwd(a), "dbs_sparse_attn_fwd launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+dbs_status dbs_sparse_attn_fwd(const void* q_r, const void* k_r, const void* v_r, dbs_dtype dt, int B,
+                               int Hh, int N, int Npad, int d, int b, float scale,
+                               const int32_t* kv_count, const int32_t* kv_idx, const int32_t* order,
+                               const void* k_g, const void* v_g, int Ng, int n_pool, void* o_r, float* lse,
+                               hipStream_t stream) {
+  DBS_GUARD_BEGIN
+  REQUIRE(q_r && o_r, DBS_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(aligned16(q_r) && aligned16(o_r), DBS_ERR_ALIGNMENT, "misaligned pointer");
+  REQUIRE(dt == DBS_BF16, DBS_ERR_UNSUPPORTED, "sparse_attn_fwd computes on bf16 inputs");
+  return attn_impl(q_r, k_r, v_r, B, Hh, N, Npad, d, b, scale, kv_count, kv_idx, order, k_g, v_g, Ng, n_pool,
+                   o_r, lse, dbs::TokIO{}, stream);
+  DBS_GUARD_END
+}
+
+dbs_status dbs_sparse_attn_fwd_tok(const void* q, dbs_dtype q_dt, int64_t qsb, int64_t qsn, int64_t qsh,
+                                   const int32_t* perm, int perm_per_head, const void* k_r, const void* v_r,
+                                   int B, int Hh, int N, int Npad, int d, int b, float scale,
+                                   const int32_t* kv_count, const int32_t* kv_idx, const int32_t* order,
+                                   const void* k_g, const void* v_g, int Ng, int n_pool, void* out,
+                                   dbs_dtype out_dt, int64_t osb, int64_t osn, int64_t osh, float* lse,
+                                   hipStream_t stream) {
+  DBS_GUARD_BEGIN
+  dbs_status st = check_tok(q, q_dt, qsb, qsn, qsh, perm, perm_per_head);
+  if (st != DBS_OK) return st;
+  st = check_tok(out, out_dt, osb, osn, osh, perm, perm_per_head);
+  if (st != DBS_OK) return st;
+  dbs::TokIO tok{};
+  tok.q = q; tok.q_f32 = q_dt == DBS_FP32; tok.qsb = qsb; tok.qsn = qsn; tok.qsh = qsh;
+  tok.out = out; tok.out_f32 = out_dt == DBS_FP32; tok.osb = osb; tok.osn = osn; tok.osh = osh;
+  tok.perm = perm; tok.perm_h_stride = perm_per_head ? N : 0;
+  return attn_impl(nullptr, k_r, v_r, B, Hh, N, Npad, d, b, scale, kv_count, kv_idx, order, k_g, v_g, Ng, n_pool,
+                   nullptr, lse, tok, stream);
   DBS_GUARD_END
 }
 

@@ -137,7 +137,7 @@ void attn_fwd_kernel(
     const int32_t* __restrict__ order,
     const __bf16* __restrict__ k_g, const __bf16* __restrict__ v_g,
     __bf16* __restrict__ o_r, float* __restrict__ lse,
-    int Hh, int N, int Npad, int nb, int Ng, float sl2, float bias_n, float bias_last, int total) {
+    int Hh, int N, int Npad, int nb, int Ng, float sl2, float bias_n, float bias_last, int total, TokIO tok) {
   using C = AttnCfg<D, BLK>;
   // Four distinct arrays whose roles are static in each half of the 2x-unrolled
   // pipeline, so the compiler can prove LDS reads never alias a DMA in flight
@@ -245,12 +245,39 @@ void attn_fwd_kernel(
     return *reinterpret_cast<const bf16x8_t*>(vb + vbase + dt * 32 * C::kVStride + st * 32);
   };
 
-  // Q^T operand: lane (l32, g) holds Q[q0 + l32][16 kk + 8 g .. +7].
+  // Q^T operand: lane (l32, g) holds Q[q0 + l32][16 kk + 8 g .. +7], from the
+  // reordered rows or, in token order, from the row's token (bf16, or float32
+  // rounded to bf16 as the reorder rounds it; rows >= N are zero).
+  const int bi = bh / Hh, hh = bh % Hh;
+  auto token_of = [&](int row) {
+    const int t = tok.perm[(int64_t)hh * tok.perm_h_stride + row];
+    return t < 0 ? 0 : (t >= N ? N - 1 : t);
+  };
   bf16x8_t qreg[D / 16];
-  {
+  if (tok.q == nullptr) {
     const __bf16* qp = q_r + (rowbase + q0 + l32) * D + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * kk);
+  } else if (q0 + l32 >= N) {
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = bf16x8_t{};
+  } else {
+    const int64_t off = bi * tok.qsb + (int64_t)token_of(q0 + l32) * tok.qsn + hh * tok.qsh + 8 * g;
+    if (tok.q_f32) {
+      const float* qp = reinterpret_cast<const float*>(tok.q) + off;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const float4 a = reinterpret_cast<const float4*>(qp + 16 * kk)[0];
+        const float4 c = reinterpret_cast<const float4*>(qp + 16 * kk)[1];
+        const uint4 w = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(c.x, c.y),
+                                   pack_bf16x2(c.z, c.w));
+        qreg[kk] = __builtin_bit_cast(bf16x8_t, w);
+      }
+    } else {
+      const __bf16* qp = reinterpret_cast<const __bf16*>(tok.q) + off;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * kk);
+    }
   }
 
   f32x16_t oacc[D / 32];
@@ -451,15 +478,36 @@ void attn_fwd_kernel(
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const int q = q0 + l32;
   if (q < N) {
-    __bf16* op = o_r + (rowbase + q) * D + 4 * g;
+    // lane (l32, g) holds channels 32 dt + 8 i + 4 g .. +3 of its query row
+    if (tok.out != nullptr && tok.out_f32) {
+      float* op = reinterpret_cast<float*>(tok.out) + bi * tok.osb + (int64_t)token_of(q) * tok.osn +
+                  hh * tok.osh + 4 * g;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
+      for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint2 w;
-        w.x = cvt_pk(oacc[dt][i * 4 + 0] * inv, oacc[dt][i * 4 + 1] * inv);
-        w.y = cvt_pk(oacc[dt][i * 4 + 2] * inv, oacc[dt][i * 4 + 3] * inv);
-        *reinterpret_cast<uint2*>(op + 32 * dt + 8 * i) = w;
+        for (int i = 0; i < 4; ++i) {
+          // the bf16 value of the output, widened exactly
+          const uint32_t lo = cvt_pk(oacc[dt][i * 4 + 0] * inv, oacc[dt][i * 4 + 1] * inv);
+          const uint32_t hi = cvt_pk(oacc[dt][i * 4 + 2] * inv, oacc[dt][i * 4 + 3] * inv);
+          *reinterpret_cast<float4*>(op + 32 * dt + 8 * i) =
+              make_float4(__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u),
+                          __uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u));
+        }
+      }
+    } else {
+      __bf16* op = tok.out != nullptr
+                       ? reinterpret_cast<__bf16*>(tok.out) + bi * tok.osb + (int64_t)token_of(q) * tok.osn +
+                             hh * tok.osh + 4 * g
+                       : o_r + (rowbase + q) * D + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint2 w;
+          w.x = cvt_pk(oacc[dt][i * 4 + 0] * inv, oacc[dt][i * 4 + 1] * inv);
+          w.y = cvt_pk(oacc[dt][i * 4 + 2] * inv, oacc[dt][i * 4 + 3] * inv);
+          *reinterpret_cast<uint2*>(op + 32 * dt + 8 * i) = w;
+        }
       }
     }
     if (lse != nullptr && g == 0) {
@@ -482,7 +530,7 @@ hipError_t launch(const AttnArgs& a) {
                      a.stream, (const __bf16*)a.q_r, (const __bf16*)a.k_r, (const __bf16*)a.v_t,
                      a.kv_count, a.kv_idx, a.order, (const __bf16*)a.k_g, (const __bf16*)a.v_g,
                      (__bf16*)a.o_r, a.lse, a.Hh, a.N, a.Npad, a.nb, a.Ng, sl2, bias_n, bias_last,
-                     total);
+                     total, a.tok);
   return hipGetLastError();
 }
 

@@ -76,11 +76,13 @@ __device__ __forceinline__ void wg_coords(const SampleGeom& sg, int& bh, int& sp
 }
 
 // Compact copies of the sampled rows: qs/ks [BH][nsp_pad][D], zero rows for
-// empty slots and padding.  One thread per 16-byte chunk.
+// empty slots and padding.  One thread per 16-byte chunk.  Q comes from the
+// reordered rows, or (tok.q set) from the token of the sampled row in token
+// order, float32 rounded to bf16 as the reorder rounds it.
 template <int D>
 __global__ __launch_bounds__(256) void est_gather_kernel(
     const __bf16* __restrict__ q_r, const __bf16* __restrict__ k_r, __bf16* __restrict__ qs,
-    __bf16* __restrict__ ks, SampleGeom sg, int Npad) {
+    __bf16* __restrict__ ks, SampleGeom sg, int Npad, int Hh, TokIO tok) {
   const int bh = blockIdx.y;
   const int idx = blockIdx.x * 256 + threadIdx.x;
   const int r = idx / (D / 8), c = idx % (D / 8);
@@ -89,8 +91,22 @@ __global__ __launch_bounds__(256) void est_gather_kernel(
   uint4 vq = make_uint4(0, 0, 0, 0), vk = vq;
   if (src >= 0) {
     const int64_t off = ((int64_t)bh * Npad + src) * D + 8 * c;
-    vq = *reinterpret_cast<const uint4*>(q_r + off);
     vk = *reinterpret_cast<const uint4*>(k_r + off);
+    if (tok.q == nullptr) {
+      vq = *reinterpret_cast<const uint4*>(q_r + off);
+    } else {
+      const int bi = bh / Hh, h = bh % Hh;
+      int t = tok.perm[(int64_t)h * tok.perm_h_stride + src];
+      t = t < 0 ? 0 : (t >= sg.N ? sg.N - 1 : t);
+      const int64_t qo = bi * tok.qsb + (int64_t)t * tok.qsn + h * tok.qsh + 8 * c;
+      if (tok.q_f32) {
+        const float4 a = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(tok.q) + qo)[0];
+        const float4 b = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(tok.q) + qo)[1];
+        vq = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w));
+      } else {
+        vq = *reinterpret_cast<const uint4*>(reinterpret_cast<const __bf16*>(tok.q) + qo);
+      }
+    }
   }
   const int64_t dst = ((int64_t)bh * sg.nsp_pad + r) * D + 8 * c;
   *reinterpret_cast<uint4*>(qs + dst) = vq;
@@ -423,7 +439,7 @@ hipError_t launch_d(const EstimateArgs& a) {
   float* tmax = reinterpret_cast<float*>(part + (int64_t)BH * sg.splits * sg.nsp);
 
   hipLaunchKernelGGL((est_gather_kernel<D>), dim3((sg.nsp_pad * (D / 8) + 255) / 256, BH), dim3(256), 0,
-                     a.stream, (const __bf16*)a.q_r, (const __bf16*)a.k_r, qs, ks, sg, a.Npad);
+                     a.stream, (const __bf16*)a.q_r, (const __bf16*)a.k_r, qs, ks, sg, a.Npad, a.Hh, a.tok);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid((unsigned)(((sg.nsp + kQPerWg - 1) / kQPerWg) * sg.splits * BH));

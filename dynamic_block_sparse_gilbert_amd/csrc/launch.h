@@ -29,6 +29,18 @@ struct MeanpoolArgs {
   hipStream_t stream;
 };
 
+// Token-order operands of the fused entry points: element (b, i, h, :) of a
+// [B, N, Hh, d] tensor at b * sb + perm_h[i] * sn + h * sh, perm_h = perm +
+// h * perm_h_stride (curve position i -> token).
+struct TokIO {
+  const void* q;        // nullable: Q read in token order instead of from q_r
+  void* out;            // nullable: output written in token order instead of to o_r
+  const int32_t* perm;
+  int64_t qsb, qsn, qsh, osb, osn, osh;   // element strides
+  int perm_h_stride;
+  int q_f32, out_f32;   // element types (float32 when set, else bf16)
+};
+
 struct EstimateArgs {
   const void* q_r;
   const void* k_r;
@@ -36,6 +48,7 @@ struct EstimateArgs {
   void* workspace;      // compact Q_s, K_s (bf16) and lse2 (float); see estimate_workspace_bytes
   int B, Hh, N, Npad, d, b, k, nb;
   float scale;
+  TokIO tok;            // tok.q set: sampled Q rows gathered in token order (out unused)
   hipStream_t stream;
 };
 
@@ -63,6 +76,7 @@ struct AttnArgs {
   float* lse;
   int B, Hh, N, Npad, d, b, nb, Ng, n_pool;
   float scale;
+  TokIO tok;            // zero: reordered Q in, reordered O out
   hipStream_t stream;
 };
 

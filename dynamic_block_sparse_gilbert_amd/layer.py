@@ -2,8 +2,13 @@
 
 Video-BLADE: "Preprocessing" (reorder), "Step 1" (estimate), "Step 2.1"
 (mask), "Step 2.2" (block-sparse attention, optional global tokens), then the
-output goes back to token order.  Buffers are allocated once per shape and
-reused; permutations are built on the host by the library and uploaded once.
+output goes back to token order.  K and V are reordered into the curve-order
+layouts the attention streams; Q is read in token order through the
+permutation by the estimator and the attention, which also writes the output
+straight to token order (dbs_estimate_blocks_tok, dbs_sparse_attn_fwd_tok),
+so neither Q nor the output makes an extra pass through HBM.  Buffers are
+allocated once per shape and reused; permutations are built on the host by
+the library and uploaded once.
 """
 from __future__ import annotations
 
@@ -74,10 +79,9 @@ class AsaLayer:
         s = spec
         B, Hh, Npad, d, nb = s.batch, s.heads, s.Npad, s.d, s.nb
         bf = dict(dtype=torch.bfloat16, device=self.device)
-        self.q_r = torch.empty((B, Hh, Npad, d), **bf)
         self.k_r = torch.empty((B, Hh, Npad, d), **bf)
         self.v_t = torch.empty((B, Hh, nb, d, s.b), **bf)
-        self.o_r = torch.empty((B, Hh, Npad, d), **bf)
+        self.q: Optional[torch.Tensor] = None   # the caller's Q, token order
         self.p_imp = torch.empty((B, Hh, nb, nb), dtype=torch.float32, device=self.device)
         self.ws = torch.empty(max(16, ops.estimate_workspace_bytes(B, Hh, s.N, d, s.b, s.k)),
                               dtype=torch.uint8, device=self.device)
@@ -93,9 +97,9 @@ class AsaLayer:
             self.v_g = torch.empty((B, Hh, Ngpad // s.b, d, s.b), **bf)
 
     def prepare(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> None:
-        """Reorder (and pool) the inputs; q, k, v are [B, N, Hh, d]."""
+        """Reorder (and pool) K and V and keep Q; q, k, v are [B, N, Hh, d]."""
         s = self.spec
-        ops.reorder(q, self.perm, s.Npad, s.b, "rows", y=self.q_r)
+        self.q = q
         ops.reorder(k, self.perm, s.Npad, s.b, "rows", y=self.k_r)
         ops.reorder(v, self.perm, s.Npad, s.b, "tiles_t", y=self.v_t)
         if s.n_pool:
@@ -103,15 +107,17 @@ class AsaLayer:
 
     def mask(self, tau: Optional[float] = None) -> None:
         s = self.spec
-        ops.estimate_blocks(self.q_r, self.k_r, s.N, s.b, s.k, s.scale, p_imp=self.p_imp, workspace=self.ws)
+        ops.estimate_blocks_tok(self.q, self.perm, self.k_r, s.N, s.b, s.k, s.scale, p_imp=self.p_imp,
+                                workspace=self.ws)
         ops.build_mask(self.p_imp, s.tau if tau is None else tau, kv_count=self.kv_count, kv_idx=self.kv_idx,
                        order=self.order)
 
     def attend(self, out: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16) -> torch.Tensor:
         s = self.spec
-        ops.sparse_attn_fwd(self.q_r, self.k_r, self.v_t, s.N, s.b, s.scale, self.kv_count, self.kv_idx,
-                            self.k_g, self.v_g, self.Ng, s.n_pool, o_r=self.o_r, order=self.order)
-        return ops.inverse_reorder(self.o_r, self.perm, s.N, out=out, out_dtype=out_dtype)
+        out, _ = ops.sparse_attn_fwd_tok(self.q, self.perm, self.k_r, self.v_t, s.N, s.b, s.scale, self.kv_count,
+                                         self.kv_idx, self.k_g, self.v_g, self.Ng, s.n_pool, out=out,
+                                         out_dtype=out_dtype, order=self.order)
+        return out
 
     def forward(self, q, k, v, out: Optional[torch.Tensor] = None, tau: Optional[float] = None,
                 out_dtype=torch.bfloat16) -> torch.Tensor:

@@ -119,6 +119,29 @@ def estimate_blocks(q_r: torch.Tensor, k_r: torch.Tensor, N: int, b: int, k: int
     return p_imp
 
 
+def estimate_blocks_tok(q: torch.Tensor, perm: torch.Tensor, k_r: torch.Tensor, N: int, b: int, k: int,
+                        scale: float, p_imp: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """q [B, N, Hh, d] in token order (any strides, d contiguous), k_r rows [B, Hh, Npad, d] ->
+    p_imp float32 [B, Hh, nb, nb]; equal to estimate_blocks on the reordered Q."""
+    _dev(q, perm, k_r, p_imp, workspace)
+    if q.stride(3) != 1:
+        raise ValueError("the d axis of q must be contiguous")
+    B, Hh, Npad, d = k_r.shape
+    nb = Npad // b
+    if p_imp is None:
+        p_imp = torch.empty((B, Hh, nb, nb), dtype=torch.float32, device=k_r.device)
+    need = estimate_workspace_bytes(B, Hh, N, d, b, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=k_r.device)
+    per_head = 1 if perm.dim() == 2 else 0
+    check("dbs_estimate_blocks_tok", lib().dbs_estimate_blocks_tok(
+        _p(q), _dt(q), q.stride(0), q.stride(1), q.stride(2), _p(perm), per_head, _p(k_r),
+        B, Hh, N, Npad, d, b, k, float(scale), _p(p_imp), _p(workspace),
+        workspace.numel() * workspace.element_size(), _stream()))
+    return p_imp
+
+
 def build_mask(p_imp: torch.Tensor, tau: float, kv_count: Optional[torch.Tensor] = None,
                kv_idx: Optional[torch.Tensor] = None, want_mask: bool = False,
                mask: Optional[torch.Tensor] = None, order: Optional[torch.Tensor] = None,
@@ -178,3 +201,30 @@ def sparse_attn_fwd(q_r: torch.Tensor, k_r: torch.Tensor, v_t: torch.Tensor, N: 
         _p(q_r), _p(k_r), _p(v_t), _dt(q_r), B, Hh, N, Npad, d, b, float(scale), _p(kv_count), _p(kv_idx),
         _p(order), _p(k_g), _p(v_g), int(Ng), int(n_pool), _p(o_r), _p(lse), _stream()))
     return o_r, lse
+
+
+def sparse_attn_fwd_tok(q: torch.Tensor, perm: torch.Tensor, k_r: torch.Tensor, v_t: torch.Tensor, N: int,
+                        b: int, scale: float, kv_count: torch.Tensor, kv_idx: torch.Tensor,
+                        k_g: Optional[torch.Tensor] = None, v_g: Optional[torch.Tensor] = None,
+                        Ng: int = 0, n_pool: int = 0, out: Optional[torch.Tensor] = None,
+                        out_dtype: torch.dtype = torch.bfloat16, lse: Optional[torch.Tensor] = None,
+                        want_lse: bool = False, order: Optional[torch.Tensor] = None):
+    """Q [B, N, Hh, d] in token order -> (out [B, N, Hh, d] in token order, lse [B, Hh, Npad] or None);
+    equal to inverse_reorder(sparse_attn_fwd(reordered Q)) bit for bit.  out may be a strided view."""
+    _dev(q, perm, k_r, v_t, kv_count, kv_idx, k_g, v_g, out, lse, order)
+    if q.stride(3) != 1:
+        raise ValueError("the d axis of q must be contiguous")
+    B, Hh, Npad, d = k_r.shape
+    if out is None:
+        out = torch.empty((B, N, Hh, d), dtype=out_dtype, device=k_r.device)
+    if out.stride(3) != 1:
+        raise ValueError("the d axis of out must be contiguous")
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hh, Npad), dtype=torch.float32, device=k_r.device)
+    per_head = 1 if perm.dim() == 2 else 0
+    check("dbs_sparse_attn_fwd_tok", lib().dbs_sparse_attn_fwd_tok(
+        _p(q), _dt(q), q.stride(0), q.stride(1), q.stride(2), _p(perm), per_head, _p(k_r), _p(v_t),
+        B, Hh, N, Npad, d, b, float(scale), _p(kv_count), _p(kv_idx), _p(order), _p(k_g), _p(v_g),
+        int(Ng), int(n_pool), _p(out), _dt(out), out.stride(0), out.stride(1), out.stride(2), _p(lse),
+        _stream()))
+    return out, lse

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DBS_ABI_VERSION 2
+#define DBS_ABI_VERSION 3
 
 typedef enum {
   DBS_OK = 0,
@@ -147,6 +147,19 @@ dbs_status dbs_estimate_blocks(const void* q_r, const void* k_r, dbs_dtype dt,
                                float* p_imp, void* workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
+/* dbs_estimate_blocks with Q in token order: the sampled Q rows are read as
+ * q[b, perm_h[i], h, :] (element strides sb, sn, sh; d contiguous; perm as
+ * for dbs_reorder, entries clamped into [0, N)) instead of from a reordered
+ * copy, so the layer need not reorder Q.  q_dt: DBS_BF16, or DBS_FP32 rounded
+ * to bf16 (round to nearest even) exactly as dbs_reorder rounds it; the
+ * result equals dbs_estimate_blocks on dbs_reorder's output bit for bit.
+ * k_r, workspace and the errors as for dbs_estimate_blocks. */
+dbs_status dbs_estimate_blocks_tok(const void* q, dbs_dtype q_dt, int64_t sb, int64_t sn, int64_t sh,
+                                   const int32_t* perm, int perm_per_head, const void* k_r,
+                                   int B, int Hh, int N, int Npad, int d, int b, int k, float scale,
+                                   float* p_imp, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
 /* Cumulative-threshold mask (Video-BLADE "Step 2.1").  For every row
  * (b, h, I): order the blocks by p_imp value descending, then index
  * ascending, and keep the fewest m >= 1 whose exact sum reaches
@@ -208,6 +221,25 @@ dbs_status dbs_sparse_attn_fwd(const void* q_r, const void* k_r, const void* v_r
                                const int32_t* kv_count, const int32_t* kv_idx, const int32_t* order,
                                const void* k_g, const void* v_g, int Ng, int n_pool,
                                void* o_r, float* lse, hipStream_t stream);
+
+/* dbs_sparse_attn_fwd with Q read and the output written in token order
+ * (Video-BLADE "Step 2.2" followed by the return to token order, as one
+ * launch): Q row i of head h is q[b, perm_h[i], h, :] and output row i is
+ * written to out[b, perm_h[i], h, :] for i < N (element strides qsb/qsn/qsh
+ * and osb/osn/osh, d contiguous, 16-byte aligned rows; perm as for
+ * dbs_reorder, entries clamped into [0, N), a permutation for a complete
+ * output).  q_dt: DBS_BF16, or DBS_FP32 rounded to bf16 as dbs_reorder
+ * rounds it; out_dt: DBS_BF16, or DBS_FP32 holding the bf16 result widened
+ * exactly.  The output equals dbs_inverse_reorder applied to
+ * dbs_sparse_attn_fwd's o_r bit for bit; lse stays in curve order
+ * ([B, Hh, Npad]).  Everything else as for dbs_sparse_attn_fwd. */
+dbs_status dbs_sparse_attn_fwd_tok(const void* q, dbs_dtype q_dt, int64_t qsb, int64_t qsn, int64_t qsh,
+                                   const int32_t* perm, int perm_per_head, const void* k_r, const void* v_r,
+                                   int B, int Hh, int N, int Npad, int d, int b, float scale,
+                                   const int32_t* kv_count, const int32_t* kv_idx, const int32_t* order,
+                                   const void* k_g, const void* v_g, int Ng, int n_pool,
+                                   void* out, dbs_dtype out_dt, int64_t osb, int64_t osn, int64_t osh,
+                                   float* lse, hipStream_t stream);
 
 #ifdef __cplusplus
 }

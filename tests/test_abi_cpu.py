@@ -37,7 +37,7 @@ def test_all_declared_symbols_exported(dbs):
     for n in names:
         assert hasattr(h, n), n
     assert set(names) == set(L.SIGNATURES), set(names) ^ set(L.SIGNATURES)
-    assert L.lib().dbs_abi_version() == 2
+    assert L.lib().dbs_abi_version() == 3
 
 
 @pytest.mark.parametrize("T,H,W", list(itertools.product(range(1, 7), repeat=3)))
@@ -147,6 +147,55 @@ def test_estimate_validation(dbs):
     assert call(p=MIS) == -3
     assert L.lib().dbs_estimate_workspace_bytes(0, 1, 1, 64, 1, 1) == 0
     assert L.lib().dbs_estimate_workspace_bytes(1, 1, 1, 96, 1, 1) == 0
+
+
+@cpu_only
+def test_estimate_tok_validation(dbs):
+    _, L = dbs
+    f = L.lib().dbs_estimate_blocks_tok
+    ws = L.lib().dbs_estimate_workspace_bytes(1, 2, 100, 128, 64, 8)
+    # q, q_dt, sb, sn, sh, perm, per_head, k_r, B, Hh, N, Npad, d, b, k, scale, p_imp, ws, ws_bytes, stream
+    ok = [A, 0, 100 * 2 * 128, 2 * 128, 128, A, 0, A, 1, 2, 100, 128, 128, 64, 8, 0.125, A, A, ws, None]
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return f(*a)
+    assert call(0, 0) == -1               # q NULL
+    assert call(5, 0) == -1               # perm NULL
+    assert call(0, A + 2) == -3           # misaligned q
+    assert call(5, A + 2) == -3           # misaligned perm
+    assert call(1, 7) == -1               # bad dtype
+    assert call(6, 2) == -1               # perm_per_head
+    assert call(3, 2 * 128 + 4) == -3     # row stride breaks 16-byte rows
+    assert call(3, -1) == -1
+    assert call(7, 0) == -1               # k_r NULL
+    assert call(14, 6) == -2              # k not a power of two
+    assert call(18, ws - 4) == -1         # small workspace
+
+
+@cpu_only
+def test_attn_tok_validation(dbs):
+    _, L = dbs
+    f = L.lib().dbs_sparse_attn_fwd_tok
+    # q, q_dt, qsb, qsn, qsh, perm, per_head, k_r, v_r, B, Hh, N, Npad, d, b, scale, kv_count, kv_idx, order,
+    # k_g, v_g, Ng, n_pool, out, out_dt, osb, osn, osh, lse, stream
+    ok = [A, 0, 1000 * 4 * 128, 4 * 128, 128, A, 1, A, A, 1, 4, 1000, 1024, 128, 128, 0.088, A, A, None,
+          None, None, 0, 0, A, 1, 1000 * 4 * 128, 4 * 128, 128, None, None]
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return f(*a)
+    assert call(0, 0) == -1               # q NULL
+    assert call(23, 0) == -1              # out NULL
+    assert call(5, 0) == -1               # perm NULL
+    assert call(23, A + 4) == -3          # misaligned out
+    assert call(24, 9) == -1              # bad out dtype
+    assert call(26, 4 * 128 + 2) == -3    # out row stride
+    assert call(16, 0) == -1              # kv_count NULL
+    assert call(13, 80) == -2             # head dim
+    assert call(19, A) == -1              # k_g without v_g
+    a = list(ok); a[11] = 4097 * 64 - 10; a[12] = 4097 * 64; a[14] = 64
+    assert f(*a) == -2                    # nb > 4096
 
 
 @cpu_only

@@ -205,3 +205,44 @@ def test_attn_work_order_does_not_change_results(N, d, b):
         outs.append((host(o_r)[:, :, :N].view(np.uint16), host(lse)[:, :, :N]))
     for o_, l_ in outs[1:]:
         assert np.array_equal(o_, outs[0][0]) and np.array_equal(l_, outs[0][1])
+
+
+@pytest.mark.parametrize("N,d,b,n,per_head,in32,out32", [
+    (1000, 128, 128, 0, False, False, False), (700, 64, 128, 8, True, False, True),
+    (2048, 64, 64, 0, True, True, False), (1500, 128, 64, 16, False, True, True),
+])
+def test_attn_token_order_equals_reorder_then_inverse(N, d, b, n, per_head, in32, out32):
+    """sparse_attn_fwd_tok (Q read and the output written in token order
+    through the permutation) is bit-identical to reorder -> sparse_attn_fwd ->
+    inverse_reorder, for bf16 / float32 operands, shared and per-head
+    permutations, with and without global tokens, into a strided output."""
+    say("attn tok", N, d, b, n, per_head, in32, out32)
+    B, Hh = 2, 3
+    rng = np.random.default_rng(N + d + n)
+    q, k, v = smooth_qkv(N + 5, B, N, Hh, d)
+    nb = -(-N // b)
+    Npad = nb * b
+    cnt, idx = _upload(_lists("random", B * Hh, nb, rng), B, Hh, nb)
+    ops = _ops()
+    pm = (np.stack([rng.permutation(N) for _ in range(Hh)]) if per_head else rng.permutation(N)).astype(np.int32)
+    perm = dev(pm)
+    qd = dev(q) if in32 else dev_bf16(q)
+    q_r = ops.reorder(qd, perm, Npad, b, "rows")
+    k_r = ops.reorder(dev_bf16(k), perm, Npad, b, "rows")
+    v_t = ops.reorder(dev_bf16(v), perm, Npad, b, "tiles_t")
+    kg = vg = None
+    Ng = 0
+    if n:
+        kg, vg, Ng = ops.meanpool_kv(k_r, v_t, N, b, n)
+    scale = 1.0 / math.sqrt(d)
+    odt = torch.float32 if out32 else torch.bfloat16
+    o_r, lse_a = ops.sparse_attn_fwd(q_r, k_r, v_t, N, b, scale, dev(cnt), dev(idx), kg, vg, Ng, n, want_lse=True)
+    ref = ops.inverse_reorder(o_r, perm, N, out_dtype=odt)
+    # a strided destination: every other head slot of a wider buffer
+    wide = torch.full((B, N, 2 * Hh, d), 7.0, dtype=odt, device=ref.device)
+    out, lse_b = ops.sparse_attn_fwd_tok(qd, perm, k_r, v_t, N, b, scale, dev(cnt), dev(idx), kg, vg, Ng, n,
+                                         out=wide[:, :, ::2], out_dtype=odt, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    assert torch.equal(wide[:, :, 1::2], torch.full_like(wide[:, :, 1::2], 7.0))   # untouched
+    assert np.array_equal(host(lse_a)[:, :, :N], host(lse_b)[:, :, :N])

@@ -95,3 +95,26 @@ def test_estimate_deterministic():
     a = host(ops.estimate_blocks(q_r, k_r, N, b, k, 0.088))
     c = host(ops.estimate_blocks(q_r, k_r, N, b, k, 0.088))
     assert np.array_equal(a, c)
+
+
+@pytest.mark.parametrize("N,b,k,d,per_head,in32", [
+    (1000, 128, 16, 128, False, False), (777, 64, 8, 64, True, False), (520, 128, 32, 128, True, True),
+    (300, 64, 1, 64, False, True),
+])
+def test_estimate_token_order_equals_reorder(N, b, k, d, per_head, in32):
+    """estimate_blocks_tok (sampled Q rows gathered in token order) is
+    bit-identical to estimate_blocks on the reordered Q."""
+    say("estimate tok", N, b, k, d, per_head, in32)
+    B, Hh = 2, 3
+    rng = np.random.default_rng(N + k)
+    q, kk, _ = smooth_qkv(N + 3, B, N, Hh, d)
+    ops = _ops()
+    Npad = -(-N // b) * b
+    pm = (np.stack([rng.permutation(N) for _ in range(Hh)]) if per_head else rng.permutation(N)).astype(np.int32)
+    perm = dev(pm)
+    qd = dev(q) if in32 else dev_bf16(q)
+    q_r = ops.reorder(qd, perm, Npad, b, "rows")
+    k_r = ops.reorder(dev_bf16(kk), perm, Npad, b, "rows")
+    a = host(ops.estimate_blocks(q_r, k_r, N, b, k, 1.0 / np.sqrt(d)))
+    c = host(ops.estimate_blocks_tok(qd, perm, k_r, N, b, k, 1.0 / np.sqrt(d)))
+    assert np.array_equal(a, c)
