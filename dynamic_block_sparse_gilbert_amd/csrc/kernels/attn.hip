@@ -245,41 +245,7 @@ void attn_fwd_kernel(
     return *reinterpret_cast<const bf16x8_t*>(vb + vbase + dt * 32 * C::kVStride + st * 32);
   };
 
-  // Q^T operand: lane (l32, g) holds Q[q0 + l32][16 kk + 8 g .. +7], from the
-  // reordered rows or, in token order, from the row's token (bf16, or float32
-  // rounded to bf16 as the reorder rounds it; rows >= N are zero).
-  const int bi = bh / Hh, hh = bh % Hh;
-  auto token_of = [&](int row) {
-    const int t = tok.perm[(int64_t)hh * tok.perm_h_stride + row];
-    return t < 0 ? 0 : (t >= N ? N - 1 : t);
-  };
-  bf16x8_t qreg[D / 16];
-  if (tok.q == nullptr) {
-    const __bf16* qp = q_r + (rowbase + q0 + l32) * D + 8 * g;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * kk);
-  } else if (q0 + l32 >= N) {
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = bf16x8_t{};
-  } else {
-    const int64_t off = bi * tok.qsb + (int64_t)token_of(q0 + l32) * tok.qsn + hh * tok.qsh + 8 * g;
-    if (tok.q_f32) {
-      const float* qp = reinterpret_cast<const float*>(tok.q) + off;
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const float4 a = reinterpret_cast<const float4*>(qp + 16 * kk)[0];
-        const float4 c = reinterpret_cast<const float4*>(qp + 16 * kk)[1];
-        const uint4 w = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(c.x, c.y),
-                                   pack_bf16x2(c.z, c.w));
-        qreg[kk] = __builtin_bit_cast(bf16x8_t, w);
-      }
-    } else {
-      const __bf16* qp = reinterpret_cast<const __bf16*>(tok.q) + off;
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * kk);
-    }
-  }
-
+  bf16x8_t qreg[D / 16];   // Q^T operand, loaded once the kept-block list is in LDS
   f32x16_t oacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16_t{};
@@ -447,7 +413,46 @@ void attn_fwd_kernel(
       if (!ok || J * BLK + (h + 1) * C::kKT > N) w |= kPartial << h;
     idx_s[t] = (uint16_t)w;
   }
-  __syncthreads();
+  // The list is in LDS: wait for the LDS writes only (a full __syncthreads
+  // would also wait for the Q loads below, which overlap the first copies).
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  // Q^T operand: lane (l32, g) holds Q[q0 + l32][16 kk + 8 g .. +7], from the
+  // reordered rows or, in token order, from the row's token (bf16, or float32
+  // rounded to bf16 as the reorder rounds it; rows >= N are zero).
+  const int bi = bh / Hh, hh = bh % Hh;
+  auto token_of = [&](int row) {
+    const int t = tok.perm[(int64_t)hh * tok.perm_h_stride + row];
+    return t < 0 ? 0 : (t >= N ? N - 1 : t);
+  };
+  // token of this lane's query row (used again by the epilogue)
+  const int qtok = (tok.perm != nullptr && q0 + l32 < N) ? token_of(q0 + l32) : 0;
+  if (tok.q == nullptr) {
+    const __bf16* qp = q_r + (rowbase + q0 + l32) * D + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * kk);
+  } else if (q0 + l32 >= N) {
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = bf16x8_t{};
+  } else {
+    const int64_t off = bi * tok.qsb + (int64_t)qtok * tok.qsn + hh * tok.qsh + 8 * g;
+    if (tok.q_f32) {
+      const float* qp = reinterpret_cast<const float*>(tok.q) + off;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const float4 a = reinterpret_cast<const float4*>(qp + 16 * kk)[0];
+        const float4 c = reinterpret_cast<const float4*>(qp + 16 * kk)[1];
+        const uint4 w = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(c.x, c.y),
+                                   pack_bf16x2(c.z, c.w));
+        qreg[kk] = __builtin_bit_cast(bf16x8_t, w);
+      }
+    } else {
+      const __bf16* qp = reinterpret_cast<const __bf16*>(tok.q) + off;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * kk);
+    }
+  }
+
   if (U > 0) {
     const StageDesc s0 = stage(0);
     StageDesc sd = stage(min(1, U - 1));
@@ -480,7 +485,7 @@ void attn_fwd_kernel(
   if (q < N) {
     // lane (l32, g) holds channels 32 dt + 8 i + 4 g .. +3 of its query row
     if (tok.out != nullptr && tok.out_f32) {
-      float* op = reinterpret_cast<float*>(tok.out) + bi * tok.osb + (int64_t)token_of(q) * tok.osn +
+      float* op = reinterpret_cast<float*>(tok.out) + bi * tok.osb + (int64_t)qtok * tok.osn +
                   hh * tok.osh + 4 * g;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
@@ -496,7 +501,7 @@ void attn_fwd_kernel(
       }
     } else {
       __bf16* op = tok.out != nullptr
-                       ? reinterpret_cast<__bf16*>(tok.out) + bi * tok.osb + (int64_t)token_of(q) * tok.osn +
+                       ? reinterpret_cast<__bf16*>(tok.out) + bi * tok.osb + (int64_t)qtok * tok.osn +
                              hh * tok.osh + 4 * g
                        : o_r + (rowbase + q) * D + 4 * g;
 #pragma unroll
