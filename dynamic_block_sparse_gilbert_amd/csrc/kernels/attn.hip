@@ -184,11 +184,20 @@ void attn_fwd_kernel(
   // MFMA phases.  The list word carries the block index and the masking
   // flags, so a full stage costs a handful of scalar operations.
   const int cnt_m1 = cnt > 0 ? cnt - 1 : 0;
-  auto stage = [&](int u) -> StageDesc {
+  // List word of kept-block index J (see kIndexMask).
+  auto word_of = [&](int J) {
+    const bool ok = J >= 0 && J < nb;
+    int w = ok ? J : kInvalidBit;
+#pragma unroll
+    for (int h = 0; h < C::kSubs; ++h)
+      if (!ok || J * BLK + (h + 1) * C::kKT > N) w |= kPartial << h;
+    return w;
+  };
+  // Stage u from the list word w of its block (ignored for global tiles).
+  auto stage_w = [&](int u, int w) -> StageDesc {
     StageDesc s;
     const int j = (int)((unsigned)u / C::kSubs), h = (int)((unsigned)u % C::kSubs);
     const bool kept = j < cnt;
-    const int w = __builtin_amdgcn_readfirstlane((int)idx_s[min(j, cnt_m1)]);
     const int Jx = kept ? (w & kIndexMask) : j - cnt;
     s.key0 = Jx * BLK + h * C::kKT;
     s.koffs = (uint32_t)s.key0 * (uint32_t)(D * 2);
@@ -197,6 +206,10 @@ void attn_fwd_kernel(
     s.kind = kept ? ((w >> h) & kPartial ? 1 : 0) : 2;
     s.limit = kept ? ((w & kInvalidBit) ? -1 : N) : Ng;
     return s;
+  };
+  auto stage = [&](int u) -> StageDesc {
+    const int j = (int)((unsigned)u / C::kSubs);
+    return stage_w(u, __builtin_amdgcn_readfirstlane((int)idx_s[min(j, cnt_m1)]));
   };
 
   // Per-lane source offsets (elements) of the padded DMA: loop invariant.
@@ -404,18 +417,11 @@ void attn_fwd_kernel(
     phase_b(vsrc, P, unused, nullptr, nullptr, std::false_type{});
   };
 
-  for (int t = threadIdx.x; t < cnt; t += C::kThreads) {
-    const int J = idx[t];
-    const bool ok = J >= 0 && J < nb;
-    int w = ok ? J : kInvalidBit;
-#pragma unroll
-    for (int h = 0; h < C::kSubs; ++h)
-      if (!ok || J * BLK + (h + 1) * C::kKT > N) w |= kPartial << h;
-    idx_s[t] = (uint16_t)w;
-  }
-  // The list is in LDS: wait for the LDS writes only (a full __syncthreads
-  // would also wait for the Q loads below, which overlap the first copies).
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // Prologue order matters because vector loads retire in order: this
+  // thread's list entry first, then the token lookup, then the first copies;
+  // the list word is then stored without waiting for the copies, and the Q
+  // gather waits for the token lookup only.
+  const int jt = threadIdx.x < cnt ? idx[threadIdx.x] : 0;
 
   // Q^T operand: lane (l32, g) holds Q[q0 + l32][16 kk + 8 g .. +7], from the
   // reordered rows or, in token order, from the row's token (bf16, or float32
@@ -427,6 +433,27 @@ void attn_fwd_kernel(
   };
   // token of this lane's query row (used again by the epilogue)
   const int qtok = (tok.perm != nullptr && q0 + l32 < N) ? token_of(q0 + l32) : 0;
+
+  // The first two stages need list entries 0 and 1 only: their words come
+  // straight from global memory, so the first copies start before the list
+  // reaches LDS.
+  StageDesc s0{}, sd{};
+  if (U > 0) {
+    const int w0 = word_of(__builtin_amdgcn_readfirstlane(idx[0]));
+    const int w1 = word_of(__builtin_amdgcn_readfirstlane(idx[min(1, cnt_m1)]));
+    const int u1 = min(1, U - 1);
+    s0 = stage_w(0, w0);
+    sd = stage_w(u1, u1 / C::kSubs == 0 ? w0 : w1);
+    dma_k(s0, Kb0);
+    dma_v(s0, Vb0);
+    dma_k(sd, Kb1);
+  }
+  if (threadIdx.x < cnt) idx_s[threadIdx.x] = (uint16_t)word_of(jt);
+  for (int t = threadIdx.x + C::kThreads; t < cnt; t += C::kThreads) idx_s[t] = (uint16_t)word_of(idx[t]);
+  // The list is in LDS: wait for the LDS writes only (a full __syncthreads
+  // would also wait for the copies above and the Q loads below).
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
   if (tok.q == nullptr) {
     const __bf16* qp = q_r + (rowbase + q0 + l32) * D + 8 * g;
 #pragma unroll
@@ -454,11 +481,6 @@ void attn_fwd_kernel(
   }
 
   if (U > 0) {
-    const StageDesc s0 = stage(0);
-    StageDesc sd = stage(min(1, U - 1));
-    dma_k(s0, Kb0);
-    dma_v(s0, Vb0);
-    dma_k(sd, Kb1);
     wait_dma();
     __syncthreads();
     f32x16_t SA[2], SB[2];
