@@ -33,6 +33,7 @@ SIGNATURES = {
     "dbs_perm_cuboid": (_i, [_i, _i, _i, _i, _i, _i, _i, _vp]),
     "dbs_perm_invert": (_i, [_vp, _i, _vp]),
     "dbs_reorder": (_i, [_vp, _i, _i64, _i64, _i64, _vp, _i, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
+    "dbs_reorder_kv": (_i, [_vp, _vp, _i, _i64, _i64, _i64, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "dbs_inverse_reorder": (_i, [_vp, _i, _vp, _i, _i64, _i64, _i64, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "dbs_estimate_workspace_bytes": (C.c_size_t, [_i, _i, _i, _i, _i, _i]),
     "dbs_estimate_blocks": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, C.c_size_t, _vp]),

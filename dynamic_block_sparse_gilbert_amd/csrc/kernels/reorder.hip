@@ -131,6 +131,71 @@ __global__ __launch_bounds__((D / 8) * (BLK / 8)) void reorder_tiles_t_kernel(
   }
 }
 
+// K and V of one (tile J, head h, batch b) in one workgroup of 2 * (D/8) *
+// (BLK/8) threads: the first half gathers V into the tiles-transposed layout
+// exactly as reorder_tiles_t_kernel does, the second half gathers the tile's
+// BLK rows of K into the rows layout, 8 independent 16-byte chunks per thread
+// (rows tg, tg + BLK/8, ... of the tile, channel chunk c).  Both halves share
+// the permutation and run the same number of chunks, so a launch over all tiles
+// is a whole number of occupancy rounds where the two separate launches were not.
+template <typename Tin, int D, int BLK>
+__global__ __launch_bounds__(2 * (D / 8) * (BLK / 8)) void reorder_kv_kernel(
+    const Tin* __restrict__ k, const Tin* __restrict__ v, int64_t sb, int64_t sn, int64_t sh,
+    __bf16* __restrict__ k_r, __bf16* __restrict__ v_t, const int32_t* __restrict__ perm,
+    int perm_h_stride, int Hh, int N, int nb) {
+  constexpr int kHalf = (D / 8) * (BLK / 8);
+  const int J = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
+  const int t = threadIdx.x % kHalf;
+  const int c = t % (D / 8);   // channel chunk: channels 8c..8c+7
+  const int tg = t / (D / 8);  // token group
+  const int32_t* ph = perm + (int64_t)h * perm_h_stride;
+  const int64_t bh = (int64_t)bi * Hh + h;
+  uint32_t w[8][4];
+  if (threadIdx.x < kHalf) {   // wave-uniform: kHalf is a multiple of 64
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = J * BLK + tile_col(8 * tg + e);
+      uint4 o = make_uint4(0, 0, 0, 0);
+      if (i < N) {
+        Vec8<Tin> x;
+        x.load(v + bi * sb + (int64_t)clamp_tok(ph[i], N) * sn + (int64_t)h * sh + 8 * c);
+        x.to_bf16(o);
+      }
+      w[e][0] = o.x; w[e][1] = o.y; w[e][2] = o.z; w[e][3] = o.w;
+    }
+    __bf16* tile = v_t + (bh * nb + J) * (int64_t)(D * BLK);
+#pragma unroll
+    for (int ch = 0; ch < 8; ++ch) {
+      uint32_t o[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t lo = w[2 * p][ch >> 1], hi = w[2 * p + 1][ch >> 1];
+        o[p] = (ch & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+      }
+      *reinterpret_cast<uint4*>(tile + (int64_t)(8 * c + ch) * BLK + 8 * tg) =
+          make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = J * BLK + tg + e * (BLK / 8);
+      uint4 o = make_uint4(0, 0, 0, 0);
+      if (i < N) {
+        Vec8<Tin> x;
+        x.load(k + bi * sb + (int64_t)clamp_tok(ph[i], N) * sn + (int64_t)h * sh + 8 * c);
+        x.to_bf16(o);
+      }
+      w[e][0] = o.x; w[e][1] = o.y; w[e][2] = o.z; w[e][3] = o.w;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = J * BLK + tg + e * (BLK / 8);
+      *reinterpret_cast<uint4*>(k_r + (bh * nb * BLK + i) * D + 8 * c) =
+          make_uint4(w[e][0], w[e][1], w[e][2], w[e][3]);
+    }
+  }
+}
+
 // x[b, perm[i], h, :] = y[b, h, i, :] for i < N (y rows layout, bf16).
 template <typename Tout, int D>
 __global__ __launch_bounds__(kThreads) void inverse_rows_kernel(
@@ -237,6 +302,20 @@ hipError_t launch_tiles(const ReorderArgs& a) {
   return hipGetLastError();
 }
 
+template <typename Tin, int D, int BLK>
+hipError_t launch_kv(const ReorderArgs& a) {
+  dim3 grid(a.Npad / BLK, a.Hh, a.B);
+  hipLaunchKernelGGL((reorder_kv_kernel<Tin, D, BLK>), grid, dim3(2 * (D / 8) * (BLK / 8)), 0,
+                     a.stream, (const Tin*)a.x, (const Tin*)a.x2, a.sb, a.sn, a.sh, (__bf16*)a.y,
+                     (__bf16*)a.y2, a.perm, a.perm_h_stride, a.Hh, a.N, a.Npad / BLK);
+  return hipGetLastError();
+}
+
+template <typename Tin, int D>
+hipError_t dispatch_kv_b(const ReorderArgs& a) {
+  return a.b == 64 ? launch_kv<Tin, D, 64>(a) : launch_kv<Tin, D, 128>(a);
+}
+
 template <typename Tin, int D>
 hipError_t dispatch_tiles_b(const ReorderArgs& a) {
   return a.b == 64 ? launch_tiles<Tin, D, 64>(a) : launch_tiles<Tin, D, 128>(a);
@@ -287,6 +366,11 @@ hipError_t launch_meanpool(const MeanpoolArgs& a) {
 
 hipError_t launch_reorder(const ReorderArgs& a) {
   return a.d == 64 ? dispatch_reorder_d<64>(a) : dispatch_reorder_d<128>(a);
+}
+
+hipError_t launch_reorder_kv(const ReorderArgs& a) {
+  if (a.d == 64) return a.x_f32 ? dispatch_kv_b<float, 64>(a) : dispatch_kv_b<__bf16, 64>(a);
+  return a.x_f32 ? dispatch_kv_b<float, 128>(a) : dispatch_kv_b<__bf16, 128>(a);
 }
 
 hipError_t launch_inverse_reorder(const ReorderArgs& a) {

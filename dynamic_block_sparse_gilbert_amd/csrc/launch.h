@@ -12,6 +12,8 @@ struct ReorderArgs {
   const void* x;        // reorder: source [B, N, Hh, d] strided
   void* y;              // reorder: destination; inverse: source (rows)
   void* x_out;          // inverse: destination [B, N, Hh, d] strided
+  const void* x2;       // reorder_kv: V source (same strides as x, which is K)
+  void* y2;             // reorder_kv: V destination (tiles-transposed); y is K (rows)
   int64_t sb, sn, sh;
   const int32_t* perm;
   int perm_h_stride;    // 0 (shared) or N (per head)
@@ -81,6 +83,7 @@ struct AttnArgs {
 };
 
 hipError_t launch_reorder(const ReorderArgs& a);
+hipError_t launch_reorder_kv(const ReorderArgs& a);
 hipError_t launch_inverse_reorder(const ReorderArgs& a);
 hipError_t launch_meanpool(const MeanpoolArgs& a);
 hipError_t launch_estimate(const EstimateArgs& a);

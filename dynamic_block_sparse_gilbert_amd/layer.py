@@ -100,8 +100,7 @@ class AsaLayer:
         """Reorder (and pool) K and V and keep Q; q, k, v are [B, N, Hh, d]."""
         s = self.spec
         self.q = q
-        ops.reorder(k, self.perm, s.Npad, s.b, "rows", y=self.k_r)
-        ops.reorder(v, self.perm, s.Npad, s.b, "tiles_t", y=self.v_t)
+        ops.reorder_kv(k, v, self.perm, s.Npad, s.b, k_r=self.k_r, v_t=self.v_t)
         if s.n_pool:
             ops.meanpool_kv(self.k_r, self.v_t, s.N, s.b, s.n_pool, k_g=self.k_g, v_g=self.v_g)
 

@@ -81,6 +81,31 @@ def reorder(x: torch.Tensor, perm: torch.Tensor, Npad: int, b: int, layout: str 
     return y
 
 
+def reorder_kv(k: torch.Tensor, v: torch.Tensor, perm: torch.Tensor, Npad: int, b: int,
+               k_r: Optional[torch.Tensor] = None, v_t: Optional[torch.Tensor] = None):
+    """k, v [B, N, Hh, d] (same strides, d contiguous) -> k_r rows [B, Hh, Npad, d] and v_t tiles
+    [B, Hh, Npad/b, d, b], both bf16, in one launch."""
+    _dev(k, v, perm, k_r, v_t)
+    B, N, Hh, d = k.shape
+    if v.shape != k.shape or v.stride() != k.stride() or v.dtype != k.dtype:
+        raise ValueError("k and v must have the same shape, strides and dtype")
+    if k.stride(3) != 1:
+        raise ValueError("the d axis of k and v must be contiguous")
+    if k_r is None:
+        k_r = torch.empty((B, Hh, Npad, d), dtype=torch.bfloat16, device=k.device)
+    if v_t is None:
+        v_t = torch.empty((B, Hh, Npad // b, d, b), dtype=torch.bfloat16, device=k.device)
+    if k_r.shape != (B, Hh, Npad, d) or v_t.shape != (B, Hh, Npad // b, d, b):
+        raise ValueError("k_r / v_t have the wrong shape")
+    if k_r.dtype != torch.bfloat16 or v_t.dtype != torch.bfloat16 or not (k_r.is_contiguous() and v_t.is_contiguous()):
+        raise ValueError("k_r and v_t must be contiguous bf16")
+    per_head = 1 if perm.dim() == 2 else 0
+    check("dbs_reorder_kv", lib().dbs_reorder_kv(
+        _p(k), _p(v), _dt(k), k.stride(0), k.stride(1), k.stride(2), _p(k_r), _p(v_t), _p(perm), per_head,
+        B, Hh, N, Npad, d, b, _stream()))
+    return k_r, v_t
+
+
 def inverse_reorder(y: torch.Tensor, perm: torch.Tensor, N: int,
                     out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
     """y rows [B, Hh, Npad, d] bf16 -> out [B, N, Hh, d] (out may be a strided view)."""

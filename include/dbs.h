@@ -1,6 +1,6 @@
 /*
  * dbs.h -- content-adaptive block-sparse attention (ASA / ASA_G), forward pass,
- *          for AMD Instinct MI355X (gfx950).  C ABI, version 1.
+ *          for AMD Instinct MI355X (gfx950).  C ABI (version: DBS_ABI_VERSION).
  *
  * The method: Video-BLADE ("Preprocessing", "Step 1", "Step 2.1", "Step 2.2")
  * and the BLADE notes (key designs 1 and 2).  A layer runs, on one stream:
@@ -11,6 +11,14 @@
  *   dbs_build_mask                                     cumulative-threshold mask
  *   dbs_sparse_attn_fwd                                attention over kept tiles
  *   dbs_inverse_reorder(O)                             back to token order
+ *
+ * or, with the same results, in fewer launches and without the Q and O copies:
+ *
+ *   dbs_reorder_kv(K, V)                               K, V -> curve order
+ *   [dbs_meanpool_kv]
+ *   dbs_estimate_blocks_tok                            Q read in token order
+ *   dbs_build_mask
+ *   dbs_sparse_attn_fwd_tok                            Q read, O written in token order
  *
  * Conventions for every call:
  * - Device pointers are allocated and owned by the caller and must be 16-byte
@@ -45,7 +53,7 @@
 extern "C" {
 #endif
 
-#define DBS_ABI_VERSION 3
+#define DBS_ABI_VERSION 4
 
 typedef enum {
   DBS_OK = 0,
@@ -111,6 +119,19 @@ dbs_status dbs_reorder(const void* x, dbs_dtype x_dt, int64_t sb, int64_t sn, in
                        void* y, dbs_dtype y_dt, dbs_layout y_layout,
                        const int32_t* perm, int perm_per_head,
                        int B, int Hh, int N, int Npad, int d, int b, hipStream_t stream);
+
+/* K and V reordered together (Video-BLADE "Preprocessing"), in one launch:
+ *   k_r = dbs_reorder(k, rows layout, bf16), v_t = dbs_reorder(v, tiles
+ *   layout, bf16), bit for bit.
+ * k, v: element type x_dt (DBS_BF16 or DBS_FP32, rounded to bf16 to nearest
+ *    even), [B, N, Hh, d] with the same element strides (sb, sn, sh).
+ * k_r: device bf16 [B, Hh, Npad, d]; v_t: device bf16 [B, Hh, Npad/b, d, b];
+ *    rows and columns N..Npad-1 are zero.
+ * perm, sizes and limits as for dbs_reorder. */
+dbs_status dbs_reorder_kv(const void* k, const void* v, dbs_dtype x_dt,
+                          int64_t sb, int64_t sn, int64_t sh,
+                          void* k_r, void* v_t, const int32_t* perm, int perm_per_head,
+                          int B, int Hh, int N, int Npad, int d, int b, hipStream_t stream);
 
 /* Inverse of dbs_reorder for the attention output:
  *   x[b, perm_h[i], h, :] = y[b, h, i, :]  for i < N.

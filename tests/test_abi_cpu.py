@@ -37,7 +37,7 @@ def test_all_declared_symbols_exported(dbs):
     for n in names:
         assert hasattr(h, n), n
     assert set(names) == set(L.SIGNATURES), set(names) ^ set(L.SIGNATURES)
-    assert L.lib().dbs_abi_version() == 3
+    assert L.lib().dbs_abi_version() == 4
 
 
 @pytest.mark.parametrize("T,H,W", list(itertools.product(range(1, 7), repeat=3)))
@@ -196,6 +196,27 @@ def test_attn_tok_validation(dbs):
     assert call(19, A) == -1              # k_g without v_g
     a = list(ok); a[11] = 4097 * 64 - 10; a[12] = 4097 * 64; a[14] = 64
     assert f(*a) == -2                    # nb > 4096
+
+
+@cpu_only
+def test_reorder_kv_validation(dbs):
+    _, L = dbs
+    f = L.lib().dbs_reorder_kv
+    # k, v, x_dt, sb, sn, sh, k_r, v_t, perm, per_head, B, Hh, N, Npad, d, b, stream
+    ok = [A, A, 1, 1000 * 4 * 128, 4 * 128, 128, A, A, A, 0, 1, 4, 1000, 1024, 128, 128, None]
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return f(*a)
+    assert call(0, 0) == -1               # k NULL
+    assert call(1, 0) == -1               # v NULL
+    assert call(7, 0) == -1               # v_t NULL
+    assert call(6, A + 8) == -3           # misaligned k_r
+    assert call(2, 7) == -1               # bad dtype
+    assert call(4, 4 * 128 + 2) == -3     # token stride breaks 16-byte chunks
+    assert call(14, 96) == -2             # head dim
+    assert call(13, 1000) == -1           # Npad not a multiple of b
+    assert call(9, 2) == -1               # perm_per_head
 
 
 @cpu_only

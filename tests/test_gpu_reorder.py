@@ -54,6 +54,15 @@ def test_reorder_rows_and_tiles(case):
     ref = bf16_round(o_reorder(x, perm, Npad))
     assert np.array_equal(host(y), ref)
     assert np.array_equal(_tiles_to_rows(host(yt)), ref)
+    # K and V in one launch: the same rows and tiles as the two separate calls
+    v = rng.standard_normal((B, N, Hh, d)).astype(np.float32)
+    if in_dt == "bf16":
+        v = bf16_round(v)
+    vt_in = dev_bf16(v) if in_dt == "bf16" else dev(v)
+    k_r, v_t = ops.reorder_kv(xt, vt_in, pt, Npad, b)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(k_r), ref)
+    assert np.array_equal(_tiles_to_rows(host(v_t)), bf16_round(o_reorder(v, perm, Npad)))
     if in_dt == "fp32":
         y32 = ops.reorder(xt, pt, Npad, b, "rows", out_dtype=torch.float32)
         torch.cuda.synchronize()
@@ -77,11 +86,15 @@ def test_reorder_strided_views():
     perm = rng.permutation(N).astype(np.int32)
     Npad = 256
     y = ops.reorder(xt, dev(perm), Npad, b, "rows")
+    vbase = bf16_round(rng.standard_normal((B, Hh, N, d)).astype(np.float32))
+    k_r, v_t = ops.reorder_kv(xt, dev_bf16(vbase).permute(0, 2, 1, 3), dev(perm), Npad, b)
     out = torch.zeros((B, Hh, N, d), dtype=torch.bfloat16, device="cuda").permute(0, 2, 1, 3)
     ops.inverse_reorder(y, dev(perm), N, out=out)
     torch.cuda.synchronize()
     assert np.array_equal(host(y), o_reorder(x, perm, Npad))
     assert np.array_equal(host(out), x)
+    assert np.array_equal(host(k_r), o_reorder(x, perm, Npad))
+    assert np.array_equal(_tiles_to_rows(host(v_t)), o_reorder(vbase.transpose(0, 2, 1, 3), perm, Npad))
 
 
 @pytest.mark.parametrize("N,n,d,b", [(300, 8, 64, 64), (1000, 7, 128, 128), (17776, 8, 64, 128),
@@ -118,12 +131,16 @@ def test_reorder_full_wan_shape():
     cfg = get_config(2)
     say("reorder full", cfg.name)
     ops = _ops()
-    q, _, v = make_inputs(cfg)
+    q, k, v = make_inputs(cfg)
     perm = ops.perm_gilbert3d(cfg.T, cfg.H, cfg.W)
     assert np.array_equal(perm, perm_gilbert3d(cfg.T, cfg.H, cfg.W))
     pt = dev(perm)
     y = ops.reorder(dev_bf16(q), pt, cfg.Npad, cfg.b, "rows")
     yt = ops.reorder(dev_bf16(v), pt, cfg.Npad, cfg.b, "tiles_t")
+    k_r, v_t = ops.reorder_kv(dev_bf16(k), dev_bf16(v), pt, cfg.Npad, cfg.b)   # the layer's launch
     torch.cuda.synchronize()
     assert np.array_equal(host(y), o_reorder(q, perm, cfg.Npad))
-    assert np.array_equal(_tiles_to_rows(host(yt)), o_reorder(v, perm, cfg.Npad))
+    v_rows = o_reorder(v, perm, cfg.Npad)
+    assert np.array_equal(_tiles_to_rows(host(yt)), v_rows)
+    assert np.array_equal(_tiles_to_rows(host(v_t)), v_rows)
+    assert np.array_equal(host(k_r), o_reorder(k, perm, cfg.Npad))
