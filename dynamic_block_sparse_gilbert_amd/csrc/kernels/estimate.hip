@@ -136,12 +136,30 @@ struct PassCfg {
 
 // Cell maxima of one chunk (keys ck0 .. ck0 + 63) of the wave's 32 queries.
 // S[kt][v] holds key ck0 + 32 kt + (v / 4) * 8 + 4 g + v % 4 of query l32.
-// Returns the lane's maximum over its 32 scores; stores each cell maximum of
-// query rq (when `store`) at trow[cell] for the cells that start below nsp
-// (the padding keys of the last chunk have no cell).  K as in est_pass_kernel.
+// Returns the lane's maximum over its 32 scores.  The cell maxima the lane
+// must store (query rq's cells that start below nsp; the padding keys of the
+// last chunk have no cell) are left in `pend` (cell index, or -1 for none)
+// and stored later by CellStores::flush, so that the wave does not wait for
+// those stores before the next chunk.  K as in est_pass_kernel.
+template <int K>
+struct CellStores {
+  static constexpr int kN = K >= 32 ? 1 : 32 / K;   // stores per lane per chunk
+  int idx[kN];
+  float val[kN];
+  __device__ __forceinline__ void clear() {
+#pragma unroll
+    for (int i = 0; i < kN; ++i) idx[i] = -1;
+  }
+  __device__ __forceinline__ void flush(float* trow) const {
+#pragma unroll
+    for (int i = 0; i < kN; ++i)
+      if (idx[i] >= 0) trow[idx[i]] = val[i];
+  }
+};
+
 template <int K>
 __device__ __forceinline__ float cell_maxima(const f32x16_t (&S)[2], int ck0, int g, int cell_log2, int nsp,
-                                             float* trow, bool store) {
+                                             CellStores<K>& pend) {
   auto mx3 = [](float a, float b, float c) { return fmaxf(fmaxf(a, b), c); };
   auto max4 = [&](const f32x16_t& t, int v0) { return fmaxf(fmaxf(t[v0], t[v0 + 1]), fmaxf(t[v0 + 2], t[v0 + 3])); };
   auto max8 = [&](const f32x16_t& t, int v0) {
@@ -153,15 +171,19 @@ __device__ __forceinline__ float cell_maxima(const f32x16_t (&S)[2], int ck0, in
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
   };
+  auto put = [&](int i, bool ok, int cell, float v) {
+    pend.idx[i] = ok ? cell : -1;
+    pend.val[i] = v;
+  };
   if constexpr (K >= 64) {
     const float x = fmaxf(fmaxf(max8(S[0], 0), max8(S[0], 8)), fmaxf(max8(S[1], 0), max8(S[1], 8)));
     const float c = swap_max(x, x);
-    if (store && g == 0 && ck0 < nsp) trow[ck0 >> cell_log2] = c;
+    put(0, g == 0 && ck0 < nsp, ck0 >> cell_log2, c);
     return x;
   } else if constexpr (K == 32) {
     const float x0 = fmaxf(max8(S[0], 0), max8(S[0], 8)), x1 = fmaxf(max8(S[1], 0), max8(S[1], 8));
     const float c = swap_max(x0, x1);   // half 0: tile 0, half 1: tile 1
-    if (store && ck0 + 32 * g < nsp) trow[(ck0 + 32 * g) >> 5] = c;
+    put(0, ck0 + 32 * g < nsp, (ck0 + 32 * g) >> 5, c);
     return fmaxf(x0, x1);
   } else if constexpr (K == 16) {
     float x = -INFINITY;
@@ -170,7 +192,7 @@ __device__ __forceinline__ float cell_maxima(const f32x16_t (&S)[2], int ck0, in
       const float lo = max8(S[kt], 0), hi = max8(S[kt], 8);
       const float c = swap_max(lo, hi);   // half 0: keys 0-15 of the tile, half 1: keys 16-31
       const int key = ck0 + 32 * kt + 16 * g;
-      if (store && key < nsp) trow[key >> 4] = c;
+      put(kt, key < nsp, key >> 4, c);
       x = mx3(x, lo, hi);
     }
     return x;
@@ -183,7 +205,7 @@ __device__ __forceinline__ float cell_maxima(const f32x16_t (&S)[2], int ck0, in
         const float a = max4(S[kt], 8 * p), b = max4(S[kt], 8 * p + 4);
         const float c = swap_max(a, b);   // cells of keys 16p + 0-7 (half 0) and 16p + 8-15 (half 1)
         const int key = ck0 + 32 * kt + 16 * p + 8 * g;
-        if (store && key < nsp) trow[key >> 3] = c;
+        put(2 * kt + p, key < nsp, key >> 3, c);
         x = mx3(x, a, b);
       }
     }
@@ -197,19 +219,19 @@ __device__ __forceinline__ float cell_maxima(const f32x16_t (&S)[2], int ck0, in
       for (int a4 = 0; a4 < 4; ++a4) {
         const int key = ck0 + 32 * kt + 8 * a4 + 4 * g;
         const float t[4] = {S[kt][4 * a4], S[kt][4 * a4 + 1], S[kt][4 * a4 + 2], S[kt][4 * a4 + 3]};
+        const int base = (4 * kt + a4) * (4 / K);
         if constexpr (K == 4) {
           const float c = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
-          if (store && key < nsp) trow[key >> 2] = c;
+          put(base, key < nsp, key >> 2, c);
           x = fmaxf(x, c);
         } else if constexpr (K == 2) {
           const float c0 = fmaxf(t[0], t[1]), c1 = fmaxf(t[2], t[3]);
-          if (store && key < nsp) trow[key >> 1] = c0;
-          if (store && key + 2 < nsp) trow[(key >> 1) + 1] = c1;
+          put(base, key < nsp, key >> 1, c0);
+          put(base + 1, key + 2 < nsp, (key >> 1) + 1, c1);
           x = mx3(x, c0, c1);
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (store && key + e < nsp) trow[key + e] = t[e];
+          for (int e = 0; e < 4; ++e) put(base + e, key + e < nsp, key + e, t[e]);
           x = mx3(x, fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
         }
       }
@@ -289,6 +311,8 @@ __global__ __launch_bounds__(kThreads) void est_pass_kernel(
 
   float m = -INFINITY, l = 0.f;
   float* trow = tmax + ((int64_t)bh * sg.nsp + (qok ? rq : 0)) * sg.ncell;
+  CellStores<K> pend;
+  pend.clear();
   const int tail = (sg.nb - 1) * sg.k;   // first slot of the last block
   auto body = [&](int ch, f32x16_t (&S)[2]) {
     const int ck0 = ch * kChunk;
@@ -300,7 +324,7 @@ __global__ __launch_bounds__(kThreads) void est_pass_kernel(
         for (int v = 0; v < 16; ++v)
           if (!sg.valid(ck0 + 32 * kt + (v >> 2) * 8 + 4 * g + (v & 3))) S[kt][v] = -INFINITY;
     }
-    const float mx = cell_maxima<K>(S, ck0, g, sg.cell_log2, sg.nsp, trow, qok) * sl2;
+    const float mx = cell_maxima<K>(S, ck0, g, sg.cell_log2, sg.nsp, pend) * sl2;
     const float m_new = fmaxf(m, mx);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     float s0 = l * fast_exp2(m - m_use), s1 = 0.f;
@@ -316,20 +340,26 @@ __global__ __launch_bounds__(kThreads) void est_pass_kernel(
   const int c0 = split * sg.cps, c1 = min(sg.nsp_pad / kChunk, c0 + sg.cps);
   f32x16_t S[2];
   dma(c0, Kc0);
+  // The cell maxima of a chunk are stored after the next chunk's barrier, so
+  // they have a whole chunk to complete before the next wait for the copies
+  // (which also waits for stores).
   for (int ch = c0; ch < c1; ch += 2) {
     wait_dma();
     __syncthreads();
     if (ch + 1 < c1) dma(ch + 1, Kc1);
+    if (qok) pend.flush(trow);
     scores(Kc0, S);
     body(ch, S);
     if (ch + 1 < c1) {
       wait_dma();
       __syncthreads();
       if (ch + 2 < c1) dma(ch + 2, Kc0);
+      if (qok) pend.flush(trow);
       scores(Kc1, S);
       body(ch + 1, S);
     }
   }
+  if (qok) pend.flush(trow);
   // merge the two wave halves (each saw half of every chunk's keys)
   const auto rm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
   const float M = fmaxf(__uint_as_float(rm[0]), __uint_as_float(rm[1]));
