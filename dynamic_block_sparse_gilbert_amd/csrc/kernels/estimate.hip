@@ -13,11 +13,10 @@
 // so one pass over the sampled scores suffices if the k_J-wide maxima t_qJ
 // are kept (a (sampled queries) x nb float array in the workspace; for k > 64
 // a block's maximum is kept as k / 64 cell maxima, one per 64-key chunk).
-// Three launches:
-//   gather: copy the sampled rows of Q and K into compact row-major arrays
-//           (zero rows for empty slots) in the workspace;
+// Two launches:
 //   pass:   per sampled query, over a range of the sampled keys: the online
 //           max / sum (one partial per key split) and the block maxima t_qJ;
+//           the sampled rows of Q and K are read in place (no compact copy);
 //   final:  merge the partials into lse2 and form P_imp, one exp2 per
 //           (query block, key block).
 // The key range is split over enough workgroups (about 1536 of 8
@@ -25,7 +24,7 @@
 // The pass computes S^T = K_s Q_s^T on bf16 MFMA 32x32x16 with fp32
 // accumulation: a workgroup of 8 wavefronts owns 256 sampled queries (32 per
 // wavefront, in VGPRs), so each 64-key chunk copied to LDS feeds 256 queries;
-// the compact keys stream through double-buffered, row-padded LDS by the
+// the sampled keys stream through double-buffered, row-padded LDS by the
 // buffer form of the global -> LDS copy.
 #include "common.h"
 #include "../launch.h"
@@ -73,44 +72,6 @@ __device__ __forceinline__ void wg_coords(const SampleGeom& sg, int& bh, int& sp
   panel = id % panels;
   split = (id / panels) % sg.splits;
   bh = id / (panels * sg.splits);
-}
-
-// Compact copies of the sampled rows: qs/ks [BH][nsp_pad][D], zero rows for
-// empty slots and padding.  One thread per 16-byte chunk.  Q comes from the
-// reordered rows, or (tok.q set) from the token of the sampled row in token
-// order, float32 rounded to bf16 as the reorder rounds it.
-template <int D>
-__global__ __launch_bounds__(256) void est_gather_kernel(
-    const __bf16* __restrict__ q_r, const __bf16* __restrict__ k_r, __bf16* __restrict__ qs,
-    __bf16* __restrict__ ks, SampleGeom sg, int Npad, int Hh, TokIO tok) {
-  const int bh = blockIdx.y;
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  const int r = idx / (D / 8), c = idx % (D / 8);
-  if (r >= sg.nsp_pad) return;
-  const int src = sg.row(r);
-  uint4 vq = make_uint4(0, 0, 0, 0), vk = vq;
-  if (src >= 0) {
-    const int64_t off = ((int64_t)bh * Npad + src) * D + 8 * c;
-    vk = *reinterpret_cast<const uint4*>(k_r + off);
-    if (tok.q == nullptr) {
-      vq = *reinterpret_cast<const uint4*>(q_r + off);
-    } else {
-      const int bi = bh / Hh, h = bh % Hh;
-      int t = tok.perm[(int64_t)h * tok.perm_h_stride + src];
-      t = t < 0 ? 0 : (t >= sg.N ? sg.N - 1 : t);
-      const int64_t qo = bi * tok.qsb + (int64_t)t * tok.qsn + h * tok.qsh + 8 * c;
-      if (tok.q_f32) {
-        const float4 a = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(tok.q) + qo)[0];
-        const float4 b = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(tok.q) + qo)[1];
-        vq = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w));
-      } else {
-        vq = *reinterpret_cast<const uint4*>(reinterpret_cast<const __bf16*>(tok.q) + qo);
-      }
-    }
-  }
-  const int64_t dst = ((int64_t)bh * sg.nsp_pad + r) * D + 8 * c;
-  *reinterpret_cast<uint4*>(qs + dst) = vq;
-  *reinterpret_cast<uint4*>(ks + dst) = vk;
 }
 
 // Raw buffer descriptor over `bytes` bytes at `base` (gfx9 word 3: 32-bit data
@@ -246,14 +207,21 @@ __device__ __forceinline__ float cell_maxima(const f32x16_t (&S)[2], int ck0, in
 //
 // A workgroup of 8 wavefronts owns 256 sampled queries (32 per wavefront, Q^T
 // in VGPRs) and one key split: S^T = K_s Q_s^T on 32x32x16 bf16 MFMAs, with
-// the compact keys streamed through double-buffered, row-padded LDS in chunks
-// of 64 by the buffer form of the global -> LDS copy.  Each lane holds whole
-// query columns, so the online (max, sum) runs per lane and the two wave
-// halves merge at the end.
+// the sampled keys gathered straight from the reordered K rows into
+// double-buffered, row-padded LDS in chunks of 64 by the buffer form of the
+// global -> LDS copy.  Each lane holds whole query columns, so the online
+// (max, sum) runs per lane and the two wave halves merge at the end.
+//
+// Sampled slot r of a full block sits at reordered row r * (b / k) (k divides
+// b), so a chunk of full blocks is 64 rows at a fixed stride and its copy
+// offsets are one per-lane table plus a per-chunk scalar; chunks holding the
+// last block's slots or padding use the exact rows (an empty slot reads row
+// 0; its scores are masked to -inf).  Q rows are read the same way, from the
+// reordered Q or, when tok.q is set, from the token of the sampled row.
 template <int D, int K>
 __global__ __launch_bounds__(kThreads) void est_pass_kernel(
-    const __bf16* __restrict__ qs, const __bf16* __restrict__ ks, float2* __restrict__ part,
-    float* __restrict__ tmax, SampleGeom sg, float sl2) {
+    const __bf16* __restrict__ q_r, const __bf16* __restrict__ k_r, TokIO tok, int Npad, int Hh,
+    float2* __restrict__ part, float* __restrict__ tmax, SampleGeom sg, float sl2) {
   using C = PassCfg<D>;
   // Distinct arrays with static roles in each half of the 2x-unrolled loop,
   // so the LDS reads of one are not made to wait for the copy into the other.
@@ -267,34 +235,82 @@ __global__ __launch_bounds__(kThreads) void est_pass_kernel(
   const int rq = panel * kQPerWg + wave * 32 + l32;
   const bool qok = rq < sg.nsp;
 
-  // Q^T operand: lane (l32, g) holds Q_s[rq][16 kk + 8 g .. +7].
-  bf16x8_t qreg[D / 16];
-  {
-    const int rl = min(rq, sg.nsp_pad - 1);
-    const __bf16* qp = qs + ((int64_t)bh * sg.nsp_pad + rl) * D + 8 * g;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * kk);
-  }
-
   // Copies: LDS byte 1024 n + 16 lane of a chunk holds padded unit p = 64 n +
-  // lane, i.e. key row p / kRowU, unit p % kRowU (the pad unit repeats the
-  // row's last unit).  Surplus instructions repeat the chunk's last one.
-  const auto rk = make_rsrc(ks + (int64_t)bh * sg.nsp_pad * D, (uint32_t)sg.nsp_pad * (uint32_t)(D * 2));
+  // lane, i.e. key row p / kRowU of the chunk, unit p % kRowU (the pad unit
+  // repeats the row's last unit).  Surplus instructions repeat the chunk's
+  // last one.
+  const auto rk = make_rsrc(k_r + (int64_t)bh * Npad * D, (uint32_t)Npad * (uint32_t)(D * 2));
+  const int rstride = sg.b >> sg.klog2;   // reordered rows between consecutive slots of a full block
   uint32_t voff[C::kPer];
 #pragma unroll
   for (int i = 0; i < C::kPer; ++i) {
     const int n = min(wave + i * kWaves, C::kInstr - 1);
     const int p = 64 * n + lane;
     const int row = p / C::kRowU, c = min(p % C::kRowU, C::kRowU - 2);
-    voff[i] = (uint32_t)(row * D * 2 + c * 16);
+    voff[i] = (uint32_t)(row * rstride * D * 2 + c * 16);
   }
+  // From this slot on, chunks take the exact rows: the last block when it is
+  // partial (its slots are spread over fewer than b rows), and the padding.
+  const int exact_from = (sg.N < sg.nb * sg.b || sg.nsp % kChunk != 0) ? (sg.nb - 1) * sg.k : sg.nsp_pad;
   auto dma = [&](int ch, char* buf) {
+    const int ck0 = ch * kChunk;
+    if (ck0 + kChunk <= exact_from) {
 #pragma unroll
-    for (int i = 0; i < C::kPer; ++i) {
-      const int n = min(wave + i * kWaves, C::kInstr - 1);
-      copy16_lds(rk, buf + 1024 * n, voff[i], (uint32_t)ch * (uint32_t)(kChunk * D * 2));
+      for (int i = 0; i < C::kPer; ++i) {
+        const int n = min(wave + i * kWaves, C::kInstr - 1);
+        copy16_lds(rk, buf + 1024 * n, voff[i], (uint32_t)ck0 * (uint32_t)(rstride * D * 2));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::kPer; ++i) {
+        const int n = min(wave + i * kWaves, C::kInstr - 1);
+        const int p = 64 * n + lane;
+        const int row = p / C::kRowU, c = min(p % C::kRowU, C::kRowU - 2);
+        const int src = sg.row(ck0 + row);
+        copy16_lds(rk, buf + 1024 * n, (uint32_t)((src < 0 ? 0 : src) * D * 2 + c * 16), 0u);
+      }
     }
   };
+  // The first chunk's copy is issued before the Q loads so that the two
+  // latencies overlap.
+  const int c0 = split * sg.cps, c1 = min(sg.nsp_pad / kChunk, c0 + sg.cps);
+  dma(c0, Kc0);
+
+  // Q^T operand: lane (l32, g) holds Q_s[rq][16 kk + 8 g .. +7]; zero for an
+  // empty slot or padding.
+  bf16x8_t qreg[D / 16];
+  {
+    const int src = sg.row(rq);
+    if (src < 0) {
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = bf16x8_t{};
+    } else if (tok.q == nullptr) {
+      const __bf16* qp = q_r + ((int64_t)bh * Npad + src) * D + 8 * g;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * kk);
+    } else {
+      const int bi = bh / Hh, h = bh % Hh;
+      int t = tok.perm[(int64_t)h * tok.perm_h_stride + src];
+      t = t < 0 ? 0 : (t >= sg.N ? sg.N - 1 : t);
+      const int64_t qo = bi * tok.qsb + (int64_t)t * tok.qsn + h * tok.qsh + 8 * g;
+      if (tok.q_f32) {
+        const float* qp = reinterpret_cast<const float*>(tok.q) + qo;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const float4 a = reinterpret_cast<const float4*>(qp + 16 * kk)[0];
+          const float4 c = reinterpret_cast<const float4*>(qp + 16 * kk)[1];
+          const uint4 w = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(c.x, c.y),
+                                     pack_bf16x2(c.z, c.w));
+          qreg[kk] = __builtin_bit_cast(bf16x8_t, w);
+        }
+      } else {
+        const __bf16* qp = reinterpret_cast<const __bf16*>(tok.q) + qo;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * kk);
+      }
+    }
+  }
+
   const int kbase = l32 * C::kStride + 16 * g;
   auto scores = [&](const char* kb, f32x16_t (&S)[2]) {
     S[0] = f32x16_t{};
@@ -337,9 +353,7 @@ __global__ __launch_bounds__(kThreads) void est_pass_kernel(
     m = m_new;
   };
 
-  const int c0 = split * sg.cps, c1 = min(sg.nsp_pad / kChunk, c0 + sg.cps);
   f32x16_t S[2];
-  dma(c0, Kc0);
   // The cell maxima of a chunk are stored after the next chunk's barrier, so
   // they have a whole chunk to complete before the next wait for the copies
   // (which also waits for stores).
@@ -463,26 +477,21 @@ hipError_t launch_d(const EstimateArgs& a) {
   const float sl2 = a.scale * kLog2e;
   const int BH = a.B * a.Hh;
   split_plan(BH, sg.nsp, sg.splits, sg.cps);
-  __bf16* qs = reinterpret_cast<__bf16*>(a.workspace);
-  __bf16* ks = qs + (int64_t)BH * sg.nsp_pad * D;
-  float2* part = reinterpret_cast<float2*>(ks + (int64_t)BH * sg.nsp_pad * D);
+  float2* part = reinterpret_cast<float2*>(a.workspace);
   float* tmax = reinterpret_cast<float*>(part + (int64_t)BH * sg.splits * sg.nsp);
-
-  hipLaunchKernelGGL((est_gather_kernel<D>), dim3((sg.nsp_pad * (D / 8) + 255) / 256, BH), dim3(256), 0,
-                     a.stream, (const __bf16*)a.q_r, (const __bf16*)a.k_r, qs, ks, sg, a.Npad, a.Hh, a.tok);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const __bf16* qr = (const __bf16*)a.q_r;
+  const __bf16* kr = (const __bf16*)a.k_r;
   dim3 grid((unsigned)(((sg.nsp + kQPerWg - 1) / kQPerWg) * sg.splits * BH));
   switch (a.k) {
-    case 1: hipLaunchKernelGGL((est_pass_kernel<D, 1>), grid, dim3(kThreads), 0, a.stream, qs, ks, part, tmax, sg, sl2); break;
-    case 2: hipLaunchKernelGGL((est_pass_kernel<D, 2>), grid, dim3(kThreads), 0, a.stream, qs, ks, part, tmax, sg, sl2); break;
-    case 4: hipLaunchKernelGGL((est_pass_kernel<D, 4>), grid, dim3(kThreads), 0, a.stream, qs, ks, part, tmax, sg, sl2); break;
-    case 8: hipLaunchKernelGGL((est_pass_kernel<D, 8>), grid, dim3(kThreads), 0, a.stream, qs, ks, part, tmax, sg, sl2); break;
-    case 16: hipLaunchKernelGGL((est_pass_kernel<D, 16>), grid, dim3(kThreads), 0, a.stream, qs, ks, part, tmax, sg, sl2); break;
-    case 32: hipLaunchKernelGGL((est_pass_kernel<D, 32>), grid, dim3(kThreads), 0, a.stream, qs, ks, part, tmax, sg, sl2); break;
-    default: hipLaunchKernelGGL((est_pass_kernel<D, 64>), grid, dim3(kThreads), 0, a.stream, qs, ks, part, tmax, sg, sl2); break;
+    case 1: hipLaunchKernelGGL((est_pass_kernel<D, 1>), grid, dim3(kThreads), 0, a.stream, qr, kr, a.tok, a.Npad, a.Hh, part, tmax, sg, sl2); break;
+    case 2: hipLaunchKernelGGL((est_pass_kernel<D, 2>), grid, dim3(kThreads), 0, a.stream, qr, kr, a.tok, a.Npad, a.Hh, part, tmax, sg, sl2); break;
+    case 4: hipLaunchKernelGGL((est_pass_kernel<D, 4>), grid, dim3(kThreads), 0, a.stream, qr, kr, a.tok, a.Npad, a.Hh, part, tmax, sg, sl2); break;
+    case 8: hipLaunchKernelGGL((est_pass_kernel<D, 8>), grid, dim3(kThreads), 0, a.stream, qr, kr, a.tok, a.Npad, a.Hh, part, tmax, sg, sl2); break;
+    case 16: hipLaunchKernelGGL((est_pass_kernel<D, 16>), grid, dim3(kThreads), 0, a.stream, qr, kr, a.tok, a.Npad, a.Hh, part, tmax, sg, sl2); break;
+    case 32: hipLaunchKernelGGL((est_pass_kernel<D, 32>), grid, dim3(kThreads), 0, a.stream, qr, kr, a.tok, a.Npad, a.Hh, part, tmax, sg, sl2); break;
+    default: hipLaunchKernelGGL((est_pass_kernel<D, 64>), grid, dim3(kThreads), 0, a.stream, qr, kr, a.tok, a.Npad, a.Hh, part, tmax, sg, sl2); break;
   }
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(est_final_kernel, dim3((unsigned)a.nb, (unsigned)BH), dim3(kFinalThreads), 0, a.stream,
                      (const float2*)part, (const float*)tmax, a.p_imp, sg, sl2);
@@ -500,7 +509,9 @@ size_t estimate_workspace_bytes(int B, int Hh, int nb, int k, int d) {
   int klog2 = 0;
   while ((1 << klog2) < k) ++klog2;
   const int64_t cells = nsp >> (klog2 < 6 ? klog2 : 6);
-  return (size_t)(BH * nsp_pad * d * 2 * 2 + BH * splits * nsp * 8 + BH * nsp * cells * 4);
+  (void)nsp_pad;
+  (void)d;
+  return (size_t)(BH * splits * nsp * 8 + BH * nsp * cells * 4);
 }
 
 hipError_t launch_estimate(const EstimateArgs& a) {

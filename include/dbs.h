@@ -143,8 +143,7 @@ dbs_status dbs_inverse_reorder(const void* y, dbs_dtype y_dt, void* x, dbs_dtype
                                const int32_t* perm, int perm_per_head,
                                int B, int Hh, int N, int Npad, int d, hipStream_t stream);
 
-/* Bytes of device workspace dbs_estimate_blocks needs: compact copies of the
- * sampled Q and K rows (B * Hh * ceil(nb*k / 64)*64 * d bf16 each), one
+/* Bytes of device workspace dbs_estimate_blocks needs: one
  * partial softmax (max, sum) float pair per sampled query and key split (the
  * library splits the sampled keys over up to nb*k/64 workgroups per panel of
  * 256 sampled queries), and per sampled query the maximum raw score over each cell of

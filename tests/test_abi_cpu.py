@@ -127,9 +127,9 @@ def test_estimate_validation(dbs):
     _, L = dbs
     f = L.lib().dbs_estimate_blocks
     ws = L.lib().dbs_estimate_workspace_bytes(1, 2, 100, 128, 64, 8)
-    # compact Q_s, K_s (padded to 64) + 1 split of (m, l) per sampled query + the block maxima of each
-    # sampled query (nb = 2 cells of k = 8 keys)
-    assert ws == 1 * 2 * 64 * 128 * 2 * 2 + 1 * 2 * 1 * 16 * 8 + 1 * 2 * 16 * 2 * 4
+    # 1 split of (m, l) per sampled query + the block maxima of each sampled query (nb = 2 cells
+    # of k = 8 keys)
+    assert ws == 1 * 2 * 1 * 16 * 8 + 1 * 2 * 16 * 2 * 4
     ok = (A, A, 0, 1, 2, 100, 128, 128, 64, 8, 0.125, A, A, ws, None)
     def call(**kw):
         a = list(ok)
