@@ -26,6 +26,8 @@
 // wavefront, in VGPRs), so each 64-key chunk copied to LDS feeds 256 queries;
 // the sampled keys stream through double-buffered, row-padded LDS by the
 // buffer form of the global -> LDS copy.
+#include <type_traits>
+
 #include "common.h"
 #include "../launch.h"
 
@@ -329,8 +331,40 @@ __global__ __launch_bounds__(kThreads) void est_pass_kernel(
   float* trow = tmax + ((int64_t)bh * sg.nsp + (qok ? rq : 0)) * sg.ncell;
   CellStores<K> pend;
   pend.clear();
+  // k = 16: the lane partial maxima of a chunk pair are completed across the
+  // wave halves with one exchange per cell: half 0 finishes the pair's first
+  // chunk and half 1 the second, so a lane stores its query's 4 cells of one
+  // chunk as 16 contiguous bytes (and a query's 8 cells of the pair are 32).
+  float held[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  float4 pv = make_float4(0.f, 0.f, 0.f, 0.f);
+  int pcell = -1;                        // first cell of the pending 16-byte store, or -1
+  const bool vec16 = (sg.ncell & 3) == 0 && (((uintptr_t)tmax) & 15u) == 0;
+  auto pair16 = [&](int ch_first, const float (&px)[4]) {
+    float c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(held[j]), __float_as_uint(px[j]), false, false);
+      c[j] = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    pv = make_float4(c[0], c[1], c[2], c[3]);
+    const int chunk = ch_first + g;
+    pcell = chunk * kChunk < sg.nsp ? 4 * chunk : -1;
+  };
+  auto flush16 = [&]() {
+    if (qok && pcell >= 0) {
+      if (vec16 && 16 * (pcell + 3) < sg.nsp) {
+        *reinterpret_cast<float4*>(trow + pcell) = pv;
+      } else {
+        const float vv[4] = {pv.x, pv.y, pv.z, pv.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (16 * (pcell + j) < sg.nsp) trow[pcell + j] = vv[j];
+      }
+    }
+    pcell = -1;
+  };
   const int tail = (sg.nb - 1) * sg.k;   // first slot of the last block
-  auto body = [&](int ch, f32x16_t (&S)[2]) {
+  auto body = [&](int ch, f32x16_t (&S)[2], auto first) {
     const int ck0 = ch * kChunk;
     if (ck0 + kChunk > sg.nsp || (sg.kj_last < sg.k && ck0 + kChunk > tail)) {
       // rare: padding or the last block's empty slots score -inf
@@ -340,7 +374,23 @@ __global__ __launch_bounds__(kThreads) void est_pass_kernel(
         for (int v = 0; v < 16; ++v)
           if (!sg.valid(ck0 + 32 * kt + (v >> 2) * 8 + 4 * g + (v & 3))) S[kt][v] = -INFINITY;
     }
-    const float mx = cell_maxima<K>(S, ck0, g, sg.cell_log2, sg.nsp, pend) * sl2;
+    float mx;
+    if constexpr (K == 16) {
+      auto mx3 = [](float a, float b, float c) { return fmaxf(fmaxf(a, b), c); };
+      auto max8 = [&](const f32x16_t& t, int v0) {
+        return fmaxf(mx3(t[v0], t[v0 + 1], t[v0 + 2]), mx3(t[v0 + 3], mx3(t[v0 + 4], t[v0 + 5], t[v0 + 6]), t[v0 + 7]));
+      };
+      const float px[4] = {max8(S[0], 0), max8(S[0], 8), max8(S[1], 0), max8(S[1], 8)};
+      if constexpr (decltype(first)::value) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) held[j] = px[j];
+      } else {
+        pair16(ch - 1, px);
+      }
+      mx = fmaxf(fmaxf(px[0], px[1]), fmaxf(px[2], px[3])) * sl2;
+    } else {
+      mx = cell_maxima<K>(S, ck0, g, sg.cell_log2, sg.nsp, pend) * sl2;
+    }
     const float m_new = fmaxf(m, mx);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     float s0 = l * fast_exp2(m - m_use), s1 = 0.f;
@@ -361,19 +411,34 @@ __global__ __launch_bounds__(kThreads) void est_pass_kernel(
     wait_dma();
     __syncthreads();
     if (ch + 1 < c1) dma(ch + 1, Kc1);
-    if (qok) pend.flush(trow);
+    if constexpr (K == 16) {
+      flush16();
+    } else {
+      if (qok) pend.flush(trow);
+    }
     scores(Kc0, S);
-    body(ch, S);
+    body(ch, S, std::true_type{});
     if (ch + 1 < c1) {
       wait_dma();
       __syncthreads();
       if (ch + 2 < c1) dma(ch + 2, Kc0);
-      if (qok) pend.flush(trow);
+      if constexpr (K != 16) {
+        if (qok) pend.flush(trow);
+      }
       scores(Kc1, S);
-      body(ch + 1, S);
+      body(ch + 1, S, std::false_type{});
     }
   }
-  if (qok) pend.flush(trow);
+  if constexpr (K == 16) {
+    if (((c1 - c0) & 1) != 0) {   // the last chunk had no partner: half 0 completes it
+      const float none[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      pair16(c1 - 1, none);
+      if (g == 1) pcell = -1;
+    }
+    flush16();
+  } else {
+    if (qok) pend.flush(trow);
+  }
   // merge the two wave halves (each saw half of every chunk's keys)
   const auto rm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
   const float M = fmaxf(__uint_as_float(rm[0]), __uint_as_float(rm[1]));
