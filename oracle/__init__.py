@@ -8,7 +8,8 @@ never does.
 
 Modules: perm (curve and cuboid orders), reorder (gather / scatter), estimator
 (sampled block importance), mask (cumulative-threshold mask), attention
-(block-masked attention with optional global tokens), accounting (sparsity and
-FLOP).  Every function is pinned by CPU tests against closed forms, invariants
+(block-masked attention with optional global tokens), attention_bwd (its
+gradients, plain ASA, and the key-to-query block lists), accounting (sparsity
+and FLOP).  Every function is pinned by CPU tests against closed forms, invariants
 and brute force (tests/test_oracle_*.py).
 """
