@@ -45,6 +45,10 @@ SIGNATURES = {
                                  _i, _i, _vp, _vp, _vp]),
     "dbs_sparse_attn_fwd_tok": (_i, [_vp, _i, _i64, _i64, _i64, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
                                      _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _i, _i64, _i64, _i64, _vp, _vp]),
+    "dbs_transpose_lists": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
+    "dbs_attn_bwd_workspace_bytes": (C.c_size_t, [_i, _i, _i, _i]),
+    "dbs_sparse_attn_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _vp,
+                                 _vp, _vp, _vp, _vp, C.c_size_t, _vp]),
 }
 
 _lock = threading.Lock()

@@ -29,6 +29,7 @@ SOURCES = [
     "kernels/estimate.hip",
     "kernels/mask.hip",
     "kernels/attn.hip",
+    "kernels/attn_bwd.hip",
 ]
 
 # Packed fp32 VALU ops are disabled on purpose: only plain fp32 ops are emitted.

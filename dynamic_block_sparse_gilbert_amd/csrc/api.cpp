@@ -384,3 +384,61 @@ dbs_status dbs_sparse_attn_fwd_tok(const void* q, dbs_dtype q_dt, int64_t qsb, i
 }
 
 }  // extern "C"
+
+extern "C" {
+
+dbs_status dbs_transpose_lists(const int32_t* kv_count, const int32_t* kv_idx, int B, int Hh, int nb,
+                               int32_t* kvT_count, int32_t* kvT_idx, hipStream_t stream) {
+  DBS_GUARD_BEGIN
+  REQUIRE(kv_count && kv_idx && kvT_count && kvT_idx, DBS_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(((uintptr_t)kv_count & 3u) == 0 && ((uintptr_t)kv_idx & 3u) == 0 && ((uintptr_t)kvT_count & 3u) == 0 &&
+              ((uintptr_t)kvT_idx & 3u) == 0,
+          DBS_ERR_ALIGNMENT, "misaligned pointer");
+  REQUIRE(B >= 1 && Hh >= 1 && nb >= 1, DBS_ERR_INVALID_ARG, "bad sizes");
+  REQUIRE(nb <= 4096, DBS_ERR_UNSUPPORTED, "nb=%d must be <= 4096", nb);
+  REQUIRE((int64_t)B * Hh * nb * nb <= ((int64_t)1 << 40), DBS_ERR_INVALID_ARG, "lists too large");
+  dbs::TransposeListsArgs a{};
+  a.kv_count = kv_count; a.kv_idx = kv_idx; a.kvT_count = kvT_count; a.kvT_idx = kvT_idx;
+  a.B = B; a.Hh = Hh; a.nb = nb; a.stream = stream;
+  return from_hip(dbs::launch_transpose_lists(a), "dbs_transpose_lists launch");
+  DBS_GUARD_END
+}
+
+size_t dbs_attn_bwd_workspace_bytes(int B, int Hh, int Npad, int d) {
+  if (B < 1 || Hh < 1 || Npad < 1 || (d != 64 && d != 128)) return 0;
+  return dbs::attn_bwd_workspace_bytes(B, Hh, Npad, d);
+}
+
+dbs_status dbs_sparse_attn_bwd(const void* q_r, const void* k_r, const void* v_r, const void* o_r,
+                               const void* do_r, const float* lse, int B, int Hh, int N, int Npad, int d, int b,
+                               float scale, const int32_t* kv_count, const int32_t* kv_idx,
+                               const int32_t* kvT_count, const int32_t* kvT_idx, float* dq_r, float* dk_r,
+                               float* dv_r, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  DBS_GUARD_BEGIN
+  REQUIRE(q_r && k_r && v_r && o_r && do_r && lse && kv_count && kv_idx && kvT_count && kvT_idx && dq_r && dk_r &&
+              dv_r && workspace,
+          DBS_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(aligned16(q_r) && aligned16(k_r) && aligned16(v_r) && aligned16(o_r) && aligned16(do_r) &&
+              aligned16(dq_r) && aligned16(dk_r) && aligned16(dv_r) && aligned16(workspace),
+          DBS_ERR_ALIGNMENT, "misaligned pointer");
+  REQUIRE(((uintptr_t)lse & 3u) == 0 && ((uintptr_t)kv_count & 3u) == 0 && ((uintptr_t)kv_idx & 3u) == 0 &&
+              ((uintptr_t)kvT_count & 3u) == 0 && ((uintptr_t)kvT_idx & 3u) == 0,
+          DBS_ERR_ALIGNMENT, "misaligned pointer");
+  dbs_status st = check_geometry(B, Hh, N, Npad, d, b);
+  if (st != DBS_OK) return st;
+  REQUIRE(std::isfinite(scale), DBS_ERR_INVALID_ARG, "scale must be finite");
+  const int nb = Npad / b;
+  REQUIRE(nb <= 4096, DBS_ERR_UNSUPPORTED, "nb=%d must be <= 4096", nb);
+  REQUIRE((int64_t)B * Hh * nb <= INT32_MAX, DBS_ERR_INVALID_ARG, "too many blocks");
+  const size_t need = dbs::attn_bwd_workspace_bytes(B, Hh, Npad, d);
+  REQUIRE(workspace_bytes >= need, DBS_ERR_INVALID_ARG, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  dbs::AttnBwdArgs a{};
+  a.q_r = q_r; a.k_r = k_r; a.v_r = v_r; a.o_r = o_r; a.do_r = do_r; a.lse = lse;
+  a.kv_count = kv_count; a.kv_idx = kv_idx; a.kvT_count = kvT_count; a.kvT_idx = kvT_idx;
+  a.dq = dq_r; a.dk = dk_r; a.dv = dv_r; a.workspace = workspace;
+  a.B = B; a.Hh = Hh; a.N = N; a.Npad = Npad; a.d = d; a.b = b; a.nb = nb; a.scale = scale; a.stream = stream;
+  return from_hip(dbs::launch_attn_bwd(a), "dbs_sparse_attn_bwd launch");
+  DBS_GUARD_END
+}
+
+}  // extern "C"

@@ -82,6 +82,35 @@ struct AttnArgs {
   hipStream_t stream;
 };
 
+struct TransposeListsArgs {
+  const int32_t* kv_count;
+  const int32_t* kv_idx;
+  int32_t* kvT_count;
+  int32_t* kvT_idx;
+  int B, Hh, nb;
+  hipStream_t stream;
+};
+
+struct AttnBwdArgs {
+  const void* q_r;
+  const void* k_r;
+  const void* v_r;       // V in rows layout
+  const void* o_r;
+  const void* do_r;
+  const float* lse;      // natural log, from the forward
+  const int32_t* kv_count;
+  const int32_t* kv_idx;
+  const int32_t* kvT_count;
+  const int32_t* kvT_idx;
+  float* dq;
+  float* dk;
+  float* dv;
+  void* workspace;
+  int B, Hh, N, Npad, d, b, nb;
+  float scale;
+  hipStream_t stream;
+};
+
 hipError_t launch_reorder(const ReorderArgs& a);
 hipError_t launch_reorder_kv(const ReorderArgs& a);
 hipError_t launch_inverse_reorder(const ReorderArgs& a);
@@ -90,5 +119,8 @@ hipError_t launch_estimate(const EstimateArgs& a);
 size_t estimate_workspace_bytes(int B, int Hh, int nb, int k, int d);
 hipError_t launch_build_mask(const MaskArgs& a);
 hipError_t launch_attn_fwd(const AttnArgs& a);
+hipError_t launch_transpose_lists(const TransposeListsArgs& a);
+size_t attn_bwd_workspace_bytes(int B, int Hh, int Npad, int d);
+hipError_t launch_attn_bwd(const AttnBwdArgs& a);
 
 }  // namespace dbs

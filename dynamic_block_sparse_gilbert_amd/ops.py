@@ -253,3 +253,49 @@ def sparse_attn_fwd_tok(q: torch.Tensor, perm: torch.Tensor, k_r: torch.Tensor, 
         int(Ng), int(n_pool), _p(out), _dt(out), out.stride(0), out.stride(1), out.stride(2), _p(lse),
         _stream()))
     return out, lse
+
+
+# --------------------------------------------------------------------------- backward
+
+
+def transpose_lists(kv_count: torch.Tensor, kv_idx: torch.Tensor):
+    """Key-to-query lists: (kvT_count [B, Hh, nb], kvT_idx [B, Hh, nb, nb]) int32; row J lists, ascending,
+    the query blocks whose kept list holds J (entries past kvT_count unspecified)."""
+    _dev(kv_count, kv_idx)
+    B, Hh, nb = kv_count.shape
+    kvT_count = torch.empty_like(kv_count)
+    kvT_idx = torch.empty_like(kv_idx)
+    check("dbs_transpose_lists", lib().dbs_transpose_lists(
+        _p(kv_count), _p(kv_idx), B, Hh, nb, _p(kvT_count), _p(kvT_idx), _stream()))
+    return kvT_count, kvT_idx
+
+
+def attn_bwd_workspace_bytes(B: int, Hh: int, Npad: int, d: int) -> int:
+    return int(lib().dbs_attn_bwd_workspace_bytes(B, Hh, Npad, d))
+
+
+def sparse_attn_bwd(q_r: torch.Tensor, k_r: torch.Tensor, v_r: torch.Tensor, o_r: torch.Tensor,
+                    do_r: torch.Tensor, lse: torch.Tensor, N: int, b: int, scale: float,
+                    kv_count: torch.Tensor, kv_idx: torch.Tensor,
+                    kvT_count: Optional[torch.Tensor] = None, kvT_idx: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None):
+    """Gradients of sparse_attn_fwd (no global tokens).  q_r, k_r, v_r (V in rows layout), o_r, do_r:
+    rows [B, Hh, Npad, d] bf16; lse from the forward.  Returns (dq, dk, dv) float32 rows."""
+    _dev(q_r, k_r, v_r, o_r, do_r, lse, kv_count, kv_idx, kvT_count, kvT_idx, workspace)
+    B, Hh, Npad, d = q_r.shape
+    for t in (k_r, v_r, o_r, do_r):
+        if t.shape != q_r.shape or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("q_r, k_r, v_r, o_r, do_r must be contiguous bf16 rows of one shape")
+    if kvT_count is None or kvT_idx is None:
+        kvT_count, kvT_idx = transpose_lists(kv_count, kv_idx)
+    need = attn_bwd_workspace_bytes(B, Hh, Npad, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_r.device)
+    dq = torch.empty((B, Hh, Npad, d), dtype=torch.float32, device=q_r.device)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    check("dbs_sparse_attn_bwd", lib().dbs_sparse_attn_bwd(
+        _p(q_r), _p(k_r), _p(v_r), _p(o_r), _p(do_r), _p(lse), B, Hh, N, Npad, d, b, float(scale),
+        _p(kv_count), _p(kv_idx), _p(kvT_count), _p(kvT_idx), _p(dq), _p(dk), _p(dv), _p(workspace),
+        workspace.numel() * workspace.element_size(), _stream()))
+    return dq, dk, dv

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define DBS_ABI_VERSION 4
+#define DBS_ABI_VERSION 5
 
 typedef enum {
   DBS_OK = 0,
@@ -260,6 +260,48 @@ dbs_status dbs_sparse_attn_fwd_tok(const void* q, dbs_dtype q_dt, int64_t qsb, i
                                    const void* k_g, const void* v_g, int Ng, int n_pool,
                                    void* out, dbs_dtype out_dt, int64_t osb, int64_t osn, int64_t osh,
                                    float* lse, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Backward (plain ASA).  The pages define the forward only (Video-BLADE
+ * "Step 2.2"); its gradient is the derivative of that definition, and the
+ * key-to-query lists it needs are the reverse scatter of the query-to-key
+ * lists that the BSA notes (sparse kernels with forward and backward) use.
+ * ------------------------------------------------------------------------- */
+
+/* Key-to-query lists: for every (b, h, J), the query blocks I whose list
+ * (kv_count / kv_idx as written by dbs_build_mask) holds J, in ascending
+ * order.  kv_count entries are clamped to [0, nb] and kv_idx entries outside
+ * [0, nb) skipped, as the attention does; lists are expected to hold distinct
+ * blocks (a repeated entry is listed again).  kvT_count [B, Hh, nb] int32,
+ * kvT_idx [B, Hh, nb, nb] int32 (entries past kvT_count unspecified).
+ * UNSUPPORTED for nb > 4096. */
+dbs_status dbs_transpose_lists(const int32_t* kv_count, const int32_t* kv_idx, int B, int Hh, int nb,
+                               int32_t* kvT_count, int32_t* kvT_idx, hipStream_t stream);
+
+/* Bytes of device workspace dbs_sparse_attn_bwd needs: transposed-tile copies
+ * of Q, dO and K (3 * B * Hh * Npad * d bf16) and D = rowsum(dO * O)
+ * (B * Hh * Npad float).  0 for invalid sizes. */
+size_t dbs_attn_bwd_workspace_bytes(int B, int Hh, int Npad, int d);
+
+/* Gradients of dbs_sparse_attn_fwd without global tokens:
+ *   P = softmax(Q K^T * scale) over the kept blocks, dV = P^T dO,
+ *   dS = P * (dO V^T - rowsum(dO * O)), dQ = dS K * scale, dK = dS^T Q * scale.
+ * q_r, k_r, v_r, o_r, do_r: DBS_ROWS bf16 [B, Hh, Npad, d] (note: V in rows
+ * layout); rows N..Npad-1 of q_r, k_r, v_r and do_r must be finite
+ * (dbs_reorder writes zeros there), o_r's are not read.  lse: the forward's
+ * float32 [B, Hh, Npad] (rows < N read).  kv_count / kv_idx: the lists the
+ * forward used; kvT_count / kvT_idx: their dbs_transpose_lists.  dq_r, dk_r,
+ * dv_r: float32 [B, Hh, Npad, d], rows >= N written as zero; a query block
+ * with no kept block gets dQ = 0.  workspace: device, >=
+ * dbs_attn_bwd_workspace_bytes(B, Hh, Npad, d) bytes, contents irrelevant.
+ * Errors as for dbs_sparse_attn_fwd, and INVALID_ARG for a small workspace. */
+dbs_status dbs_sparse_attn_bwd(const void* q_r, const void* k_r, const void* v_r, const void* o_r,
+                               const void* do_r, const float* lse,
+                               int B, int Hh, int N, int Npad, int d, int b, float scale,
+                               const int32_t* kv_count, const int32_t* kv_idx,
+                               const int32_t* kvT_count, const int32_t* kvT_idx,
+                               float* dq_r, float* dk_r, float* dv_r,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

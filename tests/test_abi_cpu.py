@@ -37,7 +37,7 @@ def test_all_declared_symbols_exported(dbs):
     for n in names:
         assert hasattr(h, n), n
     assert set(names) == set(L.SIGNATURES), set(names) ^ set(L.SIGNATURES)
-    assert L.lib().dbs_abi_version() == 4
+    assert L.lib().dbs_abi_version() == 5
 
 
 @pytest.mark.parametrize("T,H,W", list(itertools.product(range(1, 7), repeat=3)))
@@ -217,6 +217,33 @@ def test_reorder_kv_validation(dbs):
     assert call(14, 96) == -2             # head dim
     assert call(13, 1000) == -1           # Npad not a multiple of b
     assert call(9, 2) == -1               # perm_per_head
+
+
+@cpu_only
+def test_backward_validation(dbs):
+    _, L = dbs
+    t = L.lib().dbs_transpose_lists
+    assert t(0, A, 1, 2, 16, A, A, None) == -1           # NULL
+    assert t(A, A, 1, 2, 4097, A, A, None) == -2         # nb > 4096
+    assert t(A + 2, A, 1, 2, 16, A, A, None) == -3       # misaligned
+    assert L.lib().dbs_attn_bwd_workspace_bytes(1, 2, 256, 128) == 3 * 2 * 256 * 128 * 2 + 2 * 256 * 4
+    assert L.lib().dbs_attn_bwd_workspace_bytes(1, 2, 256, 96) == 0
+    f = L.lib().dbs_sparse_attn_bwd
+    ws = L.lib().dbs_attn_bwd_workspace_bytes(1, 2, 1024, 128)
+    # q, k, v, o, do, lse, B, Hh, N, Npad, d, b, scale, cnt, idx, cntT, idxT, dq, dk, dv, ws, ws_bytes, stream
+    ok = [A, A, A, A, A, A, 1, 2, 1000, 1024, 128, 128, 0.088, A, A, A, A, A, A, A, A, ws, None]
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return f(*a)
+    assert call(4, 0) == -1                # do NULL
+    assert call(5, 0) == -1                # lse NULL
+    assert call(15, 0) == -1               # kvT_count NULL
+    assert call(17, A + 8) == -3           # misaligned dq
+    assert call(10, 96) == -2              # head dim
+    assert call(9, 1000) == -1             # Npad not a multiple of b
+    assert call(21, ws - 1) == -1          # small workspace
+    assert call(12, float("inf")) == -1    # scale
 
 
 @cpu_only
