@@ -23,13 +23,17 @@
 //       lane's registers (each lane holds one query: lse and D are scalars),
 //       dQ^T += K^T dS^T.  It also writes D for the next launch.
 //   dkdv: one workgroup per (batch, head, key block), 32 keys per wavefront,
-//     over the query blocks that keep it, in stages of 64 queries (two
-//     sub-tiles of 32): S = Q K^T, dP = dO V^T (K^T, V^T in VGPRs),
-//     dV^T += dO^T P, dK^T += Q^T dS.
+//     over the query blocks that keep it, in stages of 64 queries taken as two
+//     sub-tiles of 32 (each finished before the next, to bound the registers):
+//     S = Q K^T, dP = dO V^T (K^T, V^T in VGPRs), dV^T += dO^T P,
+//     dK^T += Q^T dS.
 // All products are bf16 MFMA 32x32x16 with fp32 accumulation; P and dS are
 // rounded to bf16 for the second product.  Stage data are copied global -> LDS
-// by the buffer form of the DMA path into row-padded LDS (one buffer per
-// operand; the other workgroup on the CU overlaps the copies).
+// by the buffer form of the DMA path into row-padded LDS, one buffer set per
+// workgroup, and both kernels are held to 256 VGPRs: two workgroups then share
+// each CU (two wavefronts per SIMD) and cover each other's copies and
+// softmax.  Double-buffered stages at one wavefront per SIMD (360 VGPRs,
+// 106-145 KiB of LDS) measured 14% slower on the whole backward.
 #include "common.h"
 #include "../launch.h"
 
@@ -162,6 +166,19 @@ __device__ __forceinline__ bf16x8_t pack_step(const f32x16_t (&T)[2], int st) {
   return __builtin_bit_cast(bf16x8_t, w);
 }
 
+// The workgroup's block list in LDS, one 16-bit word per entry (the block, or
+// kNoBlock for an entry outside [0, nb)), so a stage reads its block from LDS
+// instead of waiting on a scalar load from memory.
+constexpr uint16_t kNoBlock = 0xFFFF;
+constexpr int kMaxList = 4096;
+
+__device__ __forceinline__ void stage_list(const int32_t* __restrict__ idx, int cnt, int nb, uint16_t* list_s) {
+  for (int i = threadIdx.x; i < cnt; i += blockDim.x) {
+    const int v = idx[i];
+    list_s[i] = (v >= 0 && v < nb) ? (uint16_t)v : kNoBlock;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // rows [BH][Npad][D] bf16 -> transposed tiles [BH][nb][D][BLK] (column
 // tile_col(t) holds token J*BLK + t); tokens >= N are zero.  One workgroup per
@@ -241,16 +258,17 @@ __global__ __launch_bounds__(kTrThreads) void transpose_lists_kernel(const int32
 // ---------------------------------------------------------------------------
 // dQ.  Stage u of the list: entry u / kSubs, half u % kSubs (64 keys).
 template <int D, int BLK>
-__global__ __launch_bounds__(BLK / 32 * 64) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dq_kernel(
     const __bf16* __restrict__ q_r, const __bf16* __restrict__ k_r, const __bf16* __restrict__ v_r,
     const __bf16* __restrict__ o_r, const __bf16* __restrict__ do_r, const float* __restrict__ lse,
     const __bf16* __restrict__ k_t, const int32_t* __restrict__ kv_count, const int32_t* __restrict__ kv_idx,
     float* __restrict__ dq, float* __restrict__ dbuf, int Hh, int N, int Npad, int nb, float sl2, float scale) {
   using C = BwdCfg<D>;
   constexpr int W = BLK / 32, kSubs = BLK / 64;
-  __shared__ __attribute__((aligned(1024))) char Ks[C::kRowBytes];
-  __shared__ __attribute__((aligned(1024))) char Vs[C::kRowBytes];
-  __shared__ __attribute__((aligned(1024))) char Kts[C::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char Ks0[C::kRowBytes];
+  __shared__ __attribute__((aligned(1024))) char Vs0[C::kRowBytes];
+  __shared__ __attribute__((aligned(1024))) char Kts0[C::kTileBytes];
+
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int slot = xcd_remap(blockIdx.x, gridDim.x);
@@ -296,15 +314,26 @@ __global__ __launch_bounds__(BLK / 32 * 64) void attn_bwd_dq_kernel(
   StageCopies<D, BLK, W> cp;
   cp.init(wave, lane);
 
-  for (int u = 0; u < cnt * kSubs; ++u) {
-    const int J = __builtin_amdgcn_readfirstlane(idx[u / kSubs]), h = u % kSubs;
-    if (J < 0 || J >= nb) continue;   // invalid entries are skipped, as the forward does
+  // Stage u: list entry u / kSubs, 64-key half u % kSubs.  An invalid entry
+  // (outside [0, nb)) copies block 0 and computes nothing, as the forward
+  // skips it.
+  const int U = cnt * kSubs;
+  __shared__ uint16_t list_s[kMaxList];
+  stage_list(idx, cnt, nb, list_s);
+  __syncthreads();
+  auto block_of = [&](int u) { return __builtin_amdgcn_readfirstlane((int)list_s[u / kSubs]); };
+  auto issue = [&](int u, char* kb, char* vb, char* tb) {
+    const int J0 = block_of(u), h = u % kSubs;
+    const int J = J0 == kNoBlock ? 0 : J0;
     const int key0 = J * BLK + h * 64;
-    cp.rows(rk, (uint32_t)key0 * (uint32_t)(D * 2), Ks);
-    cp.rows(rv, (uint32_t)key0 * (uint32_t)(D * 2), Vs);
-    cp.tiles(rkt, ((uint32_t)J * (uint32_t)(D * BLK) + (uint32_t)(h * 64)) * 2u, Kts);
-    wait_dma();
-    __syncthreads();
+    cp.rows(rk, (uint32_t)key0 * (uint32_t)(D * 2), kb);
+    cp.rows(rv, (uint32_t)key0 * (uint32_t)(D * 2), vb);
+    cp.tiles(rkt, ((uint32_t)J * (uint32_t)(D * BLK) + (uint32_t)(h * 64)) * 2u, tb);
+  };
+  auto compute = [&](int u, const char* kb, const char* vb, const char* tb) {
+    const int J = block_of(u), h = u % kSubs;
+    if (J == kNoBlock) return;
+    const int key0 = J * BLK + h * 64;
     f32x16_t S[2], dP[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -312,8 +341,8 @@ __global__ __launch_bounds__(BLK / 32 * 64) void attn_bwd_dq_kernel(
       dP[t] = f32x16_t{};
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        S[t] = mfma(read_rows<D>(Ks, l32, g, t, kk), qreg[kk], S[t]);
-        dP[t] = mfma(read_rows<D>(Vs, l32, g, t, kk), doreg[kk], dP[t]);
+        S[t] = mfma(read_rows<D>(kb, l32, g, t, kk), qreg[kk], S[t]);
+        dP[t] = mfma(read_rows<D>(vb, l32, g, t, kk), doreg[kk], dP[t]);
       }
     }
     // dS^T = P^T (dP^T - D); keys >= N have P = 0
@@ -329,10 +358,16 @@ __global__ __launch_bounds__(BLK / 32 * 64) void attn_bwd_dq_kernel(
     }
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      const bf16x8_t b = pack_step(S, st);
+      const bf16x8_t bq = pack_step(S, st);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) acc[dt] = mfma(read_tiles<D>(Kts, l32, g, dt, st), b, acc[dt]);
+      for (int dt = 0; dt < D / 32; ++dt) acc[dt] = mfma(read_tiles<D>(tb, l32, g, dt, st), bq, acc[dt]);
     }
+  };
+  for (int u = 0; u < U; ++u) {
+    issue(u, Ks0, Vs0, Kts0);
+    wait_dma();
+    __syncthreads();
+    compute(u, Ks0, Vs0, Kts0);
     __syncthreads();
   }
 
@@ -356,7 +391,7 @@ __global__ __launch_bounds__(BLK / 32 * 64) void attn_bwd_dq_kernel(
 // dK, dV.  Stage u of the key block's query list: entry u / kSubs, half u % kSubs
 // (64 queries, processed as two sub-tiles of 32 to bound the registers).
 template <int D, int BLK>
-__global__ __launch_bounds__(BLK / 32 * 64) void attn_bwd_dkdv_kernel(
+__global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dkdv_kernel(
     const __bf16* __restrict__ q_r, const __bf16* __restrict__ k_r, const __bf16* __restrict__ v_r,
     const __bf16* __restrict__ do_r, const float* __restrict__ lse, const float* __restrict__ dbuf,
     const __bf16* __restrict__ q_t, const __bf16* __restrict__ do_t, const int32_t* __restrict__ kvT_count,
@@ -364,12 +399,12 @@ __global__ __launch_bounds__(BLK / 32 * 64) void attn_bwd_dkdv_kernel(
     int nb, float sl2, float scale) {
   using C = BwdCfg<D>;
   constexpr int W = BLK / 32, kSubs = BLK / 64;
-  __shared__ __attribute__((aligned(1024))) char Qs[C::kRowBytes];
-  __shared__ __attribute__((aligned(1024))) char dOs[C::kRowBytes];
-  __shared__ __attribute__((aligned(1024))) char Qts[C::kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char dOts[C::kTileBytes];
-  __shared__ __attribute__((aligned(16))) float lse_s[64];
-  __shared__ __attribute__((aligned(16))) float d_s[64];
+  __shared__ __attribute__((aligned(1024))) char Qs0[C::kRowBytes];
+  __shared__ __attribute__((aligned(1024))) char dOs0[C::kRowBytes];
+  __shared__ __attribute__((aligned(1024))) char Qts0[C::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char dOts0[C::kTileBytes];
+
+  __shared__ __attribute__((aligned(16))) float ld_s[1][128];   // lse (log2) of the stage's 64 queries, then D
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int slot = xcd_remap(blockIdx.x, gridDim.x);
@@ -407,58 +442,84 @@ __global__ __launch_bounds__(BLK / 32 * 64) void attn_bwd_dkdv_kernel(
   StageCopies<D, BLK, W> cp;
   cp.init(wave, lane);
 
-  for (int u = 0; u < cnt * kSubs; ++u) {
-    const int I = __builtin_amdgcn_readfirstlane(idx[u / kSubs]), h = u % kSubs;
-    if (I < 0 || I >= nb) continue;
+  // Stage u: query-block entry u / kSubs, 64-query half u % kSubs.  An invalid
+  // entry copies block 0 and computes nothing.
+  const int U = cnt * kSubs;
+  __shared__ uint16_t list_s[kMaxList];
+  stage_list(idx, cnt, nb, list_s);
+  __syncthreads();
+  auto block_of = [&](int u) { return __builtin_amdgcn_readfirstlane((int)list_s[u / kSubs]); };
+  // The lse / D loads go first: vector loads retire in order, so their LDS
+  // write does not wait for the tile copies issued after them.
+  auto issue = [&](int u, char* qb, char* ob, char* qtb, char* otb, float* ls) {
+    const int I0 = block_of(u), h = u % kSubs;
+    const int I = I0 == kNoBlock ? 0 : I0;
     const int qs0 = I * BLK + h * 64;
-    cp.rows(rq, (uint32_t)qs0 * (uint32_t)(D * 2), Qs);
-    cp.rows(rdo, (uint32_t)qs0 * (uint32_t)(D * 2), dOs);
-    const uint32_t toffs = ((uint32_t)I * (uint32_t)(D * BLK) + (uint32_t)(h * 64)) * 2u;
-    cp.tiles(rqt, toffs, Qts);
-    cp.tiles(rdot, toffs, dOts);
+    float lv = 0.f, dv0 = 0.f;
     if (threadIdx.x < 64) {
       const int qq = qs0 + threadIdx.x;
       const bool ok = qq < N;
-      lse_s[threadIdx.x] = ok ? lse[rowbase + qq] * kLog2e : INFINITY;   // +inf: P = 0 for rows >= N
-      d_s[threadIdx.x] = ok ? dbuf[rowbase + qq] : 0.f;
+      lv = ok ? lse[rowbase + qq] * kLog2e : INFINITY;   // +inf: P = 0 for rows >= N
+      dv0 = ok ? dbuf[rowbase + qq] : 0.f;
     }
-    wait_dma();
-    __syncthreads();
-    f32x16_t P[2], dS[2];
+    cp.rows(rq, (uint32_t)qs0 * (uint32_t)(D * 2), qb);
+    cp.rows(rdo, (uint32_t)qs0 * (uint32_t)(D * 2), ob);
+    const uint32_t toffs = ((uint32_t)I * (uint32_t)(D * BLK) + (uint32_t)(h * 64)) * 2u;
+    cp.tiles(rqt, toffs, qtb);
+    cp.tiles(rdot, toffs, otb);
+    if (threadIdx.x < 64) {
+      ls[threadIdx.x] = lv;
+      ls[64 + threadIdx.x] = dv0;
+    }
+  };
+  auto compute = [&](int u, const char* qb, const char* ob, const char* qtb, const char* otb, const float* ls) {
+    const int I = block_of(u);
+    if (I == kNoBlock) return;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       f32x16_t S = f32x16_t{}, dP = f32x16_t{};
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        S = mfma(read_rows<D>(Qs, l32, g, t, kk), kreg[kk], S);
-        dP = mfma(read_rows<D>(dOs, l32, g, t, kk), vreg[kk], dP);
+        S = mfma(read_rows<D>(qb, l32, g, t, kk), kreg[kk], S);
+        dP = mfma(read_rows<D>(ob, l32, g, t, kk), vreg[kk], dP);
       }
-      // rows of S are queries 32 t + acc_row(v, g): lse and D from LDS, 4 at a time
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int r0 = 32 * t + 8 * a + 4 * g;
-        const float4 l4 = *reinterpret_cast<const float4*>(lse_s + r0);
-        const float4 d4 = *reinterpret_cast<const float4*>(d_s + r0);
+        const float4 l4 = *reinterpret_cast<const float4*>(ls + r0);
+        const float4 d4 = *reinterpret_cast<const float4*>(ls + 64 + r0);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
         const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int v = 4 * a + j;
           const float p = fast_exp2(__builtin_fmaf(S[v], sl2, -lv[j]));
-          P[t][v] = p;
-          dS[t][v] = p * (dP[v] - dv4[j]);
+          S[v] = p;
+          dP[v] = p * (dP[v] - dv4[j]);
+        }
+      }
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        const int o = hs * 8, st = 2 * t + hs;
+        uint4 wp, ws;
+        wp.x = cvt_pk(S[o + 0], S[o + 1]); wp.y = cvt_pk(S[o + 2], S[o + 3]);
+        wp.z = cvt_pk(S[o + 4], S[o + 5]); wp.w = cvt_pk(S[o + 6], S[o + 7]);
+        ws.x = cvt_pk(dP[o + 0], dP[o + 1]); ws.y = cvt_pk(dP[o + 2], dP[o + 3]);
+        ws.z = cvt_pk(dP[o + 4], dP[o + 5]); ws.w = cvt_pk(dP[o + 6], dP[o + 7]);
+        const bf16x8_t bp = __builtin_bit_cast(bf16x8_t, wp), bs = __builtin_bit_cast(bf16x8_t, ws);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          dva[dt] = mfma(read_tiles<D>(otb, l32, g, dt, st), bp, dva[dt]);
+          dka[dt] = mfma(read_tiles<D>(qtb, l32, g, dt, st), bs, dka[dt]);
         }
       }
     }
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const bf16x8_t bp = pack_step(P, st), bs = pack_step(dS, st);
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        dva[dt] = mfma(read_tiles<D>(dOts, l32, g, dt, st), bp, dva[dt]);
-        dka[dt] = mfma(read_tiles<D>(Qts, l32, g, dt, st), bs, dka[dt]);
-      }
-    }
+  };
+  for (int u = 0; u < U; ++u) {
+    issue(u, Qs0, dOs0, Qts0, dOts0, ld_s[0]);
+    wait_dma();
+    __syncthreads();
+    compute(u, Qs0, dOs0, Qts0, dOts0, ld_s[0]);
     __syncthreads();
   }
 
