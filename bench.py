@@ -5,7 +5,8 @@ Workload: the Wan2.1-1.3B-shaped self-attention layer -- batch 1, 12 heads,
 head dim 128, bf16, latent 21 x 30 x 52 = 32,760 tokens (padded to 32,768),
 smooth-field Q/K (sigma 4) + 0.3 noise, iid V; b = 128, k = 16, Gilbert-curve
 reorder, threshold tau = 0.90 (tau = 0.95 is measured as well and reported
-under "extra").  Synthetic inputs stand in for the model's activations.
+under "extra", and so is the backward of the attention at tau = 0.90).
+Synthetic inputs stand in for the model's activations.
 
 A step is one pass of the whole hot path over that batch, all on one stream:
 reorder K, V -> estimate_blocks (sampled Q rows read in token order) ->
@@ -49,7 +50,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--tau", type=float, default=0.90)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the tau=0.95 measurement")
+    ap.add_argument("--no-extra", action="store_true", help="skip the tau=0.95 and backward measurements")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -117,6 +118,53 @@ def stage_times(layer, q, k, v, out, tau, steps, torch):
     torch.cuda.synchronize()
     return {n: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps
             for i, n in enumerate(names)}
+
+
+def backward_leg(layer, cfg, qd, vd, steps, warmup, torch):
+    """The backward of the attention (plain ASA) on the same layer and mask: the key-to-query lists
+    and the dQ / dK / dV kernels, timed back to back between two HIP events.  Q, V (rows) and dO are
+    reordered and the forward's output and lse computed beforehand, outside the timed region."""
+    import numpy as np
+    from dynamic_block_sparse_gilbert_amd import ops
+    sp = layer.spec
+    q_r = ops.reorder(qd, layer.perm, sp.Npad, sp.b, "rows")
+    v_r = ops.reorder(vd, layer.perm, sp.Npad, sp.b, "rows")
+    gen = torch.Generator(device=qd.device).manual_seed(7)
+    do = torch.randn(qd.shape, generator=gen, device=qd.device, dtype=torch.float32).to(torch.bfloat16)
+    do_r = ops.reorder(do, layer.perm, sp.Npad, sp.b, "rows")
+    o_r, lse = ops.sparse_attn_fwd(q_r, layer.k_r, layer.v_t, sp.N, sp.b, sp.scale, layer.kv_count,
+                                   layer.kv_idx, want_lse=True)
+    ws = torch.empty(ops.attn_bwd_workspace_bytes(1, sp.heads, sp.Npad, sp.d), dtype=torch.uint8,
+                     device=qd.device)
+
+    def one():
+        kc, ki = ops.transpose_lists(layer.kv_count, layer.kv_idx)
+        ops.sparse_attn_bwd(q_r, layer.k_r, v_r, o_r, do_r, lse, sp.N, sp.b, sp.scale, layer.kv_count,
+                            layer.kv_idx, kc, ki, workspace=ws)
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        one()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    cnt, idx = layer.kv_count.cpu().numpy(), layer.kv_idx.cpu().numpy()
+    pairs = kept_pair_tokens(cnt, idx, sp.N, sp.b)
+    alg = 10.0 * sp.d * pairs        # five products over the kept pairs (S, dP, dV, dQ, dK)
+    executed = 14.0 * sp.d * pairs   # S and dP are computed in both kernels
+    return {
+        "ms": round(ms, 4),
+        "what": "dbs_transpose_lists + dbs_sparse_attn_bwd (rows -> tiles copies, dQ, dK/dV kernels), "
+                "tau 0.9 mask of the timed layer",
+        "algorithmic_flop": alg,
+        "executed_flop": executed,
+        "algorithmic_tflops": round(alg / (ms * 1e-3) / 1e12, 1),
+        "executed_tflops": round(executed / (ms * 1e-3) / 1e12, 1),
+        "executed_frac_of_bf16_peak": round(executed / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+    }
 
 
 def cpu_baseline(cfg, q, k, v, perm, tau, heads=2):
@@ -233,6 +281,9 @@ def main():
             "stages_ms": {kk: round(vv, 4) for kk, vv in stage95.items()},
             "attn_executed_tflops": round(ef95 / (attn95 * 1e-3) / 1e12, 2),
         }
+        layer.forward(qd, kd, vd, out=out, tau=args.tau)   # the timed mask again
+        torch.cuda.synchronize()
+        extra["backward"] = backward_leg(layer, cfg, qd, vd, max(5, args.steps // 5), 3, torch)
 
     line = {
         "metric": "ms/layer + dense-equiv TFLOP/s, block-sparse attn at 90-95% sparsity, 1 GPU",
