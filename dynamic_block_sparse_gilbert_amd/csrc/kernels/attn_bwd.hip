@@ -11,9 +11,8 @@
 // J, the query blocks whose list holds J.
 //
 // Launches:
-//   transpose_lists: one workgroup per (batch, head); entries scattered with
-//     LDS atomics, then every key block's list sorted by query block, so the
-//     result does not depend on the order of the atomics.
+//   transpose_lists: a bit matrix (query block x key block) per group of 32
+//     key blocks in LDS, read out in ascending query block.
 //   rows_to_tiles (x3): Q, dO and K rows -> transposed b-token tiles (d-major,
 //     tokens in the order the MFMA k index wants, rows >= N zero), the A
 //     operands of the products that contract over tokens.
@@ -211,47 +210,49 @@ __global__ __launch_bounds__((D / 8) * (BLK / 8)) void rows_to_tiles_kernel(cons
 }
 
 // ---------------------------------------------------------------------------
-// Key-to-query lists of one (batch, head) per workgroup.
+// Key-to-query lists.  One workgroup per (32 key blocks, batch x head): it marks
+// in an LDS bit matrix, for each of its key blocks J, the query blocks I whose
+// list holds J (every list entry of the head, one wavefront per row), then each
+// of its threads reads one J's row of bits in ascending I.  The result is the
+// same whatever order the marks arrive in.
 constexpr int kTrThreads = 1024;
+constexpr int kTrJ = 32;          // key blocks per workgroup
 constexpr int kTrMaxNb = 4096;
 
 __global__ __launch_bounds__(kTrThreads) void transpose_lists_kernel(const int32_t* __restrict__ kv_count,
                                                                      const int32_t* __restrict__ kv_idx, int nb,
                                                                      int32_t* __restrict__ kvT_count,
                                                                      int32_t* __restrict__ kvT_idx) {
-  __shared__ int cnt[kTrMaxNb];
-  const int bh = blockIdx.x, tid = threadIdx.x;
-  const int32_t* crow = kv_count + (int64_t)bh * nb;
-  const int32_t* irow = kv_idx + (int64_t)bh * nb * nb;
-  int32_t* tout = kvT_idx + (int64_t)bh * nb * nb;
-  for (int J = tid; J < nb; J += kTrThreads) cnt[J] = 0;
+  __shared__ uint32_t bits[kTrJ][kTrMaxNb / 32];
+  __shared__ uint16_t cnt_s[kTrMaxNb];
+  const int J0 = blockIdx.x * kTrJ, bh = blockIdx.y, tid = threadIdx.x;
+  const int words = (nb + 31) / 32;
+  for (int i = tid; i < kTrJ * words; i += kTrThreads) bits[i / words][i % words] = 0u;
+  for (int I = tid; I < nb; I += kTrThreads) cnt_s[I] = (uint16_t)min(max(kv_count[(int64_t)bh * nb + I], 0), nb);
   __syncthreads();
-  for (int I = tid; I < nb; I += kTrThreads) {
-    const int c = min(max(crow[I], 0), nb);
-    for (int pos = 0; pos < c; ++pos) {
-      const int J = irow[(int64_t)I * nb + pos];
-      if (J >= 0 && J < nb) {
-        const int at = atomicAdd(&cnt[J], 1);
-        if (at < nb) tout[(int64_t)J * nb + at] = I;
-      }
+  // one wavefront per list row, its lanes over the row's entries
+  const int32_t* irow = kv_idx + (int64_t)bh * nb * nb;
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int I = wave; I < nb; I += kTrThreads / 64) {
+    const int c = cnt_s[I];
+    for (int pos = lane; pos < c; pos += 64) {
+      const int J = irow[(int64_t)I * nb + pos] - J0;
+      if (J >= 0 && J < kTrJ && J0 + J < nb) atomicOr(&bits[J][I >> 5], 1u << (I & 31));
     }
   }
   __syncthreads();
-  // Sort each key block's list (insertion sort; lists are short), so the
-  // result is the ascending order of query blocks whatever the atomics did.
-  for (int J = tid; J < nb; J += kTrThreads) {
-    const int c = min(cnt[J], nb);
-    kvT_count[(int64_t)bh * nb + J] = c;
-    int32_t* l = tout + (int64_t)J * nb;
-    for (int i = 1; i < c; ++i) {
-      const int v = l[i];
-      int j = i - 1;
-      while (j >= 0 && l[j] > v) {
-        l[j + 1] = l[j];
-        --j;
+  if (tid < kTrJ && J0 + tid < nb) {
+    const int J = J0 + tid;
+    int32_t* out = kvT_idx + ((int64_t)bh * nb + J) * nb;
+    int c = 0;
+    for (int w = 0; w < words; ++w) {
+      uint32_t m = bits[tid][w];
+      while (m) {
+        out[c++] = 32 * w + __builtin_ctz(m);
+        m &= m - 1;
       }
-      l[j + 1] = v;
     }
+    kvT_count[(int64_t)bh * nb + J] = c;
   }
 }
 
@@ -584,8 +585,8 @@ size_t attn_bwd_workspace_bytes(int B, int Hh, int Npad, int d) {
 }
 
 hipError_t launch_transpose_lists(const TransposeListsArgs& a) {
-  hipLaunchKernelGGL(transpose_lists_kernel, dim3((unsigned)(a.B * a.Hh)), dim3(kTrThreads), 0, a.stream,
-                     a.kv_count, a.kv_idx, a.nb, a.kvT_count, a.kvT_idx);
+  hipLaunchKernelGGL(transpose_lists_kernel, dim3((unsigned)((a.nb + kTrJ - 1) / kTrJ), (unsigned)(a.B * a.Hh)),
+                     dim3(kTrThreads), 0, a.stream, a.kv_count, a.kv_idx, a.nb, a.kvT_count, a.kvT_idx);
   return hipGetLastError();
 }
 

@@ -271,8 +271,9 @@ dbs_status dbs_sparse_attn_fwd_tok(const void* q, dbs_dtype q_dt, int64_t qsb, i
 /* Key-to-query lists: for every (b, h, J), the query blocks I whose list
  * (kv_count / kv_idx as written by dbs_build_mask) holds J, in ascending
  * order.  kv_count entries are clamped to [0, nb] and kv_idx entries outside
- * [0, nb) skipped, as the attention does; lists are expected to hold distinct
- * blocks (a repeated entry is listed again).  kvT_count [B, Hh, nb] int32,
+ * [0, nb) skipped, as the attention does; a row's list is taken as a set
+ * (a repeated entry counts once; dbs_build_mask never repeats one).
+ * kvT_count [B, Hh, nb] int32,
  * kvT_idx [B, Hh, nb, nb] int32 (entries past kvT_count unspecified).
  * UNSUPPORTED for nb > 4096. */
 dbs_status dbs_transpose_lists(const int32_t* kv_count, const int32_t* kv_idx, int B, int Hh, int nb,

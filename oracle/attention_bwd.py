@@ -71,19 +71,20 @@ def transpose_lists(kv_count: np.ndarray, kv_idx: np.ndarray):
 
     kv_count [nb], kv_idx [nb, nb] (the first kv_count[I] entries of row I are
     the key blocks of query block I; counts are clamped into [0, nb] and entries
-    outside [0, nb) skipped, as the attention does).  Returns (kvT_count [nb],
-    kvT_idx [nb, nb]): row J lists, in ascending order of (I, position), the
-    query blocks I whose list holds J; unused entries are -1.
+    outside [0, nb) skipped, as the attention does).  A row's list is a set of
+    blocks, as in masked_attention_bwd: a repeated entry counts once.  Returns
+    (kvT_count [nb], kvT_idx [nb, nb]): row J lists, ascending, the query blocks
+    I whose list holds J; unused entries are -1.
     """
     nb = kv_count.shape[0]
-    cnt = np.zeros(nb, dtype=np.int32)
-    idx = np.full((nb, nb), -1, dtype=np.int32)
+    holds = [set() for _ in range(nb)]
     for I in range(nb):
         c = min(max(int(kv_count[I]), 0), nb)
-        for pos in range(c):
-            J = int(kv_idx[I, pos])
+        for J in kv_idx[I, :c].tolist():
             if 0 <= J < nb:
-                if cnt[J] < nb:
-                    idx[J, cnt[J]] = I
-                cnt[J] += 1
-    return np.minimum(cnt, nb).astype(np.int32), idx
+                holds[J].add(I)
+    cnt = np.array([len(h) for h in holds], dtype=np.int32)
+    idx = np.full((nb, nb), -1, dtype=np.int32)
+    for J in range(nb):
+        idx[J, :cnt[J]] = sorted(holds[J])
+    return cnt, idx

@@ -129,10 +129,20 @@ def test_transpose_lists_brute_force(nb, seed):
             idx[I, 0] = nb + 4            # an invalid entry is skipped
     tc, ti = transpose_lists(cnt, idx)
     for J in range(nb):
-        want = [I for I in range(nb) for pos in range(min(max(int(cnt[I]), 0), nb)) if idx[I, pos] == J]
+        want = [I for I in range(nb) if J in idx[I, :min(max(int(cnt[I]), 0), nb)].tolist()]
         assert tc[J] == len(want)
         assert ti[J, :tc[J]].tolist() == want          # ascending I
         assert (ti[J, tc[J]:] == -1).all()
+    # a repeated entry counts once, as in the attention oracle's sets
+    if nb > 1:
+        dup = idx.copy()
+        c0 = min(max(int(cnt[0]), 0), nb)
+        if c0 >= 2:
+            dup[0, 1] = dup[0, 0]
+            dc, di = transpose_lists(cnt, dup)
+            J = int(dup[0, 0])
+            if 0 <= J < nb:
+                assert di[J, :dc[J]].tolist().count(0) == 1
     # transposing back gives every row's set of valid blocks
     bc, bi = transpose_lists(tc, ti)
     for I in range(nb):
