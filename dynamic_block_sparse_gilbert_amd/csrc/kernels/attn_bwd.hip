@@ -17,22 +17,23 @@
 //     tokens in the order the MFMA k index wants, rows >= N zero), the A
 //     operands of the products that contract over tokens.
 //   dq: one workgroup per (batch, head, query block), 32 query rows per
-//     wavefront, over the block's kept key blocks in stages of 64 keys:
+//     wavefront, over the block's kept key blocks in stages of 32 keys:
 //       S^T = K Q^T, dP^T = V dO^T (Q^T, dO^T in VGPRs), P^T, dS^T in the
 //       lane's registers (each lane holds one query: lse and D are scalars),
 //       dQ^T += K^T dS^T.  It also writes D for the next launch.
 //   dkdv: one workgroup per (batch, head, key block), 32 keys per wavefront,
-//     over the query blocks that keep it, in stages of 64 queries taken as two
-//     sub-tiles of 32 (each finished before the next, to bound the registers):
+//     over the query blocks that keep it, in stages of 32 queries:
 //     S = Q K^T, dP = dO V^T (K^T, V^T in VGPRs), dV^T += dO^T P,
 //     dK^T += Q^T dS.
 // All products are bf16 MFMA 32x32x16 with fp32 accumulation; P and dS are
 // rounded to bf16 for the second product.  Stage data are copied global -> LDS
-// by the buffer form of the DMA path into row-padded LDS, one buffer set per
-// workgroup, and both kernels are held to 256 VGPRs: two workgroups then share
-// each CU (two wavefronts per SIMD) and cover each other's copies and
-// softmax.  Double-buffered stages at one wavefront per SIMD (360 VGPRs,
-// 106-145 KiB of LDS) measured 14% slower on the whole backward.
+// by the buffer form of the DMA path into row-padded LDS, double-buffered (the
+// copies of stage u + 1 issued right after the barrier that opens stage u),
+// and both kernels are held to 256 VGPRs: two workgroups then share each CU
+// (two wavefronts per SIMD).  64-token stages double-buffered at one
+// wavefront per SIMD (360 VGPRs, 106-145 KiB of LDS) measured 14% slower on
+// the whole backward; 64-token stages single-buffered at two per SIMD ran as
+// fast as these.
 #include "common.h"
 #include "../launch.h"
 
@@ -69,28 +70,30 @@ __device__ __forceinline__ void copy16_lds(__amdgpu_buffer_rsrc_t r, char* lds, 
 // next product.
 __device__ __forceinline__ int tile_col(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
 
-// Stage layouts in LDS (64 tokens per stage).
-template <int D>
+// Stage layouts in LDS (KT tokens per stage), each a whole number of 1 KiB
+// copy instructions (a rows stage of 32 tokens leaves a spare half KiB that
+// the surplus lanes of its last copy fill).
+template <int D, int KT>
 struct BwdCfg {
-  static constexpr int kT = 64;                    // tokens per stage
-  static constexpr int kRowU = D / 8 + 1;          // rows stage: 64 rows of D, padded by one 16-byte unit
+  static constexpr int kT = KT;
+  static constexpr int kRowU = D / 8 + 1;          // rows stage: KT rows of D, padded by one 16-byte unit
   static constexpr int kRowStride = kRowU * 16;
-  static constexpr int kRowBytes = kT * kRowStride;
-  static constexpr int kRowInstr = kRowBytes / 1024;
-  static constexpr int kTileU = kT / 8 + 1;        // tiles stage: D rows of 64 tokens, padded by one unit
+  static constexpr int kRowInstr = (KT * kRowU + 63) / 64;
+  static constexpr int kRowBytes = kRowInstr * 1024;
+  static constexpr int kTileU = KT / 8 + 1;        // tiles stage: D rows of KT tokens, padded by one unit
   static constexpr int kTileStride = kTileU * 16;
-  static constexpr int kTileBytes = D * kTileStride;
-  static constexpr int kTileInstr = kTileBytes / 1024;
-  static_assert(kRowBytes % 1024 == 0 && kTileBytes % 1024 == 0, "stages must be whole DMA instructions");
+  static constexpr int kTileInstr = (D * kTileU + 63) / 64;
+  static constexpr int kTileBytes = kTileInstr * 1024;
 };
 
 // Per-lane source offsets (elements) of the padded copies: LDS byte 1024 n +
 // 16 lane of a stage holds padded unit p = 64 n + lane, i.e. row p / rowU,
 // unit p % rowU (the pad unit re-reads the row's last unit).  Surplus
-// instructions of a wavefront repeat the last one.
-template <int D, int BLK, int W>
+// instructions of a wavefront repeat the last one; surplus lanes of a rows
+// stage read the rows just past it (out of range: zero) into the spare bytes.
+template <int D, int BLK, int W, int KT>
 struct StageCopies {
-  using C = BwdCfg<D>;
+  using C = BwdCfg<D, KT>;
   static constexpr int kRowPer = (C::kRowInstr + W - 1) / W;
   static constexpr int kTilePer = (C::kTileInstr + W - 1) / W;
   uint32_t roff[kRowPer], toff[kTilePer];
@@ -113,7 +116,6 @@ struct StageCopies {
       toff[i] = (uint32_t)(row * BLK + c * 8) * 2u;
     }
   }
-  // 64 rows starting at byte offset soff of a rows array.
   __device__ __forceinline__ void rows(__amdgpu_buffer_rsrc_t r, uint32_t soff, char* buf) const {
 #pragma unroll
     for (int i = 0; i < kRowPer; ++i) {
@@ -121,7 +123,6 @@ struct StageCopies {
       copy16_lds(r, buf + 1024 * n, roff[i], soff);
     }
   }
-  // Columns 64 h .. 64 h + 63 of every d-row of one transposed tile at soff.
   __device__ __forceinline__ void tiles(__amdgpu_buffer_rsrc_t r, uint32_t soff, char* buf) const {
 #pragma unroll
     for (int i = 0; i < kTilePer; ++i) {
@@ -131,18 +132,29 @@ struct StageCopies {
   }
 };
 
-// MFMA operand reads (16 bytes per lane): rows stage, row 32 t + l32, k step kk
+// MFMA operand reads (16 bytes per lane): rows stage, row l32, k step kk
 // (elements 16 kk + 8 g ..); tiles stage, d-row 32 dt + l32, token step st
 // (stored columns 16 st + 8 g ..).
-template <int D>
-__device__ __forceinline__ bf16x8_t read_rows(const char* buf, int l32, int g, int t, int kk) {
-  using C = BwdCfg<D>;
-  return *reinterpret_cast<const bf16x8_t*>(buf + (32 * t + l32) * C::kRowStride + 16 * g + kk * 32);
+template <class C>
+__device__ __forceinline__ bf16x8_t read_rows(const char* buf, int l32, int g, int kk) {
+  return *reinterpret_cast<const bf16x8_t*>(buf + l32 * C::kRowStride + 16 * g + kk * 32);
 }
-template <int D>
+template <class C>
 __device__ __forceinline__ bf16x8_t read_tiles(const char* buf, int l32, int g, int dt, int st) {
-  using C = BwdCfg<D>;
   return *reinterpret_cast<const bf16x8_t*>(buf + (32 * dt + l32) * C::kTileStride + 16 * g + st * 32);
+}
+
+// B operand of a product contracting over the 32 rows of one accumulator tile
+// T, 16-row step st: the lane's 8 values of that step, in the row order
+// tile_col stores its columns.
+__device__ __forceinline__ bf16x8_t pack_half(const f32x16_t& T, int st) {
+  const int o = st * 8;
+  uint4 w;
+  w.x = cvt_pk(T[o + 0], T[o + 1]);
+  w.y = cvt_pk(T[o + 2], T[o + 3]);
+  w.z = cvt_pk(T[o + 4], T[o + 5]);
+  w.w = cvt_pk(T[o + 6], T[o + 7]);
+  return __builtin_bit_cast(bf16x8_t, w);
 }
 
 __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
@@ -152,24 +164,10 @@ __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
 // Row r of a 32 x 32 accumulator tile held in element v of lane half g.
 __device__ __forceinline__ int acc_row(int v, int g) { return (v >> 2) * 8 + 4 * g + (v & 3); }
 
-// B operand of a product contracting over the rows of two 32-row accumulator
-// tiles T[0], T[1] (64 rows = 4 steps of 16): step st packs the 8 values of the
-// lane in that step, in the row order tile_col stores its columns.
-__device__ __forceinline__ bf16x8_t pack_step(const f32x16_t (&T)[2], int st) {
-  const int t = st >> 1, o = (st & 1) * 8;
-  uint4 w;
-  w.x = cvt_pk(T[t][o + 0], T[t][o + 1]);
-  w.y = cvt_pk(T[t][o + 2], T[t][o + 3]);
-  w.z = cvt_pk(T[t][o + 4], T[t][o + 5]);
-  w.w = cvt_pk(T[t][o + 6], T[t][o + 7]);
-  return __builtin_bit_cast(bf16x8_t, w);
-}
-
-// The workgroup's block list in LDS, one 16-bit word per entry (the block, or
-// kNoBlock for an entry outside [0, nb)), so a stage reads its block from LDS
-// instead of waiting on a scalar load from memory.
+// The workgroup's block list in LDS (dynamic LDS sized by nb), one 16-bit word
+// per entry (the block, or kNoBlock for an entry outside [0, nb)), so a stage
+// reads its block from LDS instead of waiting on a scalar load from memory.
 constexpr uint16_t kNoBlock = 0xFFFF;
-constexpr int kMaxList = 4096;
 
 __device__ __forceinline__ void stage_list(const int32_t* __restrict__ idx, int cnt, int nb, uint16_t* list_s) {
   for (int i = threadIdx.x; i < cnt; i += blockDim.x) {
@@ -257,19 +255,26 @@ __global__ __launch_bounds__(kTrThreads) void transpose_lists_kernel(const int32
 }
 
 // ---------------------------------------------------------------------------
-// dQ.  Stage u of the list: entry u / kSubs, half u % kSubs (64 keys).
+// Stages of 32 tokens, double-buffered: the copies of stage u + 1 are issued
+// right after the barrier that opens stage u and land while it computes.
+constexpr int kKT = 32;
+
+// dQ.  Stage u: list entry u / kSubs, 32-key part u % kSubs.
 template <int D, int BLK>
 __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dq_kernel(
     const __bf16* __restrict__ q_r, const __bf16* __restrict__ k_r, const __bf16* __restrict__ v_r,
     const __bf16* __restrict__ o_r, const __bf16* __restrict__ do_r, const float* __restrict__ lse,
     const __bf16* __restrict__ k_t, const int32_t* __restrict__ kv_count, const int32_t* __restrict__ kv_idx,
     float* __restrict__ dq, float* __restrict__ dbuf, int Hh, int N, int Npad, int nb, float sl2, float scale) {
-  using C = BwdCfg<D>;
-  constexpr int W = BLK / 32, kSubs = BLK / 64;
+  using C = BwdCfg<D, kKT>;
+  constexpr int W = BLK / 32, kSubs = BLK / kKT;
   __shared__ __attribute__((aligned(1024))) char Ks0[C::kRowBytes];
   __shared__ __attribute__((aligned(1024))) char Vs0[C::kRowBytes];
   __shared__ __attribute__((aligned(1024))) char Kts0[C::kTileBytes];
-
+  __shared__ __attribute__((aligned(1024))) char Ks1[C::kRowBytes];
+  __shared__ __attribute__((aligned(1024))) char Vs1[C::kRowBytes];
+  __shared__ __attribute__((aligned(1024))) char Kts1[C::kTileBytes];
+  extern __shared__ uint16_t list_s[];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int slot = xcd_remap(blockIdx.x, gridDim.x);
@@ -312,64 +317,59 @@ __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2
   const auto rk = make_rsrc(k_r + rowbase * D, (uint32_t)Npad * (uint32_t)(D * 2));
   const auto rv = make_rsrc(v_r + rowbase * D, (uint32_t)Npad * (uint32_t)(D * 2));
   const auto rkt = make_rsrc(k_t + rowbase * D, (uint32_t)Npad * (uint32_t)(D * 2));
-  StageCopies<D, BLK, W> cp;
+  StageCopies<D, BLK, W, kKT> cp;
   cp.init(wave, lane);
-
-  // Stage u: list entry u / kSubs, 64-key half u % kSubs.  An invalid entry
-  // (outside [0, nb)) copies block 0 and computes nothing, as the forward
-  // skips it.
-  const int U = cnt * kSubs;
-  __shared__ uint16_t list_s[kMaxList];
   stage_list(idx, cnt, nb, list_s);
   __syncthreads();
+
+  const int U = cnt * kSubs;
   auto block_of = [&](int u) { return __builtin_amdgcn_readfirstlane((int)list_s[u / kSubs]); };
+  // An invalid entry copies block 0 and computes nothing, as the forward skips it.
   auto issue = [&](int u, char* kb, char* vb, char* tb) {
     const int J0 = block_of(u), h = u % kSubs;
     const int J = J0 == kNoBlock ? 0 : J0;
-    const int key0 = J * BLK + h * 64;
+    const int key0 = J * BLK + h * kKT;
     cp.rows(rk, (uint32_t)key0 * (uint32_t)(D * 2), kb);
     cp.rows(rv, (uint32_t)key0 * (uint32_t)(D * 2), vb);
-    cp.tiles(rkt, ((uint32_t)J * (uint32_t)(D * BLK) + (uint32_t)(h * 64)) * 2u, tb);
+    cp.tiles(rkt, ((uint32_t)J * (uint32_t)(D * BLK) + (uint32_t)(h * kKT)) * 2u, tb);
   };
   auto compute = [&](int u, const char* kb, const char* vb, const char* tb) {
     const int J = block_of(u), h = u % kSubs;
     if (J == kNoBlock) return;
-    const int key0 = J * BLK + h * 64;
-    f32x16_t S[2], dP[2];
+    const int key0 = J * BLK + h * kKT;
+    f32x16_t S = f32x16_t{}, dP = f32x16_t{};
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      S[t] = f32x16_t{};
-      dP[t] = f32x16_t{};
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        S[t] = mfma(read_rows<D>(kb, l32, g, t, kk), qreg[kk], S[t]);
-        dP[t] = mfma(read_rows<D>(vb, l32, g, t, kk), doreg[kk], dP[t]);
-      }
+    for (int kk = 0; kk < D / 16; ++kk) {
+      S = mfma(read_rows<C>(kb, l32, g, kk), qreg[kk], S);
+      dP = mfma(read_rows<C>(vb, l32, g, kk), doreg[kk], dP);
     }
     // dS^T = P^T (dP^T - D); keys >= N have P = 0
-    const bool partial = key0 + 64 > N;
+    const bool partial = key0 + kKT > N;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float p = fast_exp2(__builtin_fmaf(S[t][v], sl2, -lse2));
-        if (partial && key0 + 32 * t + acc_row(v, g) >= N) p = 0.f;
-        S[t][v] = p * (dP[t][v] - Dq);
-      }
+    for (int v = 0; v < 16; ++v) {
+      float p = fast_exp2(__builtin_fmaf(S[v], sl2, -lse2));
+      if (partial && key0 + acc_row(v, g) >= N) p = 0.f;
+      S[v] = p * (dP[v] - Dq);
     }
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const bf16x8_t bq = pack_step(S, st);
+    for (int st = 0; st < 2; ++st) {
+      const bf16x8_t bq = pack_half(S, st);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) acc[dt] = mfma(read_tiles<D>(tb, l32, g, dt, st), bq, acc[dt]);
+      for (int dt = 0; dt < D / 32; ++dt) acc[dt] = mfma(read_tiles<C>(tb, l32, g, dt, st), bq, acc[dt]);
     }
   };
-  for (int u = 0; u < U; ++u) {
-    issue(u, Ks0, Vs0, Kts0);
+  if (U > 0) issue(0, Ks0, Vs0, Kts0);
+  for (int u = 0; u < U; u += 2) {
     wait_dma();
-    __syncthreads();
+    __syncthreads();   // stage u landed; every wave is done with stage u - 1's buffers
+    if (u + 1 < U) issue(u + 1, Ks1, Vs1, Kts1);
     compute(u, Ks0, Vs0, Kts0);
-    __syncthreads();
+    if (u + 1 < U) {
+      wait_dma();
+      __syncthreads();
+      if (u + 2 < U) issue(u + 2, Ks0, Vs0, Kts0);
+      compute(u + 1, Ks1, Vs1, Kts1);
+    }
   }
 
   // lane (l32, g) holds dQ^T rows 32 dt + acc_row(v, g) of query q
@@ -389,8 +389,8 @@ __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV.  Stage u of the key block's query list: entry u / kSubs, half u % kSubs
-// (64 queries, processed as two sub-tiles of 32 to bound the registers).
+// dK, dV.  Stage u of the key block's query list: entry u / kSubs, 32-query
+// part u % kSubs.
 template <int D, int BLK>
 __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dkdv_kernel(
     const __bf16* __restrict__ q_r, const __bf16* __restrict__ k_r, const __bf16* __restrict__ v_r,
@@ -398,14 +398,18 @@ __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2
     const __bf16* __restrict__ q_t, const __bf16* __restrict__ do_t, const int32_t* __restrict__ kvT_count,
     const int32_t* __restrict__ kvT_idx, float* __restrict__ dk, float* __restrict__ dv, int Hh, int N, int Npad,
     int nb, float sl2, float scale) {
-  using C = BwdCfg<D>;
-  constexpr int W = BLK / 32, kSubs = BLK / 64;
+  using C = BwdCfg<D, kKT>;
+  constexpr int W = BLK / 32, kSubs = BLK / kKT;
   __shared__ __attribute__((aligned(1024))) char Qs0[C::kRowBytes];
   __shared__ __attribute__((aligned(1024))) char dOs0[C::kRowBytes];
   __shared__ __attribute__((aligned(1024))) char Qts0[C::kTileBytes];
   __shared__ __attribute__((aligned(1024))) char dOts0[C::kTileBytes];
-
-  __shared__ __attribute__((aligned(16))) float ld_s[1][128];   // lse (log2) of the stage's 64 queries, then D
+  __shared__ __attribute__((aligned(1024))) char Qs1[C::kRowBytes];
+  __shared__ __attribute__((aligned(1024))) char dOs1[C::kRowBytes];
+  __shared__ __attribute__((aligned(1024))) char Qts1[C::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char dOts1[C::kTileBytes];
+  __shared__ __attribute__((aligned(16))) float ld_s[2][2 * kKT];   // per buffer set: lse (log2), then D
+  extern __shared__ uint16_t list_s[];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int slot = xcd_remap(blockIdx.x, gridDim.x);
@@ -440,24 +444,22 @@ __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2
   const auto rdo = make_rsrc(do_r + rowbase * D, (uint32_t)Npad * (uint32_t)(D * 2));
   const auto rqt = make_rsrc(q_t + rowbase * D, (uint32_t)Npad * (uint32_t)(D * 2));
   const auto rdot = make_rsrc(do_t + rowbase * D, (uint32_t)Npad * (uint32_t)(D * 2));
-  StageCopies<D, BLK, W> cp;
+  StageCopies<D, BLK, W, kKT> cp;
   cp.init(wave, lane);
-
-  // Stage u: query-block entry u / kSubs, 64-query half u % kSubs.  An invalid
-  // entry copies block 0 and computes nothing.
-  const int U = cnt * kSubs;
-  __shared__ uint16_t list_s[kMaxList];
   stage_list(idx, cnt, nb, list_s);
   __syncthreads();
+
+  const int U = cnt * kSubs;
   auto block_of = [&](int u) { return __builtin_amdgcn_readfirstlane((int)list_s[u / kSubs]); };
   // The lse / D loads go first: vector loads retire in order, so their LDS
-  // write does not wait for the tile copies issued after them.
+  // write does not wait for the tile copies issued after them.  An invalid
+  // entry copies block 0 and computes nothing.
   auto issue = [&](int u, char* qb, char* ob, char* qtb, char* otb, float* ls) {
     const int I0 = block_of(u), h = u % kSubs;
     const int I = I0 == kNoBlock ? 0 : I0;
-    const int qs0 = I * BLK + h * 64;
+    const int qs0 = I * BLK + h * kKT;
     float lv = 0.f, dv0 = 0.f;
-    if (threadIdx.x < 64) {
+    if (threadIdx.x < kKT) {
       const int qq = qs0 + threadIdx.x;
       const bool ok = qq < N;
       lv = ok ? lse[rowbase + qq] * kLog2e : INFINITY;   // +inf: P = 0 for rows >= N
@@ -465,63 +467,61 @@ __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2
     }
     cp.rows(rq, (uint32_t)qs0 * (uint32_t)(D * 2), qb);
     cp.rows(rdo, (uint32_t)qs0 * (uint32_t)(D * 2), ob);
-    const uint32_t toffs = ((uint32_t)I * (uint32_t)(D * BLK) + (uint32_t)(h * 64)) * 2u;
+    const uint32_t toffs = ((uint32_t)I * (uint32_t)(D * BLK) + (uint32_t)(h * kKT)) * 2u;
     cp.tiles(rqt, toffs, qtb);
     cp.tiles(rdot, toffs, otb);
-    if (threadIdx.x < 64) {
+    if (threadIdx.x < kKT) {
       ls[threadIdx.x] = lv;
-      ls[64 + threadIdx.x] = dv0;
+      ls[kKT + threadIdx.x] = dv0;
     }
   };
   auto compute = [&](int u, const char* qb, const char* ob, const char* qtb, const char* otb, const float* ls) {
     const int I = block_of(u);
     if (I == kNoBlock) return;
+    f32x16_t S = f32x16_t{}, dP = f32x16_t{};
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      f32x16_t S = f32x16_t{}, dP = f32x16_t{};
+    for (int kk = 0; kk < D / 16; ++kk) {
+      S = mfma(read_rows<C>(qb, l32, g, kk), kreg[kk], S);
+      dP = mfma(read_rows<C>(ob, l32, g, kk), vreg[kk], dP);
+    }
+    // rows of S are queries acc_row(v, g): lse and D from LDS, 4 at a time
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        S = mfma(read_rows<D>(qb, l32, g, t, kk), kreg[kk], S);
-        dP = mfma(read_rows<D>(ob, l32, g, t, kk), vreg[kk], dP);
+    for (int a = 0; a < 4; ++a) {
+      const int r0 = 8 * a + 4 * g;
+      const float4 l4 = *reinterpret_cast<const float4*>(ls + r0);
+      const float4 d4 = *reinterpret_cast<const float4*>(ls + kKT + r0);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int v = 4 * a + j;
+        const float p = fast_exp2(__builtin_fmaf(S[v], sl2, -lv[j]));
+        S[v] = p;
+        dP[v] = p * (dP[v] - dv4[j]);
       }
+    }
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int r0 = 32 * t + 8 * a + 4 * g;
-        const float4 l4 = *reinterpret_cast<const float4*>(ls + r0);
-        const float4 d4 = *reinterpret_cast<const float4*>(ls + 64 + r0);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+    for (int st = 0; st < 2; ++st) {
+      const bf16x8_t bp = pack_half(S, st), bs = pack_half(dP, st);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int v = 4 * a + j;
-          const float p = fast_exp2(__builtin_fmaf(S[v], sl2, -lv[j]));
-          S[v] = p;
-          dP[v] = p * (dP[v] - dv4[j]);
-        }
-      }
-#pragma unroll
-      for (int hs = 0; hs < 2; ++hs) {
-        const int o = hs * 8, st = 2 * t + hs;
-        uint4 wp, ws;
-        wp.x = cvt_pk(S[o + 0], S[o + 1]); wp.y = cvt_pk(S[o + 2], S[o + 3]);
-        wp.z = cvt_pk(S[o + 4], S[o + 5]); wp.w = cvt_pk(S[o + 6], S[o + 7]);
-        ws.x = cvt_pk(dP[o + 0], dP[o + 1]); ws.y = cvt_pk(dP[o + 2], dP[o + 3]);
-        ws.z = cvt_pk(dP[o + 4], dP[o + 5]); ws.w = cvt_pk(dP[o + 6], dP[o + 7]);
-        const bf16x8_t bp = __builtin_bit_cast(bf16x8_t, wp), bs = __builtin_bit_cast(bf16x8_t, ws);
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          dva[dt] = mfma(read_tiles<D>(otb, l32, g, dt, st), bp, dva[dt]);
-          dka[dt] = mfma(read_tiles<D>(qtb, l32, g, dt, st), bs, dka[dt]);
-        }
+      for (int dt = 0; dt < D / 32; ++dt) {
+        dva[dt] = mfma(read_tiles<C>(otb, l32, g, dt, st), bp, dva[dt]);
+        dka[dt] = mfma(read_tiles<C>(qtb, l32, g, dt, st), bs, dka[dt]);
       }
     }
   };
-  for (int u = 0; u < U; ++u) {
-    issue(u, Qs0, dOs0, Qts0, dOts0, ld_s[0]);
+  if (U > 0) issue(0, Qs0, dOs0, Qts0, dOts0, ld_s[0]);
+  for (int u = 0; u < U; u += 2) {
     wait_dma();
-    __syncthreads();
+    __syncthreads();   // stage u landed (its lse / D too); stage u - 1's buffers are free
+    if (u + 1 < U) issue(u + 1, Qs1, dOs1, Qts1, dOts1, ld_s[1]);
     compute(u, Qs0, dOs0, Qts0, dOts0, ld_s[0]);
-    __syncthreads();
+    if (u + 1 < U) {
+      wait_dma();
+      __syncthreads();
+      if (u + 2 < U) issue(u + 2, Qs0, dOs0, Qts0, dOts0, ld_s[0]);
+      compute(u + 1, Qs1, dOs1, Qts1, dOts1, ld_s[1]);
+    }
   }
 
   // lane (l32, g) holds rows 32 dt + acc_row(v, g) of dK^T, dV^T for its key
@@ -564,13 +564,14 @@ hipError_t launch_bwd_db(const AttnBwdArgs& a) {
   if (e != hipSuccess) return e;
   const float sl2 = a.scale * kLog2e;
   const unsigned grid = (unsigned)(BH * a.nb);
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, BLK>), dim3(grid), dim3(BLK / 32 * 64), 0, a.stream,
+  const size_t list_bytes = ((size_t)a.nb * 2 + 15) / 16 * 16;
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, BLK>), dim3(grid), dim3(BLK / 32 * 64), list_bytes, a.stream,
                      (const __bf16*)a.q_r, (const __bf16*)a.k_r, (const __bf16*)a.v_r, (const __bf16*)a.o_r,
                      (const __bf16*)a.do_r, a.lse, (const __bf16*)kt, a.kv_count, a.kv_idx, a.dq, dbuf, a.Hh, a.N,
                      a.Npad, a.nb, sl2, a.scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, BLK>), dim3(grid), dim3(BLK / 32 * 64), 0, a.stream,
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, BLK>), dim3(grid), dim3(BLK / 32 * 64), list_bytes, a.stream,
                      (const __bf16*)a.q_r, (const __bf16*)a.k_r, (const __bf16*)a.v_r, (const __bf16*)a.do_r, a.lse,
                      (const float*)dbuf, (const __bf16*)qt, (const __bf16*)dot, a.kvT_count, a.kvT_idx, a.dk, a.dv,
                      a.Hh, a.N, a.Npad, a.nb, sl2, a.scale);
