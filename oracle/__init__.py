@@ -7,7 +7,8 @@ check and the CPU-baseline leg of the bench may import it; the product path
 never does.
 
 Modules: perm (curve and cuboid orders), reorder (gather / scatter), estimator
-(sampled block importance), mask (cumulative-threshold mask), attention
+(sampled block importance), mask (cumulative-threshold mask), mask_rules
+(the top-k and statistical-threshold alternatives), attention
 (block-masked attention with optional global tokens), attention_bwd (its
 gradients, plain ASA, and the key-to-query block lists), accounting (sparsity
 and FLOP).  Every function is pinned by CPU tests against closed forms, invariants
