@@ -167,6 +167,29 @@ def backward_leg(layer, cfg, qd, vd, steps, warmup, torch):
     }
 
 
+def mask_rules_leg(layer, steps, torch):
+    """The alternative selection rules on the timed layer's P_imp: the kept-block lists under the
+    cumulative threshold (tau 0.9), top-k (k = 16) and the statistical cutoff (u = U(1 - 16/nb)),
+    each launched `steps` times back to back between two HIP events."""
+    from dynamic_block_sparse_gilbert_amd import ops
+    nb = layer.p_imp.shape[-1]
+    out = {}
+    for name, rule, param in (("cumulative_tau0.9", "cumulative", 0.9), ("topk_16", "topk", 16),
+                              ("stat_k16", "stat", ops.stat_quantile(16, nb))):
+        ops.build_mask_rule(layer.p_imp, rule, param, kv_count=layer.kv_count, kv_idx=layer.kv_idx)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            ops.build_mask_rule(layer.p_imp, rule, param, kv_count=layer.kv_count, kv_idx=layer.kv_idx)
+        e1.record()
+        torch.cuda.synchronize()
+        cnt = layer.kv_count.cpu().numpy()
+        out[name] = {"us": round(e0.elapsed_time(e1) / steps * 1e3, 2),
+                     "block_sparsity": round(float(1.0 - cnt.sum() / (cnt.size * nb)), 4)}
+    return out
+
+
 def cpu_baseline(cfg, q, k, v, perm, tau, heads=2):
     """The oracle, as it stands, on a bounded sample of the same layer: the first
     `heads` heads in full (estimator, mask, attention over every query block),
@@ -284,6 +307,7 @@ def main():
         layer.forward(qd, kd, vd, out=out, tau=args.tau)   # the timed mask again
         torch.cuda.synchronize()
         extra["backward"] = backward_leg(layer, cfg, qd, vd, max(5, args.steps // 5), 3, torch)
+        extra["mask_rules"] = mask_rules_leg(layer, 20, torch)
 
     line = {
         "metric": "ms/layer + dense-equiv TFLOP/s, block-sparse attn at 90-95% sparsity, 1 GPU",

@@ -293,6 +293,38 @@ dbs_status dbs_build_mask(const float* p_imp, int B, int Hh, int nb, float tau, 
   DBS_GUARD_END
 }
 
+dbs_status dbs_build_mask_rule(const float* p_imp, int B, int Hh, int nb, int rule, double param,
+                               int32_t* kv_count, int32_t* kv_idx, uint8_t* mask, int32_t* order,
+                               hipStream_t stream) {
+  DBS_GUARD_BEGIN
+  REQUIRE(p_imp && kv_count && kv_idx, DBS_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(((uintptr_t)p_imp & 3u) == 0 && ((uintptr_t)kv_count & 3u) == 0 && ((uintptr_t)kv_idx & 3u) == 0 &&
+              ((uintptr_t)order & 3u) == 0,
+          DBS_ERR_ALIGNMENT, "misaligned pointer");
+  REQUIRE(B >= 1 && Hh >= 1, DBS_ERR_INVALID_ARG, "B and Hh must be >= 1");
+  REQUIRE(nb >= 1 && nb <= 4096, DBS_ERR_UNSUPPORTED, "nb=%d must be in [1, 4096]", nb);
+  REQUIRE((int64_t)B * Hh * nb <= INT32_MAX, DBS_ERR_INVALID_ARG, "too many rows");
+  REQUIRE(std::isfinite(param), DBS_ERR_INVALID_ARG, "param must be finite");
+  dbs::MaskArgs a{};
+  a.p_imp = p_imp; a.kv_count = kv_count; a.kv_idx = kv_idx; a.mask = mask; a.order = order;
+  a.rows = B * Hh * nb; a.nb = nb; a.stream = stream;
+  if (rule == DBS_RULE_CUMULATIVE) {
+    REQUIRE(param > 0.0 && param <= 1.0, DBS_ERR_INVALID_ARG, "tau=%g must be in (0, 1]", param);
+    a.rule = 0; a.tau = (float)param;
+    REQUIRE(a.tau > 0.f, DBS_ERR_INVALID_ARG, "tau=%g rounds to 0 in float32", param);
+  } else if (rule == DBS_RULE_TOPK) {
+    REQUIRE(param >= 1.0 && param == std::floor(param) && param <= 1e9, DBS_ERR_INVALID_ARG,
+            "top-k count %g must be an integer >= 1", param);
+    a.rule = 1; a.topk = param >= nb ? nb : (int)param;
+  } else if (rule == DBS_RULE_STAT) {
+    a.rule = 2; a.u = param;
+  } else {
+    return fail(DBS_ERR_INVALID_ARG, "unknown rule %d", rule);
+  }
+  return from_hip(dbs::launch_build_mask(a), "dbs_build_mask_rule launch");
+  DBS_GUARD_END
+}
+
 dbs_status dbs_meanpool_kv(const void* k_r, const void* v_r, dbs_dtype dt, int B, int Hh, int N, int Npad,
                            int d, int b, int n, void* k_g, void* v_g, hipStream_t stream) {
   DBS_GUARD_BEGIN

@@ -113,15 +113,43 @@ __device__ __forceinline__ U192 wave_inclusive_scan(U192 x, int lane) {
   return x;
 }
 
+// The selection rule (launch.h MaskRule): the cumulative threshold tau, the
+// top-k budget, or the statistical cutoff p = mean + std * u over the row's
+// scores (BSA notes, design 2, read as a per-block cutoff; at least the
+// largest block is kept).  The statistics are float64 sums in a fixed order.
+struct Rule {
+  int kind;          // 0 cumulative, 1 top-k, 2 statistical
+  uint32_t tau_bits;
+  int topk;
+  double u;
+};
+
+__device__ __forceinline__ double xor_shfl_d(double v, int m) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const int lane = threadIdx.x & 63;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ m) << 2, (int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ m) << 2, (int)(uint32_t)(b >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Sum over the 64 lanes, the same butterfly order in every lane.
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v += xor_shfl_d(v, m);
+  return v;
+}
+
 // kCap: largest nb of the size class (LDS is sized for it, so small rows keep
 // many workgroups resident); kThreads: workgroup size.
 template <int kCap, int kThreads>
 __global__ __launch_bounds__(kThreads) void build_mask_kernel(
-    const float* __restrict__ p_imp, int nb, uint32_t tau_bits, int32_t* __restrict__ kv_count,
+    const float* __restrict__ p_imp, int nb, Rule rule, int32_t* __restrict__ kv_count,
     int32_t* __restrict__ kv_idx, uint8_t* __restrict__ mask) {
+  const uint32_t tau_bits = rule.tau_bits;
   __shared__ uint64_t keys[kCap];
   __shared__ uint8_t flag[kCap];
   __shared__ uint32_t red[kThreads / 64][kLimbs];
+  __shared__ double dred[kThreads / 64];
   __shared__ int s_invalid, s_m;
   __shared__ int s_wave_cnt[kThreads / 64];
 
@@ -146,7 +174,8 @@ __global__ __launch_bounds__(kThreads) void build_mask_kernel(
   }
   if (bad) s_invalid = 1;
   __syncthreads();
-  const bool keep_all = s_invalid != 0 || tau_bits >= 0x3f800000u;
+  const bool keep_all = s_invalid != 0 || (rule.kind == 0 && tau_bits >= 0x3f800000u) ||
+                        (rule.kind == 1 && rule.topk >= nb);
 
   int m = nb;
   if (!keep_all) {
@@ -165,6 +194,33 @@ __global__ __launch_bounds__(kThreads) void build_mask_kernel(
         __syncthreads();
       }
     }
+  }
+  if (!keep_all && rule.kind == 1) {
+    m = rule.topk;
+  } else if (!keep_all && rule.kind == 2) {
+    // ---- statistical cutoff: mean, then the population deviation, float64 --------
+    auto block_sum = [&](double v) {
+      v = wave_sum_d(v);
+      if (lane == 0) dred[wave] = v;
+      __syncthreads();
+      double t = 0.0;
+      for (int w = 0; w < kThreads / 64; ++w) t += dred[w];
+      __syncthreads();
+      return t;
+    };
+    double s1 = 0.0;
+    for (int j = tid; j < nb; j += kThreads) s1 += (double)__uint_as_float(~(uint32_t)(keys[j] >> 32));
+    const double mean = block_sum(s1) / nb;
+    double s2 = 0.0;
+    for (int j = tid; j < nb; j += kThreads) {
+      const double dv = (double)__uint_as_float(~(uint32_t)(keys[j] >> 32)) - mean;
+      s2 += dv * dv;
+    }
+    const double p = mean + sqrt(block_sum(s2) / nb) * rule.u;
+    double c = 0.0;
+    for (int j = tid; j < nb; j += kThreads) c += (double)__uint_as_float(~(uint32_t)(keys[j] >> 32)) >= p ? 1.0 : 0.0;
+    m = max(1, (int)block_sum(c));
+  } else if (!keep_all) {
     // ---- exact row total ---------------------------------------------------------
     U192 part = u192_zero();
     for (int j = tid; j < nb; j += kThreads) part = u192_add(part, f32_to_u192(~(uint32_t)(keys[j] >> 32)));
@@ -297,8 +353,9 @@ __device__ __forceinline__ uint32_t lane_xor(uint32_t v, int d) {
 
 template <int KPL>
 __global__ __launch_bounds__(256) void build_mask_wave_kernel(
-    const float* __restrict__ p_imp, int nb, int rows, uint32_t tau_bits, int32_t* __restrict__ kv_count,
+    const float* __restrict__ p_imp, int nb, int rows, Rule rule, int32_t* __restrict__ kv_count,
     int32_t* __restrict__ kv_idx, uint8_t* __restrict__ mask) {
+  const uint32_t tau_bits = rule.tau_bits;
   constexpr int P2 = 64 * KPL;
   __shared__ uint8_t flag_all[4][P2];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -320,7 +377,8 @@ __global__ __launch_bounds__(256) void build_mask_wave_kernel(
       key[r] = ((uint64_t)(~bits) << 32) | (uint32_t)e;
     }
   }
-  const bool keep_all = __ballot(bad) != 0 || tau_bits >= 0x3f800000u;
+  const bool keep_all = __ballot(bad) != 0 || (rule.kind == 0 && tau_bits >= 0x3f800000u) ||
+                        (rule.kind == 1 && rule.topk >= nb);
 
   int m = nb;
   if (!keep_all) {
@@ -354,6 +412,31 @@ __global__ __launch_bounds__(256) void build_mask_wave_kernel(
         }
       }
     }
+  }
+  if (!keep_all && rule.kind == 1) {
+    m = rule.topk;
+  } else if (!keep_all && rule.kind == 2) {
+    // ---- statistical cutoff: mean, then the population deviation, float64 ----------
+    double s1 = 0.0;
+#pragma unroll
+    for (int r = 0; r < KPL; ++r)
+      if (lane * KPL + r < nb) s1 += (double)__uint_as_float(~(uint32_t)(key[r] >> 32));
+    const double mean = wave_sum_d(s1) / nb;
+    double s2 = 0.0;
+#pragma unroll
+    for (int r = 0; r < KPL; ++r) {
+      if (lane * KPL + r < nb) {
+        const double dv = (double)__uint_as_float(~(uint32_t)(key[r] >> 32)) - mean;
+        s2 += dv * dv;
+      }
+    }
+    const double p = mean + sqrt(wave_sum_d(s2) / nb) * rule.u;
+    int c = 0;
+#pragma unroll
+    for (int r = 0; r < KPL; ++r)
+      c += (lane * KPL + r < nb && (double)__uint_as_float(~(uint32_t)(key[r] >> 32)) >= p) ? 1 : 0;
+    m = max(1, (int)wave_sum_d((double)c));
+  } else if (!keep_all) {
     // ---- exact row total and target ceil(tau * total) ----------------------------
     U192 val[KPL];
     U192 lsum = u192_zero();
@@ -510,22 +593,27 @@ __global__ __launch_bounds__(kOrderThreads) void build_order_kernel(const int32_
 hipError_t launch_build_mask(const MaskArgs& a) {
   uint32_t tau_bits;
   __builtin_memcpy(&tau_bits, &a.tau, 4);
+  Rule rule;
+  rule.kind = a.rule;
+  rule.tau_bits = tau_bits;
+  rule.topk = a.topk;
+  rule.u = a.u;
   const dim3 wgrid((unsigned)((a.rows + 3) / 4));
   if (a.nb <= 64) {
     hipLaunchKernelGGL((build_mask_wave_kernel<1>), wgrid, dim3(256), 0, a.stream, a.p_imp, a.nb, a.rows,
-                       tau_bits, a.kv_count, a.kv_idx, a.mask);
+                       rule, a.kv_count, a.kv_idx, a.mask);
   } else if (a.nb <= 128) {
     hipLaunchKernelGGL((build_mask_wave_kernel<2>), wgrid, dim3(256), 0, a.stream, a.p_imp, a.nb, a.rows,
-                       tau_bits, a.kv_count, a.kv_idx, a.mask);
+                       rule, a.kv_count, a.kv_idx, a.mask);
   } else if (a.nb <= 256) {
     hipLaunchKernelGGL((build_mask_wave_kernel<4>), wgrid, dim3(256), 0, a.stream, a.p_imp, a.nb, a.rows,
-                       tau_bits, a.kv_count, a.kv_idx, a.mask);
+                       rule, a.kv_count, a.kv_idx, a.mask);
   } else if (a.nb <= 1024) {
     hipLaunchKernelGGL((build_mask_kernel<1024, 256>), dim3(a.rows), dim3(256), 0, a.stream, a.p_imp, a.nb,
-                       tau_bits, a.kv_count, a.kv_idx, a.mask);
+                       rule, a.kv_count, a.kv_idx, a.mask);
   } else {
     hipLaunchKernelGGL((build_mask_kernel<kMaxNb, 256>), dim3(a.rows), dim3(256), 0, a.stream, a.p_imp,
-                       a.nb, tau_bits, a.kv_count, a.kv_idx, a.mask);
+                       a.nb, rule, a.kv_count, a.kv_idx, a.mask);
   }
   if (a.order != nullptr) {
     const hipError_t e = hipGetLastError();

@@ -61,7 +61,10 @@ struct MaskArgs {
   uint8_t* mask;
   int32_t* order;       // nullable: attention work order
   int rows, nb;
-  float tau;
+  float tau;            // rule 0
+  int rule;             // 0 cumulative threshold, 1 top-k, 2 statistical cutoff
+  int topk;             // rule 1
+  double u;             // rule 2: the quantile in p = mean + std * u
   hipStream_t stream;
 };
 

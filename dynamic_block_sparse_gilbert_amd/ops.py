@@ -191,6 +191,36 @@ def build_mask(p_imp: torch.Tensor, tau: float, kv_count: Optional[torch.Tensor]
     return kv_count, kv_idx, mask
 
 
+MASK_RULES = {"cumulative": 0, "topk": 1, "stat": 2}
+
+
+def stat_quantile(k: float, n: int) -> float:
+    """u = U(1 - k/n), the standard normal quantile of the statistical rule (k of n blocks kept on
+    normally spread scores)."""
+    from statistics import NormalDist
+    if not 0 < k < n:
+        raise ValueError("need 0 < k < n")
+    return NormalDist().inv_cdf(1.0 - k / n)
+
+
+def build_mask_rule(p_imp: torch.Tensor, rule: str, param: float, kv_count: Optional[torch.Tensor] = None,
+                    kv_idx: Optional[torch.Tensor] = None, want_mask: bool = False,
+                    order: Optional[torch.Tensor] = None):
+    """Kept-block lists under `rule`: 'cumulative' (param = tau), 'topk' (param = k) or 'stat'
+    (param = u, see stat_quantile).  Returns (kv_count, kv_idx, mask or None)."""
+    _dev(p_imp, kv_count, kv_idx, order)
+    B, Hh, nb, _ = p_imp.shape
+    if kv_count is None:
+        kv_count = torch.empty((B, Hh, nb), dtype=torch.int32, device=p_imp.device)
+    if kv_idx is None:
+        kv_idx = torch.empty((B, Hh, nb, nb), dtype=torch.int32, device=p_imp.device)
+    mask = torch.empty((B, Hh, nb, nb), dtype=torch.uint8, device=p_imp.device) if want_mask else None
+    check("dbs_build_mask_rule", lib().dbs_build_mask_rule(
+        _p(p_imp), B, Hh, nb, MASK_RULES[rule], float(param), _p(kv_count), _p(kv_idx), _p(mask), _p(order),
+        _stream()))
+    return kv_count, kv_idx, mask
+
+
 def meanpool_kv(k_r: torch.Tensor, v_t: torch.Tensor, N: int, b: int, n: int,
                 k_g: Optional[torch.Tensor] = None, v_g: Optional[torch.Tensor] = None
                 ) -> Tuple[torch.Tensor, torch.Tensor, int]:

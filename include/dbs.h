@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define DBS_ABI_VERSION 5
+#define DBS_ABI_VERSION 6
 
 typedef enum {
   DBS_OK = 0,
@@ -201,6 +201,26 @@ dbs_status dbs_estimate_blocks_tok(const void* q, dbs_dtype q_dt, int64_t sb, in
 dbs_status dbs_build_mask(const float* p_imp, int B, int Hh, int nb, float tau,
                           int32_t* kv_count, int32_t* kv_idx, uint8_t* mask, int32_t* order,
                           hipStream_t stream);
+
+/* The same kept-block lists (and optional mask / work order) under another
+ * selection rule (one of dbs_mask_rule), for comparing rules on one P_imp:
+ *   DBS_RULE_CUMULATIVE  param = tau: exactly dbs_build_mask.
+ *   DBS_RULE_TOPK        param = k (an integer >= 1): the k blocks of largest
+ *                        importance, ties by block index (k >= nb keeps all);
+ *                        the fixed-budget rule the BSA notes compare against.
+ *   DBS_RULE_STAT        param = u: the statistical cutoff of the BSA notes
+ *                        (design 2), p = mean + std * u over the row's nb
+ *                        scores (population std, float64, fixed summation
+ *                        order), read as a per-block cutoff: every block with
+ *                        P_imp >= p is kept, and at least the largest one.
+ *                        u = U(1 - k/n), the standard normal quantile, keeps
+ *                        about k of n blocks on normally spread scores.
+ * Rows holding a value outside [0, 1] or NaN keep every block.  Output as
+ * for dbs_build_mask.  INVALID_ARG for an unknown rule or a bad param. */
+typedef enum { DBS_RULE_CUMULATIVE = 0, DBS_RULE_TOPK = 1, DBS_RULE_STAT = 2 } dbs_mask_rule;
+dbs_status dbs_build_mask_rule(const float* p_imp, int B, int Hh, int nb, int rule, double param,
+                               int32_t* kv_count, int32_t* kv_idx, uint8_t* mask, int32_t* order,
+                               hipStream_t stream);
 
 /* ASA_G global tokens (Video-BLADE "Step 2.2 (2)"; BLADE notes key design 2):
  * mean of each window of n consecutive reordered tokens,

@@ -37,7 +37,7 @@ def test_all_declared_symbols_exported(dbs):
     for n in names:
         assert hasattr(h, n), n
     assert set(names) == set(L.SIGNATURES), set(names) ^ set(L.SIGNATURES)
-    assert L.lib().dbs_abi_version() == 5
+    assert L.lib().dbs_abi_version() == 6
 
 
 @pytest.mark.parametrize("T,H,W", list(itertools.product(range(1, 7), repeat=3)))
@@ -244,6 +244,19 @@ def test_backward_validation(dbs):
     assert call(9, 1000) == -1             # Npad not a multiple of b
     assert call(21, ws - 1) == -1          # small workspace
     assert call(12, float("inf")) == -1    # scale
+
+
+@cpu_only
+def test_mask_rule_validation(dbs):
+    _, L = dbs
+    f = L.lib().dbs_build_mask_rule
+    assert f(A, 1, 1, 16, 7, 0.5, A, A, None, None, None) == -1           # unknown rule
+    assert f(A, 1, 1, 16, 0, 1.5, A, A, None, None, None) == -1           # tau > 1
+    assert f(A, 1, 1, 16, 1, 0.0, A, A, None, None, None) == -1           # k < 1
+    assert f(A, 1, 1, 16, 1, 2.5, A, A, None, None, None) == -1           # k not an integer
+    assert f(A, 1, 1, 16, 2, float("nan"), A, A, None, None, None) == -1  # u not finite
+    assert f(A, 1, 1, 4097, 2, 1.0, A, A, None, None, None) == -2         # nb > 4096
+    assert f(0, 1, 1, 16, 2, 1.0, A, A, None, None, None) == -1           # NULL
 
 
 @cpu_only
