@@ -9,9 +9,12 @@ under "extra", and so is the backward of the attention at tau = 0.90).
 Synthetic inputs stand in for the model's activations.
 
 A step is one pass of the whole hot path over that batch, all on one stream:
-reorder K, V -> estimate_blocks (sampled Q rows read in token order) ->
-build_mask -> sparse_attn_fwd (Q read and the output written in token order,
-so the return to token order is part of that launch).  Inputs are resident in
+reorder K, V -> estimate_mask (the sampled estimate, sampled Q rows read in
+token order, with the cumulative-threshold selection fused into its final
+launch, so P_imp never reaches HBM) -> sparse_attn_fwd (Q read and the output
+written in token order, so the return to token order is part of that launch).
+With --unfused the estimate and the mask run as two calls (estimate_blocks,
+build_mask), the layout the unfused time under "extra" is measured with.  Inputs are resident in
 HBM before timing starts; buffers and the permutation are set up once outside
 the timed region.
 
@@ -50,6 +53,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--tau", type=float, default=0.90)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true", help="estimate and mask as two calls")
     ap.add_argument("--no-extra", action="store_true", help="skip the tau=0.95 and backward measurements")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
@@ -98,23 +102,26 @@ def stage_times(layer, q, k, v, out, tau, steps, torch):
     launch stream between the stages of each step (each stage time carries one event's cost).
     The attention entry is the mean attention launch duration used for the roofline."""
     from dynamic_block_sparse_gilbert_amd import ops
-    names = ["reorder_kv", "estimate", "mask", "attn"]
     sp = layer.spec
+    names = ["reorder_kv", "estimate_mask", "attn"] if layer.fused else ["reorder_kv", "estimate", "mask", "attn"]
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
     for s in range(steps):
         e = ev[s]
         e[0].record()
         layer.prepare(q, k, v)
         e[1].record()
-        ops.estimate_blocks_tok(q, layer.perm, layer.k_r, sp.N, sp.b, sp.k, sp.scale, p_imp=layer.p_imp,
-                                workspace=layer.ws)
-        e[2].record()
-        ops.build_mask(layer.p_imp, tau, kv_count=layer.kv_count, kv_idx=layer.kv_idx, order=layer.order)
-        e[3].record()
+        if layer.fused:
+            layer.mask(tau)
+        else:
+            ops.estimate_blocks_tok(q, layer.perm, layer.k_r, sp.N, sp.b, sp.k, sp.scale, p_imp=layer.p_imp,
+                                    workspace=layer.ws)
+            e[2].record()
+            ops.build_mask(layer.p_imp, tau, kv_count=layer.kv_count, kv_idx=layer.kv_idx, order=layer.order)
+        e[len(names) - 1].record()
         ops.sparse_attn_fwd_tok(q, layer.perm, layer.k_r, layer.v_t, sp.N, sp.b, sp.scale, layer.kv_count,
                                 layer.kv_idx, layer.k_g, layer.v_g, layer.Ng, sp.n_pool, out=out,
                                 order=layer.order)
-        e[4].record()
+        e[len(names)].record()
     torch.cuda.synchronize()
     return {n: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps
             for i, n in enumerate(names)}
@@ -253,7 +260,7 @@ def main():
     qd, kd, vd = to(q), to(k), to(v)
     out = torch.empty_like(qd)
     spec = LayerSpec(T=cfg.T, H=cfg.H, W=cfg.W, heads=cfg.heads, d=cfg.d, b=cfg.b, k=cfg.k, tau=args.tau)
-    layer = AsaLayer(spec, device=dev)
+    layer = AsaLayer(spec, device=dev, fused=not args.unfused)
     torch.cuda.synchronize()
 
     if args.copy_calib_mib:
@@ -288,6 +295,10 @@ def main():
     e = 2
     reorder_bytes = 2.0 * 2 * cfg.heads * cfg.N * cfg.d * e
     mask_bytes = 4.0 * cfg.heads * nb * nb + 4.0 * cfg.heads * (nb + cnt.sum())
+    byte_passes = {"reorder_kv_GBs": round(reorder_bytes / (stage["reorder_kv"] * 1e-3) / 1e9, 1)}
+    if "mask" in stage:
+        byte_passes["mask_GBs"] = round(mask_bytes / (stage["mask"] * 1e-3) / 1e9, 1)
+    byte_passes["hbm_peak_GBs"] = HBM_PEAK_GBS
 
     extra = {}
     if not args.no_extra:
@@ -305,9 +316,14 @@ def main():
             "attn_executed_tflops": round(ef95 / (attn95 * 1e-3) / 1e12, 2),
         }
         layer.forward(qd, kd, vd, out=out, tau=args.tau)   # the timed mask again
+        layer.mask(args.tau, keep_p_imp=True)              # and its P_imp, for the rule comparison
         torch.cuda.synchronize()
         extra["backward"] = backward_leg(layer, cfg, qd, vd, max(5, args.steps // 5), 3, torch)
         extra["mask_rules"] = mask_rules_leg(layer, 20, torch)
+        other = AsaLayer(spec, device=dev, fused=args.unfused)
+        ms_o, _ = run_steps(other, qd, kd, vd, out, args.tau, args.steps, args.warmup, torch)
+        extra["unfused_ms_per_step" if not args.unfused else "fused_ms_per_step"] = round(ms_o, 4)
+        del other
 
     line = {
         "metric": "ms/layer + dense-equiv TFLOP/s, block-sparse attn at 90-95% sparsity, 1 GPU",
@@ -342,11 +358,7 @@ def main():
             "launch_ms": round(attn_ms, 4),
         },
         "stages_ms": {kk: round(vv, 4) for kk, vv in stage.items()},
-        "byte_passes": {
-            "reorder_kv_GBs": round(reorder_bytes / (stage["reorder_kv"] * 1e-3) / 1e9, 1),
-            "mask_GBs": round(mask_bytes / (stage["mask"] * 1e-3) / 1e9, 1),
-            "hbm_peak_GBs": HBM_PEAK_GBS,
-        },
+        "byte_passes": byte_passes,
         "step_ms_events": round(ms_ev, 4),
         "input_gen_s": round(t_gen, 2),
     }

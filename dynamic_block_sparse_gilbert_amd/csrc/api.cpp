@@ -223,10 +223,30 @@ dbs_status check_tok(const void* x, dbs_dtype dt, int64_t sb, int64_t sn, int64_
   return check_strides(sb, sn, sh, dt);
 }
 
+// The selection rule and its parameter into a, checked (rule values of dbs_mask_rule).
+dbs_status rule_args(int rule, double param, int nb, dbs::MaskArgs& a) {
+  REQUIRE(std::isfinite(param), DBS_ERR_INVALID_ARG, "param must be finite");
+  if (rule == DBS_RULE_CUMULATIVE) {
+    REQUIRE(param > 0.0 && param <= 1.0, DBS_ERR_INVALID_ARG, "tau=%g must be in (0, 1]", param);
+    a.rule = 0; a.tau = (float)param;
+    REQUIRE(a.tau > 0.f, DBS_ERR_INVALID_ARG, "tau=%g rounds to 0 in float32", param);
+  } else if (rule == DBS_RULE_TOPK) {
+    REQUIRE(param >= 1.0 && param == std::floor(param) && param <= 1e9, DBS_ERR_INVALID_ARG,
+            "top-k count %g must be an integer >= 1", param);
+    a.rule = 1; a.topk = param >= nb ? nb : (int)param;
+  } else if (rule == DBS_RULE_STAT) {
+    a.rule = 2; a.u = param;
+  } else {
+    return fail(DBS_ERR_INVALID_ARG, "unknown rule %d", rule);
+  }
+  return DBS_OK;
+}
+
+// fuse set: P_imp rows go straight into the block selection (p_imp nullable).
 dbs_status estimate_impl(const void* q_r, const void* k_r, int B, int Hh, int N, int Npad, int d, int b, int k,
                          float scale, float* p_imp, void* workspace, size_t workspace_bytes,
-                         const dbs::TokIO& tok, hipStream_t stream) {
-  REQUIRE(k_r && p_imp && workspace, DBS_ERR_INVALID_ARG, "NULL pointer");
+                         const dbs::TokIO& tok, hipStream_t stream, const dbs::MaskArgs* fuse = nullptr) {
+  REQUIRE(k_r && (p_imp || fuse) && workspace, DBS_ERR_INVALID_ARG, "NULL pointer");
   REQUIRE(aligned16(k_r) && aligned16(p_imp) && aligned16(workspace), DBS_ERR_ALIGNMENT, "misaligned pointer");
   dbs_status st = check_geometry(B, Hh, N, Npad, d, b);
   if (st != DBS_OK) return st;
@@ -241,7 +261,25 @@ dbs_status estimate_impl(const void* q_r, const void* k_r, int B, int Hh, int N,
   a.q_r = q_r; a.k_r = k_r; a.p_imp = p_imp; a.workspace = workspace;
   a.B = B; a.Hh = Hh; a.N = N; a.Npad = Npad; a.d = d; a.b = b; a.k = k; a.nb = nb;
   a.scale = scale; a.tok = tok; a.stream = stream;
+  if (fuse != nullptr) {
+    REQUIRE(nb <= 4096, DBS_ERR_UNSUPPORTED, "nb=%d must be in [1, 4096]", nb);
+    REQUIRE((int64_t)B * Hh * nb <= INT32_MAX, DBS_ERR_INVALID_ARG, "too many rows");
+    dbs::MaskArgs m = *fuse;
+    m.rows = B * Hh * nb; m.nb = nb; m.stream = stream;
+    a.fuse = &m;
+    return from_hip(dbs::launch_estimate(a), "dbs_estimate_mask launch");
+  }
   return from_hip(dbs::launch_estimate(a), "dbs_estimate_blocks launch");
+}
+
+// The kept-block outputs of the fused calls, checked, with the rule.
+dbs_status fuse_args(int rule, double param, int32_t* kv_count, int32_t* kv_idx, uint8_t* mask, int32_t* order,
+                     int Npad, int b, dbs::MaskArgs& m) {
+  REQUIRE(kv_count && kv_idx, DBS_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(((uintptr_t)kv_count & 3u) == 0 && ((uintptr_t)kv_idx & 3u) == 0 && ((uintptr_t)order & 3u) == 0,
+          DBS_ERR_ALIGNMENT, "misaligned pointer");
+  m.kv_count = kv_count; m.kv_idx = kv_idx; m.mask = mask; m.order = order;
+  return rule_args(rule, param, b > 0 ? Npad / b : 1, m);
 }
 
 }  // namespace
@@ -275,6 +313,41 @@ dbs_status dbs_estimate_blocks_tok(const void* q, dbs_dtype q_dt, int64_t sb, in
   DBS_GUARD_END
 }
 
+dbs_status dbs_estimate_mask(const void* q_r, const void* k_r, dbs_dtype dt, int B, int Hh, int N, int Npad,
+                             int d, int b, int k, float scale, int rule, double param, float* p_imp,
+                             int32_t* kv_count, int32_t* kv_idx, uint8_t* mask, int32_t* order, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  DBS_GUARD_BEGIN
+  REQUIRE(q_r, DBS_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(aligned16(q_r), DBS_ERR_ALIGNMENT, "misaligned pointer");
+  REQUIRE(dt == DBS_BF16, DBS_ERR_UNSUPPORTED, "estimate_mask computes on bf16 inputs");
+  dbs::MaskArgs m{};
+  dbs_status st = fuse_args(rule, param, kv_count, kv_idx, mask, order, Npad, b, m);
+  if (st != DBS_OK) return st;
+  return estimate_impl(q_r, k_r, B, Hh, N, Npad, d, b, k, scale, p_imp, workspace, workspace_bytes, dbs::TokIO{},
+                       stream, &m);
+  DBS_GUARD_END
+}
+
+dbs_status dbs_estimate_mask_tok(const void* q, dbs_dtype q_dt, int64_t sb, int64_t sn, int64_t sh,
+                                 const int32_t* perm, int perm_per_head, const void* k_r, int B, int Hh, int N,
+                                 int Npad, int d, int b, int k, float scale, int rule, double param, float* p_imp,
+                                 int32_t* kv_count, int32_t* kv_idx, uint8_t* mask, int32_t* order,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  DBS_GUARD_BEGIN
+  dbs_status st = check_tok(q, q_dt, sb, sn, sh, perm, perm_per_head);
+  if (st != DBS_OK) return st;
+  dbs::MaskArgs m{};
+  st = fuse_args(rule, param, kv_count, kv_idx, mask, order, Npad, b, m);
+  if (st != DBS_OK) return st;
+  dbs::TokIO tok{};
+  tok.q = q; tok.q_f32 = q_dt == DBS_FP32; tok.qsb = sb; tok.qsn = sn; tok.qsh = sh;
+  tok.perm = perm; tok.perm_h_stride = perm_per_head ? N : 0;
+  return estimate_impl(nullptr, k_r, B, Hh, N, Npad, d, b, k, scale, p_imp, workspace, workspace_bytes, tok,
+                       stream, &m);
+  DBS_GUARD_END
+}
+
 dbs_status dbs_build_mask(const float* p_imp, int B, int Hh, int nb, float tau, int32_t* kv_count,
                           int32_t* kv_idx, uint8_t* mask, int32_t* order, hipStream_t stream) {
   DBS_GUARD_BEGIN
@@ -304,23 +377,11 @@ dbs_status dbs_build_mask_rule(const float* p_imp, int B, int Hh, int nb, int ru
   REQUIRE(B >= 1 && Hh >= 1, DBS_ERR_INVALID_ARG, "B and Hh must be >= 1");
   REQUIRE(nb >= 1 && nb <= 4096, DBS_ERR_UNSUPPORTED, "nb=%d must be in [1, 4096]", nb);
   REQUIRE((int64_t)B * Hh * nb <= INT32_MAX, DBS_ERR_INVALID_ARG, "too many rows");
-  REQUIRE(std::isfinite(param), DBS_ERR_INVALID_ARG, "param must be finite");
   dbs::MaskArgs a{};
   a.p_imp = p_imp; a.kv_count = kv_count; a.kv_idx = kv_idx; a.mask = mask; a.order = order;
   a.rows = B * Hh * nb; a.nb = nb; a.stream = stream;
-  if (rule == DBS_RULE_CUMULATIVE) {
-    REQUIRE(param > 0.0 && param <= 1.0, DBS_ERR_INVALID_ARG, "tau=%g must be in (0, 1]", param);
-    a.rule = 0; a.tau = (float)param;
-    REQUIRE(a.tau > 0.f, DBS_ERR_INVALID_ARG, "tau=%g rounds to 0 in float32", param);
-  } else if (rule == DBS_RULE_TOPK) {
-    REQUIRE(param >= 1.0 && param == std::floor(param) && param <= 1e9, DBS_ERR_INVALID_ARG,
-            "top-k count %g must be an integer >= 1", param);
-    a.rule = 1; a.topk = param >= nb ? nb : (int)param;
-  } else if (rule == DBS_RULE_STAT) {
-    a.rule = 2; a.u = param;
-  } else {
-    return fail(DBS_ERR_INVALID_ARG, "unknown rule %d", rule);
-  }
+  dbs_status st = rule_args(rule, param, nb, a);
+  if (st != DBS_OK) return st;
   return from_hip(dbs::launch_build_mask(a), "dbs_build_mask_rule launch");
   DBS_GUARD_END
 }

@@ -31,6 +31,7 @@
 
 #include "common.h"
 #include "../launch.h"
+#include "mask_core.h"
 
 namespace dbs {
 namespace {
@@ -477,6 +478,42 @@ __device__ __forceinline__ float merge_lse2(const float2* part_bh, const SampleG
 constexpr int kFinalThreads = 256;
 constexpr int kMaxK = 128;   // k <= b <= 128
 
+// The lse2 values of query block I's sampled queries (slots >= k_I: +inf),
+// written by threads lane0 .. lane0 + k - 1 of the calling group.
+__device__ __forceinline__ void row_lse(const float2* __restrict__ part, const SampleGeom& sg, int bh, int I,
+                                        int kI, float* lse, int i) {
+  if (i < sg.k) {
+    const int rq = I * sg.k + i;
+    lse[i] = i < kI ? merge_lse2(part + (int64_t)bh * sg.splits * sg.nsp, sg, rq) : INFINITY;
+  }
+}
+
+// P_imp[I, J] from the row's lse2 values and the block maxima of its sampled
+// queries (t0: the first of them).  Max is exact, so the order of the terms
+// does not change the result.
+__device__ __forceinline__ float pimp_value(const float* lse, const float* __restrict__ t0, const SampleGeom& sg,
+                                            int kI, int J, float sl2) {
+  const int cpb = sg.ncell / sg.nb;   // cells per block: 1, or k / 64
+  float best = -INFINITY;
+  // 8 sampled queries at a time, their loads issued together
+  for (int t0q = 0; t0q < kI; t0q += 8) {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int t = min(t0q + e, kI - 1);
+      const float* tr = t0 + (int64_t)t * sg.ncell + J * cpb;
+      v[e] = tr[0];
+      for (int c = 1; c < cpb; ++c) v[e] = fmaxf(v[e], tr[c]);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int t = min(t0q + e, kI - 1);
+      best = fmaxf(best, __builtin_fmaf(v[e], sl2, -lse[t]));
+    }
+  }
+  return fast_exp2(best);
+}
+
 __global__ __launch_bounds__(kFinalThreads) void est_final_kernel(const float2* __restrict__ part,
                                                                   const float* __restrict__ tmax,
                                                                   float* __restrict__ p_imp, SampleGeom sg,
@@ -484,34 +521,128 @@ __global__ __launch_bounds__(kFinalThreads) void est_final_kernel(const float2* 
   __shared__ float lse[kMaxK];
   const int I = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int kI = I < sg.nb - 1 ? sg.k : sg.kj_last;
-  if (tid < sg.k) {
-    const int rq = I * sg.k + tid;
-    lse[tid] = tid < kI ? merge_lse2(part + (int64_t)bh * sg.splits * sg.nsp, sg, rq) : INFINITY;
-  }
+  row_lse(part, sg, bh, I, kI, lse, tid);
   __syncthreads();
-  const int cpb = sg.ncell / sg.nb;   // cells per block: 1, or k / 64
   const float* t0 = tmax + ((int64_t)bh * sg.nsp + (int64_t)I * sg.k) * sg.ncell;
   float* prow = p_imp + ((int64_t)bh * sg.nb + I) * sg.nb;
-  for (int J = tid; J < sg.nb; J += kFinalThreads) {
-    float best = -INFINITY;
-    // 8 sampled queries at a time, their loads issued together
-    for (int t0q = 0; t0q < kI; t0q += 8) {
-      float v[8];
+  for (int J = tid; J < sg.nb; J += kFinalThreads) prow[J] = pimp_value(lse, t0, sg, kI, J, sl2);
+}
+
+// The lane's KPL consecutive P_imp entries J = lane * KPL + r of one row, all
+// loads of a group of 16 sampled queries in flight together.  vec: one block
+// per cell and 4 * KPL-byte aligned rows, so each sampled query's KPL maxima
+// arrive in one vector load (a wavefront reads a contiguous row).  Same terms
+// and the same exact max as pimp_value, so the same bits.
+template <int KPL>
+__device__ __forceinline__ void pimp_lane(const float* lse, const float* __restrict__ t0, const SampleGeom& sg, int kI,
+                                          int lane, float sl2, bool vec, uint32_t (&out)[KPL]) {
+  float best[KPL];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int t = min(t0q + e, kI - 1);
-        const float* tr = t0 + (int64_t)t * sg.ncell + J * cpb;
-        v[e] = tr[0];
-        for (int c = 1; c < cpb; ++c) v[e] = fmaxf(v[e], tr[c]);
-      }
+  for (int r = 0; r < KPL; ++r) best[r] = -INFINITY;
+  const int J0 = lane * KPL;
+  if (vec) {
+    typedef float vf __attribute__((ext_vector_type(KPL)));
+    if (J0 < sg.nb) {
+      for (int t0q = 0; t0q < kI; t0q += 16) {
+        vf v[16];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int t = min(t0q + e, kI - 1);
-        best = fmaxf(best, __builtin_fmaf(v[e], sl2, -lse[t]));
+        for (int e = 0; e < 16; ++e) {
+          const int t = min(t0q + e, kI - 1);
+          v[e] = *reinterpret_cast<const vf*>(t0 + (int64_t)t * sg.ncell + J0);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float l = lse[min(t0q + e, kI - 1)];
+#pragma unroll
+          for (int r = 0; r < KPL; ++r) best[r] = fmaxf(best[r], __builtin_fmaf(v[e][r], sl2, -l));
+        }
       }
     }
-    prow[J] = fast_exp2(best);
+  } else {
+    const int cpb = sg.ncell / sg.nb;
+    for (int t0q = 0; t0q < kI; t0q += 8) {
+      float v[8][KPL];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int t = min(t0q + e, kI - 1);
+#pragma unroll
+        for (int r = 0; r < KPL; ++r) {
+          const int J = min(J0 + r, sg.nb - 1);
+          const float* tr = t0 + (int64_t)t * sg.ncell + J * cpb;
+          v[e][r] = tr[0];
+          for (int c = 1; c < cpb; ++c) v[e][r] = fmaxf(v[e][r], tr[c]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float l = lse[min(t0q + e, kI - 1)];
+#pragma unroll
+        for (int r = 0; r < KPL; ++r) best[r] = fmaxf(best[r], __builtin_fmaf(v[e][r], sl2, -l));
+      }
+    }
   }
+#pragma unroll
+  for (int r = 0; r < KPL; ++r) out[r] = J0 + r < sg.nb ? __float_as_uint(fast_exp2(best[r])) : 0u;
+}
+
+// The final step fused with the block selection (the a3 + a4 fusion that
+// SPADE's prepass suggests): each P_imp row goes from registers or LDS
+// straight into the mask selection and reaches HBM only when p_imp is given.
+// Rows of up to 256 blocks: one wavefront per row, four per workgroup; lane l
+// forms entries l * KPL .. l * KPL + KPL - 1, the layout the register sort
+// takes.
+template <int KPL>
+__global__ __launch_bounds__(256) void est_mask_wave_kernel(const float2* __restrict__ part,
+                                                            const float* __restrict__ tmax, SampleGeom sg, float sl2,
+                                                            maskcore::Rule rule, float* __restrict__ p_imp,
+                                                            int32_t* __restrict__ kv_count,
+                                                            int32_t* __restrict__ kv_idx,
+                                                            uint8_t* __restrict__ mask) {
+  __shared__ float lse_all[4][kMaxK];
+  __shared__ uint8_t flag_all[4][64 * KPL];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int I = blockIdx.x * 4 + w, bh = blockIdx.y;
+  if (I >= sg.nb) return;   // whole wavefronts; no workgroup barrier follows
+  const int kI = I < sg.nb - 1 ? sg.k : sg.kj_last;
+  float* lse = lse_all[w];
+  for (int i = lane; i < sg.k; i += 64) row_lse(part, sg, bh, I, kI, lse, i);
+  __builtin_amdgcn_wave_barrier();
+  const int64_t row = (int64_t)bh * sg.nb + I;
+  const float* t0 = tmax + ((int64_t)bh * sg.nsp + (int64_t)I * sg.k) * sg.ncell;
+  const bool vec = sg.ncell == sg.nb && sg.nb % KPL == 0 && ((uintptr_t)tmax & (4 * KPL - 1)) == 0;
+  uint32_t in[KPL];
+  pimp_lane<KPL>(lse, t0, sg, kI, lane, sl2, vec, in);
+  if (p_imp != nullptr) {
+#pragma unroll
+    for (int r = 0; r < KPL; ++r)
+      if (lane * KPL + r < sg.nb) p_imp[row * sg.nb + lane * KPL + r] = __uint_as_float(in[r]);
+  }
+  maskcore::mask_row_wave<KPL>(in, row, sg.nb, rule, flag_all[w], kv_count, kv_idx, mask);
+}
+
+// Longer rows: one workgroup per row, the LDS sort.
+template <int kCap>
+__global__ __launch_bounds__(256) void est_mask_lds_kernel(const float2* __restrict__ part,
+                                                           const float* __restrict__ tmax, SampleGeom sg, float sl2,
+                                                           maskcore::Rule rule, float* __restrict__ p_imp,
+                                                           int32_t* __restrict__ kv_count,
+                                                           int32_t* __restrict__ kv_idx,
+                                                           uint8_t* __restrict__ mask) {
+  __shared__ float lse[kMaxK];
+  const int I = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int kI = I < sg.nb - 1 ? sg.k : sg.kj_last;
+  row_lse(part, sg, bh, I, kI, lse, tid);
+  __syncthreads();
+  const int64_t row = (int64_t)bh * sg.nb + I;
+  const float* t0 = tmax + ((int64_t)bh * sg.nsp + (int64_t)I * sg.k) * sg.ncell;
+  float* prow = p_imp != nullptr ? p_imp + row * sg.nb : nullptr;
+  maskcore::mask_row_lds<kCap, 256>(
+      [&](int J) {
+        const float v = pimp_value(lse, t0, sg, kI, J, sl2);
+        if (prow != nullptr) prow[J] = v;
+        return __float_as_uint(v);
+      },
+      row, sg.nb, rule, kv_count, kv_idx, mask);
 }
 
 // Key splits: about 768 workgroups in total (one and a half rounds of two
@@ -561,8 +692,37 @@ hipError_t launch_d(const EstimateArgs& a) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(est_final_kernel, dim3((unsigned)a.nb, (unsigned)BH), dim3(kFinalThreads), 0, a.stream,
-                     (const float2*)part, (const float*)tmax, a.p_imp, sg, sl2);
+  if (a.fuse == nullptr) {
+    hipLaunchKernelGGL(est_final_kernel, dim3((unsigned)a.nb, (unsigned)BH), dim3(kFinalThreads), 0, a.stream,
+                       (const float2*)part, (const float*)tmax, a.p_imp, sg, sl2);
+    return hipGetLastError();
+  }
+  const MaskArgs& m = *a.fuse;
+  const maskcore::Rule rule = maskcore::make_rule(m.rule, m.tau, m.topk, m.u);
+  const float2* cp = part;
+  const float* ct = tmax;
+  const dim3 wgrid((unsigned)((a.nb + 3) / 4), (unsigned)BH), rgrid((unsigned)a.nb, (unsigned)BH);
+  if (a.nb <= 64) {
+    hipLaunchKernelGGL((est_mask_wave_kernel<1>), wgrid, dim3(256), 0, a.stream, cp, ct, sg, sl2, rule, a.p_imp,
+                       m.kv_count, m.kv_idx, m.mask);
+  } else if (a.nb <= 128) {
+    hipLaunchKernelGGL((est_mask_wave_kernel<2>), wgrid, dim3(256), 0, a.stream, cp, ct, sg, sl2, rule, a.p_imp,
+                       m.kv_count, m.kv_idx, m.mask);
+  } else if (a.nb <= 256) {
+    hipLaunchKernelGGL((est_mask_wave_kernel<4>), wgrid, dim3(256), 0, a.stream, cp, ct, sg, sl2, rule, a.p_imp,
+                       m.kv_count, m.kv_idx, m.mask);
+  } else if (a.nb <= 1024) {
+    hipLaunchKernelGGL((est_mask_lds_kernel<1024>), rgrid, dim3(256), 0, a.stream, cp, ct, sg, sl2, rule, a.p_imp,
+                       m.kv_count, m.kv_idx, m.mask);
+  } else {
+    hipLaunchKernelGGL((est_mask_lds_kernel<maskcore::kMaxNb>), rgrid, dim3(256), 0, a.stream, cp, ct, sg, sl2,
+                       rule, a.p_imp, m.kv_count, m.kv_idx, m.mask);
+  }
+  if (m.order != nullptr) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_build_order(m);
+  }
   return hipGetLastError();
 }
 

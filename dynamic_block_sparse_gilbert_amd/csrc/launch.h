@@ -51,6 +51,7 @@ struct EstimateArgs {
   int B, Hh, N, Npad, d, b, k, nb;
   float scale;
   TokIO tok;            // tok.q set: sampled Q rows gathered in token order (out unused)
+  const struct MaskArgs* fuse;   // set: the final launch also selects the kept blocks (p_imp nullable)
   hipStream_t stream;
 };
 
@@ -121,6 +122,7 @@ hipError_t launch_meanpool(const MeanpoolArgs& a);
 hipError_t launch_estimate(const EstimateArgs& a);
 size_t estimate_workspace_bytes(int B, int Hh, int nb, int k, int d);
 hipError_t launch_build_mask(const MaskArgs& a);
+hipError_t launch_build_order(const MaskArgs& a);   // a.kv_count -> a.order only
 hipError_t launch_attn_fwd(const AttnArgs& a);
 hipError_t launch_transpose_lists(const TransposeListsArgs& a);
 size_t attn_bwd_workspace_bytes(int B, int Hh, int Npad, int d);

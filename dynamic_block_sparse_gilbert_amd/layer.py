@@ -72,8 +72,11 @@ def build_perm(spec: LayerSpec) -> np.ndarray:
 class AsaLayer:
     """Holds the device permutation and the intermediate buffers of one layer shape."""
 
-    def __init__(self, spec: LayerSpec, device="cuda"):
+    def __init__(self, spec: LayerSpec, device="cuda", fused: bool = True):
+        """fused: the estimate and the mask in one call (dbs_estimate_mask_tok; P_imp is then not
+        written unless mask(keep_p_imp=True)), else dbs_estimate_blocks_tok + dbs_build_mask."""
         self.spec = spec
+        self.fused = fused
         self.device = torch.device(device)
         self.perm = torch.from_numpy(build_perm(spec)).to(self.device)
         s = spec
@@ -104,11 +107,17 @@ class AsaLayer:
         if s.n_pool:
             ops.meanpool_kv(self.k_r, self.v_t, s.N, s.b, s.n_pool, k_g=self.k_g, v_g=self.v_g)
 
-    def mask(self, tau: Optional[float] = None) -> None:
+    def mask(self, tau: Optional[float] = None, keep_p_imp: bool = False) -> None:
         s = self.spec
+        tau = s.tau if tau is None else tau
+        if self.fused:
+            ops.estimate_mask(self.q, self.k_r, s.N, s.b, s.k, s.scale, "cumulative", tau, q_perm=self.perm,
+                              kv_count=self.kv_count, kv_idx=self.kv_idx, order=self.order, workspace=self.ws,
+                              p_imp=self.p_imp if keep_p_imp else None)
+            return
         ops.estimate_blocks_tok(self.q, self.perm, self.k_r, s.N, s.b, s.k, s.scale, p_imp=self.p_imp,
                                 workspace=self.ws)
-        ops.build_mask(self.p_imp, s.tau if tau is None else tau, kv_count=self.kv_count, kv_idx=self.kv_idx,
+        ops.build_mask(self.p_imp, tau, kv_count=self.kv_count, kv_idx=self.kv_idx,
                        order=self.order)
 
     def attend(self, out: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16) -> torch.Tensor:
@@ -119,7 +128,8 @@ class AsaLayer:
         return out
 
     def forward(self, q, k, v, out: Optional[torch.Tensor] = None, tau: Optional[float] = None,
-                out_dtype=torch.bfloat16) -> torch.Tensor:
+                out_dtype=torch.bfloat16, keep_p_imp: bool = False) -> torch.Tensor:
+        """keep_p_imp: also write P_imp to self.p_imp (always written on the unfused path)."""
         self.prepare(q, k, v)
-        self.mask(tau)
+        self.mask(tau, keep_p_imp)
         return self.attend(out, out_dtype)

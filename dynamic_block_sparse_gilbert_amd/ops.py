@@ -221,6 +221,44 @@ def build_mask_rule(p_imp: torch.Tensor, rule: str, param: float, kv_count: Opti
     return kv_count, kv_idx, mask
 
 
+def estimate_mask(q_r: torch.Tensor, k_r: torch.Tensor, N: int, b: int, k: int, scale: float, rule: str,
+                  param: float, q_perm: Optional[torch.Tensor] = None, want_p_imp: bool = False,
+                  want_mask: bool = False, kv_count: Optional[torch.Tensor] = None,
+                  kv_idx: Optional[torch.Tensor] = None, order: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, p_imp: Optional[torch.Tensor] = None):
+    """The estimate and the block selection in one call (dbs_estimate_mask, or with q_perm
+    dbs_estimate_mask_tok: q is then [B, N, Hh, d] in token order).  k_r rows [B, Hh, Npad, d].
+    Returns (kv_count, kv_idx, mask or None, p_imp or None); P_imp is written when want_p_imp or a
+    p_imp buffer is given."""
+    _dev(q_r, q_perm, k_r, kv_count, kv_idx, order, workspace, p_imp)
+    B, Hh, Npad, d = k_r.shape
+    nb = Npad // b
+    dv = k_r.device
+    if kv_count is None:
+        kv_count = torch.empty((B, Hh, nb), dtype=torch.int32, device=dv)
+    if kv_idx is None:
+        kv_idx = torch.empty((B, Hh, nb, nb), dtype=torch.int32, device=dv)
+    mask = torch.empty((B, Hh, nb, nb), dtype=torch.uint8, device=dv) if want_mask else None
+    if p_imp is None and want_p_imp:
+        p_imp = torch.empty((B, Hh, nb, nb), dtype=torch.float32, device=dv)
+    need = estimate_workspace_bytes(B, Hh, N, d, b, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dv)
+    wsb = workspace.numel() * workspace.element_size()
+    tail = (b, k, float(scale), MASK_RULES[rule], float(param), _p(p_imp), _p(kv_count), _p(kv_idx), _p(mask),
+            _p(order), _p(workspace), wsb, _stream())
+    if q_perm is None:
+        check("dbs_estimate_mask", lib().dbs_estimate_mask(_p(q_r), _p(k_r), _dt(q_r), B, Hh, N, Npad, d, *tail))
+    else:
+        if q_r.stride(3) != 1:
+            raise ValueError("the d axis of q must be contiguous")
+        per_head = 1 if q_perm.dim() == 2 else 0
+        check("dbs_estimate_mask_tok", lib().dbs_estimate_mask_tok(
+            _p(q_r), _dt(q_r), q_r.stride(0), q_r.stride(1), q_r.stride(2), _p(q_perm), per_head, _p(k_r),
+            B, Hh, N, Npad, d, *tail))
+    return kv_count, kv_idx, mask, p_imp
+
+
 def meanpool_kv(k_r: torch.Tensor, v_t: torch.Tensor, N: int, b: int, n: int,
                 k_g: Optional[torch.Tensor] = None, v_g: Optional[torch.Tensor] = None
                 ) -> Tuple[torch.Tensor, torch.Tensor, int]:

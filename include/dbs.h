@@ -20,6 +20,9 @@
  *   dbs_build_mask
  *   dbs_sparse_attn_fwd_tok                            Q read, O written in token order
  *
+ * where dbs_estimate_mask_tok may stand for the estimate and mask pair: it
+ * selects the kept blocks from each P_imp row on chip (P_imp optional).
+ *
  * Conventions for every call:
  * - Device pointers are allocated and owned by the caller and must be 16-byte
  *   aligned.  The library allocates no device memory and keeps no device state.
@@ -53,7 +56,7 @@
 extern "C" {
 #endif
 
-#define DBS_ABI_VERSION 6
+#define DBS_ABI_VERSION 7
 
 typedef enum {
   DBS_OK = 0,
@@ -221,6 +224,30 @@ typedef enum { DBS_RULE_CUMULATIVE = 0, DBS_RULE_TOPK = 1, DBS_RULE_STAT = 2 } d
 dbs_status dbs_build_mask_rule(const float* p_imp, int B, int Hh, int nb, int rule, double param,
                                int32_t* kv_count, int32_t* kv_idx, uint8_t* mask, int32_t* order,
                                hipStream_t stream);
+
+/* Estimation and selection in one pass over the estimator's intermediate
+ * results (the fusion of the importance estimate with the mask builder that
+ * SPADE's fused prepass suggests): the same kv_count / kv_idx / mask / order
+ * as dbs_estimate_blocks followed by dbs_build_mask_rule(rule, param), bit for
+ * bit, but each P_imp row is formed on chip and handed straight to the
+ * selection.  p_imp (nullable): when given, P_imp is written as well, equal
+ * to dbs_estimate_blocks' output.  Inputs, workspace and limits as for
+ * dbs_estimate_blocks, outputs and rules as for dbs_build_mask_rule
+ * (nb <= 4096); the errors of both. */
+dbs_status dbs_estimate_mask(const void* q_r, const void* k_r, dbs_dtype dt,
+                             int B, int Hh, int N, int Npad, int d, int b, int k, float scale,
+                             int rule, double param, float* p_imp,
+                             int32_t* kv_count, int32_t* kv_idx, uint8_t* mask, int32_t* order,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* dbs_estimate_mask with Q read in token order, as dbs_estimate_blocks_tok
+ * reads it (same q, q_dt, strides and perm arguments). */
+dbs_status dbs_estimate_mask_tok(const void* q, dbs_dtype q_dt, int64_t sb, int64_t sn, int64_t sh,
+                                 const int32_t* perm, int perm_per_head, const void* k_r,
+                                 int B, int Hh, int N, int Npad, int d, int b, int k, float scale,
+                                 int rule, double param, float* p_imp,
+                                 int32_t* kv_count, int32_t* kv_idx, uint8_t* mask, int32_t* order,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ASA_G global tokens (Video-BLADE "Step 2.2 (2)"; BLADE notes key design 2):
  * mean of each window of n consecutive reordered tokens,

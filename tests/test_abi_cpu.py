@@ -37,7 +37,7 @@ def test_all_declared_symbols_exported(dbs):
     for n in names:
         assert hasattr(h, n), n
     assert set(names) == set(L.SIGNATURES), set(names) ^ set(L.SIGNATURES)
-    assert L.lib().dbs_abi_version() == 6
+    assert L.lib().dbs_abi_version() == 7
 
 
 @pytest.mark.parametrize("T,H,W", list(itertools.product(range(1, 7), repeat=3)))
@@ -257,6 +257,40 @@ def test_mask_rule_validation(dbs):
     assert f(A, 1, 1, 16, 2, float("nan"), A, A, None, None, None) == -1  # u not finite
     assert f(A, 1, 1, 4097, 2, 1.0, A, A, None, None, None) == -2         # nb > 4096
     assert f(0, 1, 1, 16, 2, 1.0, A, A, None, None, None) == -1           # NULL
+
+
+@cpu_only
+def test_estimate_mask_validation(dbs):
+    _, L = dbs
+    f = L.lib().dbs_estimate_mask
+    ws = L.lib().dbs_estimate_workspace_bytes(1, 2, 100, 128, 64, 8)
+    # q_r, k_r, dt, B, Hh, N, Npad, d, b, k, scale, rule, param, p_imp, kv_count, kv_idx, mask, order, ws, wsb, s
+    ok = [A, A, 0, 1, 2, 100, 128, 128, 64, 8, 0.125, 0, 0.9, None, A, A, None, None, A, ws, None]
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return f(*a)
+    assert call(0, 0) == -1               # q NULL
+    assert call(14, 0) == -1              # kv_count NULL
+    assert call(15, 0) == -1              # kv_idx NULL
+    assert call(13, A + 4) == -3          # misaligned p_imp (16 bytes, as dbs_estimate_blocks)
+    assert call(17, A + 2) == -3          # misaligned order
+    assert call(11, 9) == -1              # unknown rule
+    assert call(12, 1.5) == -1            # tau > 1
+    assert call(9, 3) == -2               # k not a power of two
+    assert call(19, ws - 1) == -1         # small workspace
+    assert call(10, float("nan")) == -1   # scale
+    g = L.lib().dbs_estimate_mask_tok
+    okt = [A, 0, 100 * 2 * 128, 2 * 128, 128, A, 0, A, 1, 2, 100, 128, 128, 64, 8, 0.125, 1, 4.0, None, A, A, None,
+           None, A, ws, None]
+    def callt(i, v):
+        a = list(okt)
+        a[i] = v
+        return g(*a)
+    assert callt(5, 0) == -1              # perm NULL
+    assert callt(17, 0.5) == -1           # top-k count not an integer >= 1
+    assert callt(20, 0) == -1             # kv_idx NULL
+    assert callt(24, ws - 1) == -1        # small workspace
 
 
 @cpu_only

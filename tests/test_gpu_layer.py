@@ -55,10 +55,10 @@ def _check_layer(cfg, heads, tau, sample_blocks=None, p_heads=None, seed=0):
     if cfg.dtype == "fp32":
         # float32 storage: the reorder rounds to bf16, the compute type; the
         # oracle gets those same rounded values
-        out = layer.forward(dev(q), dev(k), dev(v), out_dtype=torch.float32)
+        out = layer.forward(dev(q), dev(k), dev(v), out_dtype=torch.float32, keep_p_imp=True)
         q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
     else:
-        out = layer.forward(dev_bf16(q), dev_bf16(k), dev_bf16(v), out_dtype=torch.float32)
+        out = layer.forward(dev_bf16(q), dev_bf16(k), dev_bf16(v), out_dtype=torch.float32, keep_p_imp=True)
     torch.cuda.synchronize()
     P, cnt, idx, out = host(layer.p_imp), host(layer.kv_count), host(layer.kv_idx), host(out)
     qr, kr, vr = (o_reorder(x, perm, cfg.Npad) for x in (q, k, v))
