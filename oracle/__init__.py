@@ -10,7 +10,7 @@ Modules: perm (curve and cuboid orders), reorder (gather / scatter), estimator
 (sampled block importance), mask (cumulative-threshold mask), mask_rules
 (the top-k and statistical-threshold alternatives), attention
 (block-masked attention with optional global tokens), attention_bwd (its
-gradients, plain ASA, and the key-to-query block lists), accounting (sparsity
-and FLOP).  Every function is pinned by CPU tests against closed forms, invariants
+gradients, plain ASA, and the key-to-query block lists), query_prune (BSA
+query pruning and token filling), accounting (sparsity and FLOP).  Every function is pinned by CPU tests against closed forms, invariants
 and brute force (tests/test_oracle_*.py).
 """
