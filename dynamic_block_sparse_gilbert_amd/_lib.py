@@ -41,6 +41,12 @@ SIGNATURES = {
                                      _vp, _vp, C.c_size_t, _vp]),
     "dbs_build_mask": (_i, [_vp, _i, _i, _i, _f, _vp, _vp, _vp, _vp, _vp]),
     "dbs_build_mask_rule": (_i, [_vp, _i, _i, _i, _i, C.c_double, _vp, _vp, _vp, _vp, _vp]),
+    "dbs_prune_anchors": (_i, [_i, _i, _i, _i, _i, _i, _i, _vp, _vp]),
+    "dbs_query_prune": (_i, [_vp, _i, _i64, _i64, _i64, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, C.c_double, _vp, _vp,
+                             _vp, _vp]),
+    "dbs_sparse_attn_fwd_pruned_tok": (_i, [_vp, _i, _i64, _i64, _i64, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i,
+                                            _f, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i64, _i64, _i64, _vp,
+                                            _vp]),
     "dbs_estimate_mask": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, C.c_double, _vp, _vp, _vp, _vp,
                                _vp, _vp, C.c_size_t, _vp]),
     "dbs_estimate_mask_tok": (_i, [_vp, _i, _i64, _i64, _i64, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i,

@@ -30,6 +30,7 @@ SOURCES = [
     "kernels/mask.hip",
     "kernels/attn.hip",
     "kernels/attn_bwd.hip",
+    "kernels/prune.hip",
 ]
 
 # Packed fp32 VALU ops are disabled on purpose: only plain fp32 ops are emitted.

@@ -131,6 +131,41 @@ dbs_status dbs_perm_invert(const int32_t* perm, int n, int32_t* inv_out) {
   DBS_GUARD_END
 }
 
+dbs_status dbs_prune_anchors(int T, int H, int W, int prefix, int wt, int wh, int ww, const int32_t* perm,
+                             int32_t* anchor_out) {
+  DBS_GUARD_BEGIN
+  dbs_status st = check_grid(T, H, W, prefix, anchor_out);
+  if (st != DBS_OK) return st;
+  REQUIRE(perm != nullptr, DBS_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(wt >= 1 && wh >= 1 && ww >= 1, DBS_ERR_INVALID_ARG, "window sides must be >= 1");
+  const int n = prefix + T * H * W;
+  std::vector<int32_t> inv(n, -1);
+  for (int i = 0; i < n; ++i) {
+    const int32_t p = perm[i];
+    REQUIRE(p >= 0 && p < n && inv[p] == -1, DBS_ERR_INVALID_ARG, "not a permutation: entry %d is %d", i, p);
+    inv[p] = i;
+  }
+  // centre of the window holding x along an axis of n cells: offset (e - 1) / 2 in
+  // a window of extent e (windows tile from the origin; the last may be cut)
+  auto centre = [](int x, int w, int len) {
+    const int x0 = x / w * w;
+    const int e = (x0 + w < len ? x0 + w : len) - x0;
+    return x0 + (e - 1) / 2;
+  };
+  for (int i = 0; i < n; ++i) {
+    const int tok = perm[i];
+    int a = tok;
+    if (tok >= prefix) {
+      const int r = tok - prefix;
+      const int t = r / (H * W), h = r / W % H, w = r % W;
+      a = prefix + (centre(t, wt, T) * H + centre(h, wh, H)) * W + centre(w, ww, W);
+    }
+    anchor_out[i] = inv[a];
+  }
+  return ok();
+  DBS_GUARD_END
+}
+
 dbs_status dbs_reorder(const void* x, dbs_dtype x_dt, int64_t sb, int64_t sn, int64_t sh, void* y,
                        dbs_dtype y_dt, dbs_layout y_layout, const int32_t* perm, int perm_per_head,
                        int B, int Hh, int N, int Npad, int d, int b, hipStream_t stream) {
@@ -411,7 +446,8 @@ namespace {
 dbs_status attn_impl(const void* q_r, const void* k_r, const void* v_r, int B, int Hh, int N, int Npad, int d,
                      int b, float scale, const int32_t* kv_count, const int32_t* kv_idx, const int32_t* order,
                      const void* k_g, const void* v_g, int Ng, int n_pool, void* o_r, float* lse,
-                     const dbs::TokIO& tok, hipStream_t stream) {
+                     const dbs::TokIO& tok, hipStream_t stream, const int32_t* q_count = nullptr,
+                     const int32_t* rowsel = nullptr) {
   REQUIRE(k_r && v_r && kv_count && kv_idx, DBS_ERR_INVALID_ARG, "NULL pointer");
   REQUIRE(aligned16(k_r) && aligned16(v_r), DBS_ERR_ALIGNMENT, "misaligned pointer");
   REQUIRE(((uintptr_t)kv_count & 3u) == 0 && ((uintptr_t)kv_idx & 3u) == 0 && ((uintptr_t)lse & 3u) == 0 &&
@@ -432,6 +468,7 @@ dbs_status attn_impl(const void* q_r, const void* k_r, const void* v_r, int B, i
   a.k_g = k_g; a.v_g = v_g; a.o_r = o_r; a.lse = lse;
   a.B = B; a.Hh = Hh; a.N = N; a.Npad = Npad; a.d = d; a.b = b; a.nb = Npad / b;
   a.Ng = k_g ? Ng : 0; a.n_pool = k_g ? n_pool : 1; a.scale = scale; a.tok = tok; a.stream = stream;
+  a.q_count = q_count; a.rowsel = rowsel;
   REQUIRE(a.nb <= 4096, DBS_ERR_UNSUPPORTED, "nb=%d must be <= 4096", a.nb);
   REQUIRE((int64_t)B * Hh * a.nb <= INT32_MAX, DBS_ERR_INVALID_ARG, "too many query blocks");
   return from_hip(dbs::launch_attn_fwd(a), "dbs_sparse_attn_fwd launch");
@@ -479,6 +516,59 @@ dbs_status dbs_sparse_attn_fwd_tok(const void* q, dbs_dtype q_dt, int64_t qsb, i
 }  // extern "C"
 
 extern "C" {
+
+dbs_status dbs_query_prune(const void* q, dbs_dtype q_dt, int64_t sb, int64_t sn, int64_t sh, const int32_t* perm,
+                           int perm_per_head, const int32_t* anchor, int B, int Hh, int N, int Npad, int d, int b,
+                           double r, int32_t* q_count, int32_t* rowsel, uint8_t* keep, hipStream_t stream) {
+  DBS_GUARD_BEGIN
+  dbs_status st = check_tok(q, q_dt, sb, sn, sh, perm, perm_per_head);
+  if (st != DBS_OK) return st;
+  REQUIRE(anchor && q_count && rowsel && keep, DBS_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(((uintptr_t)anchor & 3u) == 0 && ((uintptr_t)q_count & 3u) == 0 && ((uintptr_t)rowsel & 3u) == 0,
+          DBS_ERR_ALIGNMENT, "misaligned pointer");
+  st = check_geometry(B, Hh, N, Npad, d, b);
+  if (st != DBS_OK) return st;
+  REQUIRE(std::isfinite(r) && r > 0.0 && r <= 1.0, DBS_ERR_INVALID_ARG, "keep ratio r=%g must be in (0, 1]", r);
+  REQUIRE((int64_t)B * Hh * (Npad / b) <= INT32_MAX / 2, DBS_ERR_INVALID_ARG, "too many query blocks");
+  dbs::PruneArgs a{};
+  a.q = q; a.qsb = sb; a.qsn = sn; a.qsh = sh; a.q_f32 = q_dt == DBS_FP32;
+  a.perm = perm; a.anchor = anchor; a.perm_h_stride = perm_per_head ? N : 0;
+  a.B = B; a.Hh = Hh; a.N = N; a.Npad = Npad; a.d = d; a.b = b; a.nb = Npad / b; a.r = r;
+  a.q_count = q_count; a.rowsel = rowsel; a.keep = keep; a.stream = stream;
+  return from_hip(dbs::launch_query_prune(a), "dbs_query_prune launch");
+  DBS_GUARD_END
+}
+
+dbs_status dbs_sparse_attn_fwd_pruned_tok(const void* q, dbs_dtype q_dt, int64_t qsb, int64_t qsn, int64_t qsh,
+                                          const int32_t* perm, int perm_per_head, const void* k_r, const void* v_r,
+                                          int B, int Hh, int N, int Npad, int d, int b, float scale,
+                                          const int32_t* kv_count, const int32_t* kv_idx, const int32_t* order,
+                                          const int32_t* q_count, const int32_t* rowsel, const int32_t* anchor,
+                                          const uint8_t* keep, void* out, dbs_dtype out_dt, int64_t osb,
+                                          int64_t osn, int64_t osh, float* lse, hipStream_t stream) {
+  DBS_GUARD_BEGIN
+  dbs_status st = check_tok(q, q_dt, qsb, qsn, qsh, perm, perm_per_head);
+  if (st != DBS_OK) return st;
+  st = check_tok(out, out_dt, osb, osn, osh, perm, perm_per_head);
+  if (st != DBS_OK) return st;
+  REQUIRE(q_count && rowsel && anchor && keep, DBS_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(((uintptr_t)q_count & 3u) == 0 && ((uintptr_t)rowsel & 3u) == 0 && ((uintptr_t)anchor & 3u) == 0,
+          DBS_ERR_ALIGNMENT, "misaligned pointer");
+  dbs::TokIO tok{};
+  tok.q = q; tok.q_f32 = q_dt == DBS_FP32; tok.qsb = qsb; tok.qsn = qsn; tok.qsh = qsh;
+  tok.out = out; tok.out_f32 = out_dt == DBS_FP32; tok.osb = osb; tok.osn = osn; tok.osh = osh;
+  tok.perm = perm; tok.perm_h_stride = perm_per_head ? N : 0;
+  st = attn_impl(nullptr, k_r, v_r, B, Hh, N, Npad, d, b, scale, kv_count, kv_idx, order, nullptr, nullptr, 0, 1,
+                 nullptr, lse, tok, stream, q_count, rowsel);
+  if (st != DBS_OK) return st;
+  dbs::FillArgs f{};
+  f.out = out; f.osb = osb; f.osn = osn; f.osh = osh; f.out_f32 = out_dt == DBS_FP32;
+  f.row_bytes = d * (out_dt == DBS_FP32 ? 4 : 2);
+  f.perm = perm; f.anchor = anchor; f.perm_h_stride = perm_per_head ? N : 0; f.keep = keep; f.lse = lse;
+  f.B = B; f.Hh = Hh; f.N = N; f.Npad = Npad; f.stream = stream;
+  return from_hip(dbs::launch_fill_pruned(f), "token filling launch");
+  DBS_GUARD_END
+}
 
 dbs_status dbs_transpose_lists(const int32_t* kv_count, const int32_t* kv_idx, int B, int Hh, int nb,
                                int32_t* kvT_count, int32_t* kvT_idx, hipStream_t stream) {

@@ -56,10 +56,10 @@ namespace {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
-template <int D, int BLK>
+template <int D, int BLK, int QB = BLK>
 struct AttnCfg {
   static constexpr int kQW = 32;                 // query rows per wavefront
-  static constexpr int kWaves = BLK / kQW;       // 4 for BLK = 128, 2 for BLK = 64
+  static constexpr int kWaves = QB / kQW;        // query rows per workgroup / 32: 4 for QB = 128, 2 for 64
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kKT = 64;                 // keys per stage
   static constexpr int kSubs = BLK / kKT;        // stages per block
@@ -129,16 +129,22 @@ struct StageDesc {
   int limit;           // keys with index >= limit are masked (kind 1, 2)
 };
 
-template <int D, int BLK>
-__global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// QB: query rows per workgroup (BLK, or 64 with BLK = 128 for pruned
+// queries).  PR: pruned queries (BSA query pruning): work item (block, sub)
+// takes rows sub * QB .. of the block's kept-row list rowsel (q_count[block]
+// of them); a sub-tile past the count exits at once.
+template <int D, int BLK, int QB, bool PR>
+__global__ __launch_bounds__(QB / 32 * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(
     const __bf16* __restrict__ q_r, const __bf16* __restrict__ k_r, const __bf16* __restrict__ v_t,
     const int32_t* __restrict__ kv_count, const int32_t* __restrict__ kv_idx,
     const int32_t* __restrict__ order,
     const __bf16* __restrict__ k_g, const __bf16* __restrict__ v_g,
     __bf16* __restrict__ o_r, float* __restrict__ lse,
-    int Hh, int N, int Npad, int nb, int Ng, float sl2, float bias_n, float bias_last, int total, TokIO tok) {
-  using C = AttnCfg<D, BLK>;
+    int Hh, int N, int Npad, int nb, int Ng, float sl2, float bias_n, float bias_last, int total, TokIO tok,
+    const int32_t* __restrict__ q_count, const int32_t* __restrict__ rowsel) {
+  using C = AttnCfg<D, BLK, QB>;
+  constexpr int kSubQ = BLK / QB;   // work items per query block
   // Four distinct arrays whose roles are static in each half of the 2x-unrolled
   // pipeline, so the compiler can prove LDS reads never alias a DMA in flight
   // and does not make them wait for it.
@@ -156,12 +162,26 @@ void attn_fwd_kernel(
   // Work item: this XCD's next entry of the schedule (longest query blocks
   // first when build_mask wrote one), clamped so a bad schedule stays in bounds.
   const int slot = xcd_remap(blockIdx.x, total);
-  const int wid = order == nullptr ? slot
-                                   : min(max(__builtin_amdgcn_readfirstlane(order[slot]), 0), total - 1);
+  const int rows_total = total / kSubQ;
+  const int wid = order == nullptr ? slot / kSubQ
+                                   : min(max(__builtin_amdgcn_readfirstlane(order[slot / kSubQ]), 0),
+                                         rows_total - 1);
   const int I = wid % nb;
   const int bh = wid / nb;
-  const int q0 = I * BLK + wave * C::kQW;
   const int64_t rowbase = (int64_t)bh * Npad;
+  // this lane's query row (reordered index) and whether it is one
+  int qrow = I * BLK + wave * C::kQW + l32;
+  bool qvalid = qrow < N;
+  if constexpr (PR) {
+    const int sub = slot % kSubQ;
+    int mq = __builtin_amdgcn_readfirstlane(q_count[(int64_t)bh * nb + I]);
+    mq = mq < 0 ? 0 : (mq > BLK ? BLK : mq);
+    if (sub * QB >= mq) return;   // the whole workgroup, before any barrier
+    const int s = sub * QB + wave * C::kQW + l32;
+    qrow = s < mq ? rowsel[((int64_t)bh * nb + I) * BLK + s] : -1;
+    qvalid = qrow >= 0 && qrow < N;
+    if (!qvalid) qrow = 0;
+  }
 
   int cnt = __builtin_amdgcn_readfirstlane(kv_count[(int64_t)bh * nb + I]);
   cnt = cnt < 0 ? 0 : (cnt > nb ? nb : cnt);
@@ -423,7 +443,7 @@ void attn_fwd_kernel(
   // gather waits for the token lookup only.
   const int jt = threadIdx.x < cnt ? idx[threadIdx.x] : 0;
 
-  // Q^T operand: lane (l32, g) holds Q[q0 + l32][16 kk + 8 g .. +7], from the
+  // Q^T operand: lane (l32, g) holds Q[qrow][16 kk + 8 g .. +7], from the
   // reordered rows or, in token order, from the row's token (bf16, or float32
   // rounded to bf16 as the reorder rounds it; rows >= N are zero).
   const int bi = bh / Hh, hh = bh % Hh;
@@ -432,7 +452,7 @@ void attn_fwd_kernel(
     return t < 0 ? 0 : (t >= N ? N - 1 : t);
   };
   // token of this lane's query row (used again by the epilogue)
-  const int qtok = (tok.perm != nullptr && q0 + l32 < N) ? token_of(q0 + l32) : 0;
+  const int qtok = (tok.perm != nullptr && qvalid) ? token_of(qrow) : 0;
 
   // The first two stages need list entries 0 and 1 only: their words come
   // straight from global memory, so the first copies start before the list
@@ -454,11 +474,11 @@ void attn_fwd_kernel(
   // would also wait for the copies above and the Q loads below).
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-  if (tok.q == nullptr) {
-    const __bf16* qp = q_r + (rowbase + q0 + l32) * D + 8 * g;
+  if (tok.q == nullptr && (!PR || qvalid)) {
+    const __bf16* qp = q_r + (rowbase + qrow) * D + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * kk);
-  } else if (q0 + l32 >= N) {
+  } else if (!qvalid) {
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = bf16x8_t{};
   } else {
@@ -503,8 +523,8 @@ void attn_fwd_kernel(
   // ---- epilogue -------------------------------------------------------------------
   const float lt = sum_halves(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  const int q = q0 + l32;
-  if (q < N) {
+  const int q = qrow;
+  if (qvalid) {
     // lane (l32, g) holds channels 32 dt + 8 i + 4 g .. +3 of its query row
     if (tok.out != nullptr && tok.out_f32) {
       float* op = reinterpret_cast<float*>(tok.out) + bi * tok.osb + (int64_t)qtok * tok.osn +
@@ -543,9 +563,9 @@ void attn_fwd_kernel(
   }
 }
 
-template <int D, int BLK>
+template <int D, int BLK, int QB = BLK, bool PR = false>
 hipError_t launch(const AttnArgs& a) {
-  const int total = a.B * a.Hh * a.nb;
+  const int total = a.B * a.Hh * a.nb * (BLK / QB);
   const float sl2 = a.scale * kLog2e;
   float bias_n = 0.f, bias_last = 0.f;
   if (a.k_g != nullptr) {
@@ -553,17 +573,21 @@ hipError_t launch(const AttnArgs& a) {
     bias_n = (float)(std::log((double)a.n_pool) / a.scale);
     bias_last = (float)(std::log((double)(a.N - (a.Ng - 1) * a.n_pool)) / a.scale);
   }
-  hipLaunchKernelGGL((attn_fwd_kernel<D, BLK>), dim3(total), dim3(AttnCfg<D, BLK>::kThreads), 0,
+  hipLaunchKernelGGL((attn_fwd_kernel<D, BLK, QB, PR>), dim3(total), dim3(AttnCfg<D, BLK, QB>::kThreads), 0,
                      a.stream, (const __bf16*)a.q_r, (const __bf16*)a.k_r, (const __bf16*)a.v_t,
                      a.kv_count, a.kv_idx, a.order, (const __bf16*)a.k_g, (const __bf16*)a.v_g,
                      (__bf16*)a.o_r, a.lse, a.Hh, a.N, a.Npad, a.nb, a.Ng, sl2, bias_n, bias_last,
-                     total, a.tok);
+                     total, a.tok, a.q_count, a.rowsel);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd(const AttnArgs& a) {
+  if (a.rowsel != nullptr) {   // pruned queries: 64-row workgroups
+    if (a.d == 64) return a.b == 64 ? launch<64, 64, 64, true>(a) : launch<64, 128, 64, true>(a);
+    return a.b == 64 ? launch<128, 64, 64, true>(a) : launch<128, 128, 64, true>(a);
+  }
   if (a.d == 64) return a.b == 64 ? launch<64, 64>(a) : launch<64, 128>(a);
   return a.b == 64 ? launch<128, 64>(a) : launch<128, 128>(a);
 }

@@ -83,6 +83,39 @@ struct AttnArgs {
   int B, Hh, N, Npad, d, b, nb, Ng, n_pool;
   float scale;
   TokIO tok;            // zero: reordered Q in, reordered O out
+  const int32_t* q_count;   // set (with rowsel): only the listed query rows of each block (pruned queries)
+  const int32_t* rowsel;    // [B * Hh * nb, b] kept reordered rows of each block, ascending
+  hipStream_t stream;
+};
+
+// Query pruning (BSA notes, key design 1): kept rows of every query block.
+struct PruneArgs {
+  const void* q;            // token order, element strides qsb / qsn / qsh, d contiguous
+  int64_t qsb, qsn, qsh;
+  int q_f32;
+  const int32_t* perm;      // reordered row -> token
+  const int32_t* anchor;    // reordered row -> reordered row of its window centre
+  int perm_h_stride;        // 0 (shared) or N (per head), for perm and anchor alike
+  int B, Hh, N, Npad, d, b, nb;
+  double r;                 // keep ratio in (0, 1]
+  int32_t* q_count;         // [B * Hh * nb]
+  int32_t* rowsel;          // [B * Hh * nb, b], -1 past the count
+  uint8_t* keep;            // [B * Hh * Npad]
+  hipStream_t stream;
+};
+
+// Token filling: pruned rows copy their centre's output row (token order).
+struct FillArgs {
+  void* out;
+  int64_t osb, osn, osh;
+  int out_f32;
+  int row_bytes;            // d * element size, a multiple of 16
+  const int32_t* perm;
+  const int32_t* anchor;
+  int perm_h_stride;
+  const uint8_t* keep;
+  float* lse;               // nullable, [B * Hh * Npad]
+  int B, Hh, N, Npad;
   hipStream_t stream;
 };
 
@@ -123,6 +156,8 @@ hipError_t launch_estimate(const EstimateArgs& a);
 size_t estimate_workspace_bytes(int B, int Hh, int nb, int k, int d);
 hipError_t launch_build_mask(const MaskArgs& a);
 hipError_t launch_build_order(const MaskArgs& a);   // a.kv_count -> a.order only
+hipError_t launch_query_prune(const PruneArgs& a);
+hipError_t launch_fill_pruned(const FillArgs& a);
 hipError_t launch_attn_fwd(const AttnArgs& a);
 hipError_t launch_transpose_lists(const TransposeListsArgs& a);
 size_t attn_bwd_workspace_bytes(int B, int Hh, int Npad, int d);

@@ -60,6 +60,15 @@ def perm_invert(perm: np.ndarray) -> np.ndarray:
     return out
 
 
+def prune_anchors(T: int, H: int, W: int, win, perm: np.ndarray, prefix: int = 0) -> np.ndarray:
+    """Reordered index of the window centre of every reordered token (query pruning)."""
+    p = np.ascontiguousarray(perm, dtype=np.int32)
+    out = np.empty_like(p)
+    check("dbs_prune_anchors", lib().dbs_prune_anchors(T, H, W, prefix, int(win[0]), int(win[1]), int(win[2]),
+                                                       p.ctypes.data, out.ctypes.data))
+    return out
+
+
 # --------------------------------------------------------------------------- device
 
 
@@ -257,6 +266,54 @@ def estimate_mask(q_r: torch.Tensor, k_r: torch.Tensor, N: int, b: int, k: int, 
             _p(q_r), _dt(q_r), q_r.stride(0), q_r.stride(1), q_r.stride(2), _p(q_perm), per_head, _p(k_r),
             B, Hh, N, Npad, d, *tail))
     return kv_count, kv_idx, mask, p_imp
+
+
+def query_prune(q: torch.Tensor, perm: torch.Tensor, anchor: torch.Tensor, Npad: int, b: int, r: float,
+                q_count: Optional[torch.Tensor] = None, rowsel: Optional[torch.Tensor] = None,
+                keep: Optional[torch.Tensor] = None):
+    """q [B, N, Hh, d] in token order -> (q_count [B, Hh, nb], rowsel [B, Hh, nb, b], keep [B, Hh, Npad])."""
+    _dev(q, perm, anchor, q_count, rowsel, keep)
+    if q.stride(3) != 1:
+        raise ValueError("the d axis of q must be contiguous")
+    B, N, Hh, d = q.shape
+    nb = Npad // b
+    dv = q.device
+    if q_count is None:
+        q_count = torch.empty((B, Hh, nb), dtype=torch.int32, device=dv)
+    if rowsel is None:
+        rowsel = torch.empty((B, Hh, nb, b), dtype=torch.int32, device=dv)
+    if keep is None:
+        keep = torch.empty((B, Hh, Npad), dtype=torch.uint8, device=dv)
+    per_head = 1 if perm.dim() == 2 else 0
+    check("dbs_query_prune", lib().dbs_query_prune(
+        _p(q), _dt(q), q.stride(0), q.stride(1), q.stride(2), _p(perm), per_head, _p(anchor), B, Hh, N, Npad, d, b,
+        float(r), _p(q_count), _p(rowsel), _p(keep), _stream()))
+    return q_count, rowsel, keep
+
+
+def sparse_attn_fwd_pruned_tok(q: torch.Tensor, perm: torch.Tensor, k_r: torch.Tensor, v_t: torch.Tensor, N: int,
+                               b: int, scale: float, kv_count: torch.Tensor, kv_idx: torch.Tensor,
+                               q_count: torch.Tensor, rowsel: torch.Tensor, anchor: torch.Tensor,
+                               keep: torch.Tensor, out: Optional[torch.Tensor] = None,
+                               out_dtype: torch.dtype = torch.bfloat16, lse: Optional[torch.Tensor] = None,
+                               want_lse: bool = False, order: Optional[torch.Tensor] = None):
+    """Attention for the kept query rows, then token filling; returns (out [B, N, Hh, d], lse or None)."""
+    _dev(q, perm, k_r, v_t, kv_count, kv_idx, q_count, rowsel, anchor, keep, out, lse, order)
+    if q.stride(3) != 1:
+        raise ValueError("the d axis of q must be contiguous")
+    B, Hh, Npad, d = k_r.shape
+    if out is None:
+        out = torch.empty((B, N, Hh, d), dtype=out_dtype, device=k_r.device)
+    if out.stride(3) != 1:
+        raise ValueError("the d axis of out must be contiguous")
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hh, Npad), dtype=torch.float32, device=k_r.device)
+    per_head = 1 if perm.dim() == 2 else 0
+    check("dbs_sparse_attn_fwd_pruned_tok", lib().dbs_sparse_attn_fwd_pruned_tok(
+        _p(q), _dt(q), q.stride(0), q.stride(1), q.stride(2), _p(perm), per_head, _p(k_r), _p(v_t),
+        B, Hh, N, Npad, d, b, float(scale), _p(kv_count), _p(kv_idx), _p(order), _p(q_count), _p(rowsel),
+        _p(anchor), _p(keep), _p(out), _dt(out), out.stride(0), out.stride(1), out.stride(2), _p(lse), _stream()))
+    return out, lse
 
 
 def meanpool_kv(k_r: torch.Tensor, v_t: torch.Tensor, N: int, b: int, n: int,

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define DBS_ABI_VERSION 7
+#define DBS_ABI_VERSION 8
 
 typedef enum {
   DBS_OK = 0,
@@ -103,6 +103,18 @@ dbs_status dbs_perm_cuboid(int T, int H, int W, int ct, int ch, int cw, int pref
 
 /* inv_out[perm[i]] = i.  INVALID_ARG if perm is not a permutation of 0..n-1. */
 dbs_status dbs_perm_invert(const int32_t* perm, int n, int32_t* inv_out);
+
+/* Window centres for query pruning (Bidirectional Sparse Attention notes, key
+ * design 1 and "a complete example"), on the host.  Windows of wt x wh x ww
+ * tile the T x H x W grid from its origin (border windows are cut); the
+ * centre of a window sits at offset (e - 1) / 2 along each axis, e the
+ * window's extent there; a text-prefix token is its own centre.
+ * anchor_out[i] = the reordered index of the centre of token perm[i], for the
+ * reordered sequence given by perm (length prefix + T*H*W).  Errors:
+ * INVALID_ARG for a side < 1, a NULL pointer or a perm that is not a
+ * permutation. */
+dbs_status dbs_prune_anchors(int T, int H, int W, int prefix, int wt, int wh, int ww, const int32_t* perm,
+                             int32_t* anchor_out);
 
 /* ---------------------------------------------------------------------------
  * Device calls.
@@ -248,6 +260,41 @@ dbs_status dbs_estimate_mask_tok(const void* q, dbs_dtype q_dt, int64_t sb, int6
                                  int rule, double param, float* p_imp,
                                  int32_t* kv_count, int32_t* kv_idx, uint8_t* mask, int32_t* order,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Query pruning (Bidirectional Sparse Attention notes, key design 1): in each
+ * query block I (reordered rows I*b .. I*b + n - 1, n valid), a row i whose
+ * centre anchor[i] (dbs_prune_anchors) is itself is a centre and always kept;
+ * of the other rows the m - c of largest 1 - cos(q[centre], q[i]) are kept
+ * (float32 from the bf16 values; ties by smaller row), where c is the block's
+ * number of centres and m = min(n, max(ceil(r * n), c)).
+ * q: token order [B, N, Hh, d] with element strides sb, sn, sh (d contiguous;
+ * bf16, or float32 rounded to bf16), read through perm as for
+ * dbs_estimate_blocks_tok; anchor: int32 [N] (or [Hh, N] when perm_per_head),
+ * reordered indices.  Outputs: q_count int32 [B, Hh, nb] = m; rowsel int32
+ * [B, Hh, nb, b], the kept rows (reordered indices) ascending, -1 after m;
+ * keep uint8 [B, Hh, Npad], 1 for a kept row (0 for rows >= N).  r in (0, 1].
+ * Errors as for dbs_estimate_blocks_tok, and INVALID_ARG for r. */
+dbs_status dbs_query_prune(const void* q, dbs_dtype q_dt, int64_t sb, int64_t sn, int64_t sh,
+                           const int32_t* perm, int perm_per_head, const int32_t* anchor,
+                           int B, int Hh, int N, int Npad, int d, int b, double r,
+                           int32_t* q_count, int32_t* rowsel, uint8_t* keep, hipStream_t stream);
+
+/* dbs_sparse_attn_fwd_tok (plain ASA, no global tokens) for the kept query
+ * rows of dbs_query_prune only, then token filling: every row with keep = 0
+ * takes the output (and lse) of its centre anchor[i], which the pruning
+ * always keeps.  Kept rows get exactly the output dbs_sparse_attn_fwd_tok
+ * gives them.  Query work is split into 64-row pieces of each block's kept
+ * list, so the attention's cost follows the kept rows.  q_count, rowsel,
+ * keep, anchor: as written / read by dbs_query_prune for the same perm.
+ * Other arguments and errors as for dbs_sparse_attn_fwd_tok. */
+dbs_status dbs_sparse_attn_fwd_pruned_tok(const void* q, dbs_dtype q_dt, int64_t qsb, int64_t qsn, int64_t qsh,
+                                          const int32_t* perm, int perm_per_head, const void* k_r,
+                                          const void* v_r, int B, int Hh, int N, int Npad, int d, int b,
+                                          float scale, const int32_t* kv_count, const int32_t* kv_idx,
+                                          const int32_t* order, const int32_t* q_count, const int32_t* rowsel,
+                                          const int32_t* anchor, const uint8_t* keep, void* out,
+                                          dbs_dtype out_dt, int64_t osb, int64_t osn, int64_t osh, float* lse,
+                                          hipStream_t stream);
 
 /* ASA_G global tokens (Video-BLADE "Step 2.2 (2)"; BLADE notes key design 2):
  * mean of each window of n consecutive reordered tokens,

@@ -37,7 +37,7 @@ def test_all_declared_symbols_exported(dbs):
     for n in names:
         assert hasattr(h, n), n
     assert set(names) == set(L.SIGNATURES), set(names) ^ set(L.SIGNATURES)
-    assert L.lib().dbs_abi_version() == 7
+    assert L.lib().dbs_abi_version() == 8
 
 
 @pytest.mark.parametrize("T,H,W", list(itertools.product(range(1, 7), repeat=3)))
@@ -291,6 +291,53 @@ def test_estimate_mask_validation(dbs):
     assert callt(17, 0.5) == -1           # top-k count not an integer >= 1
     assert callt(20, 0) == -1             # kv_idx NULL
     assert callt(24, ws - 1) == -1        # small workspace
+
+
+@pytest.mark.parametrize("T,H,W,win,prefix,order", [
+    (4, 8, 8, (2, 2, 2), 0, "cuboid"), (5, 7, 9, (2, 3, 2), 0, "gilbert"), (3, 6, 10, (1, 4, 3), 5, "gilbert"),
+    (16, 28, 52, (2, 2, 2), 0, "cuboid"), (2, 3, 3, (5, 5, 5), 2, "cuboid")])
+def test_prune_anchors_match_oracle(dbs, T, H, W, win, prefix, order):
+    from oracle.query_prune import anchors_reordered, window_anchors
+    ops, _ = dbs
+    perm = o_gilbert(T, H, W, prefix) if order == "gilbert" else o_cuboid(T, H, W, 4, 4, 4, prefix)
+    got = ops.prune_anchors(T, H, W, win, perm, prefix)
+    want = anchors_reordered(perm, window_anchors(T, H, W, win, prefix))
+    assert np.array_equal(got, want)
+
+
+@cpu_only
+def test_prune_validation(dbs):
+    ops, L = dbs
+    f = L.lib().dbs_prune_anchors
+    perm = np.arange(8, dtype=np.int32)
+    out = np.empty(8, dtype=np.int32)
+    assert f(2, 2, 2, 0, 0, 1, 1, perm.ctypes.data, out.ctypes.data) == -1        # window side 0
+    bad = perm.copy(); bad[3] = 2
+    assert f(2, 2, 2, 0, 1, 1, 1, bad.ctypes.data, out.ctypes.data) == -1         # not a permutation
+    g = L.lib().dbs_query_prune
+    # q, q_dt, sb, sn, sh, perm, pph, anchor, B, Hh, N, Npad, d, b, r, q_count, rowsel, keep, stream
+    ok = [A, 0, 100 * 2 * 128, 2 * 128, 128, A, 0, A, 1, 2, 100, 128, 128, 64, 0.5, A, A, A, None]
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return g(*a)
+    assert call(14, 0.0) == -1            # r = 0
+    assert call(14, 1.5) == -1            # r > 1
+    assert call(7, 0) == -1               # anchor NULL
+    assert call(17, 0) == -1              # keep NULL
+    assert call(15, A + 2) == -3          # misaligned q_count
+    assert call(13, 32) == -2             # block size
+    h = L.lib().dbs_sparse_attn_fwd_pruned_tok
+    okh = [A, 0, 100 * 2 * 128, 2 * 128, 128, A, 0, A, A, 1, 2, 100, 128, 128, 64, 0.125, A, A, None, A, A, A, A,
+           A, 0, 100 * 2 * 128, 2 * 128, 128, None, None]
+    def callh(i, v):
+        a = list(okh)
+        a[i] = v
+        return h(*a)
+    assert callh(19, 0) == -1             # q_count NULL
+    assert callh(22, 0) == -1             # keep NULL
+    assert callh(21, A + 1) == -3         # misaligned anchor
+    assert callh(13, 96) == -2            # head dim
 
 
 @cpu_only

@@ -1,0 +1,192 @@
+"""GPU parity: BSA query pruning (dbs_query_prune) and the attention over the kept
+queries with token filling (dbs_sparse_attn_fwd_pruned_tok), through the C ABI.
+
+- Pruning: q_count, rowsel and keep bit-exact against the oracle's float64
+  selection; blocks whose m-th and (m+1)-th candidates lie within 1e-5 in
+  dissimilarity (the oracle's tie flag: the GPU ranks float32 values) are
+  counted and skipped.
+- Attention: kept rows bit-identical to dbs_sparse_attn_fwd_tok on the same
+  inputs (the same per-row arithmetic in 64-row workgroups), pruned rows
+  bit-identical to their centre's row, and the whole output within max-abs
+  2e-2 of the oracle's float64 attention followed by its filling."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import dev, dev_bf16, host, kept_lists, say, smooth_qkv
+from oracle.attention import masked_attention
+from oracle.perm import perm_cuboid, perm_gilbert3d
+from oracle.query_prune import anchors_reordered, fill, query_prune, window_anchors
+from oracle.reorder import reorder_fast as o_reorder
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def _ops():
+    from dynamic_block_sparse_gilbert_amd import ops
+    return ops
+
+
+def _setup(T, H, W, Hh, d, b, order, win, seed, cub=(4, 4, 4)):
+    N = T * H * W
+    q, k, v = smooth_qkv(seed, 1, N, Hh, d, grid=(T, H, W))
+    perm = perm_gilbert3d(T, H, W) if order == "gilbert" else perm_cuboid(T, H, W, *cub)
+    anc = anchors_reordered(perm, window_anchors(T, H, W, win))
+    return N, q, k, v, perm.astype(np.int32), anc.astype(np.int32)
+
+
+def _check_prune(q, perm, anc, N, b, r, Hh, blocks=None):
+    ops = _ops()
+    Npad = -(-N // b) * b
+    nb = Npad // b
+    qc, rs, kp = ops.query_prune(dev_bf16(q), dev(perm), dev(anc), Npad, b, r)
+    torch.cuda.synchronize()
+    qc, rs, kp = host(qc), host(rs), host(kp)
+    qr = o_reorder(q, perm, Npad)
+    n_ties = 0
+    for h in range(Hh):
+        rc, rrs, rkeep, ties = query_prune(qr[0, h], anc, N, b, r)
+        tie = set(ties)
+        n_ties += len(tie)
+        for I in (range(nb) if blocks is None else blocks):
+            if I in tie:
+                continue
+            assert qc[0, h, I] == rc[I], (h, I)
+            assert np.array_equal(rs[0, h, I], rrs[I]), (h, I)
+            lo, hi = I * b, min((I + 1) * b, N)
+            assert np.array_equal(kp[0, h, lo:hi].astype(bool), rkeep[lo:hi]), (h, I)
+        assert (kp[0, h, N:] == 0).all()
+    return n_ties
+
+
+@pytest.mark.parametrize("T,H,W,Hh,d,b,order,win,r", [
+    (8, 16, 16, 2, 64, 64, "cuboid", (2, 2, 2), 0.5),     # the worked example's geometry, smaller grid
+    (8, 16, 16, 1, 128, 64, "cuboid", (2, 2, 2), 0.25),   # r below the centres' share: centres only
+    (5, 12, 20, 2, 128, 128, "gilbert", (1, 2, 2), 0.5),  # centres across block borders, ragged N
+    (3, 10, 14, 1, 64, 128, "gilbert", (2, 3, 3), 0.8),
+    (4, 8, 8, 1, 64, 64, "cuboid", (2, 2, 2), 1.0),       # keep all
+])
+def test_prune_bit_exact(T, H, W, Hh, d, b, order, win, r):
+    say("query_prune", T, H, W, Hh, d, b, order, win, r)
+    N, q, _, _, perm, anc = _setup(T, H, W, Hh, d, b, order, win, T * H + W)
+    ties = _check_prune(q, perm, anc, N, b, r, Hh)
+    assert ties <= max(1, (-(-N // b)) * Hh // 8)
+
+
+def test_worked_example_counts_on_gpu():
+    """The notes' example: 16 x 28 x 52 latent tokens, 4 x 4 x 4 blocks, 2 x 2 x 2 windows, r = 0.5:
+    23,296 queries -> 11,648."""
+    say("query_prune worked example")
+    ops = _ops()
+    T, H, W = 16, 28, 52
+    N, q, _, _, perm, anc = _setup(T, H, W, 1, 64, 64, "cuboid", (2, 2, 2), 5)
+    qc, rs, kp = ops.query_prune(dev_bf16(q), dev(perm), dev(anc), N, 64, 0.5)
+    torch.cuda.synchronize()
+    assert int(host(qc).sum()) == 11648 == int(host(kp).sum())
+    assert (host(qc) == 32).all()
+
+
+@pytest.mark.parametrize("T,H,W,Hh,d,b,order,win,r,fp32_out", [
+    (8, 16, 16, 2, 64, 64, "cuboid", (2, 2, 2), 0.5, False),
+    (5, 12, 20, 2, 128, 128, "gilbert", (1, 2, 2), 0.5, True),
+    (5, 12, 20, 1, 128, 128, "gilbert", (2, 2, 2), 0.7, False),   # two 64-row pieces for some blocks
+    (3, 10, 14, 1, 64, 128, "gilbert", (2, 3, 3), 0.3, False),
+])
+def test_pruned_attention(T, H, W, Hh, d, b, order, win, r, fp32_out):
+    say("pruned attention", T, H, W, Hh, d, b, order, win, r)
+    ops = _ops()
+    N, q, k, v, perm, anc = _setup(T, H, W, Hh, d, b, order, win, 3 * T + H)
+    Npad = -(-N // b) * b
+    nb = Npad // b
+    scale = 1.0 / np.sqrt(d)
+    permd = dev(perm)
+    qd = dev_bf16(q)
+    k_r = ops.reorder(dev_bf16(k), permd, Npad, b, "rows")
+    v_t = ops.reorder(dev_bf16(v), permd, Npad, b, "tiles_t")
+    P = ops.estimate_blocks(ops.reorder(qd, permd, Npad, b, "rows"), k_r, N, b, min(16, b), scale)
+    cnt, idx, _, order_buf = ops.build_mask(P, 0.6, want_order=True)
+    qc, rs, kp = ops.query_prune(qd, permd, dev(anc), Npad, b, r)
+    odt = torch.float32 if fp32_out else torch.bfloat16
+    out, lse = ops.sparse_attn_fwd_pruned_tok(qd, permd, k_r, v_t, N, b, scale, cnt, idx, qc, rs, dev(anc), kp,
+                                              out_dtype=odt, want_lse=True, order=order_buf)
+    full, lse_f = ops.sparse_attn_fwd_tok(qd, permd, k_r, v_t, N, b, scale, cnt, idx, out_dtype=odt, want_lse=True)
+    torch.cuda.synchronize()
+    o, f, keep = host(out), host(full), host(kp)[0]
+    lo, lf = host(lse), host(lse_f)
+    inv = np.empty(N, dtype=np.int64)
+    inv[perm] = np.arange(N)
+    for h in range(Hh):
+        for i in range(N):          # reordered row i is token perm[i]
+            t = perm[i]
+            if keep[h, i]:
+                assert np.array_equal(o[0, t, h], f[0, t, h]), (h, i)
+                assert lo[0, h, i] == lf[0, h, i]
+            else:
+                assert np.array_equal(o[0, t, h], o[0, perm[anc[i]], h]), (h, i)
+                assert lo[0, h, i] == lo[0, h, anc[i]]
+    # the oracle: attention on every row, then the filling
+    qr, kr, vr = (o_reorder(x, perm, Npad) for x in (q, k, v))
+    hc, hi = host(cnt), host(idx)
+    for h in range(Hh):
+        kept = kept_lists(hc[0, h], hi[0, h])[0]
+        ref, _ = masked_attention(qr[0, h], kr[0, h], vr[0, h], N, b, kept, scale)
+        ref = fill(ref, keep[h, :N].astype(bool), anc)
+        got = o[0, perm, h].astype(np.float64)          # reordered rows
+        assert np.abs(got - ref).max() <= TOL, np.abs(got - ref).max()
+
+
+def test_pruned_wan_shape():
+    """The Wan2.1-1.3B-shaped layer (12 heads, 32,760 tokens, b 128, Gilbert order) with 2 x 2 x 2
+    windows and r = 0.5: sampled blocks against the oracle's pruning and attention; every kept row
+    equal to the unpruned attention's, every pruned row to its centre's."""
+    say("pruned attention wan")
+    from workloads import get_config, make_inputs
+    ops = _ops()
+    cfg = get_config(2)
+    T, H, W = cfg.T, cfg.H, cfg.W
+    N, Hh, d, b = T * H * W, cfg.heads, cfg.d, cfg.b
+    Npad = -(-N // b) * b
+    nb = Npad // b
+    q, k, v = make_inputs(cfg)
+    perm = perm_gilbert3d(T, H, W).astype(np.int32)
+    anc = ops.prune_anchors(T, H, W, (2, 2, 2), perm)
+    permd, ancd = dev(perm), dev(anc)
+    scale = 1.0 / np.sqrt(d)
+    qd = dev_bf16(q)
+    k_r = ops.reorder(dev_bf16(k), permd, Npad, b, "rows")
+    v_t = ops.reorder(dev_bf16(v), permd, Npad, b, "tiles_t")
+    cnt, idx, _, _ = ops.estimate_mask(qd, k_r, N, b, cfg.k, scale, "cumulative", 0.9, q_perm=permd)
+    qc, rs, kp = ops.query_prune(qd, permd, ancd, Npad, b, 0.5)
+    out, _ = ops.sparse_attn_fwd_pruned_tok(qd, permd, k_r, v_t, N, b, scale, cnt, idx, qc, rs, ancd, kp)
+    full, _ = ops.sparse_attn_fwd_tok(qd, permd, k_r, v_t, N, b, scale, cnt, idx)
+    torch.cuda.synchronize()
+    o, f, keep, qch = host(out), host(full), host(kp)[0], host(qc)[0]
+    assert 0.5 * Hh * N <= int(qch.sum()) < 0.6 * Hh * N
+    for h in range(Hh):
+        kh = keep[h, :N].astype(bool)
+        toks = perm[kh]
+        assert np.array_equal(o[0, toks, h], f[0, toks, h]), h
+        pr = np.nonzero(~kh)[0]
+        assert np.array_equal(o[0, perm[pr], h], o[0, perm[anc[pr]], h]), h
+    rng = np.random.default_rng(2)
+    blocks = sorted({0, nb - 1} | set(rng.choice(nb, 6, replace=False).tolist()))
+    qr = o_reorder(q[:, :, :2], perm, Npad)
+    kr, vr = (o_reorder(x[:, :, :2], perm, Npad) for x in (k, v))
+    hc, hi = host(cnt), host(idx)
+    for h in range(2):
+        rc, rrs, rkeep, ties = query_prune(qr[0, h], anc, N, b, 0.5)
+        for I in blocks:
+            if I in ties:
+                continue
+            assert qch[h, I] == rc[I] and np.array_equal(host(rs)[0, h, I], rrs[I]), (h, I)
+        kept = kept_lists(hc[0, h], hi[0, h])[0]
+        # rows of the sampled blocks and of their centres
+        need = sorted({int(anc[i]) // b for I in blocks for i in range(I * b, min((I + 1) * b, N))} | set(blocks))
+        ref, _ = masked_attention(qr[0, h], kr[0, h], vr[0, h], N, b, kept, scale, query_blocks=need)
+        for I in blocks:
+            for i in range(I * b, min((I + 1) * b, N)):
+                src = i if keep[h, i] else int(anc[i])
+                got = o[0, perm[i], h].astype(np.float64)
+                assert np.abs(got - ref[src]).max() <= TOL, (h, i)
