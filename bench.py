@@ -65,17 +65,19 @@ def src_hash(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def kept_pair_tokens(cnt, idx, N, b):
-    """sum over kept (I, J) of |I| * |J| with valid-token block sizes."""
+def kept_pair_tokens(cnt, idx, N, b, q_rows=None):
+    """sum over kept (I, J) of |I| * |J| with valid-token block sizes; q_rows (same shape as cnt):
+    the query rows computed per block instead of |I| (pruned queries)."""
     import numpy as np
     nb = cnt.shape[-1]
     L = np.array([min(b, N - J * b) for J in range(nb)], dtype=np.float64)
     c = cnt.reshape(-1, nb)
     ix = idx.reshape(-1, nb, nb)
+    qr = None if q_rows is None else q_rows.reshape(-1, nb)
     total = 0.0
     for r in range(c.shape[0]):
         for I in range(nb):
-            total += L[I] * L[ix[r, I, :c[r, I]]].sum()
+            total += (L[I] if qr is None else qr[r, I]) * L[ix[r, I, :c[r, I]]].sum()
     return total
 
 
@@ -195,6 +197,69 @@ def mask_rules_leg(layer, steps, torch):
         out[name] = {"us": round(e0.elapsed_time(e1) / steps * 1e3, 2),
                      "block_sparsity": round(float(1.0 - cnt.sum() / (cnt.size * nb)), 4)}
     return out
+
+
+def query_pruning_leg(layer, cfg, qd, steps, torch, r=0.5, win=(2, 2, 2)):
+    """BSA query pruning on the timed layer and mask: the kept rows (centres of 2 x 2 x 2 windows plus
+    the most distinct tokens, keep ratio r), the attention over them with token filling, against the
+    unpruned attention on the same lists; each timed back to back between two HIP events."""
+    from dynamic_block_sparse_gilbert_amd import ops
+    sp = layer.spec
+    perm_h = layer.perm.cpu().numpy()
+    anc = torch.from_numpy(ops.prune_anchors(cfg.T, cfg.H, cfg.W, win, perm_h)).to(qd.device)
+    out = torch.empty_like(qd)
+
+    def prune():
+        return ops.query_prune(qd, layer.perm, anc, sp.Npad, sp.b, r)
+
+    qc, rs, kp = prune()
+
+    def pruned():
+        ops.sparse_attn_fwd_pruned_tok(qd, layer.perm, layer.k_r, layer.v_t, sp.N, sp.b, sp.scale, layer.kv_count,
+                                       layer.kv_idx, qc, rs, anc, kp, out=out, order=layer.order)
+
+    def full():
+        ops.sparse_attn_fwd_tok(qd, layer.perm, layer.k_r, layer.v_t, sp.N, sp.b, sp.scale, layer.kv_count,
+                                layer.kv_idx, out=out, order=layer.order)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    t_prune, t_pruned, t_full = timed(prune), timed(pruned), timed(full)
+    cnt, idx, qch = layer.kv_count.cpu().numpy(), layer.kv_idx.cpu().numpy(), qc.cpu().numpy()
+    kept_q = float(qch.sum()) / (qch.shape[0] * qch.shape[1] * sp.N)
+    # key blocks streamed by the paired work items (blocks 2P, 2P + 1 over the union of their lists)
+    # against the two lists' own lengths
+    nb = cnt.shape[-1]
+    c2, i2 = cnt.reshape(-1, nb), idx.reshape(-1, nb, nb)
+    own = float(c2.sum())
+    union = 0.0
+    for r_ in range(c2.shape[0]):
+        for I in range(0, nb - 1, 2):
+            union += len(set(i2[r_, I, :c2[r_, I]].tolist()) | set(i2[r_, I + 1, :c2[r_, I + 1]].tolist()))
+    ef = 4.0 * sp.d * kept_pair_tokens(cnt, idx, sp.N, sp.b, q_rows=qch)
+    kv_keep = 1.0 - float(1.0 - cnt.sum() / (cnt.size * cnt.shape[-1]))
+    return {
+        "what": "dbs_query_prune + dbs_sparse_attn_fwd_pruned_tok (64-row work items, then token filling), "
+                "2x2x2 centre windows, keep ratio %.2f, on the tau %.2f mask of the timed layer" % (r, sp.tau),
+        "query_keep": round(kept_q, 4),
+        "kv_block_keep": round(kv_keep, 4),
+        "combined_sparsity": round(1.0 - kept_q * kv_keep, 4),
+        "prune_us": round(t_prune * 1e3, 2),
+        "pruned_attn_ms": round(t_pruned, 4),
+        "unpruned_attn_ms": round(t_full, 4),
+        "pruned_attn_executed_tflops": round(ef / (t_pruned * 1e-3) / 1e12, 2),
+        "pair_union_over_own_blocks": round(2.0 * union / own, 4),
+    }
 
 
 def cpu_baseline(cfg, q, k, v, perm, tau, heads=2):
@@ -320,6 +385,8 @@ def main():
         torch.cuda.synchronize()
         extra["backward"] = backward_leg(layer, cfg, qd, vd, max(5, args.steps // 5), 3, torch)
         extra["mask_rules"] = mask_rules_leg(layer, 20, torch)
+        layer.mask(args.tau)
+        extra["query_pruning"] = query_pruning_leg(layer, cfg, qd, 20, torch)
         other = AsaLayer(spec, device=dev, fused=args.unfused)
         ms_o, _ = run_steps(other, qd, kd, vd, out, args.tau, args.steps, args.warmup, torch)
         extra["unfused_ms_per_step" if not args.unfused else "fused_ms_per_step"] = round(ms_o, 4)

@@ -129,11 +129,16 @@ struct StageDesc {
   int limit;           // keys with index >= limit are masked (kind 1, 2)
 };
 
-// QB: query rows per workgroup (BLK, or 64 with BLK = 128 for pruned
-// queries).  PR: pruned queries (BSA query pruning): work item (block, sub)
-// takes rows sub * QB .. of the block's kept-row list rowsel (q_count[block]
-// of them); a sub-tile past the count exits at once.
-template <int D, int BLK, int QB, bool PR>
+// QB: query rows per workgroup.  MODE (BSA query pruning, rowsel lists the
+// kept rows of each block, q_count[block] of them):
+//   0  every row of the query block;
+//   1  the kept rows of one block (rows sub * QB .. of its list);
+//   2  a pair of blocks (2P, 2P + 1) whose kept rows fit half a workgroup
+//      each: the first half of the wavefronts takes block 2P's rows, the
+//      second half block 2P + 1's, over the union of their kept-block lists,
+//      a wavefront masking the stages its block does not keep.  Mode 1 skips
+//      the blocks mode 2 takes, and mode 2 exits for the others.
+template <int D, int BLK, int QB, int MODE>
 __global__ __launch_bounds__(QB / 32 * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(
     const __bf16* __restrict__ q_r, const __bf16* __restrict__ k_r, const __bf16* __restrict__ v_t,
@@ -145,6 +150,8 @@ void attn_fwd_kernel(
     const int32_t* __restrict__ q_count, const int32_t* __restrict__ rowsel) {
   using C = AttnCfg<D, BLK, QB>;
   constexpr int kSubQ = BLK / QB;   // work items per query block
+  constexpr int kHalfW = C::kWaves / 2;
+  static_assert(MODE != 2 || QB == BLK, "pairs take whole-block workgroups");
   // Four distinct arrays whose roles are static in each half of the 2x-unrolled
   // pipeline, so the compiler can prove LDS reads never alias a DMA in flight
   // and does not make them wait for it.
@@ -155,6 +162,10 @@ void attn_fwd_kernel(
   // The kept-block list of this query block, one word per entry (index and
   // masking flags, see kIndexMask).
   __shared__ uint16_t idx_s[4096];
+  // Mode 2: bit 14 + x of a list word is set when block 2P + x does not keep
+  // the entry (the union holds no invalid entries, whose flag bit 14 is
+  // otherwise).
+  __shared__ int wtot_s[C::kWaves];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -162,30 +173,108 @@ void attn_fwd_kernel(
   // Work item: this XCD's next entry of the schedule (longest query blocks
   // first when build_mask wrote one), clamped so a bad schedule stays in bounds.
   const int slot = xcd_remap(blockIdx.x, total);
-  const int rows_total = total / kSubQ;
-  const int wid = order == nullptr ? slot / kSubQ
-                                   : min(max(__builtin_amdgcn_readfirstlane(order[slot / kSubQ]), 0),
-                                         rows_total - 1);
-  const int I = wid % nb;
-  const int bh = wid / nb;
+  int I, bh;
+  if constexpr (MODE == 2) {
+    const int np = (nb + 1) / 2;
+    bh = slot / np;
+    I = 2 * (slot % np);
+  } else {
+    const int rows_total = total / kSubQ;
+    const int wid = order == nullptr ? slot / kSubQ
+                                     : min(max(__builtin_amdgcn_readfirstlane(order[slot / kSubQ]), 0),
+                                           rows_total - 1);
+    I = wid % nb;
+    bh = wid / nb;
+  }
   const int64_t rowbase = (int64_t)bh * Npad;
+  // kept-row count of block J of this head, clamped
+  auto kept_rows = [&](int J) {
+    const int mq = __builtin_amdgcn_readfirstlane(q_count[(int64_t)bh * nb + J]);
+    return mq < 0 ? 0 : (mq > BLK ? BLK : mq);
+  };
+  // blocks 2P, 2P + 1 go to mode 2 together when both fit half a workgroup
+  auto paired = [&](int I0) { return I0 + 1 < nb && kept_rows(I0) <= QB / 2 && kept_rows(I0 + 1) <= QB / 2; };
   // this lane's query row (reordered index) and whether it is one
   int qrow = I * BLK + wave * C::kQW + l32;
   bool qvalid = qrow < N;
-  if constexpr (PR) {
+  int half = 0;   // mode 2: which block of the pair this wavefront serves
+  if constexpr (MODE == 1) {
     const int sub = slot % kSubQ;
-    int mq = __builtin_amdgcn_readfirstlane(q_count[(int64_t)bh * nb + I]);
-    mq = mq < 0 ? 0 : (mq > BLK ? BLK : mq);
-    if (sub * QB >= mq) return;   // the whole workgroup, before any barrier
+    const int mq = kept_rows(I);
+    if (sub * QB >= mq || paired(I & ~1)) return;   // the whole workgroup, before any barrier
     const int s = sub * QB + wave * C::kQW + l32;
     qrow = s < mq ? rowsel[((int64_t)bh * nb + I) * BLK + s] : -1;
     qvalid = qrow >= 0 && qrow < N;
     if (!qvalid) qrow = 0;
+  } else if constexpr (MODE == 2) {
+    if (!paired(I)) return;                           // the whole workgroup, before any barrier
+    half = wave / kHalfW;
+    const int mq = kept_rows(I + half);
+    const int s = (wave % kHalfW) * C::kQW + l32;
+    qrow = s < mq ? rowsel[((int64_t)bh * nb + I + half) * BLK + s] : -1;
+    qvalid = qrow >= 0 && qrow < N;
+    if (!qvalid) qrow = 0;
   }
 
+  // List word of kept-block index J (see kIndexMask).
+  auto word_of = [&](int J) {
+    const bool ok = J >= 0 && J < nb;
+    int w = ok ? J : kInvalidBit;
+#pragma unroll
+    for (int h = 0; h < C::kSubs; ++h)
+      if (!ok || J * BLK + (h + 1) * C::kKT > N) w |= kPartial << h;
+    return w;
+  };
   int cnt = __builtin_amdgcn_readfirstlane(kv_count[(int64_t)bh * nb + I]);
   cnt = cnt < 0 ? 0 : (cnt > nb ? nb : cnt);
   const int32_t* idx = kv_idx + ((int64_t)bh * nb + I) * nb;
+  if constexpr (MODE == 2) {
+    // The union of the two blocks' kept-block sets, ascending, with each
+    // entry's membership, into idx_s: both lists become bitmaps over
+    // the nb <= 4096 blocks (staged in the first K buffer, which the first
+    // copies overwrite only after the barriers below), and a scan of the
+    // union's popcounts places every block.  Entries out of [0, nb) and
+    // repeats drop out (they add nothing to the attention).
+    int c1 = __builtin_amdgcn_readfirstlane(kv_count[(int64_t)bh * nb + I + 1]);
+    c1 = c1 < 0 ? 0 : (c1 > nb ? nb : c1);
+    const int32_t* idx1 = idx + nb;
+    uint32_t* bA = reinterpret_cast<uint32_t*>(Kb0);   // 128 words each
+    uint32_t* bB = bA + 128;
+    static_assert(C::kKBytes >= 1024, "a K buffer holds the two bitmaps");
+    for (int t = threadIdx.x; t < 256; t += C::kThreads) bA[t] = 0u;   // bA and bB
+    __syncthreads();
+    for (int t = threadIdx.x; t < cnt; t += C::kThreads) {
+      const int J = idx[t];
+      if (J >= 0 && J < nb) atomicOr(&bA[J >> 5], 1u << (J & 31));
+    }
+    for (int t = threadIdx.x; t < c1; t += C::kThreads) {
+      const int J = idx1[t];
+      if (J >= 0 && J < nb) atomicOr(&bB[J >> 5], 1u << (J & 31));
+    }
+    __syncthreads();
+    const uint32_t wa = threadIdx.x < 128 ? bA[threadIdx.x] : 0u;
+    const uint32_t wb = threadIdx.x < 128 ? bB[threadIdx.x] : 0u;
+    const int pc = __popc(wa | wb);
+    int inc = pc;   // inclusive scan over the wavefront
+#pragma unroll
+    for (int dd = 1; dd < 64; dd <<= 1) {
+      const int o = __shfl_up(inc, dd, 64);
+      if (lane >= dd) inc += o;
+    }
+    if (lane == 63) wtot_s[wave] = inc;
+    __syncthreads();
+    int pos = inc - pc;
+    for (int w = 0; w < wave; ++w) pos += wtot_s[w];
+    for (uint32_t u = wa | wb; u != 0u; u &= u - 1u, ++pos) {
+      const int bit = __ffs((int)u) - 1;
+      const int absent = (((wa >> bit) & 1u) ? 0 : 0x4000) | (((wb >> bit) & 1u) ? 0 : 0x8000);
+      idx_s[pos] = (uint16_t)(word_of(threadIdx.x * 32 + bit) | absent);
+    }
+    int u = 0;
+    for (int w = 0; w < C::kWaves; ++w) u += wtot_s[w];
+    __syncthreads();
+    cnt = __builtin_amdgcn_readfirstlane(u);
+  }
   const int Ngpad = (Ng + BLK - 1) / BLK * BLK;
   const int ntg = (k_g != nullptr) ? Ngpad / BLK : 0;
   const int U = (cnt + ntg) * C::kSubs;
@@ -204,15 +293,6 @@ void attn_fwd_kernel(
   // MFMA phases.  The list word carries the block index and the masking
   // flags, so a full stage costs a handful of scalar operations.
   const int cnt_m1 = cnt > 0 ? cnt - 1 : 0;
-  // List word of kept-block index J (see kIndexMask).
-  auto word_of = [&](int J) {
-    const bool ok = J >= 0 && J < nb;
-    int w = ok ? J : kInvalidBit;
-#pragma unroll
-    for (int h = 0; h < C::kSubs; ++h)
-      if (!ok || J * BLK + (h + 1) * C::kKT > N) w |= kPartial << h;
-    return w;
-  };
   // Stage u from the list word w of its block (ignored for global tiles).
   auto stage_w = [&](int u, int w) -> StageDesc {
     StageDesc s;
@@ -224,7 +304,14 @@ void attn_fwd_kernel(
     s.voffs = ((uint32_t)Jx * (uint32_t)(D * BLK) + (uint32_t)(h * C::kKT)) * 2u;
     s.glob = !kept;
     s.kind = kept ? ((w >> h) & kPartial ? 1 : 0) : 2;
-    s.limit = kept ? ((w & kInvalidBit) ? -1 : N) : Ng;
+    s.limit = kept ? ((MODE != 2 && (w & kInvalidBit)) ? -1 : N) : Ng;
+    if constexpr (MODE == 2) {
+      // a block of the union that this wavefront's query block does not keep
+      // (selects, no branch)
+      const bool absent = kept && ((w >> (14 + half)) & 1);
+      s.kind = absent ? 1 : s.kind;
+      s.limit = absent ? -1 : s.limit;
+    }
     return s;
   };
   auto stage = [&](int u) -> StageDesc {
@@ -257,14 +344,14 @@ void attn_fwd_kernel(
 #pragma unroll
     for (int i = 0; i < C::kKPer; ++i) {
       const int n = min(wave + i * C::kWaves, C::kKInstr - 1);
-      copy16_lds(s.glob ? rkg : rk, buf + 1024 * n, (uint32_t)koff[i] * 2u, s.koffs);
+      copy16_lds((MODE == 0 && s.glob) ? rkg : rk, buf + 1024 * n, (uint32_t)koff[i] * 2u, s.koffs);
     }
   };
   auto dma_v = [&](const StageDesc& s, char* buf) {
 #pragma unroll
     for (int i = 0; i < C::kVPer; ++i) {
       const int n = min(wave + i * C::kWaves, C::kVInstr - 1);
-      copy16_lds(s.glob ? rvg : rv, buf + 1024 * n, (uint32_t)voff[i] * 2u, s.voffs);
+      copy16_lds((MODE == 0 && s.glob) ? rvg : rv, buf + 1024 * n, (uint32_t)voff[i] * 2u, s.voffs);
     }
   };
 
@@ -441,7 +528,7 @@ void attn_fwd_kernel(
   // thread's list entry first, then the token lookup, then the first copies;
   // the list word is then stored without waiting for the copies, and the Q
   // gather waits for the token lookup only.
-  const int jt = threadIdx.x < cnt ? idx[threadIdx.x] : 0;
+  const int jt = (MODE != 2 && threadIdx.x < cnt) ? idx[threadIdx.x] : 0;
 
   // Q^T operand: lane (l32, g) holds Q[qrow][16 kk + 8 g .. +7], from the
   // reordered rows or, in token order, from the row's token (bf16, or float32
@@ -459,8 +546,10 @@ void attn_fwd_kernel(
   // reaches LDS.
   StageDesc s0{}, sd{};
   if (U > 0) {
-    const int w0 = word_of(__builtin_amdgcn_readfirstlane(idx[0]));
-    const int w1 = word_of(__builtin_amdgcn_readfirstlane(idx[min(1, cnt_m1)]));
+    const int w0 = MODE == 2 ? __builtin_amdgcn_readfirstlane((int)idx_s[0])
+                             : word_of(__builtin_amdgcn_readfirstlane(idx[0]));
+    const int w1 = MODE == 2 ? __builtin_amdgcn_readfirstlane((int)idx_s[min(1, cnt_m1)])
+                             : word_of(__builtin_amdgcn_readfirstlane(idx[min(1, cnt_m1)]));
     const int u1 = min(1, U - 1);
     s0 = stage_w(0, w0);
     sd = stage_w(u1, u1 / C::kSubs == 0 ? w0 : w1);
@@ -468,13 +557,15 @@ void attn_fwd_kernel(
     dma_v(s0, Vb0);
     dma_k(sd, Kb1);
   }
-  if (threadIdx.x < cnt) idx_s[threadIdx.x] = (uint16_t)word_of(jt);
-  for (int t = threadIdx.x + C::kThreads; t < cnt; t += C::kThreads) idx_s[t] = (uint16_t)word_of(idx[t]);
+  if (MODE != 2) {
+    if (threadIdx.x < cnt) idx_s[threadIdx.x] = (uint16_t)word_of(jt);
+    for (int t = threadIdx.x + C::kThreads; t < cnt; t += C::kThreads) idx_s[t] = (uint16_t)word_of(idx[t]);
+  }
   // The list is in LDS: wait for the LDS writes only (a full __syncthreads
   // would also wait for the copies above and the Q loads below).
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-  if (tok.q == nullptr && (!PR || qvalid)) {
+  if (tok.q == nullptr && (MODE == 0 || qvalid)) {
     const __bf16* qp = q_r + (rowbase + qrow) * D + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * kk);
@@ -563,9 +654,9 @@ void attn_fwd_kernel(
   }
 }
 
-template <int D, int BLK, int QB = BLK, bool PR = false>
+template <int D, int BLK, int QB = BLK, int MODE = 0>
 hipError_t launch(const AttnArgs& a) {
-  const int total = a.B * a.Hh * a.nb * (BLK / QB);
+  const int total = MODE == 2 ? a.B * a.Hh * ((a.nb + 1) / 2) : a.B * a.Hh * a.nb * (BLK / QB);
   const float sl2 = a.scale * kLog2e;
   float bias_n = 0.f, bias_last = 0.f;
   if (a.k_g != nullptr) {
@@ -573,7 +664,7 @@ hipError_t launch(const AttnArgs& a) {
     bias_n = (float)(std::log((double)a.n_pool) / a.scale);
     bias_last = (float)(std::log((double)(a.N - (a.Ng - 1) * a.n_pool)) / a.scale);
   }
-  hipLaunchKernelGGL((attn_fwd_kernel<D, BLK, QB, PR>), dim3(total), dim3(AttnCfg<D, BLK, QB>::kThreads), 0,
+  hipLaunchKernelGGL((attn_fwd_kernel<D, BLK, QB, MODE>), dim3(total), dim3(AttnCfg<D, BLK, QB>::kThreads), 0,
                      a.stream, (const __bf16*)a.q_r, (const __bf16*)a.k_r, (const __bf16*)a.v_t,
                      a.kv_count, a.kv_idx, a.order, (const __bf16*)a.k_g, (const __bf16*)a.v_g,
                      (__bf16*)a.o_r, a.lse, a.Hh, a.N, a.Npad, a.nb, a.Ng, sl2, bias_n, bias_last,
@@ -584,9 +675,13 @@ hipError_t launch(const AttnArgs& a) {
 }  // namespace
 
 hipError_t launch_attn_fwd(const AttnArgs& a) {
-  if (a.rowsel != nullptr) {   // pruned queries: 64-row workgroups
-    if (a.d == 64) return a.b == 64 ? launch<64, 64, 64, true>(a) : launch<64, 128, 64, true>(a);
-    return a.b == 64 ? launch<128, 64, 64, true>(a) : launch<128, 128, 64, true>(a);
+  if (a.rowsel != nullptr) {   // pruned queries: pairs of blocks, then the unpaired blocks
+    hipError_t e;
+    if (a.d == 64) e = a.b == 64 ? launch<64, 64, 64, 2>(a) : launch<64, 128, 128, 2>(a);
+    else e = a.b == 64 ? launch<128, 64, 64, 2>(a) : launch<128, 128, 128, 2>(a);
+    if (e != hipSuccess) return e;
+    if (a.d == 64) return a.b == 64 ? launch<64, 64, 64, 1>(a) : launch<64, 128, 128, 1>(a);
+    return a.b == 64 ? launch<128, 64, 64, 1>(a) : launch<128, 128, 128, 1>(a);
   }
   if (a.d == 64) return a.b == 64 ? launch<64, 64>(a) : launch<64, 128>(a);
   return a.b == 64 ? launch<128, 64>(a) : launch<128, 128>(a);
