@@ -137,7 +137,9 @@ struct StageDesc {
 //      each: the first half of the wavefronts takes block 2P's rows, the
 //      second half block 2P + 1's, over the union of their kept-block lists,
 //      a wavefront masking the stages its block does not keep.  Mode 1 skips
-//      the blocks mode 2 takes, and mode 2 exits for the others.
+//      the blocks mode 2 takes, and mode 2 exits for the others.  With a
+//      work order, mode 2 walks the rows in that order and runs each pair
+//      at its first block's place (the longest pairs start first).
 template <int D, int BLK, int QB, int MODE>
 __global__ __launch_bounds__(QB / 32 * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(
@@ -175,9 +177,17 @@ void attn_fwd_kernel(
   const int slot = xcd_remap(blockIdx.x, total);
   int I, bh;
   if constexpr (MODE == 2) {
-    const int np = (nb + 1) / 2;
-    bh = slot / np;
-    I = 2 * (slot % np);
+    if (order != nullptr) {
+      // rows in the work order; a pair runs at its first block's place
+      const int wid = min(max(__builtin_amdgcn_readfirstlane(order[slot]), 0), total - 1);
+      if (wid % nb % 2 != 0) return;   // the whole workgroup, before any barrier
+      I = wid % nb;
+      bh = wid / nb;
+    } else {
+      const int np = (nb + 1) / 2;
+      bh = slot / np;
+      I = 2 * (slot % np);
+    }
   } else {
     const int rows_total = total / kSubQ;
     const int wid = order == nullptr ? slot / kSubQ
@@ -656,7 +666,9 @@ void attn_fwd_kernel(
 
 template <int D, int BLK, int QB = BLK, int MODE = 0>
 hipError_t launch(const AttnArgs& a) {
-  const int total = MODE == 2 ? a.B * a.Hh * ((a.nb + 1) / 2) : a.B * a.Hh * a.nb * (BLK / QB);
+  // mode 2: one work item per pair, or per row (odd rows exit) when a work order is given
+  const int total = (MODE == 2 && a.order == nullptr) ? a.B * a.Hh * ((a.nb + 1) / 2)
+                                                      : a.B * a.Hh * a.nb * (BLK / QB);
   const float sl2 = a.scale * kLog2e;
   float bias_n = 0.f, bias_last = 0.f;
   if (a.k_g != nullptr) {
