@@ -11,6 +11,7 @@ Modules: perm (curve and cuboid orders), reorder (gather / scatter), estimator
 (the top-k and statistical-threshold alternatives), attention
 (block-masked attention with optional global tokens), attention_bwd (its
 gradients, plain ASA, and the key-to-query block lists), query_prune (BSA
-query pruning and token filling), accounting (sparsity and FLOP).  Every function is pinned by CPU tests against closed forms, invariants
+query pruning and token filling), pooled (MEAN / TripPool block estimators
+and the SICS aggregation score), accounting (sparsity and FLOP).  Every function is pinned by CPU tests against closed forms, invariants
 and brute force (tests/test_oracle_*.py).
 """
