@@ -47,6 +47,10 @@ SIGNATURES = {
     "dbs_sparse_attn_fwd_pruned_tok": (_i, [_vp, _i, _i64, _i64, _i64, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i,
                                             _f, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i64, _i64, _i64, _vp,
                                             _vp]),
+    "dbs_pooled_workspace_bytes": (C.c_size_t, [_i, _i, _i, _i, _i]),
+    "dbs_estimate_pooled_tok": (_i, [_vp, _i, _i64, _i64, _i64, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp,
+                                     C.c_size_t, _vp]),
+    "dbs_sics_tok": (_i, [_vp, _i, _i64, _i64, _i64, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
     "dbs_estimate_mask": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, C.c_double, _vp, _vp, _vp, _vp,
                                _vp, _vp, C.c_size_t, _vp]),
     "dbs_estimate_mask_tok": (_i, [_vp, _i, _i64, _i64, _i64, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i,

@@ -31,6 +31,7 @@ SOURCES = [
     "kernels/attn.hip",
     "kernels/attn_bwd.hip",
     "kernels/prune.hip",
+    "kernels/pooled.hip",
 ]
 
 # Packed fp32 VALU ops are disabled on purpose: only plain fp32 ops are emitted.

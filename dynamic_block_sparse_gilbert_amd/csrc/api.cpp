@@ -570,6 +570,54 @@ dbs_status dbs_sparse_attn_fwd_pruned_tok(const void* q, dbs_dtype q_dt, int64_t
   DBS_GUARD_END
 }
 
+size_t dbs_pooled_workspace_bytes(int B, int Hh, int N, int d, int b) {
+  if (B < 1 || Hh < 1 || N < 1 || (d != 64 && d != 128) || (b != 64 && b != 128)) return 0;
+  return dbs::pooled_workspace_bytes(B, Hh, (N + b - 1) / b, d);
+}
+
+dbs_status dbs_estimate_pooled_tok(const void* q, dbs_dtype q_dt, int64_t sb, int64_t sn, int64_t sh,
+                                   const int32_t* perm, int perm_per_head, const void* k_r, int B, int Hh, int N,
+                                   int Npad, int d, int b, int kind, float* p_imp, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  DBS_GUARD_BEGIN
+  dbs_status st = check_tok(q, q_dt, sb, sn, sh, perm, perm_per_head);
+  if (st != DBS_OK) return st;
+  REQUIRE(k_r && p_imp && workspace, DBS_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(aligned16(k_r) && aligned16(p_imp) && aligned16(workspace), DBS_ERR_ALIGNMENT, "misaligned pointer");
+  st = check_geometry(B, Hh, N, Npad, d, b);
+  if (st != DBS_OK) return st;
+  REQUIRE(kind == DBS_POOL_MEAN || kind == DBS_POOL_TRIP, DBS_ERR_INVALID_ARG, "unknown pooling kind %d", kind);
+  const size_t need = dbs_pooled_workspace_bytes(B, Hh, N, d, b);
+  REQUIRE(workspace_bytes >= need, DBS_ERR_INVALID_ARG, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  dbs::PooledArgs a{};
+  a.k_r = k_r; a.p_imp = p_imp; a.workspace = workspace;
+  a.tok.q = q; a.tok.q_f32 = q_dt == DBS_FP32; a.tok.qsb = sb; a.tok.qsn = sn; a.tok.qsh = sh;
+  a.tok.perm = perm; a.tok.perm_h_stride = perm_per_head ? N : 0;
+  a.B = B; a.Hh = Hh; a.N = N; a.Npad = Npad; a.d = d; a.b = b; a.nb = Npad / b; a.kind = kind;
+  a.stream = stream;
+  return from_hip(dbs::launch_pooled(a), "dbs_estimate_pooled_tok launch");
+  DBS_GUARD_END
+}
+
+dbs_status dbs_sics_tok(const void* q, dbs_dtype q_dt, int64_t sb, int64_t sn, int64_t sh, const int32_t* perm,
+                        int perm_per_head, int B, int Hh, int N, int Npad, int d, int b, float* sics,
+                        float* as_out, hipStream_t stream) {
+  DBS_GUARD_BEGIN
+  dbs_status st = check_tok(q, q_dt, sb, sn, sh, perm, perm_per_head);
+  if (st != DBS_OK) return st;
+  REQUIRE(sics && as_out, DBS_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(((uintptr_t)sics & 3u) == 0 && ((uintptr_t)as_out & 3u) == 0, DBS_ERR_ALIGNMENT, "misaligned pointer");
+  st = check_geometry(B, Hh, N, Npad, d, b);
+  if (st != DBS_OK) return st;
+  dbs::SicsArgs a{};
+  a.tok.q = q; a.tok.q_f32 = q_dt == DBS_FP32; a.tok.qsb = sb; a.tok.qsn = sn; a.tok.qsh = sh;
+  a.tok.perm = perm; a.tok.perm_h_stride = perm_per_head ? N : 0;
+  a.sics = sics; a.as = as_out;
+  a.B = B; a.Hh = Hh; a.N = N; a.Npad = Npad; a.d = d; a.b = b; a.nb = Npad / b; a.stream = stream;
+  return from_hip(dbs::launch_sics(a), "dbs_sics_tok launch");
+  DBS_GUARD_END
+}
+
 dbs_status dbs_transpose_lists(const int32_t* kv_count, const int32_t* kv_idx, int B, int Hh, int nb,
                                int32_t* kvT_count, int32_t* kvT_idx, hipStream_t stream) {
   DBS_GUARD_BEGIN

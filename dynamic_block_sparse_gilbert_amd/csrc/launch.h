@@ -104,6 +104,28 @@ struct PruneArgs {
   hipStream_t stream;
 };
 
+// Pooled block estimate (MEAN / TripPool descriptors, row softmax of their products).
+struct PooledArgs {
+  const void* q_r;          // reordered rows, when tok.perm is not set
+  const void* k_r;          // reordered rows [B, Hh, Npad, d]
+  TokIO tok;                // tok.perm set: Q read in token order
+  float* p_imp;             // [B, Hh, nb, nb]
+  void* workspace;          // pooled_workspace_bytes
+  int B, Hh, N, Npad, d, b, nb;
+  int kind;                 // 0 MEAN, 1 TRIP (mean, max, min)
+  hipStream_t stream;
+};
+
+// SICS of every block and the per-head aggregation score.
+struct SicsArgs {
+  const void* q_r;
+  TokIO tok;
+  float* sics;              // [B, Hh, nb]
+  float* as;                // [B, Hh]
+  int B, Hh, N, Npad, d, b, nb;
+  hipStream_t stream;
+};
+
 // Token filling: pruned rows copy their centre's output row (token order).
 struct FillArgs {
   void* out;
@@ -158,6 +180,9 @@ hipError_t launch_build_mask(const MaskArgs& a);
 hipError_t launch_build_order(const MaskArgs& a);   // a.kv_count -> a.order only
 hipError_t launch_query_prune(const PruneArgs& a);
 hipError_t launch_fill_pruned(const FillArgs& a);
+size_t pooled_workspace_bytes(int B, int Hh, int nb, int d);
+hipError_t launch_pooled(const PooledArgs& a);
+hipError_t launch_sics(const SicsArgs& a);
 hipError_t launch_attn_fwd(const AttnArgs& a);
 hipError_t launch_transpose_lists(const TransposeListsArgs& a);
 size_t attn_bwd_workspace_bytes(int B, int Hh, int Npad, int d);

@@ -316,6 +316,61 @@ def sparse_attn_fwd_pruned_tok(q: torch.Tensor, perm: torch.Tensor, k_r: torch.T
     return out, lse
 
 
+POOL_KINDS = {"mean": 0, "trip": 1}
+
+
+def estimate_pooled(q: torch.Tensor, perm: torch.Tensor, k_r: torch.Tensor, N: int, b: int, kind: str,
+                    p_imp: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Pooled block estimate (kind 'mean' or 'trip'): q [B, N, Hh, d] token order, k_r rows ->
+    p_imp float32 [B, Hh, nb, nb]."""
+    _dev(q, perm, k_r, p_imp, workspace)
+    if q.stride(3) != 1:
+        raise ValueError("the d axis of q must be contiguous")
+    B, Hh, Npad, d = k_r.shape
+    nb = Npad // b
+    if p_imp is None:
+        p_imp = torch.empty((B, Hh, nb, nb), dtype=torch.float32, device=k_r.device)
+    need = lib().dbs_pooled_workspace_bytes(B, Hh, N, d, b)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=k_r.device)
+    per_head = 1 if perm.dim() == 2 else 0
+    check("dbs_estimate_pooled_tok", lib().dbs_estimate_pooled_tok(
+        _p(q), _dt(q), q.stride(0), q.stride(1), q.stride(2), _p(perm), per_head, _p(k_r), B, Hh, N, Npad, d, b,
+        POOL_KINDS[kind], _p(p_imp), _p(workspace), workspace.numel() * workspace.element_size(), _stream()))
+    return p_imp
+
+
+def sics(q: torch.Tensor, perm: torch.Tensor, Npad: int, b: int):
+    """SICS of every block of the reordering perm and each head's aggregation score:
+    q [B, N, Hh, d] token order -> (sics [B, Hh, nb], as [B, Hh]) float32."""
+    _dev(q, perm)
+    if q.stride(3) != 1:
+        raise ValueError("the d axis of q must be contiguous")
+    B, N, Hh, d = q.shape
+    nb = Npad // b
+    out = torch.empty((B, Hh, nb), dtype=torch.float32, device=q.device)
+    agg = torch.empty((B, Hh), dtype=torch.float32, device=q.device)
+    per_head = 1 if perm.dim() == 2 else 0
+    check("dbs_sics_tok", lib().dbs_sics_tok(
+        _p(q), _dt(q), q.stride(0), q.stride(1), q.stride(2), _p(perm), per_head, B, Hh, N, Npad, d, b, _p(out),
+        _p(agg), _stream()))
+    return out, agg
+
+
+def choose_cuboids_sics(q: torch.Tensor, T: int, H: int, W: int, candidates, b: int, prefix: int = 0):
+    """Per head, the candidate cuboid (ct, ch, cw) whose cuboid order has the largest SICS
+    aggregation score (one dbs_sics_tok call per candidate).  Returns (index per head, scores
+    [len(candidates), B, Hh])."""
+    N = prefix + T * H * W
+    Npad = -(-N // b) * b
+    scores = []
+    for c in candidates:
+        perm = torch.from_numpy(perm_cuboid(T, H, W, *c, prefix=prefix)).to(q.device)
+        scores.append(sics(q, perm, Npad, b)[1])
+    s = torch.stack(scores)
+    return s.argmax(dim=0), s
+
+
 def meanpool_kv(k_r: torch.Tensor, v_t: torch.Tensor, N: int, b: int, n: int,
                 k_g: Optional[torch.Tensor] = None, v_g: Optional[torch.Tensor] = None
                 ) -> Tuple[torch.Tensor, torch.Tensor, int]:

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define DBS_ABI_VERSION 8
+#define DBS_ABI_VERSION 9
 
 typedef enum {
   DBS_OK = 0,
@@ -295,6 +295,37 @@ dbs_status dbs_sparse_attn_fwd_pruned_tok(const void* q, dbs_dtype q_dt, int64_t
                                           const int32_t* anchor, const uint8_t* keep, void* out,
                                           dbs_dtype out_dt, int64_t osb, int64_t osn, int64_t osh, float* lse,
                                           hipStream_t stream);
+
+/* Pooled block estimate, an alternative to dbs_estimate_blocks on the same
+ * P_imp boundary (the SPADE notes' MEAN and DSA summaries; VEDA key design 1,
+ * TripPool, with its head-specific projections taken as the identity): block
+ * J of b reordered tokens (valid ones only) is summarised by
+ *   DBS_POOL_MEAN  the mean of its tokens (d values), or
+ *   DBS_POOL_TRIP  their mean, channel-wise maximum and minimum (3d values),
+ * in float32 from the bf16 values, and
+ *   p_imp[b, h, I, J] = softmax over J of desc_q(I) . desc_k(J) / sqrt(d'),
+ * d' the descriptor length.  Q in token order as for dbs_estimate_blocks_tok;
+ * k_r DBS_ROWS.  workspace >= dbs_pooled_workspace_bytes (2 * B * Hh * nb *
+ * 3d floats).  Errors as for dbs_estimate_blocks_tok, INVALID_ARG for kind. */
+typedef enum { DBS_POOL_MEAN = 0, DBS_POOL_TRIP = 1 } dbs_pool_kind;
+size_t dbs_pooled_workspace_bytes(int B, int Hh, int N, int d, int b);
+dbs_status dbs_estimate_pooled_tok(const void* q, dbs_dtype q_dt, int64_t sb, int64_t sn, int64_t sh,
+                                   const int32_t* perm, int perm_per_head, const void* k_r,
+                                   int B, int Hh, int N, int Npad, int d, int b, int kind,
+                                   float* p_imp, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+/* SICS (the SPADE notes, runtime scheme generation): for the reordering perm
+ * (a candidate block shape, e.g. dbs_perm_cuboid), every block of b reordered
+ * tokens gets SICS = || sum of its unit-normalised Q rows ||^2 (equal to the
+ * sum of all pairwise cosine similarities in the block; a zero row adds
+ * nothing), float32, sics [B, Hh, nb]; as_out [B, Hh] = the head's
+ * aggregation score, the sum over its blocks in a fixed order.  Choosing, per
+ * head, the candidate with the largest score is the notes' scheme choice.
+ * Q as for dbs_estimate_blocks_tok. */
+dbs_status dbs_sics_tok(const void* q, dbs_dtype q_dt, int64_t sb, int64_t sn, int64_t sh,
+                        const int32_t* perm, int perm_per_head, int B, int Hh, int N, int Npad, int d, int b,
+                        float* sics, float* as_out, hipStream_t stream);
 
 /* ASA_G global tokens (Video-BLADE "Step 2.2 (2)"; BLADE notes key design 2):
  * mean of each window of n consecutive reordered tokens,

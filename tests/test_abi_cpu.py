@@ -37,7 +37,7 @@ def test_all_declared_symbols_exported(dbs):
     for n in names:
         assert hasattr(h, n), n
     assert set(names) == set(L.SIGNATURES), set(names) ^ set(L.SIGNATURES)
-    assert L.lib().dbs_abi_version() == 8
+    assert L.lib().dbs_abi_version() == 9
 
 
 @pytest.mark.parametrize("T,H,W", list(itertools.product(range(1, 7), repeat=3)))
@@ -338,6 +338,35 @@ def test_prune_validation(dbs):
     assert callh(22, 0) == -1             # keep NULL
     assert callh(21, A + 1) == -3         # misaligned anchor
     assert callh(13, 96) == -2            # head dim
+
+
+@cpu_only
+def test_pooled_and_sics_validation(dbs):
+    _, L = dbs
+    ws = L.lib().dbs_pooled_workspace_bytes(1, 2, 100, 128, 64)
+    assert ws == 2 * 1 * 2 * 2 * 3 * 128 * 4
+    assert L.lib().dbs_pooled_workspace_bytes(1, 2, 100, 96, 64) == 0
+    f = L.lib().dbs_estimate_pooled_tok
+    # q, q_dt, sb, sn, sh, perm, pph, k_r, B, Hh, N, Npad, d, b, kind, p_imp, ws, wsb, stream
+    ok = [A, 0, 100 * 2 * 128, 2 * 128, 128, A, 0, A, 1, 2, 100, 128, 128, 64, 1, A, A, ws, None]
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return f(*a)
+    assert call(14, 2) == -1              # unknown kind
+    assert call(17, ws - 1) == -1         # small workspace
+    assert call(15, 0) == -1              # p_imp NULL
+    assert call(7, A + 8) == -3           # misaligned k_r
+    assert call(12, 32) == -2             # head dim
+    g = L.lib().dbs_sics_tok
+    okg = [A, 0, 100 * 2 * 128, 2 * 128, 128, A, 0, 1, 2, 100, 128, 128, 64, A, A, None]
+    def callg(i, v):
+        a = list(okg)
+        a[i] = v
+        return g(*a)
+    assert callg(13, 0) == -1             # sics NULL
+    assert callg(14, A + 2) == -3         # misaligned as
+    assert callg(12, 96) == -2            # block size
 
 
 @cpu_only

@@ -1,0 +1,102 @@
+"""GPU parity: the pooled block estimates (dbs_estimate_pooled_tok, MEAN and TRIP
+descriptors) and the SICS scores (dbs_sics_tok) against the oracle's float64
+versions (oracle/pooled.py).  The GPU forms descriptors and dot products in
+float32 from the bf16 rows: relative 1e-4 on P and on SICS; the per-head
+cuboid choice must match the oracle's argmax wherever the two best scores are
+not within 1e-4 of each other."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import dev, dev_bf16, host, say, smooth_qkv
+from oracle.perm import perm_cuboid, perm_gilbert3d
+from oracle.pooled import aggregation_score, pooled_p_imp, sics_blocks
+from oracle.reorder import reorder_fast as o_reorder
+from workloads.generator import bf16_round
+
+pytestmark = pytest.mark.gpu
+
+
+def _ops():
+    from dynamic_block_sparse_gilbert_amd import ops
+    return ops
+
+
+@pytest.mark.parametrize("T,H,W,Hh,d,b,order,kind,f32", [
+    (4, 12, 20, 2, 64, 64, "gilbert", "mean", False),
+    (4, 12, 20, 2, 128, 128, "gilbert", "trip", False),
+    (3, 10, 14, 1, 128, 64, "cuboid", "trip", True),      # ragged N, float32 input rounded to bf16
+    (5, 16, 16, 1, 64, 128, "cuboid", "mean", False),
+])
+def test_pooled_estimate(T, H, W, Hh, d, b, order, kind, f32):
+    say("pooled", T, H, W, Hh, d, b, order, kind)
+    ops = _ops()
+    N = T * H * W
+    q, k, _ = smooth_qkv(T + H + d, 1, N, Hh, d, grid=(T, H, W))
+    if f32:
+        q = q + np.float32(1e-3) * np.random.default_rng(0).standard_normal(q.shape).astype(np.float32)
+    perm = (perm_gilbert3d(T, H, W) if order == "gilbert" else perm_cuboid(T, H, W, 4, 4, 4)).astype(np.int32)
+    Npad = -(-N // b) * b
+    permd = dev(perm)
+    qd = dev(q) if f32 else dev_bf16(q)
+    k_r = ops.reorder(dev_bf16(k), permd, Npad, b, "rows")
+    P = host(ops.estimate_pooled(qd, permd, k_r, N, b, kind))
+    qr, kr = o_reorder(bf16_round(q), perm, Npad), o_reorder(k, perm, Npad)
+    for h in range(Hh):
+        ref = pooled_p_imp(qr[0, h], kr[0, h], N, b, kind)
+        np.testing.assert_allclose(P[0, h], ref, rtol=1e-4, atol=1e-9)
+
+
+@pytest.mark.parametrize("T,H,W,Hh,d,b", [(4, 16, 16, 3, 128, 64), (3, 10, 14, 2, 64, 128)])
+def test_sics_and_choice(T, H, W, Hh, d, b):
+    say("sics", T, H, W, Hh, d, b)
+    ops = _ops()
+    N = T * H * W
+    q, _, _ = smooth_qkv(7 * T + W, 1, N, Hh, d, grid=(T, H, W))
+    Npad = -(-N // b) * b
+    qd = dev_bf16(q)
+    cands = [(1, 8, 8), (4, 4, 4), (2, 4, 8), (1, 4, 16)]
+    choice, scores = ops.choose_cuboids_sics(qd, T, H, W, cands, b)
+    choice, scores = host(choice), host(scores)
+    ref = np.zeros((len(cands), Hh))
+    for ci, c in enumerate(cands):
+        perm = perm_cuboid(T, H, W, *c)
+        qr = o_reorder(q, perm, Npad)
+        s_blk, _ = ops.sics(qd, dev(perm.astype(np.int32)), Npad, b)
+        s_blk = host(s_blk)
+        for h in range(Hh):
+            want = sics_blocks(qr[0, h], N, b)
+            np.testing.assert_allclose(s_blk[0, h], want, rtol=1e-4, atol=1e-4)
+            ref[ci, h] = aggregation_score(qr[0, h], N, b)
+    np.testing.assert_allclose(scores[:, 0, :], ref, rtol=1e-4)
+    for h in range(Hh):
+        top = np.sort(ref[:, h])[::-1]
+        if top[0] - top[1] > 1e-4 * top[0]:
+            assert choice[0, h] == int(np.argmax(ref[:, h])), h
+
+
+def test_pooled_wan_shape():
+    """The Wan-shaped layer (12 heads, 32,760 tokens, b 128): TRIP estimate on every head against
+    the oracle on two heads, rows summing to one, and the cumulative mask of it through the same
+    selection as the sampled estimate."""
+    say("pooled wan")
+    from workloads import get_config, make_inputs
+    ops = _ops()
+    cfg = get_config(2)
+    T, H, W = cfg.T, cfg.H, cfg.W
+    N, Hh, d, b = T * H * W, cfg.heads, cfg.d, cfg.b
+    Npad = -(-N // b) * b
+    q, k, _ = make_inputs(cfg)
+    perm = perm_gilbert3d(T, H, W).astype(np.int32)
+    permd = dev(perm)
+    qd = dev_bf16(q)
+    k_r = ops.reorder(dev_bf16(k), permd, Npad, b, "rows")
+    Pd = ops.estimate_pooled(qd, permd, k_r, N, b, "trip")
+    cnt, idx, _ = ops.build_mask(Pd, 0.9)
+    P = host(Pd)
+    np.testing.assert_allclose(P.sum(axis=-1), 1.0, rtol=1e-5)
+    qr, kr = o_reorder(q[:, :, :2], perm, Npad), o_reorder(k[:, :, :2], perm, Npad)
+    for h in range(2):
+        np.testing.assert_allclose(P[0, h], pooled_p_imp(qr[0, h], kr[0, h], N, b, "trip"), rtol=1e-4, atol=1e-9)
+    c = host(cnt)
+    assert (c >= 1).all() and (c <= cfg.nb).all()
