@@ -262,6 +262,42 @@ def query_pruning_leg(layer, cfg, qd, steps, torch, r=0.5, win=(2, 2, 2)):
     }
 
 
+def pooled_leg(layer, cfg, qd, steps, torch):
+    """The pooled estimates (MEAN, TRIP) on the timed layer, each timed back to back between two HIP
+    events with the cumulative mask they give at the layer's tau, and the SICS aggregation score of
+    four cuboid block shapes (one call each)."""
+    from dynamic_block_sparse_gilbert_amd import ops
+    sp = layer.spec
+    out = {}
+    ws = torch.empty(max(16, ops.lib().dbs_pooled_workspace_bytes(1, sp.heads, sp.N, sp.d, sp.b)), dtype=torch.uint8,
+                     device=qd.device)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    for kind in ("mean", "trip"):
+        t = timed(lambda: ops.estimate_pooled(qd, layer.perm, layer.k_r, sp.N, sp.b, kind, p_imp=layer.p_imp,
+                                              workspace=ws))
+        cnt, _, _ = ops.build_mask(layer.p_imp, sp.tau)
+        c = cnt.cpu().numpy()
+        out[kind] = {"us": round(t * 1e3, 2), "block_sparsity_at_tau": round(float(1 - c.sum() / (c.size * sp.nb)), 4)}
+    cands = [(1, 8, 16), (2, 8, 8), (4, 4, 8), (1, 4, 32)]
+    t0 = time.perf_counter()
+    choice, scores = ops.choose_cuboids_sics(qd, cfg.T, cfg.H, cfg.W, cands, sp.b)
+    torch.cuda.synchronize()
+    out["sics"] = {"candidates": [list(c) for c in cands], "choice_per_head": choice.cpu().numpy()[0].tolist(),
+                   "wall_ms_4_candidates": round((time.perf_counter() - t0) * 1e3, 2)}
+    return out
+
+
 def cpu_baseline(cfg, q, k, v, perm, tau, heads=2):
     """The oracle, as it stands, on a bounded sample of the same layer: the first
     `heads` heads in full (estimator, mask, attention over every query block),
@@ -387,6 +423,8 @@ def main():
         extra["mask_rules"] = mask_rules_leg(layer, 20, torch)
         layer.mask(args.tau)
         extra["query_pruning"] = query_pruning_leg(layer, cfg, qd, 20, torch)
+        extra["pooled_estimates"] = pooled_leg(layer, cfg, qd, 20, torch)
+        layer.mask(args.tau)
         other = AsaLayer(spec, device=dev, fused=args.unfused)
         ms_o, _ = run_steps(other, qd, kd, vd, out, args.tau, args.steps, args.warmup, torch)
         extra["unfused_ms_per_step" if not args.unfused else "fused_ms_per_step"] = round(ms_o, 4)
