@@ -6,8 +6,9 @@
 // (MEAN) or by their mean, channel-wise maximum and minimum (TRIP, 3d
 // values); S[I, J] = desc_q(I) . desc_k(J) / sqrt(d'), P[I, :] = softmax_J S.
 //   pool_desc_kernel:  one workgroup per (block, head, Q or K); each thread
-//                      owns one channel of one row group, in float32 from the
-//                      bf16 rows (Q read in token order through the permutation).
+//                      owns eight channels of one row group (16-byte loads), in
+//                      float32 from the bf16 rows (Q read in token order
+//                      through the permutation).
 //   pooled_scores_kernel: one workgroup per 16 query blocks of a head; the
 //                      16 query descriptors sit in LDS and every key
 //                      descriptor read from L2 serves all 16 (scores into p_imp).
@@ -49,38 +50,76 @@ struct RowSrc {
   }
 };
 
+// Eight consecutive channels of one row (16 bytes of bf16, or 32 of float32
+// rounded to bf16) as float32.
+__device__ __forceinline__ void load8(const void* base, int64_t off, bool f32, float (&x)[8]) {
+  if (f32) {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
+    const float4 a = p[0], c = p[1];
+    const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = bf16_bits_to_f32(f32_to_bf16_bits(v[e]));
+  } else {
+    const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + off);
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __uint_as_float(u[e] << 16);
+      x[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+    }
+  }
+}
+
+// Each thread owns 8 channels of one row group (16-byte loads; D / 8 threads
+// cover a row), then the row groups are combined in LDS.
 template <int D>
 __global__ __launch_bounds__(kPoolThreads) void pool_desc_kernel(RowSrc q, RowSrc k, PooledArgs a, float* desc) {
-  constexpr int kGroups = kPoolThreads / D;
+  constexpr int kCpr = D / 8;                     // threads per row
+  constexpr int kGroups = kPoolThreads / kCpr;    // row groups
   __shared__ float red[3][kGroups][D];
   const int I = blockIdx.x, bh = blockIdx.y, which = blockIdx.z;   // 0: Q, 1: K
   const int bi = bh / a.Hh, hh = bh % a.Hh;
   const RowSrc& src = which == 0 ? q : k;
-  const int c = threadIdx.x % D, grp = threadIdx.x / D;
+  const int c0 = (threadIdx.x % kCpr) * 8, grp = threadIdx.x / kCpr;
   const int r0 = I * a.b, n = min(a.b, a.N - r0);
-  float s = 0.f, mx = -INFINITY, mn = INFINITY;
-  for (int r = grp; r < n; r += kGroups) {
-    const float x = load_elem<D>(src.x, src.row_off(bi, hh, r0 + r, a.Hh, a.Npad, a.N, D) + c, src.f32);
-    s += x;
-    mx = fmaxf(mx, x);
-    mn = fminf(mn, x);
+  float s[8], mx[8], mn[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    s[e] = 0.f;
+    mx[e] = -INFINITY;
+    mn[e] = INFINITY;
   }
-  red[0][grp][c] = s;
-  red[1][grp][c] = mx;
-  red[2][grp][c] = mn;
+  for (int r = grp; r < n; r += kGroups) {
+    float x[8];
+    load8(src.x, src.row_off(bi, hh, r0 + r, a.Hh, a.Npad, a.N, D) + c0, src.f32, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      s[e] += x[e];
+      mx[e] = fmaxf(mx[e], x[e]);
+      mn[e] = fminf(mn[e], x[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    red[0][grp][c0 + e] = s[e];
+    red[1][grp][c0 + e] = mx[e];
+    red[2][grp][c0 + e] = mn[e];
+  }
   __syncthreads();
-  if (grp == 0) {
-    for (int g = 1; g < kGroups; ++g) {
-      s += red[0][g][c];
-      mx = fmaxf(mx, red[1][g][c]);
-      mn = fminf(mn, red[2][g][c]);
+  if (threadIdx.x < D) {
+    const int c = threadIdx.x;
+    float ts = 0.f, tx = -INFINITY, tn = INFINITY;
+    for (int g = 0; g < kGroups; ++g) {
+      ts += red[0][g][c];
+      tx = fmaxf(tx, red[1][g][c]);
+      tn = fminf(tn, red[2][g][c]);
     }
     const int L = a.kind == 0 ? D : 3 * D;
     float* o = desc + (((int64_t)which * a.B * a.Hh + bh) * a.nb + I) * L;
-    o[c] = s / (float)n;
+    o[c] = ts / (float)n;
     if (a.kind != 0) {
-      o[D + c] = mx;
-      o[2 * D + c] = mn;
+      o[D + c] = tx;
+      o[2 * D + c] = tn;
     }
   }
 }
