@@ -51,6 +51,8 @@ SIGNATURES = {
     "dbs_estimate_pooled_tok": (_i, [_vp, _i, _i64, _i64, _i64, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp,
                                      C.c_size_t, _vp]),
     "dbs_sics_tok": (_i, [_vp, _i, _i64, _i64, _i64, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
+    "dbs_reorder_kv_pool": (_i, [_vp, _vp, _i, _i64, _i64, _i64, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
+                                 _vp, _vp, _vp]),
     "dbs_estimate_mask": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, C.c_double, _vp, _vp, _vp, _vp,
                                _vp, _vp, C.c_size_t, _vp]),
     "dbs_estimate_mask_tok": (_i, [_vp, _i, _i64, _i64, _i64, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i,

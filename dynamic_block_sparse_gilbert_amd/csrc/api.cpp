@@ -215,6 +215,39 @@ dbs_status dbs_reorder_kv(const void* k, const void* v, dbs_dtype x_dt, int64_t 
   DBS_GUARD_END
 }
 
+dbs_status dbs_reorder_kv_pool(const void* k, const void* v, dbs_dtype x_dt, int64_t sb, int64_t sn, int64_t sh,
+                               void* k_r, void* v_t, const int32_t* perm, int perm_per_head, int B, int Hh, int N,
+                               int Npad, int d, int b, int n, void* k_g, void* v_g, hipStream_t stream) {
+  DBS_GUARD_BEGIN
+  REQUIRE(k_g && v_g, DBS_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(aligned16(k_g) && aligned16(v_g), DBS_ERR_ALIGNMENT, "misaligned pointer");
+  REQUIRE(n >= 1 && n <= N, DBS_ERR_INVALID_ARG, "n=%d must be in [1, N]", n);
+  if (b % n != 0) {   // windows cross tiles: the two passes
+    dbs_status st = dbs_reorder_kv(k, v, x_dt, sb, sn, sh, k_r, v_t, perm, perm_per_head, B, Hh, N, Npad, d, b,
+                                   stream);
+    if (st != DBS_OK) return st;
+    return dbs_meanpool_kv(k_r, v_t, DBS_BF16, B, Hh, N, Npad, d, b, n, k_g, v_g, stream);
+  }
+  REQUIRE(k && v && k_r && v_t && perm, DBS_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(aligned16(k) && aligned16(v) && aligned16(k_r) && aligned16(v_t) && ((uintptr_t)perm & 3u) == 0,
+          DBS_ERR_ALIGNMENT, "misaligned pointer");
+  REQUIRE(x_dt == DBS_BF16 || x_dt == DBS_FP32, DBS_ERR_INVALID_ARG, "bad k/v dtype");
+  REQUIRE(perm_per_head == 0 || perm_per_head == 1, DBS_ERR_INVALID_ARG, "perm_per_head must be 0 or 1");
+  dbs_status st = check_geometry(B, Hh, N, Npad, d, b);
+  if (st != DBS_OK) return st;
+  st = check_strides(sb, sn, sh, x_dt);
+  if (st != DBS_OK) return st;
+  dbs::ReorderArgs a{};
+  a.x = k; a.x2 = v; a.y = k_r; a.y2 = v_t; a.sb = sb; a.sn = sn; a.sh = sh; a.perm = perm;
+  a.perm_h_stride = perm_per_head ? N : 0;
+  a.B = B; a.Hh = Hh; a.N = N; a.Npad = Npad; a.d = d; a.b = b;
+  a.x_f32 = x_dt == DBS_FP32; a.y_f32 = false; a.tiles_t = true;
+  a.k_g = k_g; a.v_g = v_g; a.n_pool = n;
+  a.stream = stream;
+  return from_hip(dbs::launch_reorder_kv(a), "dbs_reorder_kv_pool launch");
+  DBS_GUARD_END
+}
+
 dbs_status dbs_inverse_reorder(const void* y, dbs_dtype y_dt, void* x, dbs_dtype x_dt, int64_t sb,
                                int64_t sn, int64_t sh, const int32_t* perm, int perm_per_head, int B,
                                int Hh, int N, int Npad, int d, hipStream_t stream) {

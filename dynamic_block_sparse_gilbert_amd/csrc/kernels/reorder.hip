@@ -138,11 +138,36 @@ __global__ __launch_bounds__((D / 8) * (BLK / 8)) void reorder_tiles_t_kernel(
 // (rows tg, tg + BLK/8, ... of the tile, channel chunk c).  Both halves share
 // the permutation and run the same number of chunks, so a launch over all tiles
 // is a whole number of occupancy rounds where the two separate launches were not.
-template <typename Tin, int D, int BLK>
+// Global-token outputs of the fused K/V reorder (ASA_G, window n dividing b).
+struct PoolOut {
+  __bf16* k_g;   // rows [B, Hh, Ngpad, D]
+  __bf16* v_g;   // tiles-transposed [B, Hh, Ngpad / b, D, b]
+  int n, Ng;
+};
+
+// Eight channels 8 cc .. 8 cc + 7 of global token g: a 16-byte k_g row chunk,
+// or eight entries of a v_g tile column.
+template <int D, int BLK>
+__device__ __forceinline__ void pool_store_t(const PoolOut& p, bool v, int64_t bh, int g, int Ngpad, int cc,
+                                             const uint32_t (&o)[4]) {
+  if (!v) {
+    *reinterpret_cast<uint4*>(p.k_g + (bh * Ngpad + g) * D + 8 * cc) = make_uint4(o[0], o[1], o[2], o[3]);
+  } else {
+    uint16_t* out = reinterpret_cast<uint16_t*>(p.v_g) + bh * (int64_t)Ngpad * D;
+    const int64_t base = (int64_t)(g / BLK) * D * BLK + tile_col(g % BLK);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      out[base + (int64_t)(8 * cc + 2 * q) * BLK] = (uint16_t)(o[q] & 0xffffu);
+      out[base + (int64_t)(8 * cc + 2 * q + 1) * BLK] = (uint16_t)(o[q] >> 16);
+    }
+  }
+}
+
+template <typename Tin, int D, int BLK, bool POOL>
 __global__ __launch_bounds__(2 * (D / 8) * (BLK / 8)) void reorder_kv_kernel(
     const Tin* __restrict__ k, const Tin* __restrict__ v, int64_t sb, int64_t sn, int64_t sh,
     __bf16* __restrict__ k_r, __bf16* __restrict__ v_t, const int32_t* __restrict__ perm,
-    int perm_h_stride, int Hh, int N, int nb) {
+    int perm_h_stride, int Hh, int N, int nb, PoolOut pool) {
   constexpr int kHalf = (D / 8) * (BLK / 8);
   const int J = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
   const int t = threadIdx.x % kHalf;
@@ -151,6 +176,9 @@ __global__ __launch_bounds__(2 * (D / 8) * (BLK / 8)) void reorder_kv_kernel(
   const int32_t* ph = perm + (int64_t)h * perm_h_stride;
   const int64_t bh = (int64_t)bi * Hh + h;
   uint32_t w[8][4];
+  // POOL: the tile's K and V rows as bf16, token-major, for the window means
+  __shared__ __attribute__((aligned(16))) __bf16 ks[POOL ? BLK : 1][POOL ? D : 8];
+  __shared__ __attribute__((aligned(16))) __bf16 vs[POOL ? BLK : 1][POOL ? D : 8];
   if (threadIdx.x < kHalf) {   // wave-uniform: kHalf is a multiple of 64
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -162,6 +190,10 @@ __global__ __launch_bounds__(2 * (D / 8) * (BLK / 8)) void reorder_kv_kernel(
         x.to_bf16(o);
       }
       w[e][0] = o.x; w[e][1] = o.y; w[e][2] = o.z; w[e][3] = o.w;
+      if constexpr (POOL) {
+        uint32_t* row = reinterpret_cast<uint32_t*>(&vs[tile_col(8 * tg + e)][8 * c]);
+        row[0] = o.x; row[1] = o.y; row[2] = o.z; row[3] = o.w;
+      }
     }
     __bf16* tile = v_t + (bh * nb + J) * (int64_t)(D * BLK);
 #pragma unroll
@@ -186,12 +218,55 @@ __global__ __launch_bounds__(2 * (D / 8) * (BLK / 8)) void reorder_kv_kernel(
         x.to_bf16(o);
       }
       w[e][0] = o.x; w[e][1] = o.y; w[e][2] = o.z; w[e][3] = o.w;
+      if constexpr (POOL) {
+        uint32_t* row = reinterpret_cast<uint32_t*>(&ks[tg + e * (BLK / 8)][8 * c]);
+        row[0] = o.x; row[1] = o.y; row[2] = o.z; row[3] = o.w;
+      }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int i = J * BLK + tg + e * (BLK / 8);
       *reinterpret_cast<uint4*>(k_r + (bh * nb * BLK + i) * D + 8 * c) =
           make_uint4(w[e][0], w[e][1], w[e][2], w[e][3]);
+    }
+  }
+  if constexpr (POOL) {
+    // ASA_G global tokens of this tile's windows (n divides BLK): the same
+    // sums as dbs_meanpool_kv, float32 in ascending token order, divided by
+    // the window's valid count and rounded to bf16.  Threads of the first half
+    // form k_g chunks (8 channels of one window), the second half v_g chunks.
+    __syncthreads();
+    const int wpt = BLK / pool.n;                 // windows per tile
+    const int Ngpad = (pool.Ng + BLK - 1) / BLK * BLK;
+    const bool vhalf = threadIdx.x >= kHalf;
+    const int u = threadIdx.x % kHalf;
+    for (int item = u; item < wpt * (D / 8); item += kHalf) {
+      const int wi = item / (D / 8), cc = item % (D / 8);
+      const int g = J * wpt + wi;
+      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      const int r = g < pool.Ng ? min(pool.n, N - g * pool.n) : 0;
+      for (int e = 0; e < r; ++e) {
+        const uint4 x = *reinterpret_cast<const uint4*>(vhalf ? &vs[wi * pool.n + e][8 * cc] : &ks[wi * pool.n + e][8 * cc]);
+        const uint32_t xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] += bf16_bits_to_f32(xv[q] & 0xffffu);
+          acc[2 * q + 1] += bf16_bits_to_f32(xv[q] >> 16);
+        }
+      }
+      const float fr = (float)(r > 0 ? r : 1);
+      uint32_t o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = r > 0 ? pack_bf16x2(acc[2 * q] / fr, acc[2 * q + 1] / fr) : 0u;
+      if (g < Ngpad) pool_store_t<D, BLK>(pool, vhalf, bh, g, Ngpad, cc, o);
+    }
+    // rows past the last tile's windows up to Ngpad are zero
+    if (J == nb - 1) {
+      for (int item = u; item < (Ngpad - nb * wpt) * (D / 8); item += kHalf) {
+        const int g = nb * wpt + item / (D / 8), cc = item % (D / 8);
+        const uint32_t z[4] = {0u, 0u, 0u, 0u};
+        pool_store_t<D, BLK>(pool, vhalf, bh, g, Ngpad, cc, z);
+      }
     }
   }
 }
@@ -305,9 +380,15 @@ hipError_t launch_tiles(const ReorderArgs& a) {
 template <typename Tin, int D, int BLK>
 hipError_t launch_kv(const ReorderArgs& a) {
   dim3 grid(a.Npad / BLK, a.Hh, a.B);
-  hipLaunchKernelGGL((reorder_kv_kernel<Tin, D, BLK>), grid, dim3(2 * (D / 8) * (BLK / 8)), 0,
-                     a.stream, (const Tin*)a.x, (const Tin*)a.x2, a.sb, a.sn, a.sh, (__bf16*)a.y,
-                     (__bf16*)a.y2, a.perm, a.perm_h_stride, a.Hh, a.N, a.Npad / BLK);
+  PoolOut pool{(__bf16*)a.k_g, (__bf16*)a.v_g, a.n_pool, a.n_pool > 0 ? (a.N + a.n_pool - 1) / a.n_pool : 0};
+  if (a.k_g != nullptr)
+    hipLaunchKernelGGL((reorder_kv_kernel<Tin, D, BLK, true>), grid, dim3(2 * (D / 8) * (BLK / 8)), 0,
+                       a.stream, (const Tin*)a.x, (const Tin*)a.x2, a.sb, a.sn, a.sh, (__bf16*)a.y,
+                       (__bf16*)a.y2, a.perm, a.perm_h_stride, a.Hh, a.N, a.Npad / BLK, pool);
+  else
+    hipLaunchKernelGGL((reorder_kv_kernel<Tin, D, BLK, false>), grid, dim3(2 * (D / 8) * (BLK / 8)), 0,
+                       a.stream, (const Tin*)a.x, (const Tin*)a.x2, a.sb, a.sn, a.sh, (__bf16*)a.y,
+                       (__bf16*)a.y2, a.perm, a.perm_h_stride, a.Hh, a.N, a.Npad / BLK, pool);
   return hipGetLastError();
 }
 

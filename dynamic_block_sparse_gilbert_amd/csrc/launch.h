@@ -19,6 +19,9 @@ struct ReorderArgs {
   int perm_h_stride;    // 0 (shared) or N (per head)
   int B, Hh, N, Npad, d, b;
   bool x_f32, y_f32, tiles_t;
+  void* k_g;            // reorder_kv: set (with v_g, n_pool dividing b) to form the ASA_G global tokens too
+  void* v_g;
+  int n_pool;
   hipStream_t stream;
 };
 

@@ -103,9 +103,11 @@ class AsaLayer:
         """Reorder (and pool) K and V and keep Q; q, k, v are [B, N, Hh, d]."""
         s = self.spec
         self.q = q
-        ops.reorder_kv(k, v, self.perm, s.Npad, s.b, k_r=self.k_r, v_t=self.v_t)
-        if s.n_pool:
-            ops.meanpool_kv(self.k_r, self.v_t, s.N, s.b, s.n_pool, k_g=self.k_g, v_g=self.v_g)
+        if s.n_pool:   # the global tokens in the same launch (two passes when n does not divide b)
+            ops.reorder_kv(k, v, self.perm, s.Npad, s.b, k_r=self.k_r, v_t=self.v_t, n_pool=s.n_pool, k_g=self.k_g,
+                           v_g=self.v_g)
+        else:
+            ops.reorder_kv(k, v, self.perm, s.Npad, s.b, k_r=self.k_r, v_t=self.v_t)
 
     def mask(self, tau: Optional[float] = None, keep_p_imp: bool = False) -> None:
         s = self.spec

@@ -91,10 +91,12 @@ def reorder(x: torch.Tensor, perm: torch.Tensor, Npad: int, b: int, layout: str 
 
 
 def reorder_kv(k: torch.Tensor, v: torch.Tensor, perm: torch.Tensor, Npad: int, b: int,
-               k_r: Optional[torch.Tensor] = None, v_t: Optional[torch.Tensor] = None):
+               k_r: Optional[torch.Tensor] = None, v_t: Optional[torch.Tensor] = None, n_pool: int = 0,
+               k_g: Optional[torch.Tensor] = None, v_g: Optional[torch.Tensor] = None):
     """k, v [B, N, Hh, d] (same strides, d contiguous) -> k_r rows [B, Hh, Npad, d] and v_t tiles
-    [B, Hh, Npad/b, d, b], both bf16, in one launch."""
-    _dev(k, v, perm, k_r, v_t)
+    [B, Hh, Npad/b, d, b], both bf16, in one launch.  With n_pool > 0 also the ASA_G global tokens
+    (dbs_reorder_kv_pool): returns (k_r, v_t, k_g, v_g), k_g / v_g as meanpool_kv's."""
+    _dev(k, v, perm, k_r, v_t, k_g, v_g)
     B, N, Hh, d = k.shape
     if v.shape != k.shape or v.stride() != k.stride() or v.dtype != k.dtype:
         raise ValueError("k and v must have the same shape, strides and dtype")
@@ -109,6 +111,17 @@ def reorder_kv(k: torch.Tensor, v: torch.Tensor, perm: torch.Tensor, Npad: int, 
     if k_r.dtype != torch.bfloat16 or v_t.dtype != torch.bfloat16 or not (k_r.is_contiguous() and v_t.is_contiguous()):
         raise ValueError("k_r and v_t must be contiguous bf16")
     per_head = 1 if perm.dim() == 2 else 0
+    if n_pool:
+        Ng = -(-N // n_pool)
+        Ngpad = -(-Ng // b) * b
+        if k_g is None:
+            k_g = torch.empty((B, Hh, Ngpad, d), dtype=torch.bfloat16, device=k.device)
+        if v_g is None:
+            v_g = torch.empty((B, Hh, Ngpad // b, d, b), dtype=torch.bfloat16, device=k.device)
+        check("dbs_reorder_kv_pool", lib().dbs_reorder_kv_pool(
+            _p(k), _p(v), _dt(k), k.stride(0), k.stride(1), k.stride(2), _p(k_r), _p(v_t), _p(perm), per_head,
+            B, Hh, N, Npad, d, b, int(n_pool), _p(k_g), _p(v_g), _stream()))
+        return k_r, v_t, k_g, v_g
     check("dbs_reorder_kv", lib().dbs_reorder_kv(
         _p(k), _p(v), _dt(k), k.stride(0), k.stride(1), k.stride(2), _p(k_r), _p(v_t), _p(perm), per_head,
         B, Hh, N, Npad, d, b, _stream()))

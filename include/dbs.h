@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define DBS_ABI_VERSION 9
+#define DBS_ABI_VERSION 10
 
 typedef enum {
   DBS_OK = 0,
@@ -338,6 +338,18 @@ dbs_status dbs_sics_tok(const void* q, dbs_dtype q_dt, int64_t sb, int64_t sn, i
 dbs_status dbs_meanpool_kv(const void* k_r, const void* v_r, dbs_dtype dt,
                            int B, int Hh, int N, int Npad, int d, int b, int n,
                            void* k_g, void* v_g, hipStream_t stream);
+
+/* dbs_reorder_kv and dbs_meanpool_kv in one launch (the fusion of the reorder
+ * with the ASA_G pooling that SPADE's fused prepass suggests): each tile of b
+ * reordered tokens is reordered and, when n divides b, its windows' means are
+ * formed from the tile held in LDS, with exactly dbs_meanpool_kv's arithmetic
+ * (float32 sums in ascending token order), so k_r, v_t, k_g and v_g equal the
+ * two calls' outputs bit for bit.  When n does not divide b the two calls are
+ * made.  Arguments as for the two calls; k_g, v_g as for dbs_meanpool_kv. */
+dbs_status dbs_reorder_kv_pool(const void* k, const void* v, dbs_dtype x_dt, int64_t sb, int64_t sn, int64_t sh,
+                               void* k_r, void* v_t, const int32_t* perm, int perm_per_head,
+                               int B, int Hh, int N, int Npad, int d, int b, int n,
+                               void* k_g, void* v_g, hipStream_t stream);
 
 /* Block-sparse attention forward (Video-BLADE "Step 2.2").  For every query
  * row q < N of query block I:

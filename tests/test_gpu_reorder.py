@@ -144,3 +144,34 @@ def test_reorder_full_wan_shape():
     assert np.array_equal(_tiles_to_rows(host(yt)), v_rows)
     assert np.array_equal(_tiles_to_rows(host(v_t)), v_rows)
     assert np.array_equal(host(k_r), o_reorder(k, perm, cfg.Npad))
+
+
+@pytest.mark.parametrize("N,n,d,b,order,f32", [
+    (300, 8, 64, 64, "gilbert", False), (17776, 8, 64, 128, "gilbert", False),   # config 3's window and block
+    (1000, 16, 128, 128, "identity", True), (129, 1, 128, 64, "gilbert", False),
+    (1000, 7, 128, 128, "gilbert", False),    # 7 does not divide 128: the two passes
+    (640, 64, 64, 64, "identity", False), (50, 50, 64, 64, "identity", False)])
+def test_reorder_kv_pool_equals_two_calls(N, n, d, b, order, f32):
+    """dbs_reorder_kv_pool: k_r, v_t, k_g and v_g bit-identical to dbs_reorder_kv followed by
+    dbs_meanpool_kv (whose means the test above checks against the oracle)."""
+    say("reorder_kv_pool", N, n, d, b, order)
+    ops = _ops()
+    rng = np.random.default_rng(N + n)
+    B, Hh = 1, 2
+    x = rng.standard_normal((B, N, Hh, 2 * d)).astype(np.float32)
+    if not f32:
+        x = bf16_round(x)
+    kx, vx = x[..., :d].copy(), x[..., d:].copy()
+    if order == "gilbert":
+        perm = np.random.default_rng(1).permutation(N).astype(np.int32)
+    else:
+        perm = np.arange(N, dtype=np.int32)
+    Npad = -(-N // b) * b
+    kd, vd = (dev(kx), dev(vx)) if f32 else (dev_bf16(kx), dev_bf16(vx))
+    pd = dev(perm)
+    k1, v1 = ops.reorder_kv(kd, vd, pd, Npad, b)
+    kg1, vg1, _ = ops.meanpool_kv(k1, v1, N, b, n)
+    k2, v2, kg2, vg2 = ops.reorder_kv(kd, vd, pd, Npad, b, n_pool=n)
+    torch.cuda.synchronize()
+    for a, c in ((k1, k2), (v1, v2), (kg1, kg2), (vg1, vg2)):
+        assert torch.equal(a, c)
