@@ -127,6 +127,7 @@ struct StageDesc {
   int key0;            // index of the stage's first key (token, or global token)
   int kind;            // 0 full, 1 partial / invalid (mask by key index), 2 global tokens
   int limit;           // keys with index >= limit are masked (kind 1, 2)
+  bool absent;         // mode 2: a block this wavefront's query block does not keep (contributes nothing)
 };
 
 // QB: query rows per workgroup.  MODE (BSA query pruning, rowsel lists the
@@ -315,13 +316,10 @@ void attn_fwd_kernel(
     s.glob = !kept;
     s.kind = kept ? ((w >> h) & kPartial ? 1 : 0) : 2;
     s.limit = kept ? ((MODE != 2 && (w & kInvalidBit)) ? -1 : N) : Ng;
-    if constexpr (MODE == 2) {
-      // a block of the union that this wavefront's query block does not keep
-      // (selects, no branch)
-      const bool absent = kept && ((w >> (14 + half)) & 1);
-      s.kind = absent ? 1 : s.kind;
-      s.limit = absent ? -1 : s.limit;
-    }
+    // mode 2: a block of the union that this wavefront's query block does
+    // not keep; its probabilities are made zero through the exponent offset
+    // (no per-key mask) and its maximum is ignored
+    s.absent = MODE == 2 && kept && ((w >> (14 + half)) & 1);
     return s;
   };
   auto stage = [&](int u) -> StageDesc {
@@ -380,6 +378,7 @@ void attn_fwd_kernel(
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16_t{};
   float m = -INFINITY, mneg = 0.f, l = 0.f;
+  bool cur_abs = false;   // mode 2: the current stage is absent for this wavefront
 
   // S^T tiles of one stage: S[kt][v] is key 32 kt + (v/4)*8 + 4g + v%4 of
   // query l32.
@@ -450,14 +449,15 @@ void attn_fwd_kernel(
       scores(ksrc, Sn);
       dma_v(*dv, vdst);
     }
+    const float mn = (MODE == 2 && cur_abs) ? -INFINITY : mneg;
     float s0, s1;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int kt = st >> 1, o = (st & 1) * 8;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float pa = fast_exp2(__builtin_fmaf(Sc[kt][o + 2 * e], sl2, mneg));
-        const float pb = fast_exp2(__builtin_fmaf(Sc[kt][o + 2 * e + 1], sl2, mneg));
+        const float pa = fast_exp2(__builtin_fmaf(Sc[kt][o + 2 * e], sl2, mn));
+        const float pb = fast_exp2(__builtin_fmaf(Sc[kt][o + 2 * e + 1], sl2, mn));
         P[4 * st + e] = cvt_pk(pa, pb);
         s0 = (st | e) == 0 ? pa : s0 + pa;
         s1 = (st | e) == 0 ? pb : s1 + pb;
@@ -520,7 +520,11 @@ void attn_fwd_kernel(
       fixup(sn, Sn);
       mx = row_max(Sn);
     }
+    if constexpr (MODE == 2) {
+      if (sn.absent) mx = -INFINITY;
+    }
     decide(mx);
+    if constexpr (MODE == 2) cur_abs = sn.absent;
     return sk;
   };
 
@@ -607,7 +611,8 @@ void attn_fwd_kernel(
     f32x16_t SA[2], SB[2];
     scores(Kb0, SA);
     if (s0.kind != 0) fixup(s0, SA);
-    decide(row_max(SA));
+    decide((MODE == 2 && s0.absent) ? -INFINITY : row_max(SA));
+    if constexpr (MODE == 2) cur_abs = s0.absent;
     int u = 0;
     for (; u + 2 < U; u += 2) {
       sd = iterate(u, SA, SB, Kb0, Vb1, Kb1, Vb0, sd);
