@@ -99,6 +99,18 @@ class AsaLayer:
             self.k_g = torch.empty((B, Hh, Ngpad, d), **bf)
             self.v_g = torch.empty((B, Hh, Ngpad // s.b, d, s.b), **bf)
 
+    def choose_cuboids_sics(self, q: torch.Tensor, candidates: Sequence[Tuple[int, int, int]]):
+        """Per head, the candidate cuboid with the largest SICS aggregation score on q (SPADE's
+        scheme choice, dbs_sics_tok once per candidate); the layer switches to cuboid_per_head order
+        with those shapes and uploads the new permutation.  q [B, N, Hh, d] token order (the first
+        batch entry decides).  Returns the chosen cuboid of each head."""
+        s = self.spec
+        choice, _ = ops.choose_cuboids_sics(q, s.T, s.H, s.W, candidates, s.b, prefix=s.prefix)
+        chosen = [tuple(candidates[int(c)]) for c in choice[0].tolist()]
+        s.order, s.cuboids = "cuboid_per_head", chosen
+        self.perm = torch.from_numpy(build_perm(s)).to(self.device)
+        return chosen
+
     def prepare(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> None:
         """Reorder (and pool) K and V and keep Q; q, k, v are [B, N, Hh, d]."""
         s = self.spec

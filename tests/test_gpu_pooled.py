@@ -100,3 +100,36 @@ def test_pooled_wan_shape():
         np.testing.assert_allclose(P[0, h], pooled_p_imp(qr[0, h], kr[0, h], N, b, "trip"), rtol=1e-4, atol=1e-9)
     c = host(cnt)
     assert (c >= 1).all() and (c <= cfg.nb).all()
+
+
+def test_layer_sics_choice_config5():
+    """Config 5's per-head cuboid choice made by SICS instead of a seeded draw: the layer's choice
+    equals the oracle's argmax of the aggregation score per head (where the two best differ by more
+    than 1e-4), and the layer then computes exactly what a layer built with those cuboids does."""
+    say("layer sics config5")
+    from workloads import get_config, make_inputs
+    from dynamic_block_sparse_gilbert_amd.layer import AsaLayer, LayerSpec
+    cfg = get_config(5)
+    heads = [0, 1, 2]
+    q, k, v = make_inputs(cfg, heads=heads)
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    spec = LayerSpec(T=cfg.T, H=cfg.H, W=cfg.W, heads=len(heads), d=cfg.d, b=cfg.b, k=cfg.k, tau=0.9,
+                     order="gilbert")
+    layer = AsaLayer(spec)
+    chosen = layer.choose_cuboids_sics(qd, cfg.cuboid_choices)
+    N, b = cfg.N, cfg.b
+    Npad = -(-N // b) * b
+    for h in range(len(heads)):
+        scores = []
+        for c in cfg.cuboid_choices:
+            qr = o_reorder(q[:, :, h:h + 1], perm_cuboid(cfg.T, cfg.H, cfg.W, *c), Npad)
+            scores.append(aggregation_score(qr[0, 0], N, b))
+        top = np.sort(scores)[::-1]
+        if top[0] - top[1] > 1e-4 * top[0]:
+            assert tuple(chosen[h]) == tuple(cfg.cuboid_choices[int(np.argmax(scores))]), (h, scores)
+    out1 = layer.forward(qd, kd, vd)
+    ref = AsaLayer(LayerSpec(T=cfg.T, H=cfg.H, W=cfg.W, heads=len(heads), d=cfg.d, b=cfg.b, k=cfg.k, tau=0.9,
+                             order="cuboid_per_head", cuboids=chosen))
+    out2 = ref.forward(qd, kd, vd)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
