@@ -9,9 +9,9 @@
 //                      owns eight channels of one row group (16-byte loads), in
 //                      float32 from the bf16 rows (Q read in token order
 //                      through the permutation).
-//   pooled_scores_kernel: one workgroup per 16 query blocks of a head; the
-//                      16 query descriptors sit in LDS and every key
-//                      descriptor read from L2 serves all 16 (scores into p_imp).
+//   pooled_scores_kernel: one workgroup per kTileI query blocks of a head; their
+//                      descriptors sit in LDS and every key descriptor read
+//                      from L2 serves all of them (scores into p_imp).
 //   row_softmax_kernel: one wavefront per row, in place.
 // SICS (SPADE notes, scheme generation): per block, || sum_i q_i / |q_i| ||^2.
 //   sics_block_kernel: row norms first (a thread per row), then the
@@ -26,7 +26,6 @@ namespace dbs {
 namespace {
 
 constexpr int kPoolThreads = 256;
-constexpr int kTileI = 16;   // query blocks per scores workgroup
 
 template <int D>
 __device__ __forceinline__ float load_elem(const void* base, int64_t off, bool f32) {
@@ -124,9 +123,14 @@ __global__ __launch_bounds__(kPoolThreads) void pool_desc_kernel(RowSrc q, RowSr
   }
 }
 
+// kTileI query blocks per workgroup: 16 for mean descriptors (key reads
+// dominate), 4 for the 3d-long TRIP descriptors (the products dominate, and
+// four times as many workgroups fill the chip): 55 and 84 us on the Wan shape,
+// against 103 and 117 us the other way round.
 template <int L>
 __global__ __launch_bounds__(kPoolThreads) void pooled_scores_kernel(const float* __restrict__ desc, PooledArgs a,
                                                                      float inv_sqrt_l) {
+  constexpr int kTileI = L <= 128 ? 16 : 4;
   __shared__ float qd[kTileI][L];
   const int I0 = blockIdx.x * kTileI, bh = blockIdx.y;
   const int nI = min(kTileI, a.nb - I0);
@@ -241,7 +245,8 @@ hipError_t launch_pooled(const PooledArgs& a) {
   else hipLaunchKernelGGL(pool_desc_kernel<128>, pg, dim3(kPoolThreads), 0, a.stream, q, k, a, desc);
   const int L = (a.kind == 0 ? 1 : 3) * a.d;
   const float isl = (float)(1.0 / std::sqrt((double)L));
-  const dim3 sg((unsigned)((a.nb + kTileI - 1) / kTileI), (unsigned)BH);
+  const int tile = L <= 128 ? 16 : 4;
+  const dim3 sg((unsigned)((a.nb + tile - 1) / tile), (unsigned)BH);
   switch (L) {
     case 64: hipLaunchKernelGGL(pooled_scores_kernel<64>, sg, dim3(kPoolThreads), 0, a.stream, desc, a, isl); break;
     case 128: hipLaunchKernelGGL(pooled_scores_kernel<128>, sg, dim3(kPoolThreads), 0, a.stream, desc, a, isl); break;
