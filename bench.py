@@ -120,6 +120,7 @@ def stage_times(layer, q, k, v, out, tau, steps, torch):
             e[2].record()
             ops.build_mask(layer.p_imp, tau, kv_count=layer.kv_count, kv_idx=layer.kv_idx, order=layer.order)
         e[len(names) - 1].record()
+        layer.wait_v()   # V is reordered on a side stream
         ops.sparse_attn_fwd_tok(q, layer.perm, layer.k_r, layer.v_t, sp.N, sp.b, sp.scale, layer.kv_count,
                                 layer.kv_idx, layer.k_g, layer.v_g, layer.Ng, sp.n_pool, out=out,
                                 order=layer.order)

@@ -194,6 +194,7 @@ def test_bwd_full_wan_shape_sampled():
     layer = AsaLayer(LayerSpec(T=cfg.T, H=cfg.H, W=cfg.W, heads=cfg.heads, d=cfg.d, b=cfg.b, k=cfg.k, tau=0.9))
     qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
     layer.prepare(qd, kd, vd)
+    layer.wait_v()
     layer.mask(0.9)
     q_r = ops.reorder(qd, layer.perm, cfg.Npad, cfg.b, "rows")
     v_r = ops.reorder(vd, layer.perm, cfg.Npad, cfg.b, "rows")
