@@ -127,3 +127,21 @@ def test_layer_config4_cuboid_long():
 def test_layer_config5_per_head_cuboids():
     cfg = get_config(5)
     _check_layer(cfg, [0, 1], 0.90, sample_blocks=3)
+
+
+def test_layer_overlap_equals_single_stream():
+    """AsaLayer(overlap=True) (V reordered on a second stream beside the estimate) gives the same
+    output, bit for bit, as the single-launch K/V reorder, over several back-to-back steps."""
+    from dynamic_block_sparse_gilbert_amd.layer import AsaLayer, LayerSpec
+    cfg = get_config(2)
+    say("layer overlap", cfg.name)
+    heads = [0, 1, 2]
+    q, k, v = make_inputs(cfg, heads=heads)
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    spec = lambda: LayerSpec(T=cfg.T, H=cfg.H, W=cfg.W, heads=len(heads), d=cfg.d, b=cfg.b, k=cfg.k, tau=0.9)
+    a, b = AsaLayer(spec(), overlap=True), AsaLayer(spec(), overlap=False)
+    for _ in range(3):
+        oa = a.forward(qd, kd, vd)
+        ob = b.forward(qd, kd, vd)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob)
