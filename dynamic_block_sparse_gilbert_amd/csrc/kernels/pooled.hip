@@ -15,7 +15,8 @@
 //   row_softmax_kernel: one wavefront per row, in place.
 // SICS (SPADE notes, scheme generation): per block, || sum_i q_i / |q_i| ||^2.
 //   sics_block_kernel: row norms first (a thread per row), then the
-//                      channel sums of the normalised rows, then the square.
+//                      channel sums of the normalised rows (16-byte loads, eight
+//                      channels per thread), then the square.
 //   sics_head_kernel:  the head's sum over its blocks in a fixed order.
 #include <cmath>
 
@@ -27,11 +28,6 @@ namespace {
 
 constexpr int kPoolThreads = 256;
 
-template <int D>
-__device__ __forceinline__ float load_elem(const void* base, int64_t off, bool f32) {
-  if (f32) return bf16_bits_to_f32(f32_to_bf16_bits(reinterpret_cast<const float*>(base)[off]));
-  return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[off]);
-}
 
 // Element offset of reordered row r of (bi, hh): through the permutation
 // into token-order storage (x_tok) or straight into reordered rows.
@@ -177,27 +173,39 @@ __global__ __launch_bounds__(256) void row_softmax_kernel(float* p, int nb, int6
 
 template <int D>
 __global__ __launch_bounds__(kPoolThreads) void sics_block_kernel(RowSrc q, SicsArgs a) {
-  constexpr int kGroups = kPoolThreads / D;
+  constexpr int kCpr = D / 8;                     // threads per row (8 channels, 16 bytes each)
+  constexpr int kGroups = kPoolThreads / kCpr;
   __shared__ float inv_norm[128];
   __shared__ float red[kGroups][D];
   const int I = blockIdx.x, bh = blockIdx.y;
   const int bi = bh / a.Hh, hh = bh % a.Hh;
   const int r0 = I * a.b, n = min(a.b, a.N - r0);
+  // row norms, a thread per row
   if (threadIdx.x < n) {
     const int64_t off = q.row_off(bi, hh, r0 + threadIdx.x, a.Hh, a.Npad, a.N, D);
     float ss = 0.f;
-    for (int c = 0; c < D; ++c) {
-      const float x = load_elem<D>(q.x, off + c, q.f32);
-      ss = __builtin_fmaf(x, x, ss);
+#pragma unroll 4
+    for (int c = 0; c < kCpr; ++c) {
+      float x[8];
+      load8(q.x, off + 8 * c, q.f32, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
     }
     inv_norm[threadIdx.x] = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
   }
   __syncthreads();
-  const int c = threadIdx.x % D, grp = threadIdx.x / D;
-  float s = 0.f;
-  for (int r = grp; r < n; r += kGroups)
-    s = __builtin_fmaf(load_elem<D>(q.x, q.row_off(bi, hh, r0 + r, a.Hh, a.Npad, a.N, D) + c, q.f32), inv_norm[r], s);
-  red[grp][c] = s;
+  // channel sums of the normalised rows: 8 channels of one row group per thread
+  const int c0 = (threadIdx.x % kCpr) * 8, grp = threadIdx.x / kCpr;
+  float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int r = grp; r < n; r += kGroups) {
+    float x[8];
+    load8(q.x, q.row_off(bi, hh, r0 + r, a.Hh, a.Npad, a.N, D) + c0, q.f32, x);
+    const float w = inv_norm[r];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] = __builtin_fmaf(x[e], w, s[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[grp][c0 + e] = s[e];
   __syncthreads();
   if (threadIdx.x < 64) {
     float acc = 0.f;
