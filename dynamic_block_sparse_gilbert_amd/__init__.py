@@ -1,4 +1,5 @@
-"""Content-adaptive block-sparse attention (ASA / ASA_G) forward for MI355X.
+"""Content-adaptive block-sparse attention (ASA / ASA_G) for MI355X: the forward layer, its
+backward, alternative block selection and estimation, and BSA query pruning.
 
 The computation lives in libdbs.so (hand-written HIP for gfx950, C ABI in
 include/dbs.h); this package holds the ctypes binding (`ops`, one wrapper per

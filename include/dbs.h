@@ -21,7 +21,14 @@
  *   dbs_sparse_attn_fwd_tok                            Q read, O written in token order
  *
  * where dbs_estimate_mask_tok may stand for the estimate and mask pair: it
- * selects the kept blocks from each P_imp row on chip (P_imp optional).
+ * selects the kept blocks from each P_imp row on chip (P_imp optional), and
+ * dbs_reorder_kv_pool for the reorder and meanpool pair (ASA_G).
+ *
+ * Beyond the forward layer: the backward of the attention
+ * (dbs_transpose_lists, dbs_sparse_attn_bwd), other selection rules
+ * (dbs_build_mask_rule), pooled estimates and SICS block-shape scores
+ * (dbs_estimate_pooled_tok, dbs_sics_tok), and BSA query pruning with token
+ * filling (dbs_prune_anchors, dbs_query_prune, dbs_sparse_attn_fwd_pruned_tok).
  *
  * Conventions for every call:
  * - Device pointers are allocated and owned by the caller and must be 16-byte
