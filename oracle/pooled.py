@@ -17,7 +17,10 @@ the place of P_imp on the path.
 SICS (the SPADE notes, runtime scheme generation): a block's sum of intra-block
 cosine similarities over its unit-normalised tokens, SICS = sum_i sum_j
 q_i^ . q_j^ = || sum_i q_i^ ||^2, and a scheme's aggregation score is its sum
-over the blocks, AS = sum_I SICS(I).  Zero rows normalise to zero.
+over the blocks, AS = sum_I SICS(I).  Zero rows normalise to zero.  The notes
+compute the aggregation score of Query and of Key for every candidate scheme
+and pick, per head, the scheme with the highest score; read here as the score
+AS(Q | scheme) + AS(K | scheme), the first candidate winning a tie.
 
 float64 throughout.
 """
@@ -71,3 +74,22 @@ def sics_blocks(q_r: np.ndarray, N: int, b: int) -> np.ndarray:
 def aggregation_score(q_r: np.ndarray, N: int, b: int) -> float:
     """AS of one head under the scheme that produced the reordered rows q_r."""
     return float(sics_blocks(q_r, N, b).sum())
+
+
+def choose_scheme(q: np.ndarray, k, perms, b: int):
+    """One head's scheme choice: q, k [N, d] in token order (k may be None: Q alone); perms a list
+    of candidate orders (perm[new] = token).  Returns (index of the chosen candidate, the scores
+    AS(Q | c) + AS(K | c) of every candidate)."""
+    N = q.shape[0]
+    scores = []
+    for perm in perms:
+        p = np.asarray(perm)
+        sc = aggregation_score(np.asarray(q)[p], N, b)
+        if k is not None:
+            sc += aggregation_score(np.asarray(k)[p], N, b)
+        scores.append(sc)
+    best = 0
+    for c in range(1, len(scores)):
+        if scores[c] > scores[best]:
+            best = c
+    return best, np.array(scores)

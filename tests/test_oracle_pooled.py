@@ -5,7 +5,7 @@ from itertools import combinations
 import numpy as np
 import pytest
 
-from oracle.pooled import aggregation_score, descriptors, pooled_p_imp, sics_blocks
+from oracle.pooled import aggregation_score, choose_scheme, descriptors, pooled_p_imp, sics_blocks
 
 
 def _piecewise(nb, b, d, seed):
@@ -78,3 +78,45 @@ def test_sics_closed_form_and_brute_force():
     assert abs(aggregation_score(q, 2 * b, b) - sics_blocks(q, 2 * b, b).sum()) < 1e-12
     z = np.zeros((3, d))
     assert sics_blocks(z, 3, 3)[0] == 0.0
+
+
+def test_scheme_choice_counts_query_and_key():
+    # four tokens, blocks of two.  Candidate 0 pairs tokens (0, 1), (2, 3); candidate 1 pairs
+    # (0, 2), (1, 3).  SICS of a pair of unit rows is 2 + 2 cos(angle).
+    # Q: rows e0, e0, e1, e1 -> AS(Q | 0) = 4 + 4 = 8, AS(Q | 1) = 2 + 2 = 4, so Q alone picks 0.
+    # K: rows e0, e1, e0, e1 -> AS(K | 0) = 4, AS(K | 1) = 8; Q + K ties at 12 and the first wins.
+    # Scaling K changes nothing.  Q2 = e0, e0, e1, e60 (e60 at 60 degrees to e1, orthogonal to
+    # e0): AS(Q2 | 0) = 4 + 3 = 7, AS(Q2 | 1) = 2 + 2 = 4, so Q2 alone picks 0 but Q2 + K picks 1
+    # (11 < 12): a choice from Q alone, or a K term with the wrong sign, fails one of these.
+    e0, e1 = np.array([1.0, 0.0, 0.0]), np.array([0.0, 1.0, 0.0])
+    q = np.stack([e0, e0, e1, e1])
+    k = np.stack([e0, e1, e0, e1])
+    perms = [np.array([0, 1, 2, 3]), np.array([0, 2, 1, 3])]
+    c, sc = choose_scheme(q, None, perms, 2)
+    assert c == 0 and np.allclose(sc, [8.0, 4.0])
+    c, sc = choose_scheme(q, k, perms, 2)
+    assert np.allclose(sc, [12.0, 12.0]) and c == 0          # tie: the first candidate
+    c3, sc3 = choose_scheme(q, 3.0 * k, perms, 2)
+    assert c3 == 0 and np.allclose(sc3, sc)
+    e60 = np.array([0.0, 0.5, math.sqrt(3) / 2])
+    q2 = np.stack([e0, e0, e1, e60])
+    c, sc = choose_scheme(q2, None, perms, 2)
+    # AS(Q2 | 0) = 4 + (2 + 2 * 0.5) = 7; AS(Q2 | 1): pairs (e0, e1) and (e0, e60), both orthogonal: 4
+    assert c == 0 and np.allclose(sc, [7.0, 4.0])
+    c, sc = choose_scheme(q2, k, perms, 2)
+    assert c == 1 and np.allclose(sc, [11.0, 12.0])
+
+
+def test_scheme_choice_with_k_equal_q_doubles_scores():
+    rng = np.random.default_rng(5)
+    N, d, b = 24, 4, 6
+    q = rng.standard_normal((N, d))
+    perms = [rng.permutation(N) for _ in range(3)]
+    cq, sq = choose_scheme(q, None, perms, b)
+    ck, sk = choose_scheme(q, q, perms, b)
+    assert cq == ck and np.allclose(sk, 2 * sq)
+    # and the scores are the sums of the per-block values of each reordered tensor
+    k = rng.standard_normal((N, d))
+    _, s2 = choose_scheme(q, k, perms, b)
+    for c, p in enumerate(perms):
+        assert abs(s2[c] - sics_blocks(q[p], N, b).sum() - sics_blocks(k[p], N, b).sum()) < 1e-12
