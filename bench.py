@@ -1,31 +1,35 @@
 #!/usr/bin/env python3
-"""Benchmark: one ASA attention layer forward on one MI355X.
+"""Benchmark: ASA attention layers on one MI355X.
 
-Workload: the Wan2.1-1.3B-shaped self-attention layer -- batch 1, 12 heads,
-head dim 128, bf16, latent 21 x 30 x 52 = 32,760 tokens (padded to 32,768),
-smooth-field Q/K (sigma 4) + 0.3 noise, iid V; b = 128, k = 16, Gilbert-curve
-reorder, threshold tau = 0.90 (tau = 0.95 is measured as well and reported
-under "extra", and so is the backward of the attention at tau = 0.90).
-Synthetic inputs stand in for the model's activations.
+Headline workload: the long-sequence layer -- batch 1, 24 heads, head dim 128,
+bf16, latent 40 x 48 x 80 = 153,600 tokens in 4 x 4 x 8 cuboid blocks of 128,
+smooth-field Q/K (temporal sigma 2, spatial sigma 6) + 0.3 noise, iid V;
+b = 128, k = 16, and the cumulative threshold tau bisected (outside the timed
+region) to the largest value whose block sparsity is at least 0.95.  The other
+workload shapes are measured in the same run and reported under
+extra.configs: the 2 x 32 x 32 single-head layer (d 64, tau 0.9), the
+Wan2.1-1.3B-shaped layer (tau 0.90 and 0.95), the CogVideoX-5B-shaped layer
+with ASA_G global tokens (tau 0.95) and the 720p layer with per-head cuboid
+shapes (tau bisected to block sparsity 0.90 and 0.95).  Synthetic inputs
+stand in for the models' activations.
 
-A step is one pass of the whole hot path over that batch, all on one stream:
-reorder K, V -> estimate_mask (the sampled estimate, sampled Q rows read in
-token order, with the cumulative-threshold selection fused into its final
-launch, so P_imp never reaches HBM) -> sparse_attn_fwd (Q read and the output
-written in token order, so the return to token order is part of that launch).
-With --unfused the estimate and the mask run as two calls (estimate_blocks,
-build_mask), the layout the unfused time under "extra" is measured with.  Inputs are resident in
-HBM before timing starts; buffers and the permutation are set up once outside
-the timed region.
+A step is one pass of the whole hot path over one batch, on one stream:
+reorder K, V (with the ASA_G pooling where enabled) -> estimate_mask (sampled
+estimate with the selection fused into its final launch) -> sparse_attn_fwd
+(Q read and the output written in token order).  Inputs are resident in HBM
+before timing; buffers and the permutation are set up outside the timed
+region.
 
 value = dense-equivalent TFLOP/s = 4 * B * H * N^2 * d / (seconds per step).
-The timed region holds HIP events at its two ends only; the per-stage
-breakdown ("stages_ms") comes from a separate untimed pass of the same steps
-with HIP events between the stages on the launch stream.
-roofline = the attention kernel (the dominant one): executed FLOP (4 * d *
-sum over kept block pairs of |I| * |J|) / its mean launch time from that
-breakdown pass, against the bf16 dense MFMA peak.  cpu_baseline = the CPU oracle on a bounded sample of the
-same layer (two of the twelve heads in full), scaled to the whole layer.
+The timed region holds HIP events at its two ends only; per-stage times come
+from a separate untimed pass with HIP events between the stages on the launch
+stream.  roofline = the attention kernel (the dominant one): executed FLOP
+(4 d sum over kept block pairs of |I| |J|, plus 4 d N Ng per head for the
+global tokens) / its mean launch time in that pass, against the bf16 dense
+MFMA peak.  stage_rooflines add the reorder and the mask (HBM), and the
+estimate (MFMA and exponential bound).  cpu_baseline = the CPU oracle on a
+bounded sample of the same layer (some heads, some query blocks), scaled to
+the whole layer.
 """
 from __future__ import annotations
 
@@ -42,22 +46,44 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
 HBM_PEAK_GBS = 8000.0              # MI355X HBM3E peak
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_wan_traffic.json")
+# v_exp_f32 issues at half the 32-bit VALU rate (8 cycles per 64-lane wavefront):
+# 256 CUs x 4 SIMDs x 8 results per clock x 2.4 GHz
+EXP_PEAK_PER_S = 256 * 4 * 8 * 2.4e9
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_traffic.json")
 ATTN_SRC = os.path.join(ROOT, "dynamic_block_sparse_gilbert_amd", "csrc", "kernels", "attn.hip")
+METRIC = "ms/layer + dense-equiv TFLOP/s, block-sparse attn at 90-95% sparsity, 1 GPU"
+
+HEADLINE = (4, "target", 0.95)
+# config id -> the thresholds it is measured at: ("tau", value) fixed by the config,
+# ("target", s) bisected for block sparsity >= s
+EXTRA_RUNS = {1: [("tau", 0.90)], 2: [("tau", 0.90), ("tau", 0.95)], 3: [("tau", 0.95)],
+              5: [("target", 0.90), ("target", 0.95)]}
+# CPU baseline sample per config: (heads, query blocks per head or None for all)
+CPU_SAMPLE = {1: (1, None), 2: (2, 16), 3: (2, 16), 4: (2, 32), 5: (2, 8)}
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--tau", type=float, default=0.90)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=HEADLINE[0], help="headline config id")
+    ap.add_argument("--target", type=float, default=None,
+                    help="headline block-sparsity target (tau bisected); default 0.95 for config 4")
+    ap.add_argument("--tau", type=float, default=None, help="headline fixed tau instead of a target")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true", help="estimate and mask as two calls")
-    ap.add_argument("--no-extra", action="store_true", help="skip the tau=0.95 and backward measurements")
+    ap.add_argument("--no-extra", action="store_true", help="headline only: no other configs, no extra legs")
+    ap.add_argument("--no-legs", action="store_true", help="skip the backward / pruning / pooled / rules legs")
+    ap.add_argument("--configs", type=str, default="1,2,3,5", help="other configs measured under extra")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     return ap.parse_args()
+
+
+def log(*a):
+    """Progress on stderr (the result line alone goes to stdout)."""
+    print("[bench]", *a, file=sys.stderr, flush=True)
 
 
 def src_hash(path: str) -> str:
@@ -71,20 +97,36 @@ def kept_pair_tokens(cnt, idx, N, b, q_rows=None):
     import numpy as np
     nb = cnt.shape[-1]
     L = np.array([min(b, N - J * b) for J in range(nb)], dtype=np.float64)
-    c = cnt.reshape(-1, nb)
+    c = cnt.reshape(-1, nb).astype(np.int64)
     ix = idx.reshape(-1, nb, nb)
-    qr = None if q_rows is None else q_rows.reshape(-1, nb)
-    total = 0.0
-    for r in range(c.shape[0]):
-        for I in range(nb):
-            total += (L[I] if qr is None else qr[r, I]) * L[ix[r, I, :c[r, I]]].sum()
-    return total
+    qr = None if q_rows is None else q_rows.reshape(-1, nb).astype(np.float64)
+    # per row: sum of L over its first c entries (entries past the count are ignored)
+    valid = np.arange(nb)[None, None, :] < c[:, :, None]
+    kl = np.where(valid, L[np.clip(ix, 0, nb - 1)], 0.0).sum(axis=2)
+    rows = L[None, :] if qr is None else qr
+    return float((rows * kl).sum())
+
+
+def sampled_tokens(cfg):
+    return sum(min(cfg.k, min(cfg.b, cfg.N - J * cfg.b)) for J in range(cfg.nb))
+
+
+def _timed(fn, reps, torch, warm=1):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
 
 
 def run_steps(layer, q, k, v, out, tau, steps, warmup, torch):
     """The timed region: `steps` whole layer steps, back to back on one stream, with HIP events
-    only at its two ends (an event between kernels costs a cache write-back of its own).
-    Returns (host ms per step between synchronisations, event ms per step)."""
+    only at its two ends.  Returns (host ms per step between synchronisations, event ms per step)."""
     for _ in range(warmup):
         layer.forward(q, k, v, out=out, tau=tau)
     torch.cuda.synchronize()
@@ -115,26 +157,204 @@ def stage_times(layer, q, k, v, out, tau, steps, torch):
         if layer.fused:
             layer.mask(tau)
         else:
-            ops.estimate_blocks_tok(q, layer.perm, layer.k_r, sp.N, sp.b, sp.k, sp.scale, p_imp=layer.p_imp,
-                                    workspace=layer.ws)
+            layer.estimate_only()
             e[2].record()
             ops.build_mask(layer.p_imp, tau, kv_count=layer.kv_count, kv_idx=layer.kv_idx, order=layer.order)
         e[len(names) - 1].record()
-        layer.wait_v()   # V is reordered on a side stream
-        ops.sparse_attn_fwd_tok(q, layer.perm, layer.k_r, layer.v_t, sp.N, sp.b, sp.scale, layer.kv_count,
-                                layer.kv_idx, layer.k_g, layer.v_g, layer.Ng, sp.n_pool, out=out,
-                                order=layer.order)
+        layer.attend(out)
         e[len(names)].record()
     torch.cuda.synchronize()
     return {n: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps
             for i, n in enumerate(names)}
 
 
+def traffic_lookup(cid, tau):
+    """HBM bytes per attention launch from the committed counter record, if it was taken on the
+    current attention source at this config and tau; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        recs = json.load(open(TRAFFIC_FILE))["records"]
+    except Exception:
+        return None
+    h = src_hash(ATTN_SRC)
+    for r in recs:
+        if r.get("config") == cid and r.get("attn_src_sha256_16") == h and abs(r.get("tau", -1) - tau) < 1e-6:
+            return r.get("bytes_per_launch")
+    return None
+
+
+def make_layer(cfg, dev, fused=True):
+    from dynamic_block_sparse_gilbert_amd.layer import AsaLayer, LayerSpec
+    from workloads.generator import head_cuboid
+    cub = [head_cuboid(cfg, h) for h in range(cfg.heads)] if cfg.reorder == "cuboid_per_head" else None
+    spec = LayerSpec(T=cfg.T, H=cfg.H, W=cfg.W, heads=cfg.heads, d=cfg.d, b=cfg.b, k=cfg.k, tau=0.9,
+                     prefix=cfg.text_prefix, order=cfg.reorder, cuboid=cfg.cuboid, cuboids=cub,
+                     n_pool=cfg.global_pool, dtype=cfg.dtype)
+    return AsaLayer(spec, device=dev, fused=fused)
+
+
+def workload_name(cfg):
+    grid = f"{cfg.T}x{cfg.H}x{cfg.W}"
+    if cfg.text_prefix:
+        grid = f"{cfg.text_prefix} text + {grid}"
+    order = {"gilbert": "Gilbert-curve order", "cuboid": "cuboid order %s" % (cfg.cuboid,),
+             "cuboid_per_head": "per-head cuboid order"}[cfg.reorder]
+    g = f", ASA_G n={cfg.global_pool}" if cfg.global_pool else ""
+    return (f"{cfg.name}: B=1, {cfg.heads} heads, d={cfg.d}, {cfg.dtype}, {grid} = {cfg.N:,} tokens, "
+            f"b={cfg.b}, k={cfg.k}, {order}{g}")
+
+
+def measure(layer, cfg, qd, kd, vd, out, tau, steps, warmup, torch):
+    """One layer at one tau: the timed steps, the stage breakdown, the attention roofline and the
+    byte / estimate stages, each against its own bound."""
+    from dynamic_block_sparse_gilbert_amd import ops
+    sp = layer.spec
+    ms, ms_ev = run_steps(layer, qd, kd, vd, out, tau, steps, warmup, torch)
+    stage = stage_times(layer, qd, kd, vd, out, tau, max(steps, 5), torch)
+    cnt, idx = layer.kv_count.cpu().numpy(), layer.kv_idx.cpu().numpy()
+    nb, H, N, d = cfg.nb, cfg.heads, cfg.N, cfg.d
+    sparsity = 1.0 - cnt.sum() / (cnt.size * nb)
+    pairs = kept_pair_tokens(cnt, idx, N, cfg.b)
+    exec_flop = 4.0 * d * pairs + (4.0 * d * H * N * cfg.Ng if cfg.global_pool else 0.0)
+    attn_ms = stage["attn"]
+    attn_tflops = exec_flop / (attn_ms * 1e-3) / 1e12
+    dense = cfg.dense_flop()
+    reps = max(5, steps)
+    # the estimate and the mask as separate launches, each `reps` times back to back
+    t_est = _timed(layer.estimate_only, reps, torch)
+    t_mask = _timed(lambda: ops.build_mask(layer.p_imp, tau, kv_count=layer.kv_count, kv_idx=layer.kv_idx,
+                                           order=layer.order), reps, torch)
+    ns = sampled_tokens(cfg)
+    est_flop = 2.0 * H * ns * ns * d
+    est_exp = float(H) * ns * ns
+    est_bound_ms = max(est_flop / (MFMA_BF16_PEAK_TFLOPS * 1e12), est_exp / EXP_PEAK_PER_S) * 1e3
+    kept = float(cnt.sum())
+    mask_bytes = 4.0 * H * nb * nb + 4.0 * H * (nb + kept) + 4.0 * H * nb
+    e = 4 if cfg.dtype == "fp32" else 2
+    # bf16: K and V read and written; float32: Q, K and V (the float32 path reorders Q too)
+    nt = 3 if cfg.dtype == "fp32" else 2
+    reorder_bytes = nt * H * N * d * e + nt * H * cfg.Npad * d * e
+    if cfg.global_pool:
+        reorder_bytes += 2.0 * H * (-(-cfg.Ng // cfg.b) * cfg.b) * d * e
+    res = {
+        "workload": workload_name(cfg),
+        "tau": tau,
+        "block_sparsity": round(float(sparsity), 4),
+        "ms_per_step": round(ms, 4),
+        "value": round(dense / (ms * 1e-3) / 1e12, 2),
+        "unit": "dense-equiv TFLOP/s",
+        "step_ms_events": round(ms_ev, 4),
+        "stages_ms": {kk: round(vv, 4) for kk, vv in stage.items()},
+        "token_pairs_kept": pairs,
+        "executed_attn_flop": exec_flop,
+        "dense_equiv_flop": dense,
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_fwd_kernel<%d,%d>" % (d, cfg.b) if cfg.dtype != "fp32" else "attn_fwd_f32_kernel",
+            "achieved": round(attn_tflops, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS if cfg.dtype != "fp32" else 157.3,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / (MFMA_BF16_PEAK_TFLOPS if cfg.dtype != "fp32" else 157.3), 4),
+            "traffic": traffic_lookup(cfg.cid, tau),
+            "launch_ms": round(attn_ms, 4),
+        },
+        "stage_rooflines": {
+            "reorder_kv": {"bound": "hbm", "bytes": reorder_bytes, "ms": round(stage["reorder_kv"], 4),
+                           "achieved_GBs": round(reorder_bytes / (stage["reorder_kv"] * 1e-3) / 1e9, 1),
+                           "peak_GBs": HBM_PEAK_GBS,
+                           "frac": round(reorder_bytes / (stage["reorder_kv"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "estimate": {"bound": "mfma+exp", "flop": est_flop, "exp": est_exp, "ms": round(t_est, 4),
+                         "bound_ms": round(est_bound_ms, 4), "frac": round(est_bound_ms / t_est, 4),
+                         "what": "dbs_estimate_blocks_tok alone (pass + final, P_imp written); bound = "
+                                 "max(FLOP / bf16 MFMA peak, exponentials / %.3g per s)" % EXP_PEAK_PER_S},
+            "mask": {"bound": "hbm", "bytes": mask_bytes, "ms": round(t_mask, 4),
+                     "achieved_GBs": round(mask_bytes / (t_mask * 1e-3) / 1e9, 1), "peak_GBs": HBM_PEAK_GBS,
+                     "frac": round(mask_bytes / (t_mask * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "what": "dbs_build_mask alone on the P_imp (read once), lists and work order written"},
+            "estimate_mask_fused_ms": round(stage.get("estimate_mask", float("nan")), 4),
+        },
+    }
+    # restore this tau's lists (the legs above left them in place, but keep the contract explicit)
+    layer.mask(tau)
+    return res
+
+
+def cpu_baseline(cfg, q, k, v, perm, tau, heads, blocks, seed=0):
+    """The oracle, as it stands, on a bounded sample of the same layer: `heads` heads, and on each
+    either every query block or `blocks` of them (first, last and seeded random ones) for the
+    estimator rows, the mask rows and the attention rows; the time is scaled to all heads and
+    blocks (each stage's work is proportional to the query rows it covers)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle.attention import global_bias, masked_attention, meanpool
+    from oracle.estimator import p_imp
+    from oracle.mask import build_mask
+    from oracle.reorder import reorder_fast
+
+    nb = cfg.nb
+    rng = np.random.default_rng(seed)
+    t_est = t_mask = t_attn = 0.0
+    for h in range(heads):
+        ph = perm[h] if perm.ndim == 2 else perm
+        x = [reorder_fast(t[:, :, h:h + 1], ph, cfg.Npad)[0, 0] for t in (q, k, v)]
+        if blocks is None or blocks >= nb:
+            qb = list(range(nb))
+        else:
+            qb = sorted(set([0, nb - 1] + rng.choice(np.arange(1, nb - 1), size=blocks - 2, replace=False).tolist()))
+        t0 = time.perf_counter()
+        P = p_imp(x[0], x[1], cfg.N, cfg.b, cfg.k, cfg.scale, query_blocks=qb).astype(np.float32)
+        t_est += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        cnt, idx, _, _ = build_mask(P[qb], tau)
+        t_mask += time.perf_counter() - t0
+        kept = [[] for _ in range(nb)]
+        for j, I in enumerate(qb):
+            kept[I] = idx[j, :cnt[j]].tolist()
+        kg = vg = gb = None
+        t0 = time.perf_counter()
+        if cfg.global_pool:
+            kg, vg = meanpool(x[1], cfg.N, cfg.global_pool), meanpool(x[2], cfg.N, cfg.global_pool)
+            gb = global_bias(cfg.N, cfg.global_pool)
+        masked_attention(x[0], x[1], x[2], cfg.N, cfg.b, kept, cfg.scale, kg, vg, gb, query_blocks=qb)
+        t_attn += time.perf_counter() - t0
+    frac = heads / cfg.heads * len(qb) / nb
+    sample = t_est + t_mask + t_attn
+    total = sample / frac
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blk = "every query block" if len(qb) == nb else f"{len(qb)} of {nb} query blocks"
+    return {
+        "value": cfg.dense_flop() / total / 1e12,
+        "unit": "dense-equiv TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"heads 0-{heads - 1} of {cfg.heads}, {blk} each (estimator rows, mask rows, attention rows): "
+                   f"estimator {t_est:.2f} s, mask {t_mask:.2f} s, attention {t_attn:.2f} s "
+                   f"({sample:.1f} s of CPU work); scaled x{1 / frac:.4g} -> {total:.1f} s per layer"),
+        "mask_builder_single_thread_s": round(t_mask, 3),
+        "mask_rows_timed": heads * len(qb),
+        "cpu_model": model,
+        "host_cpus": os.cpu_count(),
+        "blas_threads": threads,
+    }
+
+
+# ----------------------------------------------------------------------------- legs on the Wan layer
+
 def backward_leg(layer, cfg, qd, vd, steps, warmup, torch):
     """The backward of the attention (plain ASA) on the same layer and mask: the key-to-query lists
     and the dQ / dK / dV kernels, timed back to back between two HIP events.  Q, V (rows) and dO are
     reordered and the forward's output and lse computed beforehand, outside the timed region."""
-    import numpy as np
     from dynamic_block_sparse_gilbert_amd import ops
     sp = layer.spec
     q_r = ops.reorder(qd, layer.perm, sp.Npad, sp.b, "rows")
@@ -151,16 +371,7 @@ def backward_leg(layer, cfg, qd, vd, steps, warmup, torch):
         kc, ki = ops.transpose_lists(layer.kv_count, layer.kv_idx)
         ops.sparse_attn_bwd(q_r, layer.k_r, v_r, o_r, do_r, lse, sp.N, sp.b, sp.scale, layer.kv_count,
                             layer.kv_idx, kc, ki, workspace=ws)
-    for _ in range(warmup):
-        one()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        one()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms = _timed(one, steps, torch, warm=warmup)
     cnt, idx = layer.kv_count.cpu().numpy(), layer.kv_idx.cpu().numpy()
     pairs = kept_pair_tokens(cnt, idx, sp.N, sp.b)
     alg = 10.0 * sp.d * pairs        # five products over the kept pairs (S, dP, dV, dQ, dK)
@@ -168,7 +379,7 @@ def backward_leg(layer, cfg, qd, vd, steps, warmup, torch):
     return {
         "ms": round(ms, 4),
         "what": "dbs_transpose_lists + dbs_sparse_attn_bwd (rows -> tiles copies, dQ, dK/dV kernels), "
-                "tau 0.9 mask of the timed layer",
+                "tau %.2f mask of the Wan-shaped layer" % sp.tau,
         "algorithmic_flop": alg,
         "executed_flop": executed,
         "algorithmic_tflops": round(alg / (ms * 1e-3) / 1e12, 1),
@@ -178,30 +389,23 @@ def backward_leg(layer, cfg, qd, vd, steps, warmup, torch):
 
 
 def mask_rules_leg(layer, steps, torch):
-    """The alternative selection rules on the timed layer's P_imp: the kept-block lists under the
-    cumulative threshold (tau 0.9), top-k (k = 16) and the statistical cutoff (u = U(1 - 16/nb)),
-    each launched `steps` times back to back between two HIP events."""
+    """The alternative selection rules on the layer's P_imp: the kept-block lists under the
+    cumulative threshold (tau 0.9), top-k (k = 16) and the statistical cutoff expecting 16 of nb
+    blocks (the library computes u = U(1 - 16/nb)), each launched `steps` times back to back."""
     from dynamic_block_sparse_gilbert_amd import ops
     nb = layer.p_imp.shape[-1]
     out = {}
     for name, rule, param in (("cumulative_tau0.9", "cumulative", 0.9), ("topk_16", "topk", 16),
-                              ("stat_k16", "stat", ops.stat_quantile(16, nb))):
-        ops.build_mask_rule(layer.p_imp, rule, param, kv_count=layer.kv_count, kv_idx=layer.kv_idx)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
-            ops.build_mask_rule(layer.p_imp, rule, param, kv_count=layer.kv_count, kv_idx=layer.kv_idx)
-        e1.record()
-        torch.cuda.synchronize()
+                              ("stat_k16", "stat_k", 16)):
+        t = _timed(lambda: ops.build_mask_rule(layer.p_imp, rule, param, kv_count=layer.kv_count,
+                                               kv_idx=layer.kv_idx), steps, torch)
         cnt = layer.kv_count.cpu().numpy()
-        out[name] = {"us": round(e0.elapsed_time(e1) / steps * 1e3, 2),
-                     "block_sparsity": round(float(1.0 - cnt.sum() / (cnt.size * nb)), 4)}
+        out[name] = {"us": round(t * 1e3, 2), "block_sparsity": round(float(1.0 - cnt.sum() / (cnt.size * nb)), 4)}
     return out
 
 
 def query_pruning_leg(layer, cfg, qd, steps, torch, r=0.5, win=(2, 2, 2)):
-    """BSA query pruning on the timed layer and mask: the kept rows (centres of 2 x 2 x 2 windows plus
+    """BSA query pruning on the layer and mask: the kept rows (centres of 2 x 2 x 2 windows plus
     the most distinct tokens, keep ratio r), the attention over them with token filling, against the
     unpruned attention on the same lists; each timed back to back between two HIP events."""
     from dynamic_block_sparse_gilbert_amd import ops
@@ -223,23 +427,9 @@ def query_pruning_leg(layer, cfg, qd, steps, torch, r=0.5, win=(2, 2, 2)):
         ops.sparse_attn_fwd_tok(qd, layer.perm, layer.k_r, layer.v_t, sp.N, sp.b, sp.scale, layer.kv_count,
                                 layer.kv_idx, out=out, order=layer.order)
 
-    def timed(fn):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps
-
-    t_prune, t_pruned, t_full = timed(prune), timed(pruned), timed(full)
+    t_prune, t_pruned, t_full = (_timed(f, steps, torch, warm=3) for f in (prune, pruned, full))
     cnt, idx, qch = layer.kv_count.cpu().numpy(), layer.kv_idx.cpu().numpy(), qc.cpu().numpy()
     kept_q = float(qch.sum()) / (qch.shape[0] * qch.shape[1] * sp.N)
-    # key blocks streamed by the paired work items (blocks 2P, 2P + 1 over the union of their lists)
-    # against the two lists' own lengths
     nb = cnt.shape[-1]
     c2, i2 = cnt.reshape(-1, nb), idx.reshape(-1, nb, nb)
     own = float(c2.sum())
@@ -248,15 +438,17 @@ def query_pruning_leg(layer, cfg, qd, steps, torch, r=0.5, win=(2, 2, 2)):
         for I in range(0, nb - 1, 2):
             union += len(set(i2[r_, I, :c2[r_, I]].tolist()) | set(i2[r_, I + 1, :c2[r_, I + 1]].tolist()))
     ef = 4.0 * sp.d * kept_pair_tokens(cnt, idx, sp.N, sp.b, q_rows=qch)
-    kv_keep = 1.0 - float(1.0 - cnt.sum() / (cnt.size * cnt.shape[-1]))
+    kv_keep = float(cnt.sum() / (cnt.size * cnt.shape[-1]))
     return {
-        "what": "dbs_query_prune + dbs_sparse_attn_fwd_pruned_tok (64-row work items, then token filling), "
-                "2x2x2 centre windows, keep ratio %.2f, on the tau %.2f mask of the timed layer" % (r, sp.tau),
+        "what": "dbs_query_prune + dbs_sparse_attn_fwd_pruned_tok (attention over the kept rows with token "
+                "filling), 2x2x2 centre windows, keep ratio %.2f, on the tau %.2f mask of the Wan-shaped layer"
+                % (r, sp.tau),
         "query_keep": round(kept_q, 4),
         "kv_block_keep": round(kv_keep, 4),
         "combined_sparsity": round(1.0 - kept_q * kv_keep, 4),
         "prune_us": round(t_prune * 1e3, 2),
         "pruned_attn_ms": round(t_pruned, 4),
+        "prune_plus_pruned_attn_ms": round(t_prune + t_pruned, 4),
         "unpruned_attn_ms": round(t_full, 4),
         "pruned_attn_executed_tflops": round(ef / (t_pruned * 1e-3) / 1e12, 2),
         "pair_union_over_own_blocks": round(2.0 * union / own, 4),
@@ -264,79 +456,87 @@ def query_pruning_leg(layer, cfg, qd, steps, torch, r=0.5, win=(2, 2, 2)):
 
 
 def pooled_leg(layer, cfg, qd, steps, torch):
-    """The pooled estimates (MEAN, TRIP) on the timed layer, each timed back to back between two HIP
-    events with the cumulative mask they give at the layer's tau, and the SICS aggregation score of
-    four cuboid block shapes (one call each)."""
+    """The pooled estimates (MEAN, TRIP) on the layer, each timed back to back between two HIP
+    events, with the cumulative mask they give at the layer's tau."""
     from dynamic_block_sparse_gilbert_amd import ops
     sp = layer.spec
     out = {}
     ws = torch.empty(max(16, ops.lib().dbs_pooled_workspace_bytes(1, sp.heads, sp.N, sp.d, sp.b)), dtype=torch.uint8,
                      device=qd.device)
-
-    def timed(fn):
-        fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps
-
     for kind in ("mean", "trip"):
-        t = timed(lambda: ops.estimate_pooled(qd, layer.perm, layer.k_r, sp.N, sp.b, kind, p_imp=layer.p_imp,
-                                              workspace=ws))
+        t = _timed(lambda: ops.estimate_pooled(qd, layer.perm, layer.k_r, sp.N, sp.b, kind, p_imp=layer.p_imp,
+                                               workspace=ws), steps, torch)
         cnt, _, _ = ops.build_mask(layer.p_imp, sp.tau)
         c = cnt.cpu().numpy()
         out[kind] = {"us": round(t * 1e3, 2), "block_sparsity_at_tau": round(float(1 - c.sum() / (c.size * sp.nb)), 4)}
-    cands = [(1, 8, 16), (2, 8, 8), (4, 4, 8), (1, 4, 32)]
-    t0 = time.perf_counter()
-    choice, scores = ops.choose_cuboids_sics(qd, cfg.T, cfg.H, cfg.W, cands, sp.b)
-    torch.cuda.synchronize()
-    out["sics"] = {"candidates": [list(c) for c in cands], "choice_per_head": choice.cpu().numpy()[0].tolist(),
-                   "wall_ms_4_candidates": round((time.perf_counter() - t0) * 1e3, 2)}
     return out
 
 
-def cpu_baseline(cfg, q, k, v, perm, tau, heads=2):
-    """The oracle, as it stands, on a bounded sample of the same layer: the first
-    `heads` heads in full (estimator, mask, attention over every query block),
-    scaled to all heads."""
+def sics_leg(cfg, qd, kd, steps, torch, step_ms=None):
+    """SPADE's scheme choice on the 720p layer: every candidate block shape of the config scored by
+    the SICS aggregation score of Q and K in one call (candidate permutations uploaded once), and
+    the per-head choice; timed back to back between two HIP events."""
+    from dynamic_block_sparse_gilbert_amd.layer import SicsChooser
+    ch = SicsChooser(cfg.T, cfg.H, cfg.W, cfg.cuboid_choices, cfg.b, prefix=cfg.text_prefix, device=qd.device)
+    t0 = time.perf_counter()
+    ch.choose(qd, kd)
+    torch.cuda.synchronize()
+    first = (time.perf_counter() - t0) * 1e3
+    t = _timed(lambda: ch.choose(qd, kd), steps, torch)
+    choice = ch.choice.cpu().numpy()[0].tolist()
+    res = {"candidates": [list(c) for c in cfg.cuboid_choices], "choice_per_head": choice,
+           "ms_all_candidates": round(t, 4), "first_call_wall_ms": round(first, 2),
+           "what": "dbs_sics_choose: SICS of Q and K for every candidate cuboid order and the per-head argmax, "
+                   "one call"}
+    if step_ms:
+        res["share_of_layer_step"] = round(t / step_ms, 4)
+    return res
+
+
+# ----------------------------------------------------------------------------- driver
+
+def load_inputs(cfg, torch, dev):
+    from workloads import make_inputs
+    t0 = time.perf_counter()
+    q, k, v = make_inputs(cfg, workers=16)
+    t_gen = time.perf_counter() - t0
+    dt = torch.float32 if cfg.dtype == "fp32" else torch.bfloat16
+    to = lambda a: torch.from_numpy(a).to(dt).to(dev)
+    return (q, k, v), (to(q), to(k), to(v)), t_gen
+
+
+def resolve_tau(layer, qd, kd, vd, out, mode, val):
+    if mode == "tau":
+        return float(val), {"tau_rule": "fixed by the workload"}
+    layer.forward(qd, kd, vd, out=out, tau=1.0, keep_p_imp=True)
+    tau, s = layer.tune_tau(val)
+    return tau, {"tau_rule": f"largest float32 tau with block sparsity >= {val} (bisection with dbs_build_mask "
+                             "on the layer's P_imp, outside the timed region)", "target_sparsity": val}
+
+
+def run_config(cid, rules, args, torch, dev, cpu=True):
     import numpy as np
-    from threadpoolctl import threadpool_info
-
-    from oracle.attention import masked_attention
-    from oracle.estimator import p_imp
-    from oracle.mask import build_mask
-    from oracle.reorder import reorder_fast
-
-    t_est = t_mask = t_attn = 0.0
-    for h in range(heads):
-        x = [reorder_fast(t[:, :, h:h + 1], perm, cfg.Npad)[0, 0] for t in (q, k, v)]
-        t0 = time.perf_counter()
-        P = p_imp(x[0], x[1], cfg.N, cfg.b, cfg.k, cfg.scale).astype(np.float32)
-        t_est += time.perf_counter() - t0
-        t0 = time.perf_counter()
-        cnt, idx, _, _ = build_mask(P, tau)
-        t_mask += time.perf_counter() - t0
-        kept = [idx[I, :cnt[I]].tolist() for I in range(cfg.nb)]
-        t0 = time.perf_counter()
-        masked_attention(x[0], x[1], x[2], cfg.N, cfg.b, kept, cfg.scale)
-        t_attn += time.perf_counter() - t0
-    sample = t_est + t_mask + t_attn
-    total = sample * cfg.heads / heads
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {
-        "value": cfg.dense_flop() / total / 1e12,
-        "unit": "dense-equiv TFLOP/s",
-        "cores": threads,
-        "kind": "oracle",
-        "sample": (f"heads 0-{heads - 1} of {cfg.heads} in full: estimator {t_est:.2f} s, mask {t_mask:.2f} s, "
-                   f"attention over all {cfg.nb} query blocks {t_attn:.2f} s ({sample:.1f} s of CPU work); "
-                   f"scaled x{cfg.heads / heads:g} heads -> {total:.1f} s per layer"),
-        "host_cpus": os.cpu_count(),
-    }
+    from workloads import get_config
+    cfg = get_config(cid)
+    log(f"config {cid}: inputs")
+    host, (qd, kd, vd), t_gen = load_inputs(cfg, torch, dev)
+    layer = make_layer(cfg, dev, fused=not args.unfused)
+    out = torch.empty_like(qd)
+    torch.cuda.synchronize()
+    results = []
+    for mode, val in rules:
+        tau, info = resolve_tau(layer, qd, kd, vd, out, mode, val)
+        log(f"config {cid}: tau {tau:.6g}, timing")
+        res = measure(layer, cfg, qd, kd, vd, out, tau, args.steps, args.warmup, torch)
+        res.update(info)
+        res["input_gen_s"] = round(t_gen, 2)
+        log(f"config {cid}: {res['ms_per_step']} ms/step, sparsity {res['block_sparsity']}")
+        if cpu:
+            log(f"config {cid}: cpu baseline")
+            heads, blocks = CPU_SAMPLE[cid]
+            res["cpu_baseline"] = cpu_baseline(cfg, *host, np.asarray(layer.perm.cpu().numpy()), tau, heads, blocks)
+        results.append(res)
+    return cfg, layer, (qd, kd, vd), results
 
 
 def main():
@@ -347,24 +547,9 @@ def main():
               "configuration is not part of this build.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    from dynamic_block_sparse_gilbert_amd.layer import AsaLayer, LayerSpec
-    from workloads import get_config, make_inputs
-
-    cfg = get_config(2)
-    t_gen = time.perf_counter()
-    q, k, v = make_inputs(cfg)                    # bf16-representable float32 [1, N, 12, 128]
-    t_gen = time.perf_counter() - t_gen
     dev = torch.device("cuda:0")
-    to = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)
-    qd, kd, vd = to(q), to(k), to(v)
-    out = torch.empty_like(qd)
-    spec = LayerSpec(T=cfg.T, H=cfg.H, W=cfg.W, heads=cfg.heads, d=cfg.d, b=cfg.b, k=cfg.k, tau=args.tau)
-    layer = AsaLayer(spec, device=dev, fused=not args.unfused)
-    torch.cuda.synchronize()
-
     if args.copy_calib_mib:
         n = args.copy_calib_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -373,106 +558,79 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    ms, ms_ev = run_steps(layer, qd, kd, vd, out, args.tau, args.steps, args.warmup, torch)
-    stage = stage_times(layer, qd, kd, vd, out, args.tau, args.steps, torch)
-    attn_ms = stage["attn"]
-    cnt, idx = layer.kv_count.cpu().numpy(), layer.kv_idx.cpu().numpy()
-    nb = cfg.nb
-    sparsity = 1.0 - cnt.sum() / (cnt.size * nb)
-    pairs = kept_pair_tokens(cnt, idx, cfg.N, cfg.b)
-    exec_flop = 4.0 * cfg.d * pairs
-    attn_tflops = exec_flop / (attn_ms * 1e-3) / 1e12
-    dense = cfg.dense_flop()
-
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        try:
-            tj = json.load(open(TRAFFIC_FILE))
-            if tj.get("attn_src_sha256_16") == src_hash(ATTN_SRC) and abs(tj.get("tau", -1) - args.tau) < 1e-9:
-                traffic = tj.get("bytes_per_launch")
-        except Exception:
-            traffic = None
-
-    # byte passes: reorder of K, V (read + write) and P_imp read / kv lists write
-    e = 2
-    reorder_bytes = 2.0 * 2 * cfg.heads * cfg.N * cfg.d * e
-    mask_bytes = 4.0 * cfg.heads * nb * nb + 4.0 * cfg.heads * (nb + cnt.sum())
-    byte_passes = {"reorder_kv_GBs": round(reorder_bytes / (stage["reorder_kv"] * 1e-3) / 1e9, 1)}
-    if "mask" in stage:
-        byte_passes["mask_GBs"] = round(mask_bytes / (stage["mask"] * 1e-3) / 1e9, 1)
-    byte_passes["hbm_peak_GBs"] = HBM_PEAK_GBS
-
-    extra = {}
-    if not args.no_extra:
-        n95 = max(5, args.steps // 2)
-        ms95, _ = run_steps(layer, qd, kd, vd, out, 0.95, n95, 2, torch)
-        stage95 = stage_times(layer, qd, kd, vd, out, 0.95, n95, torch)
-        attn95 = stage95["attn"]
-        c95, i95 = layer.kv_count.cpu().numpy(), layer.kv_idx.cpu().numpy()
-        ef95 = 4.0 * cfg.d * kept_pair_tokens(c95, i95, cfg.N, cfg.b)
-        extra["tau_0.95"] = {
-            "ms_per_step": round(ms95, 4),
-            "value": round(dense / (ms95 * 1e-3) / 1e12, 2),
-            "block_sparsity": round(float(1.0 - c95.sum() / (c95.size * nb)), 4),
-            "stages_ms": {kk: round(vv, 4) for kk, vv in stage95.items()},
-            "attn_executed_tflops": round(ef95 / (attn95 * 1e-3) / 1e12, 2),
-        }
-        layer.forward(qd, kd, vd, out=out, tau=args.tau)   # the timed mask again
-        layer.mask(args.tau, keep_p_imp=True)              # and its P_imp, for the rule comparison
-        torch.cuda.synchronize()
-        extra["backward"] = backward_leg(layer, cfg, qd, vd, max(5, args.steps // 5), 3, torch)
-        extra["mask_rules"] = mask_rules_leg(layer, 20, torch)
-        layer.mask(args.tau)
-        extra["query_pruning"] = query_pruning_leg(layer, cfg, qd, 20, torch)
-        extra["pooled_estimates"] = pooled_leg(layer, cfg, qd, 20, torch)
-        layer.mask(args.tau)
-        other = AsaLayer(spec, device=dev, fused=args.unfused)
-        ms_o, _ = run_steps(other, qd, kd, vd, out, args.tau, args.steps, args.warmup, torch)
-        extra["unfused_ms_per_step" if not args.unfused else "fused_ms_per_step"] = round(ms_o, 4)
-        del other
+    if args.tau is not None:
+        rule = ("tau", args.tau)
+    elif args.target is not None:
+        rule = ("target", args.target)
+    elif args.config == HEADLINE[0]:
+        rule = HEADLINE[1:]
+    else:
+        rule = EXTRA_RUNS.get(args.config, [("tau", 0.9)])[0]
+    cfg, layer, _, (head,) = run_config(args.config, [rule], args, torch, dev, cpu=not args.no_cpu_baseline)
+    del layer
+    torch.cuda.empty_cache()
 
     line = {
-        "metric": "ms/layer + dense-equiv TFLOP/s, block-sparse attn at 90-95% sparsity, 1 GPU",
-        "value": round(dense / (ms * 1e-3) / 1e12, 3),
+        "metric": METRIC,
+        "value": head["value"],
         "unit": "dense-equiv TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32" if cfg.dtype == "fp32" else "bf16",
         "data": "synthetic (seeded smooth-field Q/K, iid V; no model weights)",
         "config": {
-            "workload": "wan2.1-1.3b-shaped ASA layer: B=1, 12 heads, d=128, 21x30x52 = 32,760 tokens, "
-                        "b=128, k=16, Gilbert reorder",
-            "tau": args.tau,
-            "block_sparsity": round(float(sparsity), 4),
-            "token_pairs_kept": pairs,
-            "executed_attn_flop": exec_flop,
-            "dense_equiv_flop": dense,
+            "workload": head["workload"],
+            "tau": head["tau"],
+            "tau_rule": head["tau_rule"],
+            "block_sparsity": head["block_sparsity"],
+            "token_pairs_kept": head["token_pairs_kept"],
+            "executed_attn_flop": head["executed_attn_flop"],
+            "dense_equiv_flop": head["dense_equiv_flop"],
         },
-        "roofline": {
-            "bound": "mfma",
-            "kernel": "attn_fwd_kernel<128,128>",
-            "achieved": round(attn_tflops, 2),
-            "peak": MFMA_BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": traffic,
-            "launch_ms": round(attn_ms, 4),
-        },
-        "stages_ms": {kk: round(vv, 4) for kk, vv in stage.items()},
-        "byte_passes": byte_passes,
-        "step_ms_events": round(ms_ev, 4),
-        "input_gen_s": round(t_gen, 2),
+        "roofline": head["roofline"],
+        "stage_rooflines": head["stage_rooflines"],
+        "stages_ms": head["stages_ms"],
+        "step_ms_events": head["step_ms_events"],
+        "input_gen_s": head["input_gen_s"],
     }
-    if extra:
+    if "cpu_baseline" in head:
+        line["cpu_baseline"] = head["cpu_baseline"]
+
+    if not args.no_extra:
+        extra = {"configs": {}}
+        wan_layer = None
+        for cid in [int(c) for c in args.configs.split(",") if c.strip()]:
+            if cid == args.config or cid not in EXTRA_RUNS:
+                continue
+            c, lay, tens, results = run_config(cid, EXTRA_RUNS[cid], args, torch, dev, cpu=not args.no_cpu_baseline)
+            for (mode, val), r in zip(EXTRA_RUNS[cid], results):
+                extra["configs"][f"config{cid}_{'tau' if mode == 'tau' else 's'}{val:.2f}"] = r
+            if not args.no_legs and cid == 2:
+                lay.spec.tau = 0.90
+                lay.forward(*tens, tau=0.90, keep_p_imp=True)
+                torch.cuda.synchronize()
+                extra["backward"] = backward_leg(lay, c, tens[0], tens[2], 10, 3, torch)
+                extra["mask_rules"] = mask_rules_leg(lay, 20, torch)
+                lay.mask(0.90)
+                extra["query_pruning"] = query_pruning_leg(lay, c, tens[0], 20, torch)
+                extra["pooled_estimates"] = pooled_leg(lay, c, tens[0], 20, torch)
+                lay.mask(0.90)
+                other = make_layer(c, dev, fused=args.unfused)
+                ms_o, _ = run_steps(other, *tens, torch.empty_like(tens[0]), 0.90, args.steps, args.warmup, torch)
+                extra["wan_tau0.90_unfused_ms_per_step" if not args.unfused else "wan_tau0.90_fused_ms_per_step"] = \
+                    round(ms_o, 4)
+                del other
+            if not args.no_legs and cid == 5:
+                step = results[0]["ms_per_step"] if results else None
+                extra["sics_scheme_choice"] = sics_leg(c, tens[0], tens[1], 10, torch, step)
+            del lay, tens
+            torch.cuda.empty_cache()
         line["extra"] = extra
-    if not args.no_cpu_baseline:
-        perm = layer.perm.cpu().numpy()
-        line["cpu_baseline"] = cpu_baseline(cfg, q, k, v, perm, args.tau)
     print(json.dumps(line), flush=True)
 
 

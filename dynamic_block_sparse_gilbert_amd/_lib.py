@@ -1,8 +1,8 @@
 """ctypes loader for libdbs.so and the argument types of every C-ABI entry point.
 
-The library is loaded from this package directory only (it is built there by
-build.py); a missing library raises ImportError-style RuntimeError, there is
-no fallback of any kind.
+The library is the one build.py writes into this package directory (or the
+build that DBS_LIB_PATH names); a missing library raises RuntimeError, and
+there is no fallback of any kind.
 """
 from __future__ import annotations
 
@@ -11,7 +11,9 @@ import os
 import threading
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdbs.so")
+# DBS_LIB_PATH selects another build of the same library (the host-sanitizer
+# build that the CPU tests load); by default the one built in this directory.
+LIB_PATH = os.environ.get("DBS_LIB_PATH") or os.path.join(_HERE, "libdbs.so")
 
 DBS_OK = 0
 STATUS_NAMES = {0: "DBS_OK", -1: "DBS_ERR_INVALID_ARG", -2: "DBS_ERR_UNSUPPORTED",
@@ -51,6 +53,9 @@ SIGNATURES = {
     "dbs_estimate_pooled_tok": (_i, [_vp, _i, _i64, _i64, _i64, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp,
                                      C.c_size_t, _vp]),
     "dbs_sics_tok": (_i, [_vp, _i, _i64, _i64, _i64, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
+    "dbs_sics_choose": (_i, [_vp, _vp, _i, _i64, _i64, _i64, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp,
+                             _vp]),
+    "dbs_normal_quantile": (C.c_double, [C.c_double]),
     "dbs_reorder_kv_pool": (_i, [_vp, _vp, _i, _i64, _i64, _i64, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
                                  _vp, _vp, _vp]),
     "dbs_estimate_mask": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, C.c_double, _vp, _vp, _vp, _vp,

@@ -25,6 +25,7 @@ ARCH = "gfx950"
 SOURCES = [
     "api.cpp",
     "host/perm.cpp",
+    "host/stats.cpp",
     "kernels/reorder.hip",
     "kernels/estimate.hip",
     "kernels/mask.hip",
@@ -32,6 +33,7 @@ SOURCES = [
     "kernels/attn_bwd.hip",
     "kernels/prune.hip",
     "kernels/pooled.hip",
+    "kernels/fp32.hip",
 ]
 
 # Packed fp32 VALU ops are disabled on purpose: only plain fp32 ops are emitted.

@@ -254,8 +254,9 @@ dbs_status dbs_inverse_reorder(const void* y, dbs_dtype y_dt, void* x, dbs_dtype
   DBS_GUARD_BEGIN
   REQUIRE(x && y && perm, DBS_ERR_INVALID_ARG, "NULL pointer");
   REQUIRE(aligned16(x) && aligned16(y) && ((uintptr_t)perm & 3u) == 0, DBS_ERR_ALIGNMENT, "misaligned pointer");
-  REQUIRE(y_dt == DBS_BF16, DBS_ERR_UNSUPPORTED, "inverse_reorder reads bf16 rows");
+  REQUIRE(y_dt == DBS_BF16 || y_dt == DBS_FP32, DBS_ERR_INVALID_ARG, "bad y dtype");
   REQUIRE(x_dt == DBS_BF16 || x_dt == DBS_FP32, DBS_ERR_INVALID_ARG, "bad x dtype");
+  REQUIRE(!(y_dt == DBS_FP32 && x_dt == DBS_BF16), DBS_ERR_UNSUPPORTED, "float32 -> bf16 inverse not offered");
   REQUIRE(perm_per_head == 0 || perm_per_head == 1, DBS_ERR_INVALID_ARG, "perm_per_head must be 0 or 1");
   REQUIRE(B >= 1 && Hh >= 1 && N >= 1 && Npad >= N, DBS_ERR_INVALID_ARG, "bad sizes");
   REQUIRE(d == 64 || d == 128, DBS_ERR_UNSUPPORTED, "head dim d=%d unsupported", d);
@@ -265,7 +266,7 @@ dbs_status dbs_inverse_reorder(const void* y, dbs_dtype y_dt, void* x, dbs_dtype
   a.y = const_cast<void*>(y); a.x_out = x; a.sb = sb; a.sn = sn; a.sh = sh; a.perm = perm;
   a.perm_h_stride = perm_per_head ? N : 0;
   a.B = B; a.Hh = Hh; a.N = N; a.Npad = Npad; a.d = d; a.b = 0;
-  a.x_f32 = x_dt == DBS_FP32;
+  a.x_f32 = x_dt == DBS_FP32; a.y_f32 = y_dt == DBS_FP32;
   a.stream = stream;
   return from_hip(dbs::launch_inverse_reorder(a), "dbs_inverse_reorder launch");
   DBS_GUARD_END
@@ -304,10 +305,48 @@ dbs_status rule_args(int rule, double param, int nb, dbs::MaskArgs& a) {
     a.rule = 1; a.topk = param >= nb ? nb : (int)param;
   } else if (rule == DBS_RULE_STAT) {
     a.rule = 2; a.u = param;
+  } else if (rule == DBS_RULE_STAT_K) {
+    REQUIRE(param > 0.0 && param < (double)nb, DBS_ERR_INVALID_ARG, "expected count %g must be in (0, nb=%d)",
+            param, nb);
+    a.rule = 2; a.u = dbs::normal_quantile(1.0 - param / nb);
   } else {
     return fail(DBS_ERR_INVALID_ARG, "unknown rule %d", rule);
   }
   return DBS_OK;
+}
+
+// Float32 operands (reordered rows): the VALU estimator writes P_imp (into the
+// workspace when the fused call is given no p_imp), then the selection runs on it.
+dbs_status estimate_f32_impl(const void* q_r, const void* k_r, int B, int Hh, int N, int Npad, int d, int b,
+                             int k, float scale, float* p_imp, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream, const dbs::MaskArgs* fuse = nullptr) {
+  REQUIRE(q_r && k_r && (p_imp || fuse) && workspace, DBS_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(aligned16(q_r) && aligned16(k_r) && aligned16(p_imp) && aligned16(workspace), DBS_ERR_ALIGNMENT,
+          "misaligned pointer");
+  dbs_status st = check_geometry(B, Hh, N, Npad, d, b);
+  if (st != DBS_OK) return st;
+  REQUIRE(k >= 1 && k <= b, DBS_ERR_INVALID_ARG, "k=%d must be in [1, b=%d]", k, b);
+  REQUIRE(std::isfinite(scale) && scale > 0.f, DBS_ERR_INVALID_ARG, "scale must be finite and > 0");
+  const size_t need = dbs_estimate_workspace_bytes(B, Hh, N, d, b, k);
+  REQUIRE(workspace_bytes >= need, DBS_ERR_INVALID_ARG, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  const int nb = Npad / b;
+  REQUIRE(nb <= 4096, DBS_ERR_UNSUPPORTED, "nb=%d must be in [1, 4096]", nb);
+  REQUIRE((int64_t)B * Hh * nb <= INT32_MAX, DBS_ERR_INVALID_ARG, "too many rows");
+  float* P = p_imp;
+  if (P == nullptr) {
+    REQUIRE(workspace_bytes >= (size_t)B * Hh * nb * nb * sizeof(float), DBS_ERR_INVALID_ARG,
+            "workspace too small to hold P_imp");
+    P = reinterpret_cast<float*>(workspace);
+  }
+  dbs::EstimateArgs a{};
+  a.q_r = q_r; a.k_r = k_r; a.p_imp = P; a.workspace = workspace;
+  a.B = B; a.Hh = Hh; a.N = N; a.Npad = Npad; a.d = d; a.b = b; a.k = k; a.nb = nb;
+  a.scale = scale; a.stream = stream;
+  hipError_t e = dbs::launch_estimate_f32(a);
+  if (e != hipSuccess || fuse == nullptr) return from_hip(e, "dbs_estimate_blocks launch");
+  dbs::MaskArgs m = *fuse;
+  m.p_imp = P; m.rows = B * Hh * nb; m.nb = nb; m.stream = stream;
+  return from_hip(dbs::launch_build_mask(m), "dbs_estimate_mask launch");
 }
 
 // fuse set: P_imp rows go straight into the block selection (p_imp nullable).
@@ -360,7 +399,9 @@ dbs_status dbs_estimate_blocks(const void* q_r, const void* k_r, dbs_dtype dt, i
   DBS_GUARD_BEGIN
   REQUIRE(q_r, DBS_ERR_INVALID_ARG, "NULL pointer");
   REQUIRE(aligned16(q_r), DBS_ERR_ALIGNMENT, "misaligned pointer");
-  REQUIRE(dt == DBS_BF16, DBS_ERR_UNSUPPORTED, "estimate_blocks computes on bf16 inputs");
+  REQUIRE(dt == DBS_BF16 || dt == DBS_FP32, DBS_ERR_INVALID_ARG, "bad dtype");
+  if (dt == DBS_FP32)
+    return estimate_f32_impl(q_r, k_r, B, Hh, N, Npad, d, b, k, scale, p_imp, workspace, workspace_bytes, stream);
   return estimate_impl(q_r, k_r, B, Hh, N, Npad, d, b, k, scale, p_imp, workspace, workspace_bytes, dbs::TokIO{},
                        stream);
   DBS_GUARD_END
@@ -388,10 +429,13 @@ dbs_status dbs_estimate_mask(const void* q_r, const void* k_r, dbs_dtype dt, int
   DBS_GUARD_BEGIN
   REQUIRE(q_r, DBS_ERR_INVALID_ARG, "NULL pointer");
   REQUIRE(aligned16(q_r), DBS_ERR_ALIGNMENT, "misaligned pointer");
-  REQUIRE(dt == DBS_BF16, DBS_ERR_UNSUPPORTED, "estimate_mask computes on bf16 inputs");
+  REQUIRE(dt == DBS_BF16 || dt == DBS_FP32, DBS_ERR_INVALID_ARG, "bad dtype");
   dbs::MaskArgs m{};
   dbs_status st = fuse_args(rule, param, kv_count, kv_idx, mask, order, Npad, b, m);
   if (st != DBS_OK) return st;
+  if (dt == DBS_FP32)
+    return estimate_f32_impl(q_r, k_r, B, Hh, N, Npad, d, b, k, scale, p_imp, workspace, workspace_bytes, stream,
+                             &m);
   return estimate_impl(q_r, k_r, B, Hh, N, Npad, d, b, k, scale, p_imp, workspace, workspace_bytes, dbs::TokIO{},
                        stream, &m);
   DBS_GUARD_END
@@ -480,7 +524,7 @@ dbs_status attn_impl(const void* q_r, const void* k_r, const void* v_r, int B, i
                      int b, float scale, const int32_t* kv_count, const int32_t* kv_idx, const int32_t* order,
                      const void* k_g, const void* v_g, int Ng, int n_pool, void* o_r, float* lse,
                      const dbs::TokIO& tok, hipStream_t stream, const int32_t* q_count = nullptr,
-                     const int32_t* rowsel = nullptr) {
+                     const int32_t* rowsel = nullptr, bool f32 = false) {
   REQUIRE(k_r && v_r && kv_count && kv_idx, DBS_ERR_INVALID_ARG, "NULL pointer");
   REQUIRE(aligned16(k_r) && aligned16(v_r), DBS_ERR_ALIGNMENT, "misaligned pointer");
   REQUIRE(((uintptr_t)kv_count & 3u) == 0 && ((uintptr_t)kv_idx & 3u) == 0 && ((uintptr_t)lse & 3u) == 0 &&
@@ -504,6 +548,7 @@ dbs_status attn_impl(const void* q_r, const void* k_r, const void* v_r, int B, i
   a.q_count = q_count; a.rowsel = rowsel;
   REQUIRE(a.nb <= 4096, DBS_ERR_UNSUPPORTED, "nb=%d must be <= 4096", a.nb);
   REQUIRE((int64_t)B * Hh * a.nb <= INT32_MAX, DBS_ERR_INVALID_ARG, "too many query blocks");
+  if (f32) return from_hip(dbs::launch_attn_fwd_f32(a), "dbs_sparse_attn_fwd launch");
   return from_hip(dbs::launch_attn_fwd(a), "dbs_sparse_attn_fwd launch");
 }
 
@@ -519,7 +564,12 @@ dbs_status dbs_sparse_attn_fwd(const void* q_r, const void* k_r, const void* v_r
   DBS_GUARD_BEGIN
   REQUIRE(q_r && o_r, DBS_ERR_INVALID_ARG, "NULL pointer");
   REQUIRE(aligned16(q_r) && aligned16(o_r), DBS_ERR_ALIGNMENT, "misaligned pointer");
-  REQUIRE(dt == DBS_BF16, DBS_ERR_UNSUPPORTED, "sparse_attn_fwd computes on bf16 inputs");
+  REQUIRE(dt == DBS_BF16 || dt == DBS_FP32, DBS_ERR_INVALID_ARG, "bad dtype");
+  if (dt == DBS_FP32) {
+    REQUIRE(k_g == nullptr && v_g == nullptr, DBS_ERR_UNSUPPORTED, "float32 attention takes no global tokens");
+    return attn_impl(q_r, k_r, v_r, B, Hh, N, Npad, d, b, scale, kv_count, kv_idx, order, nullptr, nullptr, 0, 0,
+                     o_r, lse, dbs::TokIO{}, stream, nullptr, nullptr, true);
+  }
   return attn_impl(q_r, k_r, v_r, B, Hh, N, Npad, d, b, scale, kv_count, kv_idx, order, k_g, v_g, Ng, n_pool,
                    o_r, lse, dbs::TokIO{}, stream);
   DBS_GUARD_END
@@ -650,6 +700,31 @@ dbs_status dbs_sics_tok(const void* q, dbs_dtype q_dt, int64_t sb, int64_t sn, i
   return from_hip(dbs::launch_sics(a), "dbs_sics_tok launch");
   DBS_GUARD_END
 }
+
+dbs_status dbs_sics_choose(const void* q, const void* k, dbs_dtype dt, int64_t sb, int64_t sn, int64_t sh,
+                           const int32_t* perms, int n_cand, int B, int Hh, int N, int Npad, int d, int b,
+                           float* block_scores, float* scores, int32_t* choice, hipStream_t stream) {
+  DBS_GUARD_BEGIN
+  dbs_status st = check_tok(q, dt, sb, sn, sh, perms, 0);
+  if (st != DBS_OK) return st;
+  REQUIRE(k == nullptr || aligned16(k), DBS_ERR_ALIGNMENT, "misaligned pointer");
+  REQUIRE(block_scores && scores && choice, DBS_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(((uintptr_t)block_scores & 3u) == 0 && ((uintptr_t)scores & 3u) == 0 && ((uintptr_t)choice & 3u) == 0,
+          DBS_ERR_ALIGNMENT, "misaligned pointer");
+  REQUIRE(n_cand >= 1 && n_cand <= 64, DBS_ERR_INVALID_ARG, "n_cand=%d must be in [1, 64]", n_cand);
+  st = check_geometry(B, Hh, N, Npad, d, b);
+  if (st != DBS_OK) return st;
+  dbs::SicsArgs a{};
+  a.tok.q = q; a.tok.q_f32 = dt == DBS_FP32; a.tok.qsb = sb; a.tok.qsn = sn; a.tok.qsh = sh;
+  a.tok.perm = perms; a.tok.perm_h_stride = 0;
+  a.sics = block_scores; a.as = scores; a.choice = choice;
+  a.k = k; a.perms = perms; a.n_cand = n_cand; a.tensors = k != nullptr ? 2 : 1;
+  a.B = B; a.Hh = Hh; a.N = N; a.Npad = Npad; a.d = d; a.b = b; a.nb = Npad / b; a.stream = stream;
+  return from_hip(dbs::launch_sics(a), "dbs_sics_choose launch");
+  DBS_GUARD_END
+}
+
+double dbs_normal_quantile(double p) { return dbs::normal_quantile(p); }
 
 dbs_status dbs_transpose_lists(const int32_t* kv_count, const int32_t* kv_idx, int B, int Hh, int nb,
                                int32_t* kvT_count, int32_t* kvT_idx, hipStream_t stream) {

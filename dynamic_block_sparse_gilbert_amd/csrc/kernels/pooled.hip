@@ -171,15 +171,25 @@ __global__ __launch_bounds__(256) void row_softmax_kernel(float* p, int nb, int6
   for (int j = lane; j < nb; j += 64) r[j] = __expf(r[j] - m) * inv;
 }
 
+// Candidate scoring (dbs_sics_choose): blockIdx.z = candidate * tensors + tensor
+// picks the tensor (Q, then K) and the candidate's permutation; the block's
+// score goes to a.sics[(z * B * Hh + bh) * nb + I].
 template <int D>
 __global__ __launch_bounds__(kPoolThreads) void sics_block_kernel(RowSrc q, SicsArgs a) {
   constexpr int kCpr = D / 8;                     // threads per row (8 channels, 16 bytes each)
   constexpr int kGroups = kPoolThreads / kCpr;
   __shared__ float inv_norm[128];
   __shared__ float red[kGroups][D];
-  const int I = blockIdx.x, bh = blockIdx.y;
+  const int I = blockIdx.x, bh = blockIdx.y, z = blockIdx.z;
   const int bi = bh / a.Hh, hh = bh % a.Hh;
   const int r0 = I * a.b, n = min(a.b, a.N - r0);
+  if (a.n_cand > 0) {   // candidate z / tensors, tensor z % tensors
+    const int t = z % a.tensors;
+    if (t == 1) q.x = a.k;
+    q.perm = a.perms + (int64_t)(z / a.tensors) * a.N;
+    q.perm_h_stride = 0;
+  }
+  float* out = a.sics + (int64_t)z * a.B * a.Hh * a.nb;
   // row norms, a thread per row
   if (threadIdx.x < n) {
     const int64_t off = q.row_off(bi, hh, r0 + threadIdx.x, a.Hh, a.Npad, a.N, D);
@@ -215,7 +225,7 @@ __global__ __launch_bounds__(kPoolThreads) void sics_block_kernel(RowSrc q, Sics
       acc = __builtin_fmaf(t, t, acc);
     }
     for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-    if (threadIdx.x == 0) a.sics[(int64_t)bh * a.nb + I] = acc;
+    if (threadIdx.x == 0) out[(int64_t)bh * a.nb + I] = acc;
   }
 }
 
@@ -225,6 +235,28 @@ __global__ __launch_bounds__(64) void sics_head_kernel(SicsArgs a) {
   for (int I = lane; I < a.nb; I += 64) s += a.sics[(int64_t)bh * a.nb + I];
   for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
   if (lane == 0) a.as[bh] = s;
+}
+
+// Per (batch, head): each candidate's aggregation score (the sum over the
+// tensors and blocks of the block scores, lanes over blocks in a fixed order
+// and a fixed butterfly), and the candidate with the largest score (the
+// smallest index among equal ones).
+__global__ __launch_bounds__(64) void sics_choose_kernel(SicsArgs a) {
+  const int bh = blockIdx.x, lane = threadIdx.x;
+  const int64_t per = (int64_t)a.B * a.Hh * a.nb;
+  float best = -INFINITY;
+  int arg = 0;
+  for (int c = 0; c < a.n_cand; ++c) {
+    float s = 0.f;
+    for (int t = 0; t < a.tensors; ++t) {
+      const float* blk = a.sics + (int64_t)(c * a.tensors + t) * per + (int64_t)bh * a.nb;
+      for (int I = lane; I < a.nb; I += 64) s += blk[I];
+    }
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+    if (lane == 0) a.as[(int64_t)c * a.B * a.Hh + bh] = s;
+    if (c == 0 || s > best) { best = s; arg = c; }
+  }
+  if (lane == 0) a.choice[bh] = arg;
 }
 
 RowSrc make_src(const TokIO& t, const void* rows) {
@@ -269,10 +301,14 @@ hipError_t launch_pooled(const PooledArgs& a) {
 
 hipError_t launch_sics(const SicsArgs& a) {
   const RowSrc q = make_src(a.tok, a.q_r);
-  const dim3 g((unsigned)a.nb, (unsigned)(a.B * a.Hh));
+  const unsigned zs = a.n_cand > 0 ? (unsigned)(a.n_cand * a.tensors) : 1u;
+  const dim3 g((unsigned)a.nb, (unsigned)(a.B * a.Hh), zs);
   if (a.d == 64) hipLaunchKernelGGL(sics_block_kernel<64>, g, dim3(kPoolThreads), 0, a.stream, q, a);
   else hipLaunchKernelGGL(sics_block_kernel<128>, g, dim3(kPoolThreads), 0, a.stream, q, a);
-  hipLaunchKernelGGL(sics_head_kernel, dim3((unsigned)(a.B * a.Hh)), dim3(64), 0, a.stream, a);
+  if (a.n_cand > 0)
+    hipLaunchKernelGGL(sics_choose_kernel, dim3((unsigned)(a.B * a.Hh)), dim3(64), 0, a.stream, a);
+  else
+    hipLaunchKernelGGL(sics_head_kernel, dim3((unsigned)(a.B * a.Hh)), dim3(64), 0, a.stream, a);
   return hipGetLastError();
 }
 

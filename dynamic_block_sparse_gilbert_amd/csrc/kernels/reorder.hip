@@ -300,6 +300,27 @@ __global__ __launch_bounds__(kThreads) void inverse_rows_kernel(
   }
 }
 
+// x[b, perm[i], h, :] = y[b, h, i, :] for i < N, float32 rows to float32 (exact copy).
+template <int D>
+__global__ __launch_bounds__(kThreads) void inverse_rows_f32_kernel(
+    const float* __restrict__ y, float* __restrict__ x, int64_t sb, int64_t sn, int64_t sh,
+    const int32_t* __restrict__ perm, int perm_h_stride, int Hh, int N, int Npad) {
+  constexpr int kChunks = D / 4;
+  constexpr int kRowsPerPass = kThreads / kChunks;
+  constexpr int kRowsPerBlock = 64;
+  const int h = blockIdx.y, bi = blockIdx.z;
+  const int c = threadIdx.x % kChunks;
+  const int64_t ybase = ((int64_t)bi * Hh + h) * Npad;
+  const int32_t* ph = perm + (int64_t)h * perm_h_stride;
+#pragma unroll
+  for (int pass = 0; pass < kRowsPerBlock / kRowsPerPass; ++pass) {
+    const int i = blockIdx.x * kRowsPerBlock + pass * kRowsPerPass + threadIdx.x / kChunks;
+    if (i >= N) break;
+    const float4 v = *reinterpret_cast<const float4*>(y + (ybase + i) * D + 4 * c);
+    *reinterpret_cast<float4*>(x + bi * sb + (int64_t)clamp_tok(ph[i], N) * sn + (int64_t)h * sh + 4 * c) = v;
+  }
+}
+
 // Global K tokens: k_g[b, h, g, :] = mean of rows g*n .. g*n+r-1 (rows layout).
 template <int D>
 __global__ __launch_bounds__(kThreads) void meanpool_k_kernel(
@@ -414,7 +435,11 @@ hipError_t dispatch_reorder_d(const ReorderArgs& a) {
 template <int D>
 hipError_t dispatch_inverse_d(const ReorderArgs& a) {
   dim3 grid((a.Npad + 63) / 64, a.Hh, a.B);
-  if (a.x_f32) {
+  if (a.y_f32) {
+    hipLaunchKernelGGL((inverse_rows_f32_kernel<D>), grid, dim3(kThreads), 0, a.stream,
+                       (const float*)a.y, (float*)a.x_out, a.sb, a.sn, a.sh, a.perm,
+                       a.perm_h_stride, a.Hh, a.N, a.Npad);
+  } else if (a.x_f32) {
     hipLaunchKernelGGL((inverse_rows_kernel<float, D>), grid, dim3(kThreads), 0, a.stream,
                        (const __bf16*)a.y, (float*)a.x_out, a.sb, a.sn, a.sh, a.perm,
                        a.perm_h_stride, a.Hh, a.N, a.Npad);

@@ -119,13 +119,19 @@ struct PooledArgs {
   hipStream_t stream;
 };
 
-// SICS of every block and the per-head aggregation score.
+// SICS of every block and the per-head aggregation score; with n_cand > 0,
+// of every candidate permutation (and of K too when tensors == 2) and the
+// per-head choice.
 struct SicsArgs {
   const void* q_r;
   TokIO tok;
-  float* sics;              // [B, Hh, nb]
-  float* as;                // [B, Hh]
+  float* sics;              // [B, Hh, nb]; candidates: [n_cand, tensors, B, Hh, nb]
+  float* as;                // [B, Hh]; candidates: [n_cand, B, Hh]
   int B, Hh, N, Npad, d, b, nb;
+  const void* k;            // candidates: K in token order (tok's strides and type), when tensors == 2
+  const int32_t* perms;     // candidates: [n_cand, N]
+  int n_cand, tensors;
+  int32_t* choice;          // candidates: [B, Hh]
   hipStream_t stream;
 };
 
@@ -187,6 +193,9 @@ size_t pooled_workspace_bytes(int B, int Hh, int nb, int d);
 hipError_t launch_pooled(const PooledArgs& a);
 hipError_t launch_sics(const SicsArgs& a);
 hipError_t launch_attn_fwd(const AttnArgs& a);
+// Float32 operands (reordered rows; v_t holds V as rows): VALU kernels.
+hipError_t launch_estimate_f32(const EstimateArgs& a);
+hipError_t launch_attn_fwd_f32(const AttnArgs& a);
 hipError_t launch_transpose_lists(const TransposeListsArgs& a);
 size_t attn_bwd_workspace_bytes(int B, int Hh, int Npad, int d);
 hipError_t launch_attn_bwd(const AttnBwdArgs& a);

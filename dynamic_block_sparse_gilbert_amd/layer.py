@@ -38,6 +38,7 @@ class LayerSpec:
     cuboids: Optional[Sequence[Tuple[int, int, int]]] = None   # per head (cuboid_per_head)
     n_pool: int = 0                     # ASA_G window; 0 = plain ASA
     batch: int = 1
+    dtype: str = "bf16"                 # "bf16", or "fp32": float32 operands and arithmetic throughout
 
     @property
     def N(self) -> int:
@@ -69,10 +70,50 @@ def build_perm(spec: LayerSpec) -> np.ndarray:
     raise ValueError(spec.order)
 
 
+class SicsChooser:
+    """SPADE's runtime scheme choice over candidate cuboid shapes of one latent grid: the
+    candidates' token orders are built by the library and uploaded once, and each choose() is one
+    dbs_sics_choose call (SICS aggregation score of Q and, when given, K for every candidate, then
+    the per-head argmax, all on the GPU)."""
+
+    def __init__(self, T: int, H: int, W: int, candidates: Sequence[Tuple[int, int, int]], b: int,
+                 prefix: int = 0, device="cuda"):
+        self.candidates = [tuple(int(x) for x in c) for c in candidates]
+        self.b = b
+        self.N = prefix + T * H * W
+        self.Npad = -(-self.N // b) * b
+        self.host_perms = np.stack([ops.perm_cuboid(T, H, W, *c, prefix=prefix) for c in self.candidates])
+        self.perms = torch.from_numpy(self.host_perms).to(device)
+        self.choice = self.scores = self.block_scores = None
+
+    def choose(self, q: torch.Tensor, k: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """int32 [B, Hh] index of the chosen candidate of every head (left on the device)."""
+        B, _, Hh, _ = q.shape
+        if self.choice is None or self.choice.shape != (B, Hh) or \
+                self.block_scores.shape[1] != (1 if k is None else 2):
+            self.choice = self.scores = self.block_scores = None
+        self.choice, self.scores, self.block_scores = ops.sics_choose(
+            q, k, self.perms, self.Npad, self.b, block_scores=self.block_scores, scores=self.scores,
+            choice=self.choice)
+        return self.choice
+
+    def chosen(self, batch: int = 0):
+        return [self.candidates[int(c)] for c in self.choice[batch].tolist()]
+
+    def per_head_perm(self, batch: int = 0) -> torch.Tensor:
+        """int32 [Hh, N] (host): each head's order under its chosen candidate."""
+        idx = self.choice[batch].cpu().numpy()
+        return torch.from_numpy(np.ascontiguousarray(self.host_perms[idx]))
+
+
 class AsaLayer:
     """Holds the device permutation and the intermediate buffers of one layer shape."""
 
     def __init__(self, spec: LayerSpec, device="cuda", fused: bool = True, overlap: bool = False):
+        if spec.dtype not in ("bf16", "fp32"):
+            raise ValueError(f"dtype {spec.dtype!r}: bf16 or fp32")
+        if spec.dtype == "fp32" and spec.n_pool:
+            raise ValueError("the float32 path takes no ASA_G global tokens")
         """fused: the estimate and the mask in one call (dbs_estimate_mask_tok; P_imp is then not
         written unless mask(keep_p_imp=True)), else dbs_estimate_blocks_tok + dbs_build_mask.
         overlap: reorder V on a second stream (default priority) while the estimate runs, the
@@ -81,15 +122,24 @@ class AsaLayer:
         the two reorders being slower than the one launch and the V copy slowing the estimate)."""
         self.spec = spec
         self.fused = fused
-        self.overlap = overlap and not spec.n_pool
+        self.f32 = spec.dtype == "fp32"
+        self.overlap = overlap and not spec.n_pool and not self.f32
         self._side = torch.cuda.Stream(device=device) if self.overlap else None
         self.device = torch.device(device)
         self.perm = torch.from_numpy(build_perm(spec)).to(self.device)
         s = spec
         B, Hh, Npad, d, nb = s.batch, s.heads, s.Npad, s.d, s.nb
         bf = dict(dtype=torch.bfloat16, device=self.device)
-        self.k_r = torch.empty((B, Hh, Npad, d), **bf)
-        self.v_t = torch.empty((B, Hh, nb, d, s.b), **bf)
+        if self.f32:
+            # float32 rows for Q, K, V and the output (the float32 kernels read V as rows)
+            f4 = dict(dtype=torch.float32, device=self.device)
+            self.q_r = torch.empty((B, Hh, Npad, d), **f4)
+            self.k_r = torch.empty((B, Hh, Npad, d), **f4)
+            self.v_t = torch.empty((B, Hh, Npad, d), **f4)
+            self.o_r = torch.empty((B, Hh, Npad, d), **f4)
+        else:
+            self.k_r = torch.empty((B, Hh, Npad, d), **bf)
+            self.v_t = torch.empty((B, Hh, nb, d, s.b), **bf)
         self.q: Optional[torch.Tensor] = None   # the caller's Q, token order
         self.p_imp = torch.empty((B, Hh, nb, nb), dtype=torch.float32, device=self.device)
         self.ws = torch.empty(max(16, ops.estimate_workspace_bytes(B, Hh, s.N, d, s.b, s.k)),
@@ -105,22 +155,31 @@ class AsaLayer:
             self.k_g = torch.empty((B, Hh, Ngpad, d), **bf)
             self.v_g = torch.empty((B, Hh, Ngpad // s.b, d, s.b), **bf)
 
-    def choose_cuboids_sics(self, q: torch.Tensor, candidates: Sequence[Tuple[int, int, int]]):
-        """Per head, the candidate cuboid with the largest SICS aggregation score on q (SPADE's
-        scheme choice, dbs_sics_tok once per candidate); the layer switches to cuboid_per_head order
-        with those shapes and uploads the new permutation.  q [B, N, Hh, d] token order (the first
-        batch entry decides).  Returns the chosen cuboid of each head."""
+    def choose_cuboids_sics(self, q: torch.Tensor, candidates: Sequence[Tuple[int, int, int]],
+                            k: Optional[torch.Tensor] = None):
+        """Per head, the candidate cuboid with the largest SICS aggregation score of q (and k when
+        given) (SPADE's scheme choice, one dbs_sics_choose call); the layer switches to
+        cuboid_per_head order with those shapes and uploads the new permutation.  q, k
+        [B, N, Hh, d] token order (the first batch entry decides).  Returns the chosen cuboid of
+        each head."""
         s = self.spec
-        choice, _ = ops.choose_cuboids_sics(q, s.T, s.H, s.W, candidates, s.b, prefix=s.prefix)
-        chosen = [tuple(candidates[int(c)]) for c in choice[0].tolist()]
+        ch = SicsChooser(s.T, s.H, s.W, candidates, s.b, prefix=s.prefix, device=self.device)
+        ch.choose(q, k)
+        chosen = ch.chosen(0)
         s.order, s.cuboids = "cuboid_per_head", chosen
-        self.perm = torch.from_numpy(build_perm(s)).to(self.device)
+        self.perm = ch.per_head_perm(0).to(self.device)
         return chosen
 
     def prepare(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> None:
         """Reorder (and pool) K and V and keep Q; q, k, v are [B, N, Hh, d]."""
         s = self.spec
         self.q = q
+        if self.f32:
+            for x, y in ((q, self.q_r), (k, self.k_r), (v, self.v_t)):
+                if x.dtype != torch.float32:
+                    raise TypeError("the float32 layer takes float32 q, k, v")
+                ops.reorder(x, self.perm, s.Npad, s.b, "rows", y=y)
+            return
         if s.n_pool:   # the global tokens in the same launch (two passes when n does not divide b)
             ops.reorder_kv(k, v, self.perm, s.Npad, s.b, k_r=self.k_r, v_t=self.v_t, n_pool=s.n_pool, k_g=self.k_g,
                            v_g=self.v_g)
@@ -139,15 +198,60 @@ class AsaLayer:
     def mask(self, tau: Optional[float] = None, keep_p_imp: bool = False) -> None:
         s = self.spec
         tau = s.tau if tau is None else tau
+        if self.f32:
+            ops.estimate_mask(self.q_r, self.k_r, s.N, s.b, s.k, s.scale, "cumulative", tau, kv_count=self.kv_count,
+                              kv_idx=self.kv_idx, order=self.order, workspace=self.ws,
+                              p_imp=self.p_imp if (keep_p_imp or not self.fused) else None)
+            return
         if self.fused:
             ops.estimate_mask(self.q, self.k_r, s.N, s.b, s.k, s.scale, "cumulative", tau, q_perm=self.perm,
                               kv_count=self.kv_count, kv_idx=self.kv_idx, order=self.order, workspace=self.ws,
                               p_imp=self.p_imp if keep_p_imp else None)
             return
-        ops.estimate_blocks_tok(self.q, self.perm, self.k_r, s.N, s.b, s.k, s.scale, p_imp=self.p_imp,
-                                workspace=self.ws)
+        self.estimate_only()
         ops.build_mask(self.p_imp, tau, kv_count=self.kv_count, kv_idx=self.kv_idx,
                        order=self.order)
+
+    def estimate_only(self) -> torch.Tensor:
+        """The importance estimate alone (P_imp written to self.p_imp), as the unfused path runs it."""
+        s = self.spec
+        if self.f32:
+            return ops.estimate_blocks(self.q_r, self.k_r, s.N, s.b, s.k, s.scale, p_imp=self.p_imp, workspace=self.ws)
+        return ops.estimate_blocks_tok(self.q, self.perm, self.k_r, s.N, s.b, s.k, s.scale, p_imp=self.p_imp,
+                                       workspace=self.ws)
+
+    def block_sparsity(self) -> float:
+        """1 - (kept blocks) / (B * Hh * nb^2) of the current kv_count (one device-to-host copy)."""
+        s = self.spec
+        kept = int(self.kv_count.sum(dtype=torch.int64).item())
+        return 1.0 - kept / float(s.batch * s.heads * s.nb * s.nb)
+
+    def tune_tau(self, target: float, iters: int = 40) -> Tuple[float, float]:
+        """The largest float32 tau in (0, 1] whose cumulative mask on the current P_imp has block
+        sparsity >= target, found by bisection with dbs_build_mask (the kept count never falls as
+        tau grows, so the sparsity is monotone in tau).  P_imp must be current: call
+        mask(keep_p_imp=True) (or forward(..., keep_p_imp=True)) first.  Leaves the mask of the
+        returned tau in kv_count / kv_idx / order.  Returns (tau, its block sparsity)."""
+        if not 0.0 < target < 1.0:
+            raise ValueError("target sparsity must lie in (0, 1)")
+        f32 = np.float32
+        lo, hi = f32(2.0 ** -24), f32(1.0)
+
+        def sparsity_at(t):
+            ops.build_mask(self.p_imp, float(t), kv_count=self.kv_count, kv_idx=self.kv_idx, order=self.order)
+            return self.block_sparsity()
+
+        if sparsity_at(lo) < target:
+            raise ValueError(f"no tau reaches sparsity {target}: the argmax-only mask has {sparsity_at(lo):.4f}")
+        for _ in range(iters):
+            mid = f32((float(lo) + float(hi)) / 2.0)
+            if mid == lo or mid == hi:
+                break
+            if sparsity_at(mid) >= target:
+                lo = mid
+            else:
+                hi = mid
+        return float(lo), sparsity_at(lo)
 
     def wait_v(self) -> None:
         """Make the current stream wait for prepare()'s V reorder (side stream); needed before any
@@ -157,6 +261,12 @@ class AsaLayer:
 
     def attend(self, out: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16) -> torch.Tensor:
         s = self.spec
+        if self.f32:
+            ops.sparse_attn_fwd(self.q_r, self.k_r, self.v_t, s.N, s.b, s.scale, self.kv_count, self.kv_idx,
+                                o_r=self.o_r, order=self.order)
+            if out is None:
+                out = torch.empty((s.batch, s.N, s.heads, s.d), dtype=torch.float32, device=self.device)
+            return ops.inverse_reorder(self.o_r, self.perm, s.N, out=out)
         self.wait_v()
         out, _ = ops.sparse_attn_fwd_tok(self.q, self.perm, self.k_r, self.v_t, s.N, s.b, s.scale, self.kv_count,
                                          self.kv_idx, self.k_g, self.v_g, self.Ng, s.n_pool, out=out,

@@ -30,6 +30,38 @@ def _dev(*ts):
             raise ValueError("device tensors required")
 
 
+def _i32(t: Optional[torch.Tensor], name: str, last: Optional[int] = None, lead: Optional[tuple] = None) -> None:
+    """An index operand must be a contiguous int32 tensor (an int64 tensor would be read as pairs of
+    int32 words), with the given trailing dimension and leading dimensions when stated."""
+    if t is None:
+        return
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be torch.int32 (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if last is not None and (t.dim() == 0 or t.shape[-1] != last):
+        raise ValueError(f"{name} must have trailing dimension {last} (got shape {tuple(t.shape)})")
+    if lead is not None and tuple(t.shape[:-1]) != tuple(lead):
+        raise ValueError(f"{name} must have shape {tuple(lead) + (last,)} (got {tuple(t.shape)})")
+
+
+def _perm(perm: torch.Tensor, N: int, Hh: int, name: str = "perm") -> int:
+    """Checks a device permutation [N] or [Hh, N]; returns perm_per_head."""
+    _i32(perm, name, N)
+    if perm.dim() == 2:
+        if perm.shape[0] != Hh:
+            raise ValueError(f"{name} has {perm.shape[0]} rows for {Hh} heads")
+        return 1
+    if perm.dim() != 1:
+        raise ValueError(f"{name} must be [N] or [Hh, N]")
+    return 0
+
+
+def _lists(kv_count: Optional[torch.Tensor], kv_idx: Optional[torch.Tensor], B: int, Hh: int, nb: int) -> None:
+    _i32(kv_count, "kv_count", nb, (B, Hh))
+    _i32(kv_idx, "kv_idx", nb, (B, Hh, nb))
+
+
 def _stream() -> C.c_void_p:
     return C.c_void_p(torch.cuda.current_stream().cuda_stream)
 
@@ -83,7 +115,7 @@ def reorder(x: torch.Tensor, perm: torch.Tensor, Npad: int, b: int, layout: str 
     if y is None:
         shape = (B, Hh, Npad, d) if lay == DBS_ROWS else (B, Hh, Npad // b, d, b)
         y = torch.empty(shape, dtype=out_dtype, device=x.device)
-    per_head = 1 if perm.dim() == 2 else 0
+    per_head = _perm(perm, N, Hh)
     check("dbs_reorder", lib().dbs_reorder(
         _p(x), _dt(x), x.stride(0), x.stride(1), x.stride(2), _p(y), _dt(y), lay, _p(perm), per_head,
         B, Hh, N, Npad, d, b, _stream()))
@@ -110,7 +142,7 @@ def reorder_kv(k: torch.Tensor, v: torch.Tensor, perm: torch.Tensor, Npad: int, 
         raise ValueError("k_r / v_t have the wrong shape")
     if k_r.dtype != torch.bfloat16 or v_t.dtype != torch.bfloat16 or not (k_r.is_contiguous() and v_t.is_contiguous()):
         raise ValueError("k_r and v_t must be contiguous bf16")
-    per_head = 1 if perm.dim() == 2 else 0
+    per_head = _perm(perm, N, Hh)
     if n_pool:
         Ng = -(-N // n_pool)
         Ngpad = -(-Ng // b) * b
@@ -137,7 +169,7 @@ def inverse_reorder(y: torch.Tensor, perm: torch.Tensor, N: int,
         out = torch.empty((B, N, Hh, d), dtype=out_dtype, device=y.device)
     if out.stride(3) != 1:
         raise ValueError("the d axis of out must be contiguous")
-    per_head = 1 if perm.dim() == 2 else 0
+    per_head = _perm(perm, N, Hh)
     check("dbs_inverse_reorder", lib().dbs_inverse_reorder(
         _p(y), _dt(y), _p(out), _dt(out), out.stride(0), out.stride(1), out.stride(2), _p(perm), per_head,
         B, Hh, N, Npad, d, _stream()))
@@ -155,6 +187,8 @@ def estimate_blocks(q_r: torch.Tensor, k_r: torch.Tensor, N: int, b: int, k: int
     _dev(q_r, k_r, p_imp, workspace)
     B, Hh, Npad, d = q_r.shape
     nb = Npad // b
+    if q_r.dtype != k_r.dtype:
+        raise TypeError("q_r and k_r must have one dtype (it selects the compute path)")
     if p_imp is None:
         p_imp = torch.empty((B, Hh, nb, nb), dtype=torch.float32, device=q_r.device)
     need = estimate_workspace_bytes(B, Hh, N, d, b, k)
@@ -181,7 +215,7 @@ def estimate_blocks_tok(q: torch.Tensor, perm: torch.Tensor, k_r: torch.Tensor, 
     need = estimate_workspace_bytes(B, Hh, N, d, b, k)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=k_r.device)
-    per_head = 1 if perm.dim() == 2 else 0
+    per_head = _perm(perm, N, Hh)
     check("dbs_estimate_blocks_tok", lib().dbs_estimate_blocks_tok(
         _p(q), _dt(q), q.stride(0), q.stride(1), q.stride(2), _p(perm), per_head, _p(k_r),
         B, Hh, N, Npad, d, b, k, float(scale), _p(p_imp), _p(workspace),
@@ -198,6 +232,8 @@ def build_mask(p_imp: torch.Tensor, tau: float, kv_count: Optional[torch.Tensor]
     fourth element."""
     _dev(p_imp, kv_count, kv_idx, mask, order)
     B, Hh, nb, _ = p_imp.shape
+    _lists(kv_count, kv_idx, B, Hh, nb)
+    _i32(order, "order", B * Hh * nb, ())
     if kv_count is None:
         kv_count = torch.empty((B, Hh, nb), dtype=torch.int32, device=p_imp.device)
     if kv_idx is None:
@@ -213,16 +249,20 @@ def build_mask(p_imp: torch.Tensor, tau: float, kv_count: Optional[torch.Tensor]
     return kv_count, kv_idx, mask
 
 
-MASK_RULES = {"cumulative": 0, "topk": 1, "stat": 2}
+MASK_RULES = {"cumulative": 0, "topk": 1, "stat": 2, "stat_k": 3}
+
+
+def normal_quantile(p: float) -> float:
+    """The library's standard normal quantile U(p) (dbs_normal_quantile)."""
+    return float(lib().dbs_normal_quantile(float(p)))
 
 
 def stat_quantile(k: float, n: int) -> float:
-    """u = U(1 - k/n), the standard normal quantile of the statistical rule (k of n blocks kept on
-    normally spread scores)."""
-    from statistics import NormalDist
+    """u = U(1 - k/n), the quantile the statistical rule uses to keep about k of n blocks on normally
+    spread scores, from the library (rule 'stat_k' lets the library compute it itself)."""
     if not 0 < k < n:
         raise ValueError("need 0 < k < n")
-    return NormalDist().inv_cdf(1.0 - k / n)
+    return normal_quantile(1.0 - k / n)
 
 
 def build_mask_rule(p_imp: torch.Tensor, rule: str, param: float, kv_count: Optional[torch.Tensor] = None,
@@ -232,6 +272,8 @@ def build_mask_rule(p_imp: torch.Tensor, rule: str, param: float, kv_count: Opti
     (param = u, see stat_quantile).  Returns (kv_count, kv_idx, mask or None)."""
     _dev(p_imp, kv_count, kv_idx, order)
     B, Hh, nb, _ = p_imp.shape
+    _lists(kv_count, kv_idx, B, Hh, nb)
+    _i32(order, "order", B * Hh * nb, ())
     if kv_count is None:
         kv_count = torch.empty((B, Hh, nb), dtype=torch.int32, device=p_imp.device)
     if kv_idx is None:
@@ -256,6 +298,8 @@ def estimate_mask(q_r: torch.Tensor, k_r: torch.Tensor, N: int, b: int, k: int, 
     B, Hh, Npad, d = k_r.shape
     nb = Npad // b
     dv = k_r.device
+    _lists(kv_count, kv_idx, B, Hh, nb)
+    _i32(order, "order", B * Hh * nb, ())
     if kv_count is None:
         kv_count = torch.empty((B, Hh, nb), dtype=torch.int32, device=dv)
     if kv_idx is None:
@@ -270,11 +314,13 @@ def estimate_mask(q_r: torch.Tensor, k_r: torch.Tensor, N: int, b: int, k: int, 
     tail = (b, k, float(scale), MASK_RULES[rule], float(param), _p(p_imp), _p(kv_count), _p(kv_idx), _p(mask),
             _p(order), _p(workspace), wsb, _stream())
     if q_perm is None:
+        if q_r.dtype != k_r.dtype:
+            raise TypeError("q_r and k_r must have one dtype (it selects the compute path)")
         check("dbs_estimate_mask", lib().dbs_estimate_mask(_p(q_r), _p(k_r), _dt(q_r), B, Hh, N, Npad, d, *tail))
     else:
         if q_r.stride(3) != 1:
             raise ValueError("the d axis of q must be contiguous")
-        per_head = 1 if q_perm.dim() == 2 else 0
+        per_head = _perm(q_perm, N, Hh, "q_perm")
         check("dbs_estimate_mask_tok", lib().dbs_estimate_mask_tok(
             _p(q_r), _dt(q_r), q_r.stride(0), q_r.stride(1), q_r.stride(2), _p(q_perm), per_head, _p(k_r),
             B, Hh, N, Npad, d, *tail))
@@ -297,7 +343,8 @@ def query_prune(q: torch.Tensor, perm: torch.Tensor, anchor: torch.Tensor, Npad:
         rowsel = torch.empty((B, Hh, nb, b), dtype=torch.int32, device=dv)
     if keep is None:
         keep = torch.empty((B, Hh, Npad), dtype=torch.uint8, device=dv)
-    per_head = 1 if perm.dim() == 2 else 0
+    per_head = _perm(perm, N, Hh)
+    _perm(anchor, N, Hh, "anchor")
     check("dbs_query_prune", lib().dbs_query_prune(
         _p(q), _dt(q), q.stride(0), q.stride(1), q.stride(2), _p(perm), per_head, _p(anchor), B, Hh, N, Npad, d, b,
         float(r), _p(q_count), _p(rowsel), _p(keep), _stream()))
@@ -321,7 +368,12 @@ def sparse_attn_fwd_pruned_tok(q: torch.Tensor, perm: torch.Tensor, k_r: torch.T
         raise ValueError("the d axis of out must be contiguous")
     if want_lse and lse is None:
         lse = torch.empty((B, Hh, Npad), dtype=torch.float32, device=k_r.device)
-    per_head = 1 if perm.dim() == 2 else 0
+    per_head = _perm(perm, N, Hh)
+    _perm(anchor, N, Hh, "anchor")
+    _lists(kv_count, kv_idx, B, Hh, Npad // b)
+    _i32(order, "order", B * Hh * (Npad // b), ())
+    _i32(q_count, "q_count", Npad // b, (B, Hh))
+    _i32(rowsel, "rowsel", b, (B, Hh, Npad // b))
     check("dbs_sparse_attn_fwd_pruned_tok", lib().dbs_sparse_attn_fwd_pruned_tok(
         _p(q), _dt(q), q.stride(0), q.stride(1), q.stride(2), _p(perm), per_head, _p(k_r), _p(v_t),
         B, Hh, N, Npad, d, b, float(scale), _p(kv_count), _p(kv_idx), _p(order), _p(q_count), _p(rowsel),
@@ -346,7 +398,7 @@ def estimate_pooled(q: torch.Tensor, perm: torch.Tensor, k_r: torch.Tensor, N: i
     need = lib().dbs_pooled_workspace_bytes(B, Hh, N, d, b)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=k_r.device)
-    per_head = 1 if perm.dim() == 2 else 0
+    per_head = _perm(perm, N, Hh)
     check("dbs_estimate_pooled_tok", lib().dbs_estimate_pooled_tok(
         _p(q), _dt(q), q.stride(0), q.stride(1), q.stride(2), _p(perm), per_head, _p(k_r), B, Hh, N, Npad, d, b,
         POOL_KINDS[kind], _p(p_imp), _p(workspace), workspace.numel() * workspace.element_size(), _stream()))
@@ -363,25 +415,45 @@ def sics(q: torch.Tensor, perm: torch.Tensor, Npad: int, b: int):
     nb = Npad // b
     out = torch.empty((B, Hh, nb), dtype=torch.float32, device=q.device)
     agg = torch.empty((B, Hh), dtype=torch.float32, device=q.device)
-    per_head = 1 if perm.dim() == 2 else 0
+    per_head = _perm(perm, N, Hh)
     check("dbs_sics_tok", lib().dbs_sics_tok(
         _p(q), _dt(q), q.stride(0), q.stride(1), q.stride(2), _p(perm), per_head, B, Hh, N, Npad, d, b, _p(out),
         _p(agg), _stream()))
     return out, agg
 
 
-def choose_cuboids_sics(q: torch.Tensor, T: int, H: int, W: int, candidates, b: int, prefix: int = 0):
-    """Per head, the candidate cuboid (ct, ch, cw) whose cuboid order has the largest SICS
-    aggregation score (one dbs_sics_tok call per candidate).  Returns (index per head, scores
-    [len(candidates), B, Hh])."""
-    N = prefix + T * H * W
-    Npad = -(-N // b) * b
-    scores = []
-    for c in candidates:
-        perm = torch.from_numpy(perm_cuboid(T, H, W, *c, prefix=prefix)).to(q.device)
-        scores.append(sics(q, perm, Npad, b)[1])
-    s = torch.stack(scores)
-    return s.argmax(dim=0), s
+def sics_choose(q: torch.Tensor, k: Optional[torch.Tensor], perms: torch.Tensor, Npad: int, b: int,
+                block_scores: Optional[torch.Tensor] = None, scores: Optional[torch.Tensor] = None,
+                choice: Optional[torch.Tensor] = None):
+    """SPADE scheme choice in one call (dbs_sics_choose): q, k [B, N, Hh, d] token order (k may be
+    None: Q alone), perms int32 [n_cand, N] candidate orders.  Returns (choice int32 [B, Hh],
+    scores float32 [n_cand, B, Hh], block_scores float32 [n_cand, T, B, Hh, nb])."""
+    _dev(q, k, perms, block_scores, scores, choice)
+    if q.stride(3) != 1:
+        raise ValueError("the d axis of q must be contiguous")
+    B, N, Hh, d = q.shape
+    if k is not None and (k.shape != q.shape or k.stride() != q.stride() or k.dtype != q.dtype):
+        raise ValueError("k must have q's shape, strides and dtype")
+    if perms.dim() != 2:
+        raise ValueError("perms must be [n_cand, N]")
+    _i32(perms, "perms", N)
+    nc = perms.shape[0]
+    nb = Npad // b
+    T = 1 if k is None else 2
+    dv = q.device
+    if block_scores is None:
+        block_scores = torch.empty((nc, T, B, Hh, nb), dtype=torch.float32, device=dv)
+    if scores is None:
+        scores = torch.empty((nc, B, Hh), dtype=torch.float32, device=dv)
+    if choice is None:
+        choice = torch.empty((B, Hh), dtype=torch.int32, device=dv)
+    if block_scores.numel() < nc * T * B * Hh * nb or scores.numel() < nc * B * Hh or choice.numel() < B * Hh:
+        raise ValueError("output buffers too small")
+    _i32(choice, "choice")
+    check("dbs_sics_choose", lib().dbs_sics_choose(
+        _p(q), _p(k), _dt(q), q.stride(0), q.stride(1), q.stride(2), _p(perms), nc, B, Hh, N, Npad, d, b,
+        _p(block_scores), _p(scores), _p(choice), _stream()))
+    return choice, scores, block_scores
 
 
 def meanpool_kv(k_r: torch.Tensor, v_t: torch.Tensor, N: int, b: int, n: int,
@@ -411,6 +483,11 @@ def sparse_attn_fwd(q_r: torch.Tensor, k_r: torch.Tensor, v_t: torch.Tensor, N: 
     work order from build_mask (None: index order)."""
     _dev(q_r, k_r, v_t, kv_count, kv_idx, k_g, v_g, o_r, lse, order)
     B, Hh, Npad, d = q_r.shape
+    _lists(kv_count, kv_idx, B, Hh, Npad // b)
+    _i32(order, "order", B * Hh * (Npad // b), ())
+    if q_r.dtype == torch.float32 and (k_r.dtype != torch.float32 or v_t.dtype != torch.float32
+                                       or v_t.shape != q_r.shape):
+        raise TypeError("float32 attention takes float32 rows for q_r, k_r and v (v as rows [B, Hh, Npad, d])")
     if o_r is None:
         o_r = torch.empty_like(q_r)
     if want_lse and lse is None:
@@ -439,7 +516,9 @@ def sparse_attn_fwd_tok(q: torch.Tensor, perm: torch.Tensor, k_r: torch.Tensor, 
         raise ValueError("the d axis of out must be contiguous")
     if want_lse and lse is None:
         lse = torch.empty((B, Hh, Npad), dtype=torch.float32, device=k_r.device)
-    per_head = 1 if perm.dim() == 2 else 0
+    per_head = _perm(perm, N, Hh)
+    _lists(kv_count, kv_idx, B, Hh, Npad // b)
+    _i32(order, "order", B * Hh * (Npad // b), ())
     check("dbs_sparse_attn_fwd_tok", lib().dbs_sparse_attn_fwd_tok(
         _p(q), _dt(q), q.stride(0), q.stride(1), q.stride(2), _p(perm), per_head, _p(k_r), _p(v_t),
         B, Hh, N, Npad, d, b, float(scale), _p(kv_count), _p(kv_idx), _p(order), _p(k_g), _p(v_g),
@@ -456,6 +535,7 @@ def transpose_lists(kv_count: torch.Tensor, kv_idx: torch.Tensor):
     the query blocks whose kept list holds J (entries past kvT_count unspecified)."""
     _dev(kv_count, kv_idx)
     B, Hh, nb = kv_count.shape
+    _lists(kv_count, kv_idx, B, Hh, nb)
     kvT_count = torch.empty_like(kv_count)
     kvT_idx = torch.empty_like(kv_idx)
     check("dbs_transpose_lists", lib().dbs_transpose_lists(
@@ -476,6 +556,8 @@ def sparse_attn_bwd(q_r: torch.Tensor, k_r: torch.Tensor, v_r: torch.Tensor, o_r
     rows [B, Hh, Npad, d] bf16; lse from the forward.  Returns (dq, dk, dv) float32 rows."""
     _dev(q_r, k_r, v_r, o_r, do_r, lse, kv_count, kv_idx, kvT_count, kvT_idx, workspace)
     B, Hh, Npad, d = q_r.shape
+    _lists(kv_count, kv_idx, B, Hh, Npad // b)
+    _lists(kvT_count, kvT_idx, B, Hh, Npad // b)
     for t in (k_r, v_r, o_r, do_r):
         if t.shape != q_r.shape or t.dtype != torch.bfloat16 or not t.is_contiguous():
             raise ValueError("q_r, k_r, v_r, o_r, do_r must be contiguous bf16 rows of one shape")

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define DBS_ABI_VERSION 10
+#define DBS_ABI_VERSION 11
 
 typedef enum {
   DBS_OK = 0,
@@ -158,8 +158,9 @@ dbs_status dbs_reorder_kv(const void* k, const void* v, dbs_dtype x_dt,
 /* Inverse of dbs_reorder for the attention output:
  *   x[b, perm_h[i], h, :] = y[b, h, i, :]  for i < N.
  * y: DBS_ROWS, element type y_dt; x: element type x_dt with strides
- * (sb, sn, sh).  DBS_BF16 -> DBS_FP32 widens exactly.  perm as for
- * dbs_reorder (entries clamped into [0, N)). */
+ * (sb, sn, sh).  DBS_BF16 -> DBS_FP32 widens exactly and DBS_FP32 ->
+ * DBS_FP32 copies (DBS_FP32 -> DBS_BF16 is not offered: UNSUPPORTED).  perm
+ * as for dbs_reorder (entries clamped into [0, N)). */
 dbs_status dbs_inverse_reorder(const void* y, dbs_dtype y_dt, void* x, dbs_dtype x_dt,
                                int64_t sb, int64_t sn, int64_t sh,
                                const int32_t* perm, int perm_per_head,
@@ -179,7 +180,10 @@ size_t dbs_estimate_workspace_bytes(int B, int Hh, int N, int d, int b, int k);
  * alike.  P_approx = row-softmax(Q_s K_s^T * scale) over all sampled keys of
  * the (batch, head); p_imp[b, h, I, J] = max of P_approx over (samples of I) x
  * (samples of J), float32, [B, Hh, nb, nb].
- * q_r, k_r: DBS_ROWS, type dt (DBS_BF16 only).  k: a power of two, 1..b.
+ * q_r, k_r: DBS_ROWS, type dt.  DBS_BF16: bf16 products with float32
+ * accumulation and a float32 softmax (k a power of two, 1..b).  DBS_FP32:
+ * float32 operands and float32 arithmetic throughout (any k in 1..b), for
+ * workloads stored in float32.
  * workspace: device, >= dbs_estimate_workspace_bytes(...) bytes; its contents
  * on entry do not matter.  Q and K must be finite (a NaN input gives an
  * undefined result).  Errors: UNSUPPORTED for d, b, k or dt outside the
@@ -237,12 +241,20 @@ dbs_status dbs_build_mask(const float* p_imp, int B, int Hh, int nb, float tau,
  *                        P_imp >= p is kept, and at least the largest one.
  *                        u = U(1 - k/n), the standard normal quantile, keeps
  *                        about k of n blocks on normally spread scores.
+ *   DBS_RULE_STAT_K      param = k, 0 < k < nb: DBS_RULE_STAT with
+ *                        u = dbs_normal_quantile(1 - k/nb) computed here.
  * Rows holding a value outside [0, 1] or NaN keep every block.  Output as
  * for dbs_build_mask.  INVALID_ARG for an unknown rule or a bad param. */
-typedef enum { DBS_RULE_CUMULATIVE = 0, DBS_RULE_TOPK = 1, DBS_RULE_STAT = 2 } dbs_mask_rule;
+typedef enum { DBS_RULE_CUMULATIVE = 0, DBS_RULE_TOPK = 1, DBS_RULE_STAT = 2, DBS_RULE_STAT_K = 3 } dbs_mask_rule;
 dbs_status dbs_build_mask_rule(const float* p_imp, int B, int Hh, int nb, int rule, double param,
                                int32_t* kv_count, int32_t* kv_idx, uint8_t* mask, int32_t* order,
                                hipStream_t stream);
+
+/* The standard normal quantile U(p) (inverse of the normal distribution
+ * function) on the host, as the statistical rule uses it: Wichura's algorithm
+ * AS 241 (Applied Statistics 37, 1988), about 16 significant digits.
+ * p in (0, 1); U(0) = -inf, U(1) = +inf, NaN outside [0, 1]. */
+double dbs_normal_quantile(double p);
 
 /* Estimation and selection in one pass over the estimator's intermediate
  * results (the fusion of the importance estimate with the mask builder that
@@ -252,7 +264,8 @@ dbs_status dbs_build_mask_rule(const float* p_imp, int B, int Hh, int nb, int ru
  * selection.  p_imp (nullable): when given, P_imp is written as well, equal
  * to dbs_estimate_blocks' output.  Inputs, workspace and limits as for
  * dbs_estimate_blocks, outputs and rules as for dbs_build_mask_rule
- * (nb <= 4096); the errors of both. */
+ * (nb <= 4096); the errors of both.  With dt = DBS_FP32 the estimate and the
+ * selection are two launches, P_imp held in p_imp or else in the workspace. */
 dbs_status dbs_estimate_mask(const void* q_r, const void* k_r, dbs_dtype dt,
                              int B, int Hh, int N, int Npad, int d, int b, int k, float scale,
                              int rule, double param, float* p_imp,
@@ -334,6 +347,26 @@ dbs_status dbs_sics_tok(const void* q, dbs_dtype q_dt, int64_t sb, int64_t sn, i
                         const int32_t* perm, int perm_per_head, int B, int Hh, int N, int Npad, int d, int b,
                         float* sics, float* as_out, hipStream_t stream);
 
+/* The SPADE notes' scheme choice (runtime scheme generation) over n_cand
+ * candidate token orders in one call.  The notes compute the aggregation
+ * score of Query and of Key for every candidate; read here as the per-head
+ * score AS(Q | c) + AS(K | c), each the sum over the blocks of
+ * || sum of the block's unit-normalised rows ||^2 as in dbs_sics_tok.
+ * q, k: token order [B, N, Hh, d], type dt (bf16, or float32 rounded to
+ *    bf16), element strides sb, sn, sh (d contiguous); k nullable (then Q
+ *    alone is scored).
+ * perms: device int32 [n_cand, N], candidate c's order perms[c] (shared by
+ *    every head), e.g. dbs_perm_cuboid of candidate block shapes; 1 <= n_cand
+ *    <= 64.
+ * block_scores: device float32 [n_cand, T, B, Hh, nb] (T = 2 with k, else 1),
+ *    every block's score; scores: float32 [n_cand, B, Hh], the aggregation
+ *    scores (blocks summed in a fixed order); choice: int32 [B, Hh], the
+ *    candidate with the largest score, the smallest index among equal ones.
+ * Errors as for dbs_sics_tok, INVALID_ARG for n_cand. */
+dbs_status dbs_sics_choose(const void* q, const void* k, dbs_dtype dt, int64_t sb, int64_t sn, int64_t sh,
+                           const int32_t* perms, int n_cand, int B, int Hh, int N, int Npad, int d, int b,
+                           float* block_scores, float* scores, int32_t* choice, hipStream_t stream);
+
 /* ASA_G global tokens (Video-BLADE "Step 2.2 (2)"; BLADE notes key design 2):
  * mean of each window of n consecutive reordered tokens,
  *   k_g[b, h, g, :] = mean(k_r[b, h, g*n .. g*n + r_g - 1, :]),
@@ -367,9 +400,12 @@ dbs_status dbs_reorder_kv_pool(const void* k, const void* v, dbs_dtype x_dt, int
  * Scores and the softmax are float32; the probabilities are rounded to bf16
  * for the P*V product (float32 accumulation).  Rows with no key at all get
  * O = 0 and lse = -inf.
- * q_r, k_r: DBS_ROWS bf16; v_r: DBS_TILES_T bf16; k_g, v_g as written by
- * dbs_meanpool_kv.  o_r: DBS_ROWS bf16, rows >= N untouched.  lse (nullable):
- * float32 [B, Hh, Npad], natural-log normaliser of each row < N.
+ * dt = DBS_BF16: q_r, k_r DBS_ROWS bf16; v_r DBS_TILES_T bf16; k_g, v_g as
+ * written by dbs_meanpool_kv; o_r DBS_ROWS bf16, rows >= N untouched.
+ * dt = DBS_FP32 (workloads stored in float32): q_r, k_r, v_r and o_r all
+ * DBS_ROWS float32, every product and the softmax in float32 (P is not
+ * rounded); no global tokens (k_g, v_g must be NULL: UNSUPPORTED otherwise).
+ * lse (nullable): float32 [B, Hh, Npad], natural-log normaliser of each row < N.
  * kv_count is clamped to [0, nb] and kv_idx entries outside [0, nb) are
  * skipped, so malformed lists cannot read outside the K/V buffers.
  * order (nullable): the work order written by dbs_build_mask for the same

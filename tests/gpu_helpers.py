@@ -62,3 +62,20 @@ def tiles_to_rows(yt: np.ndarray) -> np.ndarray:
     B, Hh, nt, d, b = yt.shape
     cols = tile_col(np.arange(b))
     return yt[..., cols].transpose(0, 1, 2, 4, 3).reshape(B, Hh, nt * b, d)
+
+
+class Guarded:
+    """A device buffer with canary regions before and after it: `view` is the tensor the call
+    writes, `intact()` says whether every canary element still holds its fill value."""
+
+    def __init__(self, shape, dtype, fill=-12345.0, pad=4096, device="cuda"):
+        n = int(np.prod(shape))
+        self.pad = pad
+        self.fill = fill
+        # the view starts 4096 elements in, so 16-byte alignment is kept for every element size
+        self.base = torch.full((pad + n + pad,), fill, dtype=dtype, device=device)
+        self.view = self.base[pad:pad + n].view(*shape)
+
+    def intact(self) -> bool:
+        f = torch.tensor(self.fill, dtype=self.base.dtype, device=self.base.device)
+        return bool((self.base[:self.pad] == f).all().item()) and bool((self.base[-self.pad:] == f).all().item())

@@ -37,7 +37,7 @@ def test_all_declared_symbols_exported(dbs):
     for n in names:
         assert hasattr(h, n), n
     assert set(names) == set(L.SIGNATURES), set(names) ^ set(L.SIGNATURES)
-    assert L.lib().dbs_abi_version() == 10
+    assert L.lib().dbs_abi_version() == 11
 
 
 @pytest.mark.parametrize("T,H,W", list(itertools.product(range(1, 7), repeat=3)))
@@ -138,7 +138,10 @@ def test_estimate_validation(dbs):
             a[names.index(n)] = v
         return f(*a)
     assert call(q=0) == -1
-    assert call(dt=1) == -2
+    assert call(dt=2) == -1               # no such dtype (float32 is a supported path: not launched here)
+    assert call(dt=1, p=MIS) == -3
+    assert call(dt=1, k_=0) == -1
+    assert call(dt=1, wb=ws - 4) == -1
     assert call(k_=6) == -2
     assert call(k_=0) == -1
     assert call(k_=128) == -1
@@ -257,6 +260,8 @@ def test_mask_rule_validation(dbs):
     assert f(A, 1, 1, 16, 2, float("nan"), A, A, None, None, None) == -1  # u not finite
     assert f(A, 1, 1, 4097, 2, 1.0, A, A, None, None, None) == -2         # nb > 4096
     assert f(0, 1, 1, 16, 2, 1.0, A, A, None, None, None) == -1           # NULL
+    assert f(A, 1, 1, 16, 3, 0.0, A, A, None, None, None) == -1           # expected count must be > 0
+    assert f(A, 1, 1, 16, 3, 16.0, A, A, None, None, None) == -1          # ... and < nb
 
 
 @cpu_only
@@ -392,7 +397,9 @@ def test_attn_and_pool_validation(dbs):
         a[i] = v
         return f(*a)
     assert call(0, 0) == -1
-    assert call(3, 1) == -2
+    assert call(3, 2) == -1               # no such dtype
+    a = list(base); a[3] = 1; a[14] = A; a[15] = A; a[16] = 125; a[17] = 8
+    assert f(*a) == -2                    # float32 attention takes no global tokens
     assert call(8, 80) == -2
     assert call(14, A) == -1              # k_g without v_g
     a = list(base); a[14] = A; a[15] = A; a[16] = 126; a[17] = 8
@@ -423,3 +430,59 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="missing"):
         _lib.lib()
+
+
+def test_normal_quantile_matches_scipy(dbs):
+    """The library's AS 241 quantile against scipy's independent implementation (ndtri), from the
+    far tails to the centre, and its limits."""
+    from scipy.special import ndtri
+    ops, _ = dbs
+    ps = np.concatenate([np.logspace(-300, -1, 120), np.linspace(0.01, 0.99, 99), 1 - np.logspace(-15, -1, 40),
+                         [0.5, 0.075, 0.925, 1 - 16 / 1200, 1 - 16 / 256]])
+    got = np.array([ops.normal_quantile(p) for p in ps])
+    ref = ndtri(ps)
+    assert np.all(np.abs(got - ref) <= 1e-14 * np.maximum(np.abs(ref), 1.0))
+    assert ops.normal_quantile(0.5) == 0.0
+    assert ops.normal_quantile(0.0) == -np.inf and ops.normal_quantile(1.0) == np.inf
+    assert np.isnan(ops.normal_quantile(1.5)) and np.isnan(ops.normal_quantile(-0.1))
+    # the symmetry U(1 - p) = -U(p), at dyadic p (1 - p exact)
+    for p in (2.0 ** -20, 2.0 ** -7, 0.25, 0.375):
+        assert abs(ops.normal_quantile(1 - p) + ops.normal_quantile(p)) < 1e-12
+    assert abs(ops.stat_quantile(16, 256) - ndtri(1 - 16 / 256)) < 1e-14
+
+
+def test_wrappers_reject_bad_index_tensors(dbs, monkeypatch):
+    """The binding refuses index operands that the kernels would misread (an int64 permutation is
+    read as pairs of int32 words): wrong dtype, non-contiguous, wrong length.  The device check is
+    bypassed so that the argument checks run on CPU tensors; nothing reaches the library."""
+    import torch
+    ops, _ = dbs
+    monkeypatch.setattr(ops, "_dev", lambda *a: None)
+    called = []
+    monkeypatch.setattr(ops, "lib", lambda: called.append(1))
+    x = torch.zeros((1, 100, 2, 64), dtype=torch.bfloat16)
+    with pytest.raises(TypeError, match="int32"):
+        ops.reorder(x, torch.arange(100), 128, 64)                      # int64 permutation
+    with pytest.raises(ValueError, match="contiguous"):
+        ops.reorder(x, torch.arange(200, dtype=torch.int32)[::2], 128, 64)
+    with pytest.raises(ValueError, match="trailing dimension"):
+        ops.reorder(x, torch.arange(99, dtype=torch.int32), 128, 64)
+    with pytest.raises(ValueError, match="rows"):
+        ops.reorder(x, torch.zeros((3, 100), dtype=torch.int32), 128, 64)   # per-head rows != heads
+    P = torch.zeros((1, 2, 4, 4), dtype=torch.float32)
+    with pytest.raises(TypeError, match="int32"):
+        ops.build_mask(P, 0.9, kv_count=torch.zeros((1, 2, 4), dtype=torch.int64))
+    with pytest.raises(ValueError, match="shape"):
+        ops.build_mask(P, 0.9, kv_idx=torch.zeros((1, 2, 4, 3), dtype=torch.int32))
+    q = torch.zeros((1, 100, 2, 64), dtype=torch.bfloat16)
+    kr = torch.zeros((1, 2, 128, 64), dtype=torch.bfloat16)
+    vt = torch.zeros((1, 2, 2, 64, 64), dtype=torch.bfloat16)
+    cnt = torch.zeros((1, 2, 2), dtype=torch.int32)
+    idx = torch.zeros((1, 2, 2, 2), dtype=torch.int32)
+    with pytest.raises(TypeError, match="int32"):
+        ops.sparse_attn_fwd_tok(q, torch.arange(100), kr, vt, 100, 64, 0.125, cnt, idx)
+    with pytest.raises(TypeError, match="int32"):
+        ops.sparse_attn_fwd_tok(q, torch.arange(100, dtype=torch.int32), kr, vt, 100, 64, 0.125, cnt.long(), idx)
+    with pytest.raises(TypeError, match="int32"):
+        ops.sics_choose(q, None, torch.zeros((2, 100), dtype=torch.int64), 128, 64)
+    assert not called

@@ -92,3 +92,20 @@ def test_cumulative_rule_equals_build_mask():
     b = ops.build_mask_rule(P, "cumulative", 0.9, want_mask=True)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[2], b[2])   # counts and masks (entries past a count are unspecified)
+
+
+@pytest.mark.parametrize("nb", [64, 256, 1200])
+def test_stat_k_equals_stat_with_library_quantile(nb):
+    """DBS_RULE_STAT_K (the library computes u = U(1 - k/nb) itself) gives exactly the lists of
+    DBS_RULE_STAT at that u, and the oracle's rule at scipy's quantile outside ties."""
+    from scipy.special import ndtri
+    say("mask stat_k", nb)
+    ops = _ops()
+    P, rows = _case(nb, "normal", nb + 3)
+    Pd = dev(P)
+    for kk in (1, 16, nb // 3):
+        a = ops.build_mask_rule(Pd, "stat_k", kk, want_mask=True)
+        b = ops.build_mask_rule(Pd, "stat", ops.stat_quantile(kk, nb), want_mask=True)
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], b[0]) and torch.equal(a[2], b[2])
+        _compare(P, "stat", float(ndtri(1 - kk / nb)), rows)

@@ -56,7 +56,8 @@ def test_sics_and_choice(T, H, W, Hh, d, b):
     Npad = -(-N // b) * b
     qd = dev_bf16(q)
     cands = [(1, 8, 8), (4, 4, 4), (2, 4, 8), (1, 4, 16)]
-    choice, scores = ops.choose_cuboids_sics(qd, T, H, W, cands, b)
+    perms = torch.from_numpy(np.stack([ops.perm_cuboid(T, H, W, *c) for c in cands])).cuda()
+    choice, scores, _ = ops.sics_choose(qd, None, perms, Npad, b)
     choice, scores = host(choice), host(scores)
     ref = np.zeros((len(cands), Hh))
     for ci, c in enumerate(cands):
@@ -133,3 +134,44 @@ def test_layer_sics_choice_config5():
     out2 = ref.forward(qd, kd, vd)
     torch.cuda.synchronize()
     assert torch.equal(out1, out2)
+
+
+@pytest.mark.parametrize("with_k", [False, True])
+def test_sics_choose_matches_oracle_config5(with_k):
+    """dbs_sics_choose on config 5's latent grid and candidate shapes (one call for every
+    candidate): per-block scores within relative 1e-4 of the oracle's float64 SICS, the aggregation
+    scores likewise, and the per-head choice equal to the oracle's (Q + K) where its two best scores
+    differ by more than 1e-4; the output buffers are guarded by canaries."""
+    say("sics choose", with_k)
+    from gpu_helpers import Guarded
+    from oracle.pooled import choose_scheme
+    from workloads import get_config, make_inputs
+    ops = _ops()
+    cfg = get_config(5)
+    heads = [0, 1, 2, 3]
+    q, k, _ = make_inputs(cfg, heads=heads, workers=4)
+    N, b = cfg.N, cfg.b
+    Npad = -(-N // b) * b
+    nb = Npad // b
+    cands = list(cfg.cuboid_choices)
+    perms = np.stack([perm_cuboid(cfg.T, cfg.H, cfg.W, *c) for c in cands]).astype(np.int32)
+    T = 2 if with_k else 1
+    gb = Guarded((len(cands), T, 1, len(heads), nb), torch.float32)
+    gs = Guarded((len(cands), 1, len(heads)), torch.float32)
+    gc = Guarded((1, len(heads)), torch.int32, fill=-7)
+    ops.sics_choose(dev_bf16(q), dev_bf16(k) if with_k else None, dev(perms), Npad, b, block_scores=gb.view,
+                    scores=gs.view, choice=gc.view)
+    torch.cuda.synchronize()
+    assert gb.intact() and gs.intact() and gc.intact()
+    blk, sc, ch = host(gb.view), host(gs.view), host(gc.view)
+    for j in range(len(heads)):
+        best, ref = choose_scheme(q[0, :, j], k[0, :, j] if with_k else None, list(perms), b)
+        np.testing.assert_allclose(sc[:, 0, j], ref, rtol=1e-4)
+        qb = sics_blocks(q[0, perms[1], j], N, b)
+        np.testing.assert_allclose(blk[1, 0, 0, j], qb, rtol=1e-4, atol=1e-4)
+        if with_k:
+            kb = sics_blocks(k[0, perms[2], j], N, b)
+            np.testing.assert_allclose(blk[2, 1, 0, j], kb, rtol=1e-4, atol=1e-4)
+        top = np.sort(ref)[::-1]
+        if top[0] - top[1] > 1e-4 * top[0]:
+            assert ch[0, j] == best, (j, ref, ch[0, j])

@@ -96,8 +96,18 @@ def make_head(cid: int, head: int, grid: Tuple[int, int, int], d: int,
     return q.astype(np.float32), k.astype(np.float32), v
 
 
-def make_inputs(cfg: Config, heads: Optional[Sequence[int]] = None, round_bf16: Optional[bool] = None):
-    """Q, K, V as float32 [1, N, len(heads), d] (bf16-representable unless the config is fp32)."""
+def _head_job(args):
+    cfg, h, round_bf16 = args
+    qkv = make_head(cfg.cid, h, (cfg.T, cfg.H, cfg.W), cfg.d, head_sigma(cfg, h), cfg.text_prefix)
+    return tuple(bf16_round(x) if round_bf16 else x for x in qkv)
+
+
+def make_inputs(cfg: Config, heads: Optional[Sequence[int]] = None, round_bf16: Optional[bool] = None,
+                workers: int = 1):
+    """Q, K, V as float32 [1, N, len(heads), d] (bf16-representable unless the config is fp32).
+    workers > 1 draws the heads in that many threads (the filter and the draws run outside the
+    interpreter lock); every head has its own seeds, so the values do not depend on the worker
+    count."""
     if heads is None:
         heads = range(cfg.heads)
     heads = list(heads)
@@ -105,8 +115,17 @@ def make_inputs(cfg: Config, heads: Optional[Sequence[int]] = None, round_bf16: 
         round_bf16 = cfg.dtype == "bf16"
     N, d = cfg.N, cfg.d
     out = [np.empty((1, N, len(heads), d), dtype=np.float32) for _ in range(3)]
-    for j, h in enumerate(heads):
-        qkv = make_head(cfg.cid, h, (cfg.T, cfg.H, cfg.W), d, head_sigma(cfg, h), cfg.text_prefix)
-        for t in range(3):
-            out[t][0, :, j, :] = bf16_round(qkv[t]) if round_bf16 else qkv[t]
+    jobs = [(cfg, h, round_bf16) for h in heads]
+    if workers > 1 and len(heads) > 1:
+        import concurrent.futures as cf
+        with cf.ThreadPoolExecutor(max_workers=min(workers, len(heads))) as ex:
+            results = ex.map(_head_job, jobs)
+            for j, qkv in enumerate(results):
+                for t in range(3):
+                    out[t][0, :, j, :] = qkv[t]
+    else:
+        for j, job in enumerate(jobs):
+            qkv = _head_job(job)
+            for t in range(3):
+                out[t][0, :, j, :] = qkv[t]
     return out[0], out[1], out[2]
