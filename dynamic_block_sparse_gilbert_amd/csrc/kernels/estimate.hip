@@ -585,8 +585,8 @@ __device__ __forceinline__ void pimp_lane(const float* lse, const float* __restr
   for (int r = 0; r < KPL; ++r) out[r] = J0 + r < sg.nb ? __float_as_uint(fast_exp2(best[r])) : 0u;
 }
 
-// The final step fused with the block selection (the a3 + a4 fusion that
-// SPADE's prepass suggests): each P_imp row goes from registers or LDS
+// The final step fused with the block selection (estimate and mask in one
+// pass, as SPADE's prepass suggests): each P_imp row goes from registers
 // straight into the mask selection and reaches HBM only when p_imp is given.
 // Rows of up to 256 blocks: one wavefront per row, four per workgroup; lane l
 // forms entries l * KPL .. l * KPL + KPL - 1, the layout the register sort
@@ -620,29 +620,70 @@ __global__ __launch_bounds__(256) void est_mask_wave_kernel(const float2* __rest
   maskcore::mask_row_wave<KPL>(in, row, sg.nb, rule, flag_all[w], kv_count, kv_idx, mask);
 }
 
-// Longer rows: one workgroup per row, the LDS sort.
-template <int kCap>
-__global__ __launch_bounds__(256) void est_mask_lds_kernel(const float2* __restrict__ part,
-                                                           const float* __restrict__ tmax, SampleGeom sg, float sl2,
-                                                           maskcore::Rule rule, float* __restrict__ p_imp,
-                                                           int32_t* __restrict__ kv_count,
-                                                           int32_t* __restrict__ kv_idx,
-                                                           uint8_t* __restrict__ mask) {
-  __shared__ float lse[kMaxK];
-  const int I = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+// Rows of 257..4096 blocks: one wavefront per row (four per workgroup); lane l
+// forms entries l * KPL .. l * KPL + KPL - 1 four at a time (pimp_lane's terms,
+// so the same bits) and the row goes to the radix selection.
+template <int KPL>
+__global__ __launch_bounds__(256) void est_mask_radix_kernel(const float2* __restrict__ part,
+                                                             const float* __restrict__ tmax, SampleGeom sg, float sl2,
+                                                             maskcore::Rule rule, float* __restrict__ p_imp,
+                                                             int32_t* __restrict__ kv_count,
+                                                             int32_t* __restrict__ kv_idx,
+                                                             uint8_t* __restrict__ mask) {
+  __shared__ float lse_all[4][kMaxK];
+  __shared__ unsigned long long hist_all[4][512];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int I = blockIdx.x * 4 + w, bh = blockIdx.y;
+  if (I >= sg.nb) return;   // whole wavefronts; no workgroup barrier follows
   const int kI = I < sg.nb - 1 ? sg.k : sg.kj_last;
-  row_lse(part, sg, bh, I, kI, lse, tid);
-  __syncthreads();
+  float* lse = lse_all[w];
+  for (int i = lane; i < sg.k; i += 64) row_lse(part, sg, bh, I, kI, lse, i);
+  __builtin_amdgcn_wave_barrier();
   const int64_t row = (int64_t)bh * sg.nb + I;
   const float* t0 = tmax + ((int64_t)bh * sg.nsp + (int64_t)I * sg.k) * sg.ncell;
-  float* prow = p_imp != nullptr ? p_imp + row * sg.nb : nullptr;
-  maskcore::mask_row_lds<kCap, 256>(
-      [&](int J) {
-        const float v = pimp_value(lse, t0, sg, kI, J, sl2);
-        if (prow != nullptr) prow[J] = v;
-        return __float_as_uint(v);
-      },
-      row, sg.nb, rule, kv_count, kv_idx, mask);
+  const bool vec = sg.ncell == sg.nb && sg.nb % 4 == 0 && ((uintptr_t)tmax & 15u) == 0;
+  uint32_t in[KPL];
+  const int J0 = lane * KPL;
+#pragma unroll
+  for (int r = 0; r < KPL; r += 4) {
+    uint32_t q[4];
+    if (vec) {
+      // a 4-entry group inside the row: one 16-byte load per sampled query
+      float best[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      if (J0 + r < sg.nb) {
+        for (int t0q = 0; t0q < kI; t0q += 16) {
+          float4 vv[16];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int t = min(t0q + e, kI - 1);
+            vv[e] = *reinterpret_cast<const float4*>(t0 + (int64_t)t * sg.ncell + J0 + r);
+          }
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float l = lse[min(t0q + e, kI - 1)];
+            best[0] = fmaxf(best[0], __builtin_fmaf(vv[e].x, sl2, -l));
+            best[1] = fmaxf(best[1], __builtin_fmaf(vv[e].y, sl2, -l));
+            best[2] = fmaxf(best[2], __builtin_fmaf(vv[e].z, sl2, -l));
+            best[3] = fmaxf(best[3], __builtin_fmaf(vv[e].w, sl2, -l));
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) q[j] = J0 + r + j < sg.nb ? __float_as_uint(fast_exp2(best[j])) : 0u;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        q[j] = J0 + r + j < sg.nb ? __float_as_uint(pimp_value(lse, t0, sg, kI, J0 + r + j, sl2)) : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) in[r + j] = q[j];
+  }
+  if (p_imp != nullptr) {
+#pragma unroll
+    for (int r = 0; r < KPL; ++r)
+      if (J0 + r < sg.nb) p_imp[row * sg.nb + J0 + r] = __uint_as_float(in[r]);
+  }
+  maskcore::mask_row_radix<KPL>(in, row, sg.nb, rule, hist_all[w], kv_count, kv_idx, mask);
 }
 
 // Key splits: about 768 workgroups in total (one and a half rounds of two
@@ -701,7 +742,7 @@ hipError_t launch_d(const EstimateArgs& a) {
   const maskcore::Rule rule = maskcore::make_rule(m.rule, m.tau, m.topk, m.u);
   const float2* cp = part;
   const float* ct = tmax;
-  const dim3 wgrid((unsigned)((a.nb + 3) / 4), (unsigned)BH), rgrid((unsigned)a.nb, (unsigned)BH);
+  const dim3 wgrid((unsigned)((a.nb + 3) / 4), (unsigned)BH);
   if (a.nb <= 64) {
     hipLaunchKernelGGL((est_mask_wave_kernel<1>), wgrid, dim3(256), 0, a.stream, cp, ct, sg, sl2, rule, a.p_imp,
                        m.kv_count, m.kv_idx, m.mask);
@@ -711,12 +752,21 @@ hipError_t launch_d(const EstimateArgs& a) {
   } else if (a.nb <= 256) {
     hipLaunchKernelGGL((est_mask_wave_kernel<4>), wgrid, dim3(256), 0, a.stream, cp, ct, sg, sl2, rule, a.p_imp,
                        m.kv_count, m.kv_idx, m.mask);
+  } else if (a.nb <= 512) {
+    hipLaunchKernelGGL((est_mask_radix_kernel<8>), wgrid, dim3(256), 0, a.stream, cp, ct, sg, sl2, rule, a.p_imp,
+                       m.kv_count, m.kv_idx, m.mask);
   } else if (a.nb <= 1024) {
-    hipLaunchKernelGGL((est_mask_lds_kernel<1024>), rgrid, dim3(256), 0, a.stream, cp, ct, sg, sl2, rule, a.p_imp,
+    hipLaunchKernelGGL((est_mask_radix_kernel<16>), wgrid, dim3(256), 0, a.stream, cp, ct, sg, sl2, rule, a.p_imp,
+                       m.kv_count, m.kv_idx, m.mask);
+  } else if (a.nb <= 1280) {
+    hipLaunchKernelGGL((est_mask_radix_kernel<20>), wgrid, dim3(256), 0, a.stream, cp, ct, sg, sl2, rule, a.p_imp,
+                       m.kv_count, m.kv_idx, m.mask);
+  } else if (a.nb <= 2048) {
+    hipLaunchKernelGGL((est_mask_radix_kernel<32>), wgrid, dim3(256), 0, a.stream, cp, ct, sg, sl2, rule, a.p_imp,
                        m.kv_count, m.kv_idx, m.mask);
   } else {
-    hipLaunchKernelGGL((est_mask_lds_kernel<maskcore::kMaxNb>), rgrid, dim3(256), 0, a.stream, cp, ct, sg, sl2,
-                       rule, a.p_imp, m.kv_count, m.kv_idx, m.mask);
+    hipLaunchKernelGGL((est_mask_radix_kernel<64>), wgrid, dim3(256), 0, a.stream, cp, ct, sg, sl2, rule, a.p_imp,
+                       m.kv_count, m.kv_idx, m.mask);
   }
   if (m.order != nullptr) {
     const hipError_t e = hipGetLastError();

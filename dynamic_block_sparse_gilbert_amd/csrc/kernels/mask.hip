@@ -14,9 +14,10 @@
 // order by value descending and index ascending, are sorted in registers by
 // a bitonic network with cross-lane exchanges; one wavefront scan of the
 // lanes' exact sums finds the first prefix that reaches the target.  Longer
-// rows take one workgroup each and sort in LDS, wavefront 0 scanning the
-// sorted values 64 at a time.  The kept blocks are written in ascending index
-// order by a compaction.  Optionally a second launch turns the kept counts
+// rows also take one wavefront each, with no sort: a radix selection over the
+// value bits with exact weights finds the last kept value and how many of its
+// ties are kept.  The kept blocks are written in ascending index order by a
+// compaction.  Optionally a second launch turns the kept counts
 // into the attention kernel's work order.
 #include "common.h"
 #include "../launch.h"
@@ -27,15 +28,6 @@ namespace dbs {
 namespace {
 
 using namespace maskcore;
-
-template <int kCap, int kThreads>
-__global__ __launch_bounds__(kThreads) void build_mask_kernel(
-    const float* __restrict__ p_imp, int nb, Rule rule, int32_t* __restrict__ kv_count,
-    int32_t* __restrict__ kv_idx, uint8_t* __restrict__ mask) {
-  const int64_t row = blockIdx.x;
-  const uint32_t* prow = reinterpret_cast<const uint32_t*>(p_imp) + row * nb;
-  mask_row_lds<kCap, kThreads>([&](int j) { return prow[j]; }, row, nb, rule, kv_count, kv_idx, mask);
-}
 
 template <int KPL>
 __global__ __launch_bounds__(256) void build_mask_wave_kernel(
@@ -50,6 +42,34 @@ __global__ __launch_bounds__(256) void build_mask_wave_kernel(
 #pragma unroll
   for (int r = 0; r < KPL; ++r) in[r] = lane * KPL + r < nb ? prow[lane * KPL + r] : 0u;
   mask_row_wave<KPL>(in, row, nb, rule, flag_all[w], kv_count, kv_idx, mask);
+}
+
+// Rows of 257..4096 blocks: one wavefront per row (four per workgroup), lane l
+// loading entries l * KPL .. l * KPL + KPL - 1 (16 bytes at a time when the
+// rows are 16-byte aligned), then the radix selection (no sort).
+template <int KPL>
+__global__ __launch_bounds__(256) void build_mask_radix_kernel(
+    const float* __restrict__ p_imp, int nb, int rows, Rule rule, int32_t* __restrict__ kv_count,
+    int32_t* __restrict__ kv_idx, uint8_t* __restrict__ mask) {
+  __shared__ unsigned long long hist_all[4][512];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + w;
+  if (row >= rows) return;   // whole wavefronts; no workgroup barrier follows
+  const uint32_t* prow = reinterpret_cast<const uint32_t*>(p_imp) + row * nb;
+  uint32_t in[KPL];
+  const int j0 = lane * KPL;
+  if ((nb & 3) == 0 && (((uintptr_t)p_imp) & 15u) == 0) {
+#pragma unroll
+    for (int r = 0; r < KPL; r += 4) {
+      uint4 q = make_uint4(0u, 0u, 0u, 0u);
+      if (j0 + r < nb) q = *reinterpret_cast<const uint4*>(prow + j0 + r);   // nb % 4 == 0: all four valid
+      in[r] = q.x; in[r + 1] = q.y; in[r + 2] = q.z; in[r + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < KPL; ++r) in[r] = j0 + r < nb ? prow[j0 + r] : 0u;
+  }
+  mask_row_radix<KPL>(in, row, nb, rule, hist_all[w], kv_count, kv_idx, mask);
 }
 
 
@@ -120,12 +140,21 @@ hipError_t launch_build_mask(const MaskArgs& a) {
   } else if (a.nb <= 256) {
     hipLaunchKernelGGL((build_mask_wave_kernel<4>), wgrid, dim3(256), 0, a.stream, a.p_imp, a.nb, a.rows,
                        rule, a.kv_count, a.kv_idx, a.mask);
+  } else if (a.nb <= 512) {
+    hipLaunchKernelGGL((build_mask_radix_kernel<8>), wgrid, dim3(256), 0, a.stream, a.p_imp, a.nb, a.rows, rule,
+                       a.kv_count, a.kv_idx, a.mask);
   } else if (a.nb <= 1024) {
-    hipLaunchKernelGGL((build_mask_kernel<1024, 256>), dim3(a.rows), dim3(256), 0, a.stream, a.p_imp, a.nb,
-                       rule, a.kv_count, a.kv_idx, a.mask);
+    hipLaunchKernelGGL((build_mask_radix_kernel<16>), wgrid, dim3(256), 0, a.stream, a.p_imp, a.nb, a.rows, rule,
+                       a.kv_count, a.kv_idx, a.mask);
+  } else if (a.nb <= 1280) {
+    hipLaunchKernelGGL((build_mask_radix_kernel<20>), wgrid, dim3(256), 0, a.stream, a.p_imp, a.nb, a.rows, rule,
+                       a.kv_count, a.kv_idx, a.mask);
+  } else if (a.nb <= 2048) {
+    hipLaunchKernelGGL((build_mask_radix_kernel<32>), wgrid, dim3(256), 0, a.stream, a.p_imp, a.nb, a.rows, rule,
+                       a.kv_count, a.kv_idx, a.mask);
   } else {
-    hipLaunchKernelGGL((build_mask_kernel<kMaxNb, 256>), dim3(a.rows), dim3(256), 0, a.stream, a.p_imp,
-                       a.nb, rule, a.kv_count, a.kv_idx, a.mask);
+    hipLaunchKernelGGL((build_mask_radix_kernel<64>), wgrid, dim3(256), 0, a.stream, a.p_imp, a.nb, a.rows, rule,
+                       a.kv_count, a.kv_idx, a.mask);
   }
   if (a.order != nullptr) {
     const hipError_t e = hipGetLastError();

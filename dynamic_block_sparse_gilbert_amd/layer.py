@@ -57,6 +57,10 @@ class LayerSpec:
         return 1.0 / math.sqrt(self.d)
 
 
+# The largest launch (query blocks over all batches and heads) that runs longest rows first.
+ORDER_MAX_BLOCKS = 4096
+
+
 def build_perm(spec: LayerSpec) -> np.ndarray:
     """Host permutation: int32 [N] or [heads, N]."""
     if spec.order == "gilbert":
@@ -146,7 +150,13 @@ class AsaLayer:
                               dtype=torch.uint8, device=self.device)
         self.kv_count = torch.empty((B, Hh, nb), dtype=torch.int32, device=self.device)
         self.kv_idx = torch.empty((B, Hh, nb, nb), dtype=torch.int32, device=self.device)
-        self.order = torch.empty((B * Hh * nb,), dtype=torch.int32, device=self.device)
+        # Work order of the attention launch.  Longest rows first evens out the tail when the
+        # launch is a few rounds of workgroups; on larger launches the plain index order is faster
+        # (neighbouring query blocks of a head run together and share most kept key blocks in L2:
+        # 16.9 against 17.6 ms on the 153,600-token layer, 0.50 against 0.51 ms the other way on
+        # the 32,760-token one), and the mask then writes no order at all.
+        self.order = torch.empty((B * Hh * nb,), dtype=torch.int32, device=self.device) \
+            if B * Hh * nb <= ORDER_MAX_BLOCKS else None
         self.k_g = self.v_g = None
         self.Ng = 0
         if s.n_pool:
