@@ -7,11 +7,13 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 #include <exception>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -456,6 +458,85 @@ dbs_status dbs_estimate_mask_tok(const void* q, dbs_dtype q_dt, int64_t sb, int6
   tok.q = q; tok.q_f32 = q_dt == DBS_FP32; tok.qsb = sb; tok.qsn = sn; tok.qsh = sh;
   tok.perm = perm; tok.perm_h_stride = perm_per_head ? N : 0;
   return estimate_impl(nullptr, k_r, B, Hh, N, Npad, d, b, k, scale, p_imp, workspace, workspace_bytes, tok,
+                       stream, &m);
+  DBS_GUARD_END
+}
+
+}  // extern "C"
+
+// ---- the estimate-and-mask call without a workspace argument ----------------------------
+// Its workspace is this array; each device holds its own copy at its own
+// address.  In host code `scratch` names a host-side stand-in, never the
+// device memory: only the address from hipGetSymbolAddress is passed on.
+static __device__ __align__(256) unsigned char scratch[DBS_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+// The device address of `scratch` on the device of `stream` (looked up once per
+// device, with that device current).
+dbs_status scratch_address(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = stream != nullptr ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  REQUIRE(e == hipSuccess, DBS_ERR_HIP, "device of the stream: %s", hipGetErrorString(e));
+  REQUIRE(dev >= 0 && dev < kMaxScratchDevices, DBS_ERR_UNSUPPORTED, "device %d: at most %d devices", dev,
+          kMaxScratchDevices);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      int cur = -1;
+      e = hipGetDevice(&cur);
+      REQUIRE(e == hipSuccess, DBS_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+      if (cur != dev) {
+        e = hipSetDevice(dev);
+        REQUIRE(e == hipSuccess, DBS_ERR_HIP, "hipSetDevice(%d): %s", dev, hipGetErrorString(e));
+      }
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+      REQUIRE(e == hipSuccess && p != nullptr, DBS_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+              hipGetErrorString(e));
+      REQUIRE(e2 == hipSuccess, DBS_ERR_HIP, "hipSetDevice(%d): %s", cur, hipGetErrorString(e2));
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return DBS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dbs_status dbs_estimate_mask_tok_noalloc(const void* q, dbs_dtype q_dt, int64_t sb, int64_t sn, int64_t sh,
+                                         const int32_t* perm, int perm_per_head, const void* k_r, int B, int Hh,
+                                         int N, int Npad, int d, int b, int k, float scale, int rule, double param,
+                                         float* p_imp, int32_t* kv_count, int32_t* kv_idx, uint8_t* mask,
+                                         int32_t* order, hipStream_t stream) {
+  DBS_GUARD_BEGIN
+  dbs_status st = check_tok(q, q_dt, sb, sn, sh, perm, perm_per_head);
+  if (st != DBS_OK) return st;
+  dbs::MaskArgs m{};
+  st = fuse_args(rule, param, kv_count, kv_idx, mask, order, Npad, b, m);
+  if (st != DBS_OK) return st;
+  st = check_geometry(B, Hh, N, Npad, d, b);
+  if (st != DBS_OK) return st;
+  const size_t need = dbs_estimate_workspace_bytes(B, Hh, N, d, b, k);
+  REQUIRE(need <= DBS_NOALLOC_SCRATCH_BYTES, DBS_ERR_UNSUPPORTED,
+          "this shape needs %zu bytes of scratch; the static scratch holds %zu (pass a workspace to "
+          "dbs_estimate_mask_tok instead)",
+          need, (size_t)DBS_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = scratch_address(stream, &ws);
+  if (st != DBS_OK) return st;
+  dbs::TokIO tok{};
+  tok.q = q; tok.q_f32 = q_dt == DBS_FP32; tok.qsb = sb; tok.qsn = sn; tok.qsh = sh;
+  tok.perm = perm; tok.perm_h_stride = perm_per_head ? N : 0;
+  return estimate_impl(nullptr, k_r, B, Hh, N, Npad, d, b, k, scale, p_imp, ws, DBS_NOALLOC_SCRATCH_BYTES, tok,
                        stream, &m);
   DBS_GUARD_END
 }

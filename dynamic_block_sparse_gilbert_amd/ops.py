@@ -327,6 +327,38 @@ def estimate_mask(q_r: torch.Tensor, k_r: torch.Tensor, N: int, b: int, k: int, 
     return kv_count, kv_idx, mask, p_imp
 
 
+NOALLOC_SCRATCH_BYTES = 128 << 20     # DBS_NOALLOC_SCRATCH_BYTES
+
+
+def estimate_mask_noalloc(q: torch.Tensor, q_perm: torch.Tensor, k_r: torch.Tensor, N: int, b: int, k: int,
+                          scale: float, rule: str, param: float, kv_count: torch.Tensor, kv_idx: torch.Tensor,
+                          order: Optional[torch.Tensor] = None, p_imp: Optional[torch.Tensor] = None,
+                          mask: Optional[torch.Tensor] = None):
+    """estimate_mask with q in token order [B, N, Hh, d] and no workspace (dbs_estimate_mask_tok_noalloc):
+    the library's static scratch holds the intermediate results and nothing is allocated, here or
+    in the library; the caller brings every output.  Returns (kv_count, kv_idx, mask, p_imp)."""
+    _dev(q, q_perm, k_r, kv_count, kv_idx, order, p_imp, mask)
+    if q.stride(3) != 1:
+        raise ValueError("the d axis of q must be contiguous")
+    B, Hh, Npad, d = k_r.shape
+    nb = Npad // b
+    _lists(kv_count, kv_idx, B, Hh, nb)
+    _i32(order, "order", B * Hh * nb, ())
+    for t, name in ((p_imp, "p_imp"), (mask, "mask")):
+        if t is not None and (tuple(t.shape) != (B, Hh, nb, nb) or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous [{B}, {Hh}, {nb}, {nb}] tensor")
+    if p_imp is not None and p_imp.dtype != torch.float32:
+        raise TypeError("p_imp must be float32")
+    if mask is not None and mask.dtype != torch.uint8:
+        raise TypeError("mask must be uint8")
+    per_head = _perm(q_perm, N, Hh, "q_perm")
+    check("dbs_estimate_mask_tok_noalloc", lib().dbs_estimate_mask_tok_noalloc(
+        _p(q), _dt(q), q.stride(0), q.stride(1), q.stride(2), _p(q_perm), per_head, _p(k_r),
+        B, Hh, N, Npad, d, b, k, float(scale), MASK_RULES[rule], float(param), _p(p_imp), _p(kv_count),
+        _p(kv_idx), _p(mask), _p(order), _stream()))
+    return kv_count, kv_idx, mask, p_imp
+
+
 def query_prune(q: torch.Tensor, perm: torch.Tensor, anchor: torch.Tensor, Npad: int, b: int, r: float,
                 q_count: Optional[torch.Tensor] = None, rowsel: Optional[torch.Tensor] = None,
                 keep: Optional[torch.Tensor] = None):

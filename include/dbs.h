@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define DBS_ABI_VERSION 11
+#define DBS_ABI_VERSION 12
 
 typedef enum {
   DBS_OK = 0,
@@ -280,6 +280,27 @@ dbs_status dbs_estimate_mask_tok(const void* q, dbs_dtype q_dt, int64_t sb, int6
                                  int rule, double param, float* p_imp,
                                  int32_t* kv_count, int32_t* kv_idx, uint8_t* mask, int32_t* order,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * dbs_estimate_mask_tok with no workspace argument.  The estimator's
+ * intermediate results go to a static device array of
+ * DBS_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it runs
+ * on until the process ends; this call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine).  The array's address on the
+ * stream's device is looked up on the first call there.  Every argument,
+ * output and error is dbs_estimate_mask_tok's, plus: UNSUPPORTED, before any
+ * device work, when the shape needs more than DBS_NOALLOC_SCRATCH_BYTES
+ * (dbs_estimate_workspace_bytes(B, Hh, N, d, b, k) says how much).  Nothing in
+ * the array has to start at zero.  All calls on one GPU share its array:
+ * calls that overlap on one GPU (on different streams, or from several
+ * threads) race and give undefined results. */
+#define DBS_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+dbs_status dbs_estimate_mask_tok_noalloc(const void* q, dbs_dtype q_dt, int64_t sb, int64_t sn, int64_t sh,
+                                         const int32_t* perm, int perm_per_head, const void* k_r, int B, int Hh,
+                                         int N, int Npad, int d, int b, int k, float scale, int rule, double param,
+                                         float* p_imp, int32_t* kv_count, int32_t* kv_idx, uint8_t* mask,
+                                         int32_t* order, hipStream_t stream);
 
 /* Query pruning (Bidirectional Sparse Attention notes, key design 1): in each
  * query block I (reordered rows I*b .. I*b + n - 1, n valid), a row i whose

@@ -37,7 +37,7 @@ def test_all_declared_symbols_exported(dbs):
     for n in names:
         assert hasattr(h, n), n
     assert set(names) == set(L.SIGNATURES), set(names) ^ set(L.SIGNATURES)
-    assert L.lib().dbs_abi_version() == 11
+    assert L.lib().dbs_abi_version() == 12
 
 
 @pytest.mark.parametrize("T,H,W", list(itertools.product(range(1, 7), repeat=3)))
@@ -174,6 +174,39 @@ def test_estimate_tok_validation(dbs):
     assert call(7, 0) == -1               # k_r NULL
     assert call(14, 6) == -2              # k not a power of two
     assert call(18, ws - 4) == -1         # small workspace
+
+
+@cpu_only
+def test_estimate_mask_noalloc_validation(dbs):
+    """The no-alloc call checks its arguments as dbs_estimate_mask_tok does and refuses a shape whose
+    workspace exceeds the static scratch, all before any device work (nothing is launched here)."""
+    _, L = dbs
+    g = L.lib().dbs_estimate_mask_tok_noalloc
+    # q, q_dt, sb, sn, sh, perm, per_head, k_r, B, Hh, N, Npad, d, b, k, scale, rule, param, p_imp, kv_count,
+    # kv_idx, mask, order, stream
+    ok = [A, 0, 100 * 2 * 128, 2 * 128, 128, A, 0, A, 1, 2, 100, 128, 128, 64, 8, 0.125, 0, 0.9, None, A, A, None,
+          None, None]
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return g(*a)
+    assert call(a0=0) == -1               # q NULL
+    assert call(a5=0) == -1               # perm NULL
+    assert call(a19=0) == -1              # kv_count NULL
+    assert call(a22=A + 2) == -3          # misaligned order
+    assert call(a16=9) == -1              # unknown rule
+    assert call(a17=0.0) == -1            # tau 0
+    assert call(a12=96) == -2             # head dimension
+    assert call(a11=192) == -1            # Npad not the padded length
+    # 24 heads of 153,600 tokens: gigabytes of workspace, above the static maximum
+    N, b, k, Hh = 153600, 128, 16, 24
+    need = L.lib().dbs_estimate_workspace_bytes(1, Hh, N, 128, b, k)
+    assert need > 128 << 20
+    st = call(a2=N * Hh * 128, a3=Hh * 128, a4=128, a9=Hh, a10=N, a11=N, a13=b, a14=k)
+    assert st == -2
+    msg = L.lib().dbs_last_error().decode()
+    assert "scratch" in msg and str(need) in msg and str(128 << 20) in msg
 
 
 @cpu_only
