@@ -86,5 +86,58 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# ---- host-sanitizer build (CPU tests only) -------------------------------------------------
+# The host-side sources (argument checks, permutations, the normal quantile) are
+# compiled again with AddressSanitizer and UndefinedBehaviorSanitizer on the host
+# pass only (the device code is not instrumented) and linked with the ordinary
+# kernel objects into _build/asan/libdbs_asan.so.  Python loads it through
+# DBS_LIB_PATH with the sanitizer runtime preloaded (see asan_runtime()).
+HOST_SOURCES = ["api.cpp", "host/perm.cpp", "host/stats.cpp"]
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+SAN_LIB = os.path.join(BUILD, "asan", "libdbs_asan.so")
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime (to preload into Python), or ""."""
+    root = os.path.join(os.path.dirname(os.path.dirname(hipcc())), "llvm", "lib", "clang")
+    if not os.path.isdir(root):
+        return ""
+    for ver in sorted(os.listdir(root), reverse=True):
+        p = os.path.join(root, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(p):
+            return p
+    return ""
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    kernel_objs = [os.path.join(BUILD, s.replace("/", "_") + ".o") for s in SOURCES if s not in HOST_SOURCES]
+    if not all(os.path.exists(o) for o in kernel_objs):
+        build(verbose)
+    out = os.path.join(BUILD, "asan")
+    os.makedirs(out, exist_ok=True)
+    objs = []
+    for src in HOST_SOURCES:
+        obj = os.path.join(out, src.replace("/", "_") + ".o")
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-O1", "-g", "-std=c++17", "-fPIC", "-c",
+               "-I", os.path.join(ROOT, "include"), "-I", CSRC, *DEVICE_FLAGS, *SAN_FLAGS,
+               "-x", "hip", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"sanitizer compile failed: {src}\n{r.stderr}")
+        objs.append(obj)
+    tmp = SAN_LIB + f".tmp{os.getpid()}"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *SAN_FLAGS, "-shared-libasan", *objs,
+           *kernel_objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitizer link failed\n{r.stderr}")
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--host-sanitizers" in sys.argv:
+        print(build_host_sanitized(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

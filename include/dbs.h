@@ -32,7 +32,8 @@
  *
  * Conventions for every call:
  * - Device pointers are allocated and owned by the caller and must be 16-byte
- *   aligned.  The library allocates no device memory and keeps no device state.
+ *   aligned.  The library allocates no device memory.  Its only device state
+ *   is the static scratch array of dbs_estimate_mask_tok_noalloc.
  * - Device calls are asynchronous on the given stream (NULL: the default
  *   stream) and never synchronise.  Arguments are checked on the host before
  *   any launch; a failed check launches nothing.
@@ -74,8 +75,21 @@ typedef enum {
   DBS_ERR_HIP = -5           /* another HIP runtime call failed            */
 } dbs_status;
 
-typedef enum { DBS_BF16 = 0, DBS_FP32 = 1 } dbs_dtype;
-typedef enum { DBS_ROWS = 0, DBS_TILES_T = 1 } dbs_layout;
+/* Element type and layout arguments.  The two range enumerators make every
+ * int a valid value of the type, so an unknown value passed by a caller is
+ * well defined in C++ too and is rejected by the argument checks. */
+typedef enum {
+  DBS_BF16 = 0,
+  DBS_FP32 = 1,
+  DBS_DTYPE_RANGE_MIN_ = -0x7fffffff - 1,
+  DBS_DTYPE_RANGE_MAX_ = 0x7fffffff
+} dbs_dtype;
+typedef enum {
+  DBS_ROWS = 0,
+  DBS_TILES_T = 1,
+  DBS_LAYOUT_RANGE_MIN_ = -0x7fffffff - 1,
+  DBS_LAYOUT_RANGE_MAX_ = 0x7fffffff
+} dbs_layout;
 
 /* ABI version of the loaded library (DBS_ABI_VERSION). */
 int dbs_abi_version(void);
