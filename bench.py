@@ -508,7 +508,9 @@ def load_inputs(cfg, torch, dev):
 def resolve_tau(layer, qd, kd, vd, out, mode, val):
     if mode == "tau":
         return float(val), {"tau_rule": "fixed by the workload"}
-    layer.forward(qd, kd, vd, out=out, tau=1.0, keep_p_imp=True)
+    # P_imp alone (the estimate and a mask at tau 1): the bisection needs no attention
+    layer.prepare(qd, kd, vd)
+    layer.mask(1.0, keep_p_imp=True)
     tau, s = layer.tune_tau(val)
     return tau, {"tau_rule": f"largest float32 tau with block sparsity >= {val} (bisection with dbs_build_mask "
                              "on the layer's P_imp, outside the timed region)", "target_sparsity": val}

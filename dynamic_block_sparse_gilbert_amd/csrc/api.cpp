@@ -360,7 +360,6 @@ dbs_status estimate_impl(const void* q_r, const void* k_r, int B, int Hh, int N,
   dbs_status st = check_geometry(B, Hh, N, Npad, d, b);
   if (st != DBS_OK) return st;
   REQUIRE(k >= 1 && k <= b, DBS_ERR_INVALID_ARG, "k=%d must be in [1, b=%d]", k, b);
-  REQUIRE((k & (k - 1)) == 0, DBS_ERR_UNSUPPORTED, "k=%d must be a power of two", k);
   REQUIRE(std::isfinite(scale) && scale > 0.f, DBS_ERR_INVALID_ARG, "scale must be finite and > 0");
   const size_t need = dbs_estimate_workspace_bytes(B, Hh, N, d, b, k);
   REQUIRE(workspace_bytes >= need, DBS_ERR_INVALID_ARG, "workspace %zu bytes < %zu needed", workspace_bytes, need);

@@ -46,8 +46,12 @@ constexpr int kMaxChunksPerSplit = 64;   // bound on chunks per key split
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// k: slots per block, the sample count rounded up to a power of two; kf: the
+// sample count (valid slots of a full block, kf <= k); kj_last: valid slots of
+// the last block.  Slots t >= kf of a full block are empty, like the last
+// block's slots t >= kj_last.
 struct SampleGeom {
-  int N, b, k, klog2, nb, nsp, nsp_pad, kj_last;
+  int N, b, k, klog2, nb, nsp, nsp_pad, kj_last, kf;
   int splits, cps;   // key splits and 64-key chunks per split
   int cell_log2;     // block maxima are kept per cell of min(k, 64) compact keys
   int ncell;         // cells per sampled query: nsp >> cell_log2
@@ -55,14 +59,17 @@ struct SampleGeom {
   __device__ __forceinline__ int row(int r) const {
     if (r >= nsp) return -1;
     const int J = r >> klog2, t = r & (k - 1);
-    if (J < nb - 1) return J * b + t * (b >> klog2);   // full block: L = b, k_J = k
+    if (J < nb - 1) {   // full block: L = b, k_J = kf
+      if (kf == k) return J * b + t * (b >> klog2);
+      return t < kf ? J * b + (t * b) / kf : -1;
+    }
     const int L = N - J * b;
     if (t >= kj_last) return -1;
     return J * b + (t * L) / kj_last;
   }
   __device__ __forceinline__ bool valid(int r) const {
     if (r >= nsp) return false;
-    return (r >> klog2) < nb - 1 || (r & (k - 1)) < kj_last;
+    return (r & (k - 1)) < ((r >> klog2) < nb - 1 ? kf : kj_last);
   }
 };
 
@@ -255,7 +262,9 @@ __global__ __launch_bounds__(kThreads) void est_pass_kernel(
   }
   // From this slot on, chunks take the exact rows: the last block when it is
   // partial (its slots are spread over fewer than b rows), and the padding.
-  const int exact_from = (sg.N < sg.nb * sg.b || sg.nsp % kChunk != 0) ? (sg.nb - 1) * sg.k : sg.nsp_pad;
+  // Every chunk takes them when the sample count is not a power of two.
+  const int exact_from = sg.kf < sg.k ? 0
+                         : (sg.N < sg.nb * sg.b || sg.nsp % kChunk != 0) ? (sg.nb - 1) * sg.k : sg.nsp_pad;
   auto dma = [&](int ch, char* buf) {
     const int ck0 = ch * kChunk;
     if (ck0 + kChunk <= exact_from) {
@@ -368,8 +377,9 @@ __global__ __launch_bounds__(kThreads) void est_pass_kernel(
   const int tail = (sg.nb - 1) * sg.k;   // first slot of the last block
   auto body = [&](int ch, f32x16_t (&S)[2], auto first) {
     const int ck0 = ch * kChunk;
-    if (ck0 + kChunk > sg.nsp || (sg.kj_last < sg.k && ck0 + kChunk > tail)) {
-      // rare: padding or the last block's empty slots score -inf
+    if (ck0 + kChunk > sg.nsp || (sg.kj_last < sg.k && ck0 + kChunk > tail) || sg.kf < sg.k) {
+      // padding and empty slots score -inf (only the last chunks when the
+      // sample count is a power of two)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -520,7 +530,7 @@ __global__ __launch_bounds__(kFinalThreads) void est_final_kernel(const float2* 
                                                                   float sl2) {
   __shared__ float lse[kMaxK];
   const int I = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  const int kI = I < sg.nb - 1 ? sg.k : sg.kj_last;
+  const int kI = I < sg.nb - 1 ? sg.kf : sg.kj_last;
   row_lse(part, sg, bh, I, kI, lse, tid);
   __syncthreads();
   const float* t0 = tmax + ((int64_t)bh * sg.nsp + (int64_t)I * sg.k) * sg.ncell;
@@ -603,7 +613,7 @@ __global__ __launch_bounds__(256) void est_mask_wave_kernel(const float2* __rest
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int I = blockIdx.x * 4 + w, bh = blockIdx.y;
   if (I >= sg.nb) return;   // whole wavefronts; no workgroup barrier follows
-  const int kI = I < sg.nb - 1 ? sg.k : sg.kj_last;
+  const int kI = I < sg.nb - 1 ? sg.kf : sg.kj_last;
   float* lse = lse_all[w];
   for (int i = lane; i < sg.k; i += 64) row_lse(part, sg, bh, I, kI, lse, i);
   __builtin_amdgcn_wave_barrier();
@@ -635,7 +645,7 @@ __global__ __launch_bounds__(256) void est_mask_radix_kernel(const float2* __res
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int I = blockIdx.x * 4 + w, bh = blockIdx.y;
   if (I >= sg.nb) return;   // whole wavefronts; no workgroup barrier follows
-  const int kI = I < sg.nb - 1 ? sg.k : sg.kj_last;
+  const int kI = I < sg.nb - 1 ? sg.kf : sg.kj_last;
   float* lse = lse_all[w];
   for (int i = lane; i < sg.k; i += 64) row_lse(part, sg, bh, I, kI, lse, i);
   __builtin_amdgcn_wave_barrier();
@@ -705,10 +715,12 @@ void split_plan(int BH, int nsp, int& splits, int& cps) {
 template <int D>
 hipError_t launch_d(const EstimateArgs& a) {
   SampleGeom sg;
-  sg.N = a.N; sg.b = a.b; sg.k = a.k; sg.nb = a.nb;
+  sg.N = a.N; sg.b = a.b; sg.nb = a.nb;
   sg.klog2 = 0;
   while ((1 << sg.klog2) < a.k) ++sg.klog2;
-  sg.nsp = a.nb * a.k;
+  sg.k = 1 << sg.klog2;
+  sg.kf = a.k;
+  sg.nsp = a.nb * sg.k;
   sg.nsp_pad = (sg.nsp + kChunk - 1) / kChunk * kChunk;
   sg.cell_log2 = sg.klog2 < 6 ? sg.klog2 : 6;
   sg.ncell = sg.nsp >> sg.cell_log2;
@@ -722,7 +734,7 @@ hipError_t launch_d(const EstimateArgs& a) {
   const __bf16* qr = (const __bf16*)a.q_r;
   const __bf16* kr = (const __bf16*)a.k_r;
   dim3 grid((unsigned)(((sg.nsp + kQPerWg - 1) / kQPerWg) * sg.splits * BH));
-  switch (a.k) {
+  switch (sg.k) {
     case 1: hipLaunchKernelGGL((est_pass_kernel<D, 1>), grid, dim3(kThreads), 0, a.stream, qr, kr, a.tok, a.Npad, a.Hh, part, tmax, sg, sl2); break;
     case 2: hipLaunchKernelGGL((est_pass_kernel<D, 2>), grid, dim3(kThreads), 0, a.stream, qr, kr, a.tok, a.Npad, a.Hh, part, tmax, sg, sl2); break;
     case 4: hipLaunchKernelGGL((est_pass_kernel<D, 4>), grid, dim3(kThreads), 0, a.stream, qr, kr, a.tok, a.Npad, a.Hh, part, tmax, sg, sl2); break;
@@ -779,7 +791,9 @@ hipError_t launch_d(const EstimateArgs& a) {
 }  // namespace
 
 size_t estimate_workspace_bytes(int B, int Hh, int nb, int k, int d) {
-  const int64_t nsp = (int64_t)nb * k;
+  int kp = 1;
+  while (kp < k) kp <<= 1;
+  const int64_t nsp = (int64_t)nb * kp;
   const int64_t nsp_pad = (nsp + kChunk - 1) / kChunk * kChunk;
   const int64_t BH = (int64_t)B * Hh;
   int splits, cps;

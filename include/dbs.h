@@ -185,7 +185,8 @@ dbs_status dbs_inverse_reorder(const void* y, dbs_dtype y_dt, void* x, dbs_dtype
  * library splits the sampled keys over up to nb*k/64 workgroups per panel of
  * 256 sampled queries), and per sampled query the maximum raw score over each cell of
  * min(k, 64) sampled keys (B * Hh * nb*k * nb*k/min(k,64) floats; about
- * 50 MB for 12 heads, nb = 256, k = 16).  Returns 0 for invalid sizes. */
+ * 50 MB for 12 heads, nb = 256, k = 16), k rounded up to a power of two.
+ * Returns 0 for invalid sizes. */
 size_t dbs_estimate_workspace_bytes(int B, int Hh, int N, int d, int b, int k);
 
 /* Block-importance estimation (Video-BLADE "Step 1"; BLADE notes key design 1).
@@ -195,9 +196,10 @@ size_t dbs_estimate_workspace_bytes(int B, int Hh, int N, int d, int b, int k);
  * the (batch, head); p_imp[b, h, I, J] = max of P_approx over (samples of I) x
  * (samples of J), float32, [B, Hh, nb, nb].
  * q_r, k_r: DBS_ROWS, type dt.  DBS_BF16: bf16 products with float32
- * accumulation and a float32 softmax (k a power of two, 1..b).  DBS_FP32:
- * float32 operands and float32 arithmetic throughout (any k in 1..b), for
- * workloads stored in float32.
+ * accumulation and a float32 softmax; a block's sampled slots are padded to
+ * the next power of two (empty slots take no part), so any k in 1..b costs
+ * what that power of two costs.  DBS_FP32: float32 operands and float32
+ * arithmetic throughout (any k in 1..b), for workloads stored in float32.
  * workspace: device, >= dbs_estimate_workspace_bytes(...) bytes; its contents
  * on entry do not matter.  Q and K must be finite (a NaN input gives an
  * undefined result).  Errors: UNSUPPORTED for d, b, k or dt outside the

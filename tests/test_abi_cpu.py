@@ -142,7 +142,10 @@ def test_estimate_validation(dbs):
     assert call(dt=1, p=MIS) == -3
     assert call(dt=1, k_=0) == -1
     assert call(dt=1, wb=ws - 4) == -1
-    assert call(k_=6) == -2
+    # any k in [1, b] is a valid size: k = 6 reaches the workspace check (slots padded to 8)
+    assert L.lib().dbs_estimate_workspace_bytes(1, 2, 100, 128, 64, 6) == ws
+    assert call(k_=6, wb=ws - 4) == -1
+    assert "workspace" in L.lib().dbs_last_error().decode()
     assert call(k_=0) == -1
     assert call(k_=128) == -1
     assert call(wb=ws - 4) == -1
@@ -172,7 +175,9 @@ def test_estimate_tok_validation(dbs):
     assert call(3, 2 * 128 + 4) == -3     # row stride breaks 16-byte rows
     assert call(3, -1) == -1
     assert call(7, 0) == -1               # k_r NULL
-    assert call(14, 6) == -2              # k not a power of two
+    a = list(ok)
+    a[14], a[18] = 6, ws - 4              # k = 6 is accepted; the small workspace is not
+    assert f(*a) == -1 and "workspace" in L.lib().dbs_last_error().decode()
     assert call(18, ws - 4) == -1         # small workspace
 
 
@@ -315,7 +320,11 @@ def test_estimate_mask_validation(dbs):
     assert call(17, A + 2) == -3          # misaligned order
     assert call(11, 9) == -1              # unknown rule
     assert call(12, 1.5) == -1            # tau > 1
-    assert call(9, 3) == -2               # k not a power of two
+    ws3 = L.lib().dbs_estimate_workspace_bytes(1, 2, 100, 128, 64, 3)
+    assert ws3 == L.lib().dbs_estimate_workspace_bytes(1, 2, 100, 128, 64, 4)   # slots padded to 4
+    a = list(ok)
+    a[9], a[19] = 3, ws3 - 1              # k = 3 is accepted; the small workspace is not
+    assert f(*a) == -1 and "workspace" in L.lib().dbs_last_error().decode()
     assert call(19, ws - 1) == -1         # small workspace
     assert call(10, float("nan")) == -1   # scale
     g = L.lib().dbs_estimate_mask_tok

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import dev, dev_bf16, host, say, smooth_qkv
+from gpu_helpers import Guarded, dev, dev_bf16, host, say, smooth_qkv
 from oracle.estimator import p_imp as o_p_imp
 from oracle.perm import perm_gilbert3d
 from oracle.reorder import reorder_fast as o_reorder
@@ -26,8 +26,12 @@ def _run(q, k, N, b, kk, d, Hh, B=1, query_blocks=None):
     perm = np.arange(N, dtype=np.int32)
     q_r = ops.reorder(dev_bf16(q), dev(perm), Npad, b, "rows")
     k_r = ops.reorder(dev_bf16(k), dev(perm), Npad, b, "rows")
-    P = ops.estimate_blocks(q_r, k_r, N, b, kk, 1.0 / np.sqrt(d))
+    nb = Npad // b
+    gp = Guarded((B, Hh, nb, nb), torch.float32)
+    gw = Guarded((max(16, ops.estimate_workspace_bytes(B, Hh, N, d, b, kk)),), torch.uint8, fill=171)
+    P = ops.estimate_blocks(q_r, k_r, N, b, kk, 1.0 / np.sqrt(d), p_imp=gp.view, workspace=gw.view)
     torch.cuda.synchronize()
+    assert gp.intact() and gw.intact()          # nothing written outside P_imp or the workspace
     P = host(P)
     qr, kr = o_reorder(q, perm, Npad), o_reorder(k, perm, Npad)
     for bi in range(B):
@@ -44,6 +48,9 @@ def _run(q, k, N, b, kk, d, Hh, B=1, query_blocks=None):
     (200, 64, 8, 64), (1000, 64, 16, 128), (1000, 128, 16, 64), (777, 128, 16, 128),
     (300, 64, 1, 64), (300, 64, 2, 128), (300, 64, 4, 64), (520, 128, 32, 128),
     (520, 64, 64, 64), (400, 128, 128, 128), (130, 128, 128, 64), (2048, 64, 8, 64),
+    # sample counts that are not powers of two (slots padded to the next one)
+    (1000, 128, 12, 128), (700, 64, 6, 64), (333, 64, 3, 128), (900, 128, 24, 64), (500, 128, 100, 128),
+    (260, 64, 48, 64), (130, 64, 5, 64), (1500, 128, 80, 128),
 ])
 def test_estimate_small(N, b, k, d):
     say("estimate", N, b, k, d)
@@ -99,7 +106,7 @@ def test_estimate_deterministic():
 
 @pytest.mark.parametrize("N,b,k,d,per_head,in32", [
     (1000, 128, 16, 128, False, False), (777, 64, 8, 64, True, False), (520, 128, 32, 128, True, True),
-    (300, 64, 1, 64, False, True),
+    (300, 64, 1, 64, False, True), (1000, 128, 12, 128, True, False), (333, 64, 7, 64, False, True),
 ])
 def test_estimate_token_order_equals_reorder(N, b, k, d, per_head, in32):
     """estimate_blocks_tok (sampled Q rows gathered in token order) is

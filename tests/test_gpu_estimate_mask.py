@@ -48,9 +48,11 @@ def _inputs(seed, N, Hh, d, B=1):
     (1000, 64, 8, 64, 2),        # nb 16, ragged last block (KPL 1 rows)
     (6000, 64, 16, 128, 1),      # nb 94 (KPL 2), ragged
     (16384, 64, 4, 64, 1),       # nb 256 (KPL 4)
-    (16400, 64, 64, 64, 1),      # nb 257: the LDS kernel, k = b
-    (70000, 64, 2, 64, 1),       # nb 1094: the 4096-key LDS class
+    (16400, 64, 64, 64, 1),      # nb 257: the radix selection (KPL 8), k = b
+    (70000, 64, 2, 64, 1),       # nb 1094: the radix selection (KPL 20)
     (2300, 128, 128, 128, 1),    # k = 128: two 64-key cells per block
+    (3000, 128, 12, 128, 2),     # k = 12: slots padded to 16
+    (40000, 128, 20, 64, 1),     # nb 313 (radix, KPL 8), k = 20: slots padded to 32
 ])
 @pytest.mark.parametrize("rule,param", [("cumulative", 0.9), ("topk", 5), ("stat", 1.0)])
 def test_fused_equals_two_launches_and_oracle(N, b, kk, d, Hh, rule, param):

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import dev, host, say
+from gpu_helpers import Guarded, dev, host, say
 from oracle.mask import build_mask as o_build_mask
 
 pytestmark = pytest.mark.gpu
@@ -36,8 +36,13 @@ def _rows(kind: str, R: int, nb: int, rng) -> np.ndarray:
 def _compare(P: np.ndarray, tau: float, rows=None):
     ops = _ops()
     B, Hh, nb, _ = P.shape
-    cnt, idx, msk = ops.build_mask(dev(P), tau, want_mask=True)
+    g = [Guarded((B, Hh, nb), torch.int32), Guarded((B, Hh, nb, nb), torch.int32),
+         Guarded((B, Hh, nb, nb), torch.uint8, fill=171), Guarded((B * Hh * nb,), torch.int32)]
+    cnt, idx, msk, order = ops.build_mask(dev(P), tau, kv_count=g[0].view, kv_idx=g[1].view, mask=g[2].view,
+                                          order=g[3].view)
     torch.cuda.synchronize()
+    assert all(x.intact() for x in g)          # nothing written outside the outputs
+    assert np.array_equal(np.sort(host(order)), np.arange(B * Hh * nb))
     cnt, idx, msk = host(cnt), host(idx), host(msk)
     flatP = P.reshape(-1, nb)
     if rows is None:

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import dev, dev_bf16, host, kept_lists, say, smooth_qkv
+from gpu_helpers import Guarded, dev, dev_bf16, host, kept_lists, say, smooth_qkv
 from oracle.attention import masked_attention
 from oracle.perm import perm_cuboid, perm_gilbert3d
 from oracle.query_prune import anchors_reordered, fill, query_prune, window_anchors
@@ -41,8 +41,12 @@ def _check_prune(q, perm, anc, N, b, r, Hh, blocks=None):
     ops = _ops()
     Npad = -(-N // b) * b
     nb = Npad // b
-    qc, rs, kp = ops.query_prune(dev_bf16(q), dev(perm), dev(anc), Npad, b, r)
+    g = [Guarded((1, Hh, nb), torch.int32), Guarded((1, Hh, nb, b), torch.int32),
+         Guarded((1, Hh, Npad), torch.uint8, fill=171)]
+    qc, rs, kp = ops.query_prune(dev_bf16(q), dev(perm), dev(anc), Npad, b, r, q_count=g[0].view,
+                                 rowsel=g[1].view, keep=g[2].view)
     torch.cuda.synchronize()
+    assert all(x.intact() for x in g)          # nothing written outside the outputs
     qc, rs, kp = host(qc), host(rs), host(kp)
     qr = o_reorder(q, perm, Npad)
     n_ties = 0

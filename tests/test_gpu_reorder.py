@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import dev, dev_bf16, host, say, tiles_to_rows
+from gpu_helpers import Guarded, dev, dev_bf16, host, say, tiles_to_rows
 from oracle.attention import meanpool
 from oracle.perm import perm_gilbert3d
 from oracle.reorder import inverse_reorder as o_inverse
@@ -48,9 +48,12 @@ def test_reorder_rows_and_tiles(case):
     Npad = -(-N // b) * b
     xt = dev_bf16(x) if in_dt == "bf16" else dev(x)
     pt = dev(perm)
-    y = ops.reorder(xt, pt, Npad, b, "rows")
-    yt = ops.reorder(xt, pt, Npad, b, "tiles_t")
+    gy = Guarded((B, Hh, Npad, d), torch.bfloat16)
+    gt = Guarded((B, Hh, Npad // b, d, b), torch.bfloat16)
+    y = ops.reorder(xt, pt, Npad, b, "rows", y=gy.view)
+    yt = ops.reorder(xt, pt, Npad, b, "tiles_t", y=gt.view)
     torch.cuda.synchronize()
+    assert gy.intact() and gt.intact()          # nothing written outside the outputs
     ref = bf16_round(o_reorder(x, perm, Npad))
     assert np.array_equal(host(y), ref)
     assert np.array_equal(_tiles_to_rows(host(yt)), ref)
@@ -68,9 +71,11 @@ def test_reorder_rows_and_tiles(case):
         torch.cuda.synchronize()
         assert np.array_equal(host(y32), o_reorder(x, perm, Npad))
     # inverse: bf16 rows back to token order, bf16 and fp32 outputs
-    back = ops.inverse_reorder(y, pt, N)
+    gb = Guarded((B, N, Hh, d), torch.bfloat16)
+    back = ops.inverse_reorder(y, pt, N, out=gb.view)
     back32 = ops.inverse_reorder(y, pt, N, out_dtype=torch.float32)
     torch.cuda.synchronize()
+    assert gb.intact()
     assert np.array_equal(host(back), bf16_round(x))
     assert np.array_equal(host(back32), o_inverse(ref, perm, N))
 
