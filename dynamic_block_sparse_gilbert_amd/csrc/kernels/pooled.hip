@@ -14,9 +14,11 @@
 //                      from L2 serves all of them (scores into p_imp).
 //   row_softmax_kernel: one wavefront per row, in place.
 // SICS (SPADE notes, scheme generation): per block, || sum_i q_i / |q_i| ||^2.
-//   sics_block_kernel: row norms first (a thread per row), then the
-//                      channel sums of the normalised rows (16-byte loads, eight
-//                      channels per thread), then the square.
+//   sics_block_kernel: one pass over the block's rows, a group of D / 8
+//                      threads per row (16-byte loads, eight channels per
+//                      thread): the row's norm by a butterfly over the group,
+//                      then the channel sums of the normalised rows, then the
+//                      square.
 //   sics_head_kernel:  the head's sum over its blocks in a fixed order.
 #include <cmath>
 
@@ -178,7 +180,6 @@ template <int D>
 __global__ __launch_bounds__(kPoolThreads) void sics_block_kernel(RowSrc q, SicsArgs a) {
   constexpr int kCpr = D / 8;                     // threads per row (8 channels, 16 bytes each)
   constexpr int kGroups = kPoolThreads / kCpr;
-  __shared__ float inv_norm[128];
   __shared__ float red[kGroups][D];
   const int I = blockIdx.x, bh = blockIdx.y, z = blockIdx.z;
   const int bi = bh / a.Hh, hh = bh % a.Hh;
@@ -190,27 +191,20 @@ __global__ __launch_bounds__(kPoolThreads) void sics_block_kernel(RowSrc q, Sics
     q.perm_h_stride = 0;
   }
   float* out = a.sics + (int64_t)z * a.B * a.Hh * a.nb;
-  // row norms, a thread per row
-  if (threadIdx.x < n) {
-    const int64_t off = q.row_off(bi, hh, r0 + threadIdx.x, a.Hh, a.Npad, a.N, D);
-    float ss = 0.f;
-#pragma unroll 4
-    for (int c = 0; c < kCpr; ++c) {
-      float x[8];
-      load8(q.x, off + 8 * c, q.f32, x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
-    }
-    inv_norm[threadIdx.x] = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
-  }
-  __syncthreads();
-  // channel sums of the normalised rows: 8 channels of one row group per thread
+  // One pass over the rows: the kCpr threads of a row group read its 16-byte
+  // chunks together, form the squared norm by a butterfly over those lanes,
+  // and add the normalised chunk to their channel sums.
   const int c0 = (threadIdx.x % kCpr) * 8, grp = threadIdx.x / kCpr;
   float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int r = grp; r < n; r += kGroups) {
     float x[8];
     load8(q.x, q.row_off(bi, hh, r0 + r, a.Hh, a.Npad, a.N, D) + c0, q.f32, x);
-    const float w = inv_norm[r];
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
+#pragma unroll
+    for (int o = kCpr / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    const float w = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) s[e] = __builtin_fmaf(x[e], w, s[e]);
   }
