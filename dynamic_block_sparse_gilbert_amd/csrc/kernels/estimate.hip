@@ -630,9 +630,13 @@ __global__ __launch_bounds__(256) void est_mask_wave_kernel(const float2* __rest
   maskcore::mask_row_wave<KPL>(in, row, sg.nb, rule, flag_all[w], kv_count, kv_idx, mask);
 }
 
-// Rows of 257..4096 blocks: one wavefront per row (four per workgroup); lane l
-// forms entries l * KPL .. l * KPL + KPL - 1 four at a time (pimp_lane's terms,
-// so the same bits) and the row goes to the radix selection.
+// Rows of 257..4096 blocks: one wavefront per row (four per workgroup), in
+// two steps.  First the row's P_imp values are formed with coalesced loads
+// (lane l forms entries 256 g + 4 l .. + 3 of each 256-entry group g, one
+// 16-byte load per sampled query, pimp_value's terms, so the same bits) and
+// parked in the wavefront's LDS area; then lane l takes entries l * KPL ..
+// l * KPL + KPL - 1 from there, the layout of the radix selection, which
+// reuses the same LDS area for its counters.
 template <int KPL>
 __global__ __launch_bounds__(256) void est_mask_radix_kernel(const float2* __restrict__ part,
                                                              const float* __restrict__ tmax, SampleGeom sg, float sl2,
@@ -640,8 +644,9 @@ __global__ __launch_bounds__(256) void est_mask_radix_kernel(const float2* __res
                                                              int32_t* __restrict__ kv_count,
                                                              int32_t* __restrict__ kv_idx,
                                                              uint8_t* __restrict__ mask) {
+  constexpr int kWords = maskcore::RadixArea<KPL>::kWords;
   __shared__ float lse_all[4][kMaxK];
-  __shared__ unsigned long long hist_all[4][512];
+  __shared__ __attribute__((aligned(16))) unsigned long long area_all[4][kWords];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int I = blockIdx.x * 4 + w, bh = blockIdx.y;
   if (I >= sg.nb) return;   // whole wavefronts; no workgroup barrier follows
@@ -651,49 +656,54 @@ __global__ __launch_bounds__(256) void est_mask_radix_kernel(const float2* __res
   __builtin_amdgcn_wave_barrier();
   const int64_t row = (int64_t)bh * sg.nb + I;
   const float* t0 = tmax + ((int64_t)bh * sg.nsp + (int64_t)I * sg.k) * sg.ncell;
+  float* pv = reinterpret_cast<float*>(area_all[w]);
+  float* prow = p_imp != nullptr ? p_imp + row * sg.nb : nullptr;
   const bool vec = sg.ncell == sg.nb && sg.nb % 4 == 0 && ((uintptr_t)tmax & 15u) == 0;
-  uint32_t in[KPL];
-  const int J0 = lane * KPL;
-#pragma unroll
-  for (int r = 0; r < KPL; r += 4) {
-    uint32_t q[4];
-    if (vec) {
-      // a 4-entry group inside the row: one 16-byte load per sampled query
+  if (vec) {
+#pragma unroll 1
+    for (int g = 0; g < KPL / 4; ++g) {
+      const int J = 256 * g + 4 * lane;
+      const bool ok = J < sg.nb;   // nb % 4 == 0: then all four entries are
+      const int Jc = ok ? J : 0;
       float best[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      if (J0 + r < sg.nb) {
-        for (int t0q = 0; t0q < kI; t0q += 16) {
-          float4 vv[16];
+      for (int t0q = 0; t0q < kI; t0q += 16) {
+        float4 vv[16];
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int t = min(t0q + e, kI - 1);
-            vv[e] = *reinterpret_cast<const float4*>(t0 + (int64_t)t * sg.ncell + J0 + r);
-          }
+        for (int e = 0; e < 16; ++e) {
+          const int t = min(t0q + e, kI - 1);
+          vv[e] = *reinterpret_cast<const float4*>(t0 + (int64_t)t * sg.ncell + Jc);
+        }
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const float l = lse[min(t0q + e, kI - 1)];
-            best[0] = fmaxf(best[0], __builtin_fmaf(vv[e].x, sl2, -l));
-            best[1] = fmaxf(best[1], __builtin_fmaf(vv[e].y, sl2, -l));
-            best[2] = fmaxf(best[2], __builtin_fmaf(vv[e].z, sl2, -l));
-            best[3] = fmaxf(best[3], __builtin_fmaf(vv[e].w, sl2, -l));
-          }
+        for (int e = 0; e < 16; ++e) {
+          const float l = lse[min(t0q + e, kI - 1)];
+          best[0] = fmaxf(best[0], __builtin_fmaf(vv[e].x, sl2, -l));
+          best[1] = fmaxf(best[1], __builtin_fmaf(vv[e].y, sl2, -l));
+          best[2] = fmaxf(best[2], __builtin_fmaf(vv[e].z, sl2, -l));
+          best[3] = fmaxf(best[3], __builtin_fmaf(vv[e].w, sl2, -l));
         }
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) q[j] = J0 + r + j < sg.nb ? __float_as_uint(fast_exp2(best[j])) : 0u;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        q[j] = J0 + r + j < sg.nb ? __float_as_uint(pimp_value(lse, t0, sg, kI, J0 + r + j, sl2)) : 0u;
+      float4 pq = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (ok) {
+        pq = make_float4(fast_exp2(best[0]), fast_exp2(best[1]), fast_exp2(best[2]), fast_exp2(best[3]));
+        if (prow != nullptr) *reinterpret_cast<float4*>(prow + J) = pq;
+      }
+      *reinterpret_cast<float4*>(pv + J) = pq;
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) in[r + j] = q[j];
+  } else {
+#pragma unroll 1
+    for (int r = 0; r < KPL; ++r) {
+      const int J = 64 * r + lane;
+      float v = 0.f;
+      if (J < sg.nb) {
+        v = pimp_value(lse, t0, sg, kI, J, sl2);
+        if (prow != nullptr) prow[J] = v;
+      }
+      pv[J] = v;
+    }
   }
-  if (p_imp != nullptr) {
-#pragma unroll
-    for (int r = 0; r < KPL; ++r)
-      if (J0 + r < sg.nb) p_imp[row * sg.nb + J0 + r] = __uint_as_float(in[r]);
-  }
-  maskcore::mask_row_radix<KPL>(in, row, sg.nb, rule, hist_all[w], kv_count, kv_idx, mask);
+  uint32_t in[KPL];
+  maskcore::gather_lane_entries<KPL>(pv, lane, in);
+  maskcore::mask_row_radix<KPL>(in, row, sg.nb, rule, area_all[w], kv_count, kv_idx, mask);
 }
 
 // Key splits: about 768 workgroups in total (one and a half rounds of two

@@ -44,32 +44,39 @@ __global__ __launch_bounds__(256) void build_mask_wave_kernel(
   mask_row_wave<KPL>(in, row, nb, rule, flag_all[w], kv_count, kv_idx, mask);
 }
 
-// Rows of 257..4096 blocks: one wavefront per row (four per workgroup), lane l
-// loading entries l * KPL .. l * KPL + KPL - 1 (16 bytes at a time when the
-// rows are 16-byte aligned), then the radix selection (no sort).
+// Rows of 257..4096 blocks: one wavefront per row (four per workgroup).  The
+// row is read coalesced (16 bytes per lane at 256 g + 4 l when the rows are
+// 16-byte aligned) into the wavefront's LDS area, lane l then takes entries
+// l * KPL .. l * KPL + KPL - 1 from there, and the radix selection runs (no
+// sort), reusing the area for its counters.
 template <int KPL>
 __global__ __launch_bounds__(256) void build_mask_radix_kernel(
     const float* __restrict__ p_imp, int nb, int rows, Rule rule, int32_t* __restrict__ kv_count,
     int32_t* __restrict__ kv_idx, uint8_t* __restrict__ mask) {
-  __shared__ unsigned long long hist_all[4][512];
+  __shared__ __attribute__((aligned(16))) unsigned long long area_all[4][RadixArea<KPL>::kWords];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * 4 + w;
   if (row >= rows) return;   // whole wavefronts; no workgroup barrier follows
-  const uint32_t* prow = reinterpret_cast<const uint32_t*>(p_imp) + row * nb;
-  uint32_t in[KPL];
-  const int j0 = lane * KPL;
+  const float* prow = p_imp + row * nb;
+  float* pv = reinterpret_cast<float*>(area_all[w]);
   if ((nb & 3) == 0 && (((uintptr_t)p_imp) & 15u) == 0) {
 #pragma unroll
-    for (int r = 0; r < KPL; r += 4) {
-      uint4 q = make_uint4(0u, 0u, 0u, 0u);
-      if (j0 + r < nb) q = *reinterpret_cast<const uint4*>(prow + j0 + r);   // nb % 4 == 0: all four valid
-      in[r] = q.x; in[r + 1] = q.y; in[r + 2] = q.z; in[r + 3] = q.w;
+    for (int g = 0; g < KPL / 4; ++g) {
+      const int J = 256 * g + 4 * lane;
+      float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (J < nb) q = *reinterpret_cast<const float4*>(prow + J);   // nb % 4 == 0: all four valid
+      *reinterpret_cast<float4*>(pv + J) = q;
     }
   } else {
 #pragma unroll
-    for (int r = 0; r < KPL; ++r) in[r] = j0 + r < nb ? prow[j0 + r] : 0u;
+    for (int r = 0; r < KPL; ++r) {
+      const int J = 64 * r + lane;
+      pv[J] = J < nb ? prow[J] : 0.f;
+    }
   }
-  mask_row_radix<KPL>(in, row, nb, rule, hist_all[w], kv_count, kv_idx, mask);
+  uint32_t in[KPL];
+  gather_lane_entries<KPL>(pv, lane, in);
+  mask_row_radix<KPL>(in, row, nb, rule, area_all[w], kv_count, kv_idx, mask);
 }
 
 

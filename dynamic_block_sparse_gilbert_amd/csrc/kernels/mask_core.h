@@ -510,6 +510,32 @@ __device__ __forceinline__ uint32_t radix_digit(const uint32_t (&sg)[KPL], const
   return (uint32_t)(255 - 4 * L - (q < 4 ? q : 3));
 }
 
+// LDS area of one wavefront in the radix kernels: first the row's 64 * KPL
+// entries (float32 bits), written coalesced, then the selection's 512 64-bit
+// counters.
+template <int KPL>
+struct RadixArea {
+  static constexpr int kWords = KPL * 64 * 4 > 512 * 8 ? KPL * 32 : 512;   // 64-bit words
+};
+
+// in[r] = row entry lane * KPL + r from the wavefront's LDS area (16-byte
+// reads), after the wavefront wrote every entry there.  The memory clobbers
+// keep the reads after those writes and before the selection reuses the
+// area; LDS operations of one wavefront complete in order.
+template <int KPL>
+__device__ __forceinline__ void gather_lane_entries(const float* pv, int lane, uint32_t (&in)[KPL]) {
+  static_assert(KPL % 4 == 0, "16-byte reads");
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int r = 0; r < KPL; r += 4) {
+    const uint4 q = *reinterpret_cast<const uint4*>(pv + lane * KPL + r);
+    in[r] = q.x; in[r + 1] = q.y; in[r + 2] = q.z; in[r + 3] = q.w;
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+}
+
 // One wavefront, one row: lane l brings the float32 bits of entries
 // l * KPL + r (r < KPL; entries >= nb are ignored).  hist: this wavefront's 512
 // 64-bit LDS counters.  Same result as mask_row_wave (and as a full sort) under the
