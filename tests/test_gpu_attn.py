@@ -96,6 +96,43 @@ def test_attn_lists(N, d, b, kind):
             assert np.isneginf(l[bi, h, :N][empty]).all()
 
 
+def test_attn_max_nb():
+    """The largest list the kernel takes (nb = 4096 blocks, every entry of the LDS list used):
+    short random lists for most query blocks, every block for two of them, a ragged last block;
+    sampled query blocks against the oracle."""
+    say("attn max nb")
+    b, d = 64, 64
+    nb = 4096
+    N = nb * b - 9
+    rng = np.random.default_rng(4096)
+    q, k, v = smooth_qkv(11, 1, N, 1, d)
+    lists = [[sorted(rng.choice(nb, size=int(rng.integers(1, 9)), replace=False).tolist()) for _ in range(nb)]]
+    full = [5, nb - 1]
+    for I in full:
+        lists[0][I] = list(range(nb))
+    lists[0][7] = []
+    cnt, idx = _upload(lists, 1, 1, nb)
+    ops = _ops()
+    perm = dev(np.arange(N, dtype=np.int32))
+    Npad = nb * b
+    q_r = ops.reorder(dev_bf16(q), perm, Npad, b, "rows")
+    k_r = ops.reorder(dev_bf16(k), perm, Npad, b, "rows")
+    v_t = ops.reorder(dev_bf16(v), perm, Npad, b, "tiles_t")
+    scale = 1.0 / math.sqrt(d)
+    o_r, lse = ops.sparse_attn_fwd(q_r, k_r, v_t, N, b, scale, dev(cnt), dev(idx), want_lse=True)
+    torch.cuda.synchronize()
+    o, l = host(o_r), host(lse)
+    blocks = sorted(set(full + [0, 7, 1000, 2047, 3333]))
+    ref, rl = masked_attention(q[0, :, 0], k[0, :, 0], v[0, :, 0], N, b, lists[0], scale, query_blocks=blocks)
+    for I in blocks:
+        rows = np.arange(I * b, min((I + 1) * b, N))
+        if not lists[0][I]:
+            assert (o[0, 0, rows] == 0).all() and np.isneginf(l[0, 0, rows]).all()
+            continue
+        assert np.abs(o[0, 0, rows] - ref[rows]).max() <= TOL, I
+        assert np.abs(l[0, 0, rows] - rl[rows]).max() <= 1e-3, I
+
+
 def test_attn_malformed_lists_are_skipped():
     say("attn malformed")
     N, d, b, B, Hh = 600, 128, 128, 1, 3

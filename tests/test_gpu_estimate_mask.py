@@ -53,6 +53,8 @@ def _inputs(seed, N, Hh, d, B=1):
     (2300, 128, 128, 128, 1),    # k = 128: two 64-key cells per block
     (3000, 128, 12, 128, 2),     # k = 12: slots padded to 16
     (40000, 128, 20, 64, 1),     # nb 313 (radix, KPL 8), k = 20: slots padded to 32
+    (95990, 64, 4, 64, 1),       # nb 1500 (radix, KPL 32), ragged
+    (262139, 64, 2, 64, 1),      # nb 4096, the largest row (radix, KPL 64), ragged
 ])
 @pytest.mark.parametrize("rule,param", [("cumulative", 0.9), ("topk", 5), ("stat", 1.0)])
 def test_fused_equals_two_launches_and_oracle(N, b, kk, d, Hh, rule, param):
