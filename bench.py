@@ -378,7 +378,7 @@ def backward_leg(layer, cfg, qd, vd, steps, warmup, torch):
     executed = 14.0 * sp.d * pairs   # S and dP are computed in both kernels
     return {
         "ms": round(ms, 4),
-        "what": "dbs_transpose_lists + dbs_sparse_attn_bwd (rows -> tiles copies, dQ, dK/dV kernels), "
+        "what": "dbs_transpose_lists + dbs_sparse_attn_bwd (dQ, dK/dV kernels), "
                 "tau %.2f mask of the Wan-shaped layer" % sp.tau,
         "algorithmic_flop": alg,
         "executed_flop": executed,

@@ -13,9 +13,6 @@
 // Launches:
 //   transpose_lists: a bit matrix (query block x key block) per group of 32
 //     key blocks in LDS, read out in ascending query block.
-//   rows_to_tiles (x3): Q, dO and K rows -> transposed b-token tiles (d-major,
-//     tokens in the order the MFMA k index wants, rows >= N zero), the A
-//     operands of the products that contract over tokens.
 //   dq: one workgroup per (batch, head, query block), 32 query rows per
 //     wavefront, over the block's kept key blocks in stages of 32 keys:
 //       S^T = K Q^T, dP^T = V dO^T (Q^T, dO^T in VGPRs), P^T, dS^T in the
@@ -26,14 +23,16 @@
 //     S = Q K^T, dP = dO V^T (K^T, V^T in VGPRs), dV^T += dO^T P,
 //     dK^T += Q^T dS.
 // All products are bf16 MFMA 32x32x16 with fp32 accumulation; P and dS are
-// rounded to bf16 for the second product.  Stage data are copied global -> LDS
-// by the buffer form of the DMA path into row-padded LDS, double-buffered (the
-// copies of stage u + 1 issued right after the barrier that opens stage u),
-// and both kernels are held to 256 VGPRs: two workgroups then share each CU
-// (two wavefronts per SIMD).  64-token stages double-buffered at one
-// wavefront per SIMD (360 VGPRs, 106-145 KiB of LDS) measured 14% slower on
-// the whole backward; 64-token stages single-buffered at two per SIMD ran as
-// fast as these.
+// rounded to bf16 for the second product.  The products that contract over
+// tokens (dV^T += dO^T P, dK^T += Q^T dS, dQ^T += K^T dS^T) take their A
+// operand from the token rows already in LDS by transposing reads
+// (ds_read_b64_tr_b16), so no transposed copy of Q, dO or K is made; the MFMA
+// tile rows map to the stage's token rows through a fixed permutation that
+// keeps both kinds of LDS read free of bank conflicts.  Stage data are copied
+// global -> LDS by the buffer form of the DMA path into row-padded LDS through
+// a ring of two stage buffers (one stage in flight while one computes), and
+// both kernels are held to 256 VGPRs: two workgroups then share each CU (two
+// wavefronts per SIMD).
 #include "common.h"
 #include "../launch.h"
 
@@ -56,6 +55,9 @@ __device__ __forceinline__ float sum_halves(float v) {
 }
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N vector-memory instructions of this wavefront are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -63,12 +65,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ void copy16_lds(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, 0);
 }
-
-// Column of token offset t inside a transposed tile: in every 16 tokens the
-// order 0-3, 8-11, 4-7, 12-15 (bits 2 and 3 exchanged, an involution), which
-// is the order in which a lane's MFMA accumulator rows feed the k index of the
-// next product.
-__device__ __forceinline__ int tile_col(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
 
 // Stage layouts in LDS (KT tokens per stage), each a whole number of 1 KiB
 // copy instructions (a rows stage of 32 tokens leaves a spare half KiB that
@@ -80,10 +76,6 @@ struct BwdCfg {
   static constexpr int kRowStride = kRowU * 16;
   static constexpr int kRowInstr = (KT * kRowU + 63) / 64;
   static constexpr int kRowBytes = kRowInstr * 1024;
-  static constexpr int kTileU = KT / 8 + 1;        // tiles stage: D rows of KT tokens, padded by one unit
-  static constexpr int kTileStride = kTileU * 16;
-  static constexpr int kTileInstr = (D * kTileU + 63) / 64;
-  static constexpr int kTileBytes = kTileInstr * 1024;
 };
 
 // Per-lane source offsets (elements) of the padded copies: LDS byte 1024 n +
@@ -95,8 +87,7 @@ template <int D, int BLK, int W, int KT>
 struct StageCopies {
   using C = BwdCfg<D, KT>;
   static constexpr int kRowPer = (C::kRowInstr + W - 1) / W;
-  static constexpr int kTilePer = (C::kTileInstr + W - 1) / W;
-  uint32_t roff[kRowPer], toff[kTilePer];
+  uint32_t roff[kRowPer];
   int wave, lane;
   __device__ __forceinline__ void init(int w, int l) {
     wave = w;
@@ -108,13 +99,6 @@ struct StageCopies {
       const int row = p / C::kRowU, c = min(p % C::kRowU, C::kRowU - 2);
       roff[i] = (uint32_t)(row * D + c * 8) * 2u;
     }
-#pragma unroll
-    for (int i = 0; i < kTilePer; ++i) {
-      const int n = min(wave + i * W, C::kTileInstr - 1);
-      const int p = 64 * n + lane;
-      const int row = p / C::kTileU, c = min(p % C::kTileU, C::kTileU - 2);
-      toff[i] = (uint32_t)(row * BLK + c * 8) * 2u;
-    }
   }
   __device__ __forceinline__ void rows(__amdgpu_buffer_rsrc_t r, uint32_t soff, char* buf) const {
 #pragma unroll
@@ -123,30 +107,51 @@ struct StageCopies {
       copy16_lds(r, buf + 1024 * n, roff[i], soff);
     }
   }
-  __device__ __forceinline__ void tiles(__amdgpu_buffer_rsrc_t r, uint32_t soff, char* buf) const {
-#pragma unroll
-    for (int i = 0; i < kTilePer; ++i) {
-      const int n = min(wave + i * W, C::kTileInstr - 1);
-      copy16_lds(r, buf + 1024 * n, toff[i], soff);
-    }
-  }
 };
 
-// MFMA operand reads (16 bytes per lane): rows stage, row l32, k step kk
-// (elements 16 kk + 8 g ..); tiles stage, d-row 32 dt + l32, token step st
-// (stored columns 16 st + 8 g ..).
+// Tile row m of the first product of a stage (the MFMA row that lane l32 = m
+// of the A operand feeds, and accumulator row acc_row) is stage row
+// stage_row(m): within each group of 16, m = 8 h + 4 g + e goes to row
+// 4 e + 2 h + g.  The LDS serves 16 lanes of a 16-byte read or 32 lanes of an
+// 8-byte read per cycle from 64 banks; at the padded row stride (an odd
+// number of 16-byte units) the 16 rows of a 16-byte row read start in distinct
+// bank quads, and the 4 rows 4 e + c of a transposing read (64 bytes of each
+// per 32 lanes) start in distinct quarters of the banks, so neither kind of
+// read meets a bank conflict.
+__device__ __forceinline__ int stage_row(int m) { return (m & ~15) | (((m >> 3) & 1) << 1) | ((m >> 2) & 1) | ((m & 3) << 2); }
+__device__ __forceinline__ int tile_row(int r) { return (r & ~15) | (((r >> 1) & 1) << 3) | ((r & 1) << 2) | ((r >> 2) & 3); }
+
+// MFMA operand read (16 bytes per lane): rows stage, tile row l32, k step kk
+// (elements 16 kk + 8 g ..).
 template <class C>
 __device__ __forceinline__ bf16x8_t read_rows(const char* buf, int l32, int g, int kk) {
-  return *reinterpret_cast<const bf16x8_t*>(buf + l32 * C::kRowStride + 16 * g + kk * 32);
+  return *reinterpret_cast<const bf16x8_t*>(buf + stage_row(l32) * C::kRowStride + 16 * g + kk * 32);
 }
+// A operand of a product contracting over the 32 token rows of a rows stage
+// (dO^T, Q^T, K^T): lane (l32, g) receives column 32 dt + l32 of the stage rows
+// of tile rows 16 st + 4 g + e and 16 st + 8 + 4 g + e (e < 4), the k order
+// pack_half gives the B operand.  Two transposing LDS reads (ds_read_b64_tr_b16):
+// in each group of 16 lanes, lane i points at 4 consecutive columns
+// 4 (i & 3) .. of the (i >> 2)-th row of a 4-row set, and lane l receives
+// column l of the set's 4 rows.
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 template <class C>
-__device__ __forceinline__ bf16x8_t read_tiles(const char* buf, int l32, int g, int dt, int st) {
-  return *reinterpret_cast<const bf16x8_t*>(buf + (32 * dt + l32) * C::kTileStride + 16 * g + st * 32);
+__device__ __forceinline__ bf16x8_t read_rows_tr(const char* buf, int lane, int dt, int st) {
+  const int grp = lane >> 4, i = lane & 15;
+  const int row = 16 * st + (grp >> 1) + 4 * (i >> 2);   // stage_row(16 st + 4 g + (i >> 2))
+  const int col = 32 * dt + 16 * (grp & 1) + 4 * (i & 3);
+  const char* p = buf + row * C::kRowStride + 2 * col;
+  const short4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)p);
+  const short4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p + 2 * C::kRowStride));
+  typedef short short8_t __attribute__((ext_vector_type(8)));
+  const short8_t ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, ab);
 }
 
 // B operand of a product contracting over the 32 rows of one accumulator tile
-// T, 16-row step st: the lane's 8 values of that step, in the row order
-// tile_col stores its columns.
+// T, 16-row step st: the lane's 8 values of that step (tile rows 16 st + 4 g + e and
+// 16 st + 8 + 4 g + e, e < 4), the order read_rows_tr gives the A operand.
 __device__ __forceinline__ bf16x8_t pack_half(const f32x16_t& T, int st) {
   const int o = st * 8;
   uint4 w;
@@ -173,37 +178,6 @@ __device__ __forceinline__ void stage_list(const int32_t* __restrict__ idx, int 
   for (int i = threadIdx.x; i < cnt; i += blockDim.x) {
     const int v = idx[i];
     list_s[i] = (v >= 0 && v < nb) ? (uint16_t)v : kNoBlock;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// rows [BH][Npad][D] bf16 -> transposed tiles [BH][nb][D][BLK] (column
-// tile_col(t) holds token J*BLK + t); tokens >= N are zero.  One workgroup per
-// (tile, bh); thread (c, tg) moves 8 tokens x 8 channels through registers.
-template <int D, int BLK>
-__global__ __launch_bounds__((D / 8) * (BLK / 8)) void rows_to_tiles_kernel(const __bf16* __restrict__ x,
-                                                                           __bf16* __restrict__ y, int N,
-                                                                           int Npad, int nb) {
-  const int J = blockIdx.x, bh = blockIdx.y;
-  const int c = threadIdx.x % (D / 8), tg = threadIdx.x / (D / 8);
-  uint32_t w[8][4];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int i = J * BLK + tile_col(8 * tg + e);
-    uint4 o = make_uint4(0, 0, 0, 0);
-    if (i < N) o = *reinterpret_cast<const uint4*>(x + ((int64_t)bh * Npad + i) * D + 8 * c);
-    w[e][0] = o.x; w[e][1] = o.y; w[e][2] = o.z; w[e][3] = o.w;
-  }
-  __bf16* tile = y + ((int64_t)bh * nb + J) * (int64_t)(D * BLK);
-#pragma unroll
-  for (int ch = 0; ch < 8; ++ch) {
-    uint32_t o[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t lo = w[2 * p][ch >> 1], hi = w[2 * p + 1][ch >> 1];
-      o[p] = (ch & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-    }
-    *reinterpret_cast<uint4*>(tile + (int64_t)(8 * c + ch) * BLK + 8 * tg) = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 
@@ -255,25 +229,30 @@ __global__ __launch_bounds__(kTrThreads) void transpose_lists_kernel(const int32
 }
 
 // ---------------------------------------------------------------------------
-// Stages of 32 tokens, double-buffered: the copies of stage u + 1 are issued
-// right after the barrier that opens stage u and land while it computes.
+// Stages of 32 tokens in a ring of kRing buffers: the copies of stage
+// u + kRing - 1 are issued right after the barrier that opens stage u (into the
+// buffers stage u - 1 used), so kRing - 1 stages are in flight while stage u
+// computes.  Stage u waits for its own copies only: every wavefront issues the
+// same number of copies per stage, and vector-memory instructions retire in
+// order.  The buffers are distinct arrays, each named at a fixed position of
+// the kRing-times unrolled loop, so the compiler sees that no LDS read aliases
+// a copy in flight.
 constexpr int kKT = 32;
+constexpr int kRing = 2;
 
 // dQ.  Stage u: list entry u / kSubs, 32-key part u % kSubs.
 template <int D, int BLK>
 __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dq_kernel(
     const __bf16* __restrict__ q_r, const __bf16* __restrict__ k_r, const __bf16* __restrict__ v_r,
     const __bf16* __restrict__ o_r, const __bf16* __restrict__ do_r, const float* __restrict__ lse,
-    const __bf16* __restrict__ k_t, const int32_t* __restrict__ kv_count, const int32_t* __restrict__ kv_idx,
+    const int32_t* __restrict__ kv_count, const int32_t* __restrict__ kv_idx,
     float* __restrict__ dq, float* __restrict__ dbuf, int Hh, int N, int Npad, int nb, float sl2, float scale) {
   using C = BwdCfg<D, kKT>;
   constexpr int W = BLK / 32, kSubs = BLK / kKT;
   __shared__ __attribute__((aligned(1024))) char Ks0[C::kRowBytes];
   __shared__ __attribute__((aligned(1024))) char Vs0[C::kRowBytes];
-  __shared__ __attribute__((aligned(1024))) char Kts0[C::kTileBytes];
   __shared__ __attribute__((aligned(1024))) char Ks1[C::kRowBytes];
   __shared__ __attribute__((aligned(1024))) char Vs1[C::kRowBytes];
-  __shared__ __attribute__((aligned(1024))) char Kts1[C::kTileBytes];
   extern __shared__ uint16_t list_s[];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, g = lane >> 5;
@@ -316,7 +295,6 @@ __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2
   const int32_t* idx = kv_idx + ((int64_t)bh * nb + I) * nb;
   const auto rk = make_rsrc(k_r + rowbase * D, (uint32_t)Npad * (uint32_t)(D * 2));
   const auto rv = make_rsrc(v_r + rowbase * D, (uint32_t)Npad * (uint32_t)(D * 2));
-  const auto rkt = make_rsrc(k_t + rowbase * D, (uint32_t)Npad * (uint32_t)(D * 2));
   StageCopies<D, BLK, W, kKT> cp;
   cp.init(wave, lane);
   stage_list(idx, cnt, nb, list_s);
@@ -325,15 +303,14 @@ __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2
   const int U = cnt * kSubs;
   auto block_of = [&](int u) { return __builtin_amdgcn_readfirstlane((int)list_s[u / kSubs]); };
   // An invalid entry copies block 0 and computes nothing, as the forward skips it.
-  auto issue = [&](int u, char* kb, char* vb, char* tb) {
+  auto issue = [&](int u, char* kb, char* vb) {
     const int J0 = block_of(u), h = u % kSubs;
     const int J = J0 == kNoBlock ? 0 : J0;
     const int key0 = J * BLK + h * kKT;
     cp.rows(rk, (uint32_t)key0 * (uint32_t)(D * 2), kb);
     cp.rows(rv, (uint32_t)key0 * (uint32_t)(D * 2), vb);
-    cp.tiles(rkt, ((uint32_t)J * (uint32_t)(D * BLK) + (uint32_t)(h * kKT)) * 2u, tb);
   };
-  auto compute = [&](int u, const char* kb, const char* vb, const char* tb) {
+  auto compute = [&](int u, const char* kb, const char* vb) {
     const int J = block_of(u), h = u % kSubs;
     if (J == kNoBlock) return;
     const int key0 = J * BLK + h * kKT;
@@ -343,33 +320,39 @@ __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2
       S = mfma(read_rows<C>(kb, l32, g, kk), qreg[kk], S);
       dP = mfma(read_rows<C>(vb, l32, g, kk), doreg[kk], dP);
     }
-    // dS^T = P^T (dP^T - D); keys >= N have P = 0
-    const bool partial = key0 + kKT > N;
+    // dS^T = P^T (dP^T - D); keys >= N have P = 0.  Only a stage that runs
+    // past N takes the masked form (a uniform branch).
+    if (key0 + kKT > N) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      float p = fast_exp2(__builtin_fmaf(S[v], sl2, -lse2));
-      if (partial && key0 + acc_row(v, g) >= N) p = 0.f;
-      S[v] = p * (dP[v] - Dq);
+      for (int v = 0; v < 16; ++v) {
+        float p = fast_exp2(__builtin_fmaf(S[v], sl2, -lse2));
+        if (key0 + stage_row(acc_row(v, g)) >= N) p = 0.f;
+        S[v] = p * (dP[v] - Dq);
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) S[v] = fast_exp2(__builtin_fmaf(S[v], sl2, -lse2)) * (dP[v] - Dq);
     }
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const bf16x8_t bq = pack_half(S, st);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) acc[dt] = mfma(read_tiles<C>(tb, l32, g, dt, st), bq, acc[dt]);
+      for (int dt = 0; dt < D / 32; ++dt) acc[dt] = mfma(read_rows_tr<C>(kb, lane, dt, st), bq, acc[dt]);
     }
   };
-  if (U > 0) issue(0, Ks0, Vs0, Kts0);
-  for (int u = 0; u < U; u += 2) {
-    wait_dma();
+  constexpr int kCps = 2 * StageCopies<D, BLK, W, kKT>::kRowPer;   // copies per stage and wavefront
+  auto stage = [&](int u, const char* kb, const char* vb, char* nk, char* nv) {
+    if (u + kRing - 2 < U) wait_vm<(kRing - 2) * kCps>();
+    else wait_dma();
     __syncthreads();   // stage u landed; every wave is done with stage u - 1's buffers
-    if (u + 1 < U) issue(u + 1, Ks1, Vs1, Kts1);
-    compute(u, Ks0, Vs0, Kts0);
-    if (u + 1 < U) {
-      wait_dma();
-      __syncthreads();
-      if (u + 2 < U) issue(u + 2, Ks0, Vs0, Kts0);
-      compute(u + 1, Ks1, Vs1, Kts1);
-    }
+    if (u + kRing - 1 < U) issue(u + kRing - 1, nk, nv);
+    compute(u, kb, vb);
+  };
+  static_assert(kRing == 2, "the unrolled ring below names two buffers");
+  if (U > 0) issue(0, Ks0, Vs0);
+  for (int u = 0; u < U; u += kRing) {
+    stage(u, Ks0, Vs0, Ks1, Vs1);
+    if (u + 1 < U) stage(u + 1, Ks1, Vs1, Ks0, Vs0);
   }
 
   // lane (l32, g) holds dQ^T rows 32 dt + acc_row(v, g) of query q
@@ -395,20 +378,16 @@ template <int D, int BLK>
 __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dkdv_kernel(
     const __bf16* __restrict__ q_r, const __bf16* __restrict__ k_r, const __bf16* __restrict__ v_r,
     const __bf16* __restrict__ do_r, const float* __restrict__ lse, const float* __restrict__ dbuf,
-    const __bf16* __restrict__ q_t, const __bf16* __restrict__ do_t, const int32_t* __restrict__ kvT_count,
+    const int32_t* __restrict__ kvT_count,
     const int32_t* __restrict__ kvT_idx, float* __restrict__ dk, float* __restrict__ dv, int Hh, int N, int Npad,
     int nb, float sl2, float scale) {
   using C = BwdCfg<D, kKT>;
   constexpr int W = BLK / 32, kSubs = BLK / kKT;
   __shared__ __attribute__((aligned(1024))) char Qs0[C::kRowBytes];
   __shared__ __attribute__((aligned(1024))) char dOs0[C::kRowBytes];
-  __shared__ __attribute__((aligned(1024))) char Qts0[C::kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char dOts0[C::kTileBytes];
   __shared__ __attribute__((aligned(1024))) char Qs1[C::kRowBytes];
   __shared__ __attribute__((aligned(1024))) char dOs1[C::kRowBytes];
-  __shared__ __attribute__((aligned(1024))) char Qts1[C::kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char dOts1[C::kTileBytes];
-  __shared__ __attribute__((aligned(16))) float ld_s[2][2 * kKT];   // per buffer set: lse (log2), then D
+  __shared__ __attribute__((aligned(16))) float ld_s[kRing][2 * kKT];   // per buffer set: lse (log2), then D
   extern __shared__ uint16_t list_s[];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, g = lane >> 5;
@@ -442,8 +421,6 @@ __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2
   const int32_t* idx = kvT_idx + ((int64_t)bh * nb + J) * nb;
   const auto rq = make_rsrc(q_r + rowbase * D, (uint32_t)Npad * (uint32_t)(D * 2));
   const auto rdo = make_rsrc(do_r + rowbase * D, (uint32_t)Npad * (uint32_t)(D * 2));
-  const auto rqt = make_rsrc(q_t + rowbase * D, (uint32_t)Npad * (uint32_t)(D * 2));
-  const auto rdot = make_rsrc(do_t + rowbase * D, (uint32_t)Npad * (uint32_t)(D * 2));
   StageCopies<D, BLK, W, kKT> cp;
   cp.init(wave, lane);
   stage_list(idx, cnt, nb, list_s);
@@ -451,31 +428,28 @@ __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2
 
   const int U = cnt * kSubs;
   auto block_of = [&](int u) { return __builtin_amdgcn_readfirstlane((int)list_s[u / kSubs]); };
-  // The lse / D loads go first: vector loads retire in order, so their LDS
-  // write does not wait for the tile copies issued after them.  An invalid
-  // entry copies block 0 and computes nothing.
-  auto issue = [&](int u, char* qb, char* ob, char* qtb, char* otb, float* ls) {
+  // The stage's lse and D (one query per thread of the first 32) are loaded
+  // into registers with its copies and written to LDS only when the stage
+  // opens, after the wait for its copies, so no wave stalls on them at issue.
+  // An invalid entry copies block 0 and computes nothing.
+  float l_in = 0.f, d_in = 0.f;
+  bool ok_in = false;
+  auto issue = [&](int u, char* qb, char* ob) {
     const int I0 = block_of(u), h = u % kSubs;
     const int I = I0 == kNoBlock ? 0 : I0;
     const int qs0 = I * BLK + h * kKT;
-    float lv = 0.f, dv0 = 0.f;
     if (threadIdx.x < kKT) {
       const int qq = qs0 + threadIdx.x;
-      const bool ok = qq < N;
-      lv = ok ? lse[rowbase + qq] * kLog2e : INFINITY;   // +inf: P = 0 for rows >= N
-      dv0 = ok ? dbuf[rowbase + qq] : 0.f;
+      ok_in = qq < N;
+      if (ok_in) {
+        l_in = lse[rowbase + qq];
+        d_in = dbuf[rowbase + qq];
+      }
     }
     cp.rows(rq, (uint32_t)qs0 * (uint32_t)(D * 2), qb);
     cp.rows(rdo, (uint32_t)qs0 * (uint32_t)(D * 2), ob);
-    const uint32_t toffs = ((uint32_t)I * (uint32_t)(D * BLK) + (uint32_t)(h * kKT)) * 2u;
-    cp.tiles(rqt, toffs, qtb);
-    cp.tiles(rdot, toffs, otb);
-    if (threadIdx.x < kKT) {
-      ls[threadIdx.x] = lv;
-      ls[kKT + threadIdx.x] = dv0;
-    }
   };
-  auto compute = [&](int u, const char* qb, const char* ob, const char* qtb, const char* otb, const float* ls) {
+  auto compute = [&](int u, const char* qb, const char* ob, const float* ls) {
     const int I = block_of(u);
     if (I == kNoBlock) return;
     f32x16_t S = f32x16_t{}, dP = f32x16_t{};
@@ -484,7 +458,7 @@ __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2
       S = mfma(read_rows<C>(qb, l32, g, kk), kreg[kk], S);
       dP = mfma(read_rows<C>(ob, l32, g, kk), vreg[kk], dP);
     }
-    // rows of S are queries acc_row(v, g): lse and D from LDS, 4 at a time
+    // rows of S are tile rows acc_row(v, g): lse and D from LDS, 4 at a time
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const int r0 = 8 * a + 4 * g;
@@ -505,23 +479,29 @@ __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2
       const bf16x8_t bp = pack_half(S, st), bs = pack_half(dP, st);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        dva[dt] = mfma(read_tiles<C>(otb, l32, g, dt, st), bp, dva[dt]);
-        dka[dt] = mfma(read_tiles<C>(qtb, l32, g, dt, st), bs, dka[dt]);
+        dva[dt] = mfma(read_rows_tr<C>(ob, lane, dt, st), bp, dva[dt]);
+        dka[dt] = mfma(read_rows_tr<C>(qb, lane, dt, st), bs, dka[dt]);
       }
     }
   };
-  if (U > 0) issue(0, Qs0, dOs0, Qts0, dOts0, ld_s[0]);
-  for (int u = 0; u < U; u += 2) {
+  // With one stage in flight, the wait that opens stage u covers its lse / D
+  // loads (issued before its copies) as well as its copies.
+  static_assert(kRing == 2, "the lse / D registers and the unrolled ring below hold one stage in flight");
+  auto stage = [&](int u, const char* qb, const char* ob, float* ls, char* nq, char* no) {
     wait_dma();
-    __syncthreads();   // stage u landed (its lse / D too); stage u - 1's buffers are free
-    if (u + 1 < U) issue(u + 1, Qs1, dOs1, Qts1, dOts1, ld_s[1]);
-    compute(u, Qs0, dOs0, Qts0, dOts0, ld_s[0]);
-    if (u + 1 < U) {
-      wait_dma();
-      __syncthreads();
-      if (u + 2 < U) issue(u + 2, Qs0, dOs0, Qts0, dOts0, ld_s[0]);
-      compute(u + 1, Qs1, dOs1, Qts1, dOts1, ld_s[1]);
+    if (threadIdx.x < kKT) {   // at its tile row, the order of the accumulator rows
+      const int m = tile_row(threadIdx.x);
+      ls[m] = ok_in ? l_in * kLog2e : INFINITY;   // +inf: P = 0 for rows >= N
+      ls[kKT + m] = ok_in ? d_in : 0.f;
     }
+    __syncthreads();   // stage u landed, its lse / D are in LDS; stage u - 1's buffers are free
+    if (u + 1 < U) issue(u + 1, nq, no);
+    compute(u, qb, ob, ls);
+  };
+  if (U > 0) issue(0, Qs0, dOs0);
+  for (int u = 0; u < U; u += kRing) {
+    stage(u, Qs0, dOs0, ld_s[0], Qs1, dOs1);
+    if (u + 1 < U) stage(u + 1, Qs1, dOs1, ld_s[1], Qs0, dOs0);
   }
 
   // lane (l32, g) holds rows 32 dt + acc_row(v, g) of dK^T, dV^T for its key
@@ -547,42 +527,27 @@ __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2
 template <int D, int BLK>
 hipError_t launch_bwd_db(const AttnBwdArgs& a) {
   const int BH = a.B * a.Hh;
-  const int64_t elems = (int64_t)BH * a.Npad * D;
-  __bf16* kt = reinterpret_cast<__bf16*>(a.workspace);
-  __bf16* qt = kt + elems;
-  __bf16* dot = qt + elems;
-  float* dbuf = reinterpret_cast<float*>(dot + elems);
-  const dim3 tgrid((unsigned)a.nb, (unsigned)BH);
-  const dim3 tblock((D / 8) * (BLK / 8));
-  hipLaunchKernelGGL((rows_to_tiles_kernel<D, BLK>), tgrid, tblock, 0, a.stream, (const __bf16*)a.k_r, kt, a.N,
-                     a.Npad, a.nb);
-  hipLaunchKernelGGL((rows_to_tiles_kernel<D, BLK>), tgrid, tblock, 0, a.stream, (const __bf16*)a.q_r, qt, a.N,
-                     a.Npad, a.nb);
-  hipLaunchKernelGGL((rows_to_tiles_kernel<D, BLK>), tgrid, tblock, 0, a.stream, (const __bf16*)a.do_r, dot, a.N,
-                     a.Npad, a.nb);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  float* dbuf = reinterpret_cast<float*>(a.workspace);
   const float sl2 = a.scale * kLog2e;
   const unsigned grid = (unsigned)(BH * a.nb);
   const size_t list_bytes = ((size_t)a.nb * 2 + 15) / 16 * 16;
   hipLaunchKernelGGL((attn_bwd_dq_kernel<D, BLK>), dim3(grid), dim3(BLK / 32 * 64), list_bytes, a.stream,
                      (const __bf16*)a.q_r, (const __bf16*)a.k_r, (const __bf16*)a.v_r, (const __bf16*)a.o_r,
-                     (const __bf16*)a.do_r, a.lse, (const __bf16*)kt, a.kv_count, a.kv_idx, a.dq, dbuf, a.Hh, a.N,
-                     a.Npad, a.nb, sl2, a.scale);
-  e = hipGetLastError();
+                     (const __bf16*)a.do_r, a.lse, a.kv_count, a.kv_idx, a.dq, dbuf, a.Hh, a.N, a.Npad, a.nb, sl2,
+                     a.scale);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, BLK>), dim3(grid), dim3(BLK / 32 * 64), list_bytes, a.stream,
                      (const __bf16*)a.q_r, (const __bf16*)a.k_r, (const __bf16*)a.v_r, (const __bf16*)a.do_r, a.lse,
-                     (const float*)dbuf, (const __bf16*)qt, (const __bf16*)dot, a.kvT_count, a.kvT_idx, a.dk, a.dv,
-                     a.Hh, a.N, a.Npad, a.nb, sl2, a.scale);
+                     (const float*)dbuf, a.kvT_count, a.kvT_idx, a.dk, a.dv, a.Hh, a.N, a.Npad, a.nb, sl2, a.scale);
   return hipGetLastError();
 }
 
 }  // namespace
 
 size_t attn_bwd_workspace_bytes(int B, int Hh, int Npad, int d) {
-  const int64_t rows = (int64_t)B * Hh * Npad;
-  return (size_t)(3 * rows * d * 2 + rows * 4);
+  (void)d;
+  return (size_t)((int64_t)B * Hh * Npad * 4);   // D = rowsum(dO o O) per row
 }
 
 hipError_t launch_transpose_lists(const TransposeListsArgs& a) {

@@ -496,9 +496,8 @@ dbs_status dbs_sparse_attn_fwd_tok(const void* q, dbs_dtype q_dt, int64_t qsb, i
 dbs_status dbs_transpose_lists(const int32_t* kv_count, const int32_t* kv_idx, int B, int Hh, int nb,
                                int32_t* kvT_count, int32_t* kvT_idx, hipStream_t stream);
 
-/* Bytes of device workspace dbs_sparse_attn_bwd needs: transposed-tile copies
- * of Q, dO and K (3 * B * Hh * Npad * d bf16) and D = rowsum(dO * O)
- * (B * Hh * Npad float).  0 for invalid sizes. */
+/* Bytes of device workspace dbs_sparse_attn_bwd needs: D = rowsum(dO * O),
+ * one float per row (B * Hh * Npad floats).  0 for invalid sizes. */
 size_t dbs_attn_bwd_workspace_bytes(int B, int Hh, int Npad, int d);
 
 /* Gradients of dbs_sparse_attn_fwd without global tokens:

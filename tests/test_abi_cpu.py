@@ -267,7 +267,7 @@ def test_backward_validation(dbs):
     assert t(0, A, 1, 2, 16, A, A, None) == -1           # NULL
     assert t(A, A, 1, 2, 4097, A, A, None) == -2         # nb > 4096
     assert t(A + 2, A, 1, 2, 16, A, A, None) == -3       # misaligned
-    assert L.lib().dbs_attn_bwd_workspace_bytes(1, 2, 256, 128) == 3 * 2 * 256 * 128 * 2 + 2 * 256 * 4
+    assert L.lib().dbs_attn_bwd_workspace_bytes(1, 2, 256, 128) == 2 * 256 * 4      # D, one float per row
     assert L.lib().dbs_attn_bwd_workspace_bytes(1, 2, 256, 96) == 0
     f = L.lib().dbs_sparse_attn_bwd
     ws = L.lib().dbs_attn_bwd_workspace_bytes(1, 2, 1024, 128)
