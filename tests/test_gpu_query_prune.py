@@ -37,13 +37,15 @@ def _setup(T, H, W, Hh, d, b, order, win, seed, cub=(4, 4, 4)):
     return N, q, k, v, perm.astype(np.int32), anc.astype(np.int32)
 
 
-def _check_prune(q, perm, anc, N, b, r, Hh, blocks=None):
+def _check_prune(q, perm, anc, N, b, r, Hh, blocks=None, q_in=None):
+    """q_in: the device input (default: q as bf16); q is what the oracle reads."""
     ops = _ops()
     Npad = -(-N // b) * b
     nb = Npad // b
     g = [Guarded((1, Hh, nb), torch.int32), Guarded((1, Hh, nb, b), torch.int32),
          Guarded((1, Hh, Npad), torch.uint8, fill=171)]
-    qc, rs, kp = ops.query_prune(dev_bf16(q), dev(perm), dev(anc), Npad, b, r, q_count=g[0].view,
+    qc, rs, kp = ops.query_prune(dev_bf16(q) if q_in is None else q_in, dev(perm), dev(anc), Npad, b, r,
+                                 q_count=g[0].view,
                                  rowsel=g[1].view, keep=g[2].view)
     torch.cuda.synchronize()
     assert all(x.intact() for x in g)          # nothing written outside the outputs
@@ -76,6 +78,21 @@ def test_prune_bit_exact(T, H, W, Hh, d, b, order, win, r):
     say("query_prune", T, H, W, Hh, d, b, order, win, r)
     N, q, _, _, perm, anc = _setup(T, H, W, Hh, d, b, order, win, T * H + W)
     ties = _check_prune(q, perm, anc, N, b, r, Hh)
+    assert ties <= max(1, (-(-N // b)) * Hh // 8)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_prune_float32_input(d):
+    """A float32 Q is rounded to bf16 (nearest even) before the dissimilarities, as the attention
+    reads it: values within a quarter bf16 ulp of the oracle's bf16 Q give its selection."""
+    T, H, W, Hh, b = 5, 12, 20, 2, 128
+    say("query_prune float32", T, H, W, Hh, d, b)
+    N, q, _, _, perm, anc = _setup(T, H, W, Hh, d, b, "gilbert", (1, 2, 2), 17)
+    rng = np.random.default_rng(5)
+    q32 = (q + q * rng.uniform(-2.0 ** -11, 2.0 ** -11, q.shape)).astype(np.float32)
+    assert not np.array_equal(q32, q)
+    assert np.array_equal(torch.from_numpy(q32).to(torch.bfloat16).float().numpy(), q)   # rounds back to q
+    ties = _check_prune(q, perm, anc, N, b, 0.5, Hh, q_in=dev(q32))
     assert ties <= max(1, (-(-N // b)) * Hh // 8)
 
 
