@@ -14,14 +14,16 @@
 //   transpose_lists: a bit matrix (query block x key block) per group of 32
 //     key blocks in LDS, read out in ascending query block.
 //   dq: one workgroup per (batch, head, query block), 32 query rows per
-//     wavefront, over the block's kept key blocks in stages of 32 keys:
+//     wavefront, over the block's kept key blocks in tiles of 32 keys:
 //       S^T = K Q^T, dP^T = V dO^T (Q^T, dO^T in VGPRs), P^T, dS^T in the
 //       lane's registers (each lane holds one query: lse and D are scalars),
 //       dQ^T += K^T dS^T.  It also writes D for the next launch.
 //   dkdv: one workgroup per (batch, head, key block), 32 keys per wavefront,
-//     over the query blocks that keep it, in stages of 32 queries:
+//     over the query blocks that keep it, in tiles of 32 queries:
 //     S = Q K^T, dP = dO V^T (K^T, V^T in VGPRs), dV^T += dO^T P,
 //     dK^T += Q^T dS.
+// A stage (the tokens copied between two barriers) holds two tiles in a
+// 128-row workgroup and one in a 64-row workgroup.
 // All products are bf16 MFMA 32x32x16 with fp32 accumulation; P and dS are
 // rounded to bf16 for the second product.  The products that contract over
 // tokens (dV^T += dO^T P, dK^T += Q^T dS, dQ^T += K^T dS^T) take their A
@@ -239,16 +241,18 @@ __global__ __launch_bounds__(kTrThreads) void transpose_lists_kernel(const int32
 // a copy in flight.
 constexpr int kKT = 32;
 constexpr int kRing = 2;
+constexpr int kDqKT = 64;   // dQ stages of 128-row workgroups: two 32-key tiles per barrier
 
-// dQ.  Stage u: list entry u / kSubs, 32-key part u % kSubs.
+// dQ.  Stage u: list entry u / kSubs, KT-key part u % kSubs, as 32-key tiles.
 template <int D, int BLK>
 __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dq_kernel(
     const __bf16* __restrict__ q_r, const __bf16* __restrict__ k_r, const __bf16* __restrict__ v_r,
     const __bf16* __restrict__ o_r, const __bf16* __restrict__ do_r, const float* __restrict__ lse,
     const int32_t* __restrict__ kv_count, const int32_t* __restrict__ kv_idx,
     float* __restrict__ dq, float* __restrict__ dbuf, int Hh, int N, int Npad, int nb, float sl2, float scale) {
-  using C = BwdCfg<D, kKT>;
-  constexpr int W = BLK / 32, kSubs = BLK / kKT;
+  constexpr int KT = BLK >= 128 ? kDqKT : kKT;   // 64-row workgroups keep 32-key stages (copy offsets)
+  using C = BwdCfg<D, KT>;
+  constexpr int W = BLK / 32, kSubs = BLK / KT;
   __shared__ __attribute__((aligned(1024))) char Ks0[C::kRowBytes];
   __shared__ __attribute__((aligned(1024))) char Vs0[C::kRowBytes];
   __shared__ __attribute__((aligned(1024))) char Ks1[C::kRowBytes];
@@ -295,7 +299,7 @@ __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2
   const int32_t* idx = kv_idx + ((int64_t)bh * nb + I) * nb;
   const auto rk = make_rsrc(k_r + rowbase * D, (uint32_t)Npad * (uint32_t)(D * 2));
   const auto rv = make_rsrc(v_r + rowbase * D, (uint32_t)Npad * (uint32_t)(D * 2));
-  StageCopies<D, BLK, W, kKT> cp;
+  StageCopies<D, BLK, W, KT> cp;
   cp.init(wave, lane);
   stage_list(idx, cnt, nb, list_s);
   __syncthreads();
@@ -306,23 +310,27 @@ __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2
   auto issue = [&](int u, char* kb, char* vb) {
     const int J0 = block_of(u), h = u % kSubs;
     const int J = J0 == kNoBlock ? 0 : J0;
-    const int key0 = J * BLK + h * kKT;
+    const int key0 = J * BLK + h * KT;
     cp.rows(rk, (uint32_t)key0 * (uint32_t)(D * 2), kb);
     cp.rows(rv, (uint32_t)key0 * (uint32_t)(D * 2), vb);
   };
-  auto compute = [&](int u, const char* kb, const char* vb) {
+  auto compute = [&](int u, const char* kb_stage, const char* vb_stage) {
     const int J = block_of(u), h = u % kSubs;
     if (J == kNoBlock) return;
-    const int key0 = J * BLK + h * kKT;
+#pragma unroll
+    for (int t = 0; t < KT / 32; ++t) {
+    const char* kb = kb_stage + 32 * t * C::kRowStride;
+    const char* vb = vb_stage + 32 * t * C::kRowStride;
+    const int key0 = J * BLK + h * KT + 32 * t;
     f32x16_t S = f32x16_t{}, dP = f32x16_t{};
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       S = mfma(read_rows<C>(kb, l32, g, kk), qreg[kk], S);
       dP = mfma(read_rows<C>(vb, l32, g, kk), doreg[kk], dP);
     }
-    // dS^T = P^T (dP^T - D); keys >= N have P = 0.  Only a stage that runs
+    // dS^T = P^T (dP^T - D); keys >= N have P = 0.  Only a tile that runs
     // past N takes the masked form (a uniform branch).
-    if (key0 + kKT > N) {
+    if (key0 + 32 > N) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         float p = fast_exp2(__builtin_fmaf(S[v], sl2, -lse2));
@@ -339,8 +347,9 @@ __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) acc[dt] = mfma(read_rows_tr<C>(kb, lane, dt, st), bq, acc[dt]);
     }
+    }
   };
-  constexpr int kCps = 2 * StageCopies<D, BLK, W, kKT>::kRowPer;   // copies per stage and wavefront
+  constexpr int kCps = 2 * StageCopies<D, BLK, W, KT>::kRowPer;   // copies per stage and wavefront
   auto stage = [&](int u, const char* kb, const char* vb, char* nk, char* nv) {
     if (u + kRing - 2 < U) wait_vm<(kRing - 2) * kCps>();
     else wait_dma();
@@ -372,8 +381,9 @@ __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV.  Stage u of the key block's query list: entry u / kSubs, 32-query
-// part u % kSubs.
+// dK, dV.  Stage u of the key block's query list: entry u / kSubs, KT-query
+// part u % kSubs, as 32-query tiles computed one after the other (the score
+// registers serve both).
 template <int D, int BLK>
 __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dkdv_kernel(
     const __bf16* __restrict__ q_r, const __bf16* __restrict__ k_r, const __bf16* __restrict__ v_r,
@@ -381,13 +391,14 @@ __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2
     const int32_t* __restrict__ kvT_count,
     const int32_t* __restrict__ kvT_idx, float* __restrict__ dk, float* __restrict__ dv, int Hh, int N, int Npad,
     int nb, float sl2, float scale) {
-  using C = BwdCfg<D, kKT>;
-  constexpr int W = BLK / 32, kSubs = BLK / kKT;
+  constexpr int KT = BLK >= 128 ? kDqKT : kKT;   // as dQ
+  using C = BwdCfg<D, KT>;
+  constexpr int W = BLK / 32, kSubs = BLK / KT;
   __shared__ __attribute__((aligned(1024))) char Qs0[C::kRowBytes];
   __shared__ __attribute__((aligned(1024))) char dOs0[C::kRowBytes];
   __shared__ __attribute__((aligned(1024))) char Qs1[C::kRowBytes];
   __shared__ __attribute__((aligned(1024))) char dOs1[C::kRowBytes];
-  __shared__ __attribute__((aligned(16))) float ld_s[kRing][2 * kKT];   // per buffer set: lse (log2), then D
+  __shared__ __attribute__((aligned(16))) float ld_s[kRing][2 * KT];   // per buffer set: lse (log2), then D
   extern __shared__ uint16_t list_s[];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, g = lane >> 5;
@@ -421,14 +432,14 @@ __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2
   const int32_t* idx = kvT_idx + ((int64_t)bh * nb + J) * nb;
   const auto rq = make_rsrc(q_r + rowbase * D, (uint32_t)Npad * (uint32_t)(D * 2));
   const auto rdo = make_rsrc(do_r + rowbase * D, (uint32_t)Npad * (uint32_t)(D * 2));
-  StageCopies<D, BLK, W, kKT> cp;
+  StageCopies<D, BLK, W, KT> cp;
   cp.init(wave, lane);
   stage_list(idx, cnt, nb, list_s);
   __syncthreads();
 
   const int U = cnt * kSubs;
   auto block_of = [&](int u) { return __builtin_amdgcn_readfirstlane((int)list_s[u / kSubs]); };
-  // The stage's lse and D (one query per thread of the first 32) are loaded
+  // The stage's lse and D (one query per thread of the first KT) are loaded
   // into registers with its copies and written to LDS only when the stage
   // opens, after the wait for its copies, so no wave stalls on them at issue.
   // An invalid entry copies block 0 and computes nothing.
@@ -437,8 +448,8 @@ __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2
   auto issue = [&](int u, char* qb, char* ob) {
     const int I0 = block_of(u), h = u % kSubs;
     const int I = I0 == kNoBlock ? 0 : I0;
-    const int qs0 = I * BLK + h * kKT;
-    if (threadIdx.x < kKT) {
+    const int qs0 = I * BLK + h * KT;
+    if (threadIdx.x < KT) {
       const int qq = qs0 + threadIdx.x;
       ok_in = qq < N;
       if (ok_in) {
@@ -449,9 +460,14 @@ __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2
     cp.rows(rq, (uint32_t)qs0 * (uint32_t)(D * 2), qb);
     cp.rows(rdo, (uint32_t)qs0 * (uint32_t)(D * 2), ob);
   };
-  auto compute = [&](int u, const char* qb, const char* ob, const float* ls) {
+  auto compute = [&](int u, const char* qb_stage, const char* ob_stage, const float* ls_stage) {
     const int I = block_of(u);
     if (I == kNoBlock) return;
+#pragma unroll
+    for (int t = 0; t < KT / 32; ++t) {
+    const char* qb = qb_stage + 32 * t * C::kRowStride;
+    const char* ob = ob_stage + 32 * t * C::kRowStride;
+    const float* ls = ls_stage + 32 * t;   // lse of the tile; its D at ls + KT
     f32x16_t S = f32x16_t{}, dP = f32x16_t{};
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
@@ -463,7 +479,7 @@ __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2
     for (int a = 0; a < 4; ++a) {
       const int r0 = 8 * a + 4 * g;
       const float4 l4 = *reinterpret_cast<const float4*>(ls + r0);
-      const float4 d4 = *reinterpret_cast<const float4*>(ls + kKT + r0);
+      const float4 d4 = *reinterpret_cast<const float4*>(ls + KT + r0);
       const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
       const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
@@ -483,16 +499,17 @@ __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2
         dka[dt] = mfma(read_rows_tr<C>(qb, lane, dt, st), bs, dka[dt]);
       }
     }
+    }
   };
   // With one stage in flight, the wait that opens stage u covers its lse / D
   // loads (issued before its copies) as well as its copies.
   static_assert(kRing == 2, "the lse / D registers and the unrolled ring below hold one stage in flight");
   auto stage = [&](int u, const char* qb, const char* ob, float* ls, char* nq, char* no) {
     wait_dma();
-    if (threadIdx.x < kKT) {   // at its tile row, the order of the accumulator rows
-      const int m = tile_row(threadIdx.x);
+    if (threadIdx.x < KT) {   // at its tile row, the order of the accumulator rows
+      const int m = (threadIdx.x & ~31) | tile_row(threadIdx.x & 31);
       ls[m] = ok_in ? l_in * kLog2e : INFINITY;   // +inf: P = 0 for rows >= N
-      ls[kKT + m] = ok_in ? d_in : 0.f;
+      ls[KT + m] = ok_in ? d_in : 0.f;
     }
     __syncthreads();   // stage u landed, its lse / D are in LDS; stage u - 1's buffers are free
     if (u + 1 < U) issue(u + 1, nq, no);
