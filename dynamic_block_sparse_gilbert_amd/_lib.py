@@ -64,6 +64,9 @@ SIGNATURES = {
                                    C.c_double, _vp, _vp, _vp, _vp, _vp, _vp, C.c_size_t, _vp]),
     "dbs_estimate_mask_tok_noalloc": (_i, [_vp, _i, _i64, _i64, _i64, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
                                            _i, C.c_double, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "dbs_estimate_kvtok_workspace_bytes": (C.c_size_t, [_i, _i, _i, _i, _i, _i]),
+    "dbs_estimate_mask_kvtok": (_i, [_vp, _i, _i64, _i64, _i64, _vp, _i, _i64, _i64, _i64, _vp, _i, _i, _i, _i, _i,
+                                     _i, _i, _i, _f, _i, C.c_double, _vp, _vp, _vp, _vp, _vp, _vp, C.c_size_t, _vp]),
     "dbs_meanpool_kv": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
     "dbs_sparse_attn_fwd": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _vp, _vp,
                                  _i, _i, _vp, _vp, _vp]),

@@ -280,6 +280,12 @@ size_t dbs_estimate_workspace_bytes(int B, int Hh, int N, int d, int b, int k) {
   return dbs::estimate_workspace_bytes(B, Hh, nb, k, d);
 }
 
+size_t dbs_estimate_kvtok_workspace_bytes(int B, int Hh, int N, int d, int b, int k) {
+  if (B < 1 || Hh < 1 || N < 1 || b < 1 || k < 1 || (d != 64 && d != 128)) return 0;
+  const int nb = (N + b - 1) / b;
+  return dbs::estimate_kvtok_workspace_bytes(B, Hh, nb, k, d);
+}
+
 }  // extern "C"
 
 namespace {
@@ -351,17 +357,28 @@ dbs_status estimate_f32_impl(const void* q_r, const void* k_r, int B, int Hh, in
   return from_hip(dbs::launch_build_mask(m), "dbs_estimate_mask launch");
 }
 
+// The token-order K of dbs_estimate_mask_kvtok (element (b, i, h, :) at
+// b * sb + i * sn + h * sh); unset for the calls that read k_r.
+struct KeyTok {
+  const void* k = nullptr;
+  int f32 = 0;
+  int64_t sb = 0, sn = 0, sh = 0;
+};
+
 // fuse set: P_imp rows go straight into the block selection (p_imp nullable).
+// key.k set: K is read in token order (tok.perm) and k_r is not used.
 dbs_status estimate_impl(const void* q_r, const void* k_r, int B, int Hh, int N, int Npad, int d, int b, int k,
                          float scale, float* p_imp, void* workspace, size_t workspace_bytes,
-                         const dbs::TokIO& tok, hipStream_t stream, const dbs::MaskArgs* fuse = nullptr) {
-  REQUIRE(k_r && (p_imp || fuse) && workspace, DBS_ERR_INVALID_ARG, "NULL pointer");
+                         const dbs::TokIO& tok, hipStream_t stream, const dbs::MaskArgs* fuse = nullptr,
+                         const KeyTok& key = KeyTok{}) {
+  REQUIRE((k_r || key.k) && (p_imp || fuse) && workspace, DBS_ERR_INVALID_ARG, "NULL pointer");
   REQUIRE(aligned16(k_r) && aligned16(p_imp) && aligned16(workspace), DBS_ERR_ALIGNMENT, "misaligned pointer");
   dbs_status st = check_geometry(B, Hh, N, Npad, d, b);
   if (st != DBS_OK) return st;
   REQUIRE(k >= 1 && k <= b, DBS_ERR_INVALID_ARG, "k=%d must be in [1, b=%d]", k, b);
   REQUIRE(std::isfinite(scale) && scale > 0.f, DBS_ERR_INVALID_ARG, "scale must be finite and > 0");
-  const size_t need = dbs_estimate_workspace_bytes(B, Hh, N, d, b, k);
+  const size_t need = key.k ? dbs_estimate_kvtok_workspace_bytes(B, Hh, N, d, b, k)
+                            : dbs_estimate_workspace_bytes(B, Hh, N, d, b, k);
   REQUIRE(workspace_bytes >= need, DBS_ERR_INVALID_ARG, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   const int nb = Npad / b;
   REQUIRE((int64_t)nb * k <= INT32_MAX / 2, DBS_ERR_INVALID_ARG, "too many sampled tokens");
@@ -369,6 +386,7 @@ dbs_status estimate_impl(const void* q_r, const void* k_r, int B, int Hh, int N,
   a.q_r = q_r; a.k_r = k_r; a.p_imp = p_imp; a.workspace = workspace;
   a.B = B; a.Hh = Hh; a.N = N; a.Npad = Npad; a.d = d; a.b = b; a.k = k; a.nb = nb;
   a.scale = scale; a.tok = tok; a.stream = stream;
+  a.k_tok = key.k; a.k_f32 = key.f32; a.ksb = key.sb; a.ksn = key.sn; a.ksh = key.sh;
   if (fuse != nullptr) {
     REQUIRE(nb <= 4096, DBS_ERR_UNSUPPORTED, "nb=%d must be in [1, 4096]", nb);
     REQUIRE((int64_t)B * Hh * nb <= INT32_MAX, DBS_ERR_INVALID_ARG, "too many rows");
@@ -458,6 +476,30 @@ dbs_status dbs_estimate_mask_tok(const void* q, dbs_dtype q_dt, int64_t sb, int6
   tok.perm = perm; tok.perm_h_stride = perm_per_head ? N : 0;
   return estimate_impl(nullptr, k_r, B, Hh, N, Npad, d, b, k, scale, p_imp, workspace, workspace_bytes, tok,
                        stream, &m);
+  DBS_GUARD_END
+}
+
+dbs_status dbs_estimate_mask_kvtok(const void* q, dbs_dtype q_dt, int64_t qsb, int64_t qsn, int64_t qsh,
+                                   const void* key, dbs_dtype key_dt, int64_t ksb, int64_t ksn, int64_t ksh,
+                                   const int32_t* perm, int perm_per_head, int B, int Hh, int N, int Npad, int d,
+                                   int b, int k, float scale, int rule, double param, float* p_imp,
+                                   int32_t* kv_count, int32_t* kv_idx, uint8_t* mask, int32_t* order,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  DBS_GUARD_BEGIN
+  dbs_status st = check_tok(q, q_dt, qsb, qsn, qsh, perm, perm_per_head);
+  if (st != DBS_OK) return st;
+  st = check_tok(key, key_dt, ksb, ksn, ksh, perm, perm_per_head);
+  if (st != DBS_OK) return st;
+  dbs::MaskArgs m{};
+  st = fuse_args(rule, param, kv_count, kv_idx, mask, order, Npad, b, m);
+  if (st != DBS_OK) return st;
+  dbs::TokIO tok{};
+  tok.q = q; tok.q_f32 = q_dt == DBS_FP32; tok.qsb = qsb; tok.qsn = qsn; tok.qsh = qsh;
+  tok.perm = perm; tok.perm_h_stride = perm_per_head ? N : 0;
+  KeyTok kt;
+  kt.k = key; kt.f32 = key_dt == DBS_FP32; kt.sb = ksb; kt.sn = ksn; kt.sh = ksh;
+  return estimate_impl(nullptr, nullptr, B, Hh, N, Npad, d, b, k, scale, p_imp, workspace, workspace_bytes, tok,
+                       stream, &m, kt);
   DBS_GUARD_END
 }
 

@@ -55,6 +55,7 @@ struct SampleGeom {
   int splits, cps;   // key splits and 64-key chunks per split
   int cell_log2;     // block maxima are kept per cell of min(k, 64) compact keys
   int ncell;         // cells per sampled query: nsp >> cell_log2
+  int compact;       // the pass reads K from the gathered slot rows (row r = slot r), not k_r
   // Reordered row of compact slot r, or -1 for an empty slot / r >= nsp.
   __device__ __forceinline__ int row(int r) const {
     if (r >= nsp) return -1;
@@ -250,8 +251,11 @@ __global__ __launch_bounds__(kThreads) void est_pass_kernel(
   // lane, i.e. key row p / kRowU of the chunk, unit p % kRowU (the pad unit
   // repeats the row's last unit).  Surplus instructions repeat the chunk's
   // last one.
-  const auto rk = make_rsrc(k_r + (int64_t)bh * Npad * D, (uint32_t)Npad * (uint32_t)(D * 2));
-  const int rstride = sg.b >> sg.klog2;   // reordered rows between consecutive slots of a full block
+  // K rows per (batch, head): the reordered rows, or the gathered slot rows
+  const int krows = sg.compact ? sg.nsp_pad : Npad;
+  const auto rk = make_rsrc(k_r + (int64_t)bh * krows * D, (uint32_t)krows * (uint32_t)(D * 2));
+  // rows between consecutive slots of a full block
+  const int rstride = sg.compact ? 1 : sg.b >> sg.klog2;
   uint32_t voff[C::kPer];
 #pragma unroll
   for (int i = 0; i < C::kPer; ++i) {
@@ -263,7 +267,10 @@ __global__ __launch_bounds__(kThreads) void est_pass_kernel(
   // From this slot on, chunks take the exact rows: the last block when it is
   // partial (its slots are spread over fewer than b rows), and the padding.
   // Every chunk takes them when the sample count is not a power of two.
-  const int exact_from = sg.kf < sg.k ? 0
+  // (Gathered slot rows are read at unit stride throughout: their empty slots
+  // and padding are zero rows, masked like the others.)
+  const int exact_from = sg.compact ? sg.nsp_pad
+                         : sg.kf < sg.k ? 0
                          : (sg.N < sg.nb * sg.b || sg.nsp % kChunk != 0) ? (sg.nb - 1) * sg.k : sg.nsp_pad;
   auto dma = [&](int ch, char* buf) {
     const int ck0 = ch * kChunk;
@@ -706,6 +713,38 @@ __global__ __launch_bounds__(256) void est_mask_radix_kernel(const float2* __res
   maskcore::mask_row_radix<KPL>(in, row, sg.nb, rule, area_all[w], kv_count, kv_idx, mask);
 }
 
+// The sampled K rows gathered from K in token order into the layout the pass
+// reads at unit stride: row r of (batch, head) holds K at the token of
+// sampled slot r, as dbs_reorder_kv's k_r holds it (bf16; float32 rounded to
+// nearest even), and zeros for an empty slot or padding.  One thread per
+// 16-byte chunk of a row.
+template <int D>
+__global__ __launch_bounds__(256) void gather_sampled_k_kernel(const void* __restrict__ key, int k_f32, int64_t sb,
+                                                               int64_t sn, int64_t sh,
+                                                               const int32_t* __restrict__ perm, int perm_h_stride,
+                                                               int Hh, SampleGeom sg, __bf16* __restrict__ k_s) {
+  constexpr int kCpr = D / 8;   // 16-byte chunks per bf16 row
+  const int bh = blockIdx.y, bi = bh / Hh, h = bh % Hh;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)sg.nsp_pad * kCpr) return;
+  const int r = (int)(i / kCpr), c = (int)(i % kCpr);
+  const int row = sg.row(r);
+  uint4 o = make_uint4(0u, 0u, 0u, 0u);
+  if (row >= 0) {
+    int t = perm[(int64_t)h * perm_h_stride + row];
+    t = t < 0 ? 0 : (t >= sg.N ? sg.N - 1 : t);
+    const int64_t off = bi * sb + (int64_t)t * sn + (int64_t)h * sh + 8 * c;
+    if (k_f32) {
+      const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(key) + off);
+      const float4 a = p[0], b = p[1];
+      o = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w));
+    } else {
+      o = *reinterpret_cast<const uint4*>(reinterpret_cast<const __bf16*>(key) + off);
+    }
+  }
+  *reinterpret_cast<uint4*>(k_s + ((int64_t)bh * sg.nsp_pad + r) * D + 8 * c) = o;
+}
+
 // Key splits: about 768 workgroups in total (one and a half rounds of two
 // 8-wavefront workgroups per CU), each streaming a contiguous range of 64-key
 // chunks.  On the Wan-shaped layer, 768 measured 3 us faster than 1536 and
@@ -743,6 +782,19 @@ hipError_t launch_d(const EstimateArgs& a) {
   float* tmax = reinterpret_cast<float*>(part + (int64_t)BH * sg.splits * sg.nsp);
   const __bf16* qr = (const __bf16*)a.q_r;
   const __bf16* kr = (const __bf16*)a.k_r;
+  sg.compact = 0;
+  if (a.k_tok != nullptr) {
+    const size_t off = (estimate_workspace_bytes(a.B, a.Hh, a.nb, a.k, D) + 255) / 256 * 256;
+    __bf16* ks = reinterpret_cast<__bf16*>(reinterpret_cast<char*>(a.workspace) + off);
+    const int64_t chunks = (int64_t)sg.nsp_pad * (D / 8);
+    hipLaunchKernelGGL((gather_sampled_k_kernel<D>), dim3((unsigned)((chunks + 255) / 256), (unsigned)BH), dim3(256),
+                       0, a.stream, a.k_tok, a.k_f32, a.ksb, a.ksn, a.ksh, a.tok.perm, a.tok.perm_h_stride, a.Hh, sg,
+                       ks);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    kr = ks;
+    sg.compact = 1;
+  }
   dim3 grid((unsigned)(((sg.nsp + kQPerWg - 1) / kQPerWg) * sg.splits * BH));
   switch (sg.k) {
     case 1: hipLaunchKernelGGL((est_pass_kernel<D, 1>), grid, dim3(kThreads), 0, a.stream, qr, kr, a.tok, a.Npad, a.Hh, part, tmax, sg, sl2); break;
@@ -799,6 +851,14 @@ hipError_t launch_d(const EstimateArgs& a) {
 }
 
 }  // namespace
+
+size_t estimate_kvtok_workspace_bytes(int B, int Hh, int nb, int k, int d) {
+  int kp = 1;
+  while (kp < k) kp <<= 1;
+  const int64_t nsp_pad = ((int64_t)nb * kp + kChunk - 1) / kChunk * kChunk;
+  return (estimate_workspace_bytes(B, Hh, nb, k, d) + 255) / 256 * 256 +
+         (size_t)((int64_t)B * Hh * nsp_pad * d * 2);
+}
 
 size_t estimate_workspace_bytes(int B, int Hh, int nb, int k, int d) {
   int kp = 1;

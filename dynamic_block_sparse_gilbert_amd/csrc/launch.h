@@ -54,6 +54,11 @@ struct EstimateArgs {
   int B, Hh, N, Npad, d, b, k, nb;
   float scale;
   TokIO tok;            // tok.q set: sampled Q rows gathered in token order (out unused)
+  // k_tok set (with tok.perm): the sampled K rows are gathered from K in token
+  // order into the workspace (after the estimator's own part; k_r unused)
+  const void* k_tok;
+  int64_t ksb, ksn, ksh;
+  int k_f32;
   const struct MaskArgs* fuse;   // set: the final launch also selects the kept blocks (p_imp nullable)
   hipStream_t stream;
 };
@@ -185,6 +190,9 @@ hipError_t launch_inverse_reorder(const ReorderArgs& a);
 hipError_t launch_meanpool(const MeanpoolArgs& a);
 hipError_t launch_estimate(const EstimateArgs& a);
 size_t estimate_workspace_bytes(int B, int Hh, int nb, int k, int d);
+// With K in token order: the same, rounded up to 256 bytes, plus the gathered
+// sampled K rows (bf16, B * Hh * nsp_pad * d).
+size_t estimate_kvtok_workspace_bytes(int B, int Hh, int nb, int k, int d);
 hipError_t launch_build_mask(const MaskArgs& a);
 hipError_t launch_build_order(const MaskArgs& a);   // a.kv_count -> a.order only
 hipError_t launch_query_prune(const PruneArgs& a);

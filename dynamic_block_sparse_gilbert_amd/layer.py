@@ -118,16 +118,20 @@ class AsaLayer:
             raise ValueError(f"dtype {spec.dtype!r}: bf16 or fp32")
         if spec.dtype == "fp32" and spec.n_pool:
             raise ValueError("the float32 path takes no ASA_G global tokens")
-        """fused: the estimate and the mask in one call (dbs_estimate_mask_tok; P_imp is then not
-        written unless mask(keep_p_imp=True)), else dbs_estimate_blocks_tok + dbs_build_mask.
-        overlap: reorder V on a second stream (default priority) while the estimate runs, the
-        attention waiting for it; otherwise K and V are reordered in one launch (the default: on
-        the Wan-shaped layer the overlap measured 0.616-0.625 against 0.600-0.607 ms per step,
-        the two reorders being slower than the one launch and the V copy slowing the estimate)."""
+        """fused: the estimate and the mask in one call (P_imp is then not written unless
+        mask(keep_p_imp=True)), else dbs_estimate_blocks_tok + dbs_build_mask.
+        overlap (bf16, fused): the reorder of K and V (and the ASA_G pooling) runs on a second
+        stream (default priority) while the estimate, which reads its sampled K rows in token
+        order (dbs_estimate_mask_kvtok), runs on the caller's; the attention waits for both.
+        Otherwise (the default) the reorder comes first and the estimate reads the reordered K
+        (dbs_estimate_mask_tok).  The two give the same masks and outputs bit for bit; the overlap
+        measured no faster (21.12-21.20 against 21.07-21.11 ms per step on the 153,600-token
+        layer): a reorder workgroup (52 VGPRs x 8 wavefronts) does not fit beside the estimate's two
+        workgroups per CU, so the two kernels only take turns on the CUs."""
         self.spec = spec
         self.fused = fused
         self.f32 = spec.dtype == "fp32"
-        self.overlap = overlap and not spec.n_pool and not self.f32
+        self.overlap = overlap and fused and not self.f32
         self._side = torch.cuda.Stream(device=device) if self.overlap else None
         self.device = torch.device(device)
         self.perm = torch.from_numpy(build_perm(spec)).to(self.device)
@@ -146,8 +150,13 @@ class AsaLayer:
             self.v_t = torch.empty((B, Hh, nb, d, s.b), **bf)
         self.q: Optional[torch.Tensor] = None   # the caller's Q, token order
         self.p_imp = torch.empty((B, Hh, nb, nb), dtype=torch.float32, device=self.device)
-        self.ws = torch.empty(max(16, ops.estimate_workspace_bytes(B, Hh, s.N, d, s.b, s.k)),
-                              dtype=torch.uint8, device=self.device)
+        wsb = ops.estimate_workspace_bytes(B, Hh, s.N, d, s.b, s.k)
+        if self.overlap:
+            wsb = max(wsb, ops.estimate_kvtok_workspace_bytes(B, Hh, s.N, d, s.b, s.k))
+        self.ws = torch.empty(max(16, wsb), dtype=torch.uint8, device=self.device)
+        self.k: Optional[torch.Tensor] = None   # the caller's K, token order (overlap)
+        self._pending = None                      # overlap: (k, v) whose reorder is not yet queued
+        self._inputs_ready = None
         self.kv_count = torch.empty((B, Hh, nb), dtype=torch.int32, device=self.device)
         self.kv_idx = torch.empty((B, Hh, nb, nb), dtype=torch.int32, device=self.device)
         # Work order of the attention launch.  Longest rows first evens out the tail when the
@@ -190,20 +199,36 @@ class AsaLayer:
                     raise TypeError("the float32 layer takes float32 q, k, v")
                 ops.reorder(x, self.perm, s.Npad, s.b, "rows", y=y)
             return
-        if s.n_pool:   # the global tokens in the same launch (two passes when n does not divide b)
-            ops.reorder_kv(k, v, self.perm, s.Npad, s.b, k_r=self.k_r, v_t=self.v_t, n_pool=s.n_pool, k_g=self.k_g,
-                           v_g=self.v_g)
-        elif self.overlap:
-            # V is needed only by the attention: its reorder (HBM-bound) runs beside the
-            # estimate (MFMA / exp-bound); the side stream first waits for everything queued
-            # before (the inputs, and the previous step's attention reading v_t)
-            main = torch.cuda.current_stream()
-            ops.reorder(k, self.perm, s.Npad, s.b, "rows", y=self.k_r)
-            self._side.wait_stream(main)
-            with torch.cuda.stream(self._side):
-                ops.reorder(v, self.perm, s.Npad, s.b, "tiles_t", y=self.v_t)
+        if self.overlap:
+            # K and V are needed only by the attention: their reorder (HBM-bound) is queued on the
+            # side stream right after the estimate (VALU-bound), which gathers its own sampled K
+            # rows, so the estimate's workgroups are dispatched first and the reorder fills the
+            # CUs its last round leaves idle.  The side stream waits for everything queued before
+            # this point (the inputs, and the previous step's attention reading k_r / v_t).
+            self.k = k
+            self._inputs_ready = torch.cuda.Event()
+            self._inputs_ready.record(torch.cuda.current_stream())
+            self._pending = (k, v)
         else:
-            ops.reorder_kv(k, v, self.perm, s.Npad, s.b, k_r=self.k_r, v_t=self.v_t)
+            self._reorder_kv(k, v)
+
+    def _reorder_kv(self, k, v) -> None:
+        s = self.spec
+        # the global tokens in the same launch (two passes when n does not divide b)
+        pool = dict(n_pool=s.n_pool, k_g=self.k_g, v_g=self.v_g) if s.n_pool else {}
+        ops.reorder_kv(k, v, self.perm, s.Npad, s.b, k_r=self.k_r, v_t=self.v_t, **pool)
+
+    def _launch_side_reorder(self) -> None:
+        """Queue the deferred K / V reorder on the side stream (overlap), once per prepare()."""
+        if self._pending is None:
+            return
+        k, v = self._pending
+        self._pending = None
+        self._side.wait_event(self._inputs_ready)
+        with torch.cuda.stream(self._side):
+            self._reorder_kv(k, v)
+        k.record_stream(self._side)
+        v.record_stream(self._side)
 
     def mask(self, tau: Optional[float] = None, keep_p_imp: bool = False) -> None:
         s = self.spec
@@ -212,6 +237,12 @@ class AsaLayer:
             ops.estimate_mask(self.q_r, self.k_r, s.N, s.b, s.k, s.scale, "cumulative", tau, kv_count=self.kv_count,
                               kv_idx=self.kv_idx, order=self.order, workspace=self.ws,
                               p_imp=self.p_imp if (keep_p_imp or not self.fused) else None)
+            return
+        if self.overlap:
+            ops.estimate_mask_kvtok(self.q, self.k, self.perm, s.b, s.k, s.scale, "cumulative", tau,
+                                    kv_count=self.kv_count, kv_idx=self.kv_idx, order=self.order,
+                                    workspace=self.ws, p_imp=self.p_imp if keep_p_imp else None)
+            self._launch_side_reorder()
             return
         if self.fused:
             ops.estimate_mask(self.q, self.k_r, s.N, s.b, s.k, s.scale, "cumulative", tau, q_perm=self.perm,
@@ -227,6 +258,7 @@ class AsaLayer:
         s = self.spec
         if self.f32:
             return ops.estimate_blocks(self.q_r, self.k_r, s.N, s.b, s.k, s.scale, p_imp=self.p_imp, workspace=self.ws)
+        self.wait_kv()
         return ops.estimate_blocks_tok(self.q, self.perm, self.k_r, s.N, s.b, s.k, s.scale, p_imp=self.p_imp,
                                        workspace=self.ws)
 
@@ -263,10 +295,12 @@ class AsaLayer:
                 hi = mid
         return float(lo), sparsity_at(lo)
 
-    def wait_v(self) -> None:
-        """Make the current stream wait for prepare()'s V reorder (side stream); needed before any
-        direct use of self.v_t after prepare() (attend() does it)."""
+    def wait_kv(self) -> None:
+        """Make the current stream wait for prepare()'s K and V reorder (side stream); needed before
+        any direct use of self.k_r, self.v_t, self.k_g or self.v_g after prepare() (attend() and
+        estimate_only() do it)."""
         if self.overlap:
+            self._launch_side_reorder()
             torch.cuda.current_stream().wait_stream(self._side)
 
     def attend(self, out: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16) -> torch.Tensor:
@@ -277,7 +311,7 @@ class AsaLayer:
             if out is None:
                 out = torch.empty((s.batch, s.N, s.heads, s.d), dtype=torch.float32, device=self.device)
             return ops.inverse_reorder(self.o_r, self.perm, s.N, out=out)
-        self.wait_v()
+        self.wait_kv()
         out, _ = ops.sparse_attn_fwd_tok(self.q, self.perm, self.k_r, self.v_t, s.N, s.b, s.scale, self.kv_count,
                                          self.kv_idx, self.k_g, self.v_g, self.Ng, s.n_pool, out=out,
                                          out_dtype=out_dtype, order=self.order)

@@ -327,6 +327,48 @@ def estimate_mask(q_r: torch.Tensor, k_r: torch.Tensor, N: int, b: int, k: int, 
     return kv_count, kv_idx, mask, p_imp
 
 
+def estimate_kvtok_workspace_bytes(B: int, Hh: int, N: int, d: int, b: int, k: int) -> int:
+    return int(lib().dbs_estimate_kvtok_workspace_bytes(B, Hh, N, d, b, k))
+
+
+def estimate_mask_kvtok(q: torch.Tensor, key: torch.Tensor, perm: torch.Tensor, b: int, k: int, scale: float,
+                        rule: str, param: float, want_p_imp: bool = False, want_mask: bool = False,
+                        kv_count: Optional[torch.Tensor] = None, kv_idx: Optional[torch.Tensor] = None,
+                        order: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                        p_imp: Optional[torch.Tensor] = None):
+    """dbs_estimate_mask_kvtok: the estimate and the block selection with Q and K both in token
+    order ([B, N, Hh, d], d contiguous), so no reordered K is needed.  Returns (kv_count, kv_idx,
+    mask or None, p_imp or None), as estimate_mask."""
+    _dev(q, key, perm, kv_count, kv_idx, order, workspace, p_imp)
+    B, N, Hh, d = q.shape
+    if key.shape != q.shape:
+        raise ValueError("q and key must have one shape")
+    if q.stride(3) != 1 or key.stride(3) != 1:
+        raise ValueError("the d axis of q and key must be contiguous")
+    Npad = -(-N // b) * b
+    nb = Npad // b
+    dv = q.device
+    _lists(kv_count, kv_idx, B, Hh, nb)
+    _i32(order, "order", B * Hh * nb, ())
+    per_head = _perm(perm, N, Hh)
+    if kv_count is None:
+        kv_count = torch.empty((B, Hh, nb), dtype=torch.int32, device=dv)
+    if kv_idx is None:
+        kv_idx = torch.empty((B, Hh, nb, nb), dtype=torch.int32, device=dv)
+    mask = torch.empty((B, Hh, nb, nb), dtype=torch.uint8, device=dv) if want_mask else None
+    if p_imp is None and want_p_imp:
+        p_imp = torch.empty((B, Hh, nb, nb), dtype=torch.float32, device=dv)
+    need = estimate_kvtok_workspace_bytes(B, Hh, N, d, b, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dv)
+    wsb = workspace.numel() * workspace.element_size()
+    check("dbs_estimate_mask_kvtok", lib().dbs_estimate_mask_kvtok(
+        _p(q), _dt(q), q.stride(0), q.stride(1), q.stride(2), _p(key), _dt(key), key.stride(0), key.stride(1),
+        key.stride(2), _p(perm), per_head, B, Hh, N, Npad, d, b, k, float(scale), MASK_RULES[rule], float(param),
+        _p(p_imp), _p(kv_count), _p(kv_idx), _p(mask), _p(order), _p(workspace), wsb, _stream()))
+    return kv_count, kv_idx, mask, p_imp
+
+
 NOALLOC_SCRATCH_BYTES = 128 << 20     # DBS_NOALLOC_SCRATCH_BYTES
 
 

@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define DBS_ABI_VERSION 12
+#define DBS_ABI_VERSION 13
 
 typedef enum {
   DBS_OK = 0,
@@ -296,6 +296,30 @@ dbs_status dbs_estimate_mask_tok(const void* q, dbs_dtype q_dt, int64_t sb, int6
                                  int rule, double param, float* p_imp,
                                  int32_t* kv_count, int32_t* kv_idx, uint8_t* mask, int32_t* order,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device workspace dbs_estimate_mask_kvtok needs:
+ * dbs_estimate_workspace_bytes rounded up to 256, plus the sampled K rows it
+ * gathers (bf16, B * Hh * P * d with P = nb * k rounded up to a multiple of
+ * 64, k rounded up to a power of two).  Returns 0 for invalid sizes. */
+size_t dbs_estimate_kvtok_workspace_bytes(int B, int Hh, int N, int d, int b, int k);
+
+/* dbs_estimate_mask_tok with K read in token order as well (Video-BLADE
+ * "Step 1" samples K as it samples Q): the sampled K rows are gathered from
+ * key[b, perm_h[i], h, :] (element strides ksb, ksn, ksh; d contiguous;
+ * key_dt DBS_BF16, or DBS_FP32 rounded to bf16 as dbs_reorder_kv rounds it)
+ * into the workspace, so the estimate needs no reordered K.  A layer can then
+ * run dbs_reorder_kv on a second stream while this call runs.  The outputs
+ * equal dbs_estimate_mask_tok on dbs_reorder_kv's k_r bit for bit.  q, q_dt,
+ * its strides, perm and the rest as for dbs_estimate_mask_tok; workspace:
+ * device, >= dbs_estimate_kvtok_workspace_bytes(...) bytes.  Errors as for
+ * dbs_estimate_mask_tok, and for key as for q. */
+dbs_status dbs_estimate_mask_kvtok(const void* q, dbs_dtype q_dt, int64_t qsb, int64_t qsn, int64_t qsh,
+                                   const void* key, dbs_dtype key_dt, int64_t ksb, int64_t ksn, int64_t ksh,
+                                   const int32_t* perm, int perm_per_head,
+                                   int B, int Hh, int N, int Npad, int d, int b, int k, float scale,
+                                   int rule, double param, float* p_imp,
+                                   int32_t* kv_count, int32_t* kv_idx, uint8_t* mask, int32_t* order,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc):

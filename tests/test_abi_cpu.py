@@ -37,7 +37,7 @@ def test_all_declared_symbols_exported(dbs):
     for n in names:
         assert hasattr(h, n), n
     assert set(names) == set(L.SIGNATURES), set(names) ^ set(L.SIGNATURES)
-    assert L.lib().dbs_abi_version() == 12
+    assert L.lib().dbs_abi_version() == 13
 
 
 @pytest.mark.parametrize("T,H,W", list(itertools.product(range(1, 7), repeat=3)))
@@ -338,6 +338,43 @@ def test_estimate_mask_validation(dbs):
     assert callt(17, 0.5) == -1           # top-k count not an integer >= 1
     assert callt(20, 0) == -1             # kv_idx NULL
     assert callt(24, ws - 1) == -1        # small workspace
+
+
+@cpu_only
+def test_estimate_mask_kvtok_validation(dbs):
+    """The estimate with K in token order checks K as it checks Q and asks for the larger workspace
+    (the estimator's own plus the gathered sampled K rows), all before any launch."""
+    _, L = dbs
+    ws = L.lib().dbs_estimate_workspace_bytes(1, 2, 100, 128, 64, 8)
+    wk = L.lib().dbs_estimate_kvtok_workspace_bytes(1, 2, 100, 128, 64, 8)
+    # nb = 2 blocks of 8 slots: 16 slots padded to 64 rows of 128 bf16 per head, after 256-byte rounding
+    assert wk == -(-ws // 256) * 256 + 2 * 64 * 128 * 2
+    assert L.lib().dbs_estimate_kvtok_workspace_bytes(1, 2, 100, 96, 64, 8) == 0
+    assert L.lib().dbs_estimate_kvtok_workspace_bytes(1, 2, 100, 128, 64, 3) == \
+        L.lib().dbs_estimate_kvtok_workspace_bytes(1, 2, 100, 128, 64, 4)       # slots padded to 4
+    g = L.lib().dbs_estimate_mask_kvtok
+    # q, q_dt, qsb, qsn, qsh, key, key_dt, ksb, ksn, ksh, perm, per_head, B, Hh, N, Npad, d, b, k, scale, rule,
+    # param, p_imp, kv_count, kv_idx, mask, order, ws, wsb, stream
+    st = 100 * 2 * 128
+    ok = [A, 0, st, 2 * 128, 128, A, 0, st, 2 * 128, 128, A, 0, 1, 2, 100, 128, 128, 64, 8, 0.125, 0, 0.9, None, A,
+          A, None, None, A, wk, None]
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return g(*a)
+    assert call(0, 0) == -1               # q NULL
+    assert call(5, 0) == -1               # key NULL
+    assert call(10, 0) == -1              # perm NULL
+    assert call(5, A + 2) == -3           # misaligned key
+    assert call(6, 7) == -1               # bad key dtype
+    assert call(8, 2 * 128 + 4) == -3     # key row stride breaks 16-byte rows
+    assert call(9, -8) == -1              # negative key stride
+    assert call(23, 0) == -1              # kv_count NULL
+    assert call(20, 9) == -1              # unknown rule
+    assert call(16, 96) == -2             # head dimension
+    assert call(28, wk - 1) == -1         # the workspace of the reordered-K call is not enough
+    assert "workspace" in L.lib().dbs_last_error().decode()
+    assert call(28, ws) == -1
 
 
 @pytest.mark.parametrize("T,H,W,win,prefix,order", [

@@ -188,19 +188,28 @@ def test_layer_config5_operating_points(target):
     assert s >= target
 
 
-def test_layer_overlap_equals_single_stream():
-    """AsaLayer(overlap=True) (V reordered on a second stream beside the estimate) gives the same
-    output, bit for bit, as the single-launch K/V reorder, over several back-to-back steps."""
+@pytest.mark.parametrize("cid", [2, 3])
+def test_layer_overlap_equals_single_stream(cid):
+    """AsaLayer(overlap=True) (K and V, and for ASA_G their pooled tokens, reordered on a second
+    stream while the estimate reads its sampled K rows in token order) gives the same masks and
+    outputs, bit for bit, as the single-stream layer, over back-to-back steps whose inputs change
+    from step to step (so a reorder racing the previous step's attention would show)."""
     from dynamic_block_sparse_gilbert_amd.layer import AsaLayer, LayerSpec
-    cfg = get_config(2)
+    cfg = get_config(cid)
     say("layer overlap", cfg.name)
     heads = [0, 1, 2]
     q, k, v = make_inputs(cfg, heads=heads)
-    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
-    spec = lambda: LayerSpec(T=cfg.T, H=cfg.H, W=cfg.W, heads=len(heads), d=cfg.d, b=cfg.b, k=cfg.k, tau=0.9)
+    steps = [(dev_bf16(q), dev_bf16(k), dev_bf16(v)),
+             (dev_bf16(k), dev_bf16(q), dev_bf16(v[:, ::-1].copy())),
+             (dev_bf16(q), dev_bf16(v), dev_bf16(k))]
+    spec = lambda: LayerSpec(T=cfg.T, H=cfg.H, W=cfg.W, heads=len(heads), d=cfg.d, b=cfg.b, k=cfg.k, tau=0.9,
+                             prefix=cfg.text_prefix, order=cfg.reorder, cuboid=cfg.cuboid,
+                             n_pool=cfg.global_pool)
     a, b = AsaLayer(spec(), overlap=True), AsaLayer(spec(), overlap=False)
-    for _ in range(3):
+    assert a.overlap and not b.overlap
+    for qd, kd, vd in steps:
         oa = a.forward(qd, kd, vd)
         ob = b.forward(qd, kd, vd)
-    torch.cuda.synchronize()
-    assert torch.equal(oa, ob)
+        torch.cuda.synchronize()
+        assert torch.equal(a.kv_count, b.kv_count)
+        assert torch.equal(oa, ob)
