@@ -255,8 +255,9 @@ def measure(layer, cfg, qd, kd, vd, out, tau, steps, warmup, torch):
         "executed_attn_flop": exec_flop,
         "dense_equiv_flop": dense,
         "roofline": {
-            "bound": "mfma",
-            "kernel": "attn_fwd_kernel<%d,%d>" % (d, cfg.b) if cfg.dtype != "fp32" else "attn_fwd_f32_kernel",
+            # the float32 path runs on the vector ALUs (no float32 MFMA): its peak is the fp32 vector rate
+            "bound": "mfma" if cfg.dtype != "fp32" else "alu",
+            "kernel": "attn_fwd_kernel<%d,%d>" % (d, cfg.b) if cfg.dtype != "fp32" else "attn_f32_kernel",
             "achieved": round(attn_tflops, 2),
             "peak": MFMA_BF16_PEAK_TFLOPS if cfg.dtype != "fp32" else 157.3,
             "unit": "TFLOP/s",
