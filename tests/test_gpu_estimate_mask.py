@@ -161,7 +161,7 @@ def test_wan_shape_fused_equals_two_launches():
         _same_lists(two, got[:3], nb)
 
 
-@pytest.mark.parametrize("case", ["gilbert_bf16", "per_head_k12_ragged", "f32_d64_b128", "packed_qkv_view"])
+@pytest.mark.parametrize("case", ["gilbert_bf16", "per_head_k12_ragged", "f32_d64_b128", "packed_qkv_view", "batch2"])
 def test_kvtok_equals_reordered_k(case):
     """dbs_estimate_mask_kvtok (K read in token order, its sampled rows gathered into the workspace)
     against dbs_estimate_mask_tok on dbs_reorder's K rows: P_imp, kv_count, the kept lists, the mask
@@ -176,7 +176,8 @@ def test_kvtok_equals_reordered_k(case):
     elif case == "f32_d64_b128":
         d, b, f32 = 64, 128, True
     N = T * H * W
-    q, k, _ = smooth_qkv(23, 1, N, Hh, d, grid=(T, H, W))
+    Bt = 2 if case == "batch2" else 1
+    q, k, _ = smooth_qkv(23, Bt, N, Hh, d, grid=(T, H, W))
     if case == "per_head_k12_ragged":
         perm_h = np.stack([perm_gilbert3d(T, H, W), perm_cuboid(T, H, W, 2, 4, 4), perm_cuboid(T, H, W, 1, 2, 8)])
         perm = dev(perm_h.astype(np.int32))
@@ -187,7 +188,7 @@ def test_kvtok_equals_reordered_k(case):
         qd = dev((q * (1 + rng.uniform(-1e-3, 1e-3, q.shape))).astype(np.float32))
         kd = dev((k * (1 + rng.uniform(-1e-3, 1e-3, k.shape))).astype(np.float32))
     elif case == "packed_qkv_view":   # K a strided view of a packed [B, N, Hh, 3, d] tensor
-        qkv = torch.zeros((1, N, Hh, 3, d), dtype=torch.bfloat16, device="cuda")
+        qkv = torch.zeros((Bt, N, Hh, 3, d), dtype=torch.bfloat16, device="cuda")
         qkv[:, :, :, 0] = dev_bf16(q)
         qkv[:, :, :, 1] = dev_bf16(k)
         qd, kd = qkv[:, :, :, 0], qkv[:, :, :, 1]
@@ -198,8 +199,8 @@ def test_kvtok_equals_reordered_k(case):
     nb = Npad // b
     scale = 1.0 / np.sqrt(d)
     k_r = ops.reorder(kd, perm, Npad, b, "rows")
-    o1 = torch.empty(Hh * nb, dtype=torch.int32, device="cuda")
-    o2 = torch.empty(Hh * nb, dtype=torch.int32, device="cuda")
+    o1 = torch.empty(Bt * Hh * nb, dtype=torch.int32, device="cuda")
+    o2 = torch.empty(Bt * Hh * nb, dtype=torch.int32, device="cuda")
     ref = ops.estimate_mask(qd, k_r, N, b, kk, scale, "cumulative", 0.9, q_perm=perm, want_p_imp=True,
                             want_mask=True, order=o1)
     got = ops.estimate_mask_kvtok(qd, kd, perm, b, kk, scale, "cumulative", 0.9, want_p_imp=True, want_mask=True,
@@ -209,5 +210,5 @@ def test_kvtok_equals_reordered_k(case):
     _same_lists(ref[:3], got[:3], nb)
     # the work orders: permutations with the same counts along them (equal counts in any order)
     cnt = host(got[0]).reshape(-1)
-    assert sorted(host(o2).tolist()) == list(range(Hh * nb))
+    assert sorted(host(o2).tolist()) == list(range(Bt * Hh * nb))
     assert np.array_equal(cnt[host(o1)], cnt[host(o2)])
