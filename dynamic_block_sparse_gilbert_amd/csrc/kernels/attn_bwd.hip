@@ -322,7 +322,10 @@ __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2
     const char* kb = kb_stage + 32 * t * C::kRowStride;
     const char* vb = vb_stage + 32 * t * C::kRowStride;
     const int key0 = J * BLK + h * KT + 32 * t;
-    f32x16_t S = f32x16_t{}, dP = f32x16_t{};
+    // dP^T accumulates onto -D (each lane's column is one query), so it ends as dP^T - D
+    f32x16_t S = f32x16_t{}, dP;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dP[v] = -Dq;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       S = mfma(read_rows<C>(kb, l32, g, kk), qreg[kk], S);
@@ -335,11 +338,11 @@ __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(2
       for (int v = 0; v < 16; ++v) {
         float p = fast_exp2(__builtin_fmaf(S[v], sl2, -lse2));
         if (key0 + stage_row(acc_row(v, g)) >= N) p = 0.f;
-        S[v] = p * (dP[v] - Dq);
+        S[v] = p * dP[v];
       }
     } else {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) S[v] = fast_exp2(__builtin_fmaf(S[v], sl2, -lse2)) * (dP[v] - Dq);
+      for (int v = 0; v < 16; ++v) S[v] = fast_exp2(__builtin_fmaf(S[v], sl2, -lse2)) * dP[v];
     }
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
