@@ -114,10 +114,6 @@ class AsaLayer:
     """Holds the device permutation and the intermediate buffers of one layer shape."""
 
     def __init__(self, spec: LayerSpec, device="cuda", fused: bool = True, overlap: bool = False):
-        if spec.dtype not in ("bf16", "fp32"):
-            raise ValueError(f"dtype {spec.dtype!r}: bf16 or fp32")
-        if spec.dtype == "fp32" and spec.n_pool:
-            raise ValueError("the float32 path takes no ASA_G global tokens")
         """fused: the estimate and the mask in one call (P_imp is then not written unless
         mask(keep_p_imp=True)), else dbs_estimate_blocks_tok + dbs_build_mask.
         overlap (bf16, fused): the reorder of K and V (and the ASA_G pooling) runs on a second
@@ -128,6 +124,10 @@ class AsaLayer:
         measured no faster (21.12-21.20 against 21.07-21.11 ms per step on the 153,600-token
         layer): a reorder workgroup (52 VGPRs x 8 wavefronts) does not fit beside the estimate's two
         workgroups per CU, so the two kernels only take turns on the CUs."""
+        if spec.dtype not in ("bf16", "fp32"):
+            raise ValueError(f"dtype {spec.dtype!r}: bf16 or fp32")
+        if spec.dtype == "fp32" and spec.n_pool:
+            raise ValueError("the float32 path takes no ASA_G global tokens")
         self.spec = spec
         self.fused = fused
         self.f32 = spec.dtype == "fp32"
