@@ -78,6 +78,9 @@ def parse():
     ap.add_argument("--configs", type=str, default="1,2,3,5", help="other configs measured under extra")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
+    ap.add_argument("--sustain", type=float, default=0.0,
+                    help="after the headline, run each stage (and the whole step) back to back for this "
+                         "many seconds, with wall-clock stamps, for power and clock sampling beside it")
     return ap.parse_args()
 
 
@@ -501,6 +504,40 @@ def sics_leg(cfg, qd, kd, steps, torch, step_ms=None):
 
 # ----------------------------------------------------------------------------- driver
 
+def sustain_leg(layer, tens, tau, secs, torch):
+    """Each stage of the step alone, then the whole step, launched back to back for about `secs`
+    seconds of wall time, with 3 s idle gaps between them; per stage the mean time per call
+    (HIP events) and the Unix times it started and ended (for sampling the board's power and clock
+    beside the run)."""
+    qd, kd, vd = tens
+    out = torch.empty_like(qd)
+    stages = [("attention", lambda: layer.attend(out)),
+              ("estimate_mask", lambda: layer.mask(tau)),
+              ("reorder_kv", lambda: layer._reorder_kv(kd, vd)),
+              ("layer_step", lambda: layer.forward(qd, kd, vd, out=out, tau=tau))]
+    layer.forward(qd, kd, vd, out=out, tau=tau)
+    res = {}
+    for name, fn in stages:
+        torch.cuda.synchronize()
+        time.sleep(3.0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.time()
+        e0.record()
+        calls = 0
+        while calls == 0 or time.time() - t0 < secs:
+            for _ in range(10):
+                fn()
+            calls += 10
+            torch.cuda.synchronize()
+        e1.record()
+        torch.cuda.synchronize()
+        t1 = time.time()
+        res[name] = {"ms_per_call": round(e0.elapsed_time(e1) / calls, 4), "calls": calls,
+                     "start_unix": round(t0, 3), "end_unix": round(t1, 3)}
+        log(f"sustain {name} start {t0:.3f} end {t1:.3f} ms/call {res[name]['ms_per_call']}")
+    return res
+
+
 def load_inputs(cfg, torch, dev):
     from workloads import make_inputs
     t0 = time.perf_counter()
@@ -574,8 +611,9 @@ def main():
         rule = HEADLINE[1:]
     else:
         rule = EXTRA_RUNS.get(args.config, [("tau", 0.9)])[0]
-    cfg, layer, _, (head,) = run_config(args.config, [rule], args, torch, dev, cpu=not args.no_cpu_baseline)
-    del layer
+    cfg, layer, tens, (head,) = run_config(args.config, [rule], args, torch, dev, cpu=not args.no_cpu_baseline)
+    sustained = sustain_leg(layer, tens, head["tau"], args.sustain, torch) if args.sustain > 0 else None
+    del layer, tens
     torch.cuda.empty_cache()
 
     line = {
@@ -609,6 +647,8 @@ def main():
     }
     if "cpu_baseline" in head:
         line["cpu_baseline"] = head["cpu_baseline"]
+    if sustained is not None:
+        line["sustained"] = sustained
 
     if not args.no_extra:
         extra = {"configs": {}}
