@@ -588,8 +588,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): every step of the path is "
-              "independent per head, so several GPUs would each run a share of the heads; that "
-              "configuration is not part of this build.", file=sys.stderr)
+              "independent per head, so several GPUs would each run a share of the heads; the library "
+              "has no multi-GPU launch.", file=sys.stderr)
         sys.exit(2)
 
     import torch
