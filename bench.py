@@ -211,6 +211,14 @@ def workload_name(cfg):
             f"b={cfg.b}, k={cfg.k}, {order}{g}")
 
 
+def mask_stage_bytes(rows_bh, nb, kept, with_order):
+    """Bytes dbs_build_mask must move: P_imp read once (rows_bh = B * H heads of nb x nb float32),
+    kv_count written (one int32 per row), the kept entries of kv_idx written (kept = the total
+    over all rows and heads), and the work order (one int32 per row) when it is written."""
+    rows = rows_bh * nb
+    return 4.0 * rows * nb + 4.0 * rows + 4.0 * kept + (4.0 * rows if with_order else 0.0)
+
+
 def measure(layer, cfg, qd, kd, vd, out, tau, steps, warmup, torch):
     """One layer at one tau: the timed steps, the stage breakdown, the attention roofline and the
     byte / estimate stages, each against its own bound."""
@@ -235,8 +243,8 @@ def measure(layer, cfg, qd, kd, vd, out, tau, steps, warmup, torch):
     est_flop = 2.0 * H * ns * ns * d
     est_exp = float(H) * ns * ns
     est_bound_ms = max(est_flop / (MFMA_BF16_PEAK_TFLOPS * 1e12), est_exp / EXP_PEAK_PER_S) * 1e3
-    kept = float(cnt.sum())
-    mask_bytes = 4.0 * H * nb * nb + 4.0 * H * (nb + kept) + 4.0 * H * nb
+    kept = float(cnt.sum())          # kept blocks over every row of every head
+    mask_bytes = mask_stage_bytes(cnt.shape[0] * H, nb, kept, with_order=layer.order is not None)
     e = 4 if cfg.dtype == "fp32" else 2
     # bf16: K and V read and written; float32: Q, K and V (the float32 path reorders Q too)
     nt = 3 if cfg.dtype == "fp32" else 2
@@ -280,7 +288,9 @@ def measure(layer, cfg, qd, kd, vd, out, tau, steps, warmup, torch):
             "mask": {"bound": "hbm", "bytes": mask_bytes, "ms": round(t_mask, 4),
                      "achieved_GBs": round(mask_bytes / (t_mask * 1e-3) / 1e9, 1), "peak_GBs": HBM_PEAK_GBS,
                      "frac": round(mask_bytes / (t_mask * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "what": "dbs_build_mask alone on the P_imp (read once), lists and work order written"},
+                     "what": "dbs_build_mask alone on a stored P_imp (read once; kv_count, the kept kv_idx "
+                             "entries and the work order written), as the tau search and the unfused path run "
+                             "it; the timed step selects inside the fused estimate_mask call instead"},
             "estimate_mask_fused_ms": round(stage.get("estimate_mask", float("nan")), 4),
         },
     }
