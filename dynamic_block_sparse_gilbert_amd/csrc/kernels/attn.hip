@@ -25,9 +25,10 @@
 // Software pipeline per stage u (one basic block, two phases):
 //   phase A: score MFMAs of stage u+1   ||  exp / pack / row-sum of stage u
 //   phase B: PV MFMAs of stage u        ||  row maximum of stage u+1
-//   then, for partial / global-token stages only, the key mask and bias and a
-//   fresh maximum, and the (rarely taken) lazy rescale decided from stage
-//   u+1's maximum.  Two wavefronts per SIMD from different workgroups fill
+//   then, for partial stages and the last global-token tile only, the key mask
+//   and bias and a fresh maximum (the other global-token tiles add ln n to the
+//   maximum and the exponent offset instead), and the (rarely taken) lazy
+//   rescale decided from stage u+1's maximum.  Two wavefronts per SIMD from different workgroups fill
 //   each other's gaps; forcing an instruction interleave measured slower.
 // K and V stages are copied global -> LDS by the buffer form of the DMA path
 // (buffer_load_dwordx4 ... lds, no VGPR staging) into double buffers during
@@ -125,7 +126,9 @@ struct StageDesc {
   uint32_t voffs;      // byte offset of the stage's V^T columns in its head
   bool glob;           // global-token tile (K_g / V_g) rather than a kept block
   int key0;            // index of the stage's first key (token, or global token)
-  int kind;            // 0 full, 1 partial / invalid (mask by key index), 2 global tokens
+  int kind;            // 0 full, 1 partial / invalid (mask by key index), 2 global tokens (the
+                       // last tile: per-key bias and mask), 3 global tokens that all carry the
+                       // ln n bias (no mask; the bias enters the exponent offset)
   int limit;           // keys with index >= limit are masked (kind 1, 2)
   bool absent;         // mode 2: a block this wavefront's query block does not keep (contributes nothing)
 };
@@ -141,8 +144,16 @@ struct StageDesc {
 //      the blocks mode 2 takes, and mode 2 exits for the others.  With a
 //      work order, mode 2 walks the rows in that order and runs each pair
 //      at its first block's place (the longest pairs start first).
-template <int D, int BLK, int QB, int MODE>
-__global__ __launch_bounds__(QB / 32 * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+//
+// GLOB: the launch has ASA_G global tokens (k_g, v_g); without them the global
+// tiles and the kind 3 exponent offset are compiled out.  The d = 64, b = 128
+// plain kernel fits three workgroups per CU (168 VGPRs, 45 KB LDS): its softmax VALU
+// work is that of d = 128 over half the MFMAs, and the third wavefront per SIMD
+// fills more of the VALU gaps.
+template <int D, int BLK, int QB, int MODE, bool GLOB = false>
+__global__ __launch_bounds__(QB / 32 * 64)
+__attribute__((amdgpu_waves_per_eu(D == 64 && BLK == 128 && MODE == 0 ? 3 : 2,
+                                  D == 64 && BLK == 128 && MODE == 0 ? 3 : 2)))
 void attn_fwd_kernel(
     const __bf16* __restrict__ q_r, const __bf16* __restrict__ k_r, const __bf16* __restrict__ v_t,
     const int32_t* __restrict__ kv_count, const int32_t* __restrict__ kv_idx,
@@ -287,7 +298,7 @@ void attn_fwd_kernel(
     cnt = __builtin_amdgcn_readfirstlane(u);
   }
   const int Ngpad = (Ng + BLK - 1) / BLK * BLK;
-  const int ntg = (k_g != nullptr) ? Ngpad / BLK : 0;
+  const int ntg = (GLOB && k_g != nullptr) ? Ngpad / BLK : 0;
   const int U = (cnt + ntg) * C::kSubs;
 
   // Buffer descriptors of this head's K rows, V^T tiles and global-token
@@ -314,7 +325,9 @@ void attn_fwd_kernel(
     s.koffs = (uint32_t)s.key0 * (uint32_t)(D * 2);
     s.voffs = ((uint32_t)Jx * (uint32_t)(D * BLK) + (uint32_t)(h * C::kKT)) * 2u;
     s.glob = !kept;
-    s.kind = kept ? ((w >> h) & kPartial ? 1 : 0) : 2;
+    // a global tile whose keys all precede the last global token adds the same ln n to
+    // every score: it needs neither the per-key bias nor a mask
+    s.kind = kept ? ((w >> h) & kPartial ? 1 : 0) : (GLOB && s.key0 + C::kKT <= Ng - 1 ? 3 : 2);
     s.limit = kept ? ((MODE != 2 && (w & kInvalidBit)) ? -1 : N) : Ng;
     // mode 2: a block of the union that this wavefront's query block does
     // not keep; its probabilities are made zero through the exponent offset
@@ -379,6 +392,10 @@ void attn_fwd_kernel(
   for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16_t{};
   float m = -INFINITY, mneg = 0.f, l = 0.f;
   bool cur_abs = false;   // mode 2: the current stage is absent for this wavefront
+  // The current stage's constant logit bias in log2 units (kind 3 stages: ln n * log2 e); the
+  // probabilities are exp2(S * sl2 + mneg + cur_eb).
+  float cur_eb = 0.f;
+  const float eb3 = bias_n * sl2;
 
   // S^T tiles of one stage: S[kt][v] is key 32 kt + (v/4)*8 + 4g + v%4 of
   // query l32.
@@ -393,8 +410,10 @@ void attn_fwd_kernel(
     }
   };
 
-  // Partial, invalid and global-token stages: move the ASA_G bias into the raw
-  // score domain (ln r / scale) and mask keys past the stage's limit.
+  // Partial and invalid stages and the last global-token tile: move the ASA_G
+  // bias into the raw score domain (ln r / scale) and mask keys past the stage's
+  // limit.  The other global-token tiles (kind 3) carry ln n on every key, which
+  // shifts their maximum by ln n and their exponent offset by ln n * log2 e.
   auto fixup = [&](const StageDesc& s, f32x16_t (&S)[2]) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -449,7 +468,7 @@ void attn_fwd_kernel(
       scores(ksrc, Sn);
       dma_v(*dv, vdst);
     }
-    const float mn = (MODE == 2 && cur_abs) ? -INFINITY : mneg;
+    const float mn = (MODE == 2 && cur_abs) ? -INFINITY : (GLOB ? mneg + cur_eb : mneg);
     float s0, s1;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -516,14 +535,17 @@ void attn_fwd_kernel(
     // Pin the maximum inside the phase (otherwise it is sunk past the branch
     // below, away from the MFMAs it is meant to overlap).
     asm volatile("" ::"v"(mx));
-    if (sn.kind != 0) {
+    if (sn.kind == 1 || sn.kind == 2) {
       fixup(sn, Sn);
       mx = row_max(Sn);
+    } else if (sn.kind == 3) {
+      mx += bias_n;   // the maximum of the biased scores
     }
     if constexpr (MODE == 2) {
       if (sn.absent) mx = -INFINITY;
     }
     decide(mx);
+    if constexpr (GLOB) cur_eb = sn.kind == 3 ? eb3 : 0.f;
     if constexpr (MODE == 2) cur_abs = sn.absent;
     return sk;
   };
@@ -610,8 +632,9 @@ void attn_fwd_kernel(
     __syncthreads();
     f32x16_t SA[2], SB[2];
     scores(Kb0, SA);
-    if (s0.kind != 0) fixup(s0, SA);
-    decide((MODE == 2 && s0.absent) ? -INFINITY : row_max(SA));
+    if (s0.kind == 1 || s0.kind == 2) fixup(s0, SA);
+    decide((MODE == 2 && s0.absent) ? -INFINITY : row_max(SA) + (s0.kind == 3 ? bias_n : 0.f));
+    if constexpr (GLOB) cur_eb = s0.kind == 3 ? eb3 : 0.f;
     if constexpr (MODE == 2) cur_abs = s0.absent;
     int u = 0;
     for (; u + 2 < U; u += 2) {
@@ -669,7 +692,7 @@ void attn_fwd_kernel(
   }
 }
 
-template <int D, int BLK, int QB = BLK, int MODE = 0>
+template <int D, int BLK, int QB = BLK, int MODE = 0, bool GLOB = false>
 hipError_t launch(const AttnArgs& a) {
   // mode 2: one work item per pair, or per row (odd rows exit) when a work order is given
   const int total = (MODE == 2 && a.order == nullptr) ? a.B * a.Hh * ((a.nb + 1) / 2)
@@ -681,7 +704,7 @@ hipError_t launch(const AttnArgs& a) {
     bias_n = (float)(std::log((double)a.n_pool) / a.scale);
     bias_last = (float)(std::log((double)(a.N - (a.Ng - 1) * a.n_pool)) / a.scale);
   }
-  hipLaunchKernelGGL((attn_fwd_kernel<D, BLK, QB, MODE>), dim3(total), dim3(AttnCfg<D, BLK, QB>::kThreads), 0,
+  hipLaunchKernelGGL((attn_fwd_kernel<D, BLK, QB, MODE, GLOB>), dim3(total), dim3(AttnCfg<D, BLK, QB>::kThreads), 0,
                      a.stream, (const __bf16*)a.q_r, (const __bf16*)a.k_r, (const __bf16*)a.v_t,
                      a.kv_count, a.kv_idx, a.order, (const __bf16*)a.k_g, (const __bf16*)a.v_g,
                      (__bf16*)a.o_r, a.lse, a.Hh, a.N, a.Npad, a.nb, a.Ng, sl2, bias_n, bias_last,
@@ -699,6 +722,10 @@ hipError_t launch_attn_fwd(const AttnArgs& a) {
     if (e != hipSuccess) return e;
     if (a.d == 64) return a.b == 64 ? launch<64, 64, 64, 1>(a) : launch<64, 128, 128, 1>(a);
     return a.b == 64 ? launch<128, 64, 64, 1>(a) : launch<128, 128, 128, 1>(a);
+  }
+  if (a.k_g != nullptr) {
+    if (a.d == 64) return a.b == 64 ? launch<64, 64, 64, 0, true>(a) : launch<64, 128, 128, 0, true>(a);
+    return a.b == 64 ? launch<128, 64, 64, 0, true>(a) : launch<128, 128, 128, 0, true>(a);
   }
   if (a.d == 64) return a.b == 64 ? launch<64, 64>(a) : launch<64, 128>(a);
   return a.b == 64 ? launch<128, 64>(a) : launch<128, 128>(a);
