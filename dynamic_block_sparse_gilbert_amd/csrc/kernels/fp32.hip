@@ -6,19 +6,21 @@
 // Both kernels are plain VALU code: a float32 workload here is the small
 // correctness case, and float32 matrix cores would buy little over it.
 //
-// estimate: one workgroup per (query block I, batch*head).  For every chunk of
-//   up to kQc of the block's sampled queries:
+// estimate: one workgroup per (query block I, batch*head).  Each thread holds
+//   one sampled query of a chunk of up to kQc in registers and takes one of
+//   kKs slices of the keys.  For every chunk:
 //   1. the softmax normaliser of each sampled query over all sampled keys
-//      (threads stride over the sampled keys, online max / sum in the log2
-//      domain, then a workgroup merge), and
-//   2. for every key block J (threads stride over J) the largest score of
-//      each query against J's sampled keys, turned into
-//      max_q exp2(sl2 * t_qJ - lse2_q) and folded into the row held in LDS.
+//      (each thread over its slice, online max / sum in the log2 domain, then
+//      a merge of the slices), and
+//   2. for every key block J (slices stride over J) the largest score of each
+//      query against J's sampled keys, turned into
+//      max_q exp2(sl2 * t_qJ - lse2_q) (a maximum across the chunk's lanes)
+//      and folded into the row held in LDS.
 //   Sampling follows the bf16 path: slot t < k_J = min(k, L_J) of block J is
 //   row J*b + floor(t * L_J / k_J).
-// attention: one workgroup of 256 threads per query block of BLK rows; each
-//   row is served by 256 / BLK threads, each owning D * BLK / 256 channels of
-//   q and of the output.  The kept blocks' K and V rows stream through LDS in
+// attention: workgroups of 256 threads, each over 16 rows of a query block;
+//   each row is served by 16 threads, each owning D / 16 channels of q and of
+//   the output.  The kept blocks' K and V rows stream through LDS in
 //   chunks of 32 keys; scores are reduced across the row's threads by lane
 //   exchanges, and the online softmax rescales once per chunk.
 #include "common.h"
@@ -29,7 +31,12 @@ namespace {
 
 constexpr int kF32Threads = 256;
 constexpr int kQc = 16;        // sampled queries per chunk (estimate)
+constexpr int kKs = kF32Threads / kQc;   // key slices (estimate)
 constexpr int kKc = 32;        // keys per LDS chunk (attention)
+// Threads per query row (attention): 16 lanes share a row's score by lane
+// exchanges, so a 128-row block spreads over eight workgroups (four for 64 rows)
+// and each thread's chain per key is short.
+constexpr int kF32RowThreads = 16;
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
@@ -64,85 +71,91 @@ __device__ __forceinline__ void load_row(const float* p, float (&r)[D]) {
   }
 }
 
+// Dot product of a query row held in registers with a row read from memory, in
+// four independent partial sums.
+template <int D>
+__device__ __forceinline__ float dot_row(const float (&q)[D], const float* __restrict__ p) {
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+  for (int i = 0; i < D; i += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(p + i);
+    s0 = fmaf(q[i], v.x, s0);
+    s1 = fmaf(q[i + 1], v.y, s1);
+    s2 = fmaf(q[i + 2], v.z, s2);
+    s3 = fmaf(q[i + 3], v.w, s3);
+  }
+  return (s0 + s1) + (s2 + s3);
+}
+
 template <int D>
 __global__ __launch_bounds__(kF32Threads) void est_f32_kernel(const float* __restrict__ q_r,
                                                               const float* __restrict__ k_r,
                                                               float* __restrict__ p_imp, int N, int Npad, int b,
                                                               int k, int nb, float sl2) {
   extern __shared__ float pacc[];                  // [nb] the row being formed
-  __shared__ float qs[kQc][D + 4];                 // the chunk's sampled query rows
-  __shared__ float red_m[kQc][kF32Threads / 64], red_l[kQc][kF32Threads / 64];
+  __shared__ float red_m[kKs][kQc], red_l[kKs][kQc];
   __shared__ float lse2[kQc];
   const int I = blockIdx.x, bh = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
+  // thread (qq, ks): query qq of the chunk, key slice ks; the kQc threads of one
+  // slice are consecutive lanes of one wavefront
+  const int qq = tid % kQc, ks = tid / kQc;
   const float* kb = k_r + (int64_t)bh * Npad * D;
   const float* qb = q_r + (int64_t)bh * Npad * D;
   const int LI = min(b, N - I * b), kI = min(k, LI);
   const int Lk = N - (nb - 1) * b, kLast = min(k, Lk);   // the last block's length and samples
+  // sampled row t of key block J
+  auto key_row = [&](int J, int t) {
+    const int LJ = J < nb - 1 ? b : Lk, kJ = J < nb - 1 ? k : kLast;
+    return kb + (int64_t)(J * b + (t * LJ) / kJ) * D;
+  };
   for (int J = tid; J < nb; J += kF32Threads) pacc[J] = 0.f;
 
   for (int q0 = 0; q0 < kI; q0 += kQc) {
-    const int nq = min(kQc, kI - q0);
-    __syncthreads();
-    for (int e = tid; e < kQc * D; e += kF32Threads) {
-      const int qq = e / D, c = e % D;
-      qs[qq][c] = qq < nq ? qb[(int64_t)(I * b + ((q0 + qq) * LI) / kI) * D + c] : 0.f;
+    const bool act = q0 + qq < kI;
+    float q[D];
+    if (act) {
+      load_row<D>(qb + (int64_t)(I * b + ((q0 + qq) * LI) / kI) * D, q);
+    } else {
+#pragma unroll
+      for (int c = 0; c < D; ++c) q[c] = 0.f;
     }
-    __syncthreads();
-    // 1. normalisers over every sampled key
-    float m[kQc], l[kQc];
-#pragma unroll
-    for (int qq = 0; qq < kQc; ++qq) { m[qq] = -INFINITY; l[qq] = 0.f; }
-    for (int r = tid; r < nb * k; r += kF32Threads) {
+    // 1. this query's normaliser over every sampled key: slice ks takes the
+    //    sampled keys r = ks, ks + kKs, ... (online max / sum, log2 domain)
+    float m = -INFINITY, l = 0.f;
+    for (int r = ks; r < nb * k; r += kKs) {
       const int J = r / k, t = r % k;
-      const int LJ = J < nb - 1 ? b : Lk, kJ = J < nb - 1 ? k : kLast;
-      if (t >= kJ) continue;
-      float key[D];
-      load_row<D>(kb + (int64_t)(J * b + (t * LJ) / kJ) * D, key);
-#pragma unroll
-      for (int qq = 0; qq < kQc; ++qq) {
-        if (qq < nq) {
-          const float s = dot_f32<D>(qs[qq], key) * sl2;
-          if (s > m[qq]) {
-            l[qq] = (m[qq] == -INFINITY ? 0.f : l[qq] * exp2f(m[qq] - s)) + 1.f;
-            m[qq] = s;
-          } else {
-            l[qq] += exp2f(s - m[qq]);
-          }
-        }
+      if (t >= (J < nb - 1 ? k : kLast)) continue;
+      const float s = dot_row<D>(q, key_row(J, t)) * sl2;
+      if (s > m) {
+        l = (m == -INFINITY ? 0.f : l * exp2f(m - s)) + 1.f;
+        m = s;
+      } else {
+        l += exp2f(s - m);
       }
     }
-#pragma unroll
-    for (int qq = 0; qq < kQc; ++qq) {
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) merge_ml(m[qq], l[qq], xor_shfl(m[qq], off), xor_shfl(l[qq], off));
-      if (lane == 0) { red_m[qq][wave] = m[qq]; red_l[qq][wave] = l[qq]; }
-    }
+    __syncthreads();   // the previous chunk's lse2 readers are done
+    red_m[ks][qq] = m;
+    red_l[ks][qq] = l;
     __syncthreads();
     if (tid < kQc) {
-      float M = red_m[tid][0], L = red_l[tid][0];
-      for (int w = 1; w < kF32Threads / 64; ++w) merge_ml(M, L, red_m[tid][w], red_l[tid][w]);
+      float M = red_m[0][tid], L = red_l[0][tid];
+      for (int w = 1; w < kKs; ++w) merge_ml(M, L, red_m[w][tid], red_l[w][tid]);
       lse2[tid] = M + log2f(L);
     }
     __syncthreads();
-    // 2. per key block, the largest probability over the chunk's queries
-    for (int J = tid; J < nb; J += kF32Threads) {
-      const int LJ = J < nb - 1 ? b : Lk, kJ = J < nb - 1 ? k : kLast;
-      float tm[kQc];
+    // 2. per key block J (slice ks takes J = ks, ks + kKs, ...): the largest
+    //    score of this query against J's samples, as exp2(sl2 * t_qJ - lse2_q),
+    //    maximised over the chunk's queries and folded into the row
+    const float lq = lse2[qq];
+    for (int J = ks; J < nb; J += kKs) {
+      const int kJ = J < nb - 1 ? k : kLast;
+      float tm = -INFINITY;
+      for (int t = 0; t < kJ; ++t) tm = fmaxf(tm, dot_row<D>(q, key_row(J, t)) * sl2);
+      float p = act ? exp2f(tm - lq) : 0.f;
 #pragma unroll
-      for (int qq = 0; qq < kQc; ++qq) tm[qq] = -INFINITY;
-      for (int t = 0; t < kJ; ++t) {
-        float key[D];
-        load_row<D>(kb + (int64_t)(J * b + (t * LJ) / kJ) * D, key);
-#pragma unroll
-        for (int qq = 0; qq < kQc; ++qq)
-          if (qq < nq) tm[qq] = fmaxf(tm[qq], dot_f32<D>(qs[qq], key) * sl2);
-      }
-      float p = pacc[J];
-#pragma unroll
-      for (int qq = 0; qq < kQc; ++qq)
-        if (qq < nq) p = fmaxf(p, exp2f(tm[qq] - lse2[qq]));
-      pacc[J] = p;
+      for (int off = 1; off < kQc; off <<= 1) p = fmaxf(p, xor_shfl(p, off));
+      if (qq == 0) pacc[J] = fmaxf(pacc[J], p);
     }
   }
   __syncthreads();
@@ -155,16 +168,19 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(
     const float* __restrict__ q_r, const float* __restrict__ k_r, const float* __restrict__ v_r,
     const int32_t* __restrict__ kv_count, const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ order,
     float* __restrict__ o_r, float* __restrict__ lse, int N, int Npad, int nb, int rows_total, float sl2) {
-  constexpr int G = kF32Threads / BLK;   // threads per query row
+  constexpr int G = kF32RowThreads;      // threads per query row
   constexpr int C = D / G;               // channels per thread
+  constexpr int R = kF32Threads / G;     // query rows per workgroup
+  constexpr int kSub = BLK / R;          // workgroups per query block
   __shared__ float Ks[kKc][D + 4];
   __shared__ float Vs[kKc][D + 4];
   const int tid = threadIdx.x;
-  int row = blockIdx.x;
+  const int sub = blockIdx.x % kSub;
+  int row = blockIdx.x / kSub;
   if (order != nullptr) row = clampi(order[row], 0, rows_total - 1);
   const int bh = row / nb, I = row % nb;
   const int r = tid / G, part = tid % G;
-  const int qi = I * BLK + r;
+  const int qi = I * BLK + sub * R + r;
   const bool qok = qi < N;
   float q[C], o[C];
   {
@@ -255,7 +271,8 @@ hipError_t launch_estimate_f32(const EstimateArgs& a) {
 
 hipError_t launch_attn_fwd_f32(const AttnArgs& a) {
   const int rows = a.B * a.Hh * a.nb;
-  dim3 grid(rows);
+  // one workgroup per (query block, group of kF32Threads / kF32RowThreads rows)
+  dim3 grid(rows * (a.b / (kF32Threads / kF32RowThreads)));
   const float sl2 = a.scale * kLog2e;
 #define DBS_F32_ATTN(D, BLK)                                                                                 \
   hipLaunchKernelGGL((attn_f32_kernel<D, BLK>), grid, dim3(kF32Threads), 0, a.stream, (const float*)a.q_r,   \
