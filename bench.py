@@ -21,6 +21,9 @@ before timing; buffers and the permutation are set up outside the timed
 region.
 
 value = dense-equivalent TFLOP/s = 4 * B * H * N^2 * d / (seconds per step).
+graph_ms_per_step / graph_value: the same step recorded once as a HIP graph
+(AsaLayer.capture) and replayed back to back, which removes the host launch
+work per kernel (it bounds the smallest layers); value stays the eager step.
 The timed region holds HIP events at its two ends only; per-stage times come
 from a separate untimed pass with HIP events between the stages on the launch
 stream.  roofline = the attention kernel (the dominant one): executed FLOP
@@ -144,6 +147,28 @@ def run_steps(layer, q, k, v, out, tau, steps, warmup, torch):
     return wall, e0.elapsed_time(e1) / steps
 
 
+def run_graph_steps(layer, q, k, v, out, tau, steps, warmup, torch):
+    """The same step recorded once as a HIP graph (AsaLayer.capture) and replayed: `steps`
+    replays back to back with HIP events at the two ends.  Returns ms per step, or None for a
+    two-stream layer.  The replays run the same kernels on the same buffers as the eager steps
+    (bit-identical results, tested); only the host launch work per kernel is gone."""
+    if layer.overlap:
+        return None
+    g = layer.capture(q, k, v, out, tau=tau)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del g
+    return ms
+
+
 def stage_times(layer, q, k, v, out, tau, steps, torch):
     """Per-stage breakdown in a separate, untimed pass over the same steps: HIP events on the
     launch stream between the stages of each step (each stage time carries one event's cost).
@@ -225,6 +250,7 @@ def measure(layer, cfg, qd, kd, vd, out, tau, steps, warmup, torch):
     from dynamic_block_sparse_gilbert_amd import ops
     sp = layer.spec
     ms, ms_ev = run_steps(layer, qd, kd, vd, out, tau, steps, warmup, torch)
+    ms_graph = run_graph_steps(layer, qd, kd, vd, out, tau, steps, warmup, torch)
     stage = stage_times(layer, qd, kd, vd, out, tau, max(steps, 5), torch)
     cnt, idx = layer.kv_count.cpu().numpy(), layer.kv_idx.cpu().numpy()
     nb, H, N, d = cfg.nb, cfg.heads, cfg.N, cfg.d
@@ -259,6 +285,8 @@ def measure(layer, cfg, qd, kd, vd, out, tau, steps, warmup, torch):
         "value": round(dense / (ms * 1e-3) / 1e12, 2),
         "unit": "dense-equiv TFLOP/s",
         "step_ms_events": round(ms_ev, 4),
+        "graph_ms_per_step": None if ms_graph is None else round(ms_graph, 4),
+        "graph_value": None if ms_graph is None else round(dense / (ms_graph * 1e-3) / 1e12, 2),
         "stages_ms": {kk: round(vv, 4) for kk, vv in stage.items()},
         "step_streams": ("reorder_kv on a second stream beside estimate_mask (dbs_estimate_mask_kvtok); "
                          "stages_ms times the stages one after another" if layer.overlap else "one stream"),
@@ -653,6 +681,8 @@ def main():
         "stages_ms": head["stages_ms"],
         "step_streams": head["step_streams"],
         "step_ms_events": head["step_ms_events"],
+        "graph_ms_per_step": head["graph_ms_per_step"],
+        "graph_value": head["graph_value"],
         "input_gen_s": head["input_gen_s"],
     }
     if "cpu_baseline" in head:

@@ -323,3 +323,29 @@ class AsaLayer:
         self.prepare(q, k, v)
         self.mask(tau, keep_p_imp)
         return self.attend(out, out_dtype)
+
+    def capture(self, q, k, v, out: torch.Tensor, tau: Optional[float] = None, warmup: int = 1):
+        """One forward pass on these buffers recorded as a HIP graph (torch.cuda.CUDAGraph).
+
+        replay() then runs the same launches (K/V reorder, estimate and mask, attention) with no
+        host work per launch, which is what bounds the small layers' steps. q, k, v and out stay
+        bound to the graph: refill them in place between replays. The graph also reuses this
+        layer's buffers (reordered K/V, kept-block lists, estimator workspace), so a replay
+        overwrites them like forward() does. Replays and eager calls on the same layer must not
+        overlap on different streams. Every launch of the step is a kernel; the library issues no
+        memset and no host synchronisation, so the graph holds kernel nodes only. The two-stream
+        layer (overlap=True) is not captured."""
+        if self.overlap:
+            raise ValueError("capture() takes a one-stream layer (overlap=False)")
+        if out is None:
+            raise ValueError("capture() needs the output buffer the graph writes")
+        side = torch.cuda.Stream(device=self.device)
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(warmup):
+                self.forward(q, k, v, out=out, tau=tau, out_dtype=out.dtype)
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.forward(q, k, v, out=out, tau=tau, out_dtype=out.dtype)
+        return g
