@@ -451,7 +451,7 @@ def mask_rules_leg(layer, steps, torch):
     return out
 
 
-def query_pruning_leg(layer, cfg, qd, steps, torch, r=0.5, win=(2, 2, 2)):
+def query_pruning_leg(layer, cfg, qd, steps, torch, r=0.5, win=(2, 2, 2), tau=None):
     """BSA query pruning on the layer and mask: the kept rows (centres of 2 x 2 x 2 windows plus
     the most distinct tokens, keep ratio r), the attention over them with token filling, against the
     unpruned attention on the same lists; each timed back to back between two HIP events."""
@@ -488,8 +488,8 @@ def query_pruning_leg(layer, cfg, qd, steps, torch, r=0.5, win=(2, 2, 2)):
     kv_keep = float(cnt.sum() / (cnt.size * cnt.shape[-1]))
     return {
         "what": "dbs_query_prune + dbs_sparse_attn_fwd_pruned_tok (attention over the kept rows with token "
-                "filling), 2x2x2 centre windows, keep ratio %.2f, on the tau %.2f mask of the Wan-shaped layer"
-                % (r, sp.tau),
+                "filling), 2x2x2 centre windows, keep ratio %.2f, on the tau %.6g mask of the %s layer"
+                % (r, sp.tau if tau is None else tau, cfg.name),
         "query_keep": round(kept_q, 4),
         "kv_block_keep": round(kv_keep, 4),
         "combined_sparsity": round(1.0 - kept_q * kv_keep, 4),
@@ -651,6 +651,11 @@ def main():
         rule = EXTRA_RUNS.get(args.config, [("tau", 0.9)])[0]
     cfg, layer, tens, (head,) = run_config(args.config, [rule], args, torch, dev, cpu=not args.no_cpu_baseline)
     sustained = sustain_leg(layer, tens, head["tau"], args.sustain, torch) if args.sustain > 0 else None
+    # BSA query pruning on the headline layer and mask (the Wan layer's leg runs under extra)
+    qp_head = None
+    if not args.no_legs and cfg.dtype == "bf16" and not cfg.global_pool:
+        layer.mask(head["tau"])
+        qp_head = query_pruning_leg(layer, cfg, tens[0], 10, torch, tau=head["tau"])
     del layer, tens
     torch.cuda.empty_cache()
 
@@ -689,6 +694,8 @@ def main():
         line["cpu_baseline"] = head["cpu_baseline"]
     if sustained is not None:
         line["sustained"] = sustained
+    if qp_head is not None:
+        line["query_pruning"] = qp_head
 
     if not args.no_extra:
         extra = {"configs": {}}
