@@ -52,6 +52,12 @@ HBM_PEAK_GBS = 8000.0              # MI355X HBM3E peak
 # v_exp_f32 issues at half the 32-bit VALU rate (8 cycles per 64-lane wavefront):
 # 256 CUs x 4 SIMDs x 8 results per clock x 2.4 GHz
 EXP_PEAK_PER_S = 256 * 4 * 8 * 2.4e9
+# 32-bit VALU issue: 256 CUs x 4 SIMDs x 16 lanes per clock x 2.4 GHz (a 64-lane instruction takes
+# 4 clocks; packed FP32 is not used).  Every sampled score of the estimate needs an fma (scale and
+# running maximum), an add (the softmax sum), half a v_max3 (the block maximum) and an exponential
+# at half rate (two issue slots): 4.5 slots per score.
+VALU_PEAK_PER_S = 256 * 4 * 16 * 2.4e9
+EST_VALU_SLOTS_PER_SCORE = 4.5
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_traffic.json")
 ATTN_SRC = os.path.join(ROOT, "dynamic_block_sparse_gilbert_amd", "csrc", "kernels", "attn.hip")
 METRIC = "ms/layer + dense-equiv TFLOP/s, block-sparse attn at 90-95% sparsity, 1 GPU"
@@ -268,7 +274,12 @@ def measure(layer, cfg, qd, kd, vd, out, tau, steps, warmup, torch):
     ns = sampled_tokens(cfg)
     est_flop = 2.0 * H * ns * ns * d
     est_exp = float(H) * ns * ns
-    est_bound_ms = max(est_flop / (MFMA_BF16_PEAK_TFLOPS * 1e12), est_exp / EXP_PEAK_PER_S) * 1e3
+    est_valu_ms = est_exp * EST_VALU_SLOTS_PER_SCORE / VALU_PEAK_PER_S * 1e3
+    if cfg.dtype == "fp32":
+        # the float32 estimate forms its scores on the VALU too: one fma per two FLOP
+        est_valu_ms += est_flop / 2.0 / VALU_PEAK_PER_S * 1e3
+    est_bound_ms = max(est_flop / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e3 if cfg.dtype != "fp32" else 0.0,
+                       est_exp / EXP_PEAK_PER_S * 1e3, est_valu_ms)
     kept = float(cnt.sum())          # kept blocks over every row of every head
     mask_bytes = mask_stage_bytes(cnt.shape[0] * H, nb, kept, with_order=layer.order is not None)
     e = 4 if cfg.dtype == "fp32" else 2
@@ -309,10 +320,13 @@ def measure(layer, cfg, qd, kd, vd, out, tau, steps, warmup, torch):
                            "achieved_GBs": round(reorder_bytes / (stage["reorder_kv"] * 1e-3) / 1e9, 1),
                            "peak_GBs": HBM_PEAK_GBS,
                            "frac": round(reorder_bytes / (stage["reorder_kv"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-            "estimate": {"bound": "mfma+exp", "flop": est_flop, "exp": est_exp, "ms": round(t_est, 4),
+            "estimate": {"bound": "mfma+valu", "flop": est_flop, "exp": est_exp, "ms": round(t_est, 4),
                          "bound_ms": round(est_bound_ms, 4), "frac": round(est_bound_ms / t_est, 4),
+                         "valu_floor_ms": round(est_valu_ms, 4),
                          "what": "dbs_estimate_blocks_tok alone (pass + final, P_imp written); bound = "
-                                 "max(FLOP / bf16 MFMA peak, exponentials / %.3g per s)" % EXP_PEAK_PER_S},
+                                 "max(FLOP / bf16 MFMA peak, exponentials / %.3g per s, the VALU issue floor of %.1f slots "
+                                 "per sampled score at %.3g lane-slots per s)" % (EXP_PEAK_PER_S, EST_VALU_SLOTS_PER_SCORE,
+                                                                                VALU_PEAK_PER_S)},
             "mask": {"bound": "hbm", "bytes": mask_bytes, "ms": round(t_mask, 4),
                      "achieved_GBs": round(mask_bytes / (t_mask * 1e-3) / 1e9, 1), "peak_GBs": HBM_PEAK_GBS,
                      "frac": round(mask_bytes / (t_mask * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
