@@ -168,6 +168,7 @@ class AsaLayer:
             if B * Hh * nb <= ORDER_MAX_BLOCKS else None
         self.k_g = self.v_g = None
         self.Ng = 0
+        self.anchor: Optional[torch.Tensor] = None   # query pruning (enable_query_pruning)
         if s.n_pool:
             self.Ng = -(-s.N // s.n_pool)
             Ngpad = -(-self.Ng // s.b) * s.b
@@ -187,6 +188,7 @@ class AsaLayer:
         chosen = ch.chosen(0)
         s.order, s.cuboids = "cuboid_per_head", chosen
         self.perm = ch.per_head_perm(0).to(self.device)
+        self.anchor = None   # window centres follow the order: enable_query_pruning() again
         return chosen
 
     def prepare(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> None:
@@ -323,6 +325,47 @@ class AsaLayer:
         self.prepare(q, k, v)
         self.mask(tau, keep_p_imp)
         return self.attend(out, out_dtype)
+
+    def enable_query_pruning(self, r: float, window: Tuple[int, int, int] = (2, 2, 2)) -> None:
+        """BSA query pruning for forward_pruned() (the BSA notes, key design 1): every query block
+        keeps the centres of its (t, h, w) windows plus its most distinct other rows, up to ceil(r * n)
+        of its n rows; the pruned rows take their centre's output.  Computes the window centres of
+        this layer's order once (host) and allocates the pruning lists.  bf16 layers without ASA_G
+        global tokens only, as the library's pruned attention."""
+        s = self.spec
+        if self.f32 or s.n_pool:
+            raise ValueError("query pruning takes a bf16 layer without global tokens")
+        if not 0.0 < r <= 1.0:
+            raise ValueError("the keep ratio r must lie in (0, 1]")
+        perm = self.perm.cpu().numpy()
+        if perm.ndim == 1:
+            anc = ops.prune_anchors(s.T, s.H, s.W, window, perm, prefix=s.prefix)
+        else:
+            anc = np.stack([ops.prune_anchors(s.T, s.H, s.W, window, p, prefix=s.prefix) for p in perm])
+        self.anchor = torch.from_numpy(anc).to(self.device)
+        B, Hh, nb = s.batch, s.heads, s.nb
+        self.q_count = torch.empty((B, Hh, nb), dtype=torch.int32, device=self.device)
+        self.rowsel = torch.empty((B, Hh, nb, s.b), dtype=torch.int32, device=self.device)
+        self.keep = torch.empty((B, Hh, s.Npad), dtype=torch.uint8, device=self.device)
+        self.prune_r = float(r)
+
+    def forward_pruned(self, q, k, v, out: Optional[torch.Tensor] = None, tau: Optional[float] = None,
+                       out_dtype=torch.bfloat16) -> torch.Tensor:
+        """The layer with BSA query pruning: K/V reorder, estimate and mask as forward(), then the
+        kept query rows (dbs_query_prune), attention for those rows only and token filling
+        (dbs_sparse_attn_fwd_pruned_tok).  Call enable_query_pruning() first."""
+        if self.anchor is None:
+            raise RuntimeError("call enable_query_pruning() first (again after a change of order)")
+        s = self.spec
+        self.prepare(q, k, v)
+        self.mask(tau)
+        ops.query_prune(q, self.perm, self.anchor, s.Npad, s.b, self.prune_r, q_count=self.q_count,
+                        rowsel=self.rowsel, keep=self.keep)
+        self.wait_kv()
+        out, _ = ops.sparse_attn_fwd_pruned_tok(q, self.perm, self.k_r, self.v_t, s.N, s.b, s.scale, self.kv_count,
+                                                self.kv_idx, self.q_count, self.rowsel, self.anchor, self.keep,
+                                                out=out, out_dtype=out_dtype, order=self.order)
+        return out
 
     def capture(self, q, k, v, out: torch.Tensor, tau: Optional[float] = None, warmup: int = 1):
         """One forward pass on these buffers recorded as a HIP graph (torch.cuda.CUDAGraph).

@@ -211,3 +211,48 @@ def test_pruned_wan_shape():
                 src = i if keep[h, i] else int(anc[i])
                 got = o[0, perm[i], h].astype(np.float64)
                 assert np.abs(got - ref[src]).max() <= TOL, (h, i)
+
+
+@pytest.mark.parametrize("cid", [2, 5])
+def test_layer_forward_pruned(cid):
+    """AsaLayer.forward_pruned equals the library calls made one by one, bit for bit; its kept
+    rows equal the unpruned layer's rows and its pruned rows their centre's row (per head, for
+    the per-head cuboid orders of the 720p-shaped layer)."""
+    from dynamic_block_sparse_gilbert_amd.layer import AsaLayer, LayerSpec
+    from workloads import get_config, make_inputs
+    from workloads.generator import head_cuboid
+    say("layer forward_pruned", cid)
+    ops = _ops()
+    cfg = get_config(cid)
+    heads = [0, 1]
+    cub = [head_cuboid(cfg, h) for h in heads] if cfg.reorder == "cuboid_per_head" else None
+    spec = LayerSpec(T=cfg.T, H=cfg.H, W=cfg.W, heads=len(heads), d=cfg.d, b=cfg.b, k=cfg.k, tau=0.9,
+                     order=cfg.reorder, cuboid=cfg.cuboid, cuboids=cub)
+    q, k, v = (torch.from_numpy(a).to(torch.bfloat16).cuda() for a in make_inputs(cfg, heads=heads, workers=4))
+    layer = AsaLayer(spec)
+    layer.enable_query_pruning(0.5)
+    out = layer.forward_pruned(q, k, v)
+    # the same calls one by one
+    ref = AsaLayer(spec)
+    ref.prepare(q, k, v)
+    ref.mask()
+    perm_h = ref.perm.cpu().numpy()
+    anc = np.stack([ops.prune_anchors(cfg.T, cfg.H, cfg.W, (2, 2, 2), p) for p in perm_h]) if perm_h.ndim == 2 \
+        else ops.prune_anchors(cfg.T, cfg.H, cfg.W, (2, 2, 2), perm_h)
+    anc_d = torch.from_numpy(anc).cuda()
+    assert torch.equal(anc_d, layer.anchor)
+    qc, rs, kp = ops.query_prune(q, ref.perm, anc_d, spec.Npad, spec.b, 0.5)
+    out2, _ = ops.sparse_attn_fwd_pruned_tok(q, ref.perm, ref.k_r, ref.v_t, spec.N, spec.b, spec.scale,
+                                             ref.kv_count, ref.kv_idx, qc, rs, anc_d, kp, order=ref.order)
+    full = ref.attend()
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    assert torch.equal(layer.keep, kp)
+    o, f, kpn = host(out).astype(np.float32), host(full).astype(np.float32), host(kp)
+    for hi in range(len(heads)):
+        p = perm_h[hi] if perm_h.ndim == 2 else perm_h
+        a_h = anc[hi] if anc.ndim == 2 else anc
+        kept = kpn[0, hi, :spec.N].astype(bool)
+        tok = p[:spec.N]
+        np.testing.assert_array_equal(o[0, tok[kept], hi], f[0, tok[kept], hi])      # kept rows: unpruned values
+        np.testing.assert_array_equal(o[0, tok[~kept], hi], o[0, tok[a_h[:spec.N][~kept]], hi])   # filled rows
