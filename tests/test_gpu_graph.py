@@ -28,7 +28,9 @@ def _inputs(cfg, heads):
     return [torch.from_numpy(a).to(dt).cuda() for a in make_inputs(cfg, heads=heads, workers=4)]
 
 
-@pytest.mark.parametrize("cid,nheads,tau", [(1, 1, 0.9), (2, 2, 0.9), (3, 2, 0.95)])
+# the tiny float32 layer, the Wan and CogVideoX shapes (register-sorted masks, a work order, ASA_G),
+# and the long layers (radix-selected masks over 1,200 and 872 blocks, per-head orders at 720p)
+@pytest.mark.parametrize("cid,nheads,tau", [(1, 1, 0.9), (2, 2, 0.9), (3, 2, 0.95), (4, 1, 0.86), (5, 2, 0.9)])
 def test_graph_replay_equals_eager(cid, nheads, tau):
     say("graph replay", cid, nheads, tau)
     cfg = get_config(cid)
