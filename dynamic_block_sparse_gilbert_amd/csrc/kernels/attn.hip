@@ -22,7 +22,7 @@
 //                    0-3, 8-11, 4-7, 12-15, so a lane's 8 keys of one channel
 //                    are one contiguous 16-byte LDS read.
 //
-// Software pipeline per stage u (one basic block, two phases):
+// Software pipeline per stage u (two phases, a barrier before each):
 //   phase A: score MFMAs of stage u+1   ||  exp / pack / row-sum of stage u
 //   phase B: PV MFMAs of stage u        ||  row maximum of stage u+1
 //   then, for partial stages and the last global-token tile only, the key mask
@@ -32,9 +32,15 @@
 //   each other's gaps; forcing an instruction interleave measured slower.
 // K and V stages are copied global -> LDS by the buffer form of the DMA path
 // (buffer_load_dwordx4 ... lds, no VGPR staging) into double buffers during
-// the iteration before their use (K of stage u+2 and V of stage u+1 during
-// iteration u); the copies are spread between the MFMAs.  The buffer form counts on vmcnt only, so the LDS operand reads keep
-// partial lgkmcnt waits (the flat form of the same copy forces a full LDS
+// the iteration before their use: K of stage u+2 among phase A's MFMAs and V of
+// stage u+1 among phase B's.  Copies retire in order, so each phase waits only
+// for what it reads: iteration u opens with a wait that leaves the previous
+// phase B's V copies in flight (K of stage u+1 done) and a barrier, and phase B
+// opens with a wait that leaves this phase A's K copies in flight (V of stage u
+// done) and a second barrier.  Every copy thus gets about one iteration to
+// land; a single full wait per iteration gave the last copies of phase B only
+// a few MFMAs.  The buffer form counts on vmcnt only, so the LDS operand reads
+// keep partial lgkmcnt waits (the flat form of the same copy forces a full LDS
 // drain after each issue).  One sched_group_barrier order per stage keeps
 // every LDS operand read two MFMAs ahead of its use.  The kept-block list of
 // the query block is staged in LDS once, so the stage descriptors read it
@@ -460,13 +466,24 @@ void attn_fwd_kernel(
   };
 
   // Phase A: probabilities of the current stage (and, with a next stage, the
-  // next stage's score MFMAs interleaved with them).
+  // next stage's score MFMAs interleaved with them and the K copies of the
+  // stage after it).
   auto phase_a = [&](const f32x16_t (&Sc)[2], f32x16_t (&Sn)[2], const char* ksrc, uint32_t (&P)[16],
-                     const StageDesc* dv, char* vdst, auto has_next) {
+                     const StageDesc* dk, char* kdst, auto has_next) {
     constexpr bool kNext = decltype(has_next)::value;
     if constexpr (kNext) {
       scores(ksrc, Sn);
-      dma_v(*dv, vdst);
+      dma_k(*dk, kdst);
+      // The phase's order: every LDS operand read runs 2 MFMAs ahead of its
+      // use, and the K copies sit between the MFMAs.
+      constexpr int kL = 2, kMM = 2 * (D / 16);
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, kL, 0);
+#pragma unroll
+      for (int i = 0; i < kMM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        if (i + kL < kMM) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+        if (i % 3 == 1 && i / 3 < C::kKPer) __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
+      }
     }
     const float mn = (MODE == 2 && cur_abs) ? -INFINITY : (GLOB ? mneg + cur_eb : mneg);
     float s0, s1;
@@ -487,9 +504,9 @@ void attn_fwd_kernel(
   };
 
   // Phase B: O^T += V^T P^T for the current stage (and the next stage's
-  // row maximum interleaved with it).
+  // row maximum interleaved with it, and the next stage's V copies).
   auto phase_b = [&](const char* vsrc, const uint32_t (&P)[16], const f32x16_t (&Sn)[2],
-                     const StageDesc* dk, char* kdst, auto has_next) {
+                     const StageDesc* dv, char* vdst, auto has_next) {
     constexpr bool kNext = decltype(has_next)::value;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -506,10 +523,9 @@ void attn_fwd_kernel(
     float mx = -INFINITY;
     if constexpr (kNext) {
       mx = row_max(Sn);
-      dma_k(*dk, kdst);
-      // One order for the whole stage: every LDS operand read runs 2 MFMAs
-      // ahead of its use, and the copies sit between the MFMAs.
-      constexpr int kL = 2, kMM = 2 * (D / 16) + 4 * (D / 32), kVm = C::kVPer + C::kKPer;
+      dma_v(*dv, vdst);
+      // The same order for the PV MFMAs, with the V copies between them.
+      constexpr int kL = 2, kMM = 4 * (D / 32), kVm = C::kVPer;
       __builtin_amdgcn_sched_group_barrier(kSgDsRead, kL, 0);
 #pragma unroll
       for (int i = 0; i < kMM; ++i) {
@@ -526,12 +542,15 @@ void attn_fwd_kernel(
   // and vsrc holds V of stage u.
   auto iterate = [&](int u, const f32x16_t (&Sc)[2], f32x16_t (&Sn)[2], char* kdst, char* vdst,
                      const char* ksrc, const char* vsrc, const StageDesc& sn) {
-    wait_dma();
-    __syncthreads();
+    // K of stage u+1 (copied in the previous iteration's phase A) is complete
+    // once at most its V copies (phase B) are outstanding
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(C::kVPer) : "memory");
     const StageDesc sk = stage(min(u + 2, U - 1));   // past the end: a harmless repeat
     uint32_t P[16];
-    phase_a(Sc, Sn, ksrc, P, &sn, vdst, std::true_type{});
-    float mx = phase_b(vsrc, P, Sn, &sk, kdst, std::true_type{});
+    phase_a(Sc, Sn, ksrc, P, &sk, kdst, std::true_type{});
+    // V of stage u: complete once at most this iteration's K copies are outstanding
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(C::kKPer) : "memory");
+    float mx = phase_b(vsrc, P, Sn, &sn, vdst, std::true_type{});
     // Pin the maximum inside the phase (otherwise it is sunk past the branch
     // below, away from the MFMAs it is meant to overlap).
     asm volatile("" ::"v"(mx));
