@@ -256,3 +256,28 @@ def test_layer_forward_pruned(cid):
         tok = p[:spec.N]
         np.testing.assert_array_equal(o[0, tok[kept], hi], f[0, tok[kept], hi])      # kept rows: unpruned values
         np.testing.assert_array_equal(o[0, tok[~kept], hi], o[0, tok[a_h[:spec.N][~kept]], hi])   # filled rows
+
+
+def test_layer_pruning_rejects_unsupported_layers():
+    """forward_pruned needs enable_query_pruning first (and again after a change of order); the
+    float32 and ASA_G layers and keep ratios outside (0, 1] are refused before any launch."""
+    from dynamic_block_sparse_gilbert_amd.layer import AsaLayer, LayerSpec
+    say("layer pruning errors")
+    spec = LayerSpec(T=4, H=8, W=8, heads=1, d=64, b=64, k=8)
+    layer = AsaLayer(spec)
+    x = torch.zeros((1, spec.N, 1, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(RuntimeError, match="enable_query_pruning"):
+        layer.forward_pruned(x, x, x)
+    for r in (0.0, 1.5):
+        with pytest.raises(ValueError, match="keep ratio"):
+            layer.enable_query_pruning(r)
+    layer.enable_query_pruning(0.5)
+    assert layer.anchor is not None and layer.anchor.shape == (spec.N,)
+    layer.choose_cuboids_sics(x, [(1, 8, 8), (2, 4, 8)])
+    assert layer.anchor is None   # the order changed: the centres must be rebuilt
+    with pytest.raises(RuntimeError, match="enable_query_pruning"):
+        layer.forward_pruned(x, x, x)
+    with pytest.raises(ValueError, match="bf16 layer without global tokens"):
+        AsaLayer(LayerSpec(T=4, H=8, W=8, heads=1, d=64, b=64, k=8, dtype="fp32")).enable_query_pruning(0.5)
+    with pytest.raises(ValueError, match="bf16 layer without global tokens"):
+        AsaLayer(LayerSpec(T=4, H=8, W=8, heads=1, d=64, b=64, k=8, n_pool=8)).enable_query_pruning(0.5)
