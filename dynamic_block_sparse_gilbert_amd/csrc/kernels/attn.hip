@@ -32,17 +32,19 @@
 //   each other's gaps; forcing an instruction interleave measured slower.
 // K and V stages are copied global -> LDS by the buffer form of the DMA path
 // (buffer_load_dwordx4 ... lds, no VGPR staging) into double buffers during
-// the iteration before their use: K of stage u+2 among phase A's MFMAs and V of
-// stage u+1 among phase B's.  Copies retire in order, so each phase waits only
-// for what it reads: iteration u opens with a wait that leaves the previous
-// phase B's V copies in flight (K of stage u+1 done) and a barrier, and phase B
-// opens with a wait that leaves this phase A's K copies in flight (V of stage u
-// done) and a second barrier.  Every copy thus gets about one iteration to
-// land; a single full wait per iteration gave the last copies of phase B only
-// a few MFMAs.  The buffer form counts on vmcnt only, so the LDS operand reads
-// keep partial lgkmcnt waits (the flat form of the same copy forces a full LDS
-// drain after each issue).  One sched_group_barrier order per stage keeps
-// every LDS operand read two MFMAs ahead of its use.  The kept-block list of
+// the iteration before their use.  At d = 128, K of stage u+2 goes out among
+// phase A's MFMAs and V of stage u+1 among phase B's.  Copies retire in order,
+// so each phase waits only for what it reads: iteration u opens with a wait
+// that leaves the previous phase B's V copies in flight (K of stage u+1 done)
+// and a barrier, and phase B opens with a wait that leaves this phase A's K
+// copies in flight (V of stage u done) and a second barrier.  Every copy thus
+// gets about one iteration to land; a single full wait per iteration gave the
+// last copies of phase B only a few MFMAs.  At d = 64 (VALU-bound) both copies
+// go out after phase A's first MFMAs behind one full wait per iteration, which
+// saves the second barrier.  The buffer form counts on vmcnt only, so the LDS
+// operand reads keep partial lgkmcnt waits (the flat form of the same copy
+// forces a full LDS drain after each issue).  One sched_group_barrier order
+// per phase keeps every LDS operand read two MFMAs ahead of its use.  The kept-block list of
 // the query block is staged in LDS once, so the stage descriptors read it
 // there rather than with scalar loads; each stage descriptor is computed
 // once, one iteration ahead of its score MFMAs.  LDS rows are padded by one 16-byte
@@ -169,6 +171,12 @@ void attn_fwd_kernel(
     int Hh, int N, int Npad, int nb, int Ng, float sl2, float bias_n, float bias_last, int total, TokIO tok,
     const int32_t* __restrict__ q_count, const int32_t* __restrict__ rowsel) {
   using C = AttnCfg<D, BLK, QB>;
+  // d = 128: each phase waits only for the copies it reads (two barriers per
+  // iteration).  d = 64: the kernel is VALU-bound and a second barrier costs
+  // more than the lead it buys, so both copies go out after phase A's first
+  // MFMAs and one full wait opens the iteration (1.59 against 1.63-1.68 ms on
+  // the CogVideoX-shaped layer, 3% slower at d = 128 on the long layer).
+  constexpr bool kSplitWait = D == 128;
   constexpr int kSubQ = BLK / QB;   // work items per query block
   constexpr int kHalfW = C::kWaves / 2;
   static_assert(MODE != 2 || QB == BLK, "pairs take whole-block workgroups");
@@ -469,11 +477,12 @@ void attn_fwd_kernel(
   // next stage's score MFMAs interleaved with them and the K copies of the
   // stage after it).
   auto phase_a = [&](const f32x16_t (&Sc)[2], f32x16_t (&Sn)[2], const char* ksrc, uint32_t (&P)[16],
-                     const StageDesc* dk, char* kdst, auto has_next) {
+                     const StageDesc* dk, char* kdst, const StageDesc* dv, char* vdst, auto has_next) {
     constexpr bool kNext = decltype(has_next)::value;
     if constexpr (kNext) {
       scores(ksrc, Sn);
       dma_k(*dk, kdst);
+      if constexpr (!kSplitWait) dma_v(*dv, vdst);
       // The phase's order: every LDS operand read runs 2 MFMAs ahead of its
       // use, and one K copy follows each of the first MFMAs (the earliest
       // issue gives the copies the most lead; one copy every third MFMA
@@ -484,7 +493,7 @@ void attn_fwd_kernel(
       for (int i = 0; i < kMM; ++i) {
         __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
         if (i + kL < kMM) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-        if (i < C::kKPer) __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
+        if (i < C::kKPer + (kSplitWait ? 0 : C::kVPer)) __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
       }
     }
     const float mn = (MODE == 2 && cur_abs) ? -INFINITY : (GLOB ? mneg + cur_eb : mneg);
@@ -525,7 +534,7 @@ void attn_fwd_kernel(
     float mx = -INFINITY;
     if constexpr (kNext) {
       mx = row_max(Sn);
-      dma_v(*dv, vdst);
+      if constexpr (kSplitWait) dma_v(*dv, vdst);
       // The same order for the PV MFMAs, one V copy after each of the first.
       constexpr int kL = 2, kMM = 4 * (D / 32), kVm = C::kVPer;
       __builtin_amdgcn_sched_group_barrier(kSgDsRead, kL, 0);
@@ -533,7 +542,7 @@ void attn_fwd_kernel(
       for (int i = 0; i < kMM; ++i) {
         __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
         if (i + kL < kMM) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-        if (i < kVm) __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
+        if (kSplitWait && i < kVm) __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
       }
     }
     return mx;
@@ -544,14 +553,20 @@ void attn_fwd_kernel(
   // and vsrc holds V of stage u.
   auto iterate = [&](int u, const f32x16_t (&Sc)[2], f32x16_t (&Sn)[2], char* kdst, char* vdst,
                      const char* ksrc, const char* vsrc, const StageDesc& sn) {
-    // K of stage u+1 (copied in the previous iteration's phase A) is complete
-    // once at most its V copies (phase B) are outstanding
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(C::kVPer) : "memory");
     const StageDesc sk = stage(min(u + 2, U - 1));   // past the end: a harmless repeat
     uint32_t P[16];
-    phase_a(Sc, Sn, ksrc, P, &sk, kdst, std::true_type{});
-    // V of stage u: complete once at most this iteration's K copies are outstanding
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(C::kKPer) : "memory");
+    if constexpr (kSplitWait) {
+      // K of stage u+1 (copied in the previous iteration's phase A) is complete
+      // once at most its V copies (phase B) are outstanding
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(C::kVPer) : "memory");
+      phase_a(Sc, Sn, ksrc, P, &sk, kdst, &sn, vdst, std::true_type{});
+      // V of stage u: complete once at most this iteration's K copies are outstanding
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(C::kKPer) : "memory");
+    } else {
+      // every copy of the previous iteration (K of stage u+1, V of stage u) is complete
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      phase_a(Sc, Sn, ksrc, P, &sk, kdst, &sn, vdst, std::true_type{});
+    }
     float mx = phase_b(vsrc, P, Sn, &sn, vdst, std::true_type{});
     // Pin the maximum inside the phase (otherwise it is sunk past the branch
     // below, away from the MFMAs it is meant to overlap).
@@ -577,7 +592,7 @@ void attn_fwd_kernel(
     __syncthreads();
     uint32_t P[16];
     f32x16_t unused[2];
-    phase_a(Sc, unused, nullptr, P, nullptr, nullptr, std::false_type{});
+    phase_a(Sc, unused, nullptr, P, nullptr, nullptr, nullptr, nullptr, std::false_type{});
     phase_b(vsrc, P, unused, nullptr, nullptr, std::false_type{});
   };
 
